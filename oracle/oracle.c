@@ -1,0 +1,417 @@
+/*
+ * oracle.c -- plain, single-threaded CPU oracle of the W4A8 decode GEMV path.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  The GPU path shares no code,
+ * header, table or helper with it; neither includes or links the other.
+ *
+ * Every step follows the pages' definitions literally, in their order:
+ *   [Orin] "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
+ *          sections "从 FP 线性层到 INT4 DP4A 的数学推导" (FP linear -> INT4
+ *          DP4A derivation), "INT32 accumulator 是否安全" (int32 safety),
+ *          "DP4A 做了什么" (what DP4A does; the packed-word layout).
+ *   [Ascend] "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录"
+ *          sections 3.1 (Q4_0 fused dequant matmul: int4 + one fp16 scale per
+ *          32 weights), 3.2 (lm_head expanded to int8 with fp16 group scales),
+ *          5 (M=K verification of K draft tokens).
+ *
+ * Precision.  Where a floating-point value decides an integer (a weight or
+ * activation code), the decision is taken in fp32, the precision of the
+ * GPU path: correctly rounded fp32 divisions and round-half-to-even.  Every
+ * other floating-point result (the outputs y) is computed in binary64.
+ * Integer sums are exact in int64 and checked against the int32 bound.
+ * Built with -ffp-contract=off and without fast-math; x86-64 SSE arithmetic
+ * has no excess precision.
+ *
+ * Return codes: 0 ok, ORC_E_ARG (-1) bad size/argument, ORC_E_RANGE (-2)
+ * input outside the format's range, ORC_E_NONFINITE (-3) NaN/Inf input,
+ * ORC_E_BOUND (-4) accumulator outside the int32 bound.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_E_ARG (-1)
+#define ORC_E_RANGE (-2)
+#define ORC_E_NONFINITE (-3)
+#define ORC_E_BOUND (-4)
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16 <-> binary32 (the fp16 scales of [Ascend] 3.1 and 3.2,  */
+/* and the fp16 activations of the W8A16 lm_head).                          */
+/* ------------------------------------------------------------------------ */
+
+/* binary16 -> binary32, exact.  value = (-1)^s * 2^(e-15) * 1.m for normal
+ * numbers and (-1)^s * 2^-14 * 0.m for subnormals. */
+float orc_f16_to_f32(uint16_t h)
+{
+    unsigned sign = (h >> 15) & 1u;
+    unsigned e = (h >> 10) & 0x1Fu;
+    unsigned m = h & 0x3FFu;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)m, -24);                 /* m * 2^-24, exact */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024u + m), (int)e - 25); /* (1024+m) * 2^(e-25) */
+    return sign ? -v : v;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even. */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    float a = fabsf(f);
+    if (isnan(f))
+        return sign | 0x7E00u;
+    /* 65520 lies half-way between 65504 (largest finite, odd significand)
+     * and 2^16 (even): ties-to-even rounds it, and everything above, to Inf. */
+    if (a >= 65520.0f)
+        return sign | 0x7C00u;
+    if (a < 0x1p-14f) {
+        /* subnormal range: the quantum is 2^-24; a*2^24 is exact.  A result
+         * of 1024 is the bit pattern of the smallest normal, as it should be. */
+        float n = nearbyintf(a * 0x1p24f);
+        return sign | (uint16_t)n;
+    }
+    int e;
+    float m = frexpf(a, &e);                 /* a = m * 2^e, 0.5 <= m < 1   */
+    float q = nearbyintf(ldexpf(m, 11));     /* 11-bit significand, RNE     */
+    if (q == 2048.0f) {                      /* rounded up to the next binade */
+        q = 1024.0f;
+        e += 1;
+    }
+    int E = e + 14;                          /* biased exponent: (e-1) + 15 */
+    if (E >= 31)
+        return sign | 0x7C00u;
+    return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)((int)q - 1024));
+}
+
+void orc_f32_to_f16_array(const float* x, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_f32_to_f16(x[i]);
+}
+
+void orc_f16_to_f32_array(const uint16_t* x, int64_t n, float* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_f16_to_f32(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Symmetric quantisation of one value: clip(round(v / s), lo, hi) with an   */
+/* fp32 division and round-half-to-even ([Orin] derivation section).         */
+/* ------------------------------------------------------------------------ */
+static int8_t quant_code(float v, float s, int lo, int hi)
+{
+    if (s == 0.0f)
+        return 0; /* all-zero row/group/vector: every code is 0 */
+    float r = nearbyintf(v / s);
+    if (r < (float)lo)
+        r = (float)lo;
+    if (r > (float)hi)
+        r = (float)hi;
+    return (int8_t)r;
+}
+
+static int max_abs_f32(const float* v, int64_t n, float* amax)
+{
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float t = fabsf(v[i]);
+        if (!(t <= FLT_MAX))
+            return ORC_E_NONFINITE;
+        if (t > a)
+            a = t;
+    }
+    *amax = a;
+    return ORC_OK;
+}
+
+/* Per-row INT4 weights: s^W_j = max_i |W_ji| / 7 (fp32),
+ * q^W_ji = clip(round(W_ji / s^W_j), -8, 7).  [Orin] derivation section. */
+int orc_quantize_weights_int4_rowwise(const float* W, int64_t N, int64_t K,
+                                      int8_t* q, float* s)
+{
+    if (N < 0 || K <= 0)
+        return ORC_E_ARG;
+    for (int64_t j = 0; j < N; ++j) {
+        const float* row = W + j * K;
+        float amax;
+        int rc = max_abs_f32(row, K, &amax);
+        if (rc)
+            return rc;
+        float sj = amax / 7.0f;
+        s[j] = sj;
+        for (int64_t i = 0; i < K; ++i)
+            q[j * K + i] = quant_code(row[i], sj, -8, 7);
+    }
+    return ORC_OK;
+}
+
+/* Group-of-32 quantisation with one fp16 scale per group: the stored scale
+ * is fp16(max|W_g| / d) and codes are taken against that stored value. */
+static int quantize_group32(const float* W, int64_t N, int64_t K, float d, int lo,
+                            int hi, int8_t* q, uint16_t* s16)
+{
+    if (N < 0 || K <= 0 || K % 32)
+        return ORC_E_ARG;
+    int64_t G = K / 32;
+    for (int64_t j = 0; j < N; ++j) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* v = W + j * K + g * 32;
+            float amax;
+            int rc = max_abs_f32(v, 32, &amax);
+            if (rc)
+                return rc;
+            uint16_t h = orc_f32_to_f16(amax / d);
+            s16[j * G + g] = h;
+            float sg = orc_f16_to_f32(h);
+            for (int i = 0; i < 32; ++i)
+                q[j * K + g * 32 + i] = quant_code(v[i], sg, lo, hi);
+        }
+    }
+    return ORC_OK;
+}
+
+/* Q4_0-style: int4 codes in [-8, 7], one fp16 scale per 32 weights.
+ * [Ascend] 3.1 gives the block (16 bytes of 4-bit data + one fp16 scale). */
+int orc_quantize_weights_int4_group32(const float* W, int64_t N, int64_t K,
+                                      int8_t* q, uint16_t* s16)
+{
+    return quantize_group32(W, N, K, 7.0f, -8, 7, q, s16);
+}
+
+/* lm_head expanded to int8: codes in [-32, 31] (the 6-bit value range) with
+ * one fp16 scale per 32 weights.  [Ascend] 3.2. */
+int orc_quantize_weights_int8_group32(const float* W, int64_t N, int64_t K,
+                                      int8_t* q, uint16_t* s16)
+{
+    return quantize_group32(W, N, K, 31.0f, -32, 31, q, s16);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packing: eight signed INT4 codes per uint32, w0 in the low nibble,        */
+/* word = [w7 w6 w5 w4 w3 w2 w1 w0].  [Orin] section "DP4A 做了什么".          */
+/* A nibble holds the code's two's-complement low four bits.                 */
+/* ------------------------------------------------------------------------ */
+uint32_t orc_pack_word(const int8_t q[8])
+{
+    uint32_t w = 0;
+    for (int k = 0; k < 8; ++k)
+        w |= ((uint32_t)(uint8_t)q[k] & 0xFu) << (4 * k);
+    return w;
+}
+
+void orc_unpack_word(uint32_t w, int8_t q[8])
+{
+    for (int k = 0; k < 8; ++k) {
+        int n = (int)((w >> (4 * k)) & 0xFu);
+        q[k] = (int8_t)(n >= 8 ? n - 16 : n);
+    }
+}
+
+int orc_pack_int4(const int8_t* q, int64_t N, int64_t K, uint32_t* w)
+{
+    if (N < 0 || K <= 0 || K % 8)
+        return ORC_E_ARG;
+    for (int64_t i = 0; i < N * K; ++i)
+        if (q[i] < -8 || q[i] > 7)
+            return ORC_E_RANGE;
+    for (int64_t t = 0; t < N * K / 8; ++t)
+        w[t] = orc_pack_word(q + 8 * t);
+    return ORC_OK;
+}
+
+int orc_unpack_int4(const uint32_t* w, int64_t N, int64_t K, int8_t* q)
+{
+    if (N < 0 || K <= 0 || K % 8)
+        return ORC_E_ARG;
+    for (int64_t t = 0; t < N * K / 8; ++t)
+        orc_unpack_word(w[t], q + 8 * t);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic per-token activation quantisation ([Orin] derivation section):    */
+/*   s^x = max_i |x_i| / 127,  q^x_i = clip(round(x_i / s^x), -127, 127).    */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_act_f32(const float* x, int64_t M, int64_t K, int8_t* q, float* s)
+{
+    if (M < 0 || K <= 0)
+        return ORC_E_ARG;
+    for (int64_t m = 0; m < M; ++m) {
+        const float* v = x + m * K;
+        float amax;
+        int rc = max_abs_f32(v, K, &amax);
+        if (rc)
+            return rc;
+        float sx = amax / 127.0f;
+        s[m] = sx;
+        for (int64_t i = 0; i < K; ++i)
+            q[m * K + i] = quant_code(v[i], sx, -127, 127);
+    }
+    return ORC_OK;
+}
+
+/* fp16 activations are widened exactly to fp32 first. */
+int orc_quantize_act_f16(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s)
+{
+    if (M < 0 || K <= 0)
+        return ORC_E_ARG;
+    for (int64_t m = 0; m < M; ++m) {
+        float amax = 0.0f;
+        for (int64_t i = 0; i < K; ++i) {
+            float t = fabsf(orc_f16_to_f32(x[m * K + i]));
+            if (!(t <= FLT_MAX))
+                return ORC_E_NONFINITE;
+            if (t > amax)
+                amax = t;
+        }
+        float sx = amax / 127.0f;
+        s[m] = sx;
+        for (int64_t i = 0; i < K; ++i)
+            q[m * K + i] = quant_code(orc_f16_to_f32(x[m * K + i]), sx, -127, 127);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* W4A8 GEMV ([Orin] derivation section):                                    */
+/*   acc_j = sum_i q^W_ji q^x_i           (exact integer dot product)        */
+/*   y_j   = s^W_j s^x acc_j + b_j        (binary64 here)                    */
+/* The int32 check follows [Orin] "INT32 accumulator 是否安全": per term      */
+/* |q^W q^x| <= 8 * 127 = 1016, so |acc| <= 1016 K must fit in int32.        */
+/* ------------------------------------------------------------------------ */
+static int64_t dot_row_int4(const uint32_t* wrow, const int8_t* qx, int64_t K)
+{
+    int64_t acc = 0;
+    int8_t qw[8];
+    for (int64_t t = 0; t < K / 8; ++t) {
+        orc_unpack_word(wrow[t], qw);
+        for (int k = 0; k < 8; ++k)
+            acc += (int64_t)qw[k] * (int64_t)qx[8 * t + k];
+    }
+    return acc;
+}
+
+static int check_acc(int64_t acc, int64_t K)
+{
+    if (acc > 1016 * K || acc < -1016 * K || acc > INT32_MAX || acc < INT32_MIN)
+        return ORC_E_BOUND;
+    return ORC_OK;
+}
+
+int orc_gemv_w4a8(const uint32_t* w, const float* sw, const float* bias,
+                  const int8_t* qx, float sx, int64_t N, int64_t K,
+                  int32_t* acc_out, double* y)
+{
+    if (N < 0 || K <= 0 || K % 8)
+        return ORC_E_ARG;
+    if (1016 * K > (int64_t)INT32_MAX)
+        return ORC_E_BOUND;
+    for (int64_t i = 0; i < K; ++i)
+        if (qx[i] < -127)
+            return ORC_E_RANGE;
+    for (int64_t j = 0; j < N; ++j) {
+        int64_t acc = dot_row_int4(w + j * (K / 8), qx, K);
+        int rc = check_acc(acc, K);
+        if (rc)
+            return rc;
+        if (acc_out)
+            acc_out[j] = (int32_t)acc;
+        double v = (double)sw[j] * (double)sx * (double)acc;
+        y[j] = bias ? v + (double)bias[j] : v;
+    }
+    return ORC_OK;
+}
+
+/* Group-32 W4A8: acc_jg over each block of 32 weights, then
+ *   y_j = s^x * sum_g s_jg * acc_jg + b_j   (binary64, ascending g). */
+int orc_gemv_w4a8_group32(const uint32_t* w, const uint16_t* s16, const float* bias,
+                          const int8_t* qx, float sx, int64_t N, int64_t K,
+                          int32_t* accg_out, double* y)
+{
+    if (N < 0 || K <= 0 || K % 32)
+        return ORC_E_ARG;
+    if (1016 * K > (int64_t)INT32_MAX)
+        return ORC_E_BOUND;
+    for (int64_t i = 0; i < K; ++i)
+        if (qx[i] < -127)
+            return ORC_E_RANGE;
+    int64_t G = K / 32;
+    for (int64_t j = 0; j < N; ++j) {
+        double sum = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            int64_t acc = dot_row_int4(w + j * (K / 8) + g * 4, qx + g * 32, 32);
+            if (accg_out)
+                accg_out[j * G + g] = (int32_t)acc;
+            sum += (double)orc_f16_to_f32(s16[j * G + g]) * (double)acc;
+        }
+        double v = (double)sx * sum;
+        y[j] = bias ? v + (double)bias[j] : v;
+    }
+    return ORC_OK;
+}
+
+/* W8A16 lm_head: int8 codes with fp16 group-32 scales against fp16 x,
+ *   y_j = sum_g s_jg * sum_{i in g} q_ji x_i   (binary64; each group's inner
+ * sum is exact in binary64: fp16 values are multiples of 2^-24 below 2^16). */
+int orc_gemv_w8a16_group32(const int8_t* w, const uint16_t* s16, const uint16_t* x16,
+                           int64_t N, int64_t K, double* y)
+{
+    if (N < 0 || K <= 0 || K % 32)
+        return ORC_E_ARG;
+    int64_t G = K / 32;
+    for (int64_t i = 0; i < K; ++i) {
+        float t = orc_f16_to_f32(x16[i]);
+        if (!(fabsf(t) <= FLT_MAX))
+            return ORC_E_NONFINITE;
+    }
+    for (int64_t j = 0; j < N; ++j) {
+        double sum = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            double p = 0.0;
+            for (int i = 0; i < 32; ++i)
+                p += (double)w[j * K + g * 32 + i] * (double)orc_f16_to_f32(x16[g * 32 + i]);
+            sum += (double)orc_f16_to_f32(s16[j * G + g]) * p;
+        }
+        y[j] = sum;
+    }
+    return ORC_OK;
+}
+
+/* M=K verification ([Ascend] 5): the same weights against M quantised
+ * tokens; token m uses its own scale s^x_m.
+ *   acc[m][j] = sum_i q^W_ji q^x_mi,  y[m][j] = s^W_j s^x_m acc[m][j] + b_j. */
+int orc_gemm_w4a8_verify(const uint32_t* w, const float* sw, const float* bias,
+                         const int8_t* qx, const float* sx, int64_t M, int64_t N,
+                         int64_t K, int32_t* acc_out, double* y)
+{
+    if (M < 0 || N < 0 || K <= 0 || K % 8)
+        return ORC_E_ARG;
+    if (1016 * K > (int64_t)INT32_MAX)
+        return ORC_E_BOUND;
+    for (int64_t i = 0; i < M * K; ++i)
+        if (qx[i] < -127)
+            return ORC_E_RANGE;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < N; ++j) {
+            int64_t acc = dot_row_int4(w + j * (K / 8), qx + m * K, K);
+            int rc = check_acc(acc, K);
+            if (rc)
+                return rc;
+            if (acc_out)
+                acc_out[m * N + j] = (int32_t)acc;
+            double v = (double)sw[j] * (double)sx[m] * (double)acc;
+            y[m * N + j] = bias ? v + (double)bias[j] : v;
+        }
+    }
+    return ORC_OK;
+}

@@ -1,0 +1,276 @@
+"""ctypes front end of the C oracle (oracle.c).
+
+TEST INFRASTRUCTURE: imported only by tests/, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of bench.py.  Arrays are numpy; every function copies
+its inputs to C-contiguous arrays of the documented dtype and returns new
+numpy arrays.  Errors from the C side raise ``OracleError``.
+
+Pages cited (by title and section):
+  [Orin]   "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
+  [Ascend] "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录"
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_ERR = {-1: "bad argument", -2: "value outside the format's range",
+        -3: "non-finite input", -4: "accumulator outside the int32 bound"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = C.CDLL(_LIB_PATH)
+    P, I64, I32, F32 = C.c_void_p, C.c_int64, C.c_int, C.c_float
+    sig = {
+        "orc_f16_to_f32": (C.c_float, [C.c_uint16]),
+        "orc_f32_to_f16": (C.c_uint16, [C.c_float]),
+        "orc_f32_to_f16_array": (None, [P, I64, P]),
+        "orc_f16_to_f32_array": (None, [P, I64, P]),
+        "orc_quantize_weights_int4_rowwise": (I32, [P, I64, I64, P, P]),
+        "orc_quantize_weights_int4_group32": (I32, [P, I64, I64, P, P]),
+        "orc_quantize_weights_int8_group32": (I32, [P, I64, I64, P, P]),
+        "orc_pack_word": (C.c_uint32, [P]),
+        "orc_unpack_word": (None, [C.c_uint32, P]),
+        "orc_pack_int4": (I32, [P, I64, I64, P]),
+        "orc_unpack_int4": (I32, [P, I64, I64, P]),
+        "orc_quantize_act_f32": (I32, [P, I64, I64, P, P]),
+        "orc_quantize_act_f16": (I32, [P, I64, I64, P, P]),
+        "orc_gemv_w4a8": (I32, [P, P, P, P, F32, I64, I64, P, P]),
+        "orc_gemv_w4a8_group32": (I32, [P, P, P, P, F32, I64, I64, P, P]),
+        "orc_gemv_w8a16_group32": (I32, [P, P, P, I64, I64, P]),
+        "orc_gemm_w4a8_verify": (I32, [P, P, P, P, P, I64, I64, I64, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=dtype)
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise OracleError(_ERR.get(rc, f"error {rc}"))
+
+
+# ---------------------------------------------------------------- fp16 ----
+def f32_to_f16(x) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) of fp32 values, RNE."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _lib.orc_f32_to_f16_array(_p(x), x.size, _p(out))
+    return out
+
+
+def f16_to_f32(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _lib.orc_f16_to_f32_array(_p(h), h.size, _p(out))
+    return out
+
+
+# ------------------------------------------------------ weight quant ----
+def quantize_weights_int4_rowwise(W) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row INT4: s_j = max|W_j|/7, q = clip(rne(W/s), -8, 7).  [Orin] derivation."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = np.empty(N, np.float32)
+    _check(_lib.orc_quantize_weights_int4_rowwise(_p(W), N, K, _p(q), _p(s)))
+    return q, s
+
+
+def quantize_weights_int4_group32(W) -> Tuple[np.ndarray, np.ndarray]:
+    """Q4_0-style: fp16 scale per 32 weights, codes in [-8, 7].  [Ascend] 3.1."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = np.empty((N, K // 32), np.uint16)
+    _check(_lib.orc_quantize_weights_int4_group32(_p(W), N, K, _p(q), _p(s)))
+    return q, s
+
+
+def quantize_weights_int8_group32(W) -> Tuple[np.ndarray, np.ndarray]:
+    """int8 lm_head: fp16 scale per 32 weights, codes in [-32, 31].  [Ascend] 3.2."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = np.empty((N, K // 32), np.uint16)
+    _check(_lib.orc_quantize_weights_int8_group32(_p(W), N, K, _p(q), _p(s)))
+    return q, s
+
+
+# ------------------------------------------------------------ packing ----
+def pack_word(q8: Sequence[int]) -> int:
+    a = _c(q8, np.int8)
+    assert a.size == 8
+    return int(_lib.orc_pack_word(_p(a)))
+
+
+def unpack_word(w: int) -> np.ndarray:
+    out = np.empty(8, np.int8)
+    _lib.orc_unpack_word(C.c_uint32(w & 0xFFFFFFFF), _p(out))
+    return out
+
+
+def pack_int4(q) -> np.ndarray:
+    """[N, K] int8 codes -> [N, K/8] uint32, low nibble first.  [Orin] DP4A section."""
+    q = _c(q, np.int8)
+    N, K = q.shape
+    w = np.empty((N, K // 8), np.uint32)
+    _check(_lib.orc_pack_int4(_p(q), N, K, _p(w)))
+    return w
+
+
+def unpack_int4(w, K: Optional[int] = None) -> np.ndarray:
+    w = _c(w, np.uint32)
+    N, KW = w.shape
+    K = KW * 8 if K is None else K
+    q = np.empty((N, K), np.int8)
+    _check(_lib.orc_unpack_int4(_p(w), N, K, _p(q)))
+    return q
+
+
+# ---------------------------------------------------- activation quant ----
+def quantize_act(x) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token INT8: s = max|x|/127, q = clip(rne(x/s), -127, 127).  [Orin] derivation.
+
+    ``x``: float32 or float16 array, [K] or [M, K].  Returns (q int8, s float32)
+    with q shaped like x and s of shape [] or [M].
+    """
+    x = np.asarray(x)
+    one = x.ndim == 1
+    x2 = x.reshape(1, -1) if one else x
+    M, K = x2.shape
+    q = np.empty((M, K), np.int8)
+    s = np.empty(M, np.float32)
+    if x2.dtype == np.float16:
+        xb = _c(x2.view(np.uint16), np.uint16)
+        _check(_lib.orc_quantize_act_f16(_p(xb), M, K, _p(q), _p(s)))
+    else:
+        xf = _c(x2, np.float32)
+        _check(_lib.orc_quantize_act_f32(_p(xf), M, K, _p(q), _p(s)))
+    return (q[0], s[0]) if one else (q, s)
+
+
+# -------------------------------------------------------------- GEMVs ----
+def gemv_w4a8(w, sw, bias, qx, sx) -> Tuple[np.ndarray, np.ndarray]:
+    """acc_j = sum_i qW_ji qx_i (int32), y_j = sW_j sx acc_j + b_j (float64)."""
+    w = _c(w, np.uint32)
+    N, KW = w.shape
+    K = KW * 8
+    sw = _c(sw, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    qx = _c(qx, np.int8)
+    assert qx.size == K and sw.size == N and (b is None or b.size == N)
+    acc = np.empty(N, np.int32)
+    y = np.empty(N, np.float64)
+    _check(_lib.orc_gemv_w4a8(_p(w), _p(sw), _p(b), _p(qx), C.c_float(float(sx)), N, K,
+                              _p(acc), _p(y)))
+    return acc, y
+
+
+def gemv_w4a8_group32(w, s16, bias, qx, sx) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-group int32 partials acc_jg and y_j = sx sum_g s_jg acc_jg + b_j."""
+    w = _c(w, np.uint32)
+    N, KW = w.shape
+    K = KW * 8
+    s16 = _c(s16, np.uint16)
+    b = None if bias is None else _c(bias, np.float32)
+    qx = _c(qx, np.int8)
+    assert qx.size == K and s16.shape == (N, K // 32)
+    accg = np.empty((N, K // 32), np.int32)
+    y = np.empty(N, np.float64)
+    _check(_lib.orc_gemv_w4a8_group32(_p(w), _p(s16), _p(b), _p(qx), C.c_float(float(sx)),
+                                      N, K, _p(accg), _p(y)))
+    return accg, y
+
+
+def gemv_w8a16_group32(w8, s16, x16) -> np.ndarray:
+    """y_j = sum_g s_jg sum_{i in g} q_ji x_i with fp16 x (uint16 bit patterns or float16)."""
+    w8 = _c(w8, np.int8)
+    N, K = w8.shape
+    s16 = _c(s16, np.uint16)
+    x16 = np.asarray(x16)
+    xb = _c(x16.view(np.uint16) if x16.dtype == np.float16 else x16, np.uint16)
+    assert xb.size == K and s16.shape == (N, K // 32)
+    y = np.empty(N, np.float64)
+    _check(_lib.orc_gemv_w8a16_group32(_p(w8), _p(s16), _p(xb), N, K, _p(y)))
+    return y
+
+
+def gemm_w4a8_verify(w, sw, bias, qx, sx) -> Tuple[np.ndarray, np.ndarray]:
+    """M tokens at once: qx [M, K], sx [M] -> acc [M, N] int32, y [M, N] float64."""
+    w = _c(w, np.uint32)
+    N, KW = w.shape
+    K = KW * 8
+    sw = _c(sw, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    qx = _c(qx, np.int8)
+    M = qx.shape[0]
+    sx = _c(sx, np.float32)
+    assert qx.shape == (M, K) and sx.size == M
+    acc = np.empty((M, N), np.int32)
+    y = np.empty((M, N), np.float64)
+    _check(_lib.orc_gemm_w4a8_verify(_p(w), _p(sw), _p(b), _p(qx), _p(sx), M, N, K,
+                                     _p(acc), _p(y)))
+    return acc, y
+
+
+# ------------------------------------------------------- compositions ----
+def prepare_int4_rowwise(W):
+    """Load-time preparation of one linear: quantise per row, then pack."""
+    q, s = quantize_weights_int4_rowwise(W)
+    return pack_int4(q), s
+
+
+def prepare_int4_group32(W):
+    q, s16 = quantize_weights_int4_group32(W)
+    return pack_int4(q), s16
+
+
+def linear_w4a8(w, sw, bias, x) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """One decode linear: quantise the activation, then the W4A8 GEMV.
+    Returns (qx, sx, acc, y)."""
+    qx, sx = quantize_act(x)
+    acc, y = gemv_w4a8(w, sw, bias, qx, sx)
+    return qx, sx, acc, y
+
+
+def linear_w4a8_group32(w, s16, bias, x):
+    qx, sx = quantize_act(x)
+    accg, y = gemv_w4a8_group32(w, s16, bias, qx, sx)
+    return qx, sx, accg, y
+
+
+def rel_err_rowwise(y_test, y_ref, sw, sx, acc, bias) -> np.ndarray:
+    """|y_test - y_ref| / m_j with m_j = |sW_j sx acc_j| + |b_j|: the error
+    relative to the row's magnitude before cancellation (0/0 counts as 0)."""
+    m = np.abs(np.asarray(sw, np.float64) * np.float64(sx) * np.asarray(acc, np.float64))
+    if bias is not None:
+        m = m + np.abs(np.asarray(bias, np.float64))
+    d = np.abs(np.asarray(y_test, np.float64) - np.asarray(y_ref, np.float64))
+    return np.where(m > 0, d / np.where(m > 0, m, 1.0), np.where(d > 0, np.inf, 0.0))

@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+Each test checks the oracle against a value the pages print, a closed form,
+an invariant, a library routine (numpy's IEEE float16, Python's round-half-
+even ``round``, numpy's integer and float64 matmul) or brute force on tiny
+inputs.  None of them re-types the oracle's own formula as the expected
+value.  Pages cited:
+  [Orin]   "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
+  [Ascend] "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录"
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+from bit_quantized_decode_quantize_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _ints(s):
+    return [int(v, 0) for v in s.split()]
+
+
+def _floats(s):
+    return [float(v) for v in s.split()]
+
+
+# ------------------------------------------------------------------ fp16 --
+def test_f16_to_f32_exhaustive_vs_numpy():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    got = O.f16_to_f32(h)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _f32_patterns():
+    rng = np.random.default_rng(1234)
+    parts = []
+    # every (sign, exponent, top-10 mantissa bits) with low-13-bit endings at and
+    # around the rounding tie of the normal fp16 range
+    hi = np.arange(1 << 19, dtype=np.uint64) << np.uint64(13)
+    for low in (0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF):
+        parts.append((hi | np.uint64(low)).astype(np.uint32))
+    # the fp16 subnormal / underflow range (fp32 exponents 100..113), random
+    e = rng.integers(100, 114, size=2_000_000, dtype=np.uint32)
+    m = rng.integers(0, 1 << 23, size=e.size, dtype=np.uint32)
+    s = rng.integers(0, 2, size=e.size, dtype=np.uint32)
+    parts.append((s << 31) | (e << 23) | m)
+    # exact ties in the subnormal range: odd multiples of 2^-25 (half a quantum)
+    k = np.arange(0, 2048, dtype=np.float64)
+    parts.append(((2 * k + 1) * 2.0 ** -25).astype(np.float32).view(np.uint32))
+    # overflow boundary and random patterns everywhere
+    parts.append(np.array([0x477FE000, 0x477FEFFF, 0x477FF000, 0x477FF001, 0x7F7FFFFF,
+                           0x7F800000, 0xFF800000, 0x00000001, 0x80000000], np.uint32))
+    parts.append(rng.integers(0, 1 << 32, size=2_000_000, dtype=np.uint64).astype(np.uint32))
+    return np.concatenate(parts).view(np.float32)
+
+
+def test_f32_to_f16_rne_vs_numpy():
+    x = _f32_patterns()
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = O.f32_to_f16(x)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7C00) == 0x7C00) and np.all((got[nan] & 0x3FF) != 0)
+
+
+# ------------------------------------------------------------- packing --
+def test_word_layout_golden(golden):
+    g = golden("int4_word_layout.txt")
+    assert O.pack_word(_ints(g["codes"])) == int(g["word"], 16)
+    assert list(O.unpack_word(int(g["word"], 16))) == _ints(g["codes"])
+    assert O.pack_word([-1, 0, 0, 0, 0, 0, 0, 0]) == int(g["single_w0_minus1"], 16)
+    assert O.pack_word([0, 0, 0, 0, 0, 0, 0, -8]) == int(g["single_w7_minus8"], 16)
+
+
+def test_every_code_at_every_position():
+    for k in range(8):
+        for v in range(-8, 8):
+            q = [0] * 8
+            q[k] = v
+            w = O.pack_word(q)
+            assert w == ((v & 0xF) << (4 * k))          # nibble k holds v mod 16
+            assert list(O.unpack_word(w)) == q
+
+
+def test_pack_unpack_roundtrip_exhaustive(tmp_path):
+    """pack(unpack(w)) == w over all 2^32 words (OpenMP helper in C)."""
+    exe = tmp_path / "prt"
+    odir = os.path.join(ROOT, "oracle")
+    subprocess.run(["gcc", "-O2", "-fopenmp", os.path.join(ROOT, "tests/helpers/pack_roundtrip.c"),
+                    "-o", str(exe), f"-L{odir}", "-loracle", f"-Wl,-rpath,{odir}"], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "mismatches=0 out_of_range=0" in r.stdout
+
+
+def test_matrix_pack_is_wordwise_and_rejects_out_of_range():
+    q = I.uniform_int("pin/packq", (5, 48), -8, 7).numpy().astype(np.int8)
+    w = O.pack_int4(q)
+    assert w.shape == (5, 6)
+    for j in range(5):
+        for t in range(6):
+            assert w[j, t] == O.pack_word(q[j, 8 * t:8 * t + 8])
+    assert np.array_equal(O.unpack_int4(w), q)
+    bad = q.copy()
+    bad[2, 3] = 8
+    with pytest.raises(O.OracleError):
+        O.pack_int4(bad)
+    with pytest.raises(O.OracleError):
+        O.pack_int4(np.zeros((2, 12), np.int8))
+
+
+def test_row_bytes_golden(golden):
+    g = golden("row_bytes.txt")
+    K = int(g["hidden"])
+    w = O.pack_int4(np.zeros((3, K), np.int8))
+    assert w.nbytes // 3 == int(g["int4_bytes"])
+    assert K * 1 == int(g["int8_bytes"]) and K * 2 == int(g["fp16_bytes"])
+
+
+# --------------------------------------------------- activation quant --
+def test_act_quant_rne_golden(golden):
+    g = golden("act_quant_rne.txt")
+    x = np.array(_floats(g["x"]), np.float32)
+    q, s = O.quantize_act(x)
+    assert float(s) == float(g["s"])
+    assert list(q) == _ints(g["q"])
+    assert list(q) != _ints(g["q_half_away"])
+
+
+def _act_ref_python(x):
+    """Independent route: numpy fp32 division + Python's round-half-even."""
+    x = np.asarray(x, np.float32)
+    amax = np.float32(np.max(np.abs(x)))
+    s = np.float32(amax / np.float32(127.0))
+    if s == 0:
+        return [0] * x.size, s
+    q = [max(-127, min(127, round(float(np.float32(v / s))))) for v in x]
+    return q, s
+
+
+def test_act_quant_brute_force_vs_python_round():
+    for t in range(40):
+        K = 8 + 8 * (t % 9)
+        x = I.normal(f"pin/act/{t}", K, 10.0 ** ((t % 7) - 3)).numpy()
+        if t % 5 == 0:   # many exact ties: half-integers scaled so that s = 1
+            x = (np.round(x * 4) / 2).astype(np.float32)
+            x[0] = 127.0
+        q, s = O.quantize_act(x)
+        qr, sr = _act_ref_python(x)
+        assert s.view(np.uint32) == sr.view(np.uint32)
+        assert list(q) == qr
+
+
+def test_act_quant_invariants():
+    x = I.with_outliers(I.normal("pin/act/inv", 3584), "pin/act/inv/o").numpy()
+    q, s = O.quantize_act(x)
+    assert np.abs(q.astype(int)).max() == 127 and q.min() >= -127
+    i = int(np.argmax(np.abs(x)))
+    assert q[i] == (127 if x[i] > 0 else -127)
+    for k in (-20, -3, 5, 30):          # power-of-two scaling is exact in fp32
+        q2, s2 = O.quantize_act(np.ldexp(x, k).astype(np.float32))
+        assert np.array_equal(q2, q) and s2 == np.float32(np.ldexp(s, k))
+    qn, sn = O.quantize_act(-x)
+    assert np.array_equal(qn, -q) and sn == s
+    qz, sz = O.quantize_act(np.zeros(64, np.float32))
+    assert sz == 0 and not qz.any()
+    with pytest.raises(O.OracleError):
+        O.quantize_act(np.array([1.0, np.nan] + [0.0] * 6, np.float32))
+    with pytest.raises(O.OracleError):
+        O.quantize_act(np.array([1.0, np.inf] + [0.0] * 6, np.float32))
+
+
+def test_act_quant_fp16_equals_widened_fp32():
+    x16 = I.normal("pin/act/f16", (3, 1536), 1.0, dtype=__import__("torch").float16).numpy()
+    q16, s16 = O.quantize_act(x16)
+    q32, s32 = O.quantize_act(x16.astype(np.float32))
+    assert np.array_equal(q16, q32) and np.array_equal(s16, s32)
+
+
+# ------------------------------------------------------- weight quant --
+def _round_div(W, s):
+    """clip(round(W/s)) via numpy fp32 division and Python round()."""
+    out = np.zeros(W.shape, np.int64)
+    for idx in np.ndindex(W.shape):
+        if s[idx[:-1]] != 0:
+            out[idx] = round(float(np.float32(W[idx] / s[idx[:-1]])))
+    return out
+
+
+def test_weight_quant_rowwise_vs_python():
+    W = I.normal("pin/wq", (7, 64), 0.02).numpy()
+    W[3] = 0.0                                       # all-zero row
+    W[5, 10] = -0.5                                  # a dominant negative entry
+    q, s = O.quantize_weights_int4_rowwise(W)
+    amax = np.max(np.abs(W), axis=1)
+    assert np.array_equal(s, (amax / np.float32(7.0)).astype(np.float32))
+    ref = np.clip(_round_div(W, s), -8, 7)
+    assert np.array_equal(q.astype(np.int64), ref)
+    assert not q[3].any() and s[3] == 0
+    assert q[5, 10] == -7
+    # quantisation error bound |W - s q| <= s/2 (nothing clips under max/7)
+    err = np.abs(W.astype(np.float64) - s[:, None].astype(np.float64) * q)
+    assert np.all(err <= s[:, None].astype(np.float64) / 2 * (1 + 1e-6))
+    assert np.all(np.abs(q[s > 0]).max(axis=1) == 7)
+
+
+def test_weight_quant_group32_vs_numpy_fp16():
+    W = I.normal("pin/wq32", (5, 96), 0.02).numpy()
+    W[1, 32:64] = 0.0                                # an all-zero group
+    q, s16 = O.quantize_weights_int4_group32(W)
+    amax = np.max(np.abs(W.reshape(5, 3, 32)), axis=2)
+    ref_s16 = (amax / np.float32(7.0)).astype(np.float32).astype(np.float16)
+    assert np.array_equal(s16, ref_s16.view(np.uint16))
+    sg = ref_s16.astype(np.float32)
+    ref = np.clip(_round_div(W.reshape(5, 3, 32), sg), -8, 7).reshape(5, 96)
+    assert np.array_equal(q.astype(np.int64), ref)
+    assert not q[1, 32:64].any()
+
+
+def test_weight_quant_int8_group32_vs_numpy_fp16():
+    W = I.normal("pin/wq8", (4, 64), 0.02).numpy()
+    q, s16 = O.quantize_weights_int8_group32(W)
+    amax = np.max(np.abs(W.reshape(4, 2, 32)), axis=2)
+    ref_s16 = (amax / np.float32(31.0)).astype(np.float32).astype(np.float16)
+    assert np.array_equal(s16, ref_s16.view(np.uint16))
+    ref = np.clip(_round_div(W.reshape(4, 2, 32), ref_s16.astype(np.float32)), -32, 31)
+    assert np.array_equal(q.astype(np.int64), ref.reshape(4, 64))
+    assert q.min() >= -32 and q.max() <= 31
+
+
+# ------------------------------------------------------------- GEMVs --
+def test_int32_bound_golden(golden):
+    g = golden("int32_bound.txt")
+    K = int(g["hidden"])
+    assert int(g["max_abs_qw"]) * int(g["max_abs_qx"]) == int(g["max_term"])
+    w = O.pack_int4(np.full((2, K), -8, np.int8))
+    sw = np.ones(2, np.float32)
+    acc, _ = O.gemv_w4a8(w, sw, None, np.full(K, -127, np.int8), 1.0)
+    assert list(acc) == [int(g["row_bound"])] * 2
+    acc, _ = O.gemv_w4a8(w, sw, None, np.full(K, 127, np.int8), 1.0)
+    assert list(acc) == [-int(g["row_bound"])] * 2
+    assert int(g["row_bound"]) < int(g["int32_max"]) == 2 ** 31 - 1
+    # the down projection's reduction length, same argument: 18944 * 1016
+    K2 = 18944
+    w2 = O.pack_int4(np.full((1, K2), -8, np.int8))
+    acc2, _ = O.gemv_w4a8(w2, np.ones(1, np.float32), None, np.full(K2, -127, np.int8), 1.0)
+    assert acc2[0] == K2 * int(g["max_term"]) == 19247104
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 16), (9, 32), (4, 40), (7, 64), (2, 3584)])
+def test_gemv_acc_brute_force_vs_numpy_matmul(N, K):
+    q = I.uniform_int(f"pin/gq/{N}/{K}", (N, K), -8, 7).numpy().astype(np.int8)
+    q[0, 0] = -8
+    qx = I.uniform_int(f"pin/gx/{N}/{K}", K, -127, 127).numpy().astype(np.int8)
+    w = O.pack_int4(q)
+    sw = I.normal(f"pin/gs/{N}/{K}", N, 0.01).numpy()
+    b = I.normal(f"pin/gb/{N}/{K}", N, 0.01).numpy()
+    acc, y = O.gemv_w4a8(w, sw, b, qx, np.float32(0.37))
+    ref = q.astype(np.int64) @ qx.astype(np.int64)
+    assert np.array_equal(acc.astype(np.int64), ref)
+    # the same integer through DP4A's pairing: dot4(w0..3, x0..3) + dot4(w4..7, x4..7)
+    lo = q.reshape(N, -1, 8)[:, :, :4].astype(np.int64)
+    hi = q.reshape(N, -1, 8)[:, :, 4:].astype(np.int64)
+    xl = qx.reshape(-1, 8)[:, :4].astype(np.int64)
+    xh = qx.reshape(-1, 8)[:, 4:].astype(np.int64)
+    assert np.array_equal(acc.astype(np.int64), (lo * xl).sum((1, 2)) + (hi * xh).sum((1, 2)))
+    # bias off: y scales with acc alone
+    _, y0 = O.gemv_w4a8(w, sw, None, qx, np.float32(0.37))
+    assert np.allclose(y - y0, b.astype(np.float64), rtol=0, atol=1e-15)
+
+
+def test_gemv_closed_form_bound_against_unquantised_math():
+    """|y - (Wx + b)| <= sum_i (s_j/2 |x_i| + |W_ji| s^x/2 + s_j s^x/4):
+    |W - s q| <= s/2 and |x - s^x q^x| <= s^x/2 ([Orin] derivation)."""
+    d = I.single_gemv_inputs(seed=3, N=256, K=3584)
+    W, x, b = d["W"].numpy(), d["x"].numpy(), d["b"].numpy()
+    w, s = O.prepare_int4_rowwise(W)
+    qx, sx, acc, y = O.linear_w4a8(w, s, b, x)
+    exact = W.astype(np.float64) @ x.astype(np.float64) + b
+    s64, sx64 = s.astype(np.float64), float(sx)
+    bound = (s64 / 2)[:, None] * np.abs(x)[None, :] + np.abs(W) * sx64 / 2 + (s64[:, None] * sx64 / 4)
+    bound = bound.sum(1) * (1 + 1e-9) + 1e-12
+    assert np.all(np.abs(y - exact) <= bound)
+    # and the quantised result is a real approximation, not a trivially loose one
+    assert np.median(np.abs(y - exact) / (np.abs(exact) + 1e-3)) < 0.2
+
+
+def test_gemv_invariants_permutation_and_linearity():
+    q = I.uniform_int("pin/inv/q", (16, 64), -8, 7).numpy().astype(np.int8)
+    w = O.pack_int4(q)
+    sw = np.ones(16, np.float32)
+    x1 = I.uniform_int("pin/inv/x1", 64, -60, 60).numpy().astype(np.int8)
+    x2 = I.uniform_int("pin/inv/x2", 64, -60, 60).numpy().astype(np.int8)
+    a1, _ = O.gemv_w4a8(w, sw, None, x1, 1.0)
+    a2, _ = O.gemv_w4a8(w, sw, None, x2, 1.0)
+    a12, _ = O.gemv_w4a8(w, sw, None, (x1 + x2).astype(np.int8), 1.0)
+    assert np.array_equal(a12, a1 + a2)
+    perm = I.distinct_indices("pin/inv/perm", 16, 16).numpy()
+    ap, _ = O.gemv_w4a8(w[perm], sw, None, x1, 1.0)
+    assert np.array_equal(ap, a1[perm])
+
+
+def test_fused_rows_equal_separate_gemvs(golden):
+    """[Ascend] 3.1: concatenated q/k/v (and gate/up) rows stay a valid weight,
+    so one GEMV over the fused rows equals the separate GEMVs bit for bit."""
+    K = 256
+    parts = [I.normal(f"pin/fuse/{n}", (r, K), 0.02).numpy() for n, r in (("q", 24), ("k", 8), ("v", 8))]
+    bs = [I.normal(f"pin/fuse/b/{i}", p.shape[0], 0.01).numpy() for i, p in enumerate(parts)]
+    x = I.normal("pin/fuse/x", K).numpy()
+    sep = [O.linear_w4a8(*O.prepare_int4_rowwise(p), b, x) for p, b in zip(parts, bs)]
+    wf, sf = O.prepare_int4_rowwise(np.concatenate(parts))
+    _, _, accf, yf = O.linear_w4a8(wf, sf, np.concatenate(bs), x)
+    assert np.array_equal(accf, np.concatenate([r[2] for r in sep]))
+    assert np.array_equal(yf, np.concatenate([r[3] for r in sep]))
+    g = golden("fused_launches.txt")
+    assert int(g["layers"]) * 7 == int(g["launches_unfused"])
+    assert int(g["layers"]) * 4 == int(g["launches_fused"])
+
+
+def test_gemv_group32_equal_scales_reduce_to_rowwise():
+    """With every 32-group at the same max |W| = 7 * 2^-6, every fp16 group
+    scale and the fp32 row scale are exactly 2^-6: the group partials sum to
+    the per-row accumulator and both outputs agree."""
+    N, K = 6, 128
+    W = I.normal("pin/g32eq", (N, K), 0.02).numpy()
+    W = np.clip(W, -0.1, 0.1)
+    W[:, ::32] = np.float32(7 * 2.0 ** -6) * np.where(np.arange(N)[:, None] % 2, 1, -1)
+    b = I.normal("pin/g32eq/b", N, 0.01).numpy()
+    x = I.normal("pin/g32eq/x", K).numpy()
+    wr, sr = O.prepare_int4_rowwise(W)
+    wg, sg = O.prepare_int4_group32(W)
+    assert np.all(sr == np.float32(2.0 ** -6)) and np.all(O.f16_to_f32(sg) == np.float32(2.0 ** -6))
+    assert np.array_equal(wr, wg)
+    _, _, acc, yr = O.linear_w4a8(wr, sr, b, x)
+    _, _, accg, yg = O.linear_w4a8_group32(wg, sg, b, x)
+    assert np.array_equal(accg.sum(1), acc)
+    assert np.array_equal(yr, yg)
+
+
+def test_gemv_group32_vs_numpy_float64():
+    N, K = 9, 192
+    q = I.uniform_int("pin/g32/q", (N, K), -8, 7).numpy().astype(np.int8)
+    s16 = O.f32_to_f16(np.abs(I.normal("pin/g32/s", (N, K // 32), 0.003).numpy()) + 1e-4)
+    qx = I.uniform_int("pin/g32/x", K, -127, 127).numpy().astype(np.int8)
+    b = I.normal("pin/g32/b", N, 0.01).numpy()
+    sx = np.float32(0.0421)
+    accg, y = O.gemv_w4a8_group32(O.pack_int4(q), s16, b, qx, sx)
+    ref_g = np.einsum("ngk,gk->ng", q.reshape(N, -1, 32).astype(np.int64), qx.reshape(-1, 32).astype(np.int64))
+    assert np.array_equal(accg.astype(np.int64), ref_g)
+    sg = s16.view(np.float16).astype(np.float64)
+    ref = float(sx) * (sg * ref_g).sum(1) + b
+    assert np.allclose(y, ref, rtol=1e-14, atol=0)
+
+
+def test_gemv_w8a16_vs_numpy_float64_dequantised_matmul():
+    N, K = 11, 160
+    W = I.normal("pin/w8", (N, K), 0.02).numpy()
+    q, s16 = O.quantize_weights_int8_group32(W)
+    q[2, 5] = -32                                     # the code range's negative end
+    x16 = I.normal("pin/w8/x", K, 1.0, dtype=__import__("torch").float16).numpy()
+    y = O.gemv_w8a16_group32(q, s16, x16)
+    deq = q.astype(np.float64) * np.repeat(s16.view(np.float16).astype(np.float64), 32, axis=1)
+    ref = deq @ x16.astype(np.float64)
+    mag = np.abs(deq) @ np.abs(x16.astype(np.float64))
+    assert np.all(np.abs(y - ref) <= 1e-13 * mag + 1e-300)
+
+
+def test_verify_matches_per_token_gemv():
+    """[Ascend] 5: verifying M tokens streams the weights once; each token's
+    column equals the single-token GEMV, and M = 1 is the GEMV itself."""
+    N, K, M = 40, 256, 5
+    W = I.normal("pin/ver/W", (N, K), 0.02).numpy()
+    b = I.normal("pin/ver/b", N, 0.01).numpy()
+    X = I.normal("pin/ver/X", (M, K)).numpy()
+    w, s = O.prepare_int4_rowwise(W)
+    qx, sx = O.quantize_act(X)
+    acc, y = O.gemm_w4a8_verify(w, s, b, qx, sx)
+    for m in range(M):
+        a1, y1 = O.gemv_w4a8(w, s, b, qx[m], sx[m])
+        assert np.array_equal(acc[m], a1) and np.array_equal(y[m], y1)
+    a1, y1 = O.gemm_w4a8_verify(w, s, b, qx[:1], sx[:1])
+    assert np.array_equal(a1[0], acc[0]) and np.array_equal(y1[0], y[0])
+
+
+def test_errors_are_reported():
+    with pytest.raises(O.OracleError):
+        O.quantize_weights_int4_rowwise(np.array([[1.0, np.inf] + [0.0] * 6], np.float32))
+    with pytest.raises(O.OracleError):
+        O.quantize_weights_int4_group32(np.zeros((2, 48), np.float32))
+    with pytest.raises(O.OracleError):   # -128 is outside the activation code range
+        O.gemv_w4a8(np.zeros((1, 1), np.uint32), np.ones(1, np.float32), None,
+                    np.array([-128] + [0] * 7, np.int8), 1.0)
