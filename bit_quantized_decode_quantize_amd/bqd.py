@@ -1,0 +1,371 @@
+"""Python binding of libbqd.so (the C ABI in include/bqd.h).
+
+Argument marshalling only: every computation runs in the library's gfx950
+kernels.  Functions take CUDA (HIP) torch tensors, check dtypes, shapes and
+contiguity (the C ABI sees plain pointers, so buffer sizes are checked here,
+before anything is launched), allocate missing outputs with torch, and pass
+``torch.cuda.current_stream()`` unless a stream is given.  Any non-zero
+status raises ``BQDError``.  If the library has not been built, every entry
+point raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbqd.so")
+
+BQD_F32, BQD_F16 = 0, 1
+BQD_SCALE_ROW_F32, BQD_SCALE_GROUP32_F16 = 0, 1
+BQD_MAX_K = 65536
+BQD_MAX_TOKENS = 16
+
+ENTRY_POINTS = (
+    "bqd_abi_version", "bqd_status_string", "bqd_init",
+    "quantize_weights_int4_rowwise", "quantize_weights_int4_group32",
+    "quantize_weights_int8_group32", "pack_int4_rows_host", "unpack_int4_rows_host",
+    "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
+    "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
+)
+
+
+class BQDError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class LinearW4A8(C.Structure):
+    """Mirror of ``bqd_linear_w4a8``."""
+    _fields_ = [("wq", C.c_void_p), ("scales", C.c_void_p), ("bias", C.c_void_p),
+                ("N", C.c_int32), ("K", C.c_int32), ("scale_kind", C.c_int32),
+                ("r", C.c_int32), ("lanes_per_row", C.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run "
+                           "`python -m bit_quantized_decode_quantize_amd.csrc.build`")
+    L = C.CDLL(LIB_PATH)
+    P, I = C.c_void_p, C.c_int32
+    sig = {
+        "bqd_abi_version": (I, []),
+        "bqd_status_string": (C.c_char_p, [I]),
+        "bqd_init": (I, []),
+        "quantize_weights_int4_rowwise": (I, [P, I, I, P, P, P]),
+        "quantize_weights_int4_group32": (I, [P, I, I, P, P, P]),
+        "quantize_weights_int8_group32": (I, [P, I, I, P, P, P]),
+        "pack_int4_rows_host": (I, [P, I, I, P]),
+        "unpack_int4_rows_host": (I, [P, I, I, P]),
+        "quantize_act": (I, [P, I, I, I, P, P, P]),
+        "gemv_w4a8": (I, [P, P, P, P, P, P, P, I, I, I, I, P]),
+        "linear_w4a8": (I, [P, P, P, P, I, P, P, P, P, I, I, I, I, P]),
+        "gemv_w4a8_group32": (I, [P, P, P, P, P, P, P, I, I, I, I, P]),
+        "linear_w4a8_group32": (I, [P, P, P, P, I, P, P, P, P, I, I, I, I, P]),
+        "gemv_w8a16_group32": (I, [P, P, P, P, I, I, I, I, P]),
+        "gemm_w4a8_verify": (I, [P, P, P, P, P, P, P, I, I, I, I, P]),
+        "layer_w4a8_forward": (I, [C.POINTER(LinearW4A8), I, P, I, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().bqd_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return lib().bqd_abi_version()
+
+
+def _call(name: str, *args) -> None:
+    rc = getattr(lib(), name)(*args)
+    if rc != 0:
+        raise BQDError(name, rc, status_string(rc))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, numel: Optional[int] = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t
+
+
+def _opt(t, name, dtypes, numel):
+    return None if t is None else _dev(t, name, dtypes, numel)
+
+
+def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+_WORD = (torch.int32,)
+_F32 = (torch.float32,)
+_X = (torch.float32, torch.float16)
+
+
+def _xdtype(x: torch.Tensor) -> int:
+    return BQD_F32 if x.dtype == torch.float32 else BQD_F16
+
+
+# ---------------------------------------------------------------- weights --
+def quantize_weights_int4_rowwise(W: torch.Tensor, wq=None, sw=None, stream=None):
+    """W fp32 [N, K] -> (wq int32 [N, K/8] packed, sw fp32 [N])."""
+    N, K = W.shape
+    _dev(W, "W", _F32)
+    wq = _empty((N, K // 8), torch.int32, W) if wq is None else _dev(wq, "wq", _WORD, N * K // 8)
+    sw = _empty((N,), torch.float32, W) if sw is None else _dev(sw, "sw", _F32, N)
+    _call("quantize_weights_int4_rowwise", W.data_ptr(), N, K, wq.data_ptr(), sw.data_ptr(),
+          _stream(stream))
+    return wq, sw
+
+
+def quantize_weights_int4_group32(W: torch.Tensor, wq=None, s16=None, stream=None):
+    """W fp32 [N, K] -> (wq int32 [N, K/8], s16 fp16 [N, K/32])."""
+    N, K = W.shape
+    _dev(W, "W", _F32)
+    wq = _empty((N, K // 8), torch.int32, W) if wq is None else _dev(wq, "wq", _WORD, N * K // 8)
+    s16 = _empty((N, K // 32), torch.float16, W) if s16 is None else \
+        _dev(s16, "s16", (torch.float16,), N * (K // 32))
+    _call("quantize_weights_int4_group32", W.data_ptr(), N, K, wq.data_ptr(), s16.data_ptr(),
+          _stream(stream))
+    return wq, s16
+
+
+def quantize_weights_int8_group32(W: torch.Tensor, w8=None, s16=None, stream=None):
+    """W fp32 [N, K] -> (w8 int8 [N, K] codes in [-32, 31], s16 fp16 [N, K/32])."""
+    N, K = W.shape
+    _dev(W, "W", _F32)
+    w8 = _empty((N, K), torch.int8, W) if w8 is None else _dev(w8, "w8", (torch.int8,), N * K)
+    s16 = _empty((N, K // 32), torch.float16, W) if s16 is None else \
+        _dev(s16, "s16", (torch.float16,), N * (K // 32))
+    _call("quantize_weights_int8_group32", W.data_ptr(), N, K, w8.data_ptr(), s16.data_ptr(),
+          _stream(stream))
+    return w8, s16
+
+
+def pack_int4_rows_host(q: torch.Tensor) -> torch.Tensor:
+    """Host: int8 codes [N, K] in [-8, 7] -> int32 words [N, K/8]."""
+    q = q.detach().cpu().contiguous().to(torch.int8)
+    N, K = q.shape
+    out = torch.empty((N, K // 8), dtype=torch.int32)
+    _call("pack_int4_rows_host", q.data_ptr(), N, K, out.data_ptr())
+    return out
+
+
+def unpack_int4_rows_host(w: torch.Tensor, K: Optional[int] = None) -> torch.Tensor:
+    w = w.detach().cpu().contiguous().to(torch.int32)
+    N = w.shape[0]
+    K = w.shape[1] * 8 if K is None else K
+    if w.numel() != N * K // 8:
+        raise ValueError("word count does not match K")
+    out = torch.empty((N, K), dtype=torch.int8)
+    _call("unpack_int4_rows_host", w.data_ptr(), N, K, out.data_ptr())
+    return out
+
+
+# ------------------------------------------------------------ activations --
+def quantize_act(x: torch.Tensor, qx=None, sx=None, stream=None):
+    """x fp32/fp16 [K] or [M, K] -> (qx int8 like x, sx fp32 [M] (or [1]))."""
+    _dev(x, "x", _X)
+    x2 = x.view(1, -1) if x.dim() == 1 else x
+    M, K = x2.shape
+    qx = _empty(x.shape, torch.int8, x) if qx is None else _dev(qx, "qx", (torch.int8,), M * K)
+    sx = _empty((M,), torch.float32, x) if sx is None else _dev(sx, "sx", _F32, M)
+    _call("quantize_act", x.data_ptr(), _xdtype(x), M, K, qx.data_ptr(), sx.data_ptr(),
+          _stream(stream))
+    return qx, sx
+
+
+# ------------------------------------------------------------------ GEMVs --
+def _wshape(wq: torch.Tensor, K: Optional[int]):
+    N = wq.shape[0]
+    K = wq.shape[1] * 8 if K is None else K
+    return N, K
+
+
+def gemv_w4a8(wq, sw, bias, qx, sx, y=None, acc=None, r=0, lanes_per_row=0, stream=None):
+    """y[j] = sw[j]*sx*acc[j] + b[j] over packed per-row INT4 weights and int8 qx.
+    ``acc=True`` also returns the int32 accumulators."""
+    N, K = _wshape(wq, None)
+    _dev(wq, "wq", _WORD, N * K // 8)
+    _dev(sw, "sw", _F32, N)
+    _opt(bias, "bias", _F32, N)
+    _dev(qx, "qx", (torch.int8,), K)
+    _dev(sx, "sx", _F32)
+    if sx.numel() < 1:
+        raise ValueError("sx must hold one value")
+    y = _empty((N,), torch.float32, wq) if y is None else _dev(y, "y", _F32, N)
+    want = acc is True
+    acc_t = _empty((N,), torch.int32, wq) if want else _opt(acc if acc is not False else None,
+                                                            "acc", (torch.int32,), N)
+    _call("gemv_w4a8", wq.data_ptr(), sw.data_ptr(), _ptr(bias), qx.data_ptr(), sx.data_ptr(),
+          y.data_ptr(), _ptr(acc_t), N, K, r, lanes_per_row, _stream(stream))
+    return (y, acc_t) if acc_t is not None else y
+
+
+def linear_w4a8(wq, sw, bias, x, y=None, want_q=False, want_acc=False, r=0, lanes_per_row=0,
+                stream=None):
+    """Quantise x (fp32/fp16 [K]) in the GEMV prologue, then the W4A8 GEMV.
+    Returns y, plus (qx, sx) if want_q, plus acc if want_acc."""
+    N, K = _wshape(wq, None)
+    _dev(wq, "wq", _WORD, N * K // 8)
+    _dev(sw, "sw", _F32, N)
+    _opt(bias, "bias", _F32, N)
+    _dev(x, "x", _X, K)
+    y = _empty((N,), torch.float32, wq) if y is None else _dev(y, "y", _F32, N)
+    qx = _empty((K,), torch.int8, wq) if want_q else None
+    sx = _empty((1,), torch.float32, wq) if want_q else None
+    acc = _empty((N,), torch.int32, wq) if want_acc else None
+    _call("linear_w4a8", wq.data_ptr(), sw.data_ptr(), _ptr(bias), x.data_ptr(), _xdtype(x),
+          y.data_ptr(), _ptr(qx), _ptr(sx), _ptr(acc), N, K, r, lanes_per_row, _stream(stream))
+    out = [y]
+    if want_q:
+        out += [qx, sx]
+    if want_acc:
+        out.append(acc)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def gemv_w4a8_group32(wq, s16, bias, qx, sx, y=None, acc_g=None, r=0, lanes_per_row=0,
+                      stream=None):
+    """Group-32 W4A8: y = sx * sum_g s_g acc_g + b.  ``acc_g=True`` also
+    returns the int32 per-group partials [N, K/32]."""
+    N, K = _wshape(wq, None)
+    _dev(wq, "wq", _WORD, N * K // 8)
+    _dev(s16, "s16", (torch.float16,), N * (K // 32))
+    _opt(bias, "bias", _F32, N)
+    _dev(qx, "qx", (torch.int8,), K)
+    _dev(sx, "sx", _F32)
+    y = _empty((N,), torch.float32, wq) if y is None else _dev(y, "y", _F32, N)
+    accg = _empty((N, K // 32), torch.int32, wq) if acc_g is True else None
+    _call("gemv_w4a8_group32", wq.data_ptr(), s16.data_ptr(), _ptr(bias), qx.data_ptr(),
+          sx.data_ptr(), y.data_ptr(), _ptr(accg), N, K, r, lanes_per_row, _stream(stream))
+    return (y, accg) if accg is not None else y
+
+
+def linear_w4a8_group32(wq, s16, bias, x, y=None, want_q=False, want_acc=False, r=0,
+                        lanes_per_row=0, stream=None):
+    N, K = _wshape(wq, None)
+    _dev(wq, "wq", _WORD, N * K // 8)
+    _dev(s16, "s16", (torch.float16,), N * (K // 32))
+    _opt(bias, "bias", _F32, N)
+    _dev(x, "x", _X, K)
+    y = _empty((N,), torch.float32, wq) if y is None else _dev(y, "y", _F32, N)
+    qx = _empty((K,), torch.int8, wq) if want_q else None
+    sx = _empty((1,), torch.float32, wq) if want_q else None
+    accg = _empty((N, K // 32), torch.int32, wq) if want_acc else None
+    _call("linear_w4a8_group32", wq.data_ptr(), s16.data_ptr(), _ptr(bias), x.data_ptr(),
+          _xdtype(x), y.data_ptr(), _ptr(qx), _ptr(sx), _ptr(accg), N, K, r, lanes_per_row,
+          _stream(stream))
+    out = [y]
+    if want_q:
+        out += [qx, sx]
+    if want_acc:
+        out.append(accg)
+    return out[0] if len(out) == 1 else tuple(out)
+
+
+def gemv_w8a16_group32(w8, s16, x16, y=None, r=0, lanes_per_row=0, stream=None):
+    """int8 codes [N, K] x fp16 group-32 scales against fp16 x [K] -> fp32 y [N]."""
+    N, K = w8.shape
+    _dev(w8, "w8", (torch.int8,), N * K)
+    _dev(s16, "s16", (torch.float16,), N * (K // 32))
+    _dev(x16, "x16", (torch.float16,), K)
+    y = _empty((N,), torch.float32, w8) if y is None else _dev(y, "y", _F32, N)
+    _call("gemv_w8a16_group32", w8.data_ptr(), s16.data_ptr(), x16.data_ptr(), y.data_ptr(), N, K,
+          r, lanes_per_row, _stream(stream))
+    return y
+
+
+def gemm_w4a8_verify(wq, sw, bias, qx, sx, y=None, acc=None, impl=0, stream=None):
+    """M tokens: qx int8 [M, K], sx fp32 [M] -> y fp32 [M, N] (and acc [M, N])."""
+    N, K = _wshape(wq, None)
+    M = qx.shape[0]
+    _dev(wq, "wq", _WORD, N * K // 8)
+    _dev(sw, "sw", _F32, N)
+    _opt(bias, "bias", _F32, N)
+    _dev(qx, "qx", (torch.int8,), M * K)
+    _dev(sx, "sx", _F32, M)
+    y = _empty((M, N), torch.float32, wq) if y is None else _dev(y, "y", _F32, M * N)
+    acc_t = _empty((M, N), torch.int32, wq) if acc is True else None
+    _call("gemm_w4a8_verify", wq.data_ptr(), sw.data_ptr(), _ptr(bias), qx.data_ptr(),
+          sx.data_ptr(), y.data_ptr(), _ptr(acc_t), M, N, K, impl, _stream(stream))
+    return (y, acc_t) if acc_t is not None else y
+
+
+def make_linear(wq, scales, bias=None, r=0, lanes_per_row=0) -> LinearW4A8:
+    """Descriptor of one linear for layer_w4a8_forward (keeps no references:
+    the caller keeps the tensors alive)."""
+    N, K = _wshape(wq, None)
+    _dev(wq, "wq", _WORD, N * K // 8)
+    if scales.dtype == torch.float32:
+        _dev(scales, "scales", _F32, N)
+        kind = BQD_SCALE_ROW_F32
+    else:
+        _dev(scales, "scales", (torch.float16,), N * (K // 32))
+        kind = BQD_SCALE_GROUP32_F16
+    _opt(bias, "bias", _F32, N)
+    return LinearW4A8(wq.data_ptr(), scales.data_ptr(), _ptr(bias), N, K, kind, r, lanes_per_row)
+
+
+class LayerPlan:
+    """Host-side arrays for layer_w4a8_forward, built once and replayed."""
+
+    def __init__(self, linears: Sequence[LinearW4A8], xs: Sequence[torch.Tensor],
+                 ys: Sequence[torch.Tensor]):
+        n = len(linears)
+        if not (len(xs) == len(ys) == n):
+            raise ValueError("one x and one y per linear")
+        dt = xs[0].dtype if n else torch.float32
+        for i, (l, x, y) in enumerate(zip(linears, xs, ys)):
+            _dev(x, f"x[{i}]", (dt,), l.K)
+            _dev(y, f"y[{i}]", _F32, l.N)
+        self.n = n
+        self.x_dtype = BQD_F32 if dt == torch.float32 else BQD_F16
+        self.lin = (LinearW4A8 * max(n, 1))(*linears)
+        self.xp = (C.c_void_p * max(n, 1))(*[x.data_ptr() for x in xs])
+        self.yp = (C.c_void_p * max(n, 1))(*[y.data_ptr() for y in ys])
+        self._keep = (list(xs), list(ys))
+
+    def run(self, stream=None):
+        _call("layer_w4a8_forward", self.lin, self.n, C.cast(self.xp, C.c_void_p), self.x_dtype,
+              C.cast(self.yp, C.c_void_p), _stream(stream))
+
+
+def layer_w4a8_forward(linears: Sequence[LinearW4A8], xs: Sequence[torch.Tensor],
+                       ys: Sequence[torch.Tensor], stream=None) -> None:
+    """Run the linears of one layer in order (one fused launch each)."""
+    LayerPlan(linears, xs, ys).run(stream)

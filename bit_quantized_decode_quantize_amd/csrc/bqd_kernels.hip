@@ -1,0 +1,1359 @@
+// bqd_kernels.hip -- gfx950 kernels and C ABI of libbqd.so (see include/bqd.h).
+//
+// Pages cited by title and section:
+//   [Orin]   "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
+//   [Ascend] "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录"
+//
+// Design (CDNA4, wave64):
+//   * Weights stream once from HBM as 16-byte chunks (32 INT4 codes).  A row
+//     is split over L lanes (16/32/64); a "lane group" of L lanes owns r rows
+//     and keeps r int32 accumulators per lane, so every activation chunk read
+//     from LDS feeds r rows ([Orin] "o2-all 和 o4-all 为什么能加速").
+//   * The INT8 activation is staged once per workgroup in LDS in a permuted
+//     order: for each group of 8 codes, word A = codes {0,2,4,6}, word B =
+//     codes {1,3,5,7}.  A packed weight word w then meets the activation
+//     through two v_dot4_i32_i8:  (w << 4) & 0xF0F0F0F0 holds 16*q{0,2,4,6}
+//     as signed bytes and w & 0xF0F0F0F0 holds 16*q{1,3,5,7}, so
+//       sdot4(lo16(w), A) + sdot4(hi16(w), B) = 16 * sum_k q_k x_k
+//     exactly, with three bit operations per word and no sign-extension
+//     ([Orin] "DP4A 做了什么" splits the word into two int8x4 for two DP4A).
+//     Each lane divides its partial by 16 (exact) before the cross-lane sum.
+//   * Cross-lane sums use DPP row rotations inside each 16-lane row, then
+//     lane shuffles across rows; the fp32 epilogue is fused.
+//   * Activation quantisation ([Orin] derivation section) is either its own
+//     kernel or folded into the GEMV prologue (each workgroup recomputes
+//     max|x|, the fp32 scale and the RNE codes; correctly rounded fp32
+//     division, so every workgroup's codes are identical).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "bqd.h"
+
+namespace {
+
+constexpr int kThreads = 256;          // 4 waves per workgroup
+constexpr int kWave = 64;
+constexpr int kLdsBytes = 65536;       // activation staging limit per workgroup
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------------
+// Bit helpers
+// ------------------------------------------------------------------------
+
+// Signed INT4 codes {0,2,4,6} of w, each times 16, as four signed bytes.
+__device__ __forceinline__ int lo16(uint32_t w) { return (int)((w << 4) & 0xF0F0F0F0u); }
+// Signed INT4 codes {1,3,5,7} of w, each times 16, as four signed bytes.
+__device__ __forceinline__ int hi16(uint32_t w) { return (int)(w & 0xF0F0F0F0u); }
+
+// Activation bytes b0..b7 (lo = b0..b3, hi = b4..b7) -> A = [b0 b2 b4 b6].
+__device__ __forceinline__ uint32_t perm_even(uint32_t lo, uint32_t hi)
+{
+    return (lo & 0xFFu) | ((lo >> 8) & 0xFF00u) | ((hi & 0xFFu) << 16) | ((hi << 8) & 0xFF000000u);
+}
+// -> B = [b1 b3 b5 b7].
+__device__ __forceinline__ uint32_t perm_odd(uint32_t lo, uint32_t hi)
+{
+    return ((lo >> 8) & 0xFFu) | ((lo >> 16) & 0xFF00u) | ((hi << 8) & 0xFF0000u) | (hi & 0xFF000000u);
+}
+
+// 16 x (sum over the 32 codes of one chunk of w times the staged activation).
+// xa = [A0 B0 A1 B1], xb = [A2 B2 A3 B3] of the chunk's four 8-code groups.
+__device__ __forceinline__ int dot_chunk16(u32x4 w, u32x4 xa, u32x4 xb, int acc)
+{
+    acc = __builtin_amdgcn_sdot4(lo16(w.x), (int)xa.x, acc, false);
+    acc = __builtin_amdgcn_sdot4(hi16(w.x), (int)xa.y, acc, false);
+    acc = __builtin_amdgcn_sdot4(lo16(w.y), (int)xa.z, acc, false);
+    acc = __builtin_amdgcn_sdot4(hi16(w.y), (int)xa.w, acc, false);
+    acc = __builtin_amdgcn_sdot4(lo16(w.z), (int)xb.x, acc, false);
+    acc = __builtin_amdgcn_sdot4(hi16(w.z), (int)xb.y, acc, false);
+    acc = __builtin_amdgcn_sdot4(lo16(w.w), (int)xb.z, acc, false);
+    acc = __builtin_amdgcn_sdot4(hi16(w.w), (int)xb.w, acc, false);
+    return acc;
+}
+
+// ------------------------------------------------------------------------
+// Cross-lane reductions
+// ------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over L consecutive lanes (L = 16, 32, 64); every lane gets the sum.
+// Inside a 16-lane DPP row: rotations by 8, 4, 2, 1 (row_ror); across rows:
+// lane shuffles.  Integer sums are exact, so the order is immaterial.
+template <int L>
+__device__ __forceinline__ int sum_lanes(int v)
+{
+    v += dpp_i<0x128>(v);
+    v += dpp_i<0x124>(v);
+    v += dpp_i<0x122>(v);
+    v += dpp_i<0x121>(v);
+    if (L >= 32) v += __shfl_xor(v, 16);
+    if (L >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+template <int L>
+__device__ __forceinline__ float sum_lanes_f(float v)
+{
+    v += dpp_f<0x128>(v);
+    v += dpp_f<0x124>(v);
+    v += dpp_f<0x122>(v);
+    v += dpp_f<0x121>(v);
+    if (L >= 32) v += __shfl_xor(v, 16);
+    if (L >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1)
+        v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+// Max over the workgroup (every thread gets it).  red: 4 floats of LDS.
+__device__ __forceinline__ float block_max(float v, float* red)
+{
+    v = wave_max(v);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return m;
+}
+
+// ------------------------------------------------------------------------
+// Activation input: 8 consecutive values of x as fp32 (fp16 widens exactly)
+// ------------------------------------------------------------------------
+enum XIn { X_Q8 = 0, X_F32 = 1, X_F16 = 2 };
+
+template <int XIN>
+__device__ __forceinline__ void load8(const void* x, int g, float v[8])
+{
+    if constexpr (XIN == X_F32) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(x) + 2 * g;
+        f32x4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        u32x4 h = reinterpret_cast<const u32x4*>(x)[g];
+        uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[k] & 0xFFFFu));
+            v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[k] >> 16));
+        }
+    }
+}
+
+// Activation scale s = max|x| / 127 (correctly rounded fp32 division) with
+// what the code computation needs.  [Orin] derivation section.
+struct ActScale {
+    float s;    // s^x
+    float inv;  // fl(1 / s), valid when fast
+    bool fast;  // s is a normal number: the reciprocal route below applies
+};
+
+__device__ __forceinline__ ActScale act_scale(float amax)
+{
+    ActScale a;
+    a.s = amax / 127.0f;
+    a.fast = a.s >= 0x1p-126f;
+    a.inv = a.fast ? 1.0f / a.s : 0.0f;
+    return a;
+}
+
+// clip(round_half_even(fl(v / s)), -127, 127), bit-identical to the correctly
+// rounded fp32 division followed by RNE; 0 when s == 0.
+// Route: r = v * fl(1/s) is within 2^-16 of v/s (|v/s| <= 127 * (1 + 2^-23),
+// two roundings of relative size 2^-24 each), and fl(v/s) within 2^-17 of
+// v/s, so whenever r is more than 2^-15 away from a half-integer, rint(r)
+// and rint(fl(v/s)) agree.  Only closer to a tie is the exact quotient taken.
+// r - rint(r) is exact (Sterbenz), so the test itself does not round.
+__device__ __forceinline__ uint32_t act_code(float v, const ActScale& a)
+{
+    float m;
+    if (a.fast) {
+        const float r = v * a.inv;
+        m = rintf(r);
+        if (fabsf(r - m) > 0.5f - 0x1p-15f)
+            m = rintf(v / a.s);
+    } else {
+        if (a.s == 0.0f)
+            return 0u;
+        m = rintf(v / a.s);
+    }
+    m = fminf(fmaxf(m, -127.0f), 127.0f);
+    return (uint32_t)((int)m) & 0xFFu;
+}
+
+// Quantise 8 values into bytes lo = codes 0..3, hi = codes 4..7.
+__device__ __forceinline__ void quant8(const float v[8], const ActScale& a, uint32_t& lo, uint32_t& hi)
+{
+    lo = act_code(v[0], a) | (act_code(v[1], a) << 8) | (act_code(v[2], a) << 16) | (act_code(v[3], a) << 24);
+    hi = act_code(v[4], a) | (act_code(v[5], a) << 8) | (act_code(v[6], a) << 16) | (act_code(v[7], a) << 24);
+}
+
+// Stage G8 = K/8 groups of INT8 codes into LDS (permuted), from int8 memory.
+__device__ __forceinline__ void stage_q8(u32x2* xs, const int8_t* qx, int G8)
+{
+    const u32x2* q = reinterpret_cast<const u32x2*>(qx);
+    for (int g = threadIdx.x; g < G8; g += kThreads) {
+        u32x2 v = q[g];
+        xs[g] = u32x2{perm_even(v.x, v.y), perm_odd(v.x, v.y)};
+    }
+}
+
+// Quantise x (fp32/fp16, [K]) in the workgroup and stage the codes into LDS.
+// Returns s^x.  Workgroup 0 optionally writes the codes and scale out.
+template <int XIN>
+__device__ float stage_quant(u32x2* xs, const void* x, int G8, float* red, int8_t* qx_out,
+                             float* sx_out)
+{
+    float amax = 0.0f;
+    for (int g = threadIdx.x; g < G8; g += kThreads) {
+        float v[8];
+        load8<XIN>(x, g, v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            amax = fmaxf(amax, fabsf(v[k]));
+    }
+    amax = block_max(amax, red);
+    const ActScale a = act_scale(amax);
+    const float s = a.s;
+    const bool out = (qx_out != nullptr) && blockIdx.x == 0;
+    for (int g = threadIdx.x; g < G8; g += kThreads) {
+        float v[8];
+        load8<XIN>(x, g, v);
+        uint32_t lo, hi;
+        quant8(v, a, lo, hi);
+        xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+        if (out)
+            reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+    }
+    if (sx_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *sx_out = s;
+    return s;
+}
+
+// ------------------------------------------------------------------------
+// Load-time weight quantisation
+// ------------------------------------------------------------------------
+
+// One wave per row: s = max|W_row| / 7, codes clip(rne(W/s), -8, 7), packed.
+__global__ __launch_bounds__(kThreads) void k_quantize_weights_int4_rowwise(
+    const float* __restrict__ W, int N, int K, uint32_t* __restrict__ wq, float* __restrict__ sw)
+{
+    const int row = blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (row >= N)
+        return;  // whole wave exits together: no cross-wave sync below
+    const float* w = W + (size_t)row * K;
+    const int G8 = K / 8;
+    float amax = 0.0f;
+    for (int g = lane; g < G8; g += kWave) {
+        float v[8];
+        load8<X_F32>(w, g, v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            amax = fmaxf(amax, fabsf(v[k]));
+    }
+    amax = wave_max(amax);
+    const float s = amax / 7.0f;
+    if (lane == 0)
+        sw[row] = s;
+    uint32_t* out = wq + (size_t)row * G8;
+    for (int g = lane; g < G8; g += kWave) {
+        float v[8];
+        load8<X_F32>(w, g, v);
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            int q = 0;
+            if (s != 0.0f)
+                q = (int)fminf(fmaxf(rintf(v[k] / s), -8.0f), 7.0f);
+            word |= ((uint32_t)q & 0xFu) << (4 * k);
+        }
+        out[g] = word;
+    }
+}
+
+// One thread per block of 32 weights: fp16 scale fp16(max|W_block| / D),
+// codes against the stored fp16 value.  INT4 (packed) or INT8 output.
+template <bool INT8>
+__global__ __launch_bounds__(kThreads) void k_quantize_weights_group32(
+    const float* __restrict__ W, int N, int K, void* __restrict__ out, uint16_t* __restrict__ s16)
+{
+    const int G = K / 32;
+    const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= (long long)N * G)
+        return;
+    const int row = (int)(idx / G), g = (int)(idx % G);
+    const float* w = W + (size_t)row * K + (size_t)g * 32;
+    float v[32];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        load8<X_F32>(w, t, v + 8 * t);
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+        amax = fmaxf(amax, fabsf(v[k]));
+    const float D = INT8 ? 31.0f : 7.0f;
+    const float lo = INT8 ? -32.0f : -8.0f, hi = INT8 ? 31.0f : 7.0f;
+    const _Float16 h = (_Float16)(amax / D);
+    s16[(size_t)row * G + g] = __builtin_bit_cast(uint16_t, h);
+    const float s = (float)h;
+    int q[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+        q[k] = (s != 0.0f) ? (int)fminf(fmaxf(rintf(v[k] / s), lo), hi) : 0;
+    if constexpr (INT8) {
+        u32x4* o = reinterpret_cast<u32x4*>(reinterpret_cast<int8_t*>(out) + (size_t)row * K + (size_t)g * 32);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            uint32_t wv[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int b = 16 * t + 4 * d;
+                wv[d] = ((uint32_t)q[b] & 0xFFu) | (((uint32_t)q[b + 1] & 0xFFu) << 8) |
+                        (((uint32_t)q[b + 2] & 0xFFu) << 16) | (((uint32_t)q[b + 3] & 0xFFu) << 24);
+            }
+            o[t] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        }
+    } else {
+        uint32_t wv[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                word |= ((uint32_t)q[8 * d + k] & 0xFu) << (4 * k);
+            wv[d] = word;
+        }
+        reinterpret_cast<u32x4*>(reinterpret_cast<uint32_t*>(out) + (size_t)row * (K / 8))[g] =
+            u32x4{wv[0], wv[1], wv[2], wv[3]};
+    }
+}
+
+// ------------------------------------------------------------------------
+// Activation quantisation: one workgroup per token row.
+// ------------------------------------------------------------------------
+template <int XIN>
+__global__ __launch_bounds__(kThreads) void k_quantize_act(const void* __restrict__ x, int K,
+                                                           int8_t* __restrict__ qx, float* __restrict__ sx)
+{
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    const int G8 = K / 8;
+    const size_t esz = XIN == X_F32 ? 4 : 2;
+    const void* xr = reinterpret_cast<const char*>(x) + (size_t)m * K * esz;
+    float amax = 0.0f;
+    for (int g = threadIdx.x; g < G8; g += kThreads) {
+        float v[8];
+        load8<XIN>(xr, g, v);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            amax = fmaxf(amax, fabsf(v[k]));
+    }
+    amax = block_max(amax, red);
+    const ActScale a = act_scale(amax);
+    u32x2* q = reinterpret_cast<u32x2*>(qx + (size_t)m * K);
+    for (int g = threadIdx.x; g < G8; g += kThreads) {
+        float v[8];
+        load8<XIN>(xr, g, v);
+        uint32_t lo, hi;
+        quant8(v, a, lo, hi);
+        q[g] = u32x2{lo, hi};
+    }
+    if (threadIdx.x == 0)
+        sx[m] = a.s;
+}
+
+// ------------------------------------------------------------------------
+// W4A8 GEMV, per-row scales.
+//   R: rows per lane group; L: lanes per row; U: chunk iterations per
+//   pipeline step; XIN: activation input form.
+//   Workgroup tile = (256/L) lane groups x R rows; workgroups walk tiles in a
+//   grid-stride loop.  Each lane streams its rows in steps of U chunks
+//   (R*U 16-byte loads); step s+1 (possibly of the next tile) is loaded while
+//   step s is computed, and the first step is issued before the activation
+//   prologue so that its latency overlaps the staging.  Rows past N read
+//   row N-1 (in bounds) and are never written.
+// ------------------------------------------------------------------------
+template <int R, int L, int U>
+__device__ __forceinline__ void load_step(u32x4 (&buf)[U][R], const u32x4* __restrict__ wq, int N,
+                                          int C, int row0, int step, int lane)
+{
+    const u32x4* wrow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        wrow[r] = wq + (size_t)min(row0 + r, N - 1) * C;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (step * U + u) * L + lane;
+        const bool ok = c < C;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            buf[u][r] = ok ? wrow[r][c] : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int R, int L, int U>
+__device__ __forceinline__ void load_scales(uint16_t (&buf)[U][R], const uint16_t* __restrict__ s16,
+                                            int N, int C, int row0, int step, int lane)
+{
+    const uint16_t* srow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        srow[r] = s16 + (size_t)min(row0 + r, N - 1) * C;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (step * U + u) * L + lane;
+        const bool ok = c < C;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            buf[u][r] = ok ? srow[r][c] : (uint16_t)0;
+    }
+}
+
+template <int XIN>
+__device__ __forceinline__ float stage_activation(u32x4* xs, const void* xin, const float* sx_in, int C,
+                                                  float* red, int8_t* qx_out, float* sx_out)
+{
+    if constexpr (XIN == X_Q8) {
+        stage_q8(reinterpret_cast<u32x2*>(xs), reinterpret_cast<const int8_t*>(xin), 4 * C);
+        return *sx_in;
+    } else {
+        return stage_quant<XIN>(reinterpret_cast<u32x2*>(xs), xin, 4 * C, red, qx_out, sx_out);
+    }
+}
+
+template <int R, int L, int U, int XIN>
+__global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
+    const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
+    const void* __restrict__ xin, const float* __restrict__ sx_in, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out, float* __restrict__ sx_out, int N,
+    int C)
+{
+    extern __shared__ u32x4 xs[];  // 2*C chunks' activation = K bytes
+    __shared__ float red[4];
+    constexpr int GROUPS = kThreads / L;
+    constexpr int ROWS = GROUPS * R;
+    const int lane = threadIdx.x % L;
+    const int grp = threadIdx.x / L;
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int iters = (C + L - 1) / L;
+    const int steps = (iters + U - 1) / U;
+
+    int tile = blockIdx.x;
+    u32x4 cur[U][R];
+    load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+    const float sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out);
+    __syncthreads();
+
+    for (; tile < tiles; tile += gridDim.x) {
+        const int row0 = tile * ROWS + grp * R;
+        int acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = 0;
+        for (int st = 0; st < steps; ++st) {
+            u32x4 nxt[U][R];
+            int ntile = tile, nst = st + 1;
+            if (nst == steps) {
+                ntile += gridDim.x;
+                nst = 0;
+            }
+            const bool more = ntile < tiles;
+            if (more)
+                load_step<R, L, U>(nxt, wq, N, C, ntile * ROWS + grp * R, nst, lane);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (st * U + u < iters) {  // uniform across the wave
+                    const int c = min((st * U + u) * L + lane, C - 1);
+                    const u32x4 xa = xs[2 * c], xb = xs[2 * c + 1];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r] = dot_chunk16(cur[u][r], xa, xb, acc[r]);
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        cur[u][r] = nxt[u][r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = sum_lanes<L>(acc[r] >> 4);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r;
+            if (lane == r && row < N) {
+                if (acc_out)
+                    acc_out[row] = acc[r];
+                const float t = sw[row] * sx;
+                y[row] = fmaf(t, (float)acc[r], bias ? bias[row] : 0.0f);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// W4A8 GEMV, one fp16 scale per 32 codes (= per 16-byte chunk).
+//   y = sx * sum_g s_g * acc_g + b; acc_g exact int32, the scaled sum fp32.
+//   Same pipeline as k_gemv_w4a8, with each chunk's scale loaded beside it.
+// ------------------------------------------------------------------------
+template <int R, int L, int U, int XIN>
+__global__ __launch_bounds__(kThreads) void k_gemv_w4a8_g32(
+    const u32x4* __restrict__ wq, const uint16_t* __restrict__ s16, const float* __restrict__ bias,
+    const void* __restrict__ xin, const float* __restrict__ sx_in, float* __restrict__ y,
+    int32_t* __restrict__ accg_out, int8_t* __restrict__ qx_out, float* __restrict__ sx_out, int N,
+    int C)
+{
+    extern __shared__ u32x4 xs[];
+    __shared__ float red[4];
+    constexpr int GROUPS = kThreads / L;
+    constexpr int ROWS = GROUPS * R;
+    const int lane = threadIdx.x % L;
+    const int grp = threadIdx.x / L;
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int iters = (C + L - 1) / L;
+    const int steps = (iters + U - 1) / U;
+
+    int tile = blockIdx.x;
+    u32x4 cur[U][R];
+    uint16_t scur[U][R];
+    load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+    load_scales<R, L, U>(scur, s16, N, C, tile * ROWS + grp * R, 0, lane);
+    const float sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out);
+    __syncthreads();
+
+    for (; tile < tiles; tile += gridDim.x) {
+        const int row0 = tile * ROWS + grp * R;
+        float facc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = 0.0f;
+        for (int st = 0; st < steps; ++st) {
+            u32x4 nxt[U][R];
+            uint16_t snxt[U][R];
+            int ntile = tile, nst = st + 1;
+            if (nst == steps) {
+                ntile += gridDim.x;
+                nst = 0;
+            }
+            const bool more = ntile < tiles;
+            if (more) {
+                load_step<R, L, U>(nxt, wq, N, C, ntile * ROWS + grp * R, nst, lane);
+                load_scales<R, L, U>(snxt, s16, N, C, ntile * ROWS + grp * R, nst, lane);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (st * U + u < iters) {
+                    const int c = (st * U + u) * L + lane;
+                    const int cc = min(c, C - 1);
+                    const u32x4 xa = xs[2 * cc], xb = xs[2 * cc + 1];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const int ag = dot_chunk16(cur[u][r], xa, xb, 0) >> 4;
+                        const float sg = (float)__builtin_bit_cast(_Float16, scur[u][r]);
+                        facc[r] = fmaf((float)ag, sg, facc[r]);
+                        if (accg_out != nullptr && c < C && row0 + r < N)
+                            accg_out[(size_t)(row0 + r) * C + c] = ag;
+                    }
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        cur[u][r] = nxt[u][r];
+                        scur[u][r] = snxt[u][r];
+                    }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = sum_lanes_f<L>(facc[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r;
+            if (lane == r && row < N)
+                y[row] = fmaf(sx, facc[r], bias ? bias[row] : 0.0f);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// W8A16 GEMV (int8 codes, fp16 group-32 scales, fp16 activation).
+//   A lane handles whole 32-code groups (two 16-byte chunks).  Each byte
+//   code q in [-32, 31] becomes an exact fp16 by the magic-number route:
+//   u = (q ^ 32) & 63 = q + 32, fp16 bits 0x6400 | u = 1024 + u, minus 1056.
+//   Pairs then go through v_dot2_f32_f16 against the staged fp16 x.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ float dot4_w8_f16(uint32_t w, uint32_t x01, uint32_t x23, float acc)
+{
+    const uint32_t u = (w ^ 0x20202020u) & 0x3F3F3F3Fu;
+    const uint32_t h01 = (u & 0xFFu) | ((u & 0xFF00u) << 8) | 0x64006400u;
+    const uint32_t h23 = ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u;
+    const h16x2 bias = {(_Float16)1056.0f, (_Float16)1056.0f};
+    const h16x2 q01 = __builtin_bit_cast(h16x2, h01) - bias;
+    const h16x2 q23 = __builtin_bit_cast(h16x2, h23) - bias;
+    acc = __builtin_amdgcn_fdot2(q01, __builtin_bit_cast(h16x2, x01), acc, false);
+    acc = __builtin_amdgcn_fdot2(q23, __builtin_bit_cast(h16x2, x23), acc, false);
+    return acc;
+}
+
+template <int R, int L>
+__global__ __launch_bounds__(kThreads) void k_gemv_w8a16_g32(
+    const u32x4* __restrict__ w8, const uint16_t* __restrict__ s16, const u32x4* __restrict__ x16,
+    float* __restrict__ y, int N, int G)
+{
+    extern __shared__ u32x4 xs[];  // 4 chunks (32 fp16) per group
+    for (int i = threadIdx.x; i < 4 * G; i += kThreads)
+        xs[i] = x16[i];
+    __syncthreads();
+
+    constexpr int GROUPS = kThreads / L;
+    constexpr int ROWS = GROUPS * R;
+    constexpr int U = 2;
+    const int lane = threadIdx.x % L;
+    const int grp = threadIdx.x / L;
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int iters = (G + L - 1) / L;
+
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int row0 = tile * ROWS + grp * R;
+        const u32x4* wrow[R];
+        const uint16_t* srow[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const size_t rr = (size_t)min(row0 + r, N - 1);
+            wrow[r] = w8 + rr * (2 * (size_t)G);
+            srow[r] = s16 + rr * G;
+        }
+        float facc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = 0.0f;
+        for (int it = 0; it < iters; it += U) {
+            u32x4 w[U][R][2];
+            uint16_t sc[U][R];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int g = (it + u) * L + lane;
+                const bool ok = (it + u < iters) && (g < G);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    w[u][r][0] = ok ? wrow[r][2 * g] : u32x4{0u, 0u, 0u, 0u};
+                    w[u][r][1] = ok ? wrow[r][2 * g + 1] : u32x4{0u, 0u, 0u, 0u};
+                    sc[u][r] = ok ? srow[r][g] : (uint16_t)0;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int g = min((it + u) * L + lane, G - 1);
+                const u32x4 x0 = xs[4 * g], x1 = xs[4 * g + 1], x2 = xs[4 * g + 2], x3 = xs[4 * g + 3];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const u32x4 a = w[u][r][0], b = w[u][r][1];
+                    float p = 0.0f;
+                    p = dot4_w8_f16(a.x, x0.x, x0.y, p);
+                    p = dot4_w8_f16(a.y, x0.z, x0.w, p);
+                    p = dot4_w8_f16(a.z, x1.x, x1.y, p);
+                    p = dot4_w8_f16(a.w, x1.z, x1.w, p);
+                    p = dot4_w8_f16(b.x, x2.x, x2.y, p);
+                    p = dot4_w8_f16(b.y, x2.z, x2.w, p);
+                    p = dot4_w8_f16(b.z, x3.x, x3.y, p);
+                    p = dot4_w8_f16(b.w, x3.z, x3.w, p);
+                    facc[r] = fmaf((float)__builtin_bit_cast(_Float16, sc[u][r]), p, facc[r]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = sum_lanes_f<L>(facc[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r;
+            if (lane == r && row < N)
+                y[row] = facc[r];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// M-token verify GEMM, integer dot products.  MT >= M tokens are staged in
+// LDS per K-segment (padding tokens are zero); each weight chunk is loaded
+// and split once and meets all MT tokens.
+// ------------------------------------------------------------------------
+template <int MT, int R, int L>
+__global__ __launch_bounds__(kThreads) void k_verify_w4a8(
+    const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int M, int N, int C, int SEGC)
+{
+    extern __shared__ u32x4 xs[];  // [MT][SEGC][2] chunks
+    constexpr int GROUPS = kThreads / L;
+    constexpr int ROWS = GROUPS * R;
+    const int lane = threadIdx.x % L;
+    const int grp = threadIdx.x / L;
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int K = 32 * C;
+    const bool single = SEGC >= C;
+
+    // Stage tokens' codes of chunks [c0, c0 + nc) into LDS (zeros for m >= M).
+    auto stage = [&](int c0, int nc) {
+        const int groups = 4 * nc;
+        u32x2* xs2 = reinterpret_cast<u32x2*>(xs);
+        for (int i = threadIdx.x; i < MT * groups; i += kThreads) {
+            const int m = i / groups, g = i % groups;
+            u32x2 v = {0u, 0u};
+            if (m < M)
+                v = reinterpret_cast<const u32x2*>(qx + (size_t)m * K)[4 * c0 + g];
+            xs2[(size_t)m * 4 * SEGC + g] = u32x2{perm_even(v.x, v.y), perm_odd(v.x, v.y)};
+        }
+    };
+    if (single) {
+        stage(0, C);
+        __syncthreads();
+    }
+
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int row0 = tile * ROWS + grp * R;
+        const u32x4* wrow[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            wrow[r] = wq + (size_t)min(row0 + r, N - 1) * C;
+        int acc[MT][R];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[m][r] = 0;
+
+        for (int c0 = 0; c0 < C; c0 += SEGC) {
+            const int nc = min(SEGC, C - c0);
+            if (!single) {
+                __syncthreads();
+                stage(c0, nc);
+                __syncthreads();
+            }
+            for (int cl = lane; cl < nc; cl += L) {
+                u32x4 w[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    w[r] = wrow[r][c0 + cl];
+                int lo[R][4], hi[R][4];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    lo[r][0] = lo16(w[r].x); hi[r][0] = hi16(w[r].x);
+                    lo[r][1] = lo16(w[r].y); hi[r][1] = hi16(w[r].y);
+                    lo[r][2] = lo16(w[r].z); hi[r][2] = hi16(w[r].z);
+                    lo[r][3] = lo16(w[r].w); hi[r][3] = hi16(w[r].w);
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const u32x4 xa = xs[((size_t)m * SEGC + cl) * 2];
+                    const u32x4 xb = xs[((size_t)m * SEGC + cl) * 2 + 1];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        int a = acc[m][r];
+                        a = __builtin_amdgcn_sdot4(lo[r][0], (int)xa.x, a, false);
+                        a = __builtin_amdgcn_sdot4(hi[r][0], (int)xa.y, a, false);
+                        a = __builtin_amdgcn_sdot4(lo[r][1], (int)xa.z, a, false);
+                        a = __builtin_amdgcn_sdot4(hi[r][1], (int)xa.w, a, false);
+                        a = __builtin_amdgcn_sdot4(lo[r][2], (int)xb.x, a, false);
+                        a = __builtin_amdgcn_sdot4(hi[r][2], (int)xb.y, a, false);
+                        a = __builtin_amdgcn_sdot4(lo[r][3], (int)xb.z, a, false);
+                        a = __builtin_amdgcn_sdot4(hi[r][3], (int)xb.w, a, false);
+                        acc[m][r] = a;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[m][r] = sum_lanes<L>(acc[m][r] >> 4);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r;
+            if (lane == r && row < N) {
+                const float swr = sw[row];
+                const float b = bias ? bias[row] : 0.0f;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    if (m < M) {
+                        if (acc_out)
+                            acc_out[(size_t)m * N + row] = acc[m][r];
+                        y[(size_t)m * N + row] = fmaf(swr * sx[m], (float)acc[m][r], b);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 rejected
+int g_dev_cus[kMaxDevices];
+std::mutex g_dev_mutex;
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline int current_cus()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 256;
+    return g_dev_cus[dev] > 0 ? g_dev_cus[dev] : 256;
+}
+
+inline int launched()
+{
+    return hipGetLastError() == hipSuccess ? BQD_OK : BQD_ERR_LAUNCH;
+}
+
+inline int check_k(int K, int mult = 32)
+{
+    if (K <= 0 || K % mult)
+        return BQD_ERR_SHAPE;
+    if (K > BQD_MAX_K)
+        return BQD_ERR_BOUND;
+    return BQD_OK;
+}
+
+// Launch shape of a GEMV: r rows per lane group, L lanes per row, U chunk
+// iterations per pipeline step, and the number of workgroups.
+struct GemvCfg {
+    int r, L, U, grid;
+};
+
+constexpr int kWgPerCu = 8;  // grid cap: workgroups per CU in the grid-stride loop
+
+inline int pow2ceil(int v)
+{
+    int p = 1;
+    while (p < v)
+        p <<= 1;
+    return p;
+}
+
+// Largest U for r rows: R*U 16-byte loads are double-buffered in VGPRs.
+inline int max_unroll(int r) { return r >= 8 ? 2 : (r >= 4 ? 4 : 8); }
+
+inline bool valid_config(int r, int L)
+{
+    return (r == 0 || r == 1 || r == 2 || r == 4 || r == 8) && (L == 0 || L == 16 || L == 32 || L == 64);
+}
+
+// Automatic choice where the caller passes 0.  Small matrices spread a row
+// over more lanes so that every CU gets rows; large ones use 16 lanes per
+// row and r = 4 rows per lane group.  U covers a lane's whole row when it
+// fits the register budget.
+inline GemvCfg make_cfg(int N, int C, int r, int L)
+{
+    GemvCfg c;
+    c.L = L ? L : (N >= 16384 ? 16 : (N >= 8192 ? 32 : 64));
+    c.r = r ? r : (c.L == 16 ? 4 : (c.L == 32 ? 2 : 1));
+    const int iters = (C + c.L - 1) / c.L;
+    c.U = pow2ceil(iters) < max_unroll(c.r) ? pow2ceil(iters) : max_unroll(c.r);
+    const long long rows = (long long)(kThreads / c.L) * c.r;
+    const long long tiles = (N + rows - 1) / rows;
+    const long long cap = (long long)current_cus() * kWgPerCu;
+    c.grid = (int)(tiles < cap ? tiles : cap);
+    return c;
+}
+
+inline unsigned grid_for(long long tiles)
+{
+    const long long cap = 1LL << 30;
+    return (unsigned)(tiles < cap ? tiles : cap);
+}
+
+// Every (R, L, U) instance: R*U <= 16 loads per step.
+#define BQD_FOR_CFGS_L(X, LL)                                                                     \
+    X(1, LL, 1) X(1, LL, 2) X(1, LL, 4) X(1, LL, 8) X(2, LL, 1) X(2, LL, 2) X(2, LL, 4) X(2, LL, 8) \
+    X(4, LL, 1) X(4, LL, 2) X(4, LL, 4) X(8, LL, 1) X(8, LL, 2)
+#define BQD_FOR_CFGS(X) BQD_FOR_CFGS_L(X, 16) BQD_FOR_CFGS_L(X, 32) BQD_FOR_CFGS_L(X, 64)
+
+template <int XIN>
+int launch_gemv_rowwise(const uint32_t* wq, const float* sw, const float* bias, const void* xin,
+                        const float* sx, float* y, int32_t* acc, int8_t* qx_out, float* sx_out,
+                        int N, int K, const GemvCfg& c, hipStream_t st)
+{
+    const int C = K / 32;
+    const dim3 grid(c.grid), block(kThreads);
+    const size_t lds = (size_t)K;
+    const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+#define BQD_GEMV_CASE(RR, LL, UU)                                                                \
+    if (c.r == RR && c.L == LL && c.U == UU) {                                                   \
+        hipLaunchKernelGGL((k_gemv_w4a8<RR, LL, UU, XIN>), grid, block, lds, st, w, sw, bias, xin, \
+                           sx, y, acc, qx_out, sx_out, N, C);                                    \
+        return launched();                                                                       \
+    }
+    BQD_FOR_CFGS(BQD_GEMV_CASE)
+#undef BQD_GEMV_CASE
+    return BQD_ERR_CONFIG;
+}
+
+template <int XIN>
+int launch_gemv_group32(const uint32_t* wq, const uint16_t* s16, const float* bias, const void* xin,
+                        const float* sx, float* y, int32_t* accg, int8_t* qx_out, float* sx_out,
+                        int N, int K, const GemvCfg& c, hipStream_t st)
+{
+    const int C = K / 32;
+    const dim3 grid(c.grid), block(kThreads);
+    const size_t lds = (size_t)K;
+    const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+#define BQD_G32_CASE(RR, LL, UU)                                                                    \
+    if (c.r == RR && c.L == LL && c.U == UU) {                                                      \
+        hipLaunchKernelGGL((k_gemv_w4a8_g32<RR, LL, UU, XIN>), grid, block, lds, st, w, s16, bias,    \
+                           xin, sx, y, accg, qx_out, sx_out, N, C);                                 \
+        return launched();                                                                          \
+    }
+    BQD_FOR_CFGS(BQD_G32_CASE)
+#undef BQD_G32_CASE
+    return BQD_ERR_CONFIG;
+}
+
+int check_x_dtype(int d) { return (d == BQD_F32 || d == BQD_F16) ? BQD_OK : BQD_ERR_DTYPE; }
+
+}  // namespace
+
+// ==========================================================================
+// C ABI
+// ==========================================================================
+extern "C" {
+
+int bqd_abi_version(void) { return BQD_ABI_VERSION; }
+
+const char* bqd_status_string(int status)
+{
+    switch (status) {
+    case BQD_OK: return "ok";
+    case BQD_ERR_NULL: return "a required pointer is NULL";
+    case BQD_ERR_SHAPE: return "bad shape: N/M < 0, K <= 0 or K not a multiple of 32, or bad count";
+    case BQD_ERR_ALIGN: return "a pointer is not aligned as required";
+    case BQD_ERR_BOUND: return "K above BQD_MAX_K or token count above BQD_MAX_TOKENS";
+    case BQD_ERR_DTYPE: return "unknown dtype or scale kind";
+    case BQD_ERR_CONFIG: return "unsupported r / lanes_per_row";
+    case BQD_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case BQD_ERR_DEVICE: return "no HIP device, or the current device is not a gfx950";
+    default: return "unknown status";
+    }
+}
+
+int bqd_init(void)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return BQD_ERR_DEVICE;
+    int s = g_dev_state[dev].load(std::memory_order_acquire);
+    if (s == 1)
+        return BQD_OK;
+    if (s == -1)
+        return BQD_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+            s = -1;
+        } else {
+            s = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+            g_dev_cus[dev] = p.multiProcessorCount;
+        }
+        g_dev_state[dev].store(s, std::memory_order_release);
+    }
+    return s == 1 ? BQD_OK : BQD_ERR_DEVICE;
+}
+
+int quantize_weights_int4_rowwise(const float* W, int32_t N, int32_t K, uint32_t* wq, float* sw,
+                                  void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (N == 0)
+        return BQD_OK;
+    if (!W || !wq || !sw)
+        return BQD_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(wq, 16) || !aligned(sw, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    const int rows_per_block = kThreads / kWave;
+    hipLaunchKernelGGL(k_quantize_weights_int4_rowwise, dim3((N + rows_per_block - 1) / rows_per_block),
+                       dim3(kThreads), 0, (hipStream_t)stream, W, N, K, wq, sw);
+    return launched();
+}
+
+static int quantize_group32_common(bool int8, const float* W, int32_t N, int32_t K, void* out,
+                                   uint16_t* s16, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (N == 0)
+        return BQD_OK;
+    if (!W || !out || !s16)
+        return BQD_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(out, 16) || !aligned(s16, 2))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    const long long n = (long long)N * (K / 32);
+    const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+    if (int8)
+        hipLaunchKernelGGL(k_quantize_weights_group32<true>, grid, dim3(kThreads), 0, (hipStream_t)stream,
+                           W, N, K, out, s16);
+    else
+        hipLaunchKernelGGL(k_quantize_weights_group32<false>, grid, dim3(kThreads), 0, (hipStream_t)stream,
+                           W, N, K, out, s16);
+    return launched();
+}
+
+int quantize_weights_int4_group32(const float* W, int32_t N, int32_t K, uint32_t* wq, uint16_t* s16,
+                                  void* stream)
+{
+    return quantize_group32_common(false, W, N, K, wq, s16, stream);
+}
+
+int quantize_weights_int8_group32(const float* W, int32_t N, int32_t K, int8_t* w8, uint16_t* s16,
+                                  void* stream)
+{
+    return quantize_group32_common(true, W, N, K, w8, s16, stream);
+}
+
+int pack_int4_rows_host(const int8_t* q, int32_t N, int32_t K, uint32_t* out)
+{
+    if (!q || !out)
+        return BQD_ERR_NULL;
+    if (N < 0 || K <= 0 || K % 8)
+        return BQD_ERR_SHAPE;
+    const size_t n = (size_t)N * (size_t)K;
+    for (size_t i = 0; i < n; ++i)
+        if (q[i] < -8 || q[i] > 7)
+            return BQD_ERR_SHAPE;
+    for (size_t t = 0; t < n / 8; ++t) {
+        uint32_t w = 0;
+        for (int k = 0; k < 8; ++k)
+            w |= ((uint32_t)(uint8_t)q[8 * t + k] & 0xFu) << (4 * k);
+        out[t] = w;
+    }
+    return BQD_OK;
+}
+
+int unpack_int4_rows_host(const uint32_t* w, int32_t N, int32_t K, int8_t* out)
+{
+    if (!w || !out)
+        return BQD_ERR_NULL;
+    if (N < 0 || K <= 0 || K % 8)
+        return BQD_ERR_SHAPE;
+    const size_t words = (size_t)N * (size_t)K / 8;
+    for (size_t t = 0; t < words; ++t)
+        for (int k = 0; k < 8; ++k) {
+            // sign-extend the nibble: shift it to the top of a 32-bit int, then back
+            const int32_t v = (int32_t)(w[t] << (28 - 4 * k)) >> 28;
+            out[8 * t + k] = (int8_t)v;
+        }
+    return BQD_OK;
+}
+
+int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K, int8_t* qx, float* sx,
+                 void* stream)
+{
+    int rc = check_x_dtype(x_dtype);
+    if (rc)
+        return rc;
+    if (M < 0)
+        return BQD_ERR_SHAPE;
+    if ((rc = check_k(K)))
+        return rc;
+    if (M == 0)
+        return BQD_OK;
+    if (!x || !qx || !sx)
+        return BQD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(sx, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    if (x_dtype == BQD_F32)
+        hipLaunchKernelGGL(k_quantize_act<X_F32>, dim3(M), dim3(kThreads), 0, (hipStream_t)stream, x, K, qx, sx);
+    else
+        hipLaunchKernelGGL(k_quantize_act<X_F16>, dim3(M), dim3(kThreads), 0, (hipStream_t)stream, x, K, qx, sx);
+    return launched();
+}
+
+int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8_t* qx,
+              const float* sx, float* y, int32_t* acc, int32_t N, int32_t K, int32_t r,
+              int32_t lanes_per_row, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (!valid_config(r, lanes_per_row))
+        return BQD_ERR_CONFIG;
+    if (N == 0)
+        return BQD_OK;
+    if (!wq || !sw || !qx || !sx || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(qx, 16) || !aligned(sw, 4) || !aligned(sx, 4) ||
+        !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    return launch_gemv_rowwise<X_Q8>(wq, sw, bias, qx, sx, y, acc, nullptr, nullptr, N, K,
+                                     make_cfg(N, K / 32, r, lanes_per_row), (hipStream_t)stream);
+}
+
+int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const void* x,
+                int32_t x_dtype, float* y, int8_t* qx_out, float* sx_out, int32_t* acc, int32_t N,
+                int32_t K, int32_t r, int32_t lanes_per_row, void* stream)
+{
+    int rc = check_x_dtype(x_dtype);
+    if (rc)
+        return rc;
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    if ((rc = check_k(K)))
+        return rc;
+    if (N == 0)
+        return BQD_OK;
+    if (!wq || !sw || !x || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(qx_out, 16) || !aligned(sw, 4) ||
+        !aligned(sx_out, 4) || !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4))
+        return BQD_ERR_ALIGN;
+    if (!valid_config(r, lanes_per_row))
+        return BQD_ERR_CONFIG;
+    if ((rc = bqd_init()))
+        return rc;
+    const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row);
+    if (x_dtype == BQD_F32)
+        return launch_gemv_rowwise<X_F32>(wq, sw, bias, x, nullptr, y, acc, qx_out, sx_out, N, K, c,
+                                          (hipStream_t)stream);
+    return launch_gemv_rowwise<X_F16>(wq, sw, bias, x, nullptr, y, acc, qx_out, sx_out, N, K, c,
+                                      (hipStream_t)stream);
+}
+
+int gemv_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias, const int8_t* qx,
+                      const float* sx, float* y, int32_t* acc_g, int32_t N, int32_t K, int32_t r,
+                      int32_t lanes_per_row, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (N == 0)
+        return BQD_OK;
+    if (!wq || !s16 || !qx || !sx || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(qx, 16) || !aligned(s16, 2) || !aligned(sx, 4) ||
+        !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc_g, 4))
+        return BQD_ERR_ALIGN;
+    if (!valid_config(r, lanes_per_row))
+        return BQD_ERR_CONFIG;
+    if ((rc = bqd_init()))
+        return rc;
+    return launch_gemv_group32<X_Q8>(wq, s16, bias, qx, sx, y, acc_g, nullptr, nullptr, N, K,
+                                     make_cfg(N, K / 32, r, lanes_per_row), (hipStream_t)stream);
+}
+
+int linear_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias, const void* x,
+                        int32_t x_dtype, float* y, int8_t* qx_out, float* sx_out, int32_t* acc_g,
+                        int32_t N, int32_t K, int32_t r, int32_t lanes_per_row, void* stream)
+{
+    int rc = check_x_dtype(x_dtype);
+    if (rc)
+        return rc;
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    if ((rc = check_k(K)))
+        return rc;
+    if (N == 0)
+        return BQD_OK;
+    if (!wq || !s16 || !x || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(x, 16) || !aligned(qx_out, 16) || !aligned(s16, 2) ||
+        !aligned(sx_out, 4) || !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc_g, 4))
+        return BQD_ERR_ALIGN;
+    if (!valid_config(r, lanes_per_row))
+        return BQD_ERR_CONFIG;
+    if ((rc = bqd_init()))
+        return rc;
+    const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row);
+    if (x_dtype == BQD_F32)
+        return launch_gemv_group32<X_F32>(wq, s16, bias, x, nullptr, y, acc_g, qx_out, sx_out, N, K,
+                                          c, (hipStream_t)stream);
+    return launch_gemv_group32<X_F16>(wq, s16, bias, x, nullptr, y, acc_g, qx_out, sx_out, N, K, c,
+                                      (hipStream_t)stream);
+}
+
+int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x16, float* y,
+                       int32_t N, int32_t K, int32_t r, int32_t lanes_per_row, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (2 * (size_t)K > (size_t)kLdsBytes)
+        return BQD_ERR_BOUND;
+    if (N == 0)
+        return BQD_OK;
+    if (!w8 || !s16 || !x16 || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(w8, 16) || !aligned(x16, 16) || !aligned(s16, 2) || !aligned(y, 4))
+        return BQD_ERR_ALIGN;
+    if (!valid_config(r, lanes_per_row))
+        return BQD_ERR_CONFIG;
+    const int L = lanes_per_row ? lanes_per_row : 16;
+    if (r == 0)
+        r = 4;
+    if ((rc = bqd_init()))
+        return rc;
+    const int G = K / 32;
+    const int rows = (kThreads / L) * r;
+    const dim3 grid(grid_for((N + rows - 1) / rows)), block(kThreads);
+    const size_t lds = 2 * (size_t)K;
+    const u32x4* w = reinterpret_cast<const u32x4*>(w8);
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x16);
+    hipStream_t st = (hipStream_t)stream;
+#define BQD_W8_CASE(RR, LL)                                                                     \
+    if (r == RR && L == LL) {                                                                   \
+        hipLaunchKernelGGL((k_gemv_w8a16_g32<RR, LL>), grid, block, lds, st, w, s16, xv, y, N, G); \
+        return launched();                                                                      \
+    }
+    BQD_W8_CASE(1, 16) BQD_W8_CASE(2, 16) BQD_W8_CASE(4, 16) BQD_W8_CASE(8, 16)
+    BQD_W8_CASE(1, 32) BQD_W8_CASE(2, 32) BQD_W8_CASE(4, 32) BQD_W8_CASE(8, 32)
+    BQD_W8_CASE(1, 64) BQD_W8_CASE(2, 64) BQD_W8_CASE(4, 64) BQD_W8_CASE(8, 64)
+#undef BQD_W8_CASE
+    return BQD_ERR_CONFIG;
+}
+
+int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, const int8_t* qx,
+                     const float* sx, float* y, int32_t* acc, int32_t M, int32_t N, int32_t K,
+                     int32_t impl, void* stream)
+{
+    if (M < 0 || N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (M > BQD_MAX_TOKENS)
+        return BQD_ERR_BOUND;
+    if (impl != 0 && impl != 1)
+        return BQD_ERR_CONFIG;
+    if (M == 0 || N == 0)
+        return BQD_OK;
+    if (!wq || !sw || !qx || !sx || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(qx, 16) || !aligned(sw, 4) || !aligned(sx, 4) ||
+        !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    const int C = K / 32;
+    const int MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    constexpr int L = 16, R = 2;
+    // LDS holds MT tokens x SEGC chunks x 32 bytes; SEGC a multiple of L.
+    int segc = kLdsBytes / (MT * 32);
+    segc -= segc % L;
+    if (segc >= C)
+        segc = C;
+    const size_t lds = (size_t)MT * segc * 32;
+    const int rows = (kThreads / L) * R;
+    const dim3 grid(grid_for((N + rows - 1) / rows)), block(kThreads);
+    const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+    hipStream_t st = (hipStream_t)stream;
+#define BQD_VER_CASE(MM)                                                                          \
+    if (MT == MM) {                                                                               \
+        hipLaunchKernelGGL((k_verify_w4a8<MM, R, L>), grid, block, lds, st, w, sw, bias, qx, sx, y, \
+                           acc, M, N, C, segc);                                                   \
+        return launched();                                                                        \
+    }
+    BQD_VER_CASE(1) BQD_VER_CASE(2) BQD_VER_CASE(4) BQD_VER_CASE(8) BQD_VER_CASE(16)
+#undef BQD_VER_CASE
+    return BQD_ERR_CONFIG;
+}
+
+int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const* x,
+                       int32_t x_dtype, float* const* y, void* stream)
+{
+    if (n < 0 || n > 64)
+        return BQD_ERR_SHAPE;
+    if (n == 0)
+        return BQD_OK;
+    if (!lin || !x || !y)
+        return BQD_ERR_NULL;
+    int rc = check_x_dtype(x_dtype);
+    if (rc)
+        return rc;
+    // Validate every linear before launching any of them.
+    for (int i = 0; i < n; ++i) {
+        const bqd_linear_w4a8& l = lin[i];
+        if (!l.wq || !l.scales || !x[i] || !y[i])
+            return BQD_ERR_NULL;
+        if (l.scale_kind != BQD_SCALE_ROW_F32 && l.scale_kind != BQD_SCALE_GROUP32_F16)
+            return BQD_ERR_DTYPE;
+        if (l.N < 0)
+            return BQD_ERR_SHAPE;
+        if ((rc = check_k(l.K)))
+            return rc;
+        if (!aligned(l.wq, 16) || !aligned(x[i], 16) || !aligned(l.scales, 2) ||
+            !aligned(l.bias, 4) || !aligned(y[i], 4))
+            return BQD_ERR_ALIGN;
+        if (!valid_config(l.r, l.lanes_per_row))
+            return BQD_ERR_CONFIG;
+    }
+    for (int i = 0; i < n; ++i) {
+        const bqd_linear_w4a8& l = lin[i];
+        if (l.scale_kind == BQD_SCALE_ROW_F32)
+            rc = linear_w4a8(l.wq, (const float*)l.scales, l.bias, x[i], x_dtype, y[i], nullptr,
+                             nullptr, nullptr, l.N, l.K, l.r, l.lanes_per_row, stream);
+        else
+            rc = linear_w4a8_group32(l.wq, (const uint16_t*)l.scales, l.bias, x[i], x_dtype, y[i],
+                                     nullptr, nullptr, nullptr, l.N, l.K, l.r, l.lanes_per_row,
+                                     stream);
+        if (rc)
+            return rc;
+    }
+    return BQD_OK;
+}
+
+}  // extern "C"

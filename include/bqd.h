@@ -1,0 +1,222 @@
+/*
+ * bqd.h -- C ABI of libbqd.so, the MI355X (gfx950) W4A8 single-token decode
+ * GEMV library.
+ *
+ * The operation, from the page "Jetson Orin AGX INT4 推理优化实践：super 分支
+ * 从 9 tok/s 到 24 tok/s", section "从 FP 线性层到 INT4 DP4A 的数学推导"
+ * (FP linear layer -> INT4 DP4A derivation):
+ *
+ *     y_j = s^W_j * s^x * sum_i q^W_ji * q^x_i + b_j
+ *
+ * with per-row INT4 weight codes q^W in [-8, 7] and scale s^W_j, a per-token
+ * INT8 activation q^x in [-127, 127] with s^x = max_i |x_i| / 127, and an
+ * exact int32 accumulator.  Variants from the page "在香橙派上跑 Gemma4：vLLM
+ * 适配昇腾 310B 的内核开发实录": one fp16 scale per 32 weights (section 3.1),
+ * an int8-expanded lm_head with fp16 group scales against fp16 activations
+ * (section 3.2), and the M-token verification of speculative decoding
+ * (section 5).
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are HIP device pointers owned by the caller;
+ *     (host) pointers are ordinary host memory.  The library never allocates,
+ *     frees, or keeps a reference to caller memory after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
+ *     work is enqueued on it; calls return after enqueue, never synchronise.
+ *   - Return value: BQD_OK (0) or a negative BQD_ERR_* code.  Arguments are
+ *     validated on the host before anything is enqueued; on error nothing is
+ *     launched.  Faults inside a launched kernel surface at the caller's
+ *     next synchronisation, as for any HIP kernel.
+ *   - Layouts are row-major.  Packed INT4: eight codes per uint32, code 0 of
+ *     the eight in the least-significant nibble (word = [w7 ... w0], the page
+ *     "Jetson Orin AGX INT4 ..." section "DP4A 做了什么"), each nibble the
+ *     two's-complement low four bits of the code.  Row j of an [N, K] matrix
+ *     is K/8 consecutive words.
+ *   - K must be a positive multiple of 32 and at most BQD_MAX_K; N >= 0
+ *     (N == 0 or M == 0 enqueue nothing).  Packed weights, int8 activations
+ *     and fp32/fp16 activation inputs must be 16-byte aligned; every other
+ *     array 4-byte aligned (2-byte for fp16 arrays).
+ *   - Only gfx950 devices are accepted (BQD_ERR_DEVICE otherwise).
+ */
+#ifndef BQD_H
+#define BQD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQD_ABI_VERSION 1
+
+#define BQD_OK 0
+#define BQD_ERR_NULL (-1)      /* a required pointer is NULL                 */
+#define BQD_ERR_SHAPE (-2)     /* N/M < 0, K <= 0, K % 32 != 0, bad count     */
+#define BQD_ERR_ALIGN (-3)     /* a pointer violates its alignment           */
+#define BQD_ERR_BOUND (-4)     /* K > BQD_MAX_K or M > BQD_MAX_TOKENS        */
+#define BQD_ERR_DTYPE (-5)     /* unknown dtype or scale kind                */
+#define BQD_ERR_CONFIG (-6)    /* unsupported r / lanes_per_row              */
+#define BQD_ERR_LAUNCH (-7)    /* the HIP runtime rejected a launch          */
+#define BQD_ERR_DEVICE (-8)    /* no HIP device, or not a gfx950 device      */
+
+#define BQD_F32 0              /* activation dtype: IEEE binary32            */
+#define BQD_F16 1              /* activation dtype: IEEE binary16            */
+
+#define BQD_SCALE_ROW_F32 0    /* float[N]: one fp32 scale per output row    */
+#define BQD_SCALE_GROUP32_F16 1 /* uint16[N, K/32]: fp16 scale per 32 codes  */
+
+/* Largest reduction length.  The int32 argument of the page "Jetson Orin AGX
+ * INT4 ..." section "INT32 accumulator 是否安全" bounds each product by
+ * 8 * 127 = 1016 and so allows K up to floor((2^31 - 1) / 1016) = 2,113,665;
+ * the kernels stage the whole activation in 64 KiB of LDS, which is the
+ * tighter limit. */
+#define BQD_MAX_K 65536
+/* Largest token count of gemm_w4a8_verify. */
+#define BQD_MAX_TOKENS 16
+
+/* Version of this header's ABI (BQD_ABI_VERSION). */
+int bqd_abi_version(void);
+
+/* Static, human-readable text for a status code.  Never NULL. */
+const char* bqd_status_string(int status);
+
+/* Checks that the current HIP device is a gfx950 and caches its properties.
+ * Idempotent; every entry point calls it for the current device. */
+int bqd_init(void);
+
+/* ---------------------------------------------------------------------- */
+/* Load-time weight preparation (not on the per-token path).               */
+/* ---------------------------------------------------------------------- */
+
+/* Per-row INT4 ("Jetson Orin AGX INT4 ...", derivation section):
+ *   sw[j] = max_i |W[j,i]| / 7                      (fp32, correctly rounded)
+ *   code  = clip(round_half_even(W[j,i] / sw[j]), -8, 7)   (fp32 division;
+ *           every code of an all-zero row is 0)
+ * W (device) fp32 [N, K]; wq (device) uint32 [N, K/8] packed; sw (device)
+ * float [N].  W must be finite. */
+int quantize_weights_int4_rowwise(const float* W, int32_t N, int32_t K,
+                                  uint32_t* wq, float* sw, void* stream);
+
+/* Q4_0-style group-32 INT4 ("在香橙派上跑 Gemma4 ...", section 3.1): per block of
+ * 32 weights s = fp16_rne(max|W_block| / 7), codes taken against the stored
+ * fp16 value, clip to [-8, 7].  wq (device) uint32 [N, K/8]; s16 (device)
+ * uint16 fp16 bit patterns [N, K/32]. */
+int quantize_weights_int4_group32(const float* W, int32_t N, int32_t K,
+                                  uint32_t* wq, uint16_t* s16, void* stream);
+
+/* int8-expanded lm_head ("在香橙派上跑 Gemma4 ...", section 3.2): per block of 32
+ * weights s = fp16_rne(max|W_block| / 31), codes clip(round(W / s), -32, 31)
+ * stored one per byte.  w8 (device) int8 [N, K]; s16 (device) uint16 [N, K/32]. */
+int quantize_weights_int8_group32(const float* W, int32_t N, int32_t K,
+                                  int8_t* w8, uint16_t* s16, void* stream);
+
+/* Host helpers: pack int8 codes in [-8, 7] (host, [N, K]) into words (host,
+ * [N, K/8]) and back.  K % 8 == 0 is enough here.  Out-of-range codes give
+ * BQD_ERR_SHAPE with nothing written. */
+int pack_int4_rows_host(const int8_t* q, int32_t N, int32_t K, uint32_t* out);
+int unpack_int4_rows_host(const uint32_t* w, int32_t N, int32_t K, int8_t* out);
+
+/* ---------------------------------------------------------------------- */
+/* Per-token hot path.                                                     */
+/* ---------------------------------------------------------------------- */
+
+/* Dynamic per-token INT8 activation quantisation ("Jetson Orin AGX INT4 ...",
+ * derivation section), one token per row of x:
+ *   sx[m] = max_i |x[m,i]| / 127                     (fp32, correctly rounded)
+ *   qx[m,i] = clip(round_half_even(x[m,i] / sx[m]), -127, 127)  (fp32 division;
+ *             all zero when sx[m] == 0)
+ * x (device) [M, K] of x_dtype (BQD_F32 or BQD_F16; fp16 is widened exactly);
+ * qx (device) int8 [M, K]; sx (device) float [M].  x must be finite. */
+int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K,
+                 int8_t* qx, float* sx, void* stream);
+
+/* W4A8 GEMV over per-row scales ("Jetson Orin AGX INT4 ...", derivation and
+ * "o2-all 和 o4-all 为什么能加速" sections):
+ *   acc[j] = sum_i q^W[j,i] * qx[i]            (exact int32)
+ *   y[j]   = (sw[j] * sx[0]) * acc[j] + bias[j] (fp32; bias may be NULL)
+ * wq (device) uint32 [N, K/8]; sw, bias (device) float [N]; qx (device) int8
+ * [K] with codes in [-127, 127]; sx (device) float [1]; y (device) float [N];
+ * acc (device) int32 [N] or NULL (written only when given).
+ * r: output rows each lane group accumulates at once, reusing every staged
+ * activation chunk r times (the pages' "o-r" kernels): 1, 2, 4 or 8;
+ * lanes_per_row: lanes that split one row's reduction, 16, 32 or 64;
+ * 0 for either picks it from N and K. */
+int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias,
+              const int8_t* qx, const float* sx, float* y, int32_t* acc,
+              int32_t N, int32_t K, int32_t r, int32_t lanes_per_row, void* stream);
+
+/* One decode linear in one launch: the activation quantisation of
+ * quantize_act folded into the prologue of gemv_w4a8 (every workgroup
+ * quantises x itself, bit-identically), so no int8 copy of x goes through
+ * memory.  x (device) [K] of x_dtype.  qx_out (device int8 [K]) and sx_out
+ * (device float [1]) are optional copies of the quantised activation written
+ * by one workgroup; acc as in gemv_w4a8. */
+int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias,
+                const void* x, int32_t x_dtype, float* y, int8_t* qx_out,
+                float* sx_out, int32_t* acc, int32_t N, int32_t K, int32_t r,
+                int32_t lanes_per_row, void* stream);
+
+/* Group-32 W4A8 GEMV ("在香橙派上跑 Gemma4 ...", section 3.1 format with the
+ * INT8 activation of "Jetson Orin AGX INT4 ..."):
+ *   acc_g[j,g] = sum_{i in block g} q^W[j,i] * qx[i]            (exact int32)
+ *   y[j] = sx[0] * sum_g fp32(s16[j,g]) * acc_g[j,g] + bias[j]   (fp32)
+ * s16 (device) uint16 fp16 [N, K/32]; acc_g (device) int32 [N, K/32] or
+ * NULL; other arguments as in gemv_w4a8. */
+int gemv_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias,
+                      const int8_t* qx, const float* sx, float* y, int32_t* acc_g,
+                      int32_t N, int32_t K, int32_t r, int32_t lanes_per_row,
+                      void* stream);
+
+/* linear_w4a8 for group-32 weights: quantise x in the prologue, then
+ * gemv_w4a8_group32.  qx_out, sx_out, acc_g optional. */
+int linear_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias,
+                        const void* x, int32_t x_dtype, float* y, int8_t* qx_out,
+                        float* sx_out, int32_t* acc_g, int32_t N, int32_t K, int32_t r,
+                        int32_t lanes_per_row, void* stream);
+
+/* W8A16 lm_head ("在香橙派上跑 Gemma4 ...", section 3.2): int8 codes times fp16
+ * group scales against fp16 activations, fp32 accumulation:
+ *   y[j] = sum_g fp32(s16[j,g]) * sum_{i in block g} w8[j,i] * fp32(x16[i])
+ * w8 (device) int8 [N, K] (codes in [-32, 31]); s16 (device) uint16 [N, K/32];
+ * x16 (device) uint16 fp16 [K] (finite); y (device) float [N]. */
+int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x16,
+                       float* y, int32_t N, int32_t K, int32_t r,
+                       int32_t lanes_per_row, void* stream);
+
+/* M-token verification ("在香橙派上跑 Gemma4 ...", section 5): one pass over the
+ * weights serves M quantised tokens.
+ *   acc[m,j] = sum_i q^W[j,i] * qx[m,i],  y[m,j] = (sw[j] * sx[m]) * acc[m,j] + bias[j]
+ * qx (device) int8 [M, K]; sx (device) float [M]; y (device) float [M, N];
+ * acc (device) int32 [M, N] or NULL.  1 <= M <= BQD_MAX_TOKENS.
+ * impl: 0 automatic, 1 integer dot-product kernel. */
+int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias,
+                     const int8_t* qx, const float* sx, float* y, int32_t* acc,
+                     int32_t M, int32_t N, int32_t K, int32_t impl, void* stream);
+
+/* One linear of a decoder layer, as handed to layer_w4a8_forward.  The
+ * struct lives in host memory; its pointers are device pointers. */
+typedef struct bqd_linear_w4a8 {
+    const uint32_t* wq;    /* packed codes [N, K/8]                         */
+    const void* scales;    /* float[N] or uint16 fp16 [N, K/32]             */
+    const float* bias;     /* [N] or NULL                                   */
+    int32_t N;
+    int32_t K;
+    int32_t scale_kind;    /* BQD_SCALE_ROW_F32 or BQD_SCALE_GROUP32_F16    */
+    int32_t r;             /* as in gemv_w4a8; 0 = automatic                */
+    int32_t lanes_per_row; /* as in gemv_w4a8; 0 = automatic                */
+} bqd_linear_w4a8;
+
+/* The linears of one decoder layer in order on one stream, each one launch
+ * of linear_w4a8 / linear_w4a8_group32 (quantise x[i], GEMV into y[i]).
+ * With q/k/v and gate/up rows concatenated at load time ("在香橙派上跑 Gemma4
+ * ...", section 3.1) a layer is 4 linears and 4 launches.  lin (host) [n];
+ * x (host) array of n device pointers to [K_i] activations of x_dtype;
+ * y (host) array of n device pointers to float [N_i].  0 <= n <= 64. */
+int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const* x,
+                       int32_t x_dtype, float* const* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQD_H */

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library loads, exports every function include/bqd.h declares, and its
+argument validation rejects bad calls before anything touches a device.
+Every call here is built to fail validation (fake, non-null device pointers
+never reach a kernel), so the tests are safe on a GPU machine too.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_decode_quantize_amd as bqd
+import oracle as O
+from bit_quantized_decode_quantize_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, ALIGN, BOUND, DTYPE, CONFIG, LAUNCH, DEVICE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+P = 0x10000          # a fake, 64 KiB-aligned "device" address: never dereferenced
+P4 = P + 4           # 4-byte but not 16-byte aligned
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "bqd.h"), encoding="utf-8").read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s+(\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 16
+    lib = bqd.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bqd.ENTRY_POINTS)
+
+
+def test_version_and_status_strings():
+    assert bqd.abi_version() == 1
+    for s in (OK, NULL, SHAPE, ALIGN, BOUND, DTYPE, CONFIG, LAUNCH, DEVICE):
+        assert bqd.status_string(s)
+    assert bqd.status_string(12345) == "unknown status"
+
+
+def test_init_reports_device_state():
+    rc = bqd.lib().bqd_init()
+    assert rc in (OK, DEVICE)
+    if not torch.cuda.is_available():
+        assert rc == DEVICE
+
+
+L = None
+
+
+def _lib():
+    return bqd.lib()
+
+
+@pytest.mark.parametrize("args,expected", [
+    # (wq, sw, bias, qx, sx, y, acc, N, K, r, lanes)
+    ((None, P, None, P, P, P, None, 8, 64, 0, 0), NULL),
+    ((P, P, None, P, P, None, None, 8, 64, 0, 0), NULL),
+    ((P, P, None, P, P, P, None, -1, 64, 0, 0), SHAPE),
+    ((P, P, None, P, P, P, None, 8, 0, 0, 0), SHAPE),
+    ((P, P, None, P, P, P, None, 8, 40, 0, 0), SHAPE),
+    ((P, P, None, P, P, P, None, 8, 65536 + 32, 0, 0), BOUND),
+    ((P4, P, None, P, P, P, None, 8, 64, 0, 0), ALIGN),
+    ((P, P, None, P4, P, P, None, 8, 64, 0, 0), ALIGN),
+    ((P, P + 2, None, P, P, P, None, 8, 64, 0, 0), ALIGN),
+    ((P, P, P + 1, P, P, P, None, 8, 64, 0, 0), ALIGN),
+    ((P, P, None, P, P, P, None, 8, 64, 3, 0), CONFIG),
+    ((P, P, None, P, P, P, None, 8, 64, 4, 8), CONFIG),
+    ((P, P, None, P, P, P, None, 8, 64, 16, 16), CONFIG),
+])
+def test_gemv_w4a8_validation(args, expected):
+    assert _lib().gemv_w4a8(*args, None) == expected
+
+
+def test_other_entry_points_validate_before_launch():
+    L = _lib()
+    # quantize_act(x, dtype, M, K, qx, sx, stream)
+    assert L.quantize_act(P, 2, 1, 64, P, P, None) == DTYPE
+    assert L.quantize_act(None, 0, 1, 64, P, P, None) == NULL
+    assert L.quantize_act(P, 0, -1, 64, P, P, None) == SHAPE
+    assert L.quantize_act(P4, 0, 1, 64, P, P, None) == ALIGN
+    assert L.quantize_act(P, 0, 1, 48, P, P, None) == SHAPE
+    # linear_w4a8(wq, sw, bias, x, dtype, y, qx_out, sx_out, acc, N, K, r, lanes, stream)
+    assert L.linear_w4a8(P, P, None, P, 7, P, None, None, None, 8, 64, 0, 0, None) == DTYPE
+    assert L.linear_w4a8(P, P, None, P4, 0, P, None, None, None, 8, 64, 0, 0, None) == ALIGN
+    assert L.linear_w4a8(P, P, None, P, 0, P, P4, None, None, 8, 64, 0, 0, None) == ALIGN
+    assert L.linear_w4a8(P, P, None, P, 0, P, None, None, None, 8, 64, 5, 0, None) == CONFIG
+    # group-32
+    assert L.gemv_w4a8_group32(P, P + 1, None, P, P, P, None, 8, 64, 0, 0, None) == ALIGN
+    assert L.gemv_w4a8_group32(P, P, None, P, P, P, None, 8, 96 + 8, 0, 0, None) == SHAPE
+    assert L.linear_w4a8_group32(P, None, None, P, 0, P, None, None, None, 8, 64, 0, 0, None) == NULL
+    # W8A16: K above the LDS staging limit for fp16 activations
+    assert L.gemv_w8a16_group32(P, P, P, P, 8, 65536, 0, 0, None) == BOUND
+    assert L.gemv_w8a16_group32(P, P, P4, P, 8, 64, 0, 0, None) == ALIGN
+    # verify: token count bound, impl
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 17, 8, 64, 0, None) == BOUND
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 2, 8, 64, 9, None) == CONFIG
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, -1, 8, 64, 0, None) == SHAPE
+    # weight quantisers
+    assert L.quantize_weights_int4_rowwise(P, 8, 36, P, P, None) == SHAPE
+    assert L.quantize_weights_int4_group32(P4, 8, 64, P, P, None) == ALIGN
+    assert L.quantize_weights_int8_group32(None, 8, 64, P, P, None) == NULL
+
+
+def test_layer_forward_validates_every_linear_first():
+    L = _lib()
+    good = bqd.LinearW4A8(P, P, 0, 8, 64, 0, 0, 0)
+    bad_k = bqd.LinearW4A8(P, P, 0, 8, 40, 0, 0, 0)
+    bad_kind = bqd.LinearW4A8(P, P, 0, 8, 64, 3, 0, 0)
+    xs = (C.c_void_p * 2)(P, P)
+    ys = (C.c_void_p * 2)(P, P)
+    arr = (bqd.LinearW4A8 * 2)(good, bad_k)
+    assert L.layer_w4a8_forward(arr, 2, C.cast(xs, C.c_void_p), 0, C.cast(ys, C.c_void_p), None) == SHAPE
+    arr = (bqd.LinearW4A8 * 2)(good, bad_kind)
+    assert L.layer_w4a8_forward(arr, 2, C.cast(xs, C.c_void_p), 0, C.cast(ys, C.c_void_p), None) == DTYPE
+    assert L.layer_w4a8_forward(arr, 65, C.cast(xs, C.c_void_p), 0, C.cast(ys, C.c_void_p), None) == SHAPE
+    assert L.layer_w4a8_forward(None, 0, None, 0, None, None) == OK
+
+
+def test_host_pack_helpers_match_oracle():
+    q = I.uniform_int("abi/pack", (37, 96), -8, 7).to(torch.int8)
+    q[0, :16] = torch.arange(-8, 8, dtype=torch.int8)
+    w = bqd.pack_int4_rows_host(q)
+    assert np.array_equal(w.numpy().view(np.uint32), O.pack_int4(q.numpy()))
+    assert torch.equal(bqd.unpack_int4_rows_host(w), q)
+    words = I.random_words("abi/words", (11, 12))
+    assert np.array_equal(bqd.unpack_int4_rows_host(words).numpy(),
+                          O.unpack_int4(words.numpy().view(np.uint32)))
+    bad = q.clone()
+    bad[3, 3] = 9
+    with pytest.raises(bqd.BQDError):
+        bqd.pack_int4_rows_host(bad)
+
+
+def test_binding_rejects_mismatched_buffers_before_the_call():
+    """Shape checks live in the binding: the C ABI cannot see buffer sizes."""
+    with pytest.raises((ValueError, TypeError)):
+        bqd.bqd._dev(torch.zeros(4), "x", (torch.float32,))   # CPU tensor
