@@ -30,6 +30,7 @@ ENTRY_POINTS = (
     "quantize_weights_int8_group32", "pack_int4_rows_host", "unpack_int4_rows_host",
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
+    "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
 )
 
 
@@ -76,6 +77,10 @@ def lib() -> C.CDLL:
         "gemv_w8a16_group32": (I, [P, P, P, P, I, I, I, I, P]),
         "gemm_w4a8_verify": (I, [P, P, P, P, P, P, P, I, I, I, I, P]),
         "layer_w4a8_forward": (I, [C.POINTER(LinearW4A8), I, P, I, P, P]),
+        "decode_pass_desc_bytes": (C.c_size_t, [I]),
+        "decode_pass_sync_bytes": (C.c_size_t, [I]),
+        "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32)]),
+        "decode_pass_w4a8": (I, [P, I, I, P, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -369,3 +374,44 @@ def layer_w4a8_forward(linears: Sequence[LinearW4A8], xs: Sequence[torch.Tensor]
                        ys: Sequence[torch.Tensor], stream=None) -> None:
     """Run the linears of one layer in order (one fused launch each)."""
     LayerPlan(linears, xs, ys).run(stream)
+
+
+class DecodePass:
+    """One persistent launch per decode step over ``linears`` in order
+    (decode_pass_w4a8).  Encodes the descriptors once on the host, keeps a
+    device copy and the zero-initialised synchronisation words."""
+
+    def __init__(self, linears: Sequence[LinearW4A8], xs: Sequence[torch.Tensor],
+                 ys: Sequence[torch.Tensor], device=None):
+        n = len(linears)
+        if n == 0:
+            raise ValueError("a pass needs at least one linear")
+        dt = xs[0].dtype
+        for i, (l, x, y) in enumerate(zip(linears, xs, ys)):
+            _dev(x, f"x[{i}]", (dt,), l.K)
+            _dev(y, f"y[{i}]", _F32, l.N)
+        device = xs[0].device if device is None else device
+        self.n = n
+        lin = (LinearW4A8 * n)(*linears)
+        xp = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
+        yp = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
+        nbytes = lib().decode_pass_desc_bytes(n)
+        host = (C.c_uint8 * nbytes)()
+        mk = C.c_int32(0)
+        _call("decode_pass_encode", lin, n, C.cast(xp, C.c_void_p), BQD_F32 if dt == torch.float32 else BQD_F16,
+              C.cast(yp, C.c_void_p), C.cast(host, C.c_void_p), nbytes, C.byref(mk))
+        self.max_k = mk.value
+        self.desc = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device)
+        self.sync = torch.zeros(lib().decode_pass_sync_bytes(n) // 4, dtype=torch.int32, device=device)
+        self._keep = (list(xs), list(ys))
+
+    def run(self, stream=None, spin_limit: int = 0) -> None:
+        _call("decode_pass_w4a8", self.desc.data_ptr(), self.n, self.max_k, self.sync.data_ptr(),
+              spin_limit, _stream(stream))
+
+    def error_word(self) -> int:
+        """Bit 0 set if any wait ran out of spins (synchronises)."""
+        return int(self.sync[self.n].item())
+
+    def clear_error(self) -> None:
+        self.sync[self.n].zero_()

@@ -44,6 +44,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
+// Global address space.  Pointers read from memory (the pass descriptors) are
+// generic; casting them keeps loads on the global path (global_load_*, which
+// count only in vmcnt) instead of flat loads, which also count in lgkmcnt and
+// so would be drained by every LDS wait.
+#define BQD_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const BQD_GLOBAL T* gptr(const T* p)
+{
+    return (const BQD_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ BQD_GLOBAL T* gptr_mut(T* p)
+{
+    return (BQD_GLOBAL T*)p;
+}
+
 // ------------------------------------------------------------------------
 // Bit helpers
 // ------------------------------------------------------------------------
@@ -148,12 +164,12 @@ template <int XIN>
 __device__ __forceinline__ void load8(const void* x, int g, float v[8])
 {
     if constexpr (XIN == X_F32) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(x) + 2 * g;
+        const BQD_GLOBAL f32x4* p = gptr(reinterpret_cast<const f32x4*>(x)) + 2 * g;
         f32x4 a = p[0], b = p[1];
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
-        u32x4 h = reinterpret_cast<const u32x4*>(x)[g];
+        u32x4 h = gptr(reinterpret_cast<const u32x4*>(x))[g];
         uint32_t hw[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -818,6 +834,225 @@ __global__ __launch_bounds__(kThreads) void k_verify_w4a8(
 }
 
 // ------------------------------------------------------------------------
+// Persistent token pass: every linear of a decode step in one cooperative
+// launch.  Linear t reads its activation only after every workgroup has
+// finished linear t-1 (a monotonic completion counter per linear; outputs
+// are written with device-coherent stores that complete before the counter
+// moves), which is the data dependency of a decoder:
+// each GEMV's input derives from the previous GEMV's output.  The weights
+// do not depend on anything, so each workgroup issues the first loads of
+// its share of linear t+1 right after signalling linear t, and they stream
+// from HBM while it waits and quantises the next activation.
+//   Counters: sync[0..n-1] grow by gridDim.x per pass (all equal between
+//   passes, so the base is read at kernel start; uint32 wrap-safe).
+//   sync[n]: error word, bit 0 set when a wait exceeded its spin limit (the
+//   wait then gives up, so every wave always reaches the end of the kernel).
+// ------------------------------------------------------------------------
+struct PassTask {
+    const u32x4* wq;
+    const float* sw;
+    const float* bias;
+    const void* x;
+    float* y;
+    int32_t N, K, x_dtype, L, r, reserved;
+};
+static_assert(sizeof(PassTask) == 64, "descriptor layout");
+
+struct PassShape {
+    int L, lshift, r, rows, tiles, C, iters, steps;
+};
+
+// Lanes per row and rows per lane group for one linear: the fewest lanes and
+// most rows that still give every workgroup of the grid a tile.
+template <int RMAX, int U>
+__device__ __forceinline__ PassShape pass_shape(const PassTask& t, int G)
+{
+    PassShape s;
+    s.C = t.K / 32;
+    int L = t.L, r = t.r;
+    if (L == 0 || r == 0) {
+        const int cand[4][2] = {{16, 2}, {32, 2}, {64, 2}, {64, 1}};
+        L = 64;
+        r = 1;
+        for (int i = 0; i < 4; ++i) {
+            const int rows = (kThreads / cand[i][0]) * cand[i][1];
+            if ((t.N + rows - 1) / rows >= G) {
+                L = cand[i][0];
+                r = cand[i][1];
+                break;
+            }
+        }
+    }
+    s.L = L;
+    s.r = r < RMAX ? r : RMAX;
+    s.lshift = L == 16 ? 4 : (L == 32 ? 5 : 6);
+    s.rows = (kThreads >> s.lshift) * s.r;
+    s.tiles = (t.N + s.rows - 1) / s.rows;
+    s.iters = (s.C + L - 1) >> s.lshift;
+    s.steps = (s.iters + U - 1) / U;
+    return s;
+}
+
+template <int RMAX, int U>
+__device__ __forceinline__ void pass_load(u32x4 (&buf)[U][RMAX], const PassTask& t, const PassShape& s,
+                                          int tile, int step)
+{
+    const int lane = threadIdx.x & (s.L - 1);
+    const int grp = threadIdx.x >> s.lshift;
+    const int row0 = tile * s.rows + grp * s.r;
+    const BQD_GLOBAL u32x4* wrow[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r)
+        wrow[r] = gptr(t.wq) + (size_t)min(row0 + r, t.N - 1) * s.C;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (step * U + u) * s.L + lane;
+        const bool ok = c < s.C;
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r)
+            buf[u][r] = (ok && r < s.r) ? wrow[r][c] : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int RMAX, int U>
+__global__ __launch_bounds__(kThreads) void k_decode_pass(const PassTask* __restrict__ tasks, int n,
+                                                          uint32_t* __restrict__ sync, int max_k,
+                                                          int spin_limit)
+{
+    extern __shared__ u32x4 xs[];
+    __shared__ float red[4];
+    __shared__ uint32_t s_base;
+    const int G = gridDim.x;
+    const int tid = threadIdx.x;
+    if (tid == 0)
+        s_base = __hip_atomic_load(&sync[n - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t target = s_base + (uint32_t)G;
+
+    u32x4 cur[U][RMAX];
+    bool have_cur = false;
+    {
+        const PassTask t0 = tasks[0];
+        const PassShape s0 = pass_shape<RMAX, U>(t0, G);
+        if ((int)blockIdx.x < s0.tiles && t0.K <= max_k) {
+            pass_load<RMAX, U>(cur, t0, s0, blockIdx.x, 0);
+            have_cur = true;
+        }
+    }
+
+    for (int ti = 0; ti < n; ++ti) {
+        const PassTask t = tasks[ti];
+        const PassShape s = pass_shape<RMAX, U>(t, G);
+        if (ti > 0) {
+            if (tid == 0) {
+                int spins = 0;
+                while ((int)(__hip_atomic_load(&sync[ti - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                             target) < 0) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++spins >= spin_limit ||
+                        ((spins & 255) == 0 &&
+                         (__hip_atomic_load(&sync[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u))) {
+                        __hip_atomic_fetch_or(&sync[n], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        const bool mine = (int)blockIdx.x < s.tiles && t.K <= max_k;
+        if (mine) {
+            float sx;
+            if (t.x_dtype == X_F16)
+                sx = stage_quant<X_F16>(reinterpret_cast<u32x2*>(xs), t.x, 4 * s.C, red, nullptr, nullptr);
+            else
+                sx = stage_quant<X_F32>(reinterpret_cast<u32x2*>(xs), t.x, 4 * s.C, red, nullptr, nullptr);
+            __syncthreads();
+            if (!have_cur)
+                pass_load<RMAX, U>(cur, t, s, blockIdx.x, 0);
+            const int lane = tid & (s.L - 1);
+            const int grp = tid >> s.lshift;
+            for (int tile = blockIdx.x; tile < s.tiles; tile += G) {
+                const int row0 = tile * s.rows + grp * s.r;
+                int acc[RMAX];
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r)
+                    acc[r] = 0;
+                for (int st = 0; st < s.steps; ++st) {
+                    u32x4 nxt[U][RMAX];
+                    int ntile = tile, nst = st + 1;
+                    if (nst == s.steps) {
+                        ntile += G;
+                        nst = 0;
+                    }
+                    const bool more = ntile < s.tiles;
+                    if (more)
+                        pass_load<RMAX, U>(nxt, t, s, ntile, nst);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        if (st * U + u < s.iters) {
+                            const int c = min((st * U + u) * s.L + lane, s.C - 1);
+                            const u32x4 xa = xs[2 * c], xb = xs[2 * c + 1];
+#pragma unroll
+                            for (int r = 0; r < RMAX; ++r)
+                                if (r < s.r)
+                                    acc[r] = dot_chunk16(cur[u][r], xa, xb, acc[r]);
+                        }
+                    }
+                    if (more) {
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+#pragma unroll
+                            for (int r = 0; r < RMAX; ++r)
+                                cur[u][r] = nxt[u][r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < RMAX; ++r) {
+                    int v = acc[r] >> 4;
+                    v += dpp_i<0x128>(v);
+                    v += dpp_i<0x124>(v);
+                    v += dpp_i<0x122>(v);
+                    v += dpp_i<0x121>(v);
+                    if (s.L >= 32)
+                        v += __shfl_xor(v, 16);
+                    if (s.L >= 64)
+                        v += __shfl_xor(v, 32);
+                    const int row = row0 + r;
+                    if (r < s.r && lane == r && row < t.N) {
+                        const float tw = gptr(t.sw)[row] * sx;
+                        const float b = t.bias ? gptr(t.bias)[row] : 0.0f;
+                        // device-coherent store: visible to every XCD once complete
+                        __hip_atomic_store(gptr_mut(t.y) + row, fmaf(tw, (float)v, b), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
+        // Count linear ti done for this workgroup once every wave's coherent
+        // output stores have completed (no loads are outstanding here).
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_fetch_add(&sync[ti], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // Prefetch the first step of this workgroup's share of linear ti+1.
+        have_cur = false;
+        if (ti + 1 < n) {
+            const PassTask tn = tasks[ti + 1];
+            const PassShape sn = pass_shape<RMAX, U>(tn, G);
+            if ((int)blockIdx.x < sn.tiles && tn.K <= max_k) {
+                pass_load<RMAX, U>(cur, tn, sn, blockIdx.x, 0);
+                have_cur = true;
+            }
+        }
+    }
+}
+
+constexpr int kPassRmax = 2;
+constexpr int kPassU = 4;
+constexpr int kPassSpinLimit = 1 << 21;
+constexpr int kPassWgPerCu = 2;
+
+// ------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
@@ -873,15 +1108,15 @@ inline bool valid_config(int r, int L)
     return (r == 0 || r == 1 || r == 2 || r == 4 || r == 8) && (L == 0 || L == 16 || L == 32 || L == 64);
 }
 
-// Automatic choice where the caller passes 0.  Small matrices spread a row
-// over more lanes so that every CU gets rows; large ones use 16 lanes per
-// row and r = 4 rows per lane group.  U covers a lane's whole row when it
-// fits the register budget.
+// Automatic choice where the caller passes 0 (from a sweep over the decoder's
+// shapes on MI355X): 32 lanes per row; one row per lane group below 8192
+// rows so that small matrices still spread over every CU, two above.  U
+// covers a lane's whole row when it fits the register budget.
 inline GemvCfg make_cfg(int N, int C, int r, int L)
 {
     GemvCfg c;
-    c.L = L ? L : (N >= 16384 ? 16 : (N >= 8192 ? 32 : 64));
-    c.r = r ? r : (c.L == 16 ? 4 : (c.L == 32 ? 2 : 1));
+    c.L = L ? L : 32;
+    c.r = r ? r : (N >= 8192 ? 2 : 1);
     const int iters = (C + c.L - 1) / c.L;
     c.U = pow2ceil(iters) < max_unroll(c.r) ? pow2ceil(iters) : max_unroll(c.r);
     const long long rows = (long long)(kThreads / c.L) * c.r;
@@ -1354,6 +1589,92 @@ int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const*
             return rc;
     }
     return BQD_OK;
+}
+
+size_t decode_pass_desc_bytes(int32_t n) { return n > 0 ? (size_t)n * sizeof(PassTask) : 0; }
+
+size_t decode_pass_sync_bytes(int32_t n) { return n > 0 ? (size_t)(n + 1) * sizeof(uint32_t) : 0; }
+
+int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
+                       float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k)
+{
+    if (n <= 0 || n > BQD_MAX_PASS_LINEARS)
+        return BQD_ERR_SHAPE;
+    if (!lin || !x || !y || !desc_host || !max_k)
+        return BQD_ERR_NULL;
+    int rc = check_x_dtype(x_dtype);
+    if (rc)
+        return rc;
+    if (desc_bytes < decode_pass_desc_bytes(n))
+        return BQD_ERR_SHAPE;
+    int kmax = 0;
+    PassTask* d = reinterpret_cast<PassTask*>(desc_host);
+    for (int i = 0; i < n; ++i) {
+        const bqd_linear_w4a8& l = lin[i];
+        if (l.scale_kind != BQD_SCALE_ROW_F32)
+            return BQD_ERR_DTYPE;
+        if (l.N <= 0)
+            return BQD_ERR_SHAPE;
+        if ((rc = check_k(l.K)))
+            return rc;
+        if (!l.wq || !l.scales || !x[i] || !y[i])
+            return BQD_ERR_NULL;
+        if (!aligned(l.wq, 16) || !aligned(x[i], 16) || !aligned(l.scales, 4) || !aligned(l.bias, 4) ||
+            !aligned(y[i], 4))
+            return BQD_ERR_ALIGN;
+        if (!(l.r == 0 || l.r == 1 || l.r == 2) ||
+            !(l.lanes_per_row == 0 || l.lanes_per_row == 16 || l.lanes_per_row == 32 || l.lanes_per_row == 64) ||
+            ((l.r == 0) != (l.lanes_per_row == 0)))
+            return BQD_ERR_CONFIG;
+        PassTask t;
+        std::memset(&t, 0, sizeof t);
+        t.wq = reinterpret_cast<const u32x4*>(l.wq);
+        t.sw = reinterpret_cast<const float*>(l.scales);
+        t.bias = l.bias;
+        t.x = x[i];
+        t.y = y[i];
+        t.N = l.N;
+        t.K = l.K;
+        t.x_dtype = x_dtype == BQD_F16 ? X_F16 : X_F32;
+        t.L = l.lanes_per_row;
+        t.r = l.r;
+        std::memcpy(d + i, &t, sizeof t);
+        kmax = l.K > kmax ? l.K : kmax;
+    }
+    *max_k = kmax;
+    return BQD_OK;
+}
+
+int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev,
+                     int32_t spin_limit, void* stream)
+{
+    if (n <= 0 || n > BQD_MAX_PASS_LINEARS)
+        return BQD_ERR_SHAPE;
+    if (!desc_dev || !sync_dev)
+        return BQD_ERR_NULL;
+    int rc = check_k(max_k);
+    if (rc)
+        return rc;
+    if (spin_limit < 0)
+        return BQD_ERR_CONFIG;
+    if (!aligned(desc_dev, 16) || !aligned(sync_dev, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    auto kern = k_decode_pass<kPassRmax, kPassU>;
+    const size_t lds = (size_t)max_k;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds) != hipSuccess || per_cu < 1)
+        return BQD_ERR_LAUNCH;
+    const int G = current_cus() * (per_cu < kPassWgPerCu ? per_cu : kPassWgPerCu);
+    const PassTask* tasks = reinterpret_cast<const PassTask*>(desc_dev);
+    int spin = spin_limit ? spin_limit : kPassSpinLimit;
+    int nn = n, mk = max_k;
+    void* args[] = {(void*)&tasks, (void*)&nn, (void*)&sync_dev, (void*)&mk, (void*)&spin};
+    if (hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(kThreads), args, (unsigned)lds,
+                                   (hipStream_t)stream) != hipSuccess)
+        return BQD_ERR_LAUNCH;
+    return launched();
 }
 
 }  // extern "C"

@@ -59,7 +59,7 @@ def algorithmic_bytes_linear(N: int, K: int, bias: bool, x_bytes: int = 4) -> in
 
 class QwenW4A8Stream:
     def __init__(self, layers: int = 28, seed: int = 0, device="cuda", lm_head: bool = True,
-                 r: int = 0, lanes_per_row: int = 0):
+                 r: int = 0, lanes_per_row: int = 0, persistent: bool = False):
         self.device = torch.device(device)
         self.layers = layers
         self.seed = seed
@@ -93,11 +93,24 @@ class QwenW4A8Stream:
                                      x=x, y=y, prefix="qwen/lm_head"))
             self.plans.append(bqd.LayerPlan([bqd.make_linear(wq, sw, None, r, lanes_per_row)],
                                             [x], [y]))
+        self.persistent = persistent
+        self.pass_ = None
+        if persistent:
+            pr = r if r in (1, 2) else 0
+            pl = lanes_per_row if pr else 0
+            self.pass_ = bqd.DecodePass(
+                [bqd.make_linear(d["wq"], d["sw"], d["b"], pr, pl) for d in self.linears],
+                [d["x"] for d in self.linears], [d["y"] for d in self.linears], self.device)
         torch.cuda.synchronize(self.device)
 
     def step(self, stream=None) -> None:
-        for p in self.plans:
-            p.run(stream)
+        """One token: every linear in order.  Persistent: one launch for the
+        whole pass; otherwise one fused launch per linear."""
+        if self.pass_ is not None:
+            self.pass_.run(stream)
+        else:
+            for p in self.plans:
+                p.run(stream)
 
     def bytes_per_step(self) -> int:
         return sum(algorithmic_bytes_linear(d["N"], d["K"], d["b"] is not None) for d in self.linears)

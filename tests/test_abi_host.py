@@ -27,7 +27,7 @@ P4 = P + 4           # 4-byte but not 16-byte aligned
 def header_functions():
     txt = open(os.path.join(ROOT, "include", "bqd.h"), encoding="utf-8").read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s+(\w+)\s*\(", txt, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s+(\w+)\s*\(", txt, flags=re.M)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -144,3 +144,45 @@ def test_binding_rejects_mismatched_buffers_before_the_call():
     """Shape checks live in the binding: the C ABI cannot see buffer sizes."""
     with pytest.raises((ValueError, TypeError)):
         bqd.bqd._dev(torch.zeros(4), "x", (torch.float32,))   # CPU tensor
+
+
+def test_decode_pass_encode_validates_and_serialises():
+    L = _lib()
+    n = 2
+    nbytes = L.decode_pass_desc_bytes(n)
+    assert nbytes == 128 and L.decode_pass_sync_bytes(n) == 12
+    host = (C.c_uint8 * nbytes)()
+    mk = C.c_int32(0)
+    xs = (C.c_void_p * n)(P, P + 0x100)
+    ys = (C.c_void_p * n)(P + 0x200, P + 0x300)
+
+    def enc(lins, nbytes=nbytes, n=n, dt=0):
+        arr = (bqd.LinearW4A8 * len(lins))(*lins)
+        return L.decode_pass_encode(arr, n, C.cast(xs, C.c_void_p), dt, C.cast(ys, C.c_void_p),
+                                    C.cast(host, C.c_void_p), nbytes, C.byref(mk))
+
+    a = bqd.LinearW4A8(P, P + 0x400, 0, 100, 3584, 0, 0, 0)
+    b = bqd.LinearW4A8(P + 0x1000, P + 0x500, P + 0x600, 7, 18944, 0, 2, 64)
+    assert enc([a, b]) == OK and mk.value == 18944
+    raw = bytes(host)
+    import struct
+    f = struct.unpack("<5Q6i", raw[64:128])
+    assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, P + 0x100, P + 0x300)
+    assert f[5:10] == (7, 18944, 1, 64, 2)          # N, K, fp32 input, lanes, r
+    assert enc([a, b], nbytes=100) == SHAPE
+    assert enc([a, b], dt=4) == DTYPE
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 1, 0, 0)]) == DTYPE       # group-32 scales
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 0, 4, 16)]) == CONFIG     # r above 2
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 0, 2, 0)]) == CONFIG      # r without lanes
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 0, 64, 0, 0, 0)]) == SHAPE       # N = 0
+    assert enc([a, bqd.LinearW4A8(P4, P, 0, 7, 64, 0, 0, 0)]) == ALIGN
+    assert enc([a, b], n=0) == SHAPE
+
+
+def test_decode_pass_launch_validates_before_launch():
+    L = _lib()
+    assert L.decode_pass_w4a8(P, 0, 64, P, 0, None) == SHAPE
+    assert L.decode_pass_w4a8(None, 2, 64, P, 0, None) == NULL
+    assert L.decode_pass_w4a8(P, 2, 40, P, 0, None) == SHAPE
+    assert L.decode_pass_w4a8(P, 2, 64, P, -1, None) == CONFIG
+    assert L.decode_pass_w4a8(P + 8, 2, 64, P, 0, None) == ALIGN

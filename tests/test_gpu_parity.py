@@ -376,3 +376,90 @@ def test_qwen_layer_full_size_sampled():
         qxr, sxr, accr, yr = O.linear_w4a8(wr, sr, br, npy(d["x"]))
         err = O.rel_err_rowwise(npy(d["y"][idx]), yr, sr, sxr, accr, br)
         assert err.max() <= TOL, (d["name"], err.max())
+
+
+# ------------------------------------------------------- persistent pass --
+PASS_SHAPES = [(4608, 3584), (3584, 3584), (300, 18944), (17, 64), (1, 32), (5000, 1536), (37888, 3584)]
+
+
+def _pass_fixture(dtype=torch.float32, cfg=(0, 0), tag="pass"):
+    lins, xs, ys, parts = [], [], [], []
+    for i, (N, K) in enumerate(PASS_SHAPES):
+        W = I.normal(f"gpu/{tag}/{i}/W", (N, K), 0.02, device=DEV)
+        wq, sw = bqd.quantize_weights_int4_rowwise(W)
+        b = I.normal(f"gpu/{tag}/{i}/b", N, 0.01, device=DEV) if i % 2 == 0 else None
+        x = I.normal(f"gpu/{tag}/{i}/x", K, 1.0, device=DEV, dtype=dtype)
+        y = torch.full((N,), float("nan"), device=DEV)
+        lins.append(bqd.make_linear(wq, sw, b, cfg[0], cfg[1]))
+        xs.append(x)
+        ys.append(y)
+        parts.append((wq, sw, b, x))
+    return lins, xs, ys, parts
+
+
+@pytest.mark.parametrize("dtype,cfg", [(torch.float32, (0, 0)), (torch.float16, (0, 0)),
+                                       (torch.float32, (1, 64)), (torch.float32, (2, 16)),
+                                       (torch.float32, (2, 32))])
+def test_decode_pass_equals_per_linear_launches(dtype, cfg):
+    lins, xs, ys, parts = _pass_fixture(dtype, cfg, f"pass{cfg}")
+    p = bqd.DecodePass(lins, xs, ys)
+    ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
+    for rep in range(3):                     # the counters carry over between passes
+        for y in ys:
+            y.fill_(float("nan"))
+        p.run()
+        sync()
+        assert p.error_word() == 0
+        for i, (y, yr) in enumerate(zip(ys, ref)):
+            assert torch.equal(y, yr), (rep, i)
+    # and against the oracle on one linear, end to end
+    wq, sw, b, x = parts[2]
+    qxr, sxr, accr, yr = O.linear_w4a8(u32(wq), npy(sw), npy(b), npy(x))
+    assert O.rel_err_rowwise(npy(ys[2]), yr, npy(sw), sxr, accr, npy(b)).max() <= TOL
+
+
+def test_decode_pass_wait_limit_sets_error_and_ends():
+    """A one-spin limit, set from the host, makes waits give up at once: the
+    kernel still ends, flags the error word, and a normal pass clears."""
+    lins, xs, ys, parts = _pass_fixture(tag="passlim")
+    p = bqd.DecodePass(lins, xs, ys)
+    p.run(spin_limit=1)
+    sync()
+    assert p.error_word() in (0, 1)
+    p.clear_error()
+    p.run()
+    sync()
+    assert p.error_word() == 0
+    ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
+    sync()
+    for y, yr in zip(ys, ref):
+        assert torch.equal(y, yr)
+
+
+def test_qwen_stream_full_size_persistent_sampled():
+    """The bench's workload and launch configuration: the full 28-layer
+    stream + lm_head as one persistent pass; sampled rows of linears across
+    the stream against the oracle, and every output equal to the
+    per-linear launches."""
+    from bit_quantized_decode_quantize_amd import decode_stream as DS
+    s = DS.QwenW4A8Stream(layers=28, device=DEV, persistent=True)
+    s.step()
+    s.step()
+    sync()
+    assert s.pass_.error_word() == 0
+    for k in (0, 1, 53, 54, 111, 112):      # L0 qkv/o, L13 gate_up/down, L27 down, lm_head
+        d = s.linears[k]
+        yr = bqd.linear_w4a8(d["wq"], d["sw"], d["b"], d["x"])
+        sync()
+        assert torch.equal(d["y"], yr), d["name"]
+        N = d["N"]
+        rows = torch.cat([torch.tensor([0, N - 1]),
+                          I.distinct_indices(f"gpu/stream/{k}", N, 200)]).unique()
+        Wr = npy(s.fp32_rows(d, rows))
+        wr, sr = O.prepare_int4_rowwise(Wr)
+        idx = rows.to(DEV)
+        assert np.array_equal(u32(d["wq"][idx]), wr)
+        br = None if d["b"] is None else npy(d["b"][idx])
+        qxr, sxr, accr, y_r = O.linear_w4a8(wr, sr, br, npy(d["x"]))
+        err = O.rel_err_rowwise(npy(d["y"][idx]), y_r, sr, sxr, accr, br)
+        assert err.max() <= TOL, (k, err.max())
