@@ -9,8 +9,10 @@ fp32 epilogue.  Prints one JSON line (rank 0, N=1).
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,11 +32,33 @@ def parse():
     p.add_argument("--layers", type=int, default=28)
     p.add_argument("--r", type=int, default=0, help="rows per lane group (0 = automatic)")
     p.add_argument("--lanes", type=int, default=0, help="lanes per row (0 = automatic)")
-    p.add_argument("--persistent", action="store_true",
-                   help="one persistent launch per step instead of one launch per linear")
+    p.add_argument("--per-linear", action="store_true",
+                   help="one launch per linear instead of one persistent launch per step")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="before the timed region, run one plain device copy of this many MiB "
+                        "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_pass_qwen2-7b-28L_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "bit_quantized_decode_quantize_amd", "csrc", "bqd_kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per pass launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (copy-calibrated), or None once the kernel source
+    differs from the one the counters were taken on."""
+    try:
+        text = open(TRAFFIC_SUMMARY, encoding="utf-8").read()
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_source_sha256): (\S+)$", text, re.M))
+    if vals.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(stream, seconds):
@@ -83,10 +107,19 @@ def main():
     torch.cuda.set_device(dev)
     t0 = time.time()
     s = DS.QwenW4A8Stream(layers=a.layers, device=dev, r=a.r, lanes_per_row=a.lanes,
-                          persistent=a.persistent)
+                          persistent=not a.per_linear)
     print(f"[bench] stream built: {len(s.linears)} linears, {s.weight_bytes() / 1e9:.3f} GB packed, "
           f"{time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     st = torch.cuda.current_stream()
+    if a.copy_calibration:
+        src = torch.empty(a.copy_calibration << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     for _ in range(a.warmup):
         s.step()
@@ -153,14 +186,15 @@ def main():
         "dtype": "int8", "data": "synthetic",
         "config": {"workload": "qwen2-7b-shaped 28-layer W4A8 decode weight stream + int4 lm_head "
                                "(per-row scales, fused QKV and gate/up, fused act-quant)",
-                   "launch": "persistent pass" if a.persistent else "per-linear",
+                   "launch": "per-linear" if a.per_linear else "persistent pass",
                    "layers": a.layers, "hidden": 3584, "kv_dim": 512, "intermediate": 18944,
                    "vocab": 152064, "global_batch": 1, "parallelism": "none",
                    "bytes_per_step": step_bytes, "packed_weight_bytes": s.weight_bytes()},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tok_per_s": round(1e3 / ms, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if s.persistent else None,
                      "kernel": kernel,
                      "avg_launch_us": round(avg_us, 3), "avg_algorithmic_bytes": int(avg_bytes)},
     }

@@ -410,8 +410,9 @@ class DecodePass:
               spin_limit, _stream(stream))
 
     def error_word(self) -> int:
-        """Bit 0 set if any wait ran out of spins (synchronises)."""
-        return int(self.sync[self.n].item())
+        """Bit 0: a wait ran out of spins; bit 1: descriptors for another
+        grid (synchronises)."""
+        return int(self.sync[0].item())
 
     def clear_error(self) -> None:
-        self.sync[self.n].zero_()
+        self.sync[0].zero_()

@@ -835,222 +835,364 @@ __global__ __launch_bounds__(kThreads) void k_verify_w4a8(
 
 // ------------------------------------------------------------------------
 // Persistent token pass: every linear of a decode step in one cooperative
-// launch.  Linear t reads its activation only after every workgroup has
-// finished linear t-1 (a monotonic completion counter per linear; outputs
-// are written with device-coherent stores that complete before the counter
-// moves), which is the data dependency of a decoder:
-// each GEMV's input derives from the previous GEMV's output.  The weights
-// do not depend on anything, so each workgroup issues the first loads of
-// its share of linear t+1 right after signalling linear t, and they stream
-// from HBM while it waits and quantises the next activation.
-//   Counters: sync[0..n-1] grow by gridDim.x per pass (all equal between
-//   passes, so the base is read at kernel start; uint32 wrap-safe).
-//   sync[n]: error word, bit 0 set when a wait exceeded its spin limit (the
-//   wait then gives up, so every wave always reaches the end of the kernel).
+// launch, one 1024-thread workgroup per CU.  Linear t reads its activation
+// only after every workgroup has finished linear t-1: each workgroup writes
+// its output rows with device-coherent stores, waits for them to complete,
+// and then stores the pass's epoch into its own completion flag for t-1;
+// waiters read all flags of t-1 (one wave, 4 flags per lane) and vote.  That
+// is the data dependency of a decoder, where each GEMV's input derives from
+// the previous GEMV's output.  The weights depend on nothing, so right after
+// flagging a linear the worker waves issue the loads of the first step of
+// their share of the next one; they stream from HBM while the control waves
+// wait and quantise the next activation.
+//   Work split: workgroup w owns a contiguous, balanced range of rows of
+//   every linear; its lane groups (2^lshift lanes per row, r rows per group)
+//   take the range in batches; a lane streams its rows in steps of 8
+//   16-byte chunks, double-buffered in registers.  Shapes are chosen and
+//   encoded on the host for the grid the launch uses (checked in the kernel).
+//   Sync words: err[0], flags[16 + t * 1024 + w].  Every workgroup writes
+//   each of its flags once per pass, so between passes all flags hold the
+//   same value and a pass derives its epoch from its own flag.  A wait that
+//   exceeds its spin limit sets err bit 0 and proceeds, so every wave always
+//   reaches the end of the kernel; descriptors for another grid or another
+//   n set bit 1 and the kernel returns at once.
 // ------------------------------------------------------------------------
+struct PassHeader {
+    int32_t n, grid, max_k, reserved;
+};
+static_assert(sizeof(PassHeader) == 16, "descriptor header layout");
+
 struct PassTask {
     const u32x4* wq;
     const float* sw;
     const float* bias;
     const void* x;
     float* y;
-    int32_t N, K, x_dtype, L, r, reserved;
+    int32_t N, C;                   // rows; 16-byte chunks per row (K / 32)
+    int32_t rows_base, rows_extra;  // workgroup w owns rows_base + (w < rows_extra) rows
+    int32_t lshift, r;              // 2^lshift lanes per row; r rows per lane group
+    int32_t iters, batches;         // chunk iterations per row per lane; row batches
+    int32_t steps, x_dtype;         // pipeline steps per batch; X_F32 or X_F16
 };
-static_assert(sizeof(PassTask) == 64, "descriptor layout");
+static_assert(sizeof(PassTask) == 80, "descriptor layout");
 
-struct PassShape {
-    int L, lshift, r, rows, tiles, C, iters, steps;
-};
+constexpr int kPassThreads = 1024;    // 16 waves: one workgroup per CU
+// Waves 0..11 stream weights; waves 12..15 poll, stage the activation and
+// signal.  The control waves never hold weight loads: vmcnt completes in
+// order, so a poll or activation load issued behind a wave's own prefetch
+// could not be used until that prefetch had landed.
+constexpr int kPassWorkers = 768;
+constexpr int kPassControl = kPassThreads - kPassWorkers;
+constexpr int kPassSlots = 8;         // 16-byte chunks per lane per pipeline step
+constexpr int kPassMaxGrid = 1024;    // completion flags per linear
+constexpr int kPassSpinLimit = 1 << 21;
+constexpr int kPassWgPerCu = 1;
+constexpr int kPassMaxK = 24576;      // LDS: codes (K bytes) + fp32 activation (4K bytes)
 
-// Lanes per row and rows per lane group for one linear: the fewest lanes and
-// most rows that still give every workgroup of the grid a tile.
-template <int RMAX, int U>
-__device__ __forceinline__ PassShape pass_shape(const PassTask& t, int G)
+inline size_t pass_lds_bytes(int max_k) { return (size_t)((max_k + 15) & ~15) + 4 * (size_t)max_k; }
+
+__device__ __forceinline__ void pass_range(const PassTask& t, int w, int& row_start, int& rows)
 {
-    PassShape s;
-    s.C = t.K / 32;
-    int L = t.L, r = t.r;
-    if (L == 0 || r == 0) {
-        const int cand[4][2] = {{16, 2}, {32, 2}, {64, 2}, {64, 1}};
-        L = 64;
-        r = 1;
-        for (int i = 0; i < 4; ++i) {
-            const int rows = (kThreads / cand[i][0]) * cand[i][1];
-            if ((t.N + rows - 1) / rows >= G) {
-                L = cand[i][0];
-                r = cand[i][1];
-                break;
+    rows = t.rows_base + (w < t.rows_extra ? 1 : 0);
+    row_start = w * t.rows_base + (w < t.rows_extra ? w : t.rows_extra);
+}
+
+// Streamed once: non-temporal, so weights do not push the activation out of L2.
+__device__ __forceinline__ u32x4 ld_stream(const BQD_GLOBAL u32x4* p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
+template <int R>
+__device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], const PassTask& t, int row_start,
+                                          int rows, int b, int j)
+{
+    constexpr int U = kPassSlots / R;
+    const int L = 1 << t.lshift;
+    const int lane = threadIdx.x & (L - 1);
+    const int groups = kPassWorkers >> t.lshift;
+    const int grp = threadIdx.x >> t.lshift;
+    const BQD_GLOBAL u32x4* wrow[R];
+    bool vr[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        const int rl = (b * groups + grp) * R + rr;
+        vr[rr] = rl < rows;
+        wrow[rr] = gptr(t.wq) + (size_t)(row_start + (vr[rr] ? rl : 0)) * t.C;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = (j * U + u) * L + lane;
+        const bool ok = c < t.C;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+            buf[u * R + rr] = (ok && vr[rr]) ? ld_stream(wrow[rr] + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// One linear's share of this workgroup: batches of rows, each streamed in
+// steps with the next step's loads in flight during the current step.
+template <int R>
+__device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], bool have_cur, const PassTask& t,
+                                         int row_start, int rows, const u32x4* xs, float sx)
+{
+    constexpr int U = kPassSlots / R;
+    const int L = 1 << t.lshift;
+    const int lane = threadIdx.x & (L - 1);
+    const int groups = kPassWorkers >> t.lshift;
+    const int grp = threadIdx.x >> t.lshift;
+    if (!have_cur)
+        pass_load<R>(cur, t, row_start, rows, 0, 0);
+    for (int b = 0; b < t.batches; ++b) {
+        int acc[R];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+            acc[rr] = 0;
+        for (int j = 0; j < t.steps; ++j) {
+            u32x4 nxt[kPassSlots];
+            int nb = b, nj = j + 1;
+            if (nj == t.steps) {
+                nb = b + 1;
+                nj = 0;
+            }
+            const bool more = nb < t.batches;
+            if (more)
+                pass_load<R>(nxt, t, row_start, rows, nb, nj);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = j * U + u;
+                if (i < t.iters) {  // uniform across the wave
+                    const int c = min(i * L + lane, t.C - 1);
+                    const u32x4 xa = xs[2 * c], xb = xs[2 * c + 1];
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr)
+                        acc[rr] = dot_chunk16(cur[u * R + rr], xa, xb, acc[rr]);
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int k = 0; k < kPassSlots; ++k)
+                    cur[k] = nxt[k];
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            int v = acc[rr] >> 4;
+            v += dpp_i<0x128>(v);
+            v += dpp_i<0x124>(v);
+            v += dpp_i<0x122>(v);
+            v += dpp_i<0x121>(v);
+            if (L >= 32)
+                v += __shfl_xor(v, 16);
+            if (L >= 64)
+                v += __shfl_xor(v, 32);
+            const int rl = (b * groups + grp) * R + rr;
+            if (lane == rr && rl < rows) {
+                const int row = row_start + rl;
+                const float tw = gptr(t.sw)[row] * sx;
+                const float bv = t.bias ? gptr(t.bias)[row] : 0.0f;
+                // device-coherent store: visible to every XCD once complete
+                __hip_atomic_store(gptr_mut(t.y) + row, fmaf(tw, (float)v, bv), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
-    s.L = L;
-    s.r = r < RMAX ? r : RMAX;
-    s.lshift = L == 16 ? 4 : (L == 32 ? 5 : 6);
-    s.rows = (kThreads >> s.lshift) * s.r;
-    s.tiles = (t.N + s.rows - 1) / s.rows;
-    s.iters = (s.C + L - 1) >> s.lshift;
-    s.steps = (s.iters + U - 1) / U;
-    return s;
 }
 
-template <int RMAX, int U>
-__device__ __forceinline__ void pass_load(u32x4 (&buf)[U][RMAX], const PassTask& t, const PassShape& s,
-                                          int tile, int step)
+// Codes of 8 values, bytes lo = codes 0..3, hi = codes 4..7, bit-identical to
+// act_code: the reciprocal route for all 8, then one (rare) branch to the
+// exact quotient if any of them lies within 2^-15 of a rounding tie.
+__device__ __forceinline__ void quant8_fast(const float v[8], const ActScale& a, uint32_t& lo, uint32_t& hi)
 {
-    const int lane = threadIdx.x & (s.L - 1);
-    const int grp = threadIdx.x >> s.lshift;
-    const int row0 = tile * s.rows + grp * s.r;
-    const BQD_GLOBAL u32x4* wrow[RMAX];
+    float m[8];
+    bool near = !a.fast;
+    if (a.fast) {
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r)
-        wrow[r] = gptr(t.wq) + (size_t)min(row0 + r, t.N - 1) * s.C;
+        for (int e = 0; e < 8; ++e) {
+            const float r = v[e] * a.inv;
+            m[e] = rintf(r);
+            near |= fabsf(r - m[e]) > 0.5f - 0x1p-15f;
+        }
+    }
+    if (near) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = (step * U + u) * s.L + lane;
-        const bool ok = c < s.C;
+        for (int e = 0; e < 8; ++e)
+            m[e] = a.s == 0.0f ? 0.0f : rintf(v[e] / a.s);
+    }
+    uint32_t b[8];
 #pragma unroll
-        for (int r = 0; r < RMAX; ++r)
-            buf[u][r] = (ok && r < s.r) ? wrow[r][c] : u32x4{0u, 0u, 0u, 0u};
+    for (int e = 0; e < 8; ++e)
+        b[e] = (uint32_t)((int)__builtin_amdgcn_fmed3f(m[e], -127.0f, 127.0f)) & 0xFFu;
+    lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+}
+
+// Activation staging in two phases around a workgroup barrier, by `nst`
+// threads (index st): phase 1 reads x once from memory, keeps it as fp32 in
+// LDS (xf, fp16 widened exactly) and reduces max |x| per wave; phase 2 reads
+// xf back from LDS and writes the permuted codes.
+template <int XIN>
+__device__ __forceinline__ float stage_max(const void* x, f32x4* xf, int G8, int st, int nst)
+{
+    float amax = 0.0f;
+    for (int g = st; g < G8; g += nst) {
+        float u[8];
+        load8<XIN>(x, g, u);
+        xf[2 * g] = f32x4{u[0], u[1], u[2], u[3]};
+        xf[2 * g + 1] = f32x4{u[4], u[5], u[6], u[7]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            amax = fmaxf(amax, fabsf(u[e]));
+    }
+    return wave_max(amax);
+}
+
+__device__ __forceinline__ void stage_codes(u32x2* xs, const f32x4* xf, int G8, int st, int nst,
+                                            const ActScale& a)
+{
+    for (int g = st; g < G8; g += nst) {
+        const f32x4 p = xf[2 * g], q = xf[2 * g + 1];
+        const float u[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+        uint32_t lo, hi;
+        quant8_fast(u, a, lo, hi);
+        xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
     }
 }
 
-template <int RMAX, int U>
-__global__ __launch_bounds__(kThreads) void k_decode_pass(const PassTask* __restrict__ tasks, int n,
-                                                          uint32_t* __restrict__ sync, int max_k,
-                                                          int spin_limit)
-{
-    extern __shared__ u32x4 xs[];
-    __shared__ float red[4];
-    __shared__ uint32_t s_base;
-    const int G = gridDim.x;
-    const int tid = threadIdx.x;
-    if (tid == 0)
-        s_base = __hip_atomic_load(&sync[n - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const uint32_t target = s_base + (uint32_t)G;
+// Above this many 8-value groups (K > 8192) every wave stages; below, only
+// the control waves, which hold no weight loads.
+constexpr int kPassStageAllAbove = 1024;
 
-    u32x4 cur[U][RMAX];
+template <int R>
+__device__ __forceinline__ void pass_prefetch(u32x4 (&cur)[kPassSlots], const PassTask& t, int w)
+{
+    int row_start, rows;
+    pass_range(t, w, row_start, rows);
+    if (rows > 0)
+        pass_load<R>(cur, t, row_start, rows, 0, 0);
+}
+
+__global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* __restrict__ hdr,
+                                                              const PassTask* __restrict__ tasks, int n_launch,
+                                                              int max_k_launch, uint32_t* __restrict__ sync,
+                                                              int spin_limit)
+{
+    extern __shared__ u32x4 xs[];  // codes: max_k bytes, then fp32 x at xf_offset
+    const int xf_offset = (hdr->max_k + 15) & ~15;
+    __shared__ float red[2][kPassThreads / kWave];
+    __shared__ uint32_t s_epoch;
+    const int n = hdr->n;
+    const int G = gridDim.x;
+    const int w = blockIdx.x;
+    const int tid = threadIdx.x;
+    const bool worker = tid < kPassWorkers;  // uniform per wave
+    const int ct = tid - kPassWorkers;       // control-thread index (>= 0 on control waves)
+    uint32_t* err = sync;
+    uint32_t* flags = sync + 16;             // flags[ti * kPassMaxGrid + w]
+    if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || G > kPassMaxGrid) {
+        // uniform: every workgroup leaves
+        if (tid == 0 && w == 0)
+            __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    // Every workgroup writes each of its flags once per pass, so all flags
+    // hold the same value between passes: this pass writes that value + 1.
+    if (tid == 0)
+        s_epoch = __hip_atomic_load(&flags[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    __syncthreads();
+    const uint32_t epoch = s_epoch;
+
+    u32x4 cur[kPassSlots];
+    PassTask t = tasks[0];
     bool have_cur = false;
-    {
-        const PassTask t0 = tasks[0];
-        const PassShape s0 = pass_shape<RMAX, U>(t0, G);
-        if ((int)blockIdx.x < s0.tiles && t0.K <= max_k) {
-            pass_load<RMAX, U>(cur, t0, s0, blockIdx.x, 0);
+    if (worker) {
+        int rs, rw;
+        pass_range(t, w, rs, rw);
+        if (rw > 0) {
+            if (t.r == 2)
+                pass_prefetch<2>(cur, t, w);
+            else
+                pass_prefetch<1>(cur, t, w);
             have_cur = true;
         }
     }
-
     for (int ti = 0; ti < n; ++ti) {
-        const PassTask t = tasks[ti];
-        const PassShape s = pass_shape<RMAX, U>(t, G);
-        if (ti > 0) {
-            if (tid == 0) {
-                int spins = 0;
-                while ((int)(__hip_atomic_load(&sync[ti - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                             target) < 0) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++spins >= spin_limit ||
-                        ((spins & 255) == 0 &&
-                         (__hip_atomic_load(&sync[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u))) {
-                        __hip_atomic_fetch_or(&sync[n], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-        const bool mine = (int)blockIdx.x < s.tiles && t.K <= max_k;
-        if (mine) {
-            float sx;
-            if (t.x_dtype == X_F16)
-                sx = stage_quant<X_F16>(reinterpret_cast<u32x2*>(xs), t.x, 4 * s.C, red, nullptr, nullptr);
-            else
-                sx = stage_quant<X_F32>(reinterpret_cast<u32x2*>(xs), t.x, 4 * s.C, red, nullptr, nullptr);
-            __syncthreads();
-            if (!have_cur)
-                pass_load<RMAX, U>(cur, t, s, blockIdx.x, 0);
-            const int lane = tid & (s.L - 1);
-            const int grp = tid >> s.lshift;
-            for (int tile = blockIdx.x; tile < s.tiles; tile += G) {
-                const int row0 = tile * s.rows + grp * s.r;
-                int acc[RMAX];
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r)
-                    acc[r] = 0;
-                for (int st = 0; st < s.steps; ++st) {
-                    u32x4 nxt[U][RMAX];
-                    int ntile = tile, nst = st + 1;
-                    if (nst == s.steps) {
-                        ntile += G;
-                        nst = 0;
-                    }
-                    const bool more = ntile < s.tiles;
-                    if (more)
-                        pass_load<RMAX, U>(nxt, t, s, ntile, nst);
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        if (st * U + u < s.iters) {
-                            const int c = min((st * U + u) * s.L + lane, s.C - 1);
-                            const u32x4 xa = xs[2 * c], xb = xs[2 * c + 1];
-#pragma unroll
-                            for (int r = 0; r < RMAX; ++r)
-                                if (r < s.r)
-                                    acc[r] = dot_chunk16(cur[u][r], xa, xb, acc[r]);
-                        }
-                    }
-                    if (more) {
-#pragma unroll
-                        for (int u = 0; u < U; ++u)
-#pragma unroll
-                            for (int r = 0; r < RMAX; ++r)
-                                cur[u][r] = nxt[u][r];
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < RMAX; ++r) {
-                    int v = acc[r] >> 4;
-                    v += dpp_i<0x128>(v);
-                    v += dpp_i<0x124>(v);
-                    v += dpp_i<0x122>(v);
-                    v += dpp_i<0x121>(v);
-                    if (s.L >= 32)
-                        v += __shfl_xor(v, 16);
-                    if (s.L >= 64)
-                        v += __shfl_xor(v, 32);
-                    const int row = row0 + r;
-                    if (r < s.r && lane == r && row < t.N) {
-                        const float tw = gptr(t.sw)[row] * sx;
-                        const float b = t.bias ? gptr(t.bias)[row] : 0.0f;
-                        // device-coherent store: visible to every XCD once complete
-                        __hip_atomic_store(gptr_mut(t.y) + row, fmaf(tw, (float)v, b), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                    }
+        const PassTask tn = tasks[ti + 1 < n ? ti + 1 : ti];
+        // 1. wait until every workgroup has flagged linear ti-1: the first
+        //    control wave reads all G flags (4 per lane per round) and votes.
+        if (ti > 0 && ct >= 0 && ct < kWave) {
+            const uint32_t* f = flags + (size_t)(ti - 1) * kPassMaxGrid;
+            int spins = 0;
+            while (true) {
+                bool done = true;
+                for (int i = ct; i < G; i += kWave)
+                    done &= __hip_atomic_load(&f[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+                if (__all(done))
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+                if (++spins >= spin_limit ||
+                    ((spins & 255) == 0 && (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u))) {
+                    if (ct == 0)
+                        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
                 }
             }
         }
-        // Count linear ti done for this workgroup once every wave's coherent
-        // output stores have completed (no loads are outstanding here).
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0)
-            __hip_atomic_fetch_add(&sync[ti], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // Prefetch the first step of this workgroup's share of linear ti+1.
+        int row_start, rows;
+        pass_range(t, w, row_start, rows);
+        const int G8 = 4 * t.C;
+        float* rd = red[ti & 1];
+        // 2. max |x| (control waves; every wave for long activations)
+        const bool all_stage = G8 > kPassStageAllAbove;
+        const int st = all_stage ? tid : ct;
+        const int nst = all_stage ? kPassThreads : kPassControl;
+        f32x4* xf = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(xs) + xf_offset);
+        if (rows > 0 && st >= 0) {
+            const float m = t.x_dtype == X_F16 ? stage_max<X_F16>(t.x, xf, G8, st, nst)
+                                               : stage_max<X_F32>(t.x, xf, G8, st, nst);
+            if ((st & (kWave - 1)) == 0)
+                rd[st / kWave] = m;
+        }
+        __syncthreads();
+        float amax = rd[0];
+        const int nw = all_stage ? kPassThreads / kWave : kPassControl / kWave;
+        for (int i = 1; i < nw; ++i)
+            amax = fmaxf(amax, rd[i]);
+        const ActScale a = act_scale(amax);
+        // 3. codes into LDS
+        if (rows > 0 && st >= 0)
+            stage_codes(reinterpret_cast<u32x2*>(xs), xf, G8, st, nst, a);
+        __syncthreads();
+        // 4. workers: stream the weights, write the rows, wait for the stores
+        if (rows > 0 && worker) {
+            if (t.r == 2)
+                pass_run<2>(cur, have_cur, t, row_start, rows, xs, a.s);
+            else
+                pass_run<1>(cur, have_cur, t, row_start, rows, xs, a.s);
+        }
+        if (worker)
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // 5. flag linear ti done for this workgroup; workers prefetch ti+1
+        if (ct == 0)
+            __hip_atomic_store(&flags[(size_t)ti * kPassMaxGrid + w], epoch, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         have_cur = false;
-        if (ti + 1 < n) {
-            const PassTask tn = tasks[ti + 1];
-            const PassShape sn = pass_shape<RMAX, U>(tn, G);
-            if ((int)blockIdx.x < sn.tiles && tn.K <= max_k) {
-                pass_load<RMAX, U>(cur, tn, sn, blockIdx.x, 0);
+        if (worker && ti + 1 < n) {
+            int rs, rw;
+            pass_range(tn, w, rs, rw);
+            if (rw > 0) {
+                if (tn.r == 2)
+                    pass_prefetch<2>(cur, tn, w);
+                else
+                    pass_prefetch<1>(cur, tn, w);
                 have_cur = true;
             }
         }
+        t = tn;
     }
 }
-
-constexpr int kPassRmax = 2;
-constexpr int kPassU = 4;
-constexpr int kPassSpinLimit = 1 << 21;
-constexpr int kPassWgPerCu = 2;
 
 // ------------------------------------------------------------------------
 // Host side
@@ -1591,9 +1733,56 @@ int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const*
     return BQD_OK;
 }
 
-size_t decode_pass_desc_bytes(int32_t n) { return n > 0 ? (size_t)n * sizeof(PassTask) : 0; }
+size_t decode_pass_desc_bytes(int32_t n)
+{
+    return n > 0 ? sizeof(PassHeader) + (size_t)n * sizeof(PassTask) : 0;
+}
 
-size_t decode_pass_sync_bytes(int32_t n) { return n > 0 ? (size_t)(n + 1) * sizeof(uint32_t) : 0; }
+size_t decode_pass_sync_bytes(int32_t n)
+{
+    return n > 0 ? (16 + (size_t)n * kPassMaxGrid) * sizeof(uint32_t) : 0;
+}
+
+// Grid of the pass on the current device: co-resident workgroups, at most
+// kPassWgPerCu per CU, for a given activation staging size.
+static int pass_grid(int max_k, int* grid)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pass, kPassThreads, pass_lds_bytes(max_k)) !=
+            hipSuccess ||
+        per_cu < 1)
+        return BQD_ERR_LAUNCH;
+    *grid = current_cus() * (per_cu < kPassWgPerCu ? per_cu : kPassWgPerCu);
+    return BQD_OK;
+}
+
+// Lanes per row and rows per lane group for one linear on a grid of G
+// workgroups: fewest loads per lane, plus a charge per pipeline step (small
+// linears then take one step, whose loads are all issued before the wait).
+static void pass_shape_host(int N, int C, int G, PassTask& t)
+{
+    const int rows_max = (N + G - 1) / G;
+    long best = -1;
+    for (int ls = 4; ls <= 6; ++ls) {
+        for (int r = 2; r >= 1; --r) {
+            const int L = 1 << ls, groups = kPassWorkers >> ls;
+            const int iters = (C + L - 1) / L;
+            const int batches = (rows_max + groups * r - 1) / (groups * r);
+            const int steps = (iters * r + kPassSlots - 1) / kPassSlots;
+            const long cost = (long)batches * r * iters + 4L * batches * steps;
+            if (best < 0 || cost < best) {
+                best = cost;
+                t.lshift = ls;
+                t.r = r;
+                t.iters = iters;
+                t.batches = batches;
+                t.steps = steps;
+            }
+        }
+    }
+    t.rows_base = N / G;
+    t.rows_extra = N % G;
+}
 
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
                        float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k)
@@ -1608,7 +1797,6 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
     if (desc_bytes < decode_pass_desc_bytes(n))
         return BQD_ERR_SHAPE;
     int kmax = 0;
-    PassTask* d = reinterpret_cast<PassTask*>(desc_host);
     for (int i = 0; i < n; ++i) {
         const bqd_linear_w4a8& l = lin[i];
         if (l.scale_kind != BQD_SCALE_ROW_F32)
@@ -1622,10 +1810,24 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         if (!aligned(l.wq, 16) || !aligned(x[i], 16) || !aligned(l.scales, 4) || !aligned(l.bias, 4) ||
             !aligned(y[i], 4))
             return BQD_ERR_ALIGN;
-        if (!(l.r == 0 || l.r == 1 || l.r == 2) ||
-            !(l.lanes_per_row == 0 || l.lanes_per_row == 16 || l.lanes_per_row == 32 || l.lanes_per_row == 64) ||
-            ((l.r == 0) != (l.lanes_per_row == 0)))
-            return BQD_ERR_CONFIG;
+        if (l.r != 0 || l.lanes_per_row != 0)
+            return BQD_ERR_CONFIG;  // the pass chooses its own work split
+        if (l.K > kPassMaxK)
+            return BQD_ERR_BOUND;
+        kmax = l.K > kmax ? l.K : kmax;
+    }
+    if ((rc = bqd_init()))
+        return rc;
+    int G = 0;
+    if ((rc = pass_grid(kmax, &G)))
+        return rc;
+    if (G > kPassMaxGrid)
+        return BQD_ERR_LAUNCH;
+    PassHeader h{n, G, kmax, 0};  // reserved = 0
+    std::memcpy(desc_host, &h, sizeof h);
+    PassTask* d = reinterpret_cast<PassTask*>(reinterpret_cast<char*>(desc_host) + sizeof(PassHeader));
+    for (int i = 0; i < n; ++i) {
+        const bqd_linear_w4a8& l = lin[i];
         PassTask t;
         std::memset(&t, 0, sizeof t);
         t.wq = reinterpret_cast<const u32x4*>(l.wq);
@@ -1634,12 +1836,10 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         t.x = x[i];
         t.y = y[i];
         t.N = l.N;
-        t.K = l.K;
+        t.C = l.K / 32;
         t.x_dtype = x_dtype == BQD_F16 ? X_F16 : X_F32;
-        t.L = l.lanes_per_row;
-        t.r = l.r;
+        pass_shape_host(t.N, t.C, G, t);
         std::memcpy(d + i, &t, sizeof t);
-        kmax = l.K > kmax ? l.K : kmax;
     }
     *max_k = kmax;
     return BQD_OK;
@@ -1655,23 +1855,25 @@ int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* s
     int rc = check_k(max_k);
     if (rc)
         return rc;
+    if (max_k > kPassMaxK)
+        return BQD_ERR_BOUND;
     if (spin_limit < 0)
         return BQD_ERR_CONFIG;
     if (!aligned(desc_dev, 16) || !aligned(sync_dev, 4))
         return BQD_ERR_ALIGN;
     if ((rc = bqd_init()))
         return rc;
-    auto kern = k_decode_pass<kPassRmax, kPassU>;
-    const size_t lds = (size_t)max_k;
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds) != hipSuccess || per_cu < 1)
-        return BQD_ERR_LAUNCH;
-    const int G = current_cus() * (per_cu < kPassWgPerCu ? per_cu : kPassWgPerCu);
-    const PassTask* tasks = reinterpret_cast<const PassTask*>(desc_dev);
+    int G = 0;
+    if ((rc = pass_grid(max_k, &G)))
+        return rc;
+    const PassHeader* hdr = reinterpret_cast<const PassHeader*>(desc_dev);
+    const PassTask* tasks =
+        reinterpret_cast<const PassTask*>(reinterpret_cast<const char*>(desc_dev) + sizeof(PassHeader));
     int spin = spin_limit ? spin_limit : kPassSpinLimit;
     int nn = n, mk = max_k;
-    void* args[] = {(void*)&tasks, (void*)&nn, (void*)&sync_dev, (void*)&mk, (void*)&spin};
-    if (hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(kThreads), args, (unsigned)lds,
+    void* args[] = {(void*)&hdr, (void*)&tasks, (void*)&nn, (void*)&mk, (void*)&sync_dev, (void*)&spin};
+    if (hipLaunchCooperativeKernel((const void*)k_decode_pass, dim3(G), dim3(kPassThreads), args,
+                                   (unsigned)pass_lds_bytes(max_k),
                                    (hipStream_t)stream) != hipSuccess)
         return BQD_ERR_LAUNCH;
     return launched();

@@ -46,9 +46,23 @@ def linear_weight_fp32(prefix: str, name: str, seed: int, device) -> torch.Tenso
     return torch.cat([I.normal(f"{prefix}/{p}/W", (n, K), 0.02, seed, device) for p, n in parts])
 
 
-def linear_bias(prefix: str, name: str, seed: int, device) -> torch.Tensor:
-    parts, _ = _qwen_part_shapes()[name]
-    return torch.cat([I.normal(f"{prefix}/{p}/b", n, 0.01, seed, device) for p, n in parts])
+def layer_biases(prefix: str, seed: int, device) -> Dict[str, torch.Tensor]:
+    """fp32 biases ~N(0, 0.01^2) of one layer's four fused linears, drawn in
+    one stream and split in row order (q, k, v | o | gate, up | down)."""
+    sizes = [(name, N) for name, N, _ in I.qwen_layer_linears()]
+    allb = I.normal(f"{prefix}/biases", sum(n for _, n in sizes), 0.01, seed, device)
+    return dict(zip([nm for nm, _ in sizes], torch.split(allb, [n for _, n in sizes])))
+
+
+def layer_inputs(prefix: str, seed: int, device) -> Dict[str, torch.Tensor]:
+    """Activations of one layer's four linears: N(0, 1) for QKV, O and gate/up
+    (one stream, split), silu(g)*u for the down projection."""
+    lin = I.qwen_layer_linears()
+    ks = [K for name, _, K in lin if name != "down"]
+    xs = torch.split(I.normal(f"{prefix}/x", sum(ks), 1.0, seed, device), ks)
+    out = dict(zip([name for name, _, _ in lin if name != "down"], [x.contiguous() for x in xs]))
+    out["down"] = I.swiglu_like(f"{prefix}/down/x", dict((n, k) for n, _, k in lin)["down"], seed, device)
+    return out
 
 
 def algorithmic_bytes_linear(N: int, K: int, bias: bool, x_bytes: int = 4) -> int:
@@ -59,7 +73,7 @@ def algorithmic_bytes_linear(N: int, K: int, bias: bool, x_bytes: int = 4) -> in
 
 class QwenW4A8Stream:
     def __init__(self, layers: int = 28, seed: int = 0, device="cuda", lm_head: bool = True,
-                 r: int = 0, lanes_per_row: int = 0, persistent: bool = False):
+                 r: int = 0, lanes_per_row: int = 0, persistent: bool = True):
         self.device = torch.device(device)
         self.layers = layers
         self.seed = seed
@@ -68,13 +82,15 @@ class QwenW4A8Stream:
         for l in range(layers):
             prefix = f"qwen/L{l}"
             descs, xs, ys = [], [], []
+            biases = layer_biases(prefix, seed, self.device)
+            inputs = layer_inputs(prefix, seed, self.device)
             for name, N, K in I.qwen_layer_linears():
                 W = linear_weight_fp32(prefix, name, seed, self.device)
                 assert W.shape == (N, K)
                 wq, sw = bqd.quantize_weights_int4_rowwise(W)
                 del W
-                b = linear_bias(prefix, name, seed, self.device)
-                x = I.linear_input(prefix, name, K, seed, self.device)
+                b = biases[name]
+                x = inputs[name]
                 y = torch.empty(N, dtype=torch.float32, device=self.device)
                 d = dict(layer=l, name=name, N=N, K=K, wq=wq, sw=sw, b=b, x=x, y=y, prefix=prefix)
                 self.linears.append(d)
@@ -96,10 +112,8 @@ class QwenW4A8Stream:
         self.persistent = persistent
         self.pass_ = None
         if persistent:
-            pr = r if r in (1, 2) else 0
-            pl = lanes_per_row if pr else 0
             self.pass_ = bqd.DecodePass(
-                [bqd.make_linear(d["wq"], d["sw"], d["b"], pr, pl) for d in self.linears],
+                [bqd.make_linear(d["wq"], d["sw"], d["b"]) for d in self.linears],
                 [d["x"] for d in self.linears], [d["y"] for d in self.linears], self.device)
         torch.cuda.synchronize(self.device)
 

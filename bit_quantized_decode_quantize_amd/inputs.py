@@ -86,7 +86,7 @@ def _uniform53(z: torch.Tensor) -> torch.Tensor:
     return (_lsr(z, 11).to(torch.float64) + 0.5) * (2.0 ** -53)
 
 
-_CHUNK = 1 << 24
+_CHUNK = 1 << 26
 
 
 def _normal_f64(key: int, start: int, count: int, device) -> torch.Tensor:

@@ -222,36 +222,40 @@ int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const*
 /* Most linears one pass may hold (a Qwen2-7B-shaped decoder has 113). */
 #define BQD_MAX_PASS_LINEARS 4096
 
-/* Bytes of the descriptor array decode_pass_encode writes for n linears. */
+/* Bytes of the descriptors decode_pass_encode writes for n linears. */
 size_t decode_pass_desc_bytes(int32_t n);
 
-/* Bytes of the synchronisation words of a pass over n linears: n completion
- * counters plus one error word.  The caller allocates them on the device,
- * zero-fills them once, and hands the same buffer to every pass over the
- * same descriptors; passes over one buffer must not overlap in time. */
+/* Bytes of the synchronisation words of a pass over n linears: an error
+ * word and one completion flag per linear and workgroup.
+ * The caller allocates them on the device, zero-fills them once, and hands
+ * the same buffer to every pass over the same descriptors; passes over one
+ * buffer must not overlap in time. */
 size_t decode_pass_sync_bytes(int32_t n);
 
-/* Host only.  Validates n per-row linears (bqd_linear_w4a8 with
- * BQD_SCALE_ROW_F32, as for layer_w4a8_forward; r in {0, 1, 2} and
- * lanes_per_row in {0, 16, 32, 64}, both 0 or both set) with their activation
- * x[i] (device, [K_i] of x_dtype) and output y[i] (device float [N_i]), and
- * serialises them into desc_host (host, decode_pass_desc_bytes(n) bytes).
- * *max_k receives the largest K.  The caller copies desc_host to device
- * memory unchanged (16-byte aligned) before decode_pass_w4a8 uses it. */
+/* Validates n per-row linears (bqd_linear_w4a8 with BQD_SCALE_ROW_F32 and
+ * r = lanes_per_row = 0: the pass chooses its own work split) with their
+ * activation x[i] (device, [K_i] of x_dtype) and output y[i] (device float
+ * [N_i], N_i > 0), and serialises them into desc_host (host,
+ * decode_pass_desc_bytes(n) bytes) for the current device: the work split
+ * is encoded for the grid the launch will use there.  *max_k receives the
+ * largest K.  The caller copies desc_host unchanged to 16-byte-aligned
+ * device memory before decode_pass_w4a8 reads it. */
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
                        float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k);
 
 /* One decode step over the n encoded linears in order, in one cooperative
  * launch: for each linear, the activation quantisation of quantize_act and
  * the GEMV of gemv_w4a8 (same codes, same y bits as linear_w4a8).  Linear
- * i+1 reads its activation only after every workgroup has finished and
- * published linear i (the decoder's data dependency); weights of linear i+1
- * are prefetched while waiting.  desc_dev (device) holds the encoded
- * descriptors; max_k is the value decode_pass_encode reported; sync_dev
- * (device) the zero-initialised words of decode_pass_sync_bytes(n).
- * spin_limit bounds each wait (0 = default, about 0.1 s); a wait that runs
- * out sets bit 0 of sync_dev[n] and proceeds, so the kernel always ends.
- * The caller reads sync_dev[n] to check it and clears it to reuse. */
+ * i+1 reads its activation only after every workgroup has finished linear
+ * i and its output stores have completed (the decoder's data dependency);
+ * weights of linear i+1 are prefetched while waiting.  desc_dev (device)
+ * holds the encoded descriptors; max_k is the value decode_pass_encode
+ * reported; sync_dev (device) the zero-initialised words of
+ * decode_pass_sync_bytes(n).  spin_limit bounds each wait (0 = default,
+ * about 0.1 s); a wait that runs out sets bit 0 of sync_dev[0] and
+ * proceeds, so the kernel always ends; bit 1 is set (and nothing computed)
+ * when the descriptors were encoded for another grid or another n.  The
+ * caller reads sync_dev[0] to check, and clears it to reuse. */
 int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev,
                      int32_t spin_limit, void* stream);
 

@@ -150,7 +150,7 @@ def test_decode_pass_encode_validates_and_serialises():
     L = _lib()
     n = 2
     nbytes = L.decode_pass_desc_bytes(n)
-    assert nbytes == 128 and L.decode_pass_sync_bytes(n) == 12
+    assert nbytes == 16 + 2 * 80 and L.decode_pass_sync_bytes(n) == (16 + 2 * 1024) * 4
     host = (C.c_uint8 * nbytes)()
     mk = C.c_int32(0)
     xs = (C.c_void_p * n)(P, P + 0x100)
@@ -162,21 +162,30 @@ def test_decode_pass_encode_validates_and_serialises():
                                     C.cast(host, C.c_void_p), nbytes, C.byref(mk))
 
     a = bqd.LinearW4A8(P, P + 0x400, 0, 100, 3584, 0, 0, 0)
-    b = bqd.LinearW4A8(P + 0x1000, P + 0x500, P + 0x600, 7, 18944, 0, 2, 64)
-    assert enc([a, b]) == OK and mk.value == 18944
-    raw = bytes(host)
-    import struct
-    f = struct.unpack("<5Q6i", raw[64:128])
-    assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, P + 0x100, P + 0x300)
-    assert f[5:10] == (7, 18944, 1, 64, 2)          # N, K, fp32 input, lanes, r
+    b = bqd.LinearW4A8(P + 0x1000, P + 0x500, P + 0x600, 7, 18944, 0, 0, 0)
     assert enc([a, b], nbytes=100) == SHAPE
     assert enc([a, b], dt=4) == DTYPE
     assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 1, 0, 0)]) == DTYPE       # group-32 scales
-    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 0, 4, 16)]) == CONFIG     # r above 2
-    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 0, 2, 0)]) == CONFIG      # r without lanes
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 0, 2, 16)]) == CONFIG     # the pass picks the split
     assert enc([a, bqd.LinearW4A8(P, P, 0, 0, 64, 0, 0, 0)]) == SHAPE       # N = 0
     assert enc([a, bqd.LinearW4A8(P4, P, 0, 7, 64, 0, 0, 0)]) == ALIGN
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 40, 0, 0, 0)]) == SHAPE       # K % 32
     assert enc([a, b], n=0) == SHAPE
+    rc = enc([a, b])                         # valid: encoding needs the device's grid
+    if not torch.cuda.is_available():
+        assert rc == DEVICE
+        return
+    assert rc == OK and mk.value == 18944
+    import struct
+    raw = bytes(host)
+    hn, grid, hk, reserved = struct.unpack("<4i", raw[:16])
+    assert (hn, hk, reserved) == (2, 18944, 0) and 0 < grid <= 1024
+    f = struct.unpack("<5Q10i", raw[16 + 80:16 + 160])
+    assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, P + 0x100, P + 0x300)
+    N, C_, base, extra, lshift, r, iters, batches, steps, xdt = f[5:]
+    assert (N, C_, base, extra, xdt) == (7, 592, 7 // grid, 7 % grid, 1)
+    assert lshift in (4, 5, 6) and r in (1, 2)
+    assert iters == -(-592 // (1 << lshift)) and steps == -(-iters * r // 8)
 
 
 def test_decode_pass_launch_validates_before_launch():

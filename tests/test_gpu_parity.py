@@ -343,7 +343,7 @@ def test_layer_forward_fused_rows_equal_separate_linears():
     three linears run on their row slices."""
     from bit_quantized_decode_quantize_amd import decode_stream as DS
     W = DS.linear_weight_fp32("gpu/layer", "qkv", 0, DEV)
-    b = DS.linear_bias("gpu/layer", "qkv", 0, DEV)
+    b = DS.layer_biases("gpu/layer", 0, DEV)["qkv"]
     x = I.normal("gpu/layer/x", 3584, 1.0, device=DEV)
     wq, sw = bqd.quantize_weights_int4_rowwise(W)
     y = torch.empty(4608, device=DEV)
@@ -355,12 +355,13 @@ def test_layer_forward_fused_rows_equal_separate_linears():
     assert torch.equal(y, torch.cat(parts))
 
 
-def test_qwen_layer_full_size_sampled():
-    """One Qwen2-7B-shaped layer at full size through layer_w4a8_forward, in
-    the launch configuration the bench times; 300 sampled rows per linear
+@pytest.mark.parametrize("persistent", [False, True])
+def test_qwen_layer_full_size_sampled(persistent):
+    """One Qwen2-7B-shaped layer at full size, through layer_w4a8_forward (one
+    launch per linear) or the persistent pass; 300 sampled rows per linear
     (plus the first and last) against the oracle."""
     from bit_quantized_decode_quantize_amd import decode_stream as DS
-    s = DS.QwenW4A8Stream(layers=1, lm_head=False, device=DEV)
+    s = DS.QwenW4A8Stream(layers=1, lm_head=False, device=DEV, persistent=persistent)
     s.step()
     sync()
     for d in s.linears:
@@ -382,7 +383,7 @@ def test_qwen_layer_full_size_sampled():
 PASS_SHAPES = [(4608, 3584), (3584, 3584), (300, 18944), (17, 64), (1, 32), (5000, 1536), (37888, 3584)]
 
 
-def _pass_fixture(dtype=torch.float32, cfg=(0, 0), tag="pass"):
+def _pass_fixture(dtype=torch.float32, tag="pass"):
     lins, xs, ys, parts = [], [], [], []
     for i, (N, K) in enumerate(PASS_SHAPES):
         W = I.normal(f"gpu/{tag}/{i}/W", (N, K), 0.02, device=DEV)
@@ -390,18 +391,16 @@ def _pass_fixture(dtype=torch.float32, cfg=(0, 0), tag="pass"):
         b = I.normal(f"gpu/{tag}/{i}/b", N, 0.01, device=DEV) if i % 2 == 0 else None
         x = I.normal(f"gpu/{tag}/{i}/x", K, 1.0, device=DEV, dtype=dtype)
         y = torch.full((N,), float("nan"), device=DEV)
-        lins.append(bqd.make_linear(wq, sw, b, cfg[0], cfg[1]))
+        lins.append(bqd.make_linear(wq, sw, b))
         xs.append(x)
         ys.append(y)
         parts.append((wq, sw, b, x))
     return lins, xs, ys, parts
 
 
-@pytest.mark.parametrize("dtype,cfg", [(torch.float32, (0, 0)), (torch.float16, (0, 0)),
-                                       (torch.float32, (1, 64)), (torch.float32, (2, 16)),
-                                       (torch.float32, (2, 32))])
-def test_decode_pass_equals_per_linear_launches(dtype, cfg):
-    lins, xs, ys, parts = _pass_fixture(dtype, cfg, f"pass{cfg}")
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_decode_pass_equals_per_linear_launches(dtype):
+    lins, xs, ys, parts = _pass_fixture(dtype, f"pass{dtype}")
     p = bqd.DecodePass(lins, xs, ys)
     ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
     for rep in range(3):                     # the counters carry over between passes
@@ -463,3 +462,25 @@ def test_qwen_stream_full_size_persistent_sampled():
         qxr, sxr, accr, y_r = O.linear_w4a8(wr, sr, br, npy(d["x"]))
         err = O.rel_err_rowwise(npy(d["y"][idx]), y_r, sr, sxr, accr, br)
         assert err.max() <= TOL, (k, err.max())
+
+
+def test_decode_pass_rejects_descriptors_for_another_grid():
+    """Descriptors encoded for another grid size are refused in the kernel
+    (error bit 1, nothing computed) instead of being misread."""
+    lins, xs, ys, parts = _pass_fixture(tag="passgrid")
+    p = bqd.DecodePass(lins, xs, ys)
+    grid = int(p.desc[4:8].cpu().view(torch.int32).item())
+    bad = torch.tensor([grid + 1], dtype=torch.int32).view(torch.uint8).to(p.desc.device)
+    good = p.desc[4:8].clone()
+    for y in ys:
+        y.fill_(float("nan"))
+    p.desc[4:8] = bad
+    p.run()
+    sync()
+    assert p.error_word() & 2
+    assert all(torch.isnan(y).all() for y in ys)
+    p.desc[4:8] = good
+    p.clear_error()
+    p.run()
+    sync()
+    assert p.error_word() == 0 and not any(torch.isnan(y).any() for y in ys)
