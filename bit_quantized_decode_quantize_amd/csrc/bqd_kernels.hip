@@ -887,7 +887,8 @@ constexpr int kPassSlots = 8;         // 16-byte chunks per lane per pipeline st
 constexpr int kPassMaxGrid = 1024;    // completion flags per linear
 constexpr int kPassSpinLimit = 1 << 21;
 constexpr int kPassWgPerCu = 1;
-constexpr int kPassMaxK = 24576;      // LDS: codes (K bytes) + fp32 activation (4K bytes)
+constexpr int kPassMaxK = BQD_MAX_PASS_K;  // LDS: codes (K bytes) + fp32 activation (4K bytes)
+static_assert(5 * kPassMaxK <= 160 * 1024, "pass activation must fit LDS");
 
 inline size_t pass_lds_bytes(int max_k) { return (size_t)((max_k + 15) & ~15) + 4 * (size_t)max_k; }
 

@@ -221,6 +221,9 @@ int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const*
 
 /* Most linears one pass may hold (a Qwen2-7B-shaped decoder has 113). */
 #define BQD_MAX_PASS_LINEARS 4096
+/* Largest K of a linear in a pass: a workgroup keeps the fp32 activation
+ * and its int8 codes in LDS (5 bytes per element of 160 KiB). */
+#define BQD_MAX_PASS_K 24576
 
 /* Bytes of the descriptors decode_pass_encode writes for n linears. */
 size_t decode_pass_desc_bytes(int32_t n);
@@ -237,9 +240,11 @@ size_t decode_pass_sync_bytes(int32_t n);
  * activation x[i] (device, [K_i] of x_dtype) and output y[i] (device float
  * [N_i], N_i > 0), and serialises them into desc_host (host,
  * decode_pass_desc_bytes(n) bytes) for the current device: the work split
- * is encoded for the grid the launch will use there.  *max_k receives the
- * largest K.  The caller copies desc_host unchanged to 16-byte-aligned
- * device memory before decode_pass_w4a8 reads it. */
+ * is encoded for the grid the launch will use there, so a device must be
+ * current (BQD_ERR_DEVICE otherwise).  *max_k receives the largest K.
+ * K_i % 32 == 0 and K_i <= BQD_MAX_PASS_K (BQD_ERR_BOUND otherwise).  The
+ * caller copies desc_host unchanged to 16-byte-aligned device memory
+ * before decode_pass_w4a8 reads it. */
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
                        float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k);
 
