@@ -1,12 +1,24 @@
-"""Decode-stream benchmark: one step = one token's pass over the Qwen2-7B-shaped
-28-layer W4A8 weight stream plus the int4 lm_head, all resident in HBM.
+"""Decode GEMV benchmark.  Prints one JSON line (rank 0, N=1).
 
-Each of the 113 linears (28 layers x {fused QKV, O, fused gate/up, down} +
-lm_head) is one launch of the library's fused kernel: per-token activation
-quantisation in the prologue, INT4 x INT8 dot products, int32 accumulation,
-fp32 epilogue.  Prints one JSON line (rank 0, N=1).
+Default workload (``--workload stream``): one step = one token's pass over
+the Qwen2-7B-shaped 28-layer W4A8 weight stream plus the int4 lm_head, all
+resident in HBM: 113 linears (28 layers x {fused QKV, O, fused gate/up, down}
++ lm_head), by default one launch of the persistent pass (``--per-linear``:
+one fused launch per linear).  Each linear quantises its activation per token
+in the prologue, takes INT4 x INT8 dot products into exact int32 and applies
+the fp32 epilogue.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Other workloads (each one JSON line of the same form):
+  single  one Q-projection linear [3584, 3584], 1 % outliers in x
+  layer   one decoder layer (fused QKV, O, fused gate/up, down)
+  gemma   35 Gemma-shaped group-32 layers (fp16 x) + the W8A16 lm_head
+  verify  the M-token verify GEMM over [18944, 3584] and [3584, 18944],
+          M in --verify-m (default 1,2,4,8,16)
+Weights that fit the Infinity Cache rotate through a >= 1 GB pool of copies.
+Per-linear launches are captured once into a HIP graph and replayed
+(``--eager``: launched from Python every step).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload ...]
 """
 import argparse
 import hashlib
@@ -22,6 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) for W4A8 decode GEMV; implied 28-layer tok/s"
 HBM_PEAK_GBS = 8000.0
+WORKLOADS = ("stream", "single", "layer", "gemma", "verify")
 
 
 def parse():
@@ -29,11 +42,17 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--layers", type=int, default=28)
+    p.add_argument("--workload", choices=WORKLOADS, default="stream")
+    p.add_argument("--layers", type=int, default=0, help="decoder layers (0 = the model's: 28 / 35)")
     p.add_argument("--r", type=int, default=0, help="rows per lane group (0 = automatic)")
     p.add_argument("--lanes", type=int, default=0, help="lanes per row (0 = automatic)")
     p.add_argument("--per-linear", action="store_true",
-                   help="one launch per linear instead of one persistent launch per step")
+                   help="stream / layer: one launch per linear instead of the persistent pass")
+    p.add_argument("--eager", action="store_true",
+                   help="launch per-linear kernels from Python each step instead of replaying "
+                        "them from a captured HIP graph")
+    p.add_argument("--verify-m", default="1,2,4,8,16")
+    p.add_argument("--impl", type=int, default=0, help="verify kernel: 0 automatic, 1 dot4, 2 MFMA")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the timed region, run one plain device copy of this many MiB "
                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -46,12 +65,12 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_pass_qwen2-7b-28L_tra
 KERNEL_SOURCE = os.path.join(ROOT, "bit_quantized_decode_quantize_amd", "csrc", "bqd_kernels.hip")
 
 
-def measured_traffic():
-    """HBM bytes per pass launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary (copy-calibrated), or None once the kernel source
-    differs from the one the counters were taken on."""
+def measured_traffic(summary=TRAFFIC_SUMMARY):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary (copy-calibrated), or None once the kernel source differs from
+    the one the counters were taken on."""
     try:
-        text = open(TRAFFIC_SUMMARY, encoding="utf-8").read()
+        text = open(summary, encoding="utf-8").read()
         sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
@@ -61,55 +80,80 @@ def measured_traffic():
     return int(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(stream, seconds):
-    """The C oracle, single-threaded on this host, over layer 0 of the same
-    stream (its four linears: activation quantisation + GEMV), repeated for
-    about ``seconds``; reported as algorithmic GB/s and implied tok/s."""
-    import numpy as np
-    import oracle as O
-    from bit_quantized_decode_quantize_amd import decode_stream as DS
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    work = []
-    for d in stream.linears[:4]:
-        rows = __import__("torch").arange(d["N"])
-        W = stream.fp32_rows(d, rows).cpu().numpy()
-        w, s = O.prepare_int4_rowwise(W)
-        del W
-        b = None if d["b"] is None else d["b"].cpu().numpy()
-        work.append((w, s, b, d["x"].cpu().numpy(), DS.algorithmic_bytes_linear(d["N"], d["K"], b is not None)))
-    sample_bytes = sum(wk[4] for wk in work)
+
+# --------------------------------------------------------------- timing ---
+def time_steps(step, steps, warmup, graph_steps=0):
+    """Mean ms per step over ``steps`` steps on the current stream, events
+    around the whole region.  graph_steps > 0: capture that many consecutive
+    steps into one HIP graph and replay it ceil(steps / graph_steps) times.
+    Returns (ms_per_step, steps actually timed)."""
+    import torch
+    st = torch.cuda.current_stream()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if graph_steps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(graph_steps):
+                step()
+        torch.cuda.synchronize()
+        g.replay()  # warm replay
+        torch.cuda.synchronize()
+        reps = max(1, -(-steps // graph_steps))
+        run, n = (lambda: g.replay()), reps * graph_steps
+        calls = reps
+    else:
+        run, n, calls = step, steps, steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(calls):
+        run()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n, n
+
+
+def roofline(achieved_gbs, kernel, avg_us, avg_bytes, traffic=None):
+    return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+            "avg_launch_us": round(avg_us, 3), "avg_algorithmic_bytes": int(avg_bytes)}
+
+
+def base_line(a, value, ms, steps, config, dtype="int8"):
+    return {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": dtype, "data": "synthetic", "config": config,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2)}
+
+
+def cpu_loop(fn, sample_bytes, seconds):
     reps, t0 = 0, time.perf_counter()
     while True:
-        for w, s, b, x, _ in work:
-            O.linear_w4a8(w, s, b, x)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    gbs = sample_bytes * reps / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 of the stream (fused QKV, O, gate/up, down: {sample_bytes} algorithmic bytes), "
-                      f"{reps} passes in {el:.1f} s, single-threaded C; implied tok/s over the full "
-                      f"stream {gbs * 1e9 / stream.bytes_per_step():.4f}"}
+            return sample_bytes * reps / el / 1e9, reps, el
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {a.gpus} requested); the path's sharding "
-              "is described in DESIGN.md", file=sys.stderr)
-        sys.exit(2)
+# ------------------------------------------------------------ workloads ---
+def run_stream(a, dev):
     import torch
     from bit_quantized_decode_quantize_amd import bqd
     from bit_quantized_decode_quantize_amd import decode_stream as DS
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    layers = a.layers or 28
     t0 = time.time()
-    s = DS.QwenW4A8Stream(layers=a.layers, device=dev, r=a.r, lanes_per_row=a.lanes,
+    s = DS.QwenW4A8Stream(layers=layers, device=dev, r=a.r, lanes_per_row=a.lanes,
                           persistent=not a.per_linear)
-    print(f"[bench] stream built: {len(s.linears)} linears, {s.weight_bytes() / 1e9:.3f} GB packed, "
-          f"{time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    log(f"stream built: {len(s.linears)} linears, {s.weight_bytes() / 1e9:.3f} GB packed, "
+        f"{time.time() - t0:.1f} s")
     st = torch.cuda.current_stream()
     if a.copy_calibration:
         src = torch.empty(a.copy_calibration << 18, dtype=torch.float32, device=dev).fill_(1.0)
@@ -117,23 +161,11 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(f"[bench] calibration copy: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written",
-              file=sys.stderr, flush=True)
+        log(f"calibration copy: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
         del src, dst
 
-    for _ in range(a.warmup):
-        s.step()
-    torch.cuda.synchronize()
-
-    # Timed region: K whole steps back to back on one stream.
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(st)
-    for _ in range(a.steps):
-        s.step()
-    e1.record(st)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / a.steps
+    graph_steps = 1 if ((not a.eager) and a.per_linear) else 0
+    ms, n = time_steps(s.step, a.steps, a.warmup, graph_steps)
     step_bytes = s.bytes_per_step()
     gbs = step_bytes / (ms * 1e-3) / 1e9
 
@@ -152,12 +184,12 @@ def main():
         if err:
             raise RuntimeError(f"decode pass reported a wait time-out (error word {err})")
         dur_us = [b0.elapsed_time(b1) * 1e3 for b0, b1 in evs]
-        avg_us = sum(dur_us) / len(dur_us)
-        avg_bytes = step_bytes
-        kernel = "k_decode_pass (persistent: whole token pass, 113 linears, one launch)"
+        avg_us, avg_bytes = sum(dur_us) / len(dur_us), step_bytes
+        kernel = f"k_decode_pass (persistent: whole token pass, {len(s.linears)} linears, one launch)"
+        traffic = measured_traffic() if layers == 28 else None
     else:
-        # Dominant kernel: the gate/up linears + lm_head (most of the bytes).
-        # Second pass of the same K steps, each such launch bracketed by events.
+        # Dominant kernel: the gate/up linears + lm_head (most of the bytes),
+        # each launch bracketed by events in a second eager pass.
         dom = [i for i, d in enumerate(s.linears) if d["name"] in ("gate_up", "lm_head")]
         evs = []
         for _ in range(a.steps):
@@ -174,32 +206,209 @@ def main():
         dur_us = [b0.elapsed_time(b1) * 1e3 for b0, b1, _ in evs]
         dom_bytes = [DS.algorithmic_bytes_linear(s.linears[i]["N"], s.linears[i]["K"], s.linears[i]["b"] is not None)
                      for _, _, i in evs]
-        avg_us = sum(dur_us) / len(dur_us)
-        avg_bytes = sum(dom_bytes) / len(dom_bytes)
+        avg_us, avg_bytes = sum(dur_us) / len(dur_us), sum(dom_bytes) / len(dom_bytes)
         kernel = "k_gemv_w4a8 (fused gate/up linears and lm_head, one launch per linear)"
+        traffic = None
     achieved = avg_bytes / (avg_us * 1e-6) / 1e9
-
-    out = {
-        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8", "data": "synthetic",
-        "config": {"workload": "qwen2-7b-shaped 28-layer W4A8 decode weight stream + int4 lm_head "
-                               "(per-row scales, fused QKV and gate/up, fused act-quant)",
-                   "launch": "per-linear" if a.per_linear else "persistent pass",
-                   "layers": a.layers, "hidden": 3584, "kv_dim": 512, "intermediate": 18944,
-                   "vocab": 152064, "global_batch": 1, "parallelism": "none",
-                   "bytes_per_step": step_bytes, "packed_weight_bytes": s.weight_bytes()},
-        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "tok_per_s": round(1e3 / ms, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if s.persistent else None,
-                     "kernel": kernel,
-                     "avg_launch_us": round(avg_us, 3), "avg_algorithmic_bytes": int(avg_bytes)},
-    }
+    launch = "persistent pass" if s.persistent else ("per-linear, HIP graph" if graph_steps else "per-linear")
+    out = base_line(a, gbs, ms, n, {
+        "workload": f"qwen2-7b-shaped {layers}-layer W4A8 decode weight stream + int4 lm_head "
+                    "(per-row scales, fused QKV and gate/up, fused act-quant)",
+        "launch": launch, "layers": layers, "hidden": 3584, "kv_dim": 512, "intermediate": 18944,
+        "vocab": 152064, "global_batch": 1, "parallelism": "none",
+        "bytes_per_step": step_bytes, "packed_weight_bytes": s.weight_bytes()})
+    out["tok_per_s"] = round(1e3 / ms, 2)
+    out["us_per_gemv"] = round(ms * 1e3 / len(s.linears), 3)
+    out["roofline"] = roofline(achieved, kernel, avg_us, avg_bytes, traffic)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(s, a.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_stream(s, a.cpu_seconds)
+    return out
+
+
+def cpu_baseline_stream(stream, seconds):
+    """The C oracle, single-threaded on this host, over layer 0 of the same
+    stream (its four linears: activation quantisation + GEMV), repeated for
+    about ``seconds``; reported as algorithmic GB/s and implied tok/s."""
+    import torch
+    import oracle as O
+    from bit_quantized_decode_quantize_amd import decode_stream as DS
+
+    work = []
+    for d in stream.linears[:4]:
+        W = stream.fp32_rows(d, torch.arange(d["N"])).cpu().numpy()
+        w, s = O.prepare_int4_rowwise(W)
+        del W
+        b = None if d["b"] is None else d["b"].cpu().numpy()
+        work.append((w, s, b, d["x"].cpu().numpy(), DS.algorithmic_bytes_linear(d["N"], d["K"], b is not None)))
+    sample_bytes = sum(wk[4] for wk in work)
+
+    def once():
+        for w, s, b, x, _ in work:
+            O.linear_w4a8(w, s, b, x)
+    gbs, reps, el = cpu_loop(once, sample_bytes, seconds)
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0 of the stream (fused QKV, O, gate/up, down: {sample_bytes} algorithmic bytes), "
+                      f"{reps} passes in {el:.1f} s, single-threaded C; implied tok/s over the full "
+                      f"stream {gbs * 1e9 / stream.bytes_per_step():.4f}"}
+
+
+def run_single(a, dev):
+    from bit_quantized_decode_quantize_amd import workloads as WL
+    from bit_quantized_decode_quantize_amd import inputs as I
+
+    w = WL.SingleGemvPool(device=dev)
+    log(f"single GEMV pool: {w.copies} copies of {w.weight_bytes()} B")
+    ms, n = time_steps(w.step, a.steps, a.warmup, w.copies if (not a.eager) else 0)
+    gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
+    out = base_line(a, gbs, ms, n, {
+        "workload": "single W4A8 linear (Q projection) [3584, 3584], per-row int4, x fp32 with 1% x20 "
+                    "outliers, fused act-quant", "launch": "HIP graph" if (not a.eager) else "eager",
+        "N": w.N, "K": w.K, "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
+    out["us_per_gemv"] = round(ms * 1e3, 3)
+    out["roofline"] = roofline(gbs, "k_gemv_w4a8 (fused linear, one launch per step)", ms * 1e3,
+                               w.bytes_per_step())
+    if not a.no_cpu_baseline:
+        import oracle as O
+        d = I.single_gemv_inputs(0, "cpu")
+        wq, sw = O.prepare_int4_rowwise(d["W"].numpy())
+        x, b = d["x"].numpy(), d["b"].numpy()
+        g, reps, el = cpu_loop(lambda: O.linear_w4a8(wq, sw, b, x), w.bytes_per_step(), a.cpu_seconds)
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the same linear, {reps} calls in {el:.1f} s, single-threaded C"}
+    return out
+
+
+def run_layer(a, dev):
+    from bit_quantized_decode_quantize_amd import workloads as WL
+
+    w = WL.LayerPool(device=dev, persistent=not a.per_linear)
+    log(f"layer pool: {w.copies} copies of {w.weight_bytes()} B")
+    if w.persistent:
+        ms_call, n = time_steps(w.step, max(1, a.steps // w.copies), a.warmup)
+        ms, n = ms_call / w.steps_per_call, n * w.steps_per_call
+        kernel = f"k_decode_pass (persistent: {w.copies} layers = {4 * w.copies} linears per launch)"
+        avg_us, avg_bytes = ms_call * 1e3, w.bytes_per_step() * w.steps_per_call
+    else:
+        ms, n = time_steps(w.step, a.steps, a.warmup, w.copies if (not a.eager) else 0)
+        kernel = "k_gemv_w4a8 (4 fused linears per layer, one launch each)"
+        avg_us, avg_bytes = ms * 1e3 / 4, w.bytes_per_step() / 4
+    gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
+    launch = "persistent pass" if w.persistent else ("per-linear, HIP graph" if (not a.eager) else "per-linear")
+    out = base_line(a, gbs, ms, n, {
+        "workload": "one qwen2-7b-shaped decoder layer: fused QKV [4608,3584], O [3584,3584], fused gate/up "
+                    "[37888,3584], down [3584,18944], per-row int4, fused act-quant",
+        "launch": launch, "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
+    out["us_per_layer"] = round(ms * 1e3, 3)
+    out["implied_28_layer_gemv_us"] = round(28 * ms * 1e3, 1)
+    out["roofline"] = roofline(avg_bytes / (avg_us * 1e-6) / 1e9, kernel, avg_us, avg_bytes)
+    if not a.no_cpu_baseline:
+        import oracle as O
+        from bit_quantized_decode_quantize_amd import decode_stream as DS
+        work = []
+        for e in w.layers[0]:
+            W = DS.linear_weight_fp32("qwen/L0", e["name"], 0, dev).cpu().numpy()
+            wq, sw = O.prepare_int4_rowwise(W)
+            del W
+            work.append((wq, sw, e["b"].cpu().numpy(), e["x"].cpu().numpy()))
+        g, reps, el = cpu_loop(lambda: [O.linear_w4a8(*t) for t in work], w.bytes_per_step(), a.cpu_seconds)
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the same layer, {reps} passes in {el:.1f} s, single-threaded C"}
+    return out
+
+
+def run_gemma(a, dev):
+    from bit_quantized_decode_quantize_amd import workloads as WL
+    from bit_quantized_decode_quantize_amd import inputs as I
+
+    layers = a.layers or 35
+    t0 = time.time()
+    w = WL.GemmaG32Stream(layers=layers, device=dev)
+    log(f"gemma stream built: {w.launches_per_step} launches, {w.weight_bytes() / 1e9:.3f} GB, "
+        f"{time.time() - t0:.1f} s")
+    ms, n = time_steps(w.step, a.steps, a.warmup, 1 if (not a.eager) else 0)
+    gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
+    # lm_head alone (the largest single matrix), back to back.
+    ms_head, _ = time_steps(w.lm_head, max(20, a.steps), 2, 0)
+    head_bytes = WL.bytes_w8a16(*w.head_NK)
+    out = base_line(a, gbs, ms, n, {
+        "workload": f"gemma-shaped {layers}-layer Q4_0-style group-32 W4A8 stream (fp16 x) + W8A16 lm_head "
+                    "[262144,1536] (int8 in [-32,31], fp16 group-32 scales)",
+        "launch": "per-linear, HIP graph" if (not a.eager) else "per-linear", "layers": layers,
+        "bytes_per_step": w.bytes_per_step(), "weight_bytes": w.weight_bytes()}, dtype="int8+fp16")
+    out["tok_per_s"] = round(1e3 / ms, 2)
+    out["us_per_gemv"] = round(ms * 1e3 / w.launches_per_step, 3)
+    out["lm_head"] = {"us": round(ms_head * 1e3, 2), "GB/s": round(head_bytes / (ms_head * 1e-3) / 1e9, 1)}
+    out["roofline"] = roofline(head_bytes / (ms_head * 1e-3) / 1e9,
+                               "k_gemv_w8a16_g32 (lm_head, largest single launch)", ms_head * 1e3, head_bytes)
+    if not a.no_cpu_baseline:
+        import oracle as O
+        work = []
+        for d in w.linears[:4]:
+            W = I.normal(f"gemma/L0/{d['name']}/W", (d["N"], d["K"]), 0.02, 0, dev).cpu().numpy()
+            wq, s16 = O.prepare_int4_group32(W)
+            del W
+            work.append((wq, s16, None, d["x"].cpu().numpy()))
+        sample = sum(WL.bytes_group32_linear(d["N"], d["K"], False) for d in w.linears[:4])
+        g, reps, el = cpu_loop(lambda: [O.linear_w4a8_group32(*t) for t in work], sample, a.cpu_seconds)
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"layer 0 of the stream (4 group-32 linears, {sample} B), {reps} "
+                                         f"passes in {el:.1f} s, single-threaded C"}
+    return out
+
+
+def run_verify(a, dev):
+    import torch
+    from bit_quantized_decode_quantize_amd import workloads as WL
+
+    ms_list = [int(m) for m in a.verify_m.split(",")]
+    sweep = []
+    for N, K in ((18944, 3584), (3584, 18944)):
+        for M in ms_list:
+            w = WL.VerifyPool(N, K, M, device=dev, impl=a.impl)
+            ms, n = time_steps(w.step, max(a.steps, 2 * w.copies), a.warmup, w.copies if (not a.eager) else 0)
+            sweep.append({"N": N, "K": K, "M": M, "us": round(ms * 1e3, 3),
+                          "GB/s": round(w.bytes_per_step() / (ms * 1e-3) / 1e9, 1),
+                          "Tops": round(w.int_ops_per_step() / (ms * 1e-3) / 1e12, 2),
+                          "rotation_copies": w.copies, "steps": n})
+            log(f"verify {N}x{K} M={M}: {sweep[-1]}")
+            del w
+            torch.cuda.empty_cache()
+    last = max((r for r in sweep if r["N"] == 18944), key=lambda r: r["M"])
+    ms = last["us"] * 1e-3
+    out = base_line(a, last["GB/s"], ms, last["steps"], {
+        "workload": "M-token verify GEMM, per-row int4 weights [18944,3584] and [3584,18944], int8 X [M,K] "
+                    "(per-token scales), bias", "impl": a.impl, "M": ms_list})
+    out["sweep"] = sweep
+    wl_bytes = WL.bytes_verify(last["M"], 18944, 3584)
+    out["roofline"] = roofline(last["GB/s"], f"k_verify_w4a8 (M={last['M']}, [18944,3584])", last["us"], wl_bytes)
+    if not a.no_cpu_baseline:
+        import oracle as O
+        from bit_quantized_decode_quantize_amd import inputs as I
+        N, K, M = 18944, 3584, last["M"]
+        W = I.normal(f"verify/{N}x{K}/W", (N, K), 0.02, 0, dev).cpu().numpy()
+        wq, sw = O.prepare_int4_rowwise(W)
+        del W
+        b = I.normal(f"verify/{N}x{K}/b", N, 0.01, 0, dev).cpu().numpy()
+        X = I.normal(f"verify/{N}x{K}/X", (M, K), 1.0, 0, dev).cpu().numpy()
+        qx, sx = O.quantize_act(X)
+        g, reps, el = cpu_loop(lambda: O.gemm_w4a8_verify(wq, sw, b, qx, sx), wl_bytes, a.cpu_seconds)
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"verify [18944,3584] at M={M}, {reps} calls in {el:.1f} s, "
+                                         "single-threaded C"}
+    return out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {a.gpus} requested); the path's sharding "
+              "is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    out = {"stream": run_stream, "single": run_single, "layer": run_layer, "gemma": run_gemma,
+           "verify": run_verify}[a.workload](a, dev)
     print(json.dumps(out), flush=True)
 
 
