@@ -38,6 +38,7 @@ namespace {
 constexpr int kThreads = 256;          // 4 waves per workgroup
 constexpr int kWave = 64;
 constexpr int kLdsBytes = 65536;       // activation staging limit per workgroup
+constexpr int kLdsMaxBytes = 160 * 1024;  // LDS of one CU (gfx950)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -827,6 +828,148 @@ __global__ __launch_bounds__(kThreads) void k_verify_w4a8(
                             acc_out[(size_t)m * N + row] = acc[m][r];
                         y[(size_t)m * N + row] = fmaf(swr * sx[m], (float)acc[m][r], b);
                     }
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// M-token verify GEMM on the matrix cores.
+//   v_mfma_i32_16x16x64_i8 computes D[i][j] += sum over 4 lane groups g and
+//   16 bytes t of A_lane(i + 16g)[t] * B_lane(j + 16g)[t]; lane l receives
+//   D[4*(l/16) + e][l % 16], e = 0..3.  A is a 16-row weight tile (lane l:
+//   row l % 16), B the 16 token columns (lane l: token l % 16, zeros past
+//   M); both take, per lane, the same 16 code positions.  A lane loads one
+//   16-byte chunk (32 codes) of its row and feeds two MFMAs: words x, y as
+//   [lo16(x) hi16(x) lo16(y) hi16(y)] against the staged activation chunk
+//   half [A0 B0 A1 B1], then words z, w against [A2 B2 A3 B3] -- the pairing
+//   of dot_chunk16, so the int32 result is 16 * acc exactly.
+//   The 4 lane groups of a wave take 4 consecutive chunks of each of 16 rows
+//   (64 contiguous bytes per row per load).  SPLIT consecutive waves share
+//   a 16-row tile's K range and add their exact partials through LDS
+//   (SPLIT = 1: each wave owns a tile).  The M tokens'
+//   codes are staged per K segment in LDS; weight loads run U chunks ahead
+//   of the MFMAs.
+// ------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 mfma_chunk(u32x4 w, u32x4 xa, u32x4 xb, i32x4 acc)
+{
+    const i32x4 a0 = {lo16(w.x), hi16(w.x), lo16(w.y), hi16(w.y)};
+    const i32x4 a1 = {lo16(w.z), hi16(w.z), lo16(w.w), hi16(w.w)};
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, __builtin_bit_cast(i32x4, xa), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, __builtin_bit_cast(i32x4, xb), acc, 0, 0, 0);
+    return acc;
+}
+
+template <int U>
+__device__ __forceinline__ void load_quads(u32x4 (&buf)[U], const u32x4* __restrict__ wrow, int c0,
+                                           int nc, int q, int q1, int g)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = 4 * (q + u) + g;
+        buf[u] = (q + u < q1 && c < nc) ? wrow[c0 + c] : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int SPLIT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
+    const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int M, int N, int C, int SEGC)
+{
+    // Staged codes of the M tokens: token m's chunk c at xs[m * TS + 2c] and
+    // [.. + 1]; the 16-byte pad per token row spreads the 16 token columns of
+    // one read over the LDS banks.
+    extern __shared__ u32x4 xs[];
+    __shared__ i32x4 part[WAVES][kWave];
+    constexpr int U = 8;
+    constexpr int NT = WAVES * kWave;
+    constexpr int kStageBatch = WAVES > 8 ? 4 : 8;  // staging loads in flight per thread
+    constexpr int TPW = WAVES / SPLIT;  // row tiles per workgroup
+    const int TS = 2 * SEGC + 1;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int g = lane >> 4, col = lane & 15;
+    const bool tok = col < M;           // lanes past M feed zero columns
+    const int xrow = (tok ? col : 0) * TS;
+    const int tiles = (N + 15) >> 4;
+    const int groups = (tiles + TPW - 1) / TPW;
+    const int K = 32 * C;
+
+    for (int grp = blockIdx.x; grp < groups; grp += gridDim.x) {
+        const int tile = grp * TPW + wave / SPLIT;
+        const int sub = wave % SPLIT;
+        const u32x4* wrow = wq + (size_t)min(tile * 16 + col, N - 1) * C;
+        i32x4 acc = {0, 0, 0, 0};
+        for (int c0 = 0; c0 < C; c0 += SEGC) {
+            const int nc = min(SEGC, C - c0);
+            const int nq = (nc + 3) >> 2;
+            const int q0 = sub * nq / SPLIT, q1 = (sub + 1) * nq / SPLIT;
+            u32x4 cur[U];
+            load_quads<U>(cur, wrow, c0, nc, q0, q1, g);  // overlaps the staging
+            __syncthreads();                              // readers of the last segment are done
+            const int nh = 2 * nc;                        // 16-code halves per token
+            for (int i0 = threadIdx.x; i0 < M * nh; i0 += kStageBatch * NT) {
+                u32x4 v[kStageBatch];                     // all loads in flight, then the stores
+#pragma unroll
+                for (int j = 0; j < kStageBatch; ++j) {
+                    const int i = i0 + j * NT;
+                    v[j] = u32x4{0u, 0u, 0u, 0u};
+                    if (i < M * nh)
+                        v[j] = reinterpret_cast<const u32x4*>(qx + (size_t)(i / nh) * K)[2 * c0 + i % nh];
+                }
+#pragma unroll
+                for (int j = 0; j < kStageBatch; ++j) {
+                    const int i = i0 + j * NT;
+                    if (i < M * nh)
+                        xs[(i / nh) * TS + i % nh] = u32x4{perm_even(v[j].x, v[j].y), perm_odd(v[j].x, v[j].y),
+                                                           perm_even(v[j].z, v[j].w), perm_odd(v[j].z, v[j].w)};
+                }
+            }
+            __syncthreads();
+            for (int q = q0; q < q1; q += U) {
+                u32x4 nxt[U];
+                const bool more = q + U < q1;  // uniform across the wave
+                if (more)
+                    load_quads<U>(nxt, wrow, c0, nc, q + U, q1, g);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (q + u < q1) {
+                        const int c = min(4 * (q + u) + g, nc - 1);
+                        u32x4 xa = xs[xrow + 2 * c], xb = xs[xrow + 2 * c + 1];
+                        if (!tok)
+                            xa = xb = u32x4{0u, 0u, 0u, 0u};
+                        acc = mfma_chunk(cur[u], xa, xb, acc);
+                    }
+                }
+                if (more) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        cur[u] = nxt[u];
+                }
+            }
+        }
+        if (SPLIT > 1) {  // waves wave - sub .. wave - sub + SPLIT - 1 share a tile
+            part[wave][lane] = acc;
+            __syncthreads();
+            if (sub == 0) {
+#pragma unroll
+                for (int s2 = 1; s2 < SPLIT; ++s2)
+                    acc += part[wave + s2][lane];
+            }
+            __syncthreads();
+        }
+        if (sub == 0 && tok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = tile * 16 + 4 * g + e;
+                if (row < N) {
+                    const int a = acc[e] >> 4;
+                    if (acc_out)
+                        acc_out[(size_t)col * N + row] = a;
+                    y[(size_t)col * N + row] = fmaf(sw[row] * sx[col], (float)a, bias ? bias[row] : 0.0f);
                 }
             }
         }
@@ -1655,7 +1798,7 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
         return rc;
     if (M > BQD_MAX_TOKENS)
         return BQD_ERR_BOUND;
-    if (impl != 0 && impl != 1)
+    if (impl < 0 || impl > 2)
         return BQD_ERR_CONFIG;
     if (M == 0 || N == 0)
         return BQD_OK;
@@ -1667,6 +1810,51 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
     if ((rc = bqd_init()))
         return rc;
     const int C = K / 32;
+    hipStream_t st = (hipStream_t)stream;
+    const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+    if (impl == 0) {
+        // One token is the decode GEMV; from two tokens on the matrix cores
+        // beat the dot-product kernel on both verify shapes (measured).
+        if (M == 1)
+            return gemv_w4a8(wq, sw, bias, qx, sx, y, acc, N, K, 0, 0, stream);
+        impl = 2;
+    }
+    if (impl == 2) {
+        // Matrix cores, 16-row tiles x 16 token columns.  The smallest K split
+        // over waves that still gives about 8 waves per CU (each wave's chain
+        // of dependent weight steps shortens as the split grows); with more
+        // than 8 tokens and at least 4 tiles per CU, 4 waves per CU (every
+        // workgroup stages all tokens' codes: fewer, larger workgroups).  A
+        // workgroup holds max(4, split) waves.
+        const long long tiles = (N + 15) / 16;
+        const long long cus = current_cus();
+        const long long want = (M > 8 && tiles >= 4 * cus ? 4 : 8) * cus;
+        int split = 16;
+        for (int sp = 1; sp < 16; sp *= 2)
+            if (tiles * sp >= want) {
+                split = sp;
+                break;
+            }
+        const int waves = split < 4 ? 4 : split;
+        const long long groups = (tiles + waves / split - 1) / (waves / split);
+        // One workgroup per CU at most: stage longer segments (fewer barriers).
+        const int budget = groups <= current_cus() ? kLdsMaxBytes - (waves + 2) * 1024 : kLdsBytes;
+        int segc = (budget / M - 16) / 32;  // chunks per staged segment
+        if (segc > C)
+            segc = C;
+        const size_t lds = (size_t)M * (32 * segc + 16);
+        const dim3 grid(grid_for(groups)), block(waves * kWave);
+#define BQD_MFMA_CASE(SP, WV)                                                                      \
+    if (split == SP) {                                                                             \
+        hipLaunchKernelGGL((k_verify_mfma<SP, WV>), grid, block, lds, st, w, sw, bias, qx, sx, y, acc, \
+                           M, N, C, segc);                                                         \
+        return launched();                                                                         \
+    }
+        BQD_MFMA_CASE(1, 4) BQD_MFMA_CASE(2, 4) BQD_MFMA_CASE(4, 4) BQD_MFMA_CASE(8, 8)
+        BQD_MFMA_CASE(16, 16)
+#undef BQD_MFMA_CASE
+        return BQD_ERR_CONFIG;
+    }
     const int MT = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
     constexpr int L = 16, R = 2;
     // LDS holds MT tokens x SEGC chunks x 32 bytes; SEGC a multiple of L.
@@ -1677,8 +1865,6 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
     const size_t lds = (size_t)MT * segc * 32;
     const int rows = (kThreads / L) * R;
     const dim3 grid(grid_for((N + rows - 1) / rows)), block(kThreads);
-    const u32x4* w = reinterpret_cast<const u32x4*>(wq);
-    hipStream_t st = (hipStream_t)stream;
 #define BQD_VER_CASE(MM)                                                                          \
     if (MT == MM) {                                                                               \
         hipLaunchKernelGGL((k_verify_w4a8<MM, R, L>), grid, block, lds, st, w, sw, bias, qx, sx, y, \

@@ -188,7 +188,10 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
  *   acc[m,j] = sum_i q^W[j,i] * qx[m,i],  y[m,j] = (sw[j] * sx[m]) * acc[m,j] + bias[j]
  * qx (device) int8 [M, K]; sx (device) float [M]; y (device) float [M, N];
  * acc (device) int32 [M, N] or NULL.  1 <= M <= BQD_MAX_TOKENS.
- * impl: 0 automatic, 1 integer dot-product kernel. */
+ * impl: 1 integer dot-product kernel (v_dot4_i32_i8); 2 matrix-core
+ * kernel (v_mfma_i32_16x16x64_i8, 16 token columns); 0 automatic: M = 1
+ * runs gemv_w4a8's kernel, M >= 2 the matrix-core kernel.  Every impl gives
+ * the same acc and y bits. */
 int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias,
                      const int8_t* qx, const float* sx, float* y, int32_t* acc,
                      int32_t M, int32_t N, int32_t K, int32_t impl, void* stream);

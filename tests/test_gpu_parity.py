@@ -317,13 +317,17 @@ def test_gemv_w8a16_lm_head_codes_from_weights():
 
 
 # -------------------------------------------------------------- verify --
+@pytest.mark.parametrize("impl", [0, 1, 2])
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16])
-@pytest.mark.parametrize("N,K", [(200, 3584), (150, 18944), (33, 64)])
-def test_gemm_w4a8_verify(M, N, K):
+@pytest.mark.parametrize("N,K", [(200, 3584), (150, 18944), (33, 64), (70, 96)])
+def test_gemm_w4a8_verify(M, N, K, impl):
+    """impl 1: dot-product kernel; impl 2: matrix cores (K split over 16
+    waves here: few rows; K = 64 / 96 leave lane groups without a chunk);
+    impl 0: automatic (the GEMV kernel for one token)."""
     w, _, sw, b, _ = _rand_gemv(N, K, f"ver/{N}/{K}")
     X = I.normal(f"gpu/ver/{M}/{K}/X", (M, K), 1.0, device=DEV)
     qx, sx = bqd.quantize_act(X)
-    y, acc = bqd.gemm_w4a8_verify(w, sw, b, qx, sx, acc=True)
+    y, acc = bqd.gemm_w4a8_verify(w, sw, b, qx, sx, acc=True, impl=impl)
     sync()
     acc_r, y_r = O.gemm_w4a8_verify(u32(w), npy(sw), npy(b), npy(qx), npy(sx))
     assert np.array_equal(npy(acc), acc_r)
@@ -335,6 +339,28 @@ def test_gemm_w4a8_verify(M, N, K):
         y1 = bqd.gemv_w4a8(w, sw, b, qx[m].contiguous(), sx[m:m + 1].contiguous())
         sync()
         assert torch.equal(y1, y[m])
+
+
+@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("N,K", [(32770, 64), (16400, 256), (8200, 128), (4100, 160)])
+def test_gemm_w4a8_verify_mfma_row_tilings(M, N, K):
+    """Matrix-core verify on a 256-CU device: one wave per 16-row tile
+    (N = 32770), 2, 4 and 8 waves per tile (N = 16400, 8200, 4100; the small
+    shapes of the test above take 16); ragged last tile.  Bit-exact acc
+    against the oracle, y within tolerance, y identical to the dot-product
+    kernel."""
+    w, _, sw, b, _ = _rand_gemv(N, K, f"vermf/{N}/{K}")
+    X = I.normal(f"gpu/vermf/{M}/{K}/X", (M, K), 1.0, device=DEV)
+    qx, sx = bqd.quantize_act(X)
+    y, acc = bqd.gemm_w4a8_verify(w, sw, b, qx, sx, acc=True, impl=2)
+    y1 = bqd.gemm_w4a8_verify(w, sw, b, qx, sx, impl=1)
+    sync()
+    acc_r, y_r = O.gemm_w4a8_verify(u32(w), npy(sw), npy(b), npy(qx), npy(sx))
+    assert np.array_equal(npy(acc), acc_r)
+    for m in range(M):
+        err = O.rel_err_rowwise(npy(y)[m], y_r[m], npy(sw), npy(sx)[m], acc_r[m], npy(b))
+        assert err.max() <= TOL
+    assert torch.equal(y, y1)
 
 
 # -------------------------------------------------------- layer launcher --
