@@ -1047,9 +1047,12 @@ __device__ __forceinline__ u32x4 ld_stream(const BQD_GLOBAL u32x4* p)
     return __builtin_nontemporal_load(p);
 }
 
+// Loads step j of row batch b into buf; with the first step of a batch, lane
+// rr of each lane group also loads the scale and bias of the group's row rr
+// (the epilogue's operands arrive with the weights, not after them).
 template <int R>
-__device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], const PassTask& t, int row_start,
-                                          int rows, int b, int j)
+__device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], float& esw, float& eb, const PassTask& t,
+                                          int row_start, int rows, int b, int j)
 {
     constexpr int U = kPassSlots / R;
     const int L = 1 << t.lshift;
@@ -1072,13 +1075,19 @@ __device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], const PassTa
         for (int rr = 0; rr < R; ++rr)
             buf[u * R + rr] = (ok && vr[rr]) ? ld_stream(wrow[rr] + c) : u32x4{0u, 0u, 0u, 0u};
     }
+    if (j == 0) {
+        const int rl = (b * groups + grp) * R + lane;
+        const bool own = lane < R && rl < rows;
+        esw = own ? gptr(t.sw)[row_start + rl] : 0.0f;
+        eb = (own && t.bias) ? gptr(t.bias)[row_start + rl] : 0.0f;
+    }
 }
 
 // One linear's share of this workgroup: batches of rows, each streamed in
 // steps with the next step's loads in flight during the current step.
 template <int R>
-__device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], bool have_cur, const PassTask& t,
-                                         int row_start, int rows, const u32x4* xs, float sx)
+__device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, float& eb, bool have_cur,
+                                         const PassTask& t, int row_start, int rows, const u32x4* xs, float sx)
 {
     constexpr int U = kPassSlots / R;
     const int L = 1 << t.lshift;
@@ -1086,7 +1095,8 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], bool have_cur
     const int groups = kPassWorkers >> t.lshift;
     const int grp = threadIdx.x >> t.lshift;
     if (!have_cur)
-        pass_load<R>(cur, t, row_start, rows, 0, 0);
+        pass_load<R>(cur, esw, eb, t, row_start, rows, 0, 0);
+    float nsw = 0.0f, nbv = 0.0f;  // next batch's epilogue operands
     for (int b = 0; b < t.batches; ++b) {
         int acc[R];
 #pragma unroll
@@ -1101,7 +1111,7 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], bool have_cur
             }
             const bool more = nb < t.batches;
             if (more)
-                pass_load<R>(nxt, t, row_start, rows, nb, nj);
+                pass_load<R>(nxt, nsw, nbv, t, row_start, rows, nb, nj);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = j * U + u;
@@ -1132,14 +1142,13 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], bool have_cur
                 v += __shfl_xor(v, 32);
             const int rl = (b * groups + grp) * R + rr;
             if (lane == rr && rl < rows) {
-                const int row = row_start + rl;
-                const float tw = gptr(t.sw)[row] * sx;
-                const float bv = t.bias ? gptr(t.bias)[row] : 0.0f;
                 // device-coherent store: visible to every XCD once complete
-                __hip_atomic_store(gptr_mut(t.y) + row, fmaf(tw, (float)v, bv), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(gptr_mut(t.y) + row_start + rl, fmaf(esw * sx, (float)v, eb),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        esw = nsw;
+        eb = nbv;
     }
 }
 
@@ -1208,12 +1217,13 @@ __device__ __forceinline__ void stage_codes(u32x2* xs, const f32x4* xf, int G8, 
 constexpr int kPassStageAllAbove = 1024;
 
 template <int R>
-__device__ __forceinline__ void pass_prefetch(u32x4 (&cur)[kPassSlots], const PassTask& t, int w)
+__device__ __forceinline__ void pass_prefetch(u32x4 (&cur)[kPassSlots], float& esw, float& eb, const PassTask& t,
+                                              int w)
 {
     int row_start, rows;
     pass_range(t, w, row_start, rows);
     if (rows > 0)
-        pass_load<R>(cur, t, row_start, rows, 0, 0);
+        pass_load<R>(cur, esw, eb, t, row_start, rows, 0, 0);
 }
 
 __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* __restrict__ hdr,
@@ -1247,6 +1257,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     const uint32_t epoch = s_epoch;
 
     u32x4 cur[kPassSlots];
+    float esw = 0.0f, eb = 0.0f;  // first batch's epilogue operands, loaded with cur
     PassTask t = tasks[0];
     bool have_cur = false;
     if (worker) {
@@ -1254,9 +1265,9 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         pass_range(t, w, rs, rw);
         if (rw > 0) {
             if (t.r == 2)
-                pass_prefetch<2>(cur, t, w);
+                pass_prefetch<2>(cur, esw, eb, t, w);
             else
-                pass_prefetch<1>(cur, t, w);
+                pass_prefetch<1>(cur, esw, eb, t, w);
             have_cur = true;
         }
     }
@@ -1311,9 +1322,9 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         // 4. workers: stream the weights, write the rows, wait for the stores
         if (rows > 0 && worker) {
             if (t.r == 2)
-                pass_run<2>(cur, have_cur, t, row_start, rows, xs, a.s);
+                pass_run<2>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s);
             else
-                pass_run<1>(cur, have_cur, t, row_start, rows, xs, a.s);
+                pass_run<1>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s);
         }
         if (worker)
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1328,9 +1339,9 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
             pass_range(tn, w, rs, rw);
             if (rw > 0) {
                 if (tn.r == 2)
-                    pass_prefetch<2>(cur, tn, w);
+                    pass_prefetch<2>(cur, esw, eb, tn, w);
                 else
-                    pass_prefetch<1>(cur, tn, w);
+                    pass_prefetch<1>(cur, esw, eb, tn, w);
                 have_cur = true;
             }
         }
