@@ -1,0 +1,138 @@
+"""GPU parity of the benchmark workloads at their full sizes, in the launch
+configurations bench.py times (rotation pools, per-linear HIP graphs, the
+persistent pass), against the CPU oracle on sampled rows.
+
+The oracle's inputs are regenerated from the same seeded streams on the
+device the workload drew them on (so every value is the same) and
+quantised by the oracle itself: no expected value comes from the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from bit_quantized_decode_quantize_amd import inputs as I
+from bit_quantized_decode_quantize_amd import workloads as WL
+from bit_quantized_decode_quantize_amd import decode_stream as DS
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-5
+
+
+def npy(t):
+    return t.detach().cpu().numpy()
+
+
+def f16bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _rows(N, name, count=96):
+    idx = I.distinct_indices(f"gpu/wl/{name}/rows", N, min(count, N)).numpy()
+    return np.unique(np.concatenate([idx, [0, N - 1]]))
+
+
+def _check_rowwise_rows(y, W_rows, b_rows, x, rows):
+    """Oracle on the sampled rows only: prepare, quantise x, GEMV."""
+    wr, sr = O.prepare_int4_rowwise(W_rows)
+    qxr, sxr = O.quantize_act(x)
+    accr, yr = O.gemv_w4a8(wr, sr, b_rows, qxr, float(sxr))
+    err = O.rel_err_rowwise(y[rows], yr, sr, sxr, accr, b_rows)
+    assert err.max() <= TOL, err.max()
+
+
+def _graph_replay(step, n):
+    """Capture n consecutive steps in a HIP graph and replay it once."""
+    step()  # warm (library init outside the capture)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+
+
+def test_single_gemv_pool_graph_replay():
+    """The single Q-projection linear, one graph replay over the whole pool
+    (every copy writes the one output): y matches the oracle."""
+    w = WL.SingleGemvPool(device=DEV)
+    w.y.fill_(float("nan"))
+    _graph_replay(w.step, w.copies)
+    y = npy(w.y)
+    d = I.single_gemv_inputs(0, DEV)
+    rows = _rows(w.N, "single")
+    _check_rowwise_rows(y, npy(d["W"])[rows], npy(d["b"])[rows], npy(d["x"]), rows)
+
+
+@pytest.mark.parametrize("persistent", [True, False])
+def test_layer_pool(persistent):
+    """One layer's four fused linears over the rotation pool: the persistent
+    pass (all copies in one launch) and per-linear graph replay give the
+    same bits in every copy, matching the oracle on sampled rows."""
+    w = WL.LayerPool(device=DEV, persistent=persistent)
+    if persistent:
+        w.step()
+        torch.cuda.synchronize()
+        assert w.pass_.error_word() == 0
+    else:
+        _graph_replay(w.step, w.copies)
+    for k, (name, N, K) in enumerate(I.qwen_layer_linears()):
+        y0 = w.layers[0][k]["y"]
+        for c in range(1, w.copies):
+            assert torch.equal(w.layers[c][k]["y"], y0)
+        rows = _rows(N, f"layer/{name}")
+        W = DS.linear_weight_fp32("qwen/L0", name, 0, DEV)[torch.as_tensor(rows, device=DEV)]
+        b = DS.layer_biases("qwen/L0", 0, DEV)[name]
+        x = DS.layer_inputs("qwen/L0", 0, DEV)[name]
+        _check_rowwise_rows(npy(y0), npy(W), npy(b)[rows], npy(x), rows)
+
+
+def test_gemma_stream_layer_and_lm_head():
+    """Two Gemma-shaped group-32 layers (fp16 x) and the W8A16 lm_head
+    [262144, 1536], one graph replay of the token step, against the oracle
+    on sampled rows."""
+    w = WL.GemmaG32Stream(layers=2, device=DEV)
+    _graph_replay(w.step, 1)
+    for d in w.linears:
+        rows = _rows(d["N"], f"gemma/{d['layer']}/{d['name']}", 64)
+        W = I.normal(f"gemma/L{d['layer']}/{d['name']}/W", (d["N"], d["K"]), 0.02, 0, DEV)
+        wr, s16r = O.prepare_int4_group32(npy(W)[rows])
+        qxr, sxr = O.quantize_act(npy(d["x"]))
+        accg, yr = O.gemv_w4a8_group32(wr, s16r, None, qxr, float(sxr))
+        sg = s16r.view(np.float16).astype(np.float64)
+        mag = float(sxr) * np.abs(sg * accg).sum(1)
+        err = np.abs(npy(d["y"])[rows].astype(np.float64) - yr) / np.where(mag > 0, mag, 1.0)
+        assert err.max() <= TOL, (d["name"], err.max())
+    N, K = w.head_NK
+    rows = _rows(N, "gemma/lm_head", 256)
+    W = I.normal("gemma/lm_head/W", (N, K), 0.02, 0, DEV)[torch.as_tensor(rows, device=DEV)]
+    q, s = O.quantize_weights_int8_group32(npy(W))
+    yr = O.gemv_w8a16_group32(q, s, f16bits(w.head_x))
+    sg = s.view(np.float16).astype(np.float64)
+    ax = np.abs(f16bits(w.head_x).view(np.float16).astype(np.float64))
+    mag = (sg * (np.abs(q).astype(np.float64).reshape(len(rows), -1, 32) * ax.reshape(-1, 32)).sum(2)).sum(1)
+    err = np.abs(npy(w.head_y)[rows].astype(np.float64) - yr) / mag
+    assert err.max() <= TOL, err.max()
+
+
+@pytest.mark.parametrize("N,K", [(18944, 3584), (3584, 18944)])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_verify_pool(N, K, M):
+    """The verify GEMM at its benchmark shapes, automatic kernel choice,
+    graph replay over the pool: codes bit-exact, y of every token within
+    tolerance of the oracle on sampled rows."""
+    w = WL.VerifyPool(N, K, M, device=DEV)
+    _graph_replay(w.step, w.copies)
+    y = npy(w.y)
+    rows = _rows(N, f"verify/{N}/{K}", 64)
+    W = I.normal(f"verify/{N}x{K}/W", (N, K), 0.02, 0, DEV)[torch.as_tensor(rows, device=DEV)]
+    wr, sr = O.prepare_int4_rowwise(npy(W))
+    b = npy(I.normal(f"verify/{N}x{K}/b", N, 0.01, 0, DEV))[rows]
+    qxr, sxr = O.quantize_act(npy(I.normal(f"verify/{N}x{K}/X", (M, K), 1.0, 0, DEV)))
+    assert np.array_equal(npy(w.qx), qxr)
+    accr, yr = O.gemm_w4a8_verify(wr, sr, b, qxr, sxr)
+    for m in range(M):
+        err = O.rel_err_rowwise(y[m][rows], yr[m], sr, sxr[m], accr[m], b)
+        assert err.max() <= TOL, (m, err.max())
