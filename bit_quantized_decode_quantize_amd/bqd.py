@@ -17,7 +17,8 @@ from typing import List, Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbqd.so")
+# BQD_LIB names another build of the same library (e.g. to compare two builds).
+LIB_PATH = os.environ.get("BQD_LIB") or os.path.join(_HERE, "libbqd.so")
 
 BQD_F32, BQD_F16 = 0, 1
 BQD_SCALE_ROW_F32, BQD_SCALE_GROUP32_F16 = 0, 1
