@@ -380,7 +380,10 @@ def run_verify(a, dev):
                     "(per-token scales), bias", "impl": a.impl, "M": ms_list})
     out["sweep"] = sweep
     wl_bytes = WL.bytes_verify(last["M"], 18944, 3584)
-    out["roofline"] = roofline(last["GB/s"], f"k_verify_w4a8 (M={last['M']}, [18944,3584])", last["us"], wl_bytes)
+    kname = ("k_gemv_w4a8" if last["M"] == 1 and a.impl == 0 else
+             "k_verify_w4a8" if a.impl == 1 else "k_verify_mfma")
+    out["roofline"] = roofline(last["GB/s"], f"{kname} (M={last['M']}, [18944,3584], one launch per step)",
+                               last["us"], wl_bytes)
     if not a.no_cpu_baseline:
         import oracle as O
         from bit_quantized_decode_quantize_amd import inputs as I
