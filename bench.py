@@ -256,7 +256,7 @@ def run_single(a, dev):
     from bit_quantized_decode_quantize_amd import workloads as WL
     from bit_quantized_decode_quantize_amd import inputs as I
 
-    w = WL.SingleGemvPool(device=dev)
+    w = WL.SingleGemvPool(device=dev, r=a.r, lanes_per_row=a.lanes)
     log(f"single GEMV pool: {w.copies} copies of {w.weight_bytes()} B")
     ms, n = time_steps(w.step, a.steps, a.warmup, w.copies if (not a.eager) else 0)
     gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9

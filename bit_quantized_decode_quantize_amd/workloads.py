@@ -59,8 +59,10 @@ class SingleGemvPool:
     INT4, x fp32 [3584] ~N(0, 1) with 1 % of entries x20, bias ~N(0, 0.01^2).
     One step = one fused linear (quantise x, GEMV) on the next pool copy."""
 
-    def __init__(self, seed: int = 0, device="cuda", N: int = 3584, K: int = 3584):
+    def __init__(self, seed: int = 0, device="cuda", N: int = 3584, K: int = 3584, r: int = 0,
+                 lanes_per_row: int = 0):
         self.device = torch.device(device)
+        self.r, self.lanes_per_row = r, lanes_per_row
         d = I.single_gemv_inputs(seed, self.device, K=K, N=N)
         wq, sw = bqd.quantize_weights_int4_rowwise(d["W"])
         del d["W"]
@@ -78,7 +80,8 @@ class SingleGemvPool:
     def step(self, stream=None) -> None:
         c = self.i % self.copies
         self.i += 1
-        bqd.linear_w4a8(self.wq[c], self.sw[c], self.b[c], self.x, y=self.y, stream=stream)
+        bqd.linear_w4a8(self.wq[c], self.sw[c], self.b[c], self.x, y=self.y, r=self.r,
+                        lanes_per_row=self.lanes_per_row, stream=stream)
 
     def bytes_per_step(self) -> int:
         return algorithmic_bytes_linear(self.N, self.K, True)
