@@ -118,6 +118,52 @@ def time_steps(step, steps, warmup, graph_steps=0):
     return e0.elapsed_time(e1) / n, n
 
 
+def repeat_spread(step, steps, reps=5):
+    """ms per step over ``reps`` further regions of ``steps`` steps each:
+    median, min and max (the timed region above is the reported value)."""
+    import statistics
+    import torch
+    st = torch.cuda.current_stream()
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(steps):
+            step()
+        e1.record(st)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return {"reps": reps, "steps_each": steps, "median": round(statistics.median(out), 5),
+            "min": round(min(out), 5), "max": round(max(out), 5)}
+
+
+def read_ceiling(dev, nbytes=2 << 30):
+    """Best bandwidth of the library's streaming-read kernel over a few launch
+    shapes, reading a 2 GiB buffer (8x the Infinity Cache) per launch."""
+    import torch
+    from bit_quantized_decode_quantize_amd import bqd
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1 << 14, dtype=torch.int32, device=dev)
+    best, shape = 0.0, None
+    for unroll, grid in ((1, 1024), (1, 2048), (1, 4096), (4, 512), (4, 1024), (8, 256), (8, 512)):
+        bqd.read_probe(buf, sink, grid, unroll)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            bqd.read_probe(buf, sink, grid, unroll)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = 5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if gbs > best:
+            best, shape = gbs, (unroll, grid)
+    del buf
+    torch.cuda.empty_cache()
+    return {"GB/s": round(best, 1), "kernel": "read_probe", "unroll": shape[0], "grid": shape[1],
+            "bytes_per_launch": nbytes}
+
+
 def roofline(achieved_gbs, kernel, avg_us, avg_bytes, traffic=None):
     return {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
@@ -130,6 +176,28 @@ def base_line(a, value, ms, steps, config, dtype="int8"):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": dtype, "data": "synthetic", "config": config,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2)}
+
+
+def cold_call_us(step, dev, reps=5):
+    """One call after 512 MiB of writes have flushed the caches, events
+    around the call alone; median of ``reps``.  The events and the call are
+    enqueued while the flush still runs, so host-side launch cost is not
+    counted."""
+    import statistics
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    t = []
+    for i in range(reps):
+        torch.cuda.synchronize()
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    return round(statistics.median(t), 2)
 
 
 def cpu_loop(fn, sample_bytes, seconds):
@@ -219,7 +287,11 @@ def run_stream(a, dev):
         "bytes_per_step": step_bytes, "packed_weight_bytes": s.weight_bytes()})
     out["tok_per_s"] = round(1e3 / ms, 2)
     out["us_per_gemv"] = round(ms * 1e3 / len(s.linears), 3)
+    out["ms_per_step_spread"] = repeat_spread(s.step, max(1, a.steps // 5))
     out["roofline"] = roofline(achieved, kernel, avg_us, avg_bytes, traffic)
+    ceil = read_ceiling(dev)
+    out["read_ceiling"] = ceil
+    out["pct_of_read_ceiling"] = round(100.0 * gbs / ceil["GB/s"], 2)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_stream(s, a.cpu_seconds)
     return out
@@ -265,6 +337,7 @@ def run_single(a, dev):
                     "outliers, fused act-quant", "launch": "HIP graph" if (not a.eager) else "eager",
         "N": w.N, "K": w.K, "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
     out["us_per_gemv"] = round(ms * 1e3, 3)
+    out["cold_single_call_us"] = cold_call_us(w.step, dev)
     out["roofline"] = roofline(gbs, "k_gemv_w4a8 (fused linear, one launch per step)", ms * 1e3,
                                w.bytes_per_step())
     if not a.no_cpu_baseline:

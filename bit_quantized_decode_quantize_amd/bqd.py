@@ -32,6 +32,7 @@ ENTRY_POINTS = (
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
     "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
+    "read_probe",
 )
 
 
@@ -82,6 +83,7 @@ def lib() -> C.CDLL:
         "decode_pass_sync_bytes": (C.c_size_t, [I]),
         "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32)]),
         "decode_pass_w4a8": (I, [P, I, I, P, I, P]),
+        "read_probe": (I, [P, C.c_size_t, P, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -417,3 +419,14 @@ class DecodePass:
 
     def clear_error(self) -> None:
         self.sync[0].zero_()
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int, unroll: int = 1, stream=None) -> None:
+    """Streaming read of ``buf`` (the read-ceiling reference kernel); ``sink``
+    int32/uint32 with at least ``grid`` elements."""
+    _dev(buf, "buf", (buf.dtype,))
+    _dev(sink, "sink", (torch.int32,))
+    if sink.numel() < grid:
+        raise ValueError(f"sink holds {sink.numel()} words, the grid needs {grid}")
+    _call("read_probe", buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), grid, unroll,
+          _stream(stream))

@@ -1350,6 +1350,36 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
 }
 
 // ------------------------------------------------------------------------
+// Streaming-read reference: the measured read ceiling the GEMV rooflines are
+// set against.  Each thread reads 16-byte words in a grid-stride loop, U in
+// flight, and folds them with XOR; one word per workgroup is written so no
+// load is dead.
+// ------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_read_probe(const u32x4* __restrict__ p, long long n, uint32_t* out)
+{
+    uint32_t a = 0;
+    const long long stride = (long long)gridDim.x * kThreads;
+    long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            a ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n; i += stride) {
+        const u32x4 v = p[i];
+        a ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    a ^= __shfl_xor(a, 1);
+    if (threadIdx.x == 0)
+        out[blockIdx.x] = a;
+}
+
+// ------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
@@ -2074,6 +2104,33 @@ int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* s
                                    (unsigned)pass_lds_bytes(max_k),
                                    (hipStream_t)stream) != hipSuccess)
         return BQD_ERR_LAUNCH;
+    return launched();
+}
+
+int read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll, void* stream)
+{
+    if (grid < 1 || grid > (1 << 20) || bytes % 16 != 0)
+        return BQD_ERR_SHAPE;
+    if (unroll != 1 && unroll != 4 && unroll != 8)
+        return BQD_ERR_CONFIG;
+    if (bytes == 0)
+        return BQD_OK;
+    if (!buf || !sink)
+        return BQD_ERR_NULL;
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return BQD_ERR_ALIGN;
+    int rc = bqd_init();
+    if (rc)
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const u32x4* p = reinterpret_cast<const u32x4*>(buf);
+    const long long n = (long long)(bytes / 16);
+    if (unroll == 1)
+        hipLaunchKernelGGL(k_read_probe<1>, dim3(grid), dim3(kThreads), 0, st, p, n, sink);
+    else if (unroll == 4)
+        hipLaunchKernelGGL(k_read_probe<4>, dim3(grid), dim3(kThreads), 0, st, p, n, sink);
+    else
+        hipLaunchKernelGGL(k_read_probe<8>, dim3(grid), dim3(kThreads), 0, st, p, n, sink);
     return launched();
 }
 

@@ -267,6 +267,18 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
 int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev,
                      int32_t spin_limit, void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Measurement                                                             */
+/* ---------------------------------------------------------------------- */
+
+/* Streaming read of buf (device, bytes % 16 == 0, 16-byte aligned): the
+ * reference kernel whose bandwidth is the measured read ceiling the GEMV
+ * rooflines are compared with ("在香橙派上跑 Gemma4 ..." section 4.1 sets the
+ * decode bound by the measured read bandwidth).  grid workgroups of 256
+ * threads, unroll in {1, 4, 8} 16-byte loads in flight per thread; sink
+ * (device) receives one uint32 per workgroup (an XOR of what it read). */
+int read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

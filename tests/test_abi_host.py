@@ -195,3 +195,14 @@ def test_decode_pass_launch_validates_before_launch():
     assert L.decode_pass_w4a8(P, 2, 40, P, 0, None) == SHAPE
     assert L.decode_pass_w4a8(P, 2, 64, P, -1, None) == CONFIG
     assert L.decode_pass_w4a8(P + 8, 2, 64, P, 0, None) == ALIGN
+
+
+def test_read_probe_validates_before_launch():
+    L = _lib()
+    # read_probe(buf, bytes, sink, grid, unroll, stream)
+    assert L.read_probe(P, 40, P, 8, 1, None) == SHAPE
+    assert L.read_probe(P, 64, P, 0, 1, None) == SHAPE
+    assert L.read_probe(P, 64, P, 8, 3, None) == CONFIG
+    assert L.read_probe(None, 64, P, 8, 1, None) == NULL
+    assert L.read_probe(P + 8, 64, P, 8, 1, None) == ALIGN
+    assert L.read_probe(P, 0, None, 8, 1, None) == OK

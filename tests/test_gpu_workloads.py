@@ -136,3 +136,25 @@ def test_verify_pool(N, K, M):
     for m in range(M):
         err = O.rel_err_rowwise(y[m][rows], yr[m], sr, sxr[m], accr[m], b)
         assert err.max() <= TOL, (m, err.max())
+
+
+@pytest.mark.parametrize("unroll", [1, 4, 8])
+def test_read_probe_reads_every_word(unroll):
+    """The read-ceiling kernel: workgroup b's sink word is the XOR of the
+    16-byte words threads 0 and 1 of b read in the grid-stride loop."""
+    from bit_quantized_decode_quantize_amd import bqd
+    grid, n16 = 8, 8 * 256 * 5 + 37
+    words = I.random_words("gpu/read_probe", n16 * 4, device=DEV)
+    sink = torch.zeros(grid, dtype=torch.int32, device=DEV)
+    bqd.read_probe(words, sink, grid, unroll)
+    w = npy(words).view(np.uint32).reshape(n16, 4)
+    fold = w[:, 0] ^ w[:, 1] ^ w[:, 2] ^ w[:, 3]
+    stride = grid * 256
+    expect = []
+    for b in range(grid):
+        a = np.uint32(0)
+        for t in (0, 1):
+            for i in range(b * 256 + t, n16, stride):
+                a ^= fold[i]
+        expect.append(a)
+    assert np.array_equal(npy(sink).view(np.uint32), np.array(expect, np.uint32))
