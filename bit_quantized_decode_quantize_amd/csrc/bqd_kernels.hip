@@ -1435,15 +1435,17 @@ inline bool valid_config(int r, int L)
     return (r == 0 || r == 1 || r == 2 || r == 4 || r == 8) && (L == 0 || L == 16 || L == 32 || L == 64);
 }
 
-// Automatic choice where the caller passes 0 (from a sweep over the decoder's
-// shapes on MI355X): 32 lanes per row; one row per lane group below 8192
-// rows so that small matrices still spread over every CU, two above.  U
+// Automatic choice where the caller passes 0 (measured on MI355X in the
+// decode streams, one graph-replayed launch per linear): 32 lanes per row;
+// one row per lane group, except r_large rows from 8192 rows on (per-row
+// INT4: 1 -- the Qwen-shaped stream takes 1.42 ms per token with 1 and
+// 1.51 ms with 2; group-32: 2, which the Gemma-shaped stream prefers).  U
 // covers a lane's whole row when it fits the register budget.
-inline GemvCfg make_cfg(int N, int C, int r, int L)
+inline GemvCfg make_cfg(int N, int C, int r, int L, int r_large)
 {
     GemvCfg c;
     c.L = L ? L : 32;
-    c.r = r ? r : (N >= 8192 ? 2 : 1);
+    c.r = r ? r : (N >= 8192 ? r_large : 1);
     const int iters = (C + c.L - 1) / c.L;
     c.U = pow2ceil(iters) < max_unroll(c.r) ? pow2ceil(iters) : max_unroll(c.r);
     const long long rows = (long long)(kThreads / c.L) * c.r;
@@ -1699,7 +1701,7 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8
     if ((rc = bqd_init()))
         return rc;
     return launch_gemv_rowwise<X_Q8>(wq, sw, bias, qx, sx, y, acc, nullptr, nullptr, N, K,
-                                     make_cfg(N, K / 32, r, lanes_per_row), (hipStream_t)stream);
+                                     make_cfg(N, K / 32, r, lanes_per_row, 1), (hipStream_t)stream);
 }
 
 int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const void* x,
@@ -1724,7 +1726,7 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
         return BQD_ERR_CONFIG;
     if ((rc = bqd_init()))
         return rc;
-    const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row);
+    const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 1);
     if (x_dtype == BQD_F32)
         return launch_gemv_rowwise<X_F32>(wq, sw, bias, x, nullptr, y, acc, qx_out, sx_out, N, K, c,
                                           (hipStream_t)stream);
@@ -1753,7 +1755,7 @@ int gemv_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias
     if ((rc = bqd_init()))
         return rc;
     return launch_gemv_group32<X_Q8>(wq, s16, bias, qx, sx, y, acc_g, nullptr, nullptr, N, K,
-                                     make_cfg(N, K / 32, r, lanes_per_row), (hipStream_t)stream);
+                                     make_cfg(N, K / 32, r, lanes_per_row, 2), (hipStream_t)stream);
 }
 
 int linear_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias, const void* x,
@@ -1778,7 +1780,7 @@ int linear_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bi
         return BQD_ERR_CONFIG;
     if ((rc = bqd_init()))
         return rc;
-    const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row);
+    const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 2);
     if (x_dtype == BQD_F32)
         return launch_gemv_group32<X_F32>(wq, s16, bias, x, nullptr, y, acc_g, qx_out, sx_out, N, K,
                                           c, (hipStream_t)stream);
