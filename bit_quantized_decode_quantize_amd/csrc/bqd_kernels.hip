@@ -1808,7 +1808,7 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
         return BQD_ERR_CONFIG;
     const int L = lanes_per_row ? lanes_per_row : 16;
     if (r == 0)
-        r = 4;
+        r = 2;  // [262144, 1536]: 78 us with r = 2, 84 us with 4 (16 lanes per row)
     if ((rc = bqd_init()))
         return rc;
     const int G = K / 32;
