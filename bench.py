@@ -395,7 +395,7 @@ def run_gemma(a, dev):
 
     layers = a.layers or 35
     t0 = time.time()
-    w = WL.GemmaG32Stream(layers=layers, device=dev)
+    w = WL.GemmaG32Stream(layers=layers, device=dev, r=a.r, lanes_per_row=a.lanes)
     log(f"gemma stream built: {w.launches_per_step} launches, {w.weight_bytes() / 1e9:.3f} GB, "
         f"{time.time() - t0:.1f} s")
     ms, n = time_steps(w.step, a.steps, a.warmup, 1 if (not a.eager) else 0)

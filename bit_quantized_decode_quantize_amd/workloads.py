@@ -156,8 +156,9 @@ class GemmaG32Stream:
     one token: 140 fused group-32 linears + the W8A16 lm_head, one launch each.
     Weights total 1.1 GB, so every step streams from HBM."""
 
-    def __init__(self, layers: int = 35, seed: int = 0, device="cuda"):
+    def __init__(self, layers: int = 35, seed: int = 0, device="cuda", r: int = 0, lanes_per_row: int = 0):
         self.device = torch.device(device)
+        self.r, self.lanes_per_row = r, lanes_per_row
         self.linears: List[Dict] = []
         for l in range(layers):
             prefix = f"gemma/L{l}"
@@ -180,7 +181,8 @@ class GemmaG32Stream:
 
     def step(self, stream=None) -> None:
         for d in self.linears:
-            bqd.linear_w4a8_group32(d["wq"], d["s16"], None, d["x"], y=d["y"], stream=stream)
+            bqd.linear_w4a8_group32(d["wq"], d["s16"], None, d["x"], y=d["y"], r=self.r,
+                                    lanes_per_row=self.lanes_per_row, stream=stream)
         self.lm_head(stream)
 
     def lm_head(self, stream=None) -> None:
