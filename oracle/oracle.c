@@ -387,6 +387,36 @@ int orc_gemv_w8a16_group32(const int8_t* w, const uint16_t* s16, const uint16_t*
     return ORC_OK;
 }
 
+/* W4A16 comparison GEMV (the float-unpack route [Orin] "为什么 INT4 float
+ * 解包不快" weighs against the integer dot, and the fp16-MAC dequantisation of
+ * [Ascend] 3.1): the same packed per-row INT4 weights against an fp16
+ * activation, no activation quantisation.
+ *   y_j = s^W_j * sum_i q^W_ji x_i + b_j,
+ * every product q x exact in binary64 (|q| <= 8, x an fp16), the sum in
+ * binary64 in i order. */
+int orc_gemv_w4a16(const uint32_t* w, const float* sw, const float* bias, const uint16_t* x16,
+                   int64_t N, int64_t K, double* y)
+{
+    if (N < 0 || K <= 0 || K % 8)
+        return ORC_E_ARG;
+    for (int64_t i = 0; i < K; ++i) {
+        float t = orc_f16_to_f32(x16[i]);
+        if (!(fabsf(t) <= FLT_MAX))
+            return ORC_E_NONFINITE;
+    }
+    for (int64_t j = 0; j < N; ++j) {
+        double sum = 0.0;
+        int8_t q[8];
+        for (int64_t t = 0; t < K / 8; ++t) {
+            orc_unpack_word(w[j * (K / 8) + t], q);
+            for (int k = 0; k < 8; ++k)
+                sum += (double)q[k] * (double)orc_f16_to_f32(x16[8 * t + k]);
+        }
+        y[j] = (double)sw[j] * sum + (bias ? (double)bias[j] : 0.0);
+    }
+    return ORC_OK;
+}
+
 /* M=K verification ([Ascend] 5): the same weights against M quantised
  * tokens; token m uses its own scale s^x_m.
  *   acc[m][j] = sum_i q^W_ji q^x_mi,  y[m][j] = s^W_j s^x_m acc[m][j] + b_j. */

@@ -52,6 +52,7 @@ def _load():
         "orc_gemv_w4a8_group32": (I32, [P, P, P, P, F32, I64, I64, P, P]),
         "orc_gemv_w8a16_group32": (I32, [P, P, P, I64, I64, P]),
         "orc_gemm_w4a8_verify": (I32, [P, P, P, P, P, I64, I64, I64, P, P]),
+        "orc_gemv_w4a16": (I32, [P, P, P, P, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -219,6 +220,20 @@ def gemv_w8a16_group32(w8, s16, x16) -> np.ndarray:
     assert xb.size == K and s16.shape == (N, K // 32)
     y = np.empty(N, np.float64)
     _check(_lib.orc_gemv_w8a16_group32(_p(w8), _p(s16), _p(xb), N, K, _p(y)))
+    return y
+
+
+def gemv_w4a16(w, sw, bias, x16) -> np.ndarray:
+    """W4A16 comparison GEMV: packed per-row INT4 weights against fp16 x
+    (uint16 bit patterns), y = sW * sum q x + b in binary64."""
+    w = _c(w, np.uint32)
+    N = w.shape[0]
+    K = w.shape[1] * 8
+    sw = _c(sw, np.float32)
+    b = None if bias is None else _c(bias, np.float32)
+    xb = _c(x16, np.uint16)
+    y = np.empty(N, np.float64)
+    _check(_lib.orc_gemv_w4a16(_p(w), _p(sw), _p(b), _p(xb), N, K, _p(y)))
     return y
 
 

@@ -373,6 +373,53 @@ def test_gemv_w8a16_vs_numpy_float64_dequantised_matmul():
     assert np.all(np.abs(y - ref) <= 1e-13 * mag + 1e-300)
 
 
+def _np_unpack_codes(w):
+    """Signed INT4 codes of packed words with numpy bit operations (nibble k
+    of a word is code k, two's complement)."""
+    w = np.asarray(w, np.uint32)
+    nib = (w[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF
+    q = nib.astype(np.int64)
+    q = np.where(q >= 8, q - 16, q)
+    return q.reshape(*w.shape[:-1], w.shape[-1] * 8)
+
+
+def test_gemv_w4a16_vs_numpy_float64():
+    """The float-unpack comparison GEMV: codes unpacked by numpy, a float64
+    matmul against the fp16 x; every product and (for these sizes) every
+    partial sum is exact in binary64, so only the final rounding differs."""
+    N, K = 13, 256
+    W = I.normal("pin/w4a16/W", (N, K), 0.02).numpy()
+    w, s = O.prepare_int4_rowwise(W)
+    w[3, 0] = 0x88888888                               # eight -8 codes
+    b = I.normal("pin/w4a16/b", N, 0.01).numpy()
+    x16 = I.normal("pin/w4a16/x", K, 1.0, dtype=__import__("torch").float16).numpy()
+    y = O.gemv_w4a16(w, s, b, x16.view(np.uint16))
+    q = _np_unpack_codes(w)
+    assert q[3, :8].tolist() == [-8] * 8
+    ref = s.astype(np.float64) * (q.astype(np.float64) @ x16.astype(np.float64)) + b.astype(np.float64)
+    mag = np.abs(s.astype(np.float64)) * (np.abs(q) @ np.abs(x16.astype(np.float64))) + np.abs(b)
+    assert np.all(np.abs(y - ref) <= 1e-14 * mag)
+    y0 = O.gemv_w4a16(w, s, None, x16.view(np.uint16))
+    assert np.allclose(y - y0, b.astype(np.float64), rtol=0, atol=1e-15)
+
+
+def test_gemv_w4a16_on_integer_x_equals_the_w4a8_gemv():
+    """With x = fp16 of integer codes in [-127, 127] (exact in binary16) and
+    s^x = 1, the float-unpack GEMV and the integer-dot GEMV compute the same
+    sum: y agrees exactly."""
+    N, K = 9, 3584
+    q = I.uniform_int("pin/w4a16x/q", (N, K), -8, 7).numpy().astype(np.int8)
+    w = O.pack_int4(q)
+    s = I.normal("pin/w4a16x/s", N, 0.01).numpy()
+    b = I.normal("pin/w4a16x/b", N, 0.01).numpy()
+    qx = I.uniform_int("pin/w4a16x/x", K, -127, 127).numpy().astype(np.int8)
+    x16 = qx.astype(np.float16)
+    y16 = O.gemv_w4a16(w, s, b, x16.view(np.uint16))
+    acc, y8 = O.gemv_w4a8(w, s, b, qx, np.float32(1.0))
+    assert np.array_equal(y16, y8)
+    assert np.array_equal(y16, s.astype(np.float64) * acc.astype(np.float64) + b.astype(np.float64))
+
+
 def test_verify_matches_per_token_gemv():
     """[Ascend] 5: verifying M tokens streams the weights once; each token's
     column equals the single-token GEMV, and M = 1 is the GEMV itself."""
