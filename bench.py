@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--eager", action="store_true",
                    help="launch per-linear kernels from Python each step instead of replaying "
                         "them from a captured HIP graph")
+    p.add_argument("--w4a16", action="store_true",
+                   help="stream: the float-unpack comparison (gemv_w4a16 per linear, fp16 x) "
+                        "instead of the W4A8 path")
     p.add_argument("--verify-m", default="1,2,4,8,16")
     p.add_argument("--impl", type=int, default=0, help="verify kernel: 0 automatic, 1 dot4, 2 MFMA")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -219,7 +222,9 @@ def run_stream(a, dev):
     layers = a.layers or 28
     t0 = time.time()
     s = DS.QwenW4A8Stream(layers=layers, device=dev, r=a.r, lanes_per_row=a.lanes,
-                          persistent=not a.per_linear)
+                          persistent=not (a.per_linear or a.w4a16))
+    if a.w4a16:
+        return run_stream_w4a16(a, dev, s, layers)
     log(f"stream built: {len(s.linears)} linears, {s.weight_bytes() / 1e9:.3f} GB packed, "
         f"{time.time() - t0:.1f} s")
     st = torch.cuda.current_stream()
@@ -297,6 +302,30 @@ def run_stream(a, dev):
     return out
 
 
+def run_stream_w4a16(a, dev, s, layers):
+    """The same 28-layer weights through the float-unpack comparison GEMV
+    (fp16 x, one graph-replayed launch per linear)."""
+    import torch
+    from bit_quantized_decode_quantize_amd import bqd
+    x16 = [d["x"].to(torch.float16) for d in s.linears]
+
+    def step():
+        for d, x in zip(s.linears, x16):
+            bqd.gemv_w4a16(d["wq"], d["sw"], d["b"], x, y=d["y"], r=a.r, lanes_per_row=a.lanes)
+    ms, n = time_steps(step, a.steps, a.warmup, 0 if a.eager else 1)
+    step_bytes = sum(d["N"] * d["K"] // 2 + 4 * d["N"] + (4 * d["N"] if d["b"] is not None else 0) + 2 * d["K"]
+                     + 4 * d["N"] for d in s.linears)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = base_line(a, gbs, ms, n, {
+        "workload": f"qwen2-7b-shaped {layers}-layer stream through the W4A16 float-unpack comparison GEMV "
+                    "(fp16 x, per-row int4)", "launch": "per-linear, HIP graph" if not a.eager else "per-linear",
+        "layers": layers, "bytes_per_step": step_bytes}, dtype="fp16")
+    out["tok_per_s"] = round(1e3 / ms, 2)
+    out["roofline"] = roofline(gbs, "k_gemv_w4a16 (every linear, one launch each)", ms * 1e3 / len(s.linears),
+                               step_bytes / len(s.linears))
+    return out
+
+
 def cpu_baseline_stream(stream, seconds):
     """The C oracle, single-threaded on this host, over layer 0 of the same
     stream (its four linears: activation quantisation + GEMV), repeated for
@@ -325,6 +354,7 @@ def cpu_baseline_stream(stream, seconds):
 
 
 def run_single(a, dev):
+    import torch
     from bit_quantized_decode_quantize_amd import workloads as WL
     from bit_quantized_decode_quantize_amd import inputs as I
 
@@ -338,6 +368,17 @@ def run_single(a, dev):
         "N": w.N, "K": w.K, "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
     out["us_per_gemv"] = round(ms * 1e3, 3)
     out["cold_single_call_us"] = cold_call_us(w.step, dev)
+    # The float-unpack comparison (W4A16) on the same weights, fp16 x.
+    from bit_quantized_decode_quantize_amd import bqd
+    x16 = w.x.to(torch.float16)
+    state = {"i": 0}
+
+    def step16():
+        c = state["i"] % w.copies
+        state["i"] += 1
+        bqd.gemv_w4a16(w.wq[c], w.sw[c], w.b[c], x16, y=w.y, r=a.r, lanes_per_row=a.lanes)
+    ms16, _ = time_steps(step16, a.steps, a.warmup, w.copies if (not a.eager) else 0)
+    out["w4a16_us_per_gemv"] = round(ms16 * 1e3, 3)
     out["roofline"] = roofline(gbs, "k_gemv_w4a8 (fused linear, one launch per step)", ms * 1e3,
                                w.bytes_per_step())
     if not a.no_cpu_baseline:

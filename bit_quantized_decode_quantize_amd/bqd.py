@@ -32,7 +32,7 @@ ENTRY_POINTS = (
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
     "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
-    "read_probe",
+    "read_probe", "gemv_w4a16",
 )
 
 
@@ -84,6 +84,7 @@ def lib() -> C.CDLL:
         "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32)]),
         "decode_pass_w4a8": (I, [P, I, I, P, I, P]),
         "read_probe": (I, [P, C.c_size_t, P, I, I, P]),
+        "gemv_w4a16": (I, [P, P, P, P, P, I, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -315,6 +316,20 @@ def gemv_w8a16_group32(w8, s16, x16, y=None, r=0, lanes_per_row=0, stream=None):
     y = _empty((N,), torch.float32, w8) if y is None else _dev(y, "y", _F32, N)
     _call("gemv_w8a16_group32", w8.data_ptr(), s16.data_ptr(), x16.data_ptr(), y.data_ptr(), N, K,
           r, lanes_per_row, _stream(stream))
+    return y
+
+
+def gemv_w4a16(wq, sw, bias, x16, y=None, r=0, lanes_per_row=0, stream=None):
+    """W4A16 comparison GEMV: packed per-row INT4 weights against fp16 x [K]
+    (unpacked to fp16, fp32 accumulation) -> fp32 y [N]."""
+    N, K = _wshape(wq, None)
+    _dev(wq, "wq", _WORD, N * K // 8)
+    _dev(sw, "sw", _F32, N)
+    _opt(bias, "bias", _F32, N)
+    _dev(x16, "x16", (torch.float16,), K)
+    y = _empty((N,), torch.float32, wq) if y is None else _dev(y, "y", _F32, N)
+    _call("gemv_w4a16", wq.data_ptr(), sw.data_ptr(), _ptr(bias), x16.data_ptr(), y.data_ptr(), N, K, r,
+          lanes_per_row, _stream(stream))
     return y
 
 

@@ -721,6 +721,114 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w8a16_g32(
 }
 
 // ------------------------------------------------------------------------
+// W4A16 comparison GEMV: the same packed per-row INT4 weights against an
+// fp16 activation, unpacked to fp16 and multiplied in floating point
+// ("Jetson Orin AGX INT4 ..." section "为什么 INT4 float 解包不快" weighs this
+// route against the integer dot; "在香橙派上跑 Gemma4 ..." section 3.1
+// dequantises to fp16 and uses fp16 MACs).
+//   Per word: u = w ^ 0x88888888 turns each signed nibble q into q + 8;
+//   bytes (u & 0x0F0F0F0F) hold codes {0,2,4,6}, ((u >> 4) & 0x0F0F0F0F)
+//   codes {1,3,5,7}; each byte pair is spread into fp16 bits 0x6400 | (q+8)
+//   = 1024 + q + 8, and a packed subtract of 1032 gives q exactly; then
+//   v_dot2_f32_f16 against x staged per 8-group as [x0 x2 | x4 x6 | x1 x3 |
+//   x5 x7].  The compiled loop issues about 3.4 VALU instructions per code,
+//   against about 1.1 for the integer dot.  y = fmaf(sw, acc, b) with acc
+//   the fp32 sum.
+// ------------------------------------------------------------------------
+// The word goes in by value: __builtin_bit_cast of an ext-vector element
+// (xg.y) was compiled as a read of element 0.
+__device__ __forceinline__ h16x2 as_h16x2(uint32_t v)
+{
+    return __builtin_bit_cast(h16x2, v);
+}
+
+__device__ __forceinline__ float dot8_w4_f16(uint32_t w, u32x4 xg, float acc)
+{
+    const uint32_t u = w ^ 0x88888888u;
+    const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+    // fp16 pairs [1024 + c_a, 1024 + c_b] from bytes a, b of a code word.
+    const h16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const h16x2 q02 = __builtin_bit_cast(h16x2, (lo & 0xFFu) | ((lo & 0xFF00u) << 8) | 0x64006400u) - bias;
+    const h16x2 q46 = __builtin_bit_cast(h16x2, ((lo >> 16) & 0xFFu) | ((lo >> 8) & 0xFF0000u) | 0x64006400u) - bias;
+    const h16x2 q13 = __builtin_bit_cast(h16x2, (hi & 0xFFu) | ((hi & 0xFF00u) << 8) | 0x64006400u) - bias;
+    const h16x2 q57 = __builtin_bit_cast(h16x2, ((hi >> 16) & 0xFFu) | ((hi >> 8) & 0xFF0000u) | 0x64006400u) - bias;
+    acc = __builtin_amdgcn_fdot2(q02, as_h16x2(xg.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(q46, as_h16x2(xg.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(q13, as_h16x2(xg.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(q57, as_h16x2(xg.w), acc, false);
+    return acc;
+}
+
+template <int R, int L>
+__global__ __launch_bounds__(kThreads) void k_gemv_w4a16(const u32x4* __restrict__ wq, const float* __restrict__ sw,
+                                                         const float* __restrict__ bias,
+                                                         const u32x4* __restrict__ x16, float* __restrict__ y,
+                                                         int N, int C)
+{
+    extern __shared__ u32x4 xs[];  // one 16-byte group of 8 fp16 per 8 codes, permuted
+    for (int g = threadIdx.x; g < 4 * C; g += kThreads) {
+        const u32x4 v = x16[g];  // x0..x7 as fp16 pairs (x0,x1) (x2,x3) (x4,x5) (x6,x7)
+        xs[g] = u32x4{(v.x & 0xFFFFu) | (v.y << 16), (v.z & 0xFFFFu) | (v.w << 16),
+                      (v.x >> 16) | (v.y & 0xFFFF0000u), (v.z >> 16) | (v.w & 0xFFFF0000u)};
+    }
+    __syncthreads();
+
+    constexpr int GROUPS = kThreads / L;
+    constexpr int ROWS = GROUPS * R;
+    constexpr int U = 2;
+    const int lane = threadIdx.x % L;
+    const int grp = threadIdx.x / L;
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int iters = (C + L - 1) / L;
+
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int row0 = tile * ROWS + grp * R;
+        const u32x4* wrow[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            wrow[r] = wq + (size_t)min(row0 + r, N - 1) * C;
+        float facc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = 0.0f;
+        for (int it = 0; it < iters; it += U) {
+            u32x4 w[U][R];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = (it + u) * L + lane;
+                const bool ok = (it + u < iters) && (c < C);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    w[u][r] = ok ? wrow[r][c] : u32x4{0u, 0u, 0u, 0u};  // codes 0
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = min((it + u) * L + lane, C - 1);
+                const u32x4 g0 = xs[4 * c], g1 = xs[4 * c + 1], g2 = xs[4 * c + 2], g3 = xs[4 * c + 3];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float p = facc[r];
+                    p = dot8_w4_f16(w[u][r].x, g0, p);
+                    p = dot8_w4_f16(w[u][r].y, g1, p);
+                    p = dot8_w4_f16(w[u][r].z, g2, p);
+                    p = dot8_w4_f16(w[u][r].w, g3, p);
+                    facc[r] = p;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = sum_lanes_f<L>(facc[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r;
+            if (lane == r && row < N)
+                y[row] = fmaf(sw[row], facc[r], bias ? bias[row] : 0.0f);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // M-token verify GEMM, integer dot products.  MT >= M tokens are staged in
 // LDS per K-segment (padding tokens are zero); each weight chunk is loaded
 // and split once and meets all MT tokens.
@@ -1827,6 +1935,50 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
     BQD_W8_CASE(1, 32) BQD_W8_CASE(2, 32) BQD_W8_CASE(4, 32) BQD_W8_CASE(8, 32)
     BQD_W8_CASE(1, 64) BQD_W8_CASE(2, 64) BQD_W8_CASE(4, 64) BQD_W8_CASE(8, 64)
 #undef BQD_W8_CASE
+    return BQD_ERR_CONFIG;
+}
+
+int gemv_w4a16(const uint32_t* wq, const float* sw, const float* bias, const uint16_t* x16, float* y,
+               int32_t N, int32_t K, int32_t r, int32_t lanes_per_row, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (2 * (size_t)K > (size_t)kLdsBytes)
+        return BQD_ERR_BOUND;
+    if (N == 0)
+        return BQD_OK;
+    if (!wq || !sw || !x16 || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(x16, 16) || !aligned(sw, 4) || !aligned(bias, 4) || !aligned(y, 4))
+        return BQD_ERR_ALIGN;
+    if (!valid_config(r, lanes_per_row))
+        return BQD_ERR_CONFIG;
+    // Automatic shape, from a sweep over the Qwen2-7B layer shapes: full
+    // waves per row; two rows per wave once N alone fills the chip.
+    const int L = lanes_per_row ? lanes_per_row : 64;
+    if (r == 0)
+        r = N >= 16384 ? 2 : 1;
+    if ((rc = bqd_init()))
+        return rc;
+    const int C = K / 32;
+    const int rows = (kThreads / L) * r;
+    const dim3 grid(grid_for((N + rows - 1) / rows)), block(kThreads);
+    const size_t lds = 2 * (size_t)K;
+    const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x16);
+    hipStream_t st = (hipStream_t)stream;
+#define BQD_W4A16_CASE(RR, LL)                                                                        \
+    if (r == RR && L == LL) {                                                                         \
+        hipLaunchKernelGGL((k_gemv_w4a16<RR, LL>), grid, block, lds, st, w, sw, bias, xv, y, N, C);  \
+        return launched();                                                                            \
+    }
+    BQD_W4A16_CASE(1, 16) BQD_W4A16_CASE(2, 16) BQD_W4A16_CASE(4, 16) BQD_W4A16_CASE(8, 16)
+    BQD_W4A16_CASE(1, 32) BQD_W4A16_CASE(2, 32) BQD_W4A16_CASE(4, 32) BQD_W4A16_CASE(8, 32)
+    BQD_W4A16_CASE(1, 64) BQD_W4A16_CASE(2, 64) BQD_W4A16_CASE(4, 64) BQD_W4A16_CASE(8, 64)
+#undef BQD_W4A16_CASE
     return BQD_ERR_CONFIG;
 }
 

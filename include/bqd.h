@@ -183,6 +183,20 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
                        float* y, int32_t N, int32_t K, int32_t r,
                        int32_t lanes_per_row, void* stream);
 
+/* W4A16 comparison GEMV: the same packed per-row INT4 weights against an
+ * fp16 activation, unpacked to fp16 and multiplied in floating point (the
+ * route "Jetson Orin AGX INT4 ..." section "为什么 INT4 float 解包不快"
+ * weighs against the integer dot; "在香橙派上跑 Gemma4 ..." section 3.1
+ * dequantises to fp16 for fp16 MACs):
+ *   y[j] = sw[j] * sum_i q^W[j,i] * x[i] + bias[j]   (fp32 accumulation)
+ * wq (device) uint32 [N, K/8]; sw, bias (device) float [N] (bias may be
+ * NULL); x16 (device) uint16 fp16 bit patterns [K], 16-byte aligned;
+ * y (device) float [N].  K <= 32768.  r, lanes_per_row as in gemv_w4a8,
+ * except that 0 picks 64 lanes and 2 rows per lane group when N >= 16384,
+ * else 1. */
+int gemv_w4a16(const uint32_t* wq, const float* sw, const float* bias, const uint16_t* x16, float* y,
+               int32_t N, int32_t K, int32_t r, int32_t lanes_per_row, void* stream);
+
 /* M-token verification ("在香橙派上跑 Gemma4 ...", section 5): one pass over the
  * weights serves M quantised tokens.
  *   acc[m,j] = sum_i q^W[j,i] * qx[m,i],  y[m,j] = (sw[j] * sx[m]) * acc[m,j] + bias[j]

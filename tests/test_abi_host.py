@@ -206,3 +206,14 @@ def test_read_probe_validates_before_launch():
     assert L.read_probe(None, 64, P, 8, 1, None) == NULL
     assert L.read_probe(P + 8, 64, P, 8, 1, None) == ALIGN
     assert L.read_probe(P, 0, None, 8, 1, None) == OK
+
+
+def test_gemv_w4a16_validates_before_launch():
+    L = _lib()
+    # gemv_w4a16(wq, sw, bias, x16, y, N, K, r, lanes, stream)
+    assert L.gemv_w4a16(P, P, None, P, P, 8, 48, 0, 0, None) == SHAPE
+    assert L.gemv_w4a16(P, P, None, P, P, 8, 65536, 0, 0, None) == BOUND
+    assert L.gemv_w4a16(P, P, None, None, P, 8, 64, 0, 0, None) == NULL
+    assert L.gemv_w4a16(P, P, None, P + 8, P, 8, 64, 0, 0, None) == ALIGN
+    assert L.gemv_w4a16(P, P, None, P, P, 8, 64, 3, 0, None) == CONFIG
+    assert L.gemv_w4a16(P, P, None, P, P, 0, 64, 0, 0, None) == OK

@@ -316,6 +316,40 @@ def test_gemv_w8a16_lm_head_codes_from_weights():
     assert rel_err(npy(y), yr, mag).max() <= TOL
 
 
+# --------------------------------------------------- W4A16 comparison --
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 96), (3584, 3584), (300, 18944), (16389, 64)])
+def test_gemv_w4a16(N, K):
+    """Float-unpack GEMV against the oracle: random words (every nibble,
+    -8 included) and fp16 x; every (r, lanes) configuration (N = 16389: the
+    automatic two-rows-per-wave shape with a ragged last tile)."""
+    w, _, sw, b, _ = _rand_gemv(N, K, f"w4a16/{N}/{K}")
+    x16 = I.normal(f"gpu/w4a16/{N}/{K}/x", K, 1.0, device=DEV, dtype=torch.float16)
+    yr = O.gemv_w4a16(u32(w), npy(sw), npy(b), f16bits(x16))
+    q = np.abs(O.unpack_int4(u32(w))).astype(np.float64)
+    mag = np.abs(npy(sw)).astype(np.float64) * (q @ np.abs(npy(x16).astype(np.float64))) + np.abs(npy(b))
+    for r, L in ((0, 0), (1, 16), (2, 32), (4, 64), (8, 16)):
+        y = bqd.gemv_w4a16(w, sw, b, x16, r=r, lanes_per_row=L)
+        sync()
+        assert rel_err(npy(y), yr, mag).max() <= TOL, (r, L)
+    y0 = bqd.gemv_w4a16(w, sw, None, x16)
+    sync()
+    yr0 = O.gemv_w4a16(u32(w), npy(sw), None, f16bits(x16))
+    assert rel_err(npy(y0), yr0, mag).max() <= TOL
+
+
+def test_gemv_w4a16_integer_x_equals_w4a8():
+    """x = fp16 of the int8 codes and s^x = 1: the float route reproduces the
+    integer-dot GEMV (fp32 sums of integers below 2^24 are exact)."""
+    N, K = 512, 3584
+    w, qx, sw, b, _ = _rand_gemv(N, K, "w4a16int")
+    one = torch.ones(1, device=DEV)
+    y8, acc = bqd.gemv_w4a8(w, sw, b, qx, one, acc=True)
+    y16 = bqd.gemv_w4a16(w, sw, b, qx.to(torch.float16))
+    sync()
+    assert np.abs(npy(acc)).max() < 2 ** 24
+    assert torch.equal(y8, y16)
+
+
 # -------------------------------------------------------------- verify --
 @pytest.mark.parametrize("impl", [0, 1, 2])
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16])
