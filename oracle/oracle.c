@@ -445,3 +445,146 @@ int orc_gemm_w4a8_verify(const uint32_t* w, const float* sw, const float* bias,
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Producers of the activation, fused with its quantisation ([Orin]          */
+/* "后续还能继续优化什么", items 1 and 2: RMSNorm, quantisation, SwiGLU and  */
+/* the residual add still sit behind separate kernels, and the activation    */
+/* quantisation could be fused with the operator before it).  The page names */
+/* these operators without defining them; the textbook forms are used:       */
+/*   RMSNorm  y_i = h_i / sqrt(mean_k h_k^2 + eps) * gamma_i                 */
+/*   SwiGLU   h_i = silu(g_i) * u_i,  silu(g) = g / (1 + e^-g)               */
+/* followed by the per-token quantisation above.  Every value that decides   */
+/* a code is an fp32 result of a fully specified sequence of IEEE           */
+/* operations, so any implementation of the same sequence obtains the same  */
+/* codes.                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* e^x in fp32: Cody & Waite's argument reduction x = n ln2 + r with
+ * n = round(x / ln2) and ln2 split into a head with 9 significant bits
+ * (n * head is exact) and a tail, then the degree-7 Taylor polynomial of
+ * e^r (|r| <= ln2 / 2, truncation below 6e-9 relative) in Horner form,
+ * coefficients fp32(1/k!), and e^x = p * 2^n.  Every step is one IEEE fp32
+ * operation (fmaf is a single rounding).  x is clamped to [-104, 89], where
+ * the result already underflows to 0 or overflows to +Inf. */
+float orc_exp_f32(float x)
+{
+    if (x != x)
+        return x;
+    if (x > 89.0f)
+        x = 89.0f;
+    if (x < -104.0f)
+        x = -104.0f;
+    const float n = nearbyintf(x * 1.44269504088896341f);
+    float r = fmaf(-n, 0.693359375f, x);
+    r = fmaf(-n, -2.12194440054690583e-4f, r);
+    float p = (float)(1.0 / 5040.0);
+    p = fmaf(p, r, (float)(1.0 / 720.0));
+    p = fmaf(p, r, (float)(1.0 / 120.0));
+    p = fmaf(p, r, (float)(1.0 / 24.0));
+    p = fmaf(p, r, (float)(1.0 / 6.0));
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)n);
+}
+
+void orc_exp_f32_array(const float* x, int64_t n, float* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_exp_f32(x[i]);
+}
+
+/* Residual add, RMSNorm and quantisation of M tokens of K values:
+ *   h1 = h + delta                              (fp32; delta may be NULL)
+ *   ms = sum_i h1_i^2 / K                       (binary64: each square is exact)
+ *   r  = fp32(1 / sqrt(ms + eps))               (binary64, one final rounding)
+ *   y_i = (h1_i * r) * gamma_i                  (two fp32 products)
+ *   s^x = max|y| / 127, q_i = clip(round(y_i / s^x), -127, 127).
+ * h_out (h1) and y_out are optional.  eps >= 0; a token with ms + eps = 0
+ * (all zero, eps = 0) normalises to zeros. */
+int orc_add_rmsnorm_quant(const float* h, const float* delta, const float* gamma, float eps,
+                          int64_t M, int64_t K, float* h_out, float* y_out, int8_t* q, float* s)
+{
+    if (M < 0 || K <= 0 || !(eps >= 0.0f) || !(eps <= FLT_MAX))
+        return ORC_E_ARG;
+    for (int64_t i = 0; i < K; ++i)
+        if (!(fabsf(gamma[i]) <= FLT_MAX))
+            return ORC_E_NONFINITE;
+    for (int64_t m = 0; m < M; ++m) {
+        const float* hm = h + m * K;
+        const float* dm = delta ? delta + m * K : NULL;
+        /* residual add and the mean square */
+        double ss = 0.0;
+        for (int64_t i = 0; i < K; ++i) {
+            const float a = dm ? hm[i] + dm[i] : hm[i];
+            if (!(fabsf(a) <= FLT_MAX))
+                return ORC_E_NONFINITE;
+            ss += (double)a * (double)a;
+            if (h_out)
+                h_out[m * K + i] = a;
+        }
+        const double v = ss / (double)K + (double)eps;
+        const float r = v > 0.0 ? (float)(1.0 / sqrt(v)) : 0.0f;
+        if (!(r <= FLT_MAX))
+            return ORC_E_RANGE;
+        /* normalised values and their largest magnitude */
+        float amax = 0.0f;
+        for (int64_t i = 0; i < K; ++i) {
+            const float a = dm ? hm[i] + dm[i] : hm[i];
+            const float y = (a * r) * gamma[i];
+            if (!(fabsf(y) <= FLT_MAX))
+                return ORC_E_RANGE;
+            if (fabsf(y) > amax)
+                amax = fabsf(y);
+            if (y_out)
+                y_out[m * K + i] = y;
+        }
+        /* per-token quantisation */
+        const float sx = amax / 127.0f;
+        s[m] = sx;
+        for (int64_t i = 0; i < K; ++i) {
+            const float a = dm ? hm[i] + dm[i] : hm[i];
+            q[m * K + i] = quant_code((a * r) * gamma[i], sx, -127, 127);
+        }
+    }
+    return ORC_OK;
+}
+
+/* SwiGLU and quantisation of M tokens.  gu holds each token's fused
+ * gate/up projection output, [M, 2I]: gate g = gu[m, 0:I], up u = gu[m, I:2I].
+ *   e = exp_f32(-g_i); h_i = (g_i / (1 + e)) * u_i   (fp32, correctly rounded
+ *   division), then the per-token quantisation.  h_out is optional. */
+int orc_swiglu_quant(const float* gu, int64_t M, int64_t I, float* h_out, int8_t* q, float* s)
+{
+    if (M < 0 || I <= 0)
+        return ORC_E_ARG;
+    for (int64_t m = 0; m < M; ++m) {
+        const float* g = gu + m * 2 * I;
+        const float* u = g + I;
+        float* hv = h_out ? h_out + m * I : NULL;
+        for (int64_t i = 0; i < I; ++i) {
+            if (!(fabsf(g[i]) <= FLT_MAX) || !(fabsf(u[i]) <= FLT_MAX))
+                return ORC_E_NONFINITE;
+            const float e = orc_exp_f32(-g[i]);
+            const float t = (g[i] / (1.0f + e)) * u[i];
+            if (!(fabsf(t) <= FLT_MAX))
+                return ORC_E_RANGE;
+        }
+        float amax = 0.0f;
+        for (int64_t i = 0; i < I; ++i) {
+            const float t = (g[i] / (1.0f + orc_exp_f32(-g[i]))) * u[i];
+            if (fabsf(t) > amax)
+                amax = fabsf(t);
+            if (hv)
+                hv[i] = t;
+        }
+        const float sx = amax / 127.0f;
+        s[m] = sx;
+        for (int64_t i = 0; i < I; ++i) {
+            const float t = (g[i] / (1.0f + orc_exp_f32(-g[i]))) * u[i];
+            q[m * I + i] = quant_code(t, sx, -127, 127);
+        }
+    }
+    return ORC_OK;
+}

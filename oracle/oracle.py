@@ -53,6 +53,10 @@ def _load():
         "orc_gemv_w8a16_group32": (I32, [P, P, P, I64, I64, P]),
         "orc_gemm_w4a8_verify": (I32, [P, P, P, P, P, I64, I64, I64, P, P]),
         "orc_gemv_w4a16": (I32, [P, P, P, P, I64, I64, P]),
+        "orc_exp_f32": (C.c_float, [C.c_float]),
+        "orc_exp_f32_array": (None, [P, I64, P]),
+        "orc_add_rmsnorm_quant": (I32, [P, P, P, F32, I64, I64, P, P, P, P]),
+        "orc_swiglu_quant": (I32, [P, I64, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -175,6 +179,60 @@ def quantize_act(x) -> Tuple[np.ndarray, np.ndarray]:
         xf = _c(x2, np.float32)
         _check(_lib.orc_quantize_act_f32(_p(xf), M, K, _p(q), _p(s)))
     return (q[0], s[0]) if one else (q, s)
+
+
+# ------------------------------------------- producers fused with quant ----
+def exp_f32(x) -> np.ndarray:
+    """e^x in fp32 by Cody-Waite reduction and a degree-7 Taylor polynomial,
+    every step one IEEE fp32 operation (the exponential inside SwiGLU)."""
+    x = _c(x, np.float32)
+    out = np.empty_like(x)
+    _lib.orc_exp_f32_array(_p(x), x.size, _p(out))
+    return out
+
+
+def add_rmsnorm_quant(h, delta, gamma, eps: float):
+    """Residual add, RMSNorm and per-token quantisation ([Orin] "后续还能继续优化什么",
+    items 1-2; textbook RMSNorm).  h, delta fp32 [K] or [M, K] (delta may be
+    None), gamma fp32 [K].  Returns (q int8, s fp32, h1 = h + delta, y = the
+    normalised fp32 values), shaped like h (s: [] or [M])."""
+    h = np.asarray(h)
+    one = h.ndim == 1
+    h2 = _c(h.reshape(1, -1) if one else h, np.float32)
+    M, K = h2.shape
+    d = None if delta is None else _c(np.asarray(delta).reshape(M, K), np.float32)
+    g = _c(gamma, np.float32)
+    if g.size != K:
+        raise ValueError("gamma must hold K values")
+    q = np.empty((M, K), np.int8)
+    s = np.empty(M, np.float32)
+    h1 = np.empty((M, K), np.float32)
+    y = np.empty((M, K), np.float32)
+    _check(_lib.orc_add_rmsnorm_quant(_p(h2), _p(d), _p(g), C.c_float(eps), M, K, _p(h1), _p(y),
+                                      _p(q), _p(s)))
+    if one:
+        return q[0], s[0], h1[0], y[0]
+    return q, s, h1, y
+
+
+def swiglu_quant(gu):
+    """SwiGLU h = silu(g) * u of the fused gate/up output gu = [g | u]
+    ([M, 2I] or [2I]) and per-token quantisation.  Returns (q int8, s fp32,
+    h fp32)."""
+    gu = np.asarray(gu)
+    one = gu.ndim == 1
+    g2 = _c(gu.reshape(1, -1) if one else gu, np.float32)
+    M, I2 = g2.shape
+    if I2 % 2:
+        raise ValueError("gu must hold 2I values per token")
+    I = I2 // 2
+    q = np.empty((M, I), np.int8)
+    s = np.empty(M, np.float32)
+    h = np.empty((M, I), np.float32)
+    _check(_lib.orc_swiglu_quant(_p(g2), M, I, _p(h), _p(q), _p(s)))
+    if one:
+        return q[0], s[0], h[0]
+    return q, s, h
 
 
 # -------------------------------------------------------------- GEMVs ----

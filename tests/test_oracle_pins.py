@@ -445,3 +445,130 @@ def test_errors_are_reported():
     with pytest.raises(O.OracleError):   # -128 is outside the activation code range
         O.gemv_w4a8(np.zeros((1, 1), np.uint32), np.ones(1, np.float32), None,
                     np.array([-128] + [0] * 7, np.int8), 1.0)
+
+
+# ------------------------------------------- producers fused with quant --
+# The page names RMSNorm, SwiGLU and the residual add as the operators whose
+# kernel boundaries could go ([Orin] "后续还能继续优化什么", items 1-2); the
+# textbook definitions are checked here against numpy float64.
+def _ulps(got, ref64):
+    """|got - ref| in units of the fp32 spacing at ref (ref in float64)."""
+    ref32 = ref64.astype(np.float32)
+    return np.abs(got.astype(np.float64) - ref64) / np.spacing(np.abs(ref32)).astype(np.float64)
+
+
+def _codes_tie_aware(q, v64):
+    """Codes of fp32 values against round-half-even of the float64 values:
+    equal, except within 1e-4 of a rounding tie, where either neighbour is
+    accepted (the float64 reference and the fp32 decision may fall on either
+    side)."""
+    amax = np.abs(v64).max(axis=-1, keepdims=True)
+    t = v64 / np.where(amax > 0, amax / 127.0, 1.0)
+    near = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-4
+    exact = np.clip(np.round(t), -127, 127)
+    ok = (q == exact) | (near & ((q == np.floor(t)) | (q == np.ceil(t))))
+    return ok.all(), int(near.sum())
+
+
+def test_exp_f32_within_two_ulps_of_numpy_float64():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([np.linspace(-87.0, 88.0, 1_000_001).astype(np.float32),
+                        rng.uniform(-87.0, 88.0, 200_000).astype(np.float32),
+                        (np.arange(-120, 121) * np.float32(0.6931472)).astype(np.float32),
+                        np.array([0.0, -0.0, 1e-30, -1e-30, 0.5, -0.5], np.float32)])
+    x = x[(x > -87.0) & (x < 88.0)]
+    got = O.exp_f32(x)
+    assert _ulps(got, np.exp(x.astype(np.float64))).max() <= 2.0
+    xs = np.sort(x)
+    assert np.all(np.diff(O.exp_f32(xs)) >= 0)  # monotone
+    assert O.exp_f32(np.float32([0.0]))[0] == 1.0
+    assert O.exp_f32(np.float32([89.0, 200.0]))[0] == np.inf
+    assert np.all(O.exp_f32(np.float32([-104.0, -300.0])) == 0.0)
+
+
+def test_swiglu_vs_numpy_float64():
+    rng = np.random.default_rng(11)
+    M, I_ = 3, 4096
+    g = (rng.standard_normal((M, I_)) * 2.0).astype(np.float32)
+    u = rng.standard_normal((M, I_)).astype(np.float32)
+    q, s, h = O.swiglu_quant(np.concatenate([g, u], axis=1))
+    g64, u64 = g.astype(np.float64), u.astype(np.float64)
+    h64 = g64 * u64 / (1.0 + np.exp(-g64))
+    assert _ulps(h, h64).max() <= 4.0
+    np.testing.assert_allclose(s, np.abs(h64).max(1) / 127.0, rtol=1e-6)
+    ok, near = _codes_tie_aware(q, h64)
+    assert ok and near < 10
+
+
+def test_swiglu_closed_forms_and_permutation():
+    rng = np.random.default_rng(12)
+    I_ = 512
+    # gate 0 (or up 0): h = 0, every code 0, s = 0
+    for gu in (np.concatenate([np.zeros(I_), rng.standard_normal(I_)]),
+               np.concatenate([rng.standard_normal(I_), np.zeros(I_)])):
+        q, s, h = O.swiglu_quant(gu.astype(np.float32))
+        assert s == 0.0 and not q.any() and not np.abs(h).any()
+    # gate >= 30: e^-g < 2^-24, so 1 + e rounds to 1 and silu(g) = g exactly
+    g = rng.uniform(30.0, 80.0, I_).astype(np.float32)
+    u = rng.standard_normal(I_).astype(np.float32)
+    _, _, h = O.swiglu_quant(np.concatenate([g, u]))
+    assert np.array_equal(h, g * u)
+    # pairs (g_i, u_i) permuted together permute h and the codes
+    g = rng.standard_normal(I_).astype(np.float32)
+    perm = rng.permutation(I_)
+    q, s, h = O.swiglu_quant(np.concatenate([g, u]))
+    qp, sp, hp = O.swiglu_quant(np.concatenate([g[perm], u[perm]]))
+    assert sp == s and np.array_equal(hp, h[perm]) and np.array_equal(qp, q[perm])
+
+
+def test_rmsnorm_vs_numpy_float64():
+    rng = np.random.default_rng(13)
+    M, K, eps = 3, 3584, 1e-6
+    h = rng.standard_normal((M, K)).astype(np.float32)
+    d = (rng.standard_normal((M, K)) * 0.5).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(K)).astype(np.float32)
+    q, s, h1, y = O.add_rmsnorm_quant(h, d, gamma, eps)
+    assert np.array_equal(h1, h + d)  # numpy's IEEE fp32 add
+    a = h1.astype(np.float64)
+    y64 = a / np.sqrt((a * a).mean(1, keepdims=True) + eps) * gamma.astype(np.float64)
+    assert _ulps(y, y64).max() <= 4.0
+    np.testing.assert_allclose(s, np.abs(y64).max(1) / 127.0, rtol=1e-6)
+    ok, near = _codes_tie_aware(q, y64)
+    assert ok and near < 10
+    # no residual: the same as a zero residual
+    q0, s0, h10, y0 = O.add_rmsnorm_quant(h, None, gamma, eps)
+    qz, sz, h1z, yz = O.add_rmsnorm_quant(h, np.zeros_like(h), gamma, eps)
+    assert np.array_equal(q0, qz) and np.array_equal(s0, sz) and np.array_equal(y0, yz)
+
+
+def test_rmsnorm_closed_forms():
+    K = 64
+    one = np.ones(K, np.float32)
+    # a constant token normalises to +-1: every code is +-127
+    for c in (3.0, -0.25, 1e-20):
+        q, s, _, y = O.add_rmsnorm_quant(np.full(K, c, np.float32), None, one, 0.0)
+        assert np.all(q == np.sign(c) * 127)
+        assert np.all(np.abs(np.abs(y) - 1.0) <= 2.0 ** -23)
+    # one spike a at index 5: r = 8 / |a|, y_5 = 8 sign(a), every other code 0
+    for a in (5.0, -1e3):
+        h = np.zeros(K, np.float32)
+        h[5] = a
+        q, s, _, y = O.add_rmsnorm_quant(h, None, one, 0.0)
+        assert q[5] == np.sign(a) * 127 and np.count_nonzero(q) == 1
+        assert abs(abs(float(y[5])) - 8.0) <= 8.0 * 2.0 ** -23
+    # an all-zero token with eps = 0 normalises to zeros
+    q, s, _, y = O.add_rmsnorm_quant(np.zeros(K, np.float32), None, one, 0.0)
+    assert s == 0.0 and not q.any() and not y.any()
+
+
+def test_rmsnorm_power_of_two_scale_invariance():
+    """eps = 0: scaling h by 2^k scales the mean square by 4^k and r by 2^-k
+    exactly, so y, s and the codes do not change."""
+    rng = np.random.default_rng(14)
+    h = rng.standard_normal(3584).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(3584)).astype(np.float32)
+    q, s, _, y = O.add_rmsnorm_quant(h, None, gamma, 0.0)
+    for k in (-20, 7, 30):
+        qk, sk, h1k, yk = O.add_rmsnorm_quant(np.ldexp(h, k), None, gamma, 0.0)
+        assert np.array_equal(qk, q) and sk == s and np.array_equal(yk, y)
+        assert np.array_equal(h1k, np.ldexp(h, k))
