@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) for W4A8 decode GEMV; implied 28-layer tok/s"
 HBM_PEAK_GBS = 8000.0
-WORKLOADS = ("stream", "single", "layer", "gemma", "verify")
+WORKLOADS = ("stream", "single", "layer", "gemma", "verify", "chain")
 
 
 def parse():
@@ -515,6 +515,113 @@ def run_verify(a, dev):
     return out
 
 
+def run_chain(a, dev):
+    """The 28-layer stream wired into a decoder's data flow with the
+    activation producers (residual add + RMSNorm, SwiGLU) fused with the
+    quantisation, one HIP graph per token; the same chain with fp32
+    producers and consumer-side quantisation is timed beside it."""
+    import torch
+    from bit_quantized_decode_quantize_amd import bqd
+    from bit_quantized_decode_quantize_amd import decode_stream as DS
+
+    layers = a.layers or 28
+    s = DS.QwenW4A8Stream(layers=layers, device=dev, persistent=False)
+    c = DS.DecodeChain(s)
+    log(f"chain built: {c.launches_per_step()} launches per token")
+    c.step(True)
+    torch.cuda.synchronize()
+    logits_fused = c.output().clone()
+    c.step(False)
+    torch.cuda.synchronize()
+    if not torch.equal(logits_fused, c.output()):
+        raise RuntimeError("fused and unfused chains disagree")
+    graph = 0 if a.eager else 1
+    ms, n = time_steps(lambda: c.step(True), a.steps, a.warmup, graph)
+    ms_u, _ = time_steps(lambda: c.step(False), a.steps, a.warmup, graph)
+    step_bytes = c.bytes_per_step(True)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+
+    # Kernel durations in an eager pass: events around the producers and
+    # around the int8 GEMVs of gate/up and the lm_head (most of the bytes).
+    st = torch.cuda.current_stream()
+    spans = {"add_rmsnorm_quant": [], "swiglu_quant": [], "gemv": []}
+    gemv_bytes = []
+    real = dict(add_rmsnorm_quant=bqd.add_rmsnorm_quant, swiglu_quant=bqd.swiglu_quant, gemv_w4a8=bqd.gemv_w4a8)
+
+    def timed(name, key):
+        def f(*args, **kw):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            real[name](*args, **kw)
+            e1.record(st)
+            if key == "gemv":
+                N, K = args[0].shape[0], args[0].shape[1] * 8
+                if N >= 37888:
+                    spans[key].append((e0, e1))
+                    gemv_bytes.append(DS.gemv_bytes_q8(N, K, args[2] is not None))
+            else:
+                spans[key].append((e0, e1))
+        return f
+    try:
+        bqd.add_rmsnorm_quant = timed("add_rmsnorm_quant", "add_rmsnorm_quant")
+        bqd.swiglu_quant = timed("swiglu_quant", "swiglu_quant")
+        bqd.gemv_w4a8 = timed("gemv_w4a8", "gemv")
+        for _ in range(max(1, a.steps // 5)):
+            c.step(True)
+    finally:
+        bqd.add_rmsnorm_quant, bqd.swiglu_quant, bqd.gemv_w4a8 = (
+            real["add_rmsnorm_quant"], real["swiglu_quant"], real["gemv_w4a8"])
+    torch.cuda.synchronize()
+    avg = {k: sum(e0.elapsed_time(e1) for e0, e1 in v) * 1e3 / len(v) for k, v in spans.items()}
+    avg_bytes = sum(gemv_bytes) / len(gemv_bytes)
+    out = base_line(a, gbs, ms, n, {
+        "workload": f"qwen2-7b-shaped {layers}-layer decode chain: residual add + RMSNorm + quant -> QKV, "
+                    "O (synthetic attention output), residual add + RMSNorm + quant -> gate/up, "
+                    "SwiGLU + quant -> down, final RMSNorm + quant -> int4 lm_head",
+        "launch": "per-kernel, one HIP graph per token" if graph else "per-kernel",
+        "layers": layers, "launches_per_step": c.launches_per_step(), "bytes_per_step": step_bytes})
+    out["tok_per_s"] = round(1e3 / ms, 2)
+    out["unfused_ms_per_step"] = round(ms_u, 5)
+    out["unfused_bytes_per_step"] = c.bytes_per_step(False)
+    out["producer_us"] = {k: round(avg[k], 2) for k in ("add_rmsnorm_quant", "swiglu_quant")}
+    out["roofline"] = roofline(avg_bytes / (avg["gemv"] * 1e-6) / 1e9,
+                               "k_gemv_w4a8 on int8 codes (gate/up and lm_head)", avg["gemv"], avg_bytes)
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_chain(c, a.cpu_seconds)
+    return out
+
+
+def cpu_baseline_chain(c, seconds):
+    """The C oracle, single-threaded, over layer 0 of the chain (RMSNorm +
+    quant, QKV, O with its own quantisation, RMSNorm + quant, gate/up,
+    SwiGLU + quant, down), repeated for about ``seconds``."""
+    import torch
+    import oracle as O
+    from bit_quantized_decode_quantize_amd import decode_stream as DS
+    lin = c.by_layer[0]
+    prep = {}
+    for name, d in lin.items():
+        W = c.s.fp32_rows(d, torch.arange(d["N"], device=d["wq"].device)).cpu().numpy()
+        prep[name] = O.prepare_int4_rowwise(W) + (d["b"].cpu().numpy(),)
+    h0 = c.h_in.cpu().numpy()
+    g0, g1 = c.gamma[0].cpu().numpy(), c.gamma[1].cpu().numpy()
+    xo = lin["o"]["x"].cpu().numpy()
+    sample = c.bytes_per_step(True) // (len(c.by_layer) + 1)
+
+    def once():
+        q, s, h1, _ = O.add_rmsnorm_quant(h0, None, g0, DS.RMS_EPS)
+        O.gemv_w4a8(*prep["qkv"][:2], prep["qkv"][2], q[0], float(s[0]))
+        _, _, _, yo = O.linear_w4a8(*prep["o"][:2], prep["o"][2], xo)
+        q, s, h2, _ = O.add_rmsnorm_quant(h1, yo.astype("float32").reshape(1, -1), g1, DS.RMS_EPS)
+        _, ygu = O.gemv_w4a8(*prep["gate_up"][:2], prep["gate_up"][2], q[0], float(s[0]))
+        qd, sd, _ = O.swiglu_quant(ygu.astype("float32"))
+        O.gemv_w4a8(*prep["down"][:2], prep["down"][2], qd, float(sd))
+    gbs, reps, el = cpu_loop(once, sample, seconds)
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0 of the chain (~{sample} algorithmic bytes, a layer's share of the step), "
+                      f"{reps} passes in {el:.1f} s, single-threaded C"}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -525,7 +632,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     out = {"stream": run_stream, "single": run_single, "layer": run_layer, "gemma": run_gemma,
-           "verify": run_verify}[a.workload](a, dev)
+           "verify": run_verify, "chain": run_chain}[a.workload](a, dev)
     print(json.dumps(out), flush=True)
 
 

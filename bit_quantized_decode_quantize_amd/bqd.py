@@ -24,6 +24,7 @@ BQD_F32, BQD_F16 = 0, 1
 BQD_SCALE_ROW_F32, BQD_SCALE_GROUP32_F16 = 0, 1
 BQD_MAX_K = 65536
 BQD_MAX_TOKENS = 16
+BQD_MAX_PROD_K = 32768
 
 ENTRY_POINTS = (
     "bqd_abi_version", "bqd_status_string", "bqd_init",
@@ -32,7 +33,7 @@ ENTRY_POINTS = (
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
     "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
-    "read_probe", "gemv_w4a16",
+    "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant",
 )
 
 
@@ -85,6 +86,8 @@ def lib() -> C.CDLL:
         "decode_pass_w4a8": (I, [P, I, I, P, I, P]),
         "read_probe": (I, [P, C.c_size_t, P, I, I, P]),
         "gemv_w4a16": (I, [P, P, P, P, P, I, I, I, I, P]),
+        "add_rmsnorm_quant": (I, [P, P, P, C.c_float, P, P, P, P, I, I, P]),
+        "swiglu_quant": (I, [P, P, P, P, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -215,6 +218,51 @@ def quantize_act(x: torch.Tensor, qx=None, sx=None, stream=None):
     sx = _empty((M,), torch.float32, x) if sx is None else _dev(sx, "sx", _F32, M)
     _call("quantize_act", x.data_ptr(), _xdtype(x), M, K, qx.data_ptr(), sx.data_ptr(),
           _stream(stream))
+    return qx, sx
+
+
+def add_rmsnorm_quant(h, gamma, eps: float, delta=None, qx=None, sx=None, h_out=None, y_out=None,
+                      quantize: bool = True, stream=None):
+    """Residual add + RMSNorm + per-token quantisation of h fp32 [K] or [M, K]
+    (delta: optional residual of the same shape; gamma fp32 [K]).  Returns
+    (qx int8 like h, sx fp32 [M]); with quantize=False returns (None, None)
+    and writes only the optional fp32 outputs h_out (h + delta) and y_out."""
+    _dev(h, "h", _F32)
+    h2 = h.view(1, -1) if h.dim() == 1 else h
+    M, K = h2.shape
+    _opt(delta, "delta", _F32, M * K)
+    _dev(gamma, "gamma", _F32, K)
+    _opt(h_out, "h_out", _F32, M * K)
+    _opt(y_out, "y_out", _F32, M * K)
+    if quantize:
+        qx = _empty(h.shape, torch.int8, h) if qx is None else _dev(qx, "qx", (torch.int8,), M * K)
+        sx = _empty((M,), torch.float32, h) if sx is None else _dev(sx, "sx", _F32, M)
+    else:
+        qx = sx = None
+    _call("add_rmsnorm_quant", h.data_ptr(), _ptr(delta), gamma.data_ptr(), float(eps), _ptr(h_out),
+          _ptr(y_out), _ptr(qx), _ptr(sx), M, K, _stream(stream))
+    return qx, sx
+
+
+def swiglu_quant(gu, qx=None, sx=None, h_out=None, quantize: bool = True, stream=None):
+    """SwiGLU of the fused gate/up output gu fp32 [2I] or [M, 2I] (gate, then
+    up) + per-token quantisation.  h_out (fp32 [M, I]) receives h and is
+    allocated when not given.  Returns (qx int8 [M, I] (or [I]), sx fp32
+    [M]); with quantize=False returns (None, None) and writes only h_out."""
+    _dev(gu, "gu", _F32)
+    g2 = gu.view(1, -1) if gu.dim() == 1 else gu
+    M, I2 = g2.shape
+    if I2 % 2:
+        raise ValueError("gu must hold 2I values per token")
+    I_ = I2 // 2
+    h_out = _empty((M, I_), torch.float32, gu) if h_out is None else _dev(h_out, "h_out", _F32, M * I_)
+    shape = (I_,) if gu.dim() == 1 else (M, I_)
+    if quantize:
+        qx = _empty(shape, torch.int8, gu) if qx is None else _dev(qx, "qx", (torch.int8,), M * I_)
+        sx = _empty((M,), torch.float32, gu) if sx is None else _dev(sx, "sx", _F32, M)
+    else:
+        qx = sx = None
+    _call("swiglu_quant", gu.data_ptr(), _ptr(h_out), _ptr(qx), _ptr(sx), M, I_, _stream(stream))
     return qx, sx
 
 

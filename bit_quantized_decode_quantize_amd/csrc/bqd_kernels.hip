@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cfloat>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -228,6 +229,62 @@ __device__ __forceinline__ void quant8(const float v[8], const ActScale& a, uint
     hi = act_code(v[4], a) | (act_code(v[5], a) << 8) | (act_code(v[6], a) << 16) | (act_code(v[7], a) << 24);
 }
 
+// Codes of 8 values, bytes lo = codes 0..3, hi = codes 4..7, bit-identical to
+// act_code: the reciprocal route for all 8, then one (rare) branch to the
+// exact quotient if any of them lies within 2^-15 of a rounding tie.
+__device__ __forceinline__ void quant8_fast(const float v[8], const ActScale& a, uint32_t& lo, uint32_t& hi)
+{
+    float m[8];
+    bool near = !a.fast;
+    if (a.fast) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r = v[e] * a.inv;
+            m[e] = rintf(r);
+            near |= fabsf(r - m[e]) > 0.5f - 0x1p-15f;
+        }
+    }
+    if (near) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            m[e] = a.s == 0.0f ? 0.0f : rintf(v[e] / a.s);
+    }
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        b[e] = (uint32_t)((int)__builtin_amdgcn_fmed3f(m[e], -127.0f, 127.0f)) & 0xFFu;
+    lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+}
+
+
+// Four values, the same rule: the exact quotient for all four whenever one
+// of them lies near a rounding tie.
+__device__ __forceinline__ uint32_t quant4_fast(f32x4 v, const ActScale& a)
+{
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    float m[4];
+    bool near = !a.fast;
+    if (a.fast) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float r = x[e] * a.inv;
+            m[e] = rintf(r);
+            near |= fabsf(r - m[e]) > 0.5f - 0x1p-15f;
+        }
+    }
+    if (near) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            m[e] = a.s == 0.0f ? 0.0f : rintf(x[e] / a.s);
+    }
+    uint32_t q = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        q |= ((uint32_t)((int)__builtin_amdgcn_fmed3f(m[e], -127.0f, 127.0f)) & 0xFFu) << (8 * e);
+    return q;
+}
+
 // Stage G8 = K/8 groups of INT8 codes into LDS (permuted), from int8 memory.
 __device__ __forceinline__ void stage_q8(u32x2* xs, const int8_t* qx, int G8)
 {
@@ -401,6 +458,214 @@ __global__ __launch_bounds__(kThreads) void k_quantize_act(const void* __restric
     }
     if (threadIdx.x == 0)
         sx[m] = a.s;
+}
+
+// ------------------------------------------------------------------------
+// Producers of a linear's activation fused with its quantisation ([Orin]
+// "后续还能继续优化什么", items 1 and 2: the residual add, RMSNorm and SwiGLU
+// still end in their own kernels, and the quantisation could be folded into
+// the operator before it).  Textbook forms: RMSNorm y = h / sqrt(mean h^2 +
+// eps) * gamma, SwiGLU h = silu(g) * u.  Every value that decides a code is
+// an fp32 result of a fixed sequence of IEEE operations (the sum of squares
+// aside, which is accumulated in fp64, where each square is exact), so the
+// codes do not depend on the order of the reductions.
+//   RMSNorm: one workgroup of 1024 threads per token holds the token in
+//   registers (ITEMS 16-byte items per thread, every load issued before the
+//   first use): one memory round trip, a sum and a max over the workgroup,
+//   then the codes.
+//   SwiGLU: the elementwise part is spread over many workgroups (it costs
+//   ~30 VALU operations per value); a second kernel then takes the row's max
+//   in each of a few workgroups and quantises one slice per workgroup.
+// ------------------------------------------------------------------------
+constexpr int kProdThreads = 1024;
+constexpr int kProdWaves = kProdThreads / kWave;
+constexpr int kProdMaxK = BQD_MAX_PROD_K;
+static_assert(kProdMaxK <= 8 * 4 * kProdThreads, "at most 8 items of 4 values per thread");
+
+__device__ __forceinline__ float prod_block_max(float v, float* red)
+{
+    v = wave_max(v);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kProdWaves; ++w)
+        m = fmaxf(m, red[w]);
+    __syncthreads();
+    return m;
+}
+
+// fp64 sum over the workgroup, the same value in every thread.
+__device__ __forceinline__ double prod_block_sum(double v, double* red)
+{
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1)
+        v += __shfl_xor(v, m);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kProdWaves; ++w)
+        t += red[w];
+    __syncthreads();
+    return t;
+}
+
+// e^x in fp32 (W. J. Cody and W. Waite, "Software Manual for the Elementary
+// Functions", 1980: x = n ln2 + r, n = round(x / ln2), ln2 split into a
+// 9-significant-bit head, exact against any |n| < 2^15, and a tail), then
+// e^r by its degree-7 Taylor polynomial in Horner form (|r| <= ln2 / 2:
+// truncation below 6e-9 relative) and a final scaling by 2^n.  Each step is
+// one IEEE operation (fmaf rounds once), so the result is reproducible bit
+// for bit; the argument is clamped to [-104, 89], beyond which the result is
+// already 0 or +Inf.
+__device__ __forceinline__ float exp_cw(float x)
+{
+    x = fminf(fmaxf(x, -104.0f), 89.0f);
+    const float n = rintf(x * 1.44269504088896341f);
+    float r = __builtin_fmaf(-n, 0.693359375f, x);
+    r = __builtin_fmaf(-n, -2.12194440054690583e-4f, r);
+    float p = (float)(1.0 / 5040.0);
+    p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return (g / (1.0f + exp_cw(-g))) * u;  // correctly rounded division
+}
+
+__device__ __forceinline__ float max_abs4(f32x4 v)
+{
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// h1 = h + delta; r = fp32(1 / sqrt(sum h1^2 / K + eps)) (fp64 sum, root
+// and division); y = (h1 * r) * gamma; then the codes.  Token blockIdx.x;
+// thread t holds items t, t + 1024, ... (ITEMS of them, K/4 <= 1024 ITEMS);
+// items past the row are loaded clamped and never used.  Outputs optional.
+template <int ITEMS>
+__global__ __launch_bounds__(kProdThreads) void k_add_rmsnorm_quant(
+    const float* __restrict__ h, const float* __restrict__ delta, const float* __restrict__ gamma,
+    float eps, int K, float* h_out, float* y_out, int8_t* __restrict__ qx, float* __restrict__ sx)
+{
+    __shared__ double dred[kProdWaves];
+    __shared__ float fred[kProdWaves];
+    const int K4 = K / 4;
+    const size_t base = (size_t)blockIdx.x * K4;
+    const f32x4* hp = reinterpret_cast<const f32x4*>(h) + base;
+    const f32x4* gp = reinterpret_cast<const f32x4*>(gamma);
+    f32x4 a[ITEMS], g[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const int i = min((int)threadIdx.x + k * kProdThreads, K4 - 1);
+        a[k] = hp[i];
+        g[k] = gp[i];
+    }
+    if (delta) {
+        const f32x4* dp = reinterpret_cast<const f32x4*>(delta) + base;
+        f32x4 d[ITEMS];
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k)
+            d[k] = dp[min((int)threadIdx.x + k * kProdThreads, K4 - 1)];
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k)
+            a[k] = f32x4{a[k].x + d[k].x, a[k].y + d[k].y, a[k].z + d[k].z, a[k].w + d[k].w};
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const int i = threadIdx.x + k * kProdThreads;
+        if (i < K4) {
+            if (h_out)
+                reinterpret_cast<f32x4*>(h_out)[base + i] = a[k];
+            ss += (double)a[k].x * (double)a[k].x;
+            ss += (double)a[k].y * (double)a[k].y;
+            ss += (double)a[k].z * (double)a[k].z;
+            ss += (double)a[k].w * (double)a[k].w;
+        }
+    }
+    ss = prod_block_sum(ss, dred);
+    const double v = ss / (double)K + (double)eps;
+    const float r = v > 0.0 ? (float)(1.0 / sqrt(v)) : 0.0f;
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        a[k] = f32x4{(a[k].x * r) * g[k].x, (a[k].y * r) * g[k].y, (a[k].z * r) * g[k].z, (a[k].w * r) * g[k].w};
+        amax = fmaxf(amax, max_abs4(a[k]));  // clamped items repeat a real one
+    }
+    amax = prod_block_max(amax, fred);
+    const ActScale as = act_scale(amax);
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const int i = threadIdx.x + k * kProdThreads;
+        if (i < K4) {
+            if (y_out)
+                reinterpret_cast<f32x4*>(y_out)[base + i] = a[k];
+            if (qx)
+                reinterpret_cast<uint32_t*>(qx)[base + i] = quant4_fast(a[k], as);
+        }
+    }
+    if (sx && threadIdx.x == 0)
+        sx[blockIdx.x] = as.s;
+}
+
+// h = silu(g) * u over a token's fused gate/up output [g | u] (2I fp32):
+// thread (blockIdx.x, threadIdx.x) of token blockIdx.y computes one 16-byte
+// item (4 values) into h.
+__global__ __launch_bounds__(kThreads) void k_swiglu(const float* __restrict__ gu, int I,
+                                                     float* __restrict__ h)
+{
+    const int I4 = I / 4;
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= I4)
+        return;
+    const f32x4* gp = reinterpret_cast<const f32x4*>(gu) + (size_t)blockIdx.y * 2 * I4;
+    const f32x4 g = gp[i], u = gp[I4 + i];
+    reinterpret_cast<f32x4*>(h)[(size_t)blockIdx.y * I4 + i] =
+        f32x4{silu_mul(g.x, u.x), silu_mul(g.y, u.y), silu_mul(g.z, u.z), silu_mul(g.w, u.w)};
+}
+
+// Per-token quantisation of fp32 rows [M, K], the row spread over
+// gridDim.x workgroups: each takes the max over the whole row (thread t holds
+// items t, t + 1024, ..., ITEMS of them, loads issued before the first use)
+// and writes the codes of its own slice of 1024 items; workgroup 0 writes s^x.
+template <int ITEMS>
+__global__ __launch_bounds__(kProdThreads) void k_quantize_rows(const float* __restrict__ x, int K,
+                                                                int8_t* __restrict__ qx, float* __restrict__ sx)
+{
+    __shared__ float fred[kProdWaves];
+    const int K4 = K / 4;
+    const f32x4* xr = reinterpret_cast<const f32x4*>(x) + (size_t)blockIdx.y * K4;
+    f32x4 v[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+        v[k] = xr[min((int)threadIdx.x + k * kProdThreads, K4 - 1)];
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+        amax = fmaxf(amax, max_abs4(v[k]));  // clamped items repeat a real one
+    amax = prod_block_max(amax, fred);
+    const ActScale as = act_scale(amax);
+    const int i = blockIdx.x * kProdThreads + threadIdx.x;
+    if (i < K4) {
+        f32x4 t = v[0];
+#pragma unroll
+        for (int k = 1; k < ITEMS; ++k)
+            if (k == (int)blockIdx.x)
+                t = v[k];
+        reinterpret_cast<uint32_t*>(qx)[(size_t)blockIdx.y * K4 + i] = quant4_fast(t, as);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        sx[blockIdx.y] = as.s;
 }
 
 // ------------------------------------------------------------------------
@@ -1260,34 +1525,6 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
     }
 }
 
-// Codes of 8 values, bytes lo = codes 0..3, hi = codes 4..7, bit-identical to
-// act_code: the reciprocal route for all 8, then one (rare) branch to the
-// exact quotient if any of them lies within 2^-15 of a rounding tie.
-__device__ __forceinline__ void quant8_fast(const float v[8], const ActScale& a, uint32_t& lo, uint32_t& hi)
-{
-    float m[8];
-    bool near = !a.fast;
-    if (a.fast) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float r = v[e] * a.inv;
-            m[e] = rintf(r);
-            near |= fabsf(r - m[e]) > 0.5f - 0x1p-15f;
-        }
-    }
-    if (near) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            m[e] = a.s == 0.0f ? 0.0f : rintf(v[e] / a.s);
-    }
-    uint32_t b[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        b[e] = (uint32_t)((int)__builtin_amdgcn_fmed3f(m[e], -127.0f, 127.0f)) & 0xFFu;
-    lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-    hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-}
-
 // Activation staging in two phases around a workgroup barrier, by `nst`
 // threads (index st): phase 1 reads x once from memory, keeps it as fp32 in
 // LDS (xf, fp16 widened exactly) and reduces max |x| per wave; phase 2 reads
@@ -1786,6 +2023,79 @@ int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K, int8_t* q
     else
         hipLaunchKernelGGL(k_quantize_act<X_F16>, dim3(M), dim3(kThreads), 0, (hipStream_t)stream, x, K, qx, sx);
     return launched();
+}
+
+// Items of 4 values per thread of a 1024-thread workgroup covering K values.
+inline int prod_items(int K)
+{
+    const int per = (K / 4 + kProdThreads - 1) / kProdThreads;
+    return per <= 1 ? 1 : (per <= 2 ? 2 : (per <= 4 ? 4 : 8));
+}
+
+int add_rmsnorm_quant(const float* h, const float* delta, const float* gamma, float eps, float* h_out,
+                      float* y_out, int8_t* qx, float* sx, int32_t M, int32_t K, void* stream)
+{
+    if (M < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (K > kProdMaxK)
+        return BQD_ERR_BOUND;
+    if (!(eps >= 0.0f) || !(eps <= FLT_MAX))
+        return BQD_ERR_SHAPE;
+    if (M == 0)
+        return BQD_OK;
+    if (!h || !gamma || (qx && !sx))
+        return BQD_ERR_NULL;
+    if (!aligned(h, 16) || !aligned(delta, 16) || !aligned(gamma, 16) || !aligned(h_out, 16) ||
+        !aligned(y_out, 16) || !aligned(qx, 16) || !aligned(sx, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+#define BQD_RMS_CASE(IT)                                                                                  \
+    if (prod_items(K) == IT) {                                                                            \
+        hipLaunchKernelGGL(k_add_rmsnorm_quant<IT>, dim3(M), dim3(kProdThreads), 0, st, h, delta, gamma, eps, \
+                           K, h_out, y_out, qx, sx);                                                     \
+        return launched();                                                                                \
+    }
+    BQD_RMS_CASE(1) BQD_RMS_CASE(2) BQD_RMS_CASE(4) BQD_RMS_CASE(8)
+#undef BQD_RMS_CASE
+    return BQD_ERR_CONFIG;
+}
+
+int swiglu_quant(const float* gu, float* h_out, int8_t* qx, float* sx, int32_t M, int32_t I, void* stream)
+{
+    if (M < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(I);
+    if (rc)
+        return rc;
+    if (I > kProdMaxK)
+        return BQD_ERR_BOUND;
+    if (M == 0)
+        return BQD_OK;
+    if (!gu || !h_out || (qx && !sx))
+        return BQD_ERR_NULL;
+    if (!aligned(gu, 16) || !aligned(h_out, 16) || !aligned(qx, 16) || !aligned(sx, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int I4 = I / 4;
+    hipLaunchKernelGGL(k_swiglu, dim3((I4 + kThreads - 1) / kThreads, M), dim3(kThreads), 0, st, gu, I, h_out);
+    if ((rc = launched()) || !qx)
+        return rc;
+    const dim3 grid((I4 + kProdThreads - 1) / kProdThreads, M);
+#define BQD_QROWS_CASE(IT)                                                                              \
+    if (prod_items(I) == IT) {                                                                          \
+        hipLaunchKernelGGL(k_quantize_rows<IT>, grid, dim3(kProdThreads), 0, st, h_out, I, qx, sx);     \
+        return launched();                                                                              \
+    }
+    BQD_QROWS_CASE(1) BQD_QROWS_CASE(2) BQD_QROWS_CASE(4) BQD_QROWS_CASE(8)
+#undef BQD_QROWS_CASE
+    return BQD_ERR_CONFIG;
 }
 
 int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8_t* qx,

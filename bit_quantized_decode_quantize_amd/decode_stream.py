@@ -141,3 +141,120 @@ class QwenW4A8Stream:
         out = W[rows.to(self.device)].clone()
         del W
         return out
+
+
+RMS_EPS = 1e-6
+
+
+def producer_bytes_rmsnorm(K: int, residual: bool, codes: bool) -> int:
+    """Residual add + RMSNorm producer: reads h (+ delta) and gamma, writes
+    h + delta, then int8 codes and s^x (or the fp32 values)."""
+    return 4 * K * (3 if residual else 2) + (K + 4 if codes else 4 * K)
+
+
+def producer_bytes_swiglu(I_: int, codes: bool) -> int:
+    """SwiGLU producer: reads gate and up (8I), writes codes and s^x (or fp32 h)."""
+    return 8 * I_ + (I_ + 4 if codes else 4 * I_)
+
+
+def gemv_bytes_q8(N: int, K: int, bias: bool) -> int:
+    """GEMV on int8 codes: packed weights, scales, bias, codes + s^x, y."""
+    return N * K // 2 + 4 * N + (4 * N if bias else 0) + K + 4 + 4 * N
+
+
+class DecodeChain:
+    """The stream's linears wired into a decoder's data flow, with the
+    producers of the activations ([Orin] "后续还能继续优化什么", items 1-2):
+
+        per layer:  h1 = h + y_down(prev); x = RMSNorm(h1)  -> QKV
+                    (attention is outside the path: the O projection reads a
+                     synthetic attention output and quantises it itself)
+                    h2 = h1 + y_O;         x = RMSNorm(h2)  -> gate/up
+                    x = silu(gate) * up                     -> down
+        final:      x = RMSNorm(h + y_down)                 -> lm_head
+
+    fused=True: each producer writes int8 codes + s^x and the linears are
+    int8 GEMVs (``add_rmsnorm_quant`` / ``swiglu_quant`` then ``gemv_w4a8``).
+    fused=False: the producers write fp32 and each linear quantises in its
+    own prologue (``linear_w4a8``).  Both take the same codes from the same
+    fp32 values, so their outputs are identical bit for bit.  The residual
+    stream starts from the same h_in every step."""
+
+    def __init__(self, stream: "QwenW4A8Stream", seed: int = 0):
+        self.s = stream
+        dev = stream.device
+        K, I_ = I.QWEN["hidden"], I.QWEN["inter"]
+        self.K, self.I = K, I_
+        L = stream.layers
+        self.h_in = I.normal("qwen/chain/h0", (1, K), 1.0, seed, dev)
+        g = 1.0 + I.normal("qwen/chain/gamma", (2 * L + 1, K), 0.1, seed, dev)
+        self.gamma = [g[i].contiguous() for i in range(2 * L + 1)]
+        self.h = torch.empty(1, K, device=dev)
+        self.q_h = torch.empty(1, K, dtype=torch.int8, device=dev)
+        self.s_h = torch.empty(1, device=dev)
+        self.q_i = torch.empty(1, I_, dtype=torch.int8, device=dev)
+        self.s_i = torch.empty(1, device=dev)
+        self.y_h = torch.empty(1, K, device=dev)
+        self.y_i = torch.empty(1, I_, device=dev)
+        self.by_layer = [dict((d["name"], d) for d in stream.linears if d["layer"] == l) for l in range(L)]
+        self.head = stream.linears[-1] if stream.linears[-1]["name"] == "lm_head" else None
+        torch.cuda.synchronize(dev)
+
+    def _norm(self, fused, src, delta, gamma, stream):
+        if fused:
+            bqd.add_rmsnorm_quant(src, gamma, RMS_EPS, delta=delta, h_out=self.h, qx=self.q_h, sx=self.s_h,
+                                  stream=stream)
+        else:
+            bqd.add_rmsnorm_quant(src, gamma, RMS_EPS, delta=delta, h_out=self.h, y_out=self.y_h,
+                                  quantize=False, stream=stream)
+
+    def _linear_h(self, fused, d, stream):
+        if fused:
+            bqd.gemv_w4a8(d["wq"], d["sw"], d["b"], self.q_h.view(-1), self.s_h, y=d["y"], stream=stream)
+        else:
+            bqd.linear_w4a8(d["wq"], d["sw"], d["b"], self.y_h.view(-1), y=d["y"], stream=stream)
+
+    def step(self, fused: bool = True, stream=None) -> None:
+        delta = None
+        for l, lin in enumerate(self.by_layer):
+            self._norm(fused, self.h_in if l == 0 else self.h, delta, self.gamma[2 * l], stream)
+            self._linear_h(fused, lin["qkv"], stream)
+            o = lin["o"]
+            bqd.linear_w4a8(o["wq"], o["sw"], o["b"], o["x"], y=o["y"], stream=stream)
+            self._norm(fused, self.h, o["y"].view(1, -1), self.gamma[2 * l + 1], stream)
+            self._linear_h(fused, lin["gate_up"], stream)
+            gu, dn = lin["gate_up"]["y"].view(1, -1), lin["down"]
+            if fused:
+                bqd.swiglu_quant(gu, h_out=self.y_i, qx=self.q_i, sx=self.s_i, stream=stream)
+                bqd.gemv_w4a8(dn["wq"], dn["sw"], dn["b"], self.q_i.view(-1), self.s_i, y=dn["y"], stream=stream)
+            else:
+                bqd.swiglu_quant(gu, h_out=self.y_i, quantize=False, stream=stream)
+                bqd.linear_w4a8(dn["wq"], dn["sw"], dn["b"], self.y_i.view(-1), y=dn["y"], stream=stream)
+            delta = dn["y"].view(1, -1)
+        if self.head is not None:
+            self._norm(fused, self.h, delta, self.gamma[-1], stream)
+            self._linear_h(fused, self.head, stream)
+
+    def output(self) -> torch.Tensor:
+        return (self.head or self.by_layer[-1]["down"])["y"]
+
+    def launches_per_step(self) -> int:
+        return 7 * len(self.by_layer) + (2 if self.head is not None else 0)
+
+    def bytes_per_step(self, fused: bool = True) -> int:
+        K, I_ = self.K, self.I
+        tot = 0
+        for l, lin in enumerate(self.by_layer):
+            tot += producer_bytes_rmsnorm(K, l > 0, fused) + producer_bytes_rmsnorm(K, True, fused)
+            tot += producer_bytes_swiglu(I_, fused)
+            o = lin["o"]
+            tot += algorithmic_bytes_linear(o["N"], o["K"], True)
+            for name in ("qkv", "gate_up", "down"):
+                d = lin[name]
+                tot += gemv_bytes_q8(d["N"], d["K"], d["b"] is not None) if fused else \
+                    algorithmic_bytes_linear(d["N"], d["K"], d["b"] is not None)
+        if self.head is not None:
+            d = self.head
+            tot += producer_bytes_rmsnorm(K, True, fused)
+            tot += gemv_bytes_q8(d["N"], d["K"], False) if fused else algorithmic_bytes_linear(d["N"], d["K"], False)
+        return tot

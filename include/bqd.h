@@ -130,6 +130,48 @@ int unpack_int4_rows_host(const uint32_t* w, int32_t N, int32_t K, int8_t* out);
 int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K,
                  int8_t* qx, float* sx, void* stream);
 
+/* Producers of a linear's activation fused with its quantisation ("Jetson
+ * Orin AGX INT4 ...", section "后续还能继续优化什么", items 1 and 2, which name
+ * the residual add, RMSNorm and SwiGLU as the next kernel boundaries to
+ * remove and the quantisation as the step to fold into the operator before
+ * the linear).  The page does not define the operators; the textbook forms
+ * are used.  One workgroup per token reads the token once and writes the
+ * int8 codes and scale directly; they equal quantize_act of the fp32 values
+ * the same call writes to y_out / h_out.  Every fp32 value that decides a
+ * code comes from a fixed sequence of IEEE operations, so results are
+ * reproducible bit for bit.  K (or I) % 32 == 0 and <= BQD_MAX_PROD_K
+ * (BQD_ERR_BOUND otherwise); M >= 0 tokens, any number. */
+#define BQD_MAX_PROD_K 32768
+
+/* Residual add + RMSNorm + per-token quantisation, per token m:
+ *   h1 = h + delta                        (fp32; delta may be NULL)
+ *   r  = fp32(1 / sqrt(sum_i h1_i^2 / K + eps))   (sum, root and division in
+ *        binary64; a token with a zero denominator normalises to 0)
+ *   y_i = (h1_i * r) * gamma_i            (two fp32 products)
+ *   sx[m], qx[m, :] of y as quantize_act.
+ * h, delta (device) float [M, K]; gamma (device) float [K]; eps >= 0 finite
+ * (BQD_ERR_SHAPE otherwise); h_out, y_out (device) float [M, K] or NULL
+ * (may equal h or delta); qx (device) int8 [M, K] or NULL; sx (device)
+ * float [M], required with qx.  16-byte alignment for the arrays, 4 for sx.
+ * Inputs must be finite and r finite (eps > 0 guarantees it). */
+int add_rmsnorm_quant(const float* h, const float* delta, const float* gamma, float eps,
+                      float* h_out, float* y_out, int8_t* qx, float* sx, int32_t M, int32_t K,
+                      void* stream);
+
+/* SwiGLU + per-token quantisation.  gu (device) float [M, 2I] holds each
+ * token's fused gate/up output, gate g = gu[m, 0:I] then up u = gu[m, I:2I];
+ *   h_i = (g_i / (1 + e^(-g_i))) * u_i   (fp32, correctly rounded division;
+ *   e^x by Cody-Waite reduction and a degree-7 Taylor polynomial, each step
+ *   one IEEE fp32 operation, argument clamped to [-104, 89])
+ *   sx[m], qx[m, :] of h as quantize_act.
+ * h_out (device) float [M, I], required: it receives h, which the
+ * quantisation then reads (two kernels on the stream: the elementwise part
+ * spread over the chip, then the codes).  qx (device) int8 [M, I] or NULL
+ * (h only); sx (device) float [M], required with qx.  Inputs must be
+ * finite. */
+int swiglu_quant(const float* gu, float* h_out, int8_t* qx, float* sx, int32_t M, int32_t I,
+                 void* stream);
+
 /* W4A8 GEMV over per-row scales ("Jetson Orin AGX INT4 ...", derivation and
  * "o2-all 和 o4-all 为什么能加速" sections):
  *   acc[j] = sum_i q^W[j,i] * qx[i]            (exact int32)

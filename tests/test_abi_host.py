@@ -217,3 +217,28 @@ def test_gemv_w4a16_validates_before_launch():
     assert L.gemv_w4a16(P, P, None, P + 8, P, 8, 64, 0, 0, None) == ALIGN
     assert L.gemv_w4a16(P, P, None, P, P, 8, 64, 3, 0, None) == CONFIG
     assert L.gemv_w4a16(P, P, None, P, P, 0, 64, 0, 0, None) == OK
+
+
+def test_producers_validate_before_launch():
+    L = _lib()
+    # add_rmsnorm_quant(h, delta, gamma, eps, h_out, y_out, qx, sx, M, K, stream)
+    assert L.add_rmsnorm_quant(P, None, P, 1e-6, None, None, P, P, 2, 48, None) == SHAPE
+    assert L.add_rmsnorm_quant(P, None, P, 1e-6, None, None, P, P, 2, 32800, None) == BOUND
+    assert L.add_rmsnorm_quant(P, None, P, -1.0, None, None, P, P, 2, 64, None) == SHAPE
+    assert L.add_rmsnorm_quant(P, None, P, float("inf"), None, None, P, P, 2, 64, None) == SHAPE
+    assert L.add_rmsnorm_quant(P, None, P, float("nan"), None, None, P, P, 2, 64, None) == SHAPE
+    assert L.add_rmsnorm_quant(P, None, P, 1e-6, None, None, P, P, -1, 64, None) == SHAPE
+    assert L.add_rmsnorm_quant(None, None, P, 1e-6, None, None, P, P, 2, 64, None) == NULL
+    assert L.add_rmsnorm_quant(P, None, None, 1e-6, None, None, P, P, 2, 64, None) == NULL
+    assert L.add_rmsnorm_quant(P, None, P, 1e-6, None, None, P, None, 2, 64, None) == NULL
+    assert L.add_rmsnorm_quant(P, P4, P, 1e-6, None, None, P, P, 2, 64, None) == ALIGN
+    assert L.add_rmsnorm_quant(P, None, P, 1e-6, None, P + 8, P, P, 2, 64, None) == ALIGN
+    assert L.add_rmsnorm_quant(P, None, P, 1e-6, None, None, P, P, 0, 64, None) == OK
+    # swiglu_quant(gu, h_out, qx, sx, M, I, stream)
+    assert L.swiglu_quant(P, None, P, P, 2, 40, None) == SHAPE
+    assert L.swiglu_quant(P, None, P, P, 2, 32800, None) == BOUND
+    assert L.swiglu_quant(None, None, P, P, 2, 64, None) == NULL
+    assert L.swiglu_quant(P, None, P, None, 2, 64, None) == NULL
+    assert L.swiglu_quant(P, None, P, P, 2, 64, None) == NULL  # h_out is required
+    assert L.swiglu_quant(P, P4, P, P, 2, 64, None) == ALIGN
+    assert L.swiglu_quant(P, None, P, P, 0, 64, None) == OK
