@@ -588,3 +588,131 @@ int orc_swiglu_quant(const float* gu, int64_t M, int64_t I, float* h_out, int8_t
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Packed 6-bit lm_head ([Ascend] 3.2: a Q6_K weight stores 256 weights in  */
+/* 210 bytes -- 4-bit low and 2-bit high fields of each 6-bit code, one     */
+/* int8 scale per 16 weights and one fp16 scale per 256; the page expands   */
+/* it to int8 at load time because decoding the packed fields cost too many */
+/* vector instructions on its chip).  The quantiser and the array layout    */
+/* below are this library's own (the page gives the sizes, not a rule):     */
+/*   sub-block s (16 weights):  t_s = max|w| / 31                (fp32)     */
+/*   super-block (256 weights): d = fp16(max_s t_s / 127)                   */
+/*                              sc_s = clip(round(t_s / d), 0, 127) (int8)  */
+/*   weight i in sub-block s:   q_i = clip(round(w_i / (d * sc_s)), -32, 31)*/
+/*   value:                     w_i ~ d * sc_s * q_i                        */
+/* with fp32 divisions and round-half-to-even; a zero scale gives zero      */
+/* codes.  Storage per row (K % 256 == 0), as separate aligned arrays:      */
+/*   ql [K/2] bytes:  u_i = q_i + 32 in [0, 63]; low nibble of u_i in byte  */
+/*                    i/2, bits 0-3 for even i, 4-7 for odd i;              */
+/*   qh [K/4] bytes:  per 16 weights one little-endian uint32; weight j =   */
+/*                    8k + e (k in {0,1}, e in 0..7) puts bits 4-5 of u at  */
+/*                    bit 2(e mod 4) + 8k + 16[e >= 4];                     */
+/*   sc [K/16] int8;  d [K/256] fp16.                                       */
+/* 128 + 64 + 16 + 2 = 210 bytes per 256 weights, as on the page.           */
+/* ------------------------------------------------------------------------ */
+int orc_quantize_weights_q6k(const float* W, int64_t N, int64_t K, int8_t* q, int8_t* sc,
+                             uint16_t* d)
+{
+    if (N < 0 || K <= 0 || K % 256)
+        return ORC_E_ARG;
+    for (int64_t j = 0; j < N; ++j) {
+        for (int64_t b = 0; b < K / 256; ++b) {
+            const float* wb = W + j * K + 256 * b;
+            float t[16], tmax = 0.0f;
+            for (int s = 0; s < 16; ++s) {
+                float m;
+                int rc = max_abs_f32(wb + 16 * s, 16, &m);
+                if (rc)
+                    return rc;
+                t[s] = m / 31.0f;
+                if (t[s] > tmax)
+                    tmax = t[s];
+            }
+            const uint16_t dh = orc_f32_to_f16(tmax / 127.0f);
+            const float df = orc_f16_to_f32(dh);
+            d[j * (K / 256) + b] = dh;
+            for (int s = 0; s < 16; ++s) {
+                const int8_t scs = quant_code(t[s], df, 0, 127);
+                sc[j * (K / 16) + 16 * b + s] = scs;
+                const float e = df * (float)scs; /* exact: 11 x 7 significant bits */
+                for (int i = 0; i < 16; ++i)
+                    q[j * K + 256 * b + 16 * s + i] = quant_code(wb[16 * s + i], e, -32, 31);
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+static int qh_bit(int64_t i)
+{
+    const int j = (int)(i % 16), k = j / 8, e = j % 8;
+    return 2 * (e % 4) + 8 * k + 16 * (e >= 4);
+}
+
+int orc_pack_q6k(const int8_t* q, int64_t N, int64_t K, uint8_t* ql, uint8_t* qh)
+{
+    if (N < 0 || K <= 0 || K % 256)
+        return ORC_E_ARG;
+    for (int64_t n = 0; n < N * K; ++n)
+        if (q[n] < -32 || q[n] > 31)
+            return ORC_E_RANGE;
+    memset(ql, 0, (size_t)(N * K / 2));
+    memset(qh, 0, (size_t)(N * K / 4));
+    for (int64_t j = 0; j < N; ++j) {
+        for (int64_t i = 0; i < K; ++i) {
+            const unsigned u = (unsigned)(q[j * K + i] + 32);
+            ql[j * (K / 2) + i / 2] |= (uint8_t)((u & 15u) << (4 * (i % 2)));
+            const int bit = qh_bit(i);
+            const int64_t word = j * (K / 16) + i / 16; /* one uint32 per 16 weights */
+            qh[4 * word + bit / 8] |= (uint8_t)((u >> 4) << (bit % 8));
+        }
+    }
+    return ORC_OK;
+}
+
+int orc_unpack_q6k(const uint8_t* ql, const uint8_t* qh, int64_t N, int64_t K, int8_t* q)
+{
+    if (N < 0 || K <= 0 || K % 256)
+        return ORC_E_ARG;
+    for (int64_t j = 0; j < N; ++j) {
+        for (int64_t i = 0; i < K; ++i) {
+            const unsigned lo = (ql[j * (K / 2) + i / 2] >> (4 * (i % 2))) & 15u;
+            const int bit = qh_bit(i);
+            const int64_t word = j * (K / 16) + i / 16;
+            const unsigned hi = (qh[4 * word + bit / 8] >> (bit % 8)) & 3u;
+            q[j * K + i] = (int8_t)((int)(lo | (hi << 4)) - 32);
+        }
+    }
+    return ORC_OK;
+}
+
+/* y_j = sum_b sum_s fp32(d_b) * sc_s * sum_{i in s} q_i * fp32(x_i), every
+ * product exact and the sums in binary64. */
+int orc_gemv_q6k_f16(const uint8_t* ql, const uint8_t* qh, const int8_t* sc, const uint16_t* d,
+                     const uint16_t* x16, int64_t N, int64_t K, double* y)
+{
+    if (N < 0 || K <= 0 || K % 256)
+        return ORC_E_ARG;
+    for (int64_t i = 0; i < K; ++i)
+        if (!(fabsf(orc_f16_to_f32(x16[i])) <= FLT_MAX))
+            return ORC_E_NONFINITE;
+    int8_t qrow[65536];
+    if (K > 65536)
+        return ORC_E_ARG;
+    for (int64_t j = 0; j < N; ++j) {
+        int rc = orc_unpack_q6k(ql + j * (K / 2), qh + j * (K / 4), 1, K, qrow);
+        if (rc)
+            return rc;
+        double acc = 0.0;
+        for (int64_t s = 0; s < K / 16; ++s) {
+            double part = 0.0;
+            for (int i = 0; i < 16; ++i)
+                part += (double)qrow[16 * s + i] * (double)orc_f16_to_f32(x16[16 * s + i]);
+            const double e = (double)orc_f16_to_f32(d[j * (K / 256) + s / 16]) * (double)sc[j * (K / 16) + s];
+            acc += e * part;
+        }
+        y[j] = acc;
+    }
+    return ORC_OK;
+}

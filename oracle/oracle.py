@@ -57,6 +57,10 @@ def _load():
         "orc_exp_f32_array": (None, [P, I64, P]),
         "orc_add_rmsnorm_quant": (I32, [P, P, P, F32, I64, I64, P, P, P, P]),
         "orc_swiglu_quant": (I32, [P, I64, I64, P, P, P]),
+        "orc_quantize_weights_q6k": (I32, [P, I64, I64, P, P, P]),
+        "orc_pack_q6k": (I32, [P, I64, I64, P, P]),
+        "orc_unpack_q6k": (I32, [P, P, I64, I64, P]),
+        "orc_gemv_q6k_f16": (I32, [P, P, P, P, P, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -233,6 +237,52 @@ def swiglu_quant(gu):
     if one:
         return q[0], s[0], h[0]
     return q, s, h
+
+
+# ------------------------------------------------- packed 6-bit lm_head ----
+def quantize_weights_q6k(W) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Q6_K-like weights ([Ascend] 3.2 sizes, this library's own rule): fp32
+    W [N, K] (K % 256 == 0) -> (q int8 [N, K] in [-32, 31], sc int8 [N, K/16]
+    in [0, 127], d fp16 bits uint16 [N, K/256])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    sc = np.empty((N, K // 16), np.int8)
+    d = np.empty((N, K // 256), np.uint16)
+    _check(_lib.orc_quantize_weights_q6k(_p(W), N, K, _p(q), _p(sc), _p(d)))
+    return q, sc, d
+
+
+def pack_q6k(q) -> Tuple[np.ndarray, np.ndarray]:
+    """int8 codes [N, K] in [-32, 31] -> (ql uint8 [N, K/2], qh uint8 [N, K/4])."""
+    q = _c(q, np.int8)
+    N, K = q.shape
+    ql = np.empty((N, K // 2), np.uint8)
+    qh = np.empty((N, K // 4), np.uint8)
+    _check(_lib.orc_pack_q6k(_p(q), N, K, _p(ql), _p(qh)))
+    return ql, qh
+
+
+def unpack_q6k(ql, qh) -> np.ndarray:
+    ql = _c(ql, np.uint8)
+    qh = _c(qh, np.uint8)
+    N, K = ql.shape[0], ql.shape[1] * 2
+    q = np.empty((N, K), np.int8)
+    _check(_lib.orc_unpack_q6k(_p(ql), _p(qh), N, K, _p(q)))
+    return q
+
+
+def gemv_q6k_f16(ql, qh, sc, d, x16) -> np.ndarray:
+    """y_j = sum over 16-weight sub-blocks of fp32(d) * sc * sum q x, in binary64."""
+    ql = _c(ql, np.uint8)
+    qh = _c(qh, np.uint8)
+    sc = _c(sc, np.int8)
+    d = _c(d, np.uint16)
+    xb = _c(x16, np.uint16)
+    N, K = ql.shape[0], ql.shape[1] * 2
+    y = np.empty(N, np.float64)
+    _check(_lib.orc_gemv_q6k_f16(_p(ql), _p(qh), _p(sc), _p(d), _p(xb), N, K, _p(y)))
+    return y
 
 
 # -------------------------------------------------------------- GEMVs ----

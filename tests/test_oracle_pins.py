@@ -572,3 +572,99 @@ def test_rmsnorm_power_of_two_scale_invariance():
         qk, sk, h1k, yk = O.add_rmsnorm_quant(np.ldexp(h, k), None, gamma, 0.0)
         assert np.array_equal(qk, q) and sk == s and np.array_equal(yk, y)
         assert np.array_equal(h1k, np.ldexp(h, k))
+
+
+# --------------------------------------------------- packed 6-bit lm_head --
+# [Ascend] 3.2 gives the Q6_K sizes (256 weights in 210 bytes: 4-bit low and
+# 2-bit high fields, an int8 scale per 16, an fp16 scale per 256); the
+# quantiser and the array layout are this library's own.
+def _golden_pairs(line):
+    key, *items = line.split()
+    return key, {int(a): int(b, 0) for a, b in (it.split(":") for it in items)}
+
+
+def test_q6k_layout_golden():
+    lines = [l for l in open(os.path.join(ROOT, "tests", "golden", "q6k_layout.txt"), encoding="utf-8")
+             if l.strip() and not l.startswith("#")]
+    tab = dict(_golden_pairs(l) for l in lines)
+    q = np.full((1, 256), -32, np.int8)
+    for i, c in tab["codes"].items():
+        q[0, i] = c
+    ql, qh = O.pack_q6k(q)
+    assert ql.shape == (1, 128) and qh.shape == (1, 64)
+    exp_ql = np.zeros(128, np.uint8)
+    exp_qh = np.zeros(64, np.uint8)
+    for i, v in tab["ql"].items():
+        exp_ql[i] = v
+    for i, v in tab["qh"].items():
+        exp_qh[i] = v
+    assert np.array_equal(ql[0], exp_ql) and np.array_equal(qh[0], exp_qh)
+    assert np.array_equal(O.unpack_q6k(ql, qh), q)
+    # 128 + 64 bytes of codes, 16 scales, one fp16: 210 bytes per 256 weights
+    assert ql.nbytes + qh.nbytes + 16 + 2 == 210
+
+
+def test_q6k_pack_round_trip_and_range():
+    q = I.uniform_int("pin/q6k/rt", (5, 512), -32, 31).numpy().astype(np.int8)
+    ql, qh = O.pack_q6k(q)
+    assert np.array_equal(O.unpack_q6k(ql, qh), q)
+    # every byte pattern of the packed arrays is a valid code set
+    rng = np.random.default_rng(3)
+    ql = rng.integers(0, 256, (3, 256), dtype=np.uint8)
+    qh = rng.integers(0, 256, (3, 128), dtype=np.uint8)
+    assert np.array_equal(O.pack_q6k(O.unpack_q6k(ql, qh))[0], ql)
+    assert np.array_equal(O.pack_q6k(O.unpack_q6k(ql, qh))[1], qh)
+    bad = q.copy()
+    bad[0, 0] = 32
+    with pytest.raises(O.OracleError):
+        O.pack_q6k(bad)
+
+
+def _rne(v):
+    return np.array([round(float(t)) for t in np.ravel(v)], np.float64).reshape(np.shape(v))
+
+
+def test_q6k_quantiser_vs_numpy_brute_force_and_bounds():
+    W = I.normal("pin/q6k/W", (4, 512), 0.02).numpy()
+    W[1, 256:272] = 0.0                      # a zero sub-block
+    W[2, 0:256] *= np.repeat(np.float32([1e-3, 1.0]), 128)  # tiny sub-blocks under a large one
+    q, sc, d = O.quantize_weights_q6k(W)
+    for j in range(4):
+        for b in range(2):
+            wb = W[j, 256 * b:256 * (b + 1)].reshape(16, 16)
+            t = (np.abs(wb).max(1).astype(np.float32) / np.float32(31)).astype(np.float32)
+            dh = np.float16(np.float32(t.max()) / np.float32(127))
+            assert d[j, b] == dh.view(np.uint16)
+            df = np.float32(dh)
+            exp_sc = np.clip(_rne(t / df), 0, 127) if df > 0 else np.zeros(16)
+            assert np.array_equal(sc[j, 16 * b:16 * (b + 1)], exp_sc.astype(np.int8))
+            e = (df * exp_sc.astype(np.float32)).astype(np.float32)
+            for s in range(16):
+                if e[s] == 0:
+                    assert not q[j, 256 * b + 16 * s:256 * b + 16 * s + 16].any()
+                    continue
+                exp_q = np.clip(_rne(wb[s] / e[s]), -32, 31)
+                assert np.array_equal(q[j, 256 * b + 16 * s:256 * b + 16 * s + 16], exp_q.astype(np.int8))
+                # reconstruction within half a step, and the largest weight near the top code
+                assert np.all(np.abs(wb[s].astype(np.float64) - e[s] * exp_q) <= 0.5 * e[s] * (1 + 1e-6))
+                assert np.abs(exp_q).max() >= 28
+            # the sub-block with the largest scale uses (almost) the whole int8 range
+            assert sc[j, 16 * b:16 * (b + 1)].max() >= 126 or df == 0
+    assert not sc[1, 16:32][0] and not q[1, 256:272].any()
+
+
+def test_q6k_gemv_vs_numpy_float64_dequantised_matmul():
+    N, K = 9, 1536
+    W = I.normal("pin/q6k/gW", (N, K), 0.02).numpy()
+    q, sc, d = O.quantize_weights_q6k(W)
+    ql, qh = O.pack_q6k(q)
+    x16 = I.normal("pin/q6k/x", K, 1.0, dtype=__import__("torch").float16).numpy()
+    y = O.gemv_q6k_f16(ql, qh, sc, d, x16.view(np.uint16))
+    e = (d.view(np.float16).astype(np.float64)[:, :, None] *
+         sc.reshape(N, K // 256, 16).astype(np.float64)).reshape(N, K // 16)
+    Wd = np.repeat(e, 16, axis=1) * q.astype(np.float64)
+    ref = Wd @ x16.astype(np.float64)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # and the dequantised weights stay within half a step of W
+    step = np.repeat(e, 16, axis=1)
+    assert np.all(np.abs(Wd - W) <= 0.5 * step * (1 + 1e-6) + (step == 0) * np.abs(W))
