@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--w4a16", action="store_true",
                    help="stream: the float-unpack comparison (gemv_w4a16 per linear, fp16 x) "
                         "instead of the W4A8 path")
+    p.add_argument("--lm-head", choices=("w8a16", "q6k"), default="w8a16",
+                   help="gemma: the lm_head form in the token step (int8-expanded or packed 6-bit)")
     p.add_argument("--verify-m", default="1,2,4,8,16")
     p.add_argument("--impl", type=int, default=0, help="verify kernel: 0 automatic, 1 dot4, 2 MFMA")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -436,24 +438,31 @@ def run_gemma(a, dev):
 
     layers = a.layers or 35
     t0 = time.time()
-    w = WL.GemmaG32Stream(layers=layers, device=dev, r=a.r, lanes_per_row=a.lanes)
+    w = WL.GemmaG32Stream(layers=layers, device=dev, r=a.r, lanes_per_row=a.lanes, head=a.lm_head)
     log(f"gemma stream built: {w.launches_per_step} launches, {w.weight_bytes() / 1e9:.3f} GB, "
         f"{time.time() - t0:.1f} s")
     ms, n = time_steps(w.step, a.steps, a.warmup, 1 if (not a.eager) else 0)
     gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
-    # lm_head alone (the largest single matrix), back to back.
-    ms_head, _ = time_steps(w.lm_head, max(20, a.steps), 2, 0)
-    head_bytes = WL.bytes_w8a16(*w.head_NK)
+    # Both lm_head forms alone (the largest single matrix), back to back.
+    heads = {}
+    for kind, fn in (("w8a16", w.lm_head), ("q6k", w.lm_head_q6k)):
+        ms_h, _ = time_steps(fn, max(20, a.steps), 2, 0)
+        heads[kind] = {"us": round(ms_h * 1e3, 2), "bytes": w.head_bytes(kind),
+                       "GB/s": round(w.head_bytes(kind) / (ms_h * 1e-3) / 1e9, 1)}
+    head_form = {"w8a16": "W8A16 lm_head [262144,1536] (int8 in [-32,31], fp16 group-32 scales)",
+                 "q6k": "packed 6-bit lm_head [262144,1536] (210 B per 256 weights, decoded in registers)"}
     out = base_line(a, gbs, ms, n, {
-        "workload": f"gemma-shaped {layers}-layer Q4_0-style group-32 W4A8 stream (fp16 x) + W8A16 lm_head "
-                    "[262144,1536] (int8 in [-32,31], fp16 group-32 scales)",
+        "workload": f"gemma-shaped {layers}-layer Q4_0-style group-32 W4A8 stream (fp16 x) + "
+                    + head_form[a.lm_head],
         "launch": "per-linear, HIP graph" if (not a.eager) else "per-linear", "layers": layers,
         "bytes_per_step": w.bytes_per_step(), "weight_bytes": w.weight_bytes()}, dtype="int8+fp16")
     out["tok_per_s"] = round(1e3 / ms, 2)
     out["us_per_gemv"] = round(ms * 1e3 / w.launches_per_step, 3)
-    out["lm_head"] = {"us": round(ms_head * 1e3, 2), "GB/s": round(head_bytes / (ms_head * 1e-3) / 1e9, 1)}
-    out["roofline"] = roofline(head_bytes / (ms_head * 1e-3) / 1e9,
-                               "k_gemv_w8a16_g32 (lm_head, largest single launch)", ms_head * 1e3, head_bytes)
+    out["lm_head"] = heads[a.lm_head]
+    out["lm_head_forms"] = heads
+    h = heads[a.lm_head]
+    kern = {"w8a16": "k_gemv_w8a16_g32", "q6k": "k_gemv_q6k"}[a.lm_head]
+    out["roofline"] = roofline(h["GB/s"], f"{kern} (lm_head, largest single launch)", h["us"], h["bytes"])
     if not a.no_cpu_baseline:
         import oracle as O
         work = []

@@ -34,6 +34,7 @@ ENTRY_POINTS = (
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
     "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
     "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant",
+    "quantize_weights_q6k", "gemv_q6k_f16",
 )
 
 
@@ -88,6 +89,8 @@ def lib() -> C.CDLL:
         "gemv_w4a16": (I, [P, P, P, P, P, I, I, I, I, P]),
         "add_rmsnorm_quant": (I, [P, P, P, C.c_float, P, P, P, P, I, I, P]),
         "swiglu_quant": (I, [P, P, P, P, I, I, P]),
+        "quantize_weights_q6k": (I, [P, I, I, P, P, P, P, P]),
+        "gemv_q6k_f16": (I, [P, P, P, P, P, P, I, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -364,6 +367,45 @@ def gemv_w8a16_group32(w8, s16, x16, y=None, r=0, lanes_per_row=0, stream=None):
     y = _empty((N,), torch.float32, w8) if y is None else _dev(y, "y", _F32, N)
     _call("gemv_w8a16_group32", w8.data_ptr(), s16.data_ptr(), x16.data_ptr(), y.data_ptr(), N, K,
           r, lanes_per_row, _stream(stream))
+    return y
+
+
+class Q6KWeights:
+    """Packed 6-bit weights: ql uint8 [N, K/2], qh uint8 [N, K/4], sc int8
+    [N, K/16], d fp16 [N, K/256] (the layout of ``quantize_weights_q6k``)."""
+
+    def __init__(self, ql, qh, sc, d):
+        self.ql, self.qh, self.sc, self.d = ql, qh, sc, d
+        self.N, self.K = ql.shape[0], ql.shape[1] * 2
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.ql, self.qh, self.sc, self.d))
+
+
+def quantize_weights_q6k(W: torch.Tensor, stream=None) -> Q6KWeights:
+    """fp32 W [N, K] (K % 256 == 0) on the device -> packed 6-bit weights."""
+    _dev(W, "W", _F32)
+    N, K = W.shape
+    ql = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    qh = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    sc = torch.empty((N, K // 16), dtype=torch.int8, device=W.device)
+    d = torch.empty((N, K // 256), dtype=torch.float16, device=W.device)
+    _call("quantize_weights_q6k", W.data_ptr(), N, K, ql.data_ptr(), qh.data_ptr(), sc.data_ptr(),
+          d.data_ptr(), _stream(stream))
+    return Q6KWeights(ql, qh, sc, d)
+
+
+def gemv_q6k_f16(w: Q6KWeights, x16, y=None, r=0, lanes_per_row=0, stream=None):
+    """Packed 6-bit weights against fp16 x [K] -> fp32 y [N]."""
+    N, K = w.N, w.K
+    _dev(w.ql, "ql", (torch.uint8,), N * K // 2)
+    _dev(w.qh, "qh", (torch.uint8,), N * K // 4)
+    _dev(w.sc, "sc", (torch.int8,), N * K // 16)
+    _dev(w.d, "d", (torch.float16,), N * K // 256)
+    _dev(x16, "x16", (torch.float16,), K)
+    y = _empty((N,), torch.float32, w.ql) if y is None else _dev(y, "y", _F32, N)
+    _call("gemv_q6k_f16", w.ql.data_ptr(), w.qh.data_ptr(), w.sc.data_ptr(), w.d.data_ptr(), x16.data_ptr(),
+          y.data_ptr(), N, K, r, lanes_per_row, _stream(stream))
     return y
 
 

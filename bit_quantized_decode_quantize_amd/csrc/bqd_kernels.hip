@@ -46,6 +46,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
+// fp16 pair from a 32-bit word.  The word goes in by value: __builtin_bit_cast
+// of an ext-vector element (v.y) was compiled as a read of element 0.
+__device__ __forceinline__ h16x2 as_h16x2(uint32_t v)
+{
+    return __builtin_bit_cast(h16x2, v);
+}
+
 // Global address space.  Pointers read from memory (the pass descriptors) are
 // generic; casting them keeps loads on the global path (global_load_*, which
 // count only in vmcnt) instead of flat loads, which also count in lgkmcnt and
@@ -986,6 +993,210 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w8a16_g32(
 }
 
 // ------------------------------------------------------------------------
+// Packed 6-bit lm_head ("在香橙派上跑 Gemma4 ..." section 3.2 sizes a Q6_K
+// weight at 210 bytes per 256: 4-bit low and 2-bit high fields of each code,
+// an int8 scale per 16 weights, an fp16 scale per 256; the page expands it to
+// int8 because decoding the fields was vector-instruction bound there).  This
+// library's layout: separate aligned arrays per row,
+//   ql [K/2]: low nibble of u = q + 32 in byte i/2 (bits 0-3 even i, 4-7 odd)
+//   qh [K/4]: per 16 weights a uint32; weight 8k + e (k in {0,1}) puts bits
+//             4-5 of u at bit 2(e mod 4) + 8k + 16[e >= 4]
+//   sc [K/16] int8, d [K/256] fp16;  value = d * sc * q.
+// The high-bit placement makes one shift and one mask bring the high bits of
+// the code pair (e, e + 4) of a low-nibble word to bits 4-5 of both 16-bit
+// halves, so a pair costs: shift + and-or (low nibbles, fp16 exponent 0x64),
+// shift + and-or (high bits), a packed fp16 subtract of 1056 (fp16 bits
+// 0x6400 | u = 1024 + u) and one v_dot2_f32_f16.
+// ------------------------------------------------------------------------
+
+// Load-time quantisation, one thread per 16-weight sub-block, 16 lanes per
+// 256-weight super-block (K % 256 == 0 keeps super-blocks on 16-lane
+// boundaries):  t = max|w| / 31;  d = fp16(max t / 127);  sc = clip(round(t /
+// d), 0, 127);  q = clip(round(w / (d * sc)), -32, 31) (fp32 divisions, RNE;
+// a zero scale gives zero codes).
+__global__ __launch_bounds__(kThreads) void k_quantize_weights_q6k(const float* __restrict__ W, int K,
+                                                                   long long subblocks, u32x2* __restrict__ ql,
+                                                                   uint32_t* __restrict__ qh,
+                                                                   int8_t* __restrict__ sc,
+                                                                   uint16_t* __restrict__ d)
+{
+    const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= subblocks)  // whole 16-lane super-blocks leave together
+        return;
+    const f32x4* wp = reinterpret_cast<const f32x4*>(W) + 4 * gid;
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x4 t = wp[k];
+        v[4 * k] = t.x;
+        v[4 * k + 1] = t.y;
+        v[4 * k + 2] = t.z;
+        v[4 * k + 3] = t.w;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        m = fmaxf(m, fabsf(v[i]));
+    const float t = m / 31.0f;
+    float tmax = t;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+        tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+    const _Float16 dh = (_Float16)(tmax / 127.0f);
+    const float df = (float)dh;
+    const float scf = df == 0.0f ? 0.0f : fminf(fmaxf(rintf(t / df), 0.0f), 127.0f);
+    const float e = df * scf;  // exact: 11 x 7 significant bits
+    uint32_t lo = 0, hi = 0, hw = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float qf = e == 0.0f ? 0.0f : fminf(fmaxf(rintf(v[i] / e), -32.0f), 31.0f);
+        const uint32_t u = (uint32_t)((int)qf + 32);
+        if (i < 8)
+            lo |= (u & 15u) << (4 * i);
+        else
+            hi |= (u & 15u) << (4 * (i - 8));
+        const int k = i / 8, ee = i % 8;
+        hw |= (u >> 4) << (2 * (ee % 4) + 8 * k + 16 * (ee >= 4));
+    }
+    ql[gid] = u32x2{lo, hi};
+    qh[gid] = hw;
+    sc[gid] = (int8_t)(int)scf;
+    if ((gid & 15) == 0)
+        d[gid / 16] = __builtin_bit_cast(uint16_t, dh);
+}
+
+// Eight codes of one low-nibble word w (weights 8k..8k+7) with their high
+// bits hq (already shifted so that pair e sits at bits 2e and 16 + 2e),
+// against the staged activation pairs (x_e, x_{e+4}), e = 0..3.
+__device__ __forceinline__ float dot8_q6(uint32_t w, uint32_t hq, uint32_t x04, uint32_t x15, uint32_t x26,
+                                         uint32_t x37, float acc)
+{
+    const h16x2 bias = {(_Float16)1056.0f, (_Float16)1056.0f};
+    const uint32_t xp[4] = {x04, x15, x26, x37};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = ((w >> (4 * e)) & 0x000F000Fu) | 0x64006400u;
+        const uint32_t u2 = (((hq >> (2 * e)) << 4) & 0x00300030u) | lo;
+        acc = __builtin_amdgcn_fdot2(as_h16x2(u2) - bias, as_h16x2(xp[e]), acc, false);
+    }
+    return acc;
+}
+
+// Lane reduction for 8 lanes per row (the wave64 DPP row reduction of
+// sum_lanes_f covers 16).
+template <int L>
+__device__ __forceinline__ float sum_lanes_q6(float v)
+{
+    if constexpr (L == 8) {
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        return v;
+    } else {
+        return sum_lanes_f<L>(v);
+    }
+}
+
+// A lane takes units of 64 weights (two 32-weight chunks): low fields 2 x 16
+// bytes, high fields 16 bytes, the four sub-block scales as one 4-byte word
+// and the fp16 super-block scale -- five loads per 64 weights; U units per
+// step, R rows per lane group, L lanes per row.
+template <int R, int L>
+__global__ __launch_bounds__(kThreads) void k_gemv_q6k(const u32x4* __restrict__ ql, const u32x4* __restrict__ qh,
+                                                       const uint32_t* __restrict__ sc4,
+                                                       const uint16_t* __restrict__ d16,
+                                                       const u32x4* __restrict__ x16, float* __restrict__ y, int N,
+                                                       int C)
+{
+    extern __shared__ u32x4 xs[];  // per 8 weights: (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+    for (int g = threadIdx.x; g < 4 * C; g += kThreads) {
+        const u32x4 v = x16[g];
+        xs[g] = u32x4{(v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
+                      (v.y & 0xFFFFu) | (v.w << 16), (v.y >> 16) | (v.w & 0xFFFF0000u)};
+    }
+    __syncthreads();
+
+    constexpr int GROUPS = kThreads / L;
+    constexpr int ROWS = GROUPS * R;
+    constexpr int U = 2;
+    const int lane = threadIdx.x % L;
+    const int grp = threadIdx.x / L;
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int C2 = C / 2;  // 64-weight units per row
+    const int iters = (C2 + L - 1) / L;
+    const int D = C / 8;   // super-blocks per row
+
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const int row0 = tile * ROWS + grp * R;
+        size_t rr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            rr[r] = (size_t)min(row0 + r, N - 1);
+        float facc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = 0.0f;
+        for (int it = 0; it < iters; it += U) {
+            u32x4 la[U][R], lb[U][R], hw[U][R];
+            uint32_t s4[U][R], dd[U][R];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c2 = (it + u) * L + lane;
+                const bool ok = (it + u < iters) && (c2 < C2);
+                const int cc = min(c2, C2 - 1);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    // unconditional loads at a clamped unit; past the row the
+                    // scales are zeroed, so the unit adds nothing
+                    la[u][r] = ql[rr[r] * C + 2 * cc];
+                    lb[u][r] = ql[rr[r] * C + 2 * cc + 1];
+                    hw[u][r] = qh[rr[r] * C2 + cc];
+                    const uint32_t sv = sc4[rr[r] * C2 + cc];
+                    s4[u][r] = ok ? sv : 0u;
+                    dd[u][r] = d16[rr[r] * D + cc / 4];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = 2 * min((it + u) * L + lane, C2 - 1);
+                const u32x4 g0 = xs[4 * c], g1 = xs[4 * c + 1], g2 = xs[4 * c + 2], g3 = xs[4 * c + 3];
+                const u32x4 g4 = xs[4 * c + 4], g5 = xs[4 * c + 5], g6 = xs[4 * c + 6], g7 = xs[4 * c + 7];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const u32x4 wa = la[u][r], wb = lb[u][r], h = hw[u][r];
+                    float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+                    p0 = dot8_q6(wa.x, h.x, g0.x, g0.y, g0.z, g0.w, p0);
+                    p0 = dot8_q6(wa.y, h.x >> 8, g1.x, g1.y, g1.z, g1.w, p0);
+                    p1 = dot8_q6(wa.z, h.y, g2.x, g2.y, g2.z, g2.w, p1);
+                    p1 = dot8_q6(wa.w, h.y >> 8, g3.x, g3.y, g3.z, g3.w, p1);
+                    p2 = dot8_q6(wb.x, h.z, g4.x, g4.y, g4.z, g4.w, p2);
+                    p2 = dot8_q6(wb.y, h.z >> 8, g5.x, g5.y, g5.z, g5.w, p2);
+                    p3 = dot8_q6(wb.z, h.w, g6.x, g6.y, g6.z, g6.w, p3);
+                    p3 = dot8_q6(wb.w, h.w >> 8, g7.x, g7.y, g7.z, g7.w, p3);
+                    const float df = (float)__builtin_bit_cast(_Float16, (uint16_t)dd[u][r]);
+                    const uint32_t sv = s4[u][r];
+                    float a = facc[r];
+                    a = fmaf(df * (float)(int8_t)(sv & 0xFFu), p0, a);
+                    a = fmaf(df * (float)(int8_t)((sv >> 8) & 0xFFu), p1, a);
+                    a = fmaf(df * (float)(int8_t)((sv >> 16) & 0xFFu), p2, a);
+                    a = fmaf(df * (float)(int8_t)(sv >> 24), p3, a);
+                    facc[r] = a;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            facc[r] = sum_lanes_q6<L>(facc[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r;
+            if (lane == r && row < N)
+                y[row] = facc[r];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // W4A16 comparison GEMV: the same packed per-row INT4 weights against an
 // fp16 activation, unpacked to fp16 and multiplied in floating point
 // ("Jetson Orin AGX INT4 ..." section "为什么 INT4 float 解包不快" weighs this
@@ -1000,13 +1211,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w8a16_g32(
 //   against about 1.1 for the integer dot.  y = fmaf(sw, acc, b) with acc
 //   the fp32 sum.
 // ------------------------------------------------------------------------
-// The word goes in by value: __builtin_bit_cast of an ext-vector element
-// (xg.y) was compiled as a read of element 0.
-__device__ __forceinline__ h16x2 as_h16x2(uint32_t v)
-{
-    return __builtin_bit_cast(h16x2, v);
-}
-
 __device__ __forceinline__ float dot8_w4_f16(uint32_t w, u32x4 xg, float acc)
 {
     const uint32_t u = w ^ 0x88888888u;
@@ -2245,6 +2449,77 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
     BQD_W8_CASE(1, 32) BQD_W8_CASE(2, 32) BQD_W8_CASE(4, 32) BQD_W8_CASE(8, 32)
     BQD_W8_CASE(1, 64) BQD_W8_CASE(2, 64) BQD_W8_CASE(4, 64) BQD_W8_CASE(8, 64)
 #undef BQD_W8_CASE
+    return BQD_ERR_CONFIG;
+}
+
+int quantize_weights_q6k(const float* W, int32_t N, int32_t K, uint8_t* ql, uint8_t* qh, int8_t* sc,
+                         uint16_t* d, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K, 256);
+    if (rc)
+        return rc;
+    if (K > BQD_MAX_K)
+        return BQD_ERR_BOUND;
+    if (N == 0)
+        return BQD_OK;
+    if (!W || !ql || !qh || !sc || !d)
+        return BQD_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(ql, 8) || !aligned(qh, 4) || !aligned(d, 2))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    const long long subblocks = (long long)N * (K / 16);
+    hipLaunchKernelGGL(k_quantize_weights_q6k, dim3((unsigned)((subblocks + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, (hipStream_t)stream, W, K, subblocks, reinterpret_cast<u32x2*>(ql),
+                       reinterpret_cast<uint32_t*>(qh), sc, d);
+    return launched();
+}
+
+int gemv_q6k_f16(const uint8_t* ql, const uint8_t* qh, const int8_t* sc, const uint16_t* d, const uint16_t* x16,
+                 float* y, int32_t N, int32_t K, int32_t r, int32_t lanes_per_row, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K, 256);
+    if (rc)
+        return rc;
+    if (2 * (size_t)K > (size_t)kLdsBytes)
+        return BQD_ERR_BOUND;
+    if (N == 0)
+        return BQD_OK;
+    if (!ql || !qh || !sc || !d || !x16 || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(ql, 16) || !aligned(qh, 16) || !aligned(sc, 4) || !aligned(d, 2) || !aligned(x16, 16) ||
+        !aligned(y, 4))
+        return BQD_ERR_ALIGN;
+    if (!valid_config(r, lanes_per_row == 8 ? 16 : lanes_per_row))
+        return BQD_ERR_CONFIG;
+    const int L = lanes_per_row ? lanes_per_row : 16;
+    if (r == 0)
+        r = 2;
+    if ((rc = bqd_init()))
+        return rc;
+    const int C = K / 32;
+    const int rows = (kThreads / L) * r;
+    const dim3 grid(grid_for((N + rows - 1) / rows)), block(kThreads);
+    const size_t lds = 2 * (size_t)K;
+    const u32x4* qlv = reinterpret_cast<const u32x4*>(ql);
+    const u32x4* qhv = reinterpret_cast<const u32x4*>(qh);
+    const uint32_t* scv = reinterpret_cast<const uint32_t*>(sc);
+    const u32x4* xv = reinterpret_cast<const u32x4*>(x16);
+    hipStream_t st = (hipStream_t)stream;
+#define BQD_Q6K_CASE(RR, LL)                                                                                    \
+    if (r == RR && L == LL) {                                                                                   \
+        hipLaunchKernelGGL((k_gemv_q6k<RR, LL>), grid, block, lds, st, qlv, qhv, scv, d, xv, y, N, C);           \
+        return launched();                                                                                      \
+    }
+    BQD_Q6K_CASE(1, 8) BQD_Q6K_CASE(2, 8) BQD_Q6K_CASE(4, 8) BQD_Q6K_CASE(8, 8)
+    BQD_Q6K_CASE(1, 16) BQD_Q6K_CASE(2, 16) BQD_Q6K_CASE(4, 16) BQD_Q6K_CASE(8, 16)
+    BQD_Q6K_CASE(1, 32) BQD_Q6K_CASE(2, 32) BQD_Q6K_CASE(4, 32) BQD_Q6K_CASE(8, 32)
+    BQD_Q6K_CASE(1, 64) BQD_Q6K_CASE(2, 64) BQD_Q6K_CASE(4, 64) BQD_Q6K_CASE(8, 64)
+#undef BQD_Q6K_CASE
     return BQD_ERR_CONFIG;
 }
 

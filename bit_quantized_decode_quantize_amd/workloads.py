@@ -15,8 +15,8 @@ its weights from HBM, as a decode step over a full model does.
 * ``LayerPool``: one Qwen2-7B-shaped decoder layer (fused QKV, O, fused
   gate/up, down), per-linear launches or the persistent pass.
 * ``GemmaG32Stream``: 35 Gemma-shaped layers of group-32 INT4 linears with
-  fp16 activations plus the int8-expanded W8A16 lm_head [262144, 1536]
-  (section 3 of "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录").
+  fp16 activations plus the lm_head [262144, 1536], int8-expanded (W8A16) or
+  packed 6-bit (section 3 of "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录").
 * ``VerifyPool``: the M-token verify GEMM over [18944, 3584] or
   [3584, 18944] (section 5 of the same page).
 """
@@ -46,6 +46,11 @@ def bytes_group32_linear(N: int, K: int, bias: bool, x_bytes: int = 2) -> int:
 def bytes_w8a16(N: int, K: int) -> int:
     """W8A16 GEMV: int8 codes N*K, fp16 scales 2*N*K/32, fp16 x 2K, y 4N."""
     return N * K + 2 * N * (K // 32) + 2 * K + 4 * N
+
+
+def bytes_q6k(N: int, K: int) -> int:
+    """Packed 6-bit GEMV: 210 bytes per 256 weights, fp16 x 2K, y 4N."""
+    return N * K * 210 // 256 + 2 * K + 4 * N
 
 
 def bytes_verify(M: int, N: int, K: int, bias: bool = True) -> int:
@@ -156,9 +161,13 @@ class GemmaG32Stream:
     one token: 140 fused group-32 linears + the W8A16 lm_head, one launch each.
     Weights total 1.1 GB, so every step streams from HBM."""
 
-    def __init__(self, layers: int = 35, seed: int = 0, device="cuda", r: int = 0, lanes_per_row: int = 0):
+    def __init__(self, layers: int = 35, seed: int = 0, device="cuda", r: int = 0, lanes_per_row: int = 0,
+                 head: str = "w8a16"):
+        if head not in ("w8a16", "q6k"):
+            raise ValueError(f"unknown lm_head form {head}")
         self.device = torch.device(device)
         self.r, self.lanes_per_row = r, lanes_per_row
+        self.head = head
         self.linears: List[Dict] = []
         for l in range(layers):
             prefix = f"gemma/L{l}"
@@ -172,6 +181,7 @@ class GemmaG32Stream:
         N, K = I.GEMMA["vocab"], I.GEMMA["hidden"]
         W = I.normal("gemma/lm_head/W", (N, K), 0.02, seed, self.device)
         self.w8, self.w8s = bqd.quantize_weights_int8_group32(W)
+        self.q6k = bqd.quantize_weights_q6k(W)
         del W
         self.head_x = I.normal("gemma/lm_head/x", K, 1.0, seed, self.device, torch.float16)
         self.head_y = torch.empty(N, dtype=torch.float32, device=self.device)
@@ -183,19 +193,29 @@ class GemmaG32Stream:
         for d in self.linears:
             bqd.linear_w4a8_group32(d["wq"], d["s16"], None, d["x"], y=d["y"], r=self.r,
                                     lanes_per_row=self.lanes_per_row, stream=stream)
-        self.lm_head(stream)
+        if self.head == "q6k":
+            self.lm_head_q6k(stream)
+        else:
+            self.lm_head(stream)
 
     def lm_head(self, stream=None) -> None:
+        """The int8-expanded lm_head (W8A16, fp16 group-32 scales)."""
         bqd.gemv_w8a16_group32(self.w8, self.w8s, self.head_x, y=self.head_y, stream=stream)
 
+    def lm_head_q6k(self, stream=None) -> None:
+        """The packed 6-bit lm_head, decoded in registers."""
+        bqd.gemv_q6k_f16(self.q6k, self.head_x, y=self.head_y, stream=stream)
+
+    def head_bytes(self, head=None) -> int:
+        return bytes_q6k(*self.head_NK) if (head or self.head) == "q6k" else bytes_w8a16(*self.head_NK)
+
     def bytes_per_step(self) -> int:
-        return sum(bytes_group32_linear(d["N"], d["K"], False) for d in self.linears) + \
-            bytes_w8a16(*self.head_NK)
+        return sum(bytes_group32_linear(d["N"], d["K"], False) for d in self.linears) + self.head_bytes()
 
     def weight_bytes(self) -> int:
         N, K = self.head_NK
-        return sum(d["N"] * d["K"] // 2 + 2 * d["N"] * (d["K"] // 32) for d in self.linears) + \
-            N * K + 2 * N * (K // 32)
+        head = N * K * 210 // 256 if self.head == "q6k" else N * K + 2 * N * (K // 32)
+        return sum(d["N"] * d["K"] // 2 + 2 * d["N"] * (d["K"] // 32) for d in self.linears) + head
 
 
 class VerifyPool:

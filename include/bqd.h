@@ -225,6 +225,38 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
                        float* y, int32_t N, int32_t K, int32_t r,
                        int32_t lanes_per_row, void* stream);
 
+/* Packed 6-bit lm_head ("在香橙派上跑 Gemma4 ...", section 3.2: a Q6_K weight
+ * stores 256 weights in 210 bytes -- 4-bit low and 2-bit high fields of each
+ * code, an int8 scale per 16 weights, an fp16 scale per 256 -- and the page
+ * expands it to int8 at load time because decoding the fields was vector-
+ * instruction bound on its chip).  The quantiser and the layout are this
+ * library's own.  Per row (K % 256 == 0), as separate arrays:
+ *   ql [N, K/2] uint8: low nibble of u = q + 32 in byte i/2 (bits 0-3 for
+ *      even i, 4-7 for odd i);
+ *   qh [N, K/4] uint8: per 16 weights a little-endian uint32; weight 8k + e
+ *      (k in {0, 1}, e in 0..7) puts bits 4-5 of u at bit
+ *      2(e mod 4) + 8k + 16[e >= 4];
+ *   sc [N, K/16] int8 sub-block scales; d [N, K/256] fp16 super-block scales.
+ * Value of weight i: d * sc[i/16] * q_i, q in [-32, 31]. */
+
+/* Load-time quantisation: per 16 weights t = max|w| / 31; per 256 weights
+ * d = fp16_rne(max t / 127); sc = clip(round(t / d), 0, 127); codes
+ * q = clip(round(w / (d * sc)), -32, 31) (fp32 divisions, round half to even;
+ * a zero scale gives zero codes).  W (device) float [N, K], 16-byte aligned;
+ * ql 8-, qh 4-, d 2-byte aligned.  K <= BQD_MAX_K. */
+int quantize_weights_q6k(const float* W, int32_t N, int32_t K, uint8_t* ql, uint8_t* qh,
+                         int8_t* sc, uint16_t* d, void* stream);
+
+/* y[j] = sum over 16-weight sub-blocks s of fp32(d) * sc_s * sum_{i in s} q_i * x16[i]
+ * (fp32 accumulation), the codes decoded from the packed fields in registers.
+ * x16 (device) fp16 bits [K], 16-byte aligned; y (device) float [N]; ql and
+ * qh 16-, sc 4-, d 2-byte aligned (true for row-major arrays from aligned
+ * bases).  K <= 32768.  r, lanes_per_row as in gemv_w4a8, and lanes_per_row
+ * may also be 8 (0 = 2 rows, 16 lanes). */
+int gemv_q6k_f16(const uint8_t* ql, const uint8_t* qh, const int8_t* sc, const uint16_t* d,
+                 const uint16_t* x16, float* y, int32_t N, int32_t K, int32_t r,
+                 int32_t lanes_per_row, void* stream);
+
 /* W4A16 comparison GEMV: the same packed per-row INT4 weights against an
  * fp16 activation, unpacked to fp16 and multiplied in floating point (the
  * route "Jetson Orin AGX INT4 ..." section "为什么 INT4 float 解包不快"

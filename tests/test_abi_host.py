@@ -242,3 +242,25 @@ def test_producers_validate_before_launch():
     assert L.swiglu_quant(P, None, P, P, 2, 64, None) == NULL  # h_out is required
     assert L.swiglu_quant(P, P4, P, P, 2, 64, None) == ALIGN
     assert L.swiglu_quant(P, None, P, P, 0, 64, None) == OK
+
+
+def test_q6k_entry_points_validate_before_launch():
+    L = _lib()
+    # quantize_weights_q6k(W, N, K, ql, qh, sc, d, stream)
+    assert L.quantize_weights_q6k(P, 4, 128, P, P, P, P, None) == SHAPE
+    assert L.quantize_weights_q6k(P, 4, 65536 + 256, P, P, P, P, None) == BOUND
+    assert L.quantize_weights_q6k(P, -1, 256, P, P, P, P, None) == SHAPE
+    assert L.quantize_weights_q6k(P, 4, 256, P, None, P, P, None) == NULL
+    assert L.quantize_weights_q6k(P4, 4, 256, P, P, P, P, None) == ALIGN
+    assert L.quantize_weights_q6k(P, 4, 256, P4, P, P, P, None) == ALIGN
+    assert L.quantize_weights_q6k(P, 0, 256, None, None, None, None, None) == OK
+    # gemv_q6k_f16(ql, qh, sc, d, x16, y, N, K, r, lanes, stream)
+    assert L.gemv_q6k_f16(P, P, P, P, P, P, 4, 96, 0, 0, None) == SHAPE
+    assert L.gemv_q6k_f16(P, P, P, P, P, P, 4, 65536, 0, 0, None) == BOUND
+    assert L.gemv_q6k_f16(P, P, None, P, P, P, 4, 256, 0, 0, None) == NULL
+    assert L.gemv_q6k_f16(P, P4, P, P, P, P, 4, 256, 0, 0, None) == ALIGN
+    assert L.gemv_q6k_f16(P, P + 8, P, P, P, P, 4, 256, 0, 0, None) == ALIGN
+    assert L.gemv_q6k_f16(P, P, P, P, P, P, 4, 256, 0, 4, None) == CONFIG
+    assert L.gemv_q6k_f16(P, P, P, P, P + 8, P, 4, 256, 0, 0, None) == ALIGN
+    assert L.gemv_q6k_f16(P, P, P, P, P, P, 4, 256, 3, 0, None) == CONFIG
+    assert L.gemv_q6k_f16(P, P, P, P, P, P, 0, 256, 0, 0, None) == OK

@@ -544,3 +544,68 @@ def test_decode_pass_rejects_descriptors_for_another_grid():
     p.run()
     sync()
     assert p.error_word() == 0 and not any(torch.isnan(y).any() for y in ys)
+
+
+# ------------------------------------------------ packed 6-bit lm_head --
+@pytest.mark.parametrize("N,K", [(3, 256), (37, 1536), (5, 4096)])
+def test_quantize_weights_q6k_bit_exact(N, K):
+    """Load-time 6-bit quantisation: ql, qh, sc and d bit-identical to the
+    oracle's quantiser + packer (with a zero row, a zero sub-block and tiny
+    sub-blocks under a large one)."""
+    W = I.normal(f"gpu/q6k/{N}/{K}/W", (N, K), 0.02, device=DEV)
+    W[0].zero_()
+    if N > 1:
+        W[1, 16:32] = 0.0
+        W[1, 256 * (K // 512):] *= 1e-3
+    w = bqd.quantize_weights_q6k(W)
+    sync()
+    q, sc, d = O.quantize_weights_q6k(npy(W))
+    ql, qh = O.pack_q6k(q)
+    assert np.array_equal(npy(w.ql), ql) and np.array_equal(npy(w.qh), qh)
+    assert np.array_equal(npy(w.sc), sc) and np.array_equal(f16bits(w.d), d)
+
+
+def _q6k_random(N, K, tag):
+    """Every byte pattern of ql/qh (all codes), int8 scales over the whole
+    int8 range, fp16 super-block scales."""
+    ql = I.random_words(f"gpu/q6k/{tag}/ql", (N, K // 8), device=DEV).view(torch.uint8).view(N, K // 2)
+    qh = I.random_words(f"gpu/q6k/{tag}/qh", (N, K // 16), device=DEV).view(torch.uint8).view(N, K // 4)
+    sc = I.uniform_int(f"gpu/q6k/{tag}/sc", (N, K // 16), -128, 127, device=DEV, dtype=torch.int8)
+    d = I.normal(f"gpu/q6k/{tag}/d", (N, K // 256), 1e-3, device=DEV, dtype=torch.float16)
+    return bqd.Q6KWeights(ql, qh, sc, d)
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (37, 768), (300, 1536), (2049, 1536)])
+def test_gemv_q6k_matches_oracle(N, K):
+    """In-register decode of the packed fields against the oracle, every
+    (r, lanes) configuration; rows past a tile and chunks past a row."""
+    w = _q6k_random(N, K, f"{N}/{K}")
+    x16 = I.normal(f"gpu/q6k/{N}/{K}/x", K, 1.0, device=DEV, dtype=torch.float16)
+    ql, qh, sc, d = npy(w.ql), npy(w.qh), npy(w.sc), f16bits(w.d)
+    yr = O.gemv_q6k_f16(ql, qh, sc, d, f16bits(x16))
+    q = O.unpack_q6k(ql, qh).astype(np.float64)
+    e = (d.view(np.float16).astype(np.float64)[:, :, None] * sc.reshape(N, K // 256, 16)).reshape(N, K // 16)
+    ax = np.abs(npy(x16).astype(np.float64))
+    mag = (np.abs(e) * (np.abs(q) * ax).reshape(N, K // 16, 16).sum(2)).sum(1)
+    for r, L in ((0, 0), (1, 16), (2, 32), (4, 64), (8, 16), (1, 64), (1, 8), (2, 8), (8, 8)):
+        y = bqd.gemv_q6k_f16(w, x16, r=r, lanes_per_row=L)
+        sync()
+        assert rel_err(npy(y), yr, mag).max() <= TOL, (r, L)
+
+
+def test_gemv_q6k_of_quantised_weights_tracks_the_int8_expansion():
+    """Quantise W to the packed form on the GPU, expand the codes to int8
+    with per-16 fp32 scales d*sc (the page's load-time expansion): the
+    packed GEMV equals the float64 product of the expansion."""
+    N, K = 512, 1536
+    W = I.normal("gpu/q6k/exp/W", (N, K), 0.02, device=DEV)
+    w = bqd.quantize_weights_q6k(W)
+    x16 = I.normal("gpu/q6k/exp/x", K, 1.0, device=DEV, dtype=torch.float16)
+    y = bqd.gemv_q6k_f16(w, x16)
+    sync()
+    q = O.unpack_q6k(npy(w.ql), npy(w.qh)).astype(np.float64)
+    e = (npy(w.d).astype(np.float64)[:, :, None] * npy(w.sc).reshape(N, K // 256, 16)).reshape(N, K // 16)
+    Wd = np.repeat(e, 16, axis=1) * q
+    ref = Wd @ npy(x16).astype(np.float64)
+    mag = np.abs(Wd) @ np.abs(npy(x16).astype(np.float64))
+    assert rel_err(npy(y), ref, mag).max() <= TOL

@@ -188,3 +188,26 @@ def test_decode_chain_fused_equals_unfused_and_oracle():
     qg, _ = bqd.add_rmsnorm_quant(c.h_in, c.gamma[0], DS.RMS_EPS)
     torch.cuda.synchronize()
     assert np.array_equal(npy(qg), q)
+
+
+def test_gemma_packed_6bit_lm_head():
+    """The Gemma token step with the packed 6-bit lm_head [262144, 1536], one
+    graph replay: on sampled rows the packed fields equal the oracle's
+    quantiser + packer and y matches the oracle's GEMV."""
+    w = WL.GemmaG32Stream(layers=1, device=DEV, head="q6k")
+    _graph_replay(w.step, 1)
+    N, K = w.head_NK
+    rows = _rows(N, "gemma/q6k", 256)
+    W = I.normal("gemma/lm_head/W", (N, K), 0.02, 0, DEV)[torch.as_tensor(rows, device=DEV)]
+    q, sc, d = O.quantize_weights_q6k(npy(W))
+    ql, qh = O.pack_q6k(q)
+    g = w.q6k
+    assert np.array_equal(npy(g.ql)[rows], ql) and np.array_equal(npy(g.qh)[rows], qh)
+    assert np.array_equal(npy(g.sc)[rows], sc) and np.array_equal(f16bits(g.d)[rows], d)
+    x = f16bits(w.head_x)
+    yr = O.gemv_q6k_f16(ql, qh, sc, d, x)
+    e = (d.view(np.float16).astype(np.float64)[:, :, None] * sc.reshape(len(rows), K // 256, 16)).reshape(len(rows), -1)
+    ax = np.abs(x.view(np.float16).astype(np.float64))
+    mag = (np.abs(e) * (np.abs(q.astype(np.float64)) * ax).reshape(len(rows), K // 16, 16).sum(2)).sum(1)
+    err = np.abs(npy(w.head_y)[rows].astype(np.float64) - yr) / mag
+    assert err.max() <= TOL, err.max()
