@@ -716,3 +716,156 @@ int orc_gemv_q6k_f16(const uint8_t* ql, const uint8_t* qh, const int8_t* sc, con
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* INT8-X (3,5,8) lossless codec of INT8 weights ("定長無損 INT8 壓縮與       */
+/* Triton 融合解碼", sections 2.1-2.5), over the row-major flattened tensor:  */
+/*   level 1: |v| <= 3   -> 3-bit two's complement code, stream L1          */
+/*   level 2: |v| <= 15  -> 5-bit two's complement code, stream L2          */
+/*   level 3: otherwise  -> the raw byte, stream L3                          */
+/*   B1: one bit per weight, 1 = not level 1;                                */
+/*   B2: one bit per weight outside level 1, in order, 1 = level 3;          */
+/*   b1_blk[b], b2_blk[b]: set bits of B1 and of B2 before block b (blocks   */
+/*   of blk weights; one extra entry holds the totals).                      */
+/* Bit streams are LSB-first: bit p is bit p % 32 of word p / 32.            */
+/* ------------------------------------------------------------------------ */
+static int int8x_level(int8_t v)
+{
+    const int a = v < 0 ? -(int)v : (int)v;
+    return a <= 3 ? 1 : (a <= 15 ? 2 : 3);
+}
+
+static void put_bits(uint32_t* s, int64_t pos, uint32_t val, int width)
+{
+    for (int k = 0; k < width; ++k)
+        if ((val >> k) & 1u)
+            s[(pos + k) / 32] |= 1u << ((pos + k) % 32);
+}
+
+static uint32_t get_bits(const uint32_t* s, int64_t pos, int width)
+{
+    uint32_t v = 0;
+    for (int k = 0; k < width; ++k)
+        v |= ((s[(pos + k) / 32] >> ((pos + k) % 32)) & 1u) << k;
+    return v;
+}
+
+static int32_t sign_extend(uint32_t v, int width)
+{
+    return (int32_t)(v << (32 - width)) >> (32 - width);
+}
+
+/* Level counts of n weights. */
+void orc_int8x_counts(const int8_t* q, int64_t n, int64_t* n1, int64_t* n2, int64_t* n3)
+{
+    int64_t c[4] = {0, 0, 0, 0};
+    for (int64_t t = 0; t < n; ++t)
+        c[int8x_level(q[t])]++;
+    *n1 = c[1];
+    *n2 = c[2];
+    *n3 = c[3];
+}
+
+/* Encode n weights.  Stream arrays must hold the word counts that the
+ * level counts imply (b1: ceil(n/32), b2: ceil((n2+n3)/32), l1:
+ * ceil(3 n1/32), l2: ceil(5 n2/32) words; l3: n3 bytes; b1_blk, b2_blk:
+ * ceil(n/blk) + 1 entries); they are zeroed here first. */
+int orc_int8x_encode(const int8_t* q, int64_t n, int64_t blk, uint32_t* b1, uint32_t* b2, uint32_t* l1,
+                     uint32_t* l2, uint8_t* l3, int32_t* b1_blk, int32_t* b2_blk)
+{
+    if (n <= 0 || blk <= 0 || blk % 32)
+        return ORC_E_ARG;
+    int64_t n1, n2, n3;
+    orc_int8x_counts(q, n, &n1, &n2, &n3);
+    memset(b1, 0, (size_t)((n + 31) / 32) * 4);
+    memset(b2, 0, (size_t)((n2 + n3 + 31) / 32) * 4);
+    memset(l1, 0, (size_t)((3 * n1 + 31) / 32) * 4);
+    memset(l2, 0, (size_t)((5 * n2 + 31) / 32) * 4);
+    int64_t c1 = 0, c2 = 0, c3 = 0; /* elements of each level so far */
+    for (int64_t t = 0; t < n; ++t) {
+        if (t % blk == 0) {
+            b1_blk[t / blk] = (int32_t)(c2 + c3);
+            b2_blk[t / blk] = (int32_t)c3;
+        }
+        const int lv = int8x_level(q[t]);
+        if (lv == 1) {
+            put_bits(l1, 3 * c1, (uint32_t)q[t] & 7u, 3);
+            ++c1;
+            continue;
+        }
+        b1[t / 32] |= 1u << (t % 32);
+        if (lv == 2) {
+            put_bits(l2, 5 * c2, (uint32_t)q[t] & 31u, 5);
+            ++c2;
+        } else {
+            b2[(c2 + c3) / 32] |= 1u << ((c2 + c3) % 32);
+            l3[c3] = (uint8_t)q[t];
+            ++c3;
+        }
+    }
+    const int64_t nb = (n + blk - 1) / blk;
+    b1_blk[nb] = (int32_t)(c2 + c3);
+    b2_blk[nb] = (int32_t)c3;
+    return ORC_OK;
+}
+
+/* Decode weights [t0, t0 + count) of an encoded tensor, using the block
+ * prefix sums to start at the block of t0 (the decoder of the page's
+ * section 2.4: a weight's position in its level's stream is the number of
+ * weights of that level before it). */
+int orc_int8x_decode(const uint32_t* b1, const uint32_t* b2, const uint32_t* l1, const uint32_t* l2,
+                     const uint8_t* l3, const int32_t* b1_blk, const int32_t* b2_blk, int64_t blk,
+                     int64_t t0, int64_t count, int8_t* q)
+{
+    if (blk <= 0 || blk % 32 || t0 < 0 || count < 0)
+        return ORC_E_ARG;
+    const int64_t b = t0 / blk;
+    int64_t nonl1 = b1_blk[b];            /* B1 bits set before the block */
+    int64_t c3 = b2_blk[b];               /* level-3 weights before the block */
+    int64_t c2 = nonl1 - c3;
+    int64_t c1 = b * blk - nonl1;
+    for (int64_t t = b * blk; t < t0 + count; ++t) {
+        int8_t v;
+        if (!((b1[t / 32] >> (t % 32)) & 1u)) {
+            v = (int8_t)sign_extend(get_bits(l1, 3 * c1, 3), 3);
+            ++c1;
+        } else if (!((b2[nonl1 / 32] >> (nonl1 % 32)) & 1u)) {
+            v = (int8_t)sign_extend(get_bits(l2, 5 * c2, 5), 5);
+            ++c2;
+            ++nonl1;
+        } else {
+            v = (int8_t)l3[c3];
+            ++c3;
+            ++nonl1;
+        }
+        if (t >= t0)
+            q[t - t0] = v;
+    }
+    return ORC_OK;
+}
+
+/* W8A8 GEMV over INT8-X weights [N, K] with one per-tensor weight scale:
+ *   acc_j = sum_i q_ji qx_i (exact),  y_j = sw * sx * acc_j (binary64). */
+int orc_gemv_int8x(const uint32_t* b1, const uint32_t* b2, const uint32_t* l1, const uint32_t* l2,
+                   const uint8_t* l3, const int32_t* b1_blk, const int32_t* b2_blk, int64_t blk,
+                   const int8_t* qx, float sx, float sw, int64_t N, int64_t K, int32_t* acc_out,
+                   double* y)
+{
+    if (N < 0 || K <= 0 || K > 65536)
+        return ORC_E_ARG;
+    int8_t row[65536];
+    for (int64_t j = 0; j < N; ++j) {
+        int rc = orc_int8x_decode(b1, b2, l1, l2, l3, b1_blk, b2_blk, blk, j * K, K, row);
+        if (rc)
+            return rc;
+        int64_t acc = 0;
+        for (int64_t i = 0; i < K; ++i)
+            acc += (int64_t)row[i] * (int64_t)qx[i];
+        if (acc > INT32_MAX || acc < INT32_MIN)
+            return ORC_E_BOUND;
+        if (acc_out)
+            acc_out[j] = (int32_t)acc;
+        y[j] = (double)sw * (double)sx * (double)acc;
+    }
+    return ORC_OK;
+}

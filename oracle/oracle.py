@@ -61,6 +61,10 @@ def _load():
         "orc_pack_q6k": (I32, [P, I64, I64, P, P]),
         "orc_unpack_q6k": (I32, [P, P, I64, I64, P]),
         "orc_gemv_q6k_f16": (I32, [P, P, P, P, P, I64, I64, P]),
+        "orc_int8x_counts": (None, [P, I64, P, P, P]),
+        "orc_int8x_encode": (I32, [P, I64, I64, P, P, P, P, P, P, P]),
+        "orc_int8x_decode": (I32, [P, P, P, P, P, P, P, I64, I64, I64, P]),
+        "orc_gemv_int8x": (I32, [P, P, P, P, P, P, P, I64, P, F32, F32, I64, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -283,6 +287,60 @@ def gemv_q6k_f16(ql, qh, sc, d, x16) -> np.ndarray:
     y = np.empty(N, np.float64)
     _check(_lib.orc_gemv_q6k_f16(_p(ql), _p(qh), _p(sc), _p(d), _p(xb), N, K, _p(y)))
     return y
+
+
+# ------------------------------------------------- INT8-X (3,5,8) codec ----
+INT8X_BLOCK = 512
+
+
+def int8x_counts(q) -> Tuple[int, int, int]:
+    """Weights of level 1 (|v| <= 3), 2 (|v| <= 15) and 3 (the rest)."""
+    q = _c(q, np.int8)
+    c = [C.c_int64(), C.c_int64(), C.c_int64()]
+    _lib.orc_int8x_counts(_p(q), q.size, *[C.byref(v) for v in c])
+    return tuple(int(v.value) for v in c)
+
+
+def int8x_encode(q, blk: int = INT8X_BLOCK) -> dict:
+    """INT8-X (3,5,8) encoding of the row-major flattened int8 tensor q
+    ("定長無損 INT8 壓縮與 Triton 融合解碼", sections 2.1-2.5): bitmaps b1, b2,
+    streams l1 (3-bit), l2 (5-bit), l3 (bytes), block prefix sums."""
+    q = _c(q, np.int8)
+    n = q.size
+    n1, n2, n3 = int8x_counts(q)
+    nb = (n + blk - 1) // blk
+    e = dict(b1=np.empty((n + 31) // 32, np.uint32), b2=np.empty(max(1, (n2 + n3 + 31) // 32), np.uint32),
+             l1=np.empty(max(1, (3 * n1 + 31) // 32), np.uint32), l2=np.empty(max(1, (5 * n2 + 31) // 32), np.uint32),
+             l3=np.empty(max(1, n3), np.uint8), b1_blk=np.empty(nb + 1, np.int32), b2_blk=np.empty(nb + 1, np.int32))
+    _check(_lib.orc_int8x_encode(_p(q), n, blk, _p(e["b1"]), _p(e["b2"]), _p(e["l1"]), _p(e["l2"]),
+                                 _p(e["l3"]), _p(e["b1_blk"]), _p(e["b2_blk"])))
+    e.update(n=n, n1=n1, n2=n2, n3=n3, blk=blk, shape=q.shape)
+    return e
+
+
+def int8x_bits(e: dict) -> int:
+    """Payload bits: B1 (n) + B2 (n2 + n3) + 3 n1 + 5 n2 + 8 n3."""
+    return e["n"] + e["n2"] + e["n3"] + 3 * e["n1"] + 5 * e["n2"] + 8 * e["n3"]
+
+
+def int8x_decode(e: dict, t0: int = 0, count: Optional[int] = None) -> np.ndarray:
+    count = e["n"] - t0 if count is None else count
+    q = np.empty(count, np.int8)
+    _check(_lib.orc_int8x_decode(_p(e["b1"]), _p(e["b2"]), _p(e["l1"]), _p(e["l2"]), _p(e["l3"]),
+                                 _p(e["b1_blk"]), _p(e["b2_blk"]), e["blk"], t0, count, _p(q)))
+    return q
+
+
+def gemv_int8x(e: dict, qx, sx: float, sw: float) -> Tuple[np.ndarray, np.ndarray]:
+    """W8A8 GEMV over INT8-X weights [N, K]: (acc int32 [N], y float64 [N])."""
+    N, K = e["shape"]
+    qx = _c(qx, np.int8)
+    acc = np.empty(N, np.int32)
+    y = np.empty(N, np.float64)
+    _check(_lib.orc_gemv_int8x(_p(e["b1"]), _p(e["b2"]), _p(e["l1"]), _p(e["l2"]), _p(e["l3"]),
+                               _p(e["b1_blk"]), _p(e["b2_blk"]), e["blk"], _p(qx), C.c_float(sx), C.c_float(sw),
+                               N, K, _p(acc), _p(y)))
+    return acc, y
 
 
 # -------------------------------------------------------------- GEMVs ----

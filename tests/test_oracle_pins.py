@@ -668,3 +668,62 @@ def test_q6k_gemv_vs_numpy_float64_dequantised_matmul():
     # and the dequantised weights stay within half a step of W
     step = np.repeat(e, 16, axis=1)
     assert np.all(np.abs(Wd - W) <= 0.5 * step * (1 + 1e-6) + (step == 0) * np.abs(W))
+
+
+# ---------------------------------------------------- INT8-X (3,5,8) codec --
+# "定長無損 INT8 壓縮與 Triton 融合解碼", sections 2.1-2.5.
+def test_int8x_layout_golden():
+    tab = {}
+    for l in open(os.path.join(ROOT, "tests", "golden", "int8x_layout.txt"), encoding="utf-8"):
+        if l.strip() and not l.startswith("#"):
+            k, *v = l.split()
+            tab[k] = [int(t, 0) for t in v]
+    q = np.tile(np.array(tab["pattern"], np.int8), 64).reshape(1, 512)
+    e = O.int8x_encode(q)
+    assert [e["n1"], e["n2"], e["n3"]] == tab["counts"]
+    for k in ("b1", "b2", "l1", "l2"):
+        assert int(e[k][0]) == tab[k][0], k
+    assert list(e["l3"][:4]) == tab["l3"]
+    assert list(e["b1_blk"]) == tab["b1_blk"] and list(e["b2_blk"]) == tab["b2_blk"]
+    assert np.array_equal(O.int8x_decode(e), q.ravel())
+
+
+def test_int8x_lossless_round_trip_and_block_decode():
+    rng = np.random.default_rng(21)
+    for q in (rng.integers(-128, 128, (7, 1024), dtype=np.int8),       # every byte value
+              rng.integers(-3, 4, (3, 512), dtype=np.int8),             # level 1 only
+              np.full((2, 512), -128, np.int8),                          # level 3 only
+              np.clip(np.round(rng.laplace(0, 4.3, (9, 3584))), -127, 127).astype(np.int8)):
+        e = O.int8x_encode(q)
+        assert np.array_equal(O.int8x_decode(e), q.ravel())
+        for t0, cnt in ((0, 1), (511, 3), (e["n"] - 5, 5), (e["n"] // 2 + 7, 100)):
+            assert np.array_equal(O.int8x_decode(e, t0, cnt), q.ravel()[t0:t0 + cnt])
+        n1, n2, n3 = O.int8x_counts(q)
+        a = np.abs(q.astype(np.int32))
+        assert (n1, n2, n3) == (int((a <= 3).sum()), int(((a > 3) & (a <= 15)).sum()), int((a > 15).sum()))
+
+
+def test_int8x_bit_accounting_reproduces_the_page():
+    """Level shares of 55.5 / 40.4 / 4.1 % (section 2.1) give flags 1.445 and
+    data 4.013 bit/w, 5.46 in total (section 2.3)."""
+    q = np.concatenate([np.full(555, 2), np.full(404, -9), np.full(41, 77)]).astype(np.int8)
+    e = O.int8x_encode(np.random.default_rng(5).permutation(q))
+    n = e["n"]
+    flags = (n + e["n2"] + e["n3"]) / n
+    data = (3 * e["n1"] + 5 * e["n2"] + 8 * e["n3"]) / n
+    assert abs(flags - 1.445) < 1e-12 and abs(data - 4.013) < 1e-12
+    assert round(O.int8x_bits(e) / n, 2) == 5.46
+
+
+def test_gemv_int8x_vs_numpy_integer_matmul():
+    """The GEMV over the encoded tensor against numpy's int64 matmul of the
+    original (not decoded) codes."""
+    rng = np.random.default_rng(22)
+    N, K = 11, 3584
+    q = np.clip(np.round(rng.laplace(0, 4.3, (N, K))), -127, 127).astype(np.int8)
+    q[3, :] = rng.integers(-128, 128, K)
+    qx = rng.integers(-127, 128, K).astype(np.int8)
+    acc, y = O.gemv_int8x(O.int8x_encode(q), qx, 0.0123, 0.0031)
+    ref = q.astype(np.int64) @ qx.astype(np.int64)
+    assert np.array_equal(acc, ref)
+    np.testing.assert_allclose(y, float(np.float32(0.0031)) * float(np.float32(0.0123)) * ref, rtol=1e-15)
