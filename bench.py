@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) for W4A8 decode GEMV; implied 28-layer tok/s"
 HBM_PEAK_GBS = 8000.0
-WORKLOADS = ("stream", "single", "layer", "gemma", "verify", "chain")
+WORKLOADS = ("stream", "single", "layer", "gemma", "verify", "chain", "int8x")
 
 
 def parse():
@@ -631,6 +631,46 @@ def cpu_baseline_chain(c, seconds):
                       f"{reps} passes in {el:.1f} s, single-threaded C"}
 
 
+# VALU instructions per weight of the compiled INT8-X decode loop (k_gemv_int8x:
+# one loop iteration decodes 8 weights per lane) and the chip's VALU issue
+# rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 VALU instruction holds
+# its SIMD for 4 cycles).
+INT8X_VALU_PER_WEIGHT = 250 / 8
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def run_int8x(a, dev):
+    """INT8-X (3,5,8) decode fused into a W8A8 GEMV at two Qwen2-7B linear
+    shapes (down [3584, 18944], gate/up [37888, 3584])."""
+    import torch
+    from bit_quantized_decode_quantize_amd import workloads as WL
+
+    shapes = []
+    for N, K in ((3584, 18944), (37888, 3584)):
+        w = WL.Int8XPool(N, K, device=dev, rows=a.r)
+        ms, n = time_steps(w.step, max(a.steps, 2 * w.copies), a.warmup, w.copies if (not a.eager) else 0)
+        valu = N * K * INT8X_VALU_PER_WEIGHT / (ms * 1e-3) / 1e12
+        shapes.append({"N": N, "K": K, "us": round(ms * 1e3, 3), "steps": n,
+                       "GB/s": round(w.bytes_per_step() / (ms * 1e-3) / 1e9, 1),
+                       "bits_per_weight": round(w.bits_per_weight(), 3),
+                       "level_shares": [round(c / (N * K), 4) for c in w.counts],
+                       "valu_Tops": round(valu, 2), "rotation_copies": w.copies})
+        log(f"int8x {N}x{K}: {shapes[-1]}")
+        del w
+        torch.cuda.empty_cache()
+    d = shapes[0]
+    out = base_line(a, d["GB/s"], d["us"] * 1e-3, d["steps"], {
+        "workload": "INT8-X (3,5,8) encoded int8 weights (level shares 55.5/40.4/4.1 %), decode fused into "
+                    "a W8A8 GEMV, down-projection shape [3584, 18944]",
+        "launch": "HIP graph" if (not a.eager) else "eager", "N": d["N"], "K": d["K"]}, dtype="int8")
+    out["shapes"] = shapes
+    out["roofline"] = {"bound": "alu", "achieved": d["valu_Tops"], "peak": round(VALU_PEAK_TOPS, 1),
+                       "unit": "T VALU lane-instructions/s", "frac": round(d["valu_Tops"] / VALU_PEAK_TOPS, 4),
+                       "traffic": None, "kernel": "k_gemv_int8x (decode + GEMV, one launch)",
+                       "avg_launch_us": d["us"], "valu_per_weight": INT8X_VALU_PER_WEIGHT}
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -641,7 +681,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     out = {"stream": run_stream, "single": run_single, "layer": run_layer, "gemma": run_gemma,
-           "verify": run_verify, "chain": run_chain}[a.workload](a, dev)
+           "verify": run_verify, "chain": run_chain, "int8x": run_int8x}[a.workload](a, dev)
     print(json.dumps(out), flush=True)
 
 

@@ -25,6 +25,7 @@ BQD_SCALE_ROW_F32, BQD_SCALE_GROUP32_F16 = 0, 1
 BQD_MAX_K = 65536
 BQD_MAX_TOKENS = 16
 BQD_MAX_PROD_K = 32768
+BQD_INT8X_BLOCK = 512
 
 ENTRY_POINTS = (
     "bqd_abi_version", "bqd_status_string", "bqd_init",
@@ -34,7 +35,8 @@ ENTRY_POINTS = (
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
     "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
     "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant",
-    "quantize_weights_q6k", "gemv_q6k_f16",
+    "quantize_weights_q6k", "gemv_q6k_f16", "int8x_counts_host", "int8x_stream_bytes_host",
+    "int8x_encode_host", "gemv_int8x",
 )
 
 
@@ -91,6 +93,10 @@ def lib() -> C.CDLL:
         "swiglu_quant": (I, [P, P, P, P, I, I, P]),
         "quantize_weights_q6k": (I, [P, I, I, P, P, P, P, P]),
         "gemv_q6k_f16": (I, [P, P, P, P, P, P, I, I, I, I, P]),
+        "int8x_counts_host": (I, [P, C.c_int64, P]),
+        "int8x_stream_bytes_host": (I, [C.c_int64, P, P]),
+        "int8x_encode_host": (I, [P, C.c_int64, P, P, P, P, P, P, P]),
+        "gemv_int8x": (I, [P, P, P, P, P, P, P, P, P, P, C.c_float, P, P, I, I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -407,6 +413,61 @@ def gemv_q6k_f16(w: Q6KWeights, x16, y=None, r=0, lanes_per_row=0, stream=None):
     _call("gemv_q6k_f16", w.ql.data_ptr(), w.qh.data_ptr(), w.sc.data_ptr(), w.d.data_ptr(), x16.data_ptr(),
           y.data_ptr(), N, K, r, lanes_per_row, _stream(stream))
     return y
+
+
+INT8X_ARRAYS = ("b1", "b2", "l1", "l2", "l3", "b1_blk", "b2_blk")
+
+
+class Int8XWeights:
+    """INT8-X (3,5,8) encoded weights [N, K] on the device: the seven arrays,
+    their byte sizes, the level counts and the per-tensor scale."""
+
+    def __init__(self, arrays: dict, sizes, counts, N: int, K: int, sw: float):
+        self.arrays, self.sizes, self.counts = arrays, sizes, counts
+        self.N, self.K, self.sw = N, K, float(sw)
+        self._sizes_c = (C.c_int64 * 7)(*sizes)
+
+    def payload_bits(self) -> int:
+        n1, n2, n3 = self.counts
+        n = self.N * self.K
+        return n + n2 + n3 + 3 * n1 + 5 * n2 + 8 * n3
+
+    def nbytes(self) -> int:
+        return int(sum(self.sizes))
+
+
+def int8x_encode(q: torch.Tensor, sw: float, device="cuda") -> Int8XWeights:
+    """Encode host int8 codes q [N, K] (the offline step of section 2.5) and
+    upload the arrays to ``device``."""
+    if q.dtype != torch.int8 or q.dim() != 2:
+        raise TypeError("q must be a 2-D int8 tensor")
+    q = q.detach().cpu().contiguous()
+    N, K = q.shape
+    n = N * K
+    counts = (C.c_int64 * 3)()
+    _call("int8x_counts_host", q.data_ptr(), n, counts)
+    sizes = (C.c_int64 * 7)()
+    _call("int8x_stream_bytes_host", n, counts, sizes)
+    host = {}
+    for name, nb in zip(INT8X_ARRAYS, sizes):
+        dt = torch.uint8 if name == "l3" else torch.int32
+        host[name] = torch.zeros(nb // (1 if dt == torch.uint8 else 4), dtype=dt)
+    _call("int8x_encode_host", q.data_ptr(), n, *[host[k].data_ptr() for k in INT8X_ARRAYS])
+    dev = {k: v.to(device) for k, v in host.items()}
+    return Int8XWeights(dev, list(sizes), tuple(counts), N, K, sw)
+
+
+def gemv_int8x(w: Int8XWeights, qx, sx, y=None, acc=None, rows=0, stream=None):
+    """W8A8 GEMV over INT8-X weights: qx int8 [K], sx fp32 [1] -> y fp32 [N]
+    (and acc int32 [N] with acc=True)."""
+    _dev(qx, "qx", (torch.int8,), w.K)
+    _dev(sx, "sx", _F32)
+    a = w.arrays
+    y = _empty((w.N,), torch.float32, qx) if y is None else _dev(y, "y", _F32, w.N)
+    acc_t = _empty((w.N,), torch.int32, qx) if acc is True else None
+    _call("gemv_int8x", *[a[k].data_ptr() for k in INT8X_ARRAYS], w._sizes_c, qx.data_ptr(), sx.data_ptr(),
+          w.sw, y.data_ptr(), _ptr(acc_t), w.N, w.K, rows, _stream(stream))
+    return (y, acc_t) if acc_t is not None else y
 
 
 def gemv_w4a16(wq, sw, bias, x16, y=None, r=0, lanes_per_row=0, stream=None):

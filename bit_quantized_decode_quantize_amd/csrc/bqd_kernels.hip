@@ -1197,6 +1197,134 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q6k(const u32x4* __restrict__
 }
 
 // ------------------------------------------------------------------------
+// INT8-X (3,5,8) lossless INT8 weights ("定長無損 INT8 壓縮與 Triton 融合解碼",
+// sections 2.1-2.5), decoded inside a W8A8 GEMV.  Over the row-major
+// flattened tensor: B1 (a bit per weight, 1 = not level 1), B2 (a bit per
+// non-level-1 weight, 1 = level 3), L1 (3-bit two's complement codes of
+// |v| <= 3), L2 (5-bit codes of |v| <= 15), L3 (raw bytes), all bit streams
+// LSB-first; per block of BQD_INT8X_BLOCK weights the set bits of B1 and B2
+// before it.  A wave decodes one block, 8 weights per lane: the lane's B1
+// byte gives its non-level-1 count, a wave prefix scan its place among the
+// block's, its B2 bits (a 64-bit window) its level-3 count and a second
+// scan; the block sums then locate its runs in L1, L2 and L3, read through
+// 64/96-bit windows; the 8 codes are selected branch-free, dotted with the
+// int8 activation (two v_dot4_i32_i8) and summed exactly per row in LDS.
+// Every stream index is clamped to its stream, so a malformed encoding
+// cannot read out of bounds.
+// ------------------------------------------------------------------------
+constexpr int kInt8xBlock = BQD_INT8X_BLOCK;
+static_assert(kInt8xBlock == 8 * kWave, "one wave decodes one block, 8 weights per lane");
+
+__device__ __forceinline__ int wave_excl_scan(int v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(inc, o);
+        inc += lane >= o ? t : 0;
+    }
+    return inc - v;
+}
+
+struct Int8xStreams {
+    const uint32_t* b1;
+    const uint32_t* b2;
+    const uint32_t* l1;
+    const uint32_t* l2;
+    const uint32_t* l3;  // bytes, read as words
+    const int32_t* b1_blk;
+    const int32_t* b2_blk;
+    int nb2, nl1, nl2, nl3;  // words in b2, l1, l2, l3 (>= 3: padding included)
+};
+
+// 64 bits of a word stream from bit pos, as (hi, lo); the first word index
+// is clamped to [0, n - 3] so the three reads stay inside the stream.
+__device__ __forceinline__ void window(const uint32_t* s, int pos, int n, uint32_t& lo, uint32_t& hi)
+{
+    const int w = min(max(pos >> 5, 0), n - 3);
+    const uint32_t a = s[w], b = s[w + 1], c = s[w + 2];
+    const uint32_t off = (uint32_t)pos & 31u;
+    lo = __builtin_amdgcn_alignbit(b, a, off);
+    hi = __builtin_amdgcn_alignbit(c, b, off);
+}
+
+template <int R>
+__global__ __launch_bounds__(kThreads) void k_gemv_int8x(Int8xStreams st, const int8_t* __restrict__ qx,
+                                                         const float* __restrict__ sx, float sw,
+                                                         float* __restrict__ y, int32_t* __restrict__ acc_out,
+                                                         int N, int K)
+{
+    __shared__ int racc[R];
+    if (threadIdx.x < R)
+        racc[threadIdx.x] = 0;
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int bpr = K / kInt8xBlock;  // blocks per row
+    const int row0 = blockIdx.x * R;
+    const int items = min(R, N - row0) * bpr;
+    for (int item = wave; item < items; item += kThreads / kWave) {
+        const int rr = item / bpr, bi = item % bpr;
+        const long long g = (long long)(row0 + rr) * bpr + bi;  // global block
+        const long long t0 = g * kInt8xBlock;
+        const uint32_t b1w = st.b1[(t0 >> 5) + (lane >> 2)];
+        const uint32_t bits8 = (b1w >> (8 * (lane & 3))) & 0xFFu;
+        const int nn = __builtin_popcount(bits8);
+        const int pre_nn = wave_excl_scan(nn);
+        const int blk1 = st.b1_blk[g], blk2 = st.b2_blk[g];
+        uint32_t b2lo, b2hi;
+        window(st.b2, blk1 + pre_nn, st.nb2, b2lo, b2hi);
+        const uint32_t b2bits = b2lo & ((1u << nn) - 1u);
+        const int n3 = __builtin_popcount(b2bits);
+        const int pre3 = wave_excl_scan(n3);
+        // first stream index of the lane's weights of each level
+        const int i1 = (int)(t0 - blk1) + (8 * lane - pre_nn);
+        const int i2 = (blk1 - blk2) + (pre_nn - pre3);
+        const int i3 = blk2 + pre3;
+        uint32_t w1, w1h, lo2, hi2, lo3, hi3;
+        window(st.l1, 3 * i1, st.nl1, w1, w1h);
+        window(st.l2, 5 * i2, st.nl2, lo2, hi2);
+        window(st.l3, 8 * i3, st.nl3, lo3, hi3);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // rank of weight e among the lane's non-level-1 weights, and
+            // among its level-3 ones, from the bitmap bits below it
+            const int rn = __builtin_popcount(bits8 & ((1u << e) - 1u));
+            const int r3 = __builtin_popcount(b2bits & ((1u << rn) - 1u));
+            const bool n1 = (bits8 >> e) & 1u;
+            const bool l3 = (b2bits >> rn) & 1u;
+            const int r1 = e - rn, r2 = rn - r3;
+            const int c1 = __builtin_amdgcn_sbfe((int)w1, 3 * r1, 3);
+            const int o2 = 5 * r2;  // <= 30 unless e == 7
+            const uint32_t f2 = (e == 7 && o2 >= 32) ? hi2 >> (o2 - 32) : __builtin_amdgcn_alignbit(hi2, lo2, o2);
+            const int c2 = __builtin_amdgcn_sbfe((int)f2, 0, 5);
+            const int c3 = __builtin_amdgcn_sbfe((int)__builtin_amdgcn_perm(hi3, lo3, 0x0C0C0C00u | (uint32_t)r3), 0, 8);
+            const int v = n1 ? (l3 ? c3 : c2) : c1;
+            if (e < 4)
+                lo |= ((uint32_t)v & 0xFFu) << (8 * e);
+            else
+                hi |= ((uint32_t)v & 0xFFu) << (8 * (e - 4));
+        }
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(qx + (size_t)bi * kInt8xBlock + 8 * lane);
+        int a = __builtin_amdgcn_sdot4((int)lo, (int)xv.x, 0, false);
+        a = __builtin_amdgcn_sdot4((int)hi, (int)xv.y, a, false);
+        a = sum_lanes<64>(a);
+        if (lane == 0)
+            atomicAdd(&racc[rr], a);
+    }
+    __syncthreads();
+    if (threadIdx.x < R && row0 + (int)threadIdx.x < N) {
+        const int row = row0 + threadIdx.x;
+        const int a = racc[threadIdx.x];
+        if (acc_out)
+            acc_out[row] = a;
+        y[row] = (sw * sx[0]) * (float)a;
+    }
+}
+
+// ------------------------------------------------------------------------
 // W4A16 comparison GEMV: the same packed per-row INT4 weights against an
 // fp16 activation, unpacked to fp16 and multiplied in floating point
 // ("Jetson Orin AGX INT4 ..." section "为什么 INT4 float 解包不快" weighs this
@@ -2167,6 +2295,155 @@ int quantize_weights_int8_group32(const float* W, int32_t N, int32_t K, int8_t* 
                                   void* stream)
 {
     return quantize_group32_common(true, W, N, K, w8, s16, stream);
+}
+
+int int8x_counts_host(const int8_t* q, int64_t n, int64_t* counts)
+{
+    if (!q || !counts)
+        return BQD_ERR_NULL;
+    if (n <= 0)
+        return BQD_ERR_SHAPE;
+    int64_t c[3] = {0, 0, 0};
+    for (int64_t t = 0; t < n; ++t) {
+        const int a = q[t] < 0 ? -(int)q[t] : (int)q[t];
+        c[(a > 3) + (a > 15)]++;
+    }
+    counts[0] = c[0];
+    counts[1] = c[1];
+    counts[2] = c[2];
+    return BQD_OK;
+}
+
+int int8x_stream_bytes_host(int64_t n, const int64_t* counts, int64_t* bytes)
+{
+    if (!counts || !bytes)
+        return BQD_ERR_NULL;
+    if (n <= 0 || counts[0] < 0 || counts[1] < 0 || counts[2] < 0 || counts[0] + counts[1] + counts[2] != n)
+        return BQD_ERR_SHAPE;
+    auto words = [](int64_t bits) { return (bits + 31) / 32 + 3; };  // + padding for the read windows
+    const int64_t blocks = (n + kInt8xBlock - 1) / kInt8xBlock;
+    bytes[0] = 4 * words(n);                            // b1
+    bytes[1] = 4 * words(counts[1] + counts[2]);        // b2
+    bytes[2] = 4 * words(3 * counts[0]);                // l1
+    bytes[3] = 4 * words(5 * counts[1]);                // l2
+    bytes[4] = 4 * words(8 * counts[2]);                // l3
+    bytes[5] = 4 * (blocks + 1);                        // b1_blk
+    bytes[6] = 4 * (blocks + 1);                        // b2_blk
+    return BQD_OK;
+}
+
+// Bit writer over a zeroed word stream, LSB-first.
+struct BitSink {
+    uint32_t* w;
+    int64_t pos = 0;
+    void put(uint32_t v, int width)
+    {
+        v &= (1u << width) - 1u;
+        const int64_t i = pos >> 5;
+        const int off = (int)(pos & 31);
+        w[i] |= v << off;
+        if (off + width > 32)
+            w[i + 1] |= v >> (32 - off);
+        pos += width;
+    }
+};
+
+int int8x_encode_host(const int8_t* q, int64_t n, uint32_t* b1, uint32_t* b2, uint32_t* l1, uint32_t* l2,
+                      uint8_t* l3, int32_t* b1_blk, int32_t* b2_blk)
+{
+    if (!q || !b1 || !b2 || !l1 || !l2 || !l3 || !b1_blk || !b2_blk)
+        return BQD_ERR_NULL;
+    int64_t counts[3], bytes[7];
+    int rc = int8x_counts_host(q, n, counts);
+    if (rc || (rc = int8x_stream_bytes_host(n, counts, bytes)))
+        return rc;
+    if (counts[1] + counts[2] > INT32_MAX)
+        return BQD_ERR_BOUND;
+    std::memset(b1, 0, bytes[0]);
+    std::memset(b2, 0, bytes[1]);
+    std::memset(l1, 0, bytes[2]);
+    std::memset(l2, 0, bytes[3]);
+    std::memset(l3, 0, bytes[4]);
+    BitSink s1{l1}, s2{l2}, sb2{b2};
+    int64_t n3 = 0;
+    for (int64_t t = 0; t < n; ++t) {
+        if (t % kInt8xBlock == 0) {
+            b1_blk[t / kInt8xBlock] = (int32_t)sb2.pos;  // non-level-1 weights so far
+            b2_blk[t / kInt8xBlock] = (int32_t)n3;
+        }
+        const int v = q[t];
+        const int a = v < 0 ? -v : v;
+        if (a <= 3) {
+            s1.put((uint32_t)v, 3);
+            continue;
+        }
+        b1[t >> 5] |= 1u << (t & 31);
+        if (a <= 15) {
+            sb2.put(0u, 1);
+            s2.put((uint32_t)v, 5);
+        } else {
+            sb2.put(1u, 1);
+            l3[n3++] = (uint8_t)v;
+        }
+    }
+    const int64_t blocks = (n + kInt8xBlock - 1) / kInt8xBlock;
+    b1_blk[blocks] = (int32_t)sb2.pos;
+    b2_blk[blocks] = (int32_t)n3;
+    return BQD_OK;
+}
+
+int gemv_int8x(const uint32_t* b1, const uint32_t* b2, const uint32_t* l1, const uint32_t* l2, const uint8_t* l3,
+               const int32_t* b1_blk, const int32_t* b2_blk, const int64_t* stream_bytes, const int8_t* qx,
+               const float* sx, float sw, float* y, int32_t* acc, int32_t N, int32_t K, int32_t rows,
+               void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K, kInt8xBlock);
+    if (rc)
+        return rc;
+    if (K > BQD_MAX_K)
+        return BQD_ERR_BOUND;
+    if (N == 0)
+        return BQD_OK;
+    if (!b1 || !b2 || !l1 || !l2 || !l3 || !b1_blk || !b2_blk || !stream_bytes || !qx || !sx || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(b1, 4) || !aligned(b2, 4) || !aligned(l1, 4) || !aligned(l2, 4) || !aligned(l3, 4) ||
+        !aligned(qx, 8) || !aligned(y, 4) || !aligned(acc, 4))
+        return BQD_ERR_ALIGN;
+    for (int i = 1; i < 5; ++i)  // three words at least (the encoder's padding)
+        if (stream_bytes[i] < 12 || stream_bytes[i] % 4)
+            return BQD_ERR_SHAPE;
+    // bit positions are int32 in the kernel: every stream below 2^26 words
+    if ((int64_t)N * K >= ((int64_t)1 << 31))
+        return BQD_ERR_BOUND;
+    for (int i = 1; i < 5; ++i)
+        if (stream_bytes[i] / 4 > ((int64_t)1 << 26))
+            return BQD_ERR_BOUND;
+    if (stream_bytes[0] < 4 * (((int64_t)N * K + 31) / 32) ||
+        stream_bytes[5] < 4 * ((int64_t)N * K / kInt8xBlock + 1) ||
+        stream_bytes[6] < 4 * ((int64_t)N * K / kInt8xBlock + 1))
+        return BQD_ERR_SHAPE;
+    if (rows != 0 && rows != 1 && rows != 2 && rows != 4 && rows != 8)
+        return BQD_ERR_CONFIG;
+    // automatic: one row per workgroup keeps enough waves in flight for short
+    // matrices (measured: [3584, 18944] 69 us with 1, 103 with 4); 4 from 8192 rows
+    const int R = rows ? rows : (N >= 8192 ? 4 : 1);
+    if ((rc = bqd_init()))
+        return rc;
+    Int8xStreams st{b1, b2, l1, l2, reinterpret_cast<const uint32_t*>(l3), b1_blk, b2_blk,
+                    (int)(stream_bytes[1] / 4), (int)(stream_bytes[2] / 4), (int)(stream_bytes[3] / 4),
+                    (int)(stream_bytes[4] / 4)};
+    const dim3 grid((N + R - 1) / R), block(kThreads);
+    hipStream_t sm = (hipStream_t)stream;
+#define BQD_I8X_CASE(RR)                                                                              \
+    if (R == RR) {                                                                                    \
+        hipLaunchKernelGGL(k_gemv_int8x<RR>, grid, block, 0, sm, st, qx, sx, sw, y, acc, N, K);       \
+        return launched();                                                                            \
+    }
+    BQD_I8X_CASE(1) BQD_I8X_CASE(2) BQD_I8X_CASE(4) BQD_I8X_CASE(8)
+#undef BQD_I8X_CASE
+    return BQD_ERR_CONFIG;
 }
 
 int pack_int4_rows_host(const int8_t* q, int32_t N, int32_t K, uint32_t* out)

@@ -134,6 +134,19 @@ def uniform_int(name: str, shape, lo: int, hi: int, seed: int = 0, device="cpu",
     return v.to(dtype).view(shape)
 
 
+def int8_codes_by_band(name: str, shape, shares=(555, 404, 41), seed: int = 0, device="cpu") -> torch.Tensor:
+    """int8 weight codes whose magnitude falls in the bands 0..3, 4..15 and
+    16..127 with probabilities shares / 1000 (default: the shares the INT8-X
+    page reports for its model), uniform within a band, random sign."""
+    band = uniform_int(f"{name}/band", shape, 0, 999, seed, device)
+    m1 = uniform_int(f"{name}/m1", shape, 0, 3, seed, device)
+    m2 = uniform_int(f"{name}/m2", shape, 4, 15, seed, device)
+    m3 = uniform_int(f"{name}/m3", shape, 16, 127, seed, device)
+    neg = uniform_int(f"{name}/sign", shape, 0, 1, seed, device)
+    mag = torch.where(band < shares[0], m1, torch.where(band < shares[0] + shares[1], m2, m3))
+    return torch.where(neg == 1, -mag, mag).to(torch.int8)
+
+
 def random_words(name: str, shape, seed: int = 0, device="cpu") -> torch.Tensor:
     """Uniformly random 32-bit words (every nibble pattern), as int32."""
     shape = tuple(int(s) for s in (shape if isinstance(shape, (tuple, list)) else (shape,)))

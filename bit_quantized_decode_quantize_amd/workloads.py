@@ -19,6 +19,9 @@ its weights from HBM, as a decode step over a full model does.
   packed 6-bit (section 3 of "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录").
 * ``VerifyPool``: the M-token verify GEMM over [18944, 3584] or
   [3584, 18944] (section 5 of the same page).
+* ``Int8XPool``: INT8-X (3,5,8) encoded int8 weights ("定長無損 INT8 壓縮與
+  Triton 融合解碼") at a Qwen2-7B linear's shape, codes drawn with the page's
+  level shares, through the decode-fused W8A8 GEMV.
 """
 from __future__ import annotations
 
@@ -256,3 +259,39 @@ class VerifyPool:
 
     def weight_bytes(self) -> int:
         return self.N * self.K // 2
+
+
+class Int8XPool:
+    """INT8-X encoded int8 weights [N, K] (codes with the page's level shares
+    55.5 / 40.4 / 4.1 %), int8 x ~ uniform, per-tensor scales; one step = one
+    decode-fused W8A8 GEMV on the next of >= 16 pool copies."""
+
+    def __init__(self, N: int, K: int, seed: int = 0, device="cuda", rows: int = 0):
+        self.device = torch.device(device)
+        self.N, self.K, self.rows = N, K, rows
+        q = I.int8_codes_by_band(f"int8x/{N}x{K}/q", (N, K), seed=seed)
+        base = bqd.int8x_encode(q, 0.0042, device=self.device)
+        self.counts = base.counts
+        self.copies = _copies(base.nbytes(), 16)
+        self.pool = [base] + [bqd.Int8XWeights({k: v.clone() for k, v in base.arrays.items()}, base.sizes,
+                                               base.counts, N, K, base.sw) for _ in range(self.copies - 1)]
+        self.qx = I.uniform_int(f"int8x/{N}x{K}/x", K, -127, 127, seed, self.device, torch.int8)
+        self.sx = torch.tensor([0.0173], device=self.device)
+        self.y = torch.empty(N, dtype=torch.float32, device=self.device)
+        self.i = 0
+        self.launches_per_step = 1
+        torch.cuda.synchronize(self.device)
+
+    def step(self, stream=None) -> None:
+        w = self.pool[self.i % self.copies]
+        self.i += 1
+        bqd.gemv_int8x(w, self.qx, self.sx, y=self.y, rows=self.rows, stream=stream)
+
+    def bytes_per_step(self) -> int:
+        """Encoded payload (bitmaps and streams, unpadded) + block sums + x + y."""
+        w = self.pool[0]
+        blocks = self.N * self.K // bqd.BQD_INT8X_BLOCK
+        return (w.payload_bits() + 7) // 8 + 8 * (blocks + 1) + self.K + 4 * self.N
+
+    def bits_per_weight(self) -> float:
+        return self.pool[0].payload_bits() / (self.N * self.K)

@@ -257,6 +257,45 @@ int gemv_q6k_f16(const uint8_t* ql, const uint8_t* qh, const int8_t* sc, const u
                  const uint16_t* x16, float* y, int32_t N, int32_t K, int32_t r,
                  int32_t lanes_per_row, void* stream);
 
+/* INT8-X (3,5,8): lossless INT8 weights ("定長無損 INT8 壓縮與 Triton 融合解碼",
+ * sections 2.1-2.5) over the row-major flattened tensor of n weights:
+ *   level 1 |v| <= 3: 3-bit two's complement code in the L1 stream;
+ *   level 2 |v| <= 15: 5-bit code in the L2 stream; level 3: the byte in L3;
+ *   B1: a bit per weight, 1 = not level 1; B2: a bit per non-level-1 weight
+ *   in order, 1 = level 3; b1_blk[b] / b2_blk[b]: set bits of B1 / B2 before
+ *   block b of BQD_INT8X_BLOCK weights (one extra entry holds the totals).
+ * Bit streams are LSB-first (bit p = bit p % 32 of word p / 32). */
+#define BQD_INT8X_BLOCK 512
+
+/* Host: weights of each level, counts[3] = {n1, n2, n3}. */
+int int8x_counts_host(const int8_t* q, int64_t n, int64_t* counts);
+
+/* Host: byte sizes of the seven arrays {b1, b2, l1, l2, l3, b1_blk, b2_blk}
+ * for n weights with the given level counts, the bit streams padded by
+ * three words for the decoder's read windows. */
+int int8x_stream_bytes_host(int64_t n, const int64_t* counts, int64_t* bytes);
+
+/* Host: encode q (host int8, n weights) into host arrays of the sizes
+ * above (zeroed here first).  Offline, once per tensor. */
+int int8x_encode_host(const int8_t* q, int64_t n, uint32_t* b1, uint32_t* b2, uint32_t* l1,
+                      uint32_t* l2, uint8_t* l3, int32_t* b1_blk, int32_t* b2_blk);
+
+/* W8A8 GEMV over INT8-X weights [N, K] (K % BQD_INT8X_BLOCK == 0), decoded
+ * in registers (the fused decode of section 2.4):
+ *   acc[j] = sum_i q[j,i] * qx[i] (exact int32);  y[j] = (sw * sx[0]) * acc[j]
+ * with one per-tensor weight scale sw (section 2.5: INT8 per-tensor).  The
+ * seven arrays (device, 4-byte aligned) hold what int8x_encode_host wrote;
+ * stream_bytes (host, [7]) their sizes from int8x_stream_bytes_host (reads
+ * are clamped to them; the block sums must hold N*K/BQD_INT8X_BLOCK + 1
+ * entries).  qx (device) int8 [K], 8-byte aligned; sx (device)
+ * float [1]; y (device) float [N]; acc (device) int32 [N] or NULL.  rows =
+ * rows per workgroup, 1, 2, 4 or 8, or 0 (4 from N = 8192 on, else 1).  N*K < 2^31 and each stream below
+ * 2^26 words (BQD_ERR_BOUND otherwise). */
+int gemv_int8x(const uint32_t* b1, const uint32_t* b2, const uint32_t* l1, const uint32_t* l2,
+               const uint8_t* l3, const int32_t* b1_blk, const int32_t* b2_blk,
+               const int64_t* stream_bytes, const int8_t* qx, const float* sx, float sw, float* y,
+               int32_t* acc, int32_t N, int32_t K, int32_t rows, void* stream);
+
 /* W4A16 comparison GEMV: the same packed per-row INT4 weights against an
  * fp16 activation, unpacked to fp16 and multiplied in floating point (the
  * route "Jetson Orin AGX INT4 ..." section "为什么 INT4 float 解包不快"

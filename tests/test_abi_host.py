@@ -264,3 +264,73 @@ def test_q6k_entry_points_validate_before_launch():
     assert L.gemv_q6k_f16(P, P, P, P, P + 8, P, 4, 256, 0, 0, None) == ALIGN
     assert L.gemv_q6k_f16(P, P, P, P, P, P, 4, 256, 3, 0, None) == CONFIG
     assert L.gemv_q6k_f16(P, P, P, P, P, P, 0, 256, 0, 0, None) == OK
+
+
+def _lib_int8x_encode(q):
+    """The library's host encoder into numpy arrays of its stated sizes."""
+    L = _lib()
+    q = np.ascontiguousarray(q, np.int8)
+    n = q.size
+    counts = (C.c_int64 * 3)()
+    assert L.int8x_counts_host(q.ctypes.data, n, counts) == OK
+    sizes = (C.c_int64 * 7)()
+    assert L.int8x_stream_bytes_host(n, counts, sizes) == OK
+    names = ("b1", "b2", "l1", "l2", "l3", "b1_blk", "b2_blk")
+    arr = {k: np.full(sz // (1 if k == "l3" else 4), 0x5A, np.uint8 if k == "l3" else np.uint32)
+           for k, sz in zip(names, sizes)}
+    assert L.int8x_encode_host(q.ctypes.data, n, *[arr[k].ctypes.data for k in names]) == OK
+    return arr, tuple(counts)
+
+
+@pytest.mark.parametrize("shape,dist", [((1, 512), "laplace"), ((7, 1536), "bytes"), ((3, 3584), "laplace"),
+                                        ((2, 512), "l3"), ((1, 1024), "l1")])
+def test_int8x_host_encoder_matches_the_oracle(shape, dist):
+    """The library's encoder (its own code) writes the oracle's streams bit
+    for bit; the padding words are zero."""
+    rng = np.random.default_rng(31)
+    if dist == "laplace":
+        q = np.clip(np.round(rng.laplace(0, 4.3, shape)), -127, 127).astype(np.int8)
+    elif dist == "bytes":
+        q = rng.integers(-128, 128, shape, dtype=np.int8)
+    elif dist == "l3":
+        q = rng.choice(np.int8([-128, -16, 16, 127]), shape)
+    else:
+        q = rng.integers(-3, 4, shape, dtype=np.int8)
+    arr, counts = _lib_int8x_encode(q)
+    e = O.int8x_encode(q)
+    assert counts == (e["n1"], e["n2"], e["n3"])
+    n1, n2, n3 = counts
+    used = {"b1": (q.size + 31) // 32, "b2": (n2 + n3 + 31) // 32, "l1": (3 * n1 + 31) // 32,
+            "l2": (5 * n2 + 31) // 32, "l3": n3, "b1_blk": len(e["b1_blk"]), "b2_blk": len(e["b2_blk"])}
+    for k, m in used.items():
+        assert np.array_equal(arr[k][:m], e[k][:m]), k
+        assert len(arr[k]) >= m
+        if k not in ("b1_blk", "b2_blk"):
+            assert not arr[k][m:].any(), k  # padding zeroed
+
+
+def test_int8x_entry_points_validate():
+    L = _lib()
+    counts = (C.c_int64 * 3)(5, 3, 2)
+    sizes = (C.c_int64 * 7)()
+    assert L.int8x_stream_bytes_host(10, counts, sizes) == OK
+    assert list(sizes) == [16, 16, 16, 16, 16, 8, 8]
+    assert L.int8x_stream_bytes_host(11, counts, sizes) == SHAPE
+    assert L.int8x_counts_host(None, 4, counts) == NULL
+    assert L.int8x_counts_host(P, 0, counts) == SHAPE
+    sz = (C.c_int64 * 7)(64, 16, 16, 16, 16, 8, 8)
+    huge = (C.c_int64 * 7)(64, 16, (1 << 28) + 16, 16, 16, 8, 8)
+    # gemv_int8x(b1, b2, l1, l2, l3, b1_blk, b2_blk, sizes, qx, sx, sw, y, acc, N, K, rows, stream)
+    args = [P] * 7
+    assert L.gemv_int8x(*args, sz, P, P, 1.0, P, None, 1, 500, 0, None) == SHAPE
+    assert L.gemv_int8x(*args, sz, P, P, 1.0, P, None, 1, 66048, 0, None) == BOUND
+    assert L.gemv_int8x(*args, None, P, P, 1.0, P, None, 1, 512, 0, None) == NULL
+    assert L.gemv_int8x(*args, sz, P, None, 1.0, P, None, 1, 512, 0, None) == NULL
+    assert L.gemv_int8x(*args, sz, P4, P, 1.0, P, None, 1, 512, 0, None) == ALIGN
+    assert L.gemv_int8x(*args, sz, P, P, 1.0, P, None, 1, 512, 3, None) == CONFIG
+    small = (C.c_int64 * 7)(4, 16, 16, 16, 16, 8, 8)  # b1 shorter than N*K bits
+    assert L.gemv_int8x(*args, small, P, P, 1.0, P, None, 1, 512, 0, None) == SHAPE
+    short_blk = (C.c_int64 * 7)(64, 16, 16, 16, 16, 4, 8)  # block sums need N*K/512 + 1 entries
+    assert L.gemv_int8x(*args, short_blk, P, P, 1.0, P, None, 1, 512, 0, None) == SHAPE
+    assert L.gemv_int8x(*args, huge, P, P, 1.0, P, None, 1, 512, 0, None) == BOUND
+    assert L.gemv_int8x(*args, sz, P, P, 1.0, P, None, 0, 512, 0, None) == OK

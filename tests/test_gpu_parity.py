@@ -609,3 +609,33 @@ def test_gemv_q6k_of_quantised_weights_tracks_the_int8_expansion():
     ref = Wd @ npy(x16).astype(np.float64)
     mag = np.abs(Wd) @ np.abs(npy(x16).astype(np.float64))
     assert rel_err(npy(y), ref, mag).max() <= TOL
+
+
+# ------------------------------------------------------- INT8-X (3,5,8) --
+def _int8x_codes(N, K, dist, tag):
+    if dist == "page":
+        return I.int8_codes_by_band(f"gpu/i8x/{tag}", (N, K))
+    if dist == "bytes":
+        return I.uniform_int(f"gpu/i8x/{tag}", (N, K), -128, 127, dtype=torch.int8)
+    if dist == "l1":
+        return I.uniform_int(f"gpu/i8x/{tag}", (N, K), -3, 3, dtype=torch.int8)
+    return I.int8_codes_by_band(f"gpu/i8x/{tag}", (N, K), shares=(0, 0, 1000))
+
+
+@pytest.mark.parametrize("dist", ["page", "bytes", "l1", "l3"])
+@pytest.mark.parametrize("N,K", [(1, 512), (5, 1536), (37, 3584), (9, 18944)])
+def test_gemv_int8x_matches_oracle(N, K, dist):
+    """In-register INT8-X decode + W8A8 GEMV against the oracle (its own
+    encoding and decoder): acc bit-exact, y within tolerance; every rows
+    setting, rows past N included."""
+    q = _int8x_codes(N, K, dist, f"{N}/{K}/{dist}")
+    qx = I.uniform_int(f"gpu/i8x/{N}/{K}/x", K, -127, 127, device=DEV, dtype=torch.int8)
+    sx = torch.tensor([0.0173], device=DEV)
+    w = bqd.int8x_encode(q, 0.0042, device=DEV)
+    acc_r, y_r = O.gemv_int8x(O.int8x_encode(q.numpy()), npy(qx), 0.0173, 0.0042)
+    for rows in (0, 1, 2, 8):
+        y, acc = bqd.gemv_int8x(w, qx, sx, acc=True, rows=rows)
+        sync()
+        assert np.array_equal(npy(acc), acc_r), rows
+        mag = np.abs(y_r)
+        assert np.all(np.abs(npy(y).astype(np.float64) - y_r) <= TOL * np.where(mag > 0, mag, 1.0)), rows

@@ -211,3 +211,24 @@ def test_gemma_packed_6bit_lm_head():
     mag = (np.abs(e) * (np.abs(q.astype(np.float64)) * ax).reshape(len(rows), K // 16, 16).sum(2)).sum(1)
     err = np.abs(npy(w.head_y)[rows].astype(np.float64) - yr) / mag
     assert err.max() <= TOL, err.max()
+
+
+def test_int8x_pool_down_shape_matches_oracle():
+    """INT8-X weights [3584, 18944] with the page's level shares, graph
+    replay over the pool as bench.py times it: acc bit-exact on sampled rows
+    against the oracle's own encoding and decoder."""
+    w = WL.Int8XPool(3584, 18944, device=DEV)
+    _graph_replay(w.step, w.copies)
+    y = npy(w.y)
+    q = I.int8_codes_by_band("int8x/3584x18944/q", (3584, 18944)).numpy()
+    e = O.int8x_encode(q)
+    rows = _rows(3584, "int8x")
+    qx = npy(w.qx)
+    for j in rows:
+        row = O.int8x_decode(e, int(j) * 18944, 18944)
+        acc = int(row.astype(np.int64) @ qx.astype(np.int64))
+        ref = float(np.float32(0.0042)) * float(np.float32(0.0173)) * acc
+        assert abs(float(y[j]) - ref) <= TOL * max(abs(ref), 1e-30), j
+    acc_all = bqd.gemv_int8x(w.pool[0], w.qx, w.sx, acc=True)[1]
+    torch.cuda.synchronize()
+    assert np.array_equal(npy(acc_all)[rows], (q[rows].astype(np.int64) @ qx.astype(np.int64)).astype(np.int32))
