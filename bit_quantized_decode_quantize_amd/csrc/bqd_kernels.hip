@@ -304,10 +304,42 @@ __device__ __forceinline__ void stage_q8(u32x2* xs, const int8_t* qx, int G8)
 
 // Quantise x (fp32/fp16, [K]) in the workgroup and stage the codes into LDS.
 // Returns s^x.  Workgroup 0 optionally writes the codes and scale out.
+// Up to K = 8192 each thread keeps its (at most 4) 8-value groups in
+// registers: every load is issued before the first use (one memory round
+// trip), and the codes come from the registers.  Longer activations take
+// two passes over x (the second from cache).
 template <int XIN>
 __device__ float stage_quant(u32x2* xs, const void* x, int G8, float* red, int8_t* qx_out,
                              float* sx_out)
 {
+    const bool out = (qx_out != nullptr) && blockIdx.x == 0;
+    if (G8 <= 4 * kThreads) {
+        float v[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            load8<XIN>(x, min((int)threadIdx.x + k * kThreads, G8 - 1), v[k]);
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                m = fmaxf(m, fabsf(v[k][e]));  // clamped groups repeat a real one
+        const ActScale a = act_scale(block_max(m, red));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int g = threadIdx.x + k * kThreads;
+            if (g < G8) {
+                uint32_t lo, hi;
+                quant8_fast(v[k], a, lo, hi);
+                xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+                if (out)
+                    reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+            }
+        }
+        if (sx_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+            *sx_out = a.s;
+        return a.s;
+    }
     float amax = 0.0f;
     for (int g = threadIdx.x; g < G8; g += kThreads) {
         float v[8];
@@ -319,7 +351,6 @@ __device__ float stage_quant(u32x2* xs, const void* x, int G8, float* red, int8_
     amax = block_max(amax, red);
     const ActScale a = act_scale(amax);
     const float s = a.s;
-    const bool out = (qx_out != nullptr) && blockIdx.x == 0;
     for (int g = threadIdx.x; g < G8; g += kThreads) {
         float v[8];
         load8<XIN>(x, g, v);
