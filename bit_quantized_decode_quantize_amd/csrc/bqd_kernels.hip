@@ -307,7 +307,7 @@ __device__ __forceinline__ void stage_q8(u32x2* xs, const int8_t* qx, int G8)
 // Up to K = 8192 each thread keeps its (at most 4) 8-value groups in
 // registers: every load is issued before the first use (one memory round
 // trip), and the codes come from the registers.  Longer activations take
-// two passes over x (the second from cache).
+// two passes over x (the second from cache), 4 groups per thread at a time.
 template <int XIN>
 __device__ float stage_quant(u32x2* xs, const void* x, int G8, float* red, int8_t* qx_out,
                              float* sx_out)
@@ -340,25 +340,38 @@ __device__ float stage_quant(u32x2* xs, const void* x, int G8, float* red, int8_
             *sx_out = a.s;
         return a.s;
     }
+    // batches of 4 groups per thread, the batch's loads issued together
     float amax = 0.0f;
-    for (int g = threadIdx.x; g < G8; g += kThreads) {
-        float v[8];
-        load8<XIN>(x, g, v);
+    for (int g0 = threadIdx.x; g0 < G8; g0 += 4 * kThreads) {
+        float v[4][8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            amax = fmaxf(amax, fabsf(v[k]));
+        for (int k = 0; k < 4; ++k)
+            load8<XIN>(x, min(g0 + k * kThreads, G8 - 1), v[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                amax = fmaxf(amax, fabsf(v[k][e]));  // clamped groups repeat a real one
     }
     amax = block_max(amax, red);
     const ActScale a = act_scale(amax);
     const float s = a.s;
-    for (int g = threadIdx.x; g < G8; g += kThreads) {
-        float v[8];
-        load8<XIN>(x, g, v);
-        uint32_t lo, hi;
-        quant8(v, a, lo, hi);
-        xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
-        if (out)
-            reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+    for (int g0 = threadIdx.x; g0 < G8; g0 += 4 * kThreads) {
+        float v[4][8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            load8<XIN>(x, min(g0 + k * kThreads, G8 - 1), v[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int g = g0 + k * kThreads;
+            if (g < G8) {
+                uint32_t lo, hi;
+                quant8_fast(v[k], a, lo, hi);
+                xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+                if (out)
+                    reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+            }
+        }
     }
     if (sx_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
         *sx_out = s;
