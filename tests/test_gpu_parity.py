@@ -232,6 +232,31 @@ def test_linear_w4a8_single_gemv_config(dtype):
     assert O.rel_err_rowwise(npy(y), yr, sr, sxr, accr, npy(b)).max() <= TOL
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+@pytest.mark.parametrize("K", [32, 1536, 8192, 8224, 24576, 65536])
+def test_linear_w4a8_prologue_paths(K, dtype):
+    """The fused prologue's two routes: up to K = 8192 the activation is held
+    in registers (8192 fills them exactly), above it the two passes run in
+    batches of 4 groups per thread (8224: a ragged last batch; 65536: the
+    largest K).  Codes, s^x and accumulators bit-exact, per-row and group-32;
+    1 % of x scaled by 20 so that the max sits anywhere."""
+    N = 40
+    x = I.with_outliers(I.normal(f"gpu/prol/{K}/x", K, 1.0, device=DEV), f"gpu/prol/{K}/o").to(dtype)
+    w, _, sw, b, _ = _rand_gemv(N, K, f"prol/{K}")
+    y, qx, sx, acc = bqd.linear_w4a8(w, sw, b, x, want_q=True, want_acc=True)
+    sync()
+    qxr, sxr = O.quantize_act(npy(x))
+    assert np.array_equal(npy(qx), qxr) and npy(sx)[0] == sxr
+    accr, yr = O.gemv_w4a8(u32(w), npy(sw), npy(b), qxr, float(sxr))
+    assert np.array_equal(npy(acc), accr)
+    assert O.rel_err_rowwise(npy(y), yr, npy(sw), sxr, accr, npy(b)).max() <= TOL
+    s16 = I.normal(f"gpu/prol/{K}/s16", (N, K // 32), 0.01, device=DEV, dtype=torch.float16)
+    yg, qg, sg, accg = bqd.linear_w4a8_group32(w, s16, None, x, want_q=True, want_acc=True)
+    sync()
+    assert np.array_equal(npy(qg), qxr) and npy(sg)[0] == sxr
+    _check_group32(yg, accg, w, s16, None, qg, sg)
+
+
 def test_linear_equals_quantize_then_gemv():
     """The fused prologue quantises exactly like quantize_act: same y bits."""
     w, _, sw, b, _ = _rand_gemv(1234, 18944, "fuse")
