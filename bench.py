@@ -527,8 +527,10 @@ def run_verify(a, dev):
 def run_chain(a, dev):
     """The 28-layer stream wired into a decoder's data flow with the
     activation producers (residual add + RMSNorm, SwiGLU) fused with the
-    quantisation, one HIP graph per token; the same chain with fp32
-    producers and consumer-side quantisation is timed beside it."""
+    quantisation, one HIP graph per token.  Timed three ways that give the
+    same logits: producers writing int8 codes (the value), RMSNorm +
+    quantisation in the consuming linear's prologue, and fp32 producers with
+    linears that quantise in their prologue."""
     import torch
     from bit_quantized_decode_quantize_amd import bqd
     from bit_quantized_decode_quantize_amd import decode_stream as DS
@@ -536,22 +538,27 @@ def run_chain(a, dev):
     layers = a.layers or 28
     s = DS.QwenW4A8Stream(layers=layers, device=dev, persistent=False)
     c = DS.DecodeChain(s)
-    log(f"chain built: {c.launches_per_step()} launches per token")
-    c.step(True)
-    torch.cuda.synchronize()
-    logits_fused = c.output().clone()
-    c.step(False)
-    torch.cuda.synchronize()
-    if not torch.equal(logits_fused, c.output()):
-        raise RuntimeError("fused and unfused chains disagree")
+    modes = ("producers", "prologue", "fp32")
+    logits = {}
+    for m in modes:
+        c.step(m)
+        torch.cuda.synchronize()
+        logits[m] = c.output().clone()
+    if not all(torch.equal(logits[m], logits["producers"]) for m in modes):
+        raise RuntimeError("the chain's modes disagree")
     graph = 0 if a.eager else 1
-    ms, n = time_steps(lambda: c.step(True), a.steps, a.warmup, graph)
-    ms_u, _ = time_steps(lambda: c.step(False), a.steps, a.warmup, graph)
-    step_bytes = c.bytes_per_step(True)
+    timing = {}
+    for m in modes:
+        ms_m, n_m = time_steps(lambda: c.step(m), a.steps, a.warmup, graph)
+        timing[m] = {"ms_per_step": round(ms_m, 5), "launches_per_step": c.launches_per_step(m),
+                     "bytes_per_step": c.bytes_per_step(m), "steps": n_m}
+        log(f"chain {m}: {timing[m]}")
+    ms, n = timing["producers"]["ms_per_step"], timing["producers"]["steps"]
+    step_bytes = c.bytes_per_step("producers")
     gbs = step_bytes / (ms * 1e-3) / 1e9
 
-    # Kernel durations in an eager pass: events around the producers and
-    # around the int8 GEMVs of gate/up and the lm_head (most of the bytes).
+    # Kernel durations in an eager pass of the producers mode: events around
+    # the producers and around the int8 GEMVs of gate/up and the lm_head.
     st = torch.cuda.current_stream()
     spans = {"add_rmsnorm_quant": [], "swiglu_quant": [], "gemv": []}
     gemv_bytes = []
@@ -576,7 +583,7 @@ def run_chain(a, dev):
         bqd.swiglu_quant = timed("swiglu_quant", "swiglu_quant")
         bqd.gemv_w4a8 = timed("gemv_w4a8", "gemv")
         for _ in range(max(1, a.steps // 5)):
-            c.step(True)
+            c.step("producers")
     finally:
         bqd.add_rmsnorm_quant, bqd.swiglu_quant, bqd.gemv_w4a8 = (
             real["add_rmsnorm_quant"], real["swiglu_quant"], real["gemv_w4a8"])
@@ -586,15 +593,15 @@ def run_chain(a, dev):
     out = base_line(a, gbs, ms, n, {
         "workload": f"qwen2-7b-shaped {layers}-layer decode chain: residual add + RMSNorm + quant -> QKV, "
                     "O (synthetic attention output), residual add + RMSNorm + quant -> gate/up, "
-                    "SwiGLU + quant -> down, final RMSNorm + quant -> int4 lm_head",
+                    "SwiGLU + quant -> down, final RMSNorm + quant -> int4 lm_head (producers write int8 codes)",
         "launch": "per-kernel, one HIP graph per token" if graph else "per-kernel",
-        "layers": layers, "launches_per_step": c.launches_per_step(), "bytes_per_step": step_bytes})
+        "layers": layers, "launches_per_step": c.launches_per_step("producers"), "bytes_per_step": step_bytes})
     out["tok_per_s"] = round(1e3 / ms, 2)
-    out["unfused_ms_per_step"] = round(ms_u, 5)
-    out["unfused_bytes_per_step"] = c.bytes_per_step(False)
+    out["modes"] = timing
     out["producer_us"] = {k: round(avg[k], 2) for k in ("add_rmsnorm_quant", "swiglu_quant")}
     out["roofline"] = roofline(avg_bytes / (avg["gemv"] * 1e-6) / 1e9,
-                               "k_gemv_w4a8 on int8 codes (gate/up and lm_head)", avg["gemv"], avg_bytes)
+                               "k_gemv_w4a8 on int8 codes (gate/up and lm_head, producers mode)", avg["gemv"],
+                               avg_bytes)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_chain(c, a.cpu_seconds)
     return out
@@ -615,7 +622,7 @@ def cpu_baseline_chain(c, seconds):
     h0 = c.h_in.cpu().numpy()
     g0, g1 = c.gamma[0].cpu().numpy(), c.gamma[1].cpu().numpy()
     xo = lin["o"]["x"].cpu().numpy()
-    sample = c.bytes_per_step(True) // (len(c.by_layer) + 1)
+    sample = c.bytes_per_step("producers") // (len(c.by_layer) + 1)
 
     def once():
         q, s, h1, _ = O.add_rmsnorm_quant(h0, None, g0, DS.RMS_EPS)

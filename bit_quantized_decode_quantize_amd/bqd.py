@@ -34,7 +34,7 @@ ENTRY_POINTS = (
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
     "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
-    "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant",
+    "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant", "linear_rmsnorm_w4a8",
     "quantize_weights_q6k", "gemv_q6k_f16", "int8x_counts_host", "int8x_stream_bytes_host",
     "int8x_encode_host", "gemv_int8x",
 )
@@ -91,6 +91,7 @@ def lib() -> C.CDLL:
         "gemv_w4a16": (I, [P, P, P, P, P, I, I, I, I, P]),
         "add_rmsnorm_quant": (I, [P, P, P, C.c_float, P, P, P, P, I, I, P]),
         "swiglu_quant": (I, [P, P, P, P, I, I, P]),
+        "linear_rmsnorm_w4a8": (I, [P, P, P, P, P, P, C.c_float, P, P, P, P, P, I, I, I, I, P]),
         "quantize_weights_q6k": (I, [P, I, I, P, P, P, P, P]),
         "gemv_q6k_f16": (I, [P, P, P, P, P, P, I, I, I, I, P]),
         "int8x_counts_host": (I, [P, C.c_int64, P]),
@@ -251,6 +252,35 @@ def add_rmsnorm_quant(h, gamma, eps: float, delta=None, qx=None, sx=None, h_out=
     _call("add_rmsnorm_quant", h.data_ptr(), _ptr(delta), gamma.data_ptr(), float(eps), _ptr(h_out),
           _ptr(y_out), _ptr(qx), _ptr(sx), M, K, _stream(stream))
     return qx, sx
+
+
+def linear_rmsnorm_w4a8(wq, sw, bias, h, gamma, eps: float, delta=None, h_out=None, y=None,
+                        want_q=False, want_acc=False, r=0, lanes_per_row=0, stream=None):
+    """Residual add + RMSNorm + quantisation in the prologue of the W4A8
+    linear: h, delta (optional), gamma fp32 [K]; h_out receives h + delta
+    (must be another buffer).  Returns y, plus (qx, sx) if want_q, plus acc
+    if want_acc."""
+    N, K = _wshape(wq, None)
+    _dev(wq, "wq", _WORD, N * K // 8)
+    _dev(sw, "sw", _F32, N)
+    _opt(bias, "bias", _F32, N)
+    _dev(h, "h", _F32, K)
+    _opt(delta, "delta", _F32, K)
+    _dev(gamma, "gamma", _F32, K)
+    _opt(h_out, "h_out", _F32, K)
+    y = _empty((N,), torch.float32, wq) if y is None else _dev(y, "y", _F32, N)
+    qx = _empty((K,), torch.int8, wq) if want_q else None
+    sx = _empty((1,), torch.float32, wq) if want_q else None
+    acc = _empty((N,), torch.int32, wq) if want_acc else None
+    _call("linear_rmsnorm_w4a8", wq.data_ptr(), sw.data_ptr(), _ptr(bias), h.data_ptr(), _ptr(delta),
+          gamma.data_ptr(), float(eps), _ptr(h_out), y.data_ptr(), _ptr(qx), _ptr(sx), _ptr(acc), N, K, r,
+          lanes_per_row, _stream(stream))
+    out = [y]
+    if want_q:
+        out += [qx, sx]
+    if want_acc:
+        out.append(acc)
+    return out[0] if len(out) == 1 else tuple(out)
 
 
 def swiglu_quant(gu, qx=None, sx=None, h_out=None, quantize: bool = True, stream=None):

@@ -167,7 +167,16 @@ __device__ __forceinline__ float block_max(float v, float* red)
 // ------------------------------------------------------------------------
 // Activation input: 8 consecutive values of x as fp32 (fp16 widens exactly)
 // ------------------------------------------------------------------------
-enum XIn { X_Q8 = 0, X_F32 = 1, X_F16 = 2 };
+enum XIn { X_Q8 = 0, X_F32 = 1, X_F16 = 2, X_RMS = 3 };
+
+// Operands of the RMSNorm activation (X_RMS): x = RMSNorm(h + delta) * gamma.
+struct RmsIn {
+    const float* h;      // residual stream [K]
+    const float* delta;  // added to h first, or NULL
+    const float* gamma;  // [K]
+    float* h_out;        // h + delta, written by workgroup 0, or NULL
+    float eps;
+};
 
 template <int XIN>
 __device__ __forceinline__ void load8(const void* x, int g, float v[8])
@@ -766,13 +775,95 @@ __device__ __forceinline__ void load_scales(uint16_t (&buf)[U][R], const uint16_
     }
 }
 
+// Residual add + RMSNorm + quantisation in the GEMV prologue (K <= 8192):
+// each thread holds its (at most 4) groups of h + delta and of gamma in
+// registers, all loaded before the first use; the binary64 sum of squares
+// over the workgroup gives r = fp32(1 / sqrt(ss / K + eps)), then y =
+// (a * r) * gamma and the codes -- the same fp32 operations as
+// add_rmsnorm_quant, so the same codes.  Workgroup 0 writes h + delta (and
+// optionally the codes and scale).
+__device__ float stage_rms_quant(u32x2* xs, const RmsIn& p, int G8, float* red, int8_t* qx_out, float* sx_out)
+{
+    __shared__ double dred[kThreads / kWave];
+    float a[4][8], gm[4][8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int g = min((int)threadIdx.x + k * kThreads, G8 - 1);
+        load8<X_F32>(p.h, g, a[k]);
+        load8<X_F32>(p.gamma, g, gm[k]);
+    }
+    if (p.delta) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float d[8];
+            load8<X_F32>(p.delta, min((int)threadIdx.x + k * kThreads, G8 - 1), d);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                a[k][e] = a[k][e] + d[e];
+        }
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if ((int)threadIdx.x + k * kThreads < G8)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                ss += (double)a[k][e] * (double)a[k][e];
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1)
+        ss += __shfl_xor(ss, m);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        dred[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w)
+        t += dred[w];
+    const double v = t / (double)(8 * G8) + (double)p.eps;
+    const float r = v > 0.0 ? (float)(1.0 / sqrt(v)) : 0.0f;
+    const bool w0 = blockIdx.x == 0;
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int g = threadIdx.x + k * kThreads;
+        if (w0 && p.h_out && g < G8) {
+            f32x4* o = reinterpret_cast<f32x4*>(p.h_out) + 2 * g;
+            o[0] = f32x4{a[k][0], a[k][1], a[k][2], a[k][3]};
+            o[1] = f32x4{a[k][4], a[k][5], a[k][6], a[k][7]};
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[k][e] = (a[k][e] * r) * gm[k][e];
+            m = fmaxf(m, fabsf(a[k][e]));  // clamped groups repeat a real one
+        }
+    }
+    const ActScale as = act_scale(block_max(m, red));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int g = threadIdx.x + k * kThreads;
+        if (g < G8) {
+            uint32_t lo, hi;
+            quant8_fast(a[k], as, lo, hi);
+            xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+            if (w0 && qx_out)
+                reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+        }
+    }
+    if (w0 && sx_out && threadIdx.x == 0)
+        *sx_out = as.s;
+    return as.s;
+}
+
 template <int XIN>
 __device__ __forceinline__ float stage_activation(u32x4* xs, const void* xin, const float* sx_in, int C,
-                                                  float* red, int8_t* qx_out, float* sx_out)
+                                                  float* red, int8_t* qx_out, float* sx_out,
+                                                  const RmsIn& rms = RmsIn{})
 {
     if constexpr (XIN == X_Q8) {
         stage_q8(reinterpret_cast<u32x2*>(xs), reinterpret_cast<const int8_t*>(xin), 4 * C);
         return *sx_in;
+    } else if constexpr (XIN == X_RMS) {
+        return stage_rms_quant(reinterpret_cast<u32x2*>(xs), rms, 4 * C, red, qx_out, sx_out);
     } else {
         return stage_quant<XIN>(reinterpret_cast<u32x2*>(xs), xin, 4 * C, red, qx_out, sx_out);
     }
@@ -783,7 +874,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
     const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
     const void* __restrict__ xin, const float* __restrict__ sx_in, float* __restrict__ y,
     int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out, float* __restrict__ sx_out, int N,
-    int C)
+    int C, RmsIn rms)
 {
     extern __shared__ u32x4 xs[];  // 2*C chunks' activation = K bytes
     __shared__ float red[4];
@@ -798,7 +889,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
     int tile = blockIdx.x;
     u32x4 cur[U][R];
     load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
-    const float sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out);
+    const float sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out, rms);
     __syncthreads();
 
     for (; tile < tiles; tile += gridDim.x) {
@@ -2191,7 +2282,7 @@ inline unsigned grid_for(long long tiles)
 template <int XIN>
 int launch_gemv_rowwise(const uint32_t* wq, const float* sw, const float* bias, const void* xin,
                         const float* sx, float* y, int32_t* acc, int8_t* qx_out, float* sx_out,
-                        int N, int K, const GemvCfg& c, hipStream_t st)
+                        int N, int K, const GemvCfg& c, hipStream_t st, const RmsIn& rms = RmsIn{})
 {
     const int C = K / 32;
     const dim3 grid(c.grid), block(kThreads);
@@ -2200,7 +2291,7 @@ int launch_gemv_rowwise(const uint32_t* wq, const float* sw, const float* bias, 
 #define BQD_GEMV_CASE(RR, LL, UU)                                                                \
     if (c.r == RR && c.L == LL && c.U == UU) {                                                   \
         hipLaunchKernelGGL((k_gemv_w4a8<RR, LL, UU, XIN>), grid, block, lds, st, w, sw, bias, xin, \
-                           sx, y, acc, qx_out, sx_out, N, C);                                    \
+                           sx, y, acc, qx_out, sx_out, N, C, rms);                               \
         return launched();                                                                       \
     }
     BQD_FOR_CFGS(BQD_GEMV_CASE)
@@ -2675,6 +2766,45 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
                                           (hipStream_t)stream);
     return launch_gemv_rowwise<X_F16>(wq, sw, bias, x, nullptr, y, acc, qx_out, sx_out, N, K, c,
                                       (hipStream_t)stream);
+}
+
+static bool overlaps(const float* a, const float* b, int K)
+{
+    return a && b && a < b + K && b < a + K;
+}
+
+int linear_rmsnorm_w4a8(const uint32_t* wq, const float* sw, const float* bias, const float* h,
+                        const float* delta, const float* gamma, float eps, float* h_out, float* y,
+                        int8_t* qx_out, float* sx_out, int32_t* acc, int32_t N, int32_t K, int32_t r,
+                        int32_t lanes_per_row, void* stream)
+{
+    if (N < 0)
+        return BQD_ERR_SHAPE;
+    int rc = check_k(K);
+    if (rc)
+        return rc;
+    if (K > 4 * 8 * kThreads)
+        return BQD_ERR_BOUND;
+    if (!(eps >= 0.0f) || !(eps <= FLT_MAX))
+        return BQD_ERR_SHAPE;
+    if (overlaps(h_out, h, K) || overlaps(h_out, delta, K))
+        return BQD_ERR_SHAPE;  // other workgroups still read h and delta while workgroup 0 writes
+    if (N == 0)
+        return BQD_OK;
+    if (!wq || !sw || !h || !gamma || !y)
+        return BQD_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(h, 16) || !aligned(delta, 16) || !aligned(gamma, 16) ||
+        !aligned(h_out, 16) || !aligned(qx_out, 16) || !aligned(sw, 4) || !aligned(sx_out, 4) ||
+        !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4))
+        return BQD_ERR_ALIGN;
+    if (!valid_config(r, lanes_per_row))
+        return BQD_ERR_CONFIG;
+    if ((rc = bqd_init()))
+        return rc;
+    const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 1);
+    const RmsIn rms{h, delta, gamma, h_out, eps};
+    return launch_gemv_rowwise<X_RMS>(wq, sw, bias, nullptr, nullptr, y, acc, qx_out, sx_out, N, K, c,
+                                      (hipStream_t)stream, rms);
 }
 
 int gemv_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias, const int8_t* qx,

@@ -173,12 +173,17 @@ class DecodeChain:
                     x = silu(gate) * up                     -> down
         final:      x = RMSNorm(h + y_down)                 -> lm_head
 
-    fused=True: each producer writes int8 codes + s^x and the linears are
-    int8 GEMVs (``add_rmsnorm_quant`` / ``swiglu_quant`` then ``gemv_w4a8``).
-    fused=False: the producers write fp32 and each linear quantises in its
-    own prologue (``linear_w4a8``).  Both take the same codes from the same
-    fp32 values, so their outputs are identical bit for bit.  The residual
-    stream starts from the same h_in every step."""
+    Three ways to run it, with the same codes from the same fp32 values and
+    hence outputs identical bit for bit:
+      "producers": each producer writes int8 codes + s^x and the linears are
+        int8 GEMVs (``add_rmsnorm_quant`` / ``swiglu_quant``, ``gemv_w4a8``);
+      "fp32": the producers write fp32 and each linear quantises in its own
+        prologue (``linear_w4a8``);
+      "prologue": the residual add + RMSNorm + quantisation run inside the
+        prologue of the linear that consumes them (``linear_rmsnorm_w4a8``),
+        SwiGLU as in "producers" (its elementwise work is too large to
+        repeat in every workgroup of the down projection).
+    The residual stream starts from the same h_in every step."""
 
     def __init__(self, stream: "QwenW4A8Stream", seed: int = 0):
         self.s = stream
@@ -190,6 +195,7 @@ class DecodeChain:
         g = 1.0 + I.normal("qwen/chain/gamma", (2 * L + 1, K), 0.1, seed, dev)
         self.gamma = [g[i].contiguous() for i in range(2 * L + 1)]
         self.h = torch.empty(1, K, device=dev)
+        self.h2 = torch.empty(1, K, device=dev)  # "prologue": h + delta alternates between the two
         self.q_h = torch.empty(1, K, dtype=torch.int8, device=dev)
         self.s_h = torch.empty(1, device=dev)
         self.q_i = torch.empty(1, I_, dtype=torch.int8, device=dev)
@@ -214,7 +220,12 @@ class DecodeChain:
         else:
             bqd.linear_w4a8(d["wq"], d["sw"], d["b"], self.y_h.view(-1), y=d["y"], stream=stream)
 
-    def step(self, fused: bool = True, stream=None) -> None:
+    def step(self, mode: str = "producers", stream=None) -> None:
+        if mode == "prologue":
+            return self._step_prologue(stream)
+        if mode not in ("producers", "fp32"):
+            raise ValueError(f"unknown chain mode {mode}")
+        fused = mode == "producers"
         delta = None
         for l, lin in enumerate(self.by_layer):
             self._norm(fused, self.h_in if l == 0 else self.h, delta, self.gamma[2 * l], stream)
@@ -235,14 +246,47 @@ class DecodeChain:
             self._norm(fused, self.h, delta, self.gamma[-1], stream)
             self._linear_h(fused, self.head, stream)
 
+    def _step_prologue(self, stream=None) -> None:
+        bufs = (self.h, self.h2)
+        src, delta, k = self.h_in, None, 0
+
+        def rms_linear(d, gamma):
+            nonlocal src, k
+            dst = bufs[k]
+            bqd.linear_rmsnorm_w4a8(d["wq"], d["sw"], d["b"], src.view(-1), gamma, RMS_EPS,
+                                    delta=None if delta is None else delta.view(-1), h_out=dst.view(-1),
+                                    y=d["y"], stream=stream)
+            src, k = dst, 1 - k
+
+        for l, lin in enumerate(self.by_layer):
+            rms_linear(lin["qkv"], self.gamma[2 * l])
+            o = lin["o"]
+            bqd.linear_w4a8(o["wq"], o["sw"], o["b"], o["x"], y=o["y"], stream=stream)
+            delta = o["y"]
+            rms_linear(lin["gate_up"], self.gamma[2 * l + 1])
+            dn = lin["down"]
+            bqd.swiglu_quant(lin["gate_up"]["y"].view(1, -1), h_out=self.y_i, qx=self.q_i, sx=self.s_i,
+                             stream=stream)
+            bqd.gemv_w4a8(dn["wq"], dn["sw"], dn["b"], self.q_i.view(-1), self.s_i, y=dn["y"], stream=stream)
+            delta = dn["y"]
+        if self.head is not None:
+            rms_linear(self.head, self.gamma[-1])
+
     def output(self) -> torch.Tensor:
         return (self.head or self.by_layer[-1]["down"])["y"]
 
-    def launches_per_step(self) -> int:
-        return 7 * len(self.by_layer) + (2 if self.head is not None else 0)
+    def launches_per_step(self, mode: str = "producers") -> int:
+        # per layer: QKV, O, gate/up and down, plus two RMSNorm producers
+        # (not in "prologue") and SwiGLU (two kernels with codes, one for fp32)
+        per_layer = {"producers": 8, "fp32": 7, "prologue": 6}[mode]
+        head = 1 if mode == "prologue" else 2
+        return per_layer * len(self.by_layer) + (head if self.head is not None else 0)
 
-    def bytes_per_step(self, fused: bool = True) -> int:
+    def bytes_per_step(self, mode: str = "producers") -> int:
         K, I_ = self.K, self.I
+        if mode == "prologue":
+            return self._bytes_prologue()
+        fused = mode == "producers"
         tot = 0
         for l, lin in enumerate(self.by_layer):
             tot += producer_bytes_rmsnorm(K, l > 0, fused) + producer_bytes_rmsnorm(K, True, fused)
@@ -257,4 +301,22 @@ class DecodeChain:
             d = self.head
             tot += producer_bytes_rmsnorm(K, True, fused)
             tot += gemv_bytes_q8(d["N"], d["K"], False) if fused else algorithmic_bytes_linear(d["N"], d["K"], False)
+        return tot
+
+    def _bytes_prologue(self) -> int:
+        """RMSNorm in the consumer's prologue: the linear reads h, delta and
+        gamma (12K, 8K without delta) and writes h + delta (4K) instead of
+        reading K bytes of codes; SwiGLU as with producers."""
+        K, I_ = self.K, self.I
+        tot = 0
+        for l, lin in enumerate(self.by_layer):
+            for name, with_delta in (("qkv", l > 0), ("gate_up", True)):
+                d = lin[name]
+                tot += gemv_bytes_q8(d["N"], d["K"], True) - (K + 4) + 4 * K * (3 if with_delta else 2) + 4 * K
+            o = lin["o"]
+            tot += algorithmic_bytes_linear(o["N"], o["K"], True)
+            tot += producer_bytes_swiglu(I_, True) + gemv_bytes_q8(lin["down"]["N"], lin["down"]["K"], True)
+        if self.head is not None:
+            d = self.head
+            tot += gemv_bytes_q8(d["N"], d["K"], False) - (K + 4) + 16 * K
         return tot

@@ -158,6 +158,22 @@ int add_rmsnorm_quant(const float* h, const float* delta, const float* gamma, fl
                       float* h_out, float* y_out, int8_t* qx, float* sx, int32_t M, int32_t K,
                       void* stream);
 
+/* The same residual add + RMSNorm + quantisation folded into the prologue
+ * of the W4A8 linear that consumes it (one launch instead of two): every
+ * workgroup computes h1 = h + delta, r and the codes of (h1 * r) * gamma
+ * itself -- the operations of add_rmsnorm_quant, so the same codes -- then
+ * runs the GEMV of gemv_w4a8 on them; workgroup 0 writes h1 to h_out.
+ *   y[j] = sw[j] * s^x * acc[j] + bias[j]
+ * h, delta (NULL allowed), gamma, h_out (NULL allowed): device float [K],
+ * 16-byte aligned; h_out must not overlap h or delta (BQD_ERR_SHAPE: other
+ * workgroups read them while workgroup 0 writes).  qx_out int8 [K], sx_out
+ * float [1], acc int32 [N]: optional outputs.  K % 32 == 0 and K <= 8192
+ * (BQD_ERR_BOUND); eps >= 0 finite.  r, lanes_per_row as in gemv_w4a8. */
+int linear_rmsnorm_w4a8(const uint32_t* wq, const float* sw, const float* bias, const float* h,
+                        const float* delta, const float* gamma, float eps, float* h_out, float* y,
+                        int8_t* qx_out, float* sx_out, int32_t* acc, int32_t N, int32_t K, int32_t r,
+                        int32_t lanes_per_row, void* stream);
+
 /* SwiGLU + per-token quantisation.  gu (device) float [M, 2I] holds each
  * token's fused gate/up output, gate g = gu[m, 0:I] then up u = gu[m, I:2I];
  *   h_i = (g_i / (1 + e^(-g_i))) * u_i   (fp32, correctly rounded division;

@@ -334,3 +334,19 @@ def test_int8x_entry_points_validate():
     assert L.gemv_int8x(*args, short_blk, P, P, 1.0, P, None, 1, 512, 0, None) == SHAPE
     assert L.gemv_int8x(*args, huge, P, P, 1.0, P, None, 1, 512, 0, None) == BOUND
     assert L.gemv_int8x(*args, sz, P, P, 1.0, P, None, 0, 512, 0, None) == OK
+
+
+def test_linear_rmsnorm_validates_before_launch():
+    L = _lib()
+    # linear_rmsnorm_w4a8(wq, sw, bias, h, delta, gamma, eps, h_out, y, qx, sx, acc, N, K, r, lanes, stream)
+    f = L.linear_rmsnorm_w4a8
+    assert f(P, P, None, P, None, P, 1e-6, None, P, None, None, None, 4, 48, 0, 0, None) == SHAPE
+    assert f(P, P, None, P, None, P, 1e-6, None, P, None, None, None, 4, 8224, 0, 0, None) == BOUND
+    assert f(P, P, None, P, None, P, -1.0, None, P, None, None, None, 4, 64, 0, 0, None) == SHAPE
+    assert f(P, P, None, P, None, P, 1e-6, P + 128, P, None, None, None, 4, 64, 0, 0, None) == SHAPE  # h_out overlaps h
+    assert f(P, P, None, P, P + 4096, P, 1e-6, P + 4096 + 64, P, None, None, None, 4, 64, 0, 0, None) == SHAPE
+    assert f(P, P, None, None, None, P, 1e-6, None, P, None, None, None, 4, 64, 0, 0, None) == NULL
+    assert f(P, P, None, P, None, None, 1e-6, None, P, None, None, None, 4, 64, 0, 0, None) == NULL
+    assert f(P, P, None, P + 8, None, P, 1e-6, None, P, None, None, None, 4, 64, 0, 0, None) == ALIGN
+    assert f(P, P, None, P, None, P, 1e-6, None, P, None, None, None, 4, 64, 3, 0, None) == CONFIG
+    assert f(P, P, None, P, None, P, 1e-6, None, P, None, None, None, 0, 64, 0, 0, None) == OK

@@ -217,3 +217,29 @@ def test_producers_in_a_graph_replay_match_eager():
         sync()
         for a, r in zip((qx, sx, ygu, qd, sd, h1), ref):
             assert torch.equal(a, r)
+
+
+@pytest.mark.parametrize("residual", [True, False])
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 1536), (4608, 3584), (300, 8192)])
+def test_linear_rmsnorm_w4a8_matches_producer_and_oracle(N, K, residual):
+    """RMSNorm + quantisation in the linear's prologue: the codes, s^x and
+    h + delta of the oracle's add_rmsnorm_quant bit for bit, the oracle's
+    accumulators, and the same y bits as add_rmsnorm_quant + gemv_w4a8."""
+    h, d, gamma = _rms_inputs(1, K, f"lin/{N}/{K}", residual)
+    h, d = h.view(K), (None if d is None else d.view(K))
+    W = I.normal(f"gpu/linrms/{N}/{K}/W", (N, K), 0.02, device=DEV)
+    wq, sw = bqd.quantize_weights_int4_rowwise(W)
+    b = I.normal(f"gpu/linrms/{N}/{K}/b", N, 0.01, device=DEV)
+    h_out = torch.full((K,), float("nan"), device=DEV)
+    y, qx, sx, acc = bqd.linear_rmsnorm_w4a8(wq, sw, b, h, gamma, 1e-6, delta=d, h_out=h_out, want_q=True,
+                                            want_acc=True)
+    q2, s2 = bqd.add_rmsnorm_quant(h.view(1, K), gamma, 1e-6, delta=None if d is None else d.view(1, K))
+    y2 = bqd.gemv_w4a8(wq, sw, b, q2.view(K), s2)
+    sync()
+    q, s, h1, _ = O.add_rmsnorm_quant(npy(h), None if d is None else npy(d), npy(gamma), 1e-6)
+    assert np.array_equal(npy(qx), q) and np.array_equal(bits(npy(sx)).ravel(), bits(np.atleast_1d(s)))
+    assert np.array_equal(bits(npy(h_out)), bits(h1))
+    accr, yr = O.gemv_w4a8(O.pack_int4(O.unpack_int4(npy(wq).view(np.uint32))), npy(sw), npy(b), q, float(s))
+    assert np.array_equal(npy(acc), accr)
+    assert O.rel_err_rowwise(npy(y), yr, npy(sw), float(s), accr, npy(b)).max() <= 1e-5
+    assert torch.equal(y, y2)

@@ -161,20 +161,20 @@ def test_read_probe_reads_every_word(unroll):
     assert np.array_equal(npy(sink).view(np.uint32), np.array(expect, np.uint32))
 
 
-def test_decode_chain_fused_equals_unfused_and_oracle():
-    """Two Qwen-shaped layers and the lm_head wired as a decoder (producers
-    fused with the quantisation), one graph replay per token as bench.py
-    times it: the fused and the unfused chain (fp32 producers, linears that
-    quantise in their prologue) give identical bits everywhere; the first
+def test_decode_chain_modes_agree_and_match_the_oracle():
+    """Two Qwen-shaped layers and the lm_head wired as a decoder, one graph
+    replay per token as bench.py times it: RMSNorm in the consuming linear's
+    prologue, producers writing int8 codes, and fp32 producers with linears
+    that quantise in their prologue give identical bits everywhere; the first
     producer's codes and the first QKV output match the oracle."""
     s = DS.QwenW4A8Stream(layers=2, device=DEV, persistent=False)
     c = DS.DecodeChain(s)
-    _graph_replay(lambda: c.step(True), 1)
-    fused = [d["y"].clone() for d in s.linears]
-    c.step(False)
-    torch.cuda.synchronize()
-    for d, y in zip(s.linears, fused):
-        assert torch.equal(d["y"], y), d["name"]
+    _graph_replay(lambda: c.step("prologue"), 1)
+    ref = [d["y"].clone() for d in s.linears]
+    for mode in ("producers", "fp32"):
+        _graph_replay(lambda: c.step(mode), 1)
+        for d, y in zip(s.linears, ref):
+            assert torch.equal(d["y"], y), (mode, d["name"])
     # the first producer and the first QKV against the oracle
     q, sx, _, _ = O.add_rmsnorm_quant(npy(c.h_in), None, npy(c.gamma[0]), DS.RMS_EPS)
     qkv = c.by_layer[0]["qkv"]
@@ -183,7 +183,7 @@ def test_decode_chain_fused_equals_unfused_and_oracle():
     wr, sr = O.prepare_int4_rowwise(npy(W))
     b = npy(qkv["b"])[rows]
     accr, yr = O.gemv_w4a8(wr, sr, b, q[0], float(sx[0]))
-    err = O.rel_err_rowwise(npy(fused[0])[rows], yr, sr, sx[0], accr, b)
+    err = O.rel_err_rowwise(npy(ref[0])[rows], yr, sr, sx[0], accr, b)
     assert err.max() <= TOL, err.max()
     qg, _ = bqd.add_rmsnorm_quant(c.h_in, c.gamma[0], DS.RMS_EPS)
     torch.cuda.synchronize()
