@@ -1833,7 +1833,7 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 //   take the range in batches; a lane streams its rows in steps of 8
 //   16-byte chunks, double-buffered in registers.  Shapes are chosen and
 //   encoded on the host for the grid the launch uses (checked in the kernel).
-//   Sync words: err[0], flags[16 + t * 1024 + w].  Every workgroup writes
+//   Sync words: err[0], flags[16 + (t * 1024 + w) * 16].  Every workgroup writes
 //   each of its flags once per pass, so between passes all flags hold the
 //   same value and a pass derives its epoch from its own flag.  A wait that
 //   exceeds its spin limit sets err bit 0 and proceeds, so every wave always
@@ -1868,6 +1868,10 @@ constexpr int kPassWorkers = 768;
 constexpr int kPassControl = kPassThreads - kPassWorkers;
 constexpr int kPassSlots = 8;         // 16-byte chunks per lane per pipeline step
 constexpr int kPassMaxGrid = 1024;    // completion flags per linear
+// Words from one flag to the next: each flag has a 64-byte line of its own.
+// Flags of workgroups on different XCDs sharing a line cost 3 % of the pass
+// (1.194 -> 1.158 ms per token with this stride; 256 bytes: 1.168 ms).
+constexpr int kFlagStride = 16;
 constexpr int kPassSpinLimit = 1 << 21;
 constexpr int kPassWgPerCu = 1;
 constexpr int kPassMaxK = BQD_MAX_PASS_K;  // LDS: codes (K bytes) + fp32 activation (4K bytes)
@@ -2054,7 +2058,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     const bool worker = tid < kPassWorkers;  // uniform per wave
     const int ct = tid - kPassWorkers;       // control-thread index (>= 0 on control waves)
     uint32_t* err = sync;
-    uint32_t* flags = sync + 16;             // flags[ti * kPassMaxGrid + w]
+    uint32_t* flags = sync + 16;             // flags[(ti * kPassMaxGrid + w) * kFlagStride]
     if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || G > kPassMaxGrid) {
         // uniform: every workgroup leaves
         if (tid == 0 && w == 0)
@@ -2064,7 +2068,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     // Every workgroup writes each of its flags once per pass, so all flags
     // hold the same value between passes: this pass writes that value + 1.
     if (tid == 0)
-        s_epoch = __hip_atomic_load(&flags[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        s_epoch = __hip_atomic_load(&flags[(size_t)w * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     __syncthreads();
     const uint32_t epoch = s_epoch;
 
@@ -2088,12 +2092,12 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         // 1. wait until every workgroup has flagged linear ti-1: the first
         //    control wave reads all G flags (4 per lane per round) and votes.
         if (ti > 0 && ct >= 0 && ct < kWave) {
-            const uint32_t* f = flags + (size_t)(ti - 1) * kPassMaxGrid;
+            const uint32_t* f = flags + (size_t)(ti - 1) * kPassMaxGrid * kFlagStride;
             int spins = 0;
             while (true) {
                 bool done = true;
                 for (int i = ct; i < G; i += kWave)
-                    done &= __hip_atomic_load(&f[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+                    done &= __hip_atomic_load(&f[(size_t)i * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
                 if (__all(done))
                     break;
                 __builtin_amdgcn_s_sleep(1);
@@ -2143,7 +2147,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         __syncthreads();
         // 5. flag linear ti done for this workgroup; workers prefetch ti+1
         if (ct == 0)
-            __hip_atomic_store(&flags[(size_t)ti * kPassMaxGrid + w], epoch, __ATOMIC_RELAXED,
+            __hip_atomic_store(&flags[((size_t)ti * kPassMaxGrid + w) * kFlagStride], epoch, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         have_cur = false;
         if (worker && ti + 1 < n) {
@@ -3158,7 +3162,7 @@ size_t decode_pass_desc_bytes(int32_t n)
 
 size_t decode_pass_sync_bytes(int32_t n)
 {
-    return n > 0 ? (16 + (size_t)n * kPassMaxGrid) * sizeof(uint32_t) : 0;
+    return n > 0 ? (16 + (size_t)n * kPassMaxGrid * kFlagStride) * sizeof(uint32_t) : 0;
 }
 
 // Grid of the pass on the current device: co-resident workgroups, at most

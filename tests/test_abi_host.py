@@ -150,7 +150,7 @@ def test_decode_pass_encode_validates_and_serialises():
     L = _lib()
     n = 2
     nbytes = L.decode_pass_desc_bytes(n)
-    assert nbytes == 16 + 2 * 80 and L.decode_pass_sync_bytes(n) == (16 + 2 * 1024) * 4
+    assert nbytes == 16 + 2 * 80 and L.decode_pass_sync_bytes(n) == (16 + 2 * 1024 * 16) * 4  # a 64-byte line per flag
     host = (C.c_uint8 * nbytes)()
     mk = C.c_int32(0)
     xs = (C.c_void_p * n)(P, P + 0x100)
