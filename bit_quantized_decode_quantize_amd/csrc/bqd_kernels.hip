@@ -1855,7 +1855,9 @@ struct PassTask {
     int32_t rows_base, rows_extra;  // workgroup w owns rows_base + (w < rows_extra) rows
     int32_t lshift, r;              // 2^lshift lanes per row; r rows per lane group
     int32_t iters, batches;         // chunk iterations per row per lane; row batches
-    int32_t steps, x_dtype;         // pipeline steps per batch; X_F32 or X_F16
+    int32_t steps;                  // pipeline steps per batch
+    int16_t x_dtype;                // X_F32 or X_F16
+    int16_t x_in_pass;              // 1: an earlier linear of the pass writes x
 };
 static_assert(sizeof(PassTask) == 80, "descriptor layout");
 
@@ -2000,13 +2002,53 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
 // threads (index st): phase 1 reads x once from memory, keeps it as fp32 in
 // LDS (xf, fp16 widened exactly) and reduces max |x| per wave; phase 2 reads
 // xf back from LDS and writes the permuted codes.
+//
+// An activation that an earlier linear of the same pass wrote (x_in_pass)
+// comes from workgroups on other XCDs, whose caches are not coherent with
+// this one's, and a buffer the decoder reuses may still have old lines in
+// this CU's L1 or this XCD's L2.  Such an x is read with device-scope loads
+// (sc1), coherent with the writers' device-scope stores, which completed
+// before their flag.  (An acquire fence would invalidate both caches
+// instead: 1.1 us per linear, against a few tens of ns for these loads.)
+// Any other x was written before the launch and is read through the caches.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <int XIN>
+__device__ __forceinline__ void load8_device(__amdgpu_buffer_rsrc_t r, int g, float v[8])
+{
+    constexpr int kDeviceScope = 16;  // cache-policy bit sc1
+    if constexpr (XIN == X_F32) {
+        const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g, 0, kDeviceScope));
+        const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g + 16, 0, kDeviceScope));
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const u32x4 h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * g, 0, kDeviceScope));
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[k] & 0xFFFFu));
+            v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[k] >> 16));
+        }
+    }
+}
+
+template <int XIN, bool IN_PASS>
 __device__ __forceinline__ float stage_max(const void* x, f32x4* xf, int G8, int st, int nst)
 {
+    // the descriptor is wave-uniform: keep the resource in scalar registers
+    const uint64_t xa = reinterpret_cast<uint64_t>(x);
+    const uint64_t xu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(xa >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)xa);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(xu), (short)0, G8 * (XIN == X_F32 ? 32 : 16), kBufferWord3);
     float amax = 0.0f;
     for (int g = st; g < G8; g += nst) {
         float u[8];
-        load8<XIN>(x, g, u);
+        if constexpr (IN_PASS)
+            load8_device<XIN>(r, g, u);
+        else
+            load8<XIN>(x, g, u);
         xf[2 * g] = f32x4{u[0], u[1], u[2], u[3]};
         xf[2 * g + 1] = f32x4{u[4], u[5], u[6], u[7]};
 #pragma unroll
@@ -2120,8 +2162,13 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         const int nst = all_stage ? kPassThreads : kPassControl;
         f32x4* xf = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(xs) + xf_offset);
         if (rows > 0 && st >= 0) {
-            const float m = t.x_dtype == X_F16 ? stage_max<X_F16>(t.x, xf, G8, st, nst)
-                                               : stage_max<X_F32>(t.x, xf, G8, st, nst);
+            float m;
+            if (t.x_in_pass)
+                m = t.x_dtype == X_F16 ? stage_max<X_F16, true>(t.x, xf, G8, st, nst)
+                                       : stage_max<X_F32, true>(t.x, xf, G8, st, nst);
+            else
+                m = t.x_dtype == X_F16 ? stage_max<X_F16, false>(t.x, xf, G8, st, nst)
+                                       : stage_max<X_F32, false>(t.x, xf, G8, st, nst);
             if ((st & (kWave - 1)) == 0)
                 rd[st / kWave] = m;
         }
@@ -2777,6 +2824,12 @@ static bool overlaps(const float* a, const float* b, int K)
     return a && b && a < b + K && b < a + K;
 }
 
+static bool bytes_overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
 int linear_rmsnorm_w4a8(const uint32_t* wq, const float* sw, const float* bias, const float* h,
                         const float* delta, const float* gamma, float eps, float* h_out, float* y,
                         int8_t* qx_out, float* sx_out, int32_t* acc, int32_t N, int32_t K, int32_t r,
@@ -3236,7 +3289,22 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
             return BQD_ERR_CONFIG;  // the pass chooses its own work split
         if (l.K > kPassMaxK)
             return BQD_ERR_BOUND;
+        // a linear's workgroups write y while others still read x
+        if (bytes_overlap(x[i], (size_t)l.K * (x_dtype == BQD_F32 ? 4 : 2), y[i], (size_t)l.N * 4))
+            return BQD_ERR_SHAPE;
         kmax = l.K > kmax ? l.K : kmax;
+    }
+    // Weights, scales and biases are read (and prefetched before the wait)
+    // through the caches: no output of the pass may overwrite them.
+    for (int i = 0; i < n; ++i) {
+        const size_t ny = (size_t)lin[i].N * 4;
+        for (int j = 0; j < n; ++j) {
+            const bqd_linear_w4a8& l = lin[j];
+            if (bytes_overlap(y[i], ny, l.wq, (size_t)l.N * l.K / 2) ||
+                bytes_overlap(y[i], ny, l.scales, (size_t)l.N * 4) ||
+                (l.bias && bytes_overlap(y[i], ny, l.bias, (size_t)l.N * 4)))
+                return BQD_ERR_SHAPE;
+        }
     }
     if ((rc = bqd_init()))
         return rc;
@@ -3260,6 +3328,9 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         t.N = l.N;
         t.C = l.K / 32;
         t.x_dtype = x_dtype == BQD_F16 ? X_F16 : X_F32;
+        const size_t nx = (size_t)l.K * (x_dtype == BQD_F32 ? 4 : 2);
+        for (int k = 0; k < i && !t.x_in_pass; ++k)
+            t.x_in_pass = bytes_overlap(x[i], nx, y[k], (size_t)lin[k].N * 4) ? 1 : 0;
         pass_shape_host(t.N, t.C, G, t);
         std::memcpy(d + i, &t, sizeof t);
     }

@@ -389,7 +389,10 @@ size_t decode_pass_sync_bytes(int32_t n);
  * decode_pass_desc_bytes(n) bytes) for the current device: the work split
  * is encoded for the grid the launch will use there, so a device must be
  * current (BQD_ERR_DEVICE otherwise).  *max_k receives the largest K.
- * K_i % 32 == 0 and K_i <= BQD_MAX_PASS_K (BQD_ERR_BOUND otherwise).  The
+ * K_i % 32 == 0 and K_i <= BQD_MAX_PASS_K (BQD_ERR_BOUND otherwise).
+ * x[i] must not overlap y[i] (BQD_ERR_SHAPE): a linear's workgroups write
+ * y while others still read x.  y[i] may be x[j] for any j > i (a
+ * decoder's chain, also through buffers reused within the pass).  The
  * caller copies desc_host unchanged to 16-byte-aligned device memory
  * before decode_pass_w4a8 reads it. */
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
@@ -400,7 +403,10 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
  * the GEMV of gemv_w4a8 (same codes, same y bits as linear_w4a8).  Linear
  * i+1 reads its activation only after every workgroup has finished linear
  * i and its output stores have completed (the decoder's data dependency);
- * weights of linear i+1 are prefetched while waiting.  desc_dev (device)
+ * an activation that an earlier linear of the pass wrote is read with
+ * device-scope loads, so stale lines of a reused buffer in a workgroup's
+ * caches are not served; weights of linear i+1 are prefetched while
+ * waiting.  desc_dev (device)
  * holds the encoded descriptors; max_k is the value decode_pass_encode
  * reported; sync_dev (device) the zero-initialised words of
  * decode_pass_sync_bytes(n).  spin_limit bounds each wait (0 = default,

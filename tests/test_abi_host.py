@@ -153,11 +153,13 @@ def test_decode_pass_encode_validates_and_serialises():
     assert nbytes == 16 + 2 * 80 and L.decode_pass_sync_bytes(n) == (16 + 2 * 1024 * 16) * 4  # a 64-byte line per flag
     host = (C.c_uint8 * nbytes)()
     mk = C.c_int32(0)
-    xs = (C.c_void_p * n)(P, P + 0x100)
-    ys = (C.c_void_p * n)(P + 0x200, P + 0x300)
+    # clear of the weights (a: P .. P + 0x2BC00), x[1]: 18944 fp32 = 0x12800 bytes
+    X0, X1, Y0, Y1 = P + 0x400000, P + 0x410000, P + 0x440000, P + 0x450000
 
-    def enc(lins, nbytes=nbytes, n=n, dt=0):
+    def enc(lins, nbytes=nbytes, n=n, dt=0, x=(X0, X1), y=(Y0, Y1)):
         arr = (bqd.LinearW4A8 * len(lins))(*lins)
+        xs = (C.c_void_p * 2)(*x)
+        ys = (C.c_void_p * 2)(*y)
         return L.decode_pass_encode(arr, n, C.cast(xs, C.c_void_p), dt, C.cast(ys, C.c_void_p),
                                     C.cast(host, C.c_void_p), nbytes, C.byref(mk))
 
@@ -171,6 +173,22 @@ def test_decode_pass_encode_validates_and_serialises():
     assert enc([a, bqd.LinearW4A8(P4, P, 0, 7, 64, 0, 0, 0)]) == ALIGN
     assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 40, 0, 0, 0)]) == SHAPE       # K % 32
     assert enc([a, b], n=0) == SHAPE
+    # a linear whose output overlaps its own activation: its workgroups would
+    # write y while others still read x (fp32 x[1] spans 4 * 18944 bytes, fp16 half that)
+    assert enc([a, b], y=(Y0, X1 + 4 * 18944 - 4)) == SHAPE
+    assert enc([a, b], y=(Y0, X1 - 4 * 7 + 4)) == SHAPE
+    assert enc([a, b], y=(X0 + 4 * 3584 - 4, Y1)) == SHAPE
+    assert enc([a, b], y=(Y0, X1 + 2 * 18944 - 4), dt=1) == SHAPE
+    assert enc([a, b], y=(Y0, X1 + 2 * 18944), dt=1) != SHAPE           # fp16 x ends before y
+    assert enc([a, b], y=(Y0, X1 - 4 * 7)) != SHAPE                     # y ends where x starts
+    # an output over a linear's weights, scales or bias (read, and prefetched
+    # before the wait, through the caches)
+    W, S, B = P + 0x100000, P + 0x200000, P + 0x300000
+    c = bqd.LinearW4A8(W, S, B, 64, 64, 0, 0, 0)                      # 2048 weight bytes, 256 scale bytes
+    assert enc([a, c], y=(W + 2048 - 4, Y1)) == SHAPE
+    assert enc([a, c], y=(Y0, S + 252)) == SHAPE
+    assert enc([a, c], y=(B - 4 * 64 + 4, Y1)) == SHAPE
+    assert enc([a, c], y=(W + 2048, Y1)) != SHAPE
     rc = enc([a, b])                         # valid: encoding needs the device's grid
     if not torch.cuda.is_available():
         assert rc == DEVICE
@@ -180,10 +198,10 @@ def test_decode_pass_encode_validates_and_serialises():
     raw = bytes(host)
     hn, grid, hk, reserved = struct.unpack("<4i", raw[:16])
     assert (hn, hk, reserved) == (2, 18944, 0) and 0 < grid <= 1024
-    f = struct.unpack("<5Q10i", raw[16 + 80:16 + 160])
-    assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, P + 0x100, P + 0x300)
-    N, C_, base, extra, lshift, r, iters, batches, steps, xdt = f[5:]
-    assert (N, C_, base, extra, xdt) == (7, 592, 7 // grid, 7 % grid, 1)
+    f = struct.unpack("<5Q9i2h", raw[16 + 80:16 + 160])
+    assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, X1, Y1)
+    N, C_, base, extra, lshift, r, iters, batches, steps, xdt, x_in_pass = f[5:]
+    assert (N, C_, base, extra, xdt, x_in_pass) == (7, 592, 7 // grid, 7 % grid, 1, 0)
     assert lshift in (4, 5, 6) and r in (1, 2)
     assert iters == -(-592 // (1 << lshift)) and steps == -(-iters * r // 8)
 

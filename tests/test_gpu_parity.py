@@ -487,6 +487,7 @@ def _pass_fixture(dtype=torch.float32, tag="pass"):
 def test_decode_pass_equals_per_linear_launches(dtype):
     lins, xs, ys, parts = _pass_fixture(dtype, f"pass{dtype}")
     p = bqd.DecodePass(lins, xs, ys)
+    assert _x_in_pass(p) == [0] * len(lins)  # no activation is an output of the pass
     ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
     for rep in range(3):                     # the counters carry over between passes
         for y in ys:
@@ -500,6 +501,61 @@ def test_decode_pass_equals_per_linear_launches(dtype):
     wq, sw, b, x = parts[2]
     qxr, sxr, accr, yr = O.linear_w4a8(u32(wq), npy(sw), npy(b), npy(x))
     assert O.rel_err_rowwise(npy(ys[2]), yr, npy(sw), sxr, accr, npy(b)).max() <= TOL
+
+
+def _x_in_pass(p):
+    """The descriptors' flags for activations written earlier in the pass."""
+    raw = p.desc.cpu().numpy().tobytes()
+    return [int(np.frombuffer(raw[16 + 80 * i + 78:16 + 80 * i + 80], dtype=np.int16)[0]) for i in range(p.n)]
+
+
+CHAIN_SHAPES = [(2048, 1024), (1024, 2048), (4096, 1024), (1024, 4096), (1024, 1024), (2944, 1024),
+                (1024, 2944), (8192, 1024), (1024, 8192)]
+
+
+def test_decode_pass_chained_through_reused_buffers():
+    """A decoder's chain inside one pass: linear i+1 reads what linear i
+    wrote, through two buffers used in turn, so every buffer is read again
+    after workgroups on every XCD have rewritten it (a line read earlier in
+    the pass must not be served stale).  Both buffers after each of three
+    passes equal the same chain run as one launch per linear."""
+    cap = max(max(N, K) for N, K in CHAIN_SHAPES)
+    lins, parts = [], []
+    for i, (N, K) in enumerate(CHAIN_SHAPES):
+        W = I.normal(f"gpu/chain/{i}/W", (N, K), 0.02, device=DEV)
+        wq, sw = bqd.quantize_weights_int4_rowwise(W)
+        b = I.normal(f"gpu/chain/{i}/b", N, 0.01, device=DEV) if i % 2 == 0 else None
+        lins.append(bqd.make_linear(wq, sw, b))
+        parts.append((wq, sw, b))
+    x0 = I.normal("gpu/chain/x", CHAIN_SHAPES[0][1], 1.0, device=DEV)
+    bufs = [torch.full((cap,), float("nan"), device=DEV), torch.full((cap,), float("nan"), device=DEV)]
+    xs = [bufs[i % 2][:K] for i, (N, K) in enumerate(CHAIN_SHAPES)]
+    ys = [bufs[(i + 1) % 2][:N] for i, (N, K) in enumerate(CHAIN_SHAPES)]
+    # the same chain, one launch per linear (kernel boundaries order it)
+    ref = [torch.full((cap,), float("nan"), device=DEV), torch.full((cap,), float("nan"), device=DEV)]
+    ref[0][:x0.numel()] = x0
+    for i, ((N, K), (wq, sw, b)) in enumerate(zip(CHAIN_SHAPES, parts)):
+        ref[(i + 1) % 2][:N] = bqd.linear_w4a8(wq, sw, b, ref[i % 2][:K].clone())
+    sync()
+    p = bqd.DecodePass(lins, xs, ys)
+    # every linear but the first reads an output of the pass: device-scope loads
+    assert _x_in_pass(p) == [0] + [1] * (len(CHAIN_SHAPES) - 1)
+    for rep in range(3):
+        bufs[0].fill_(float("nan"))
+        bufs[1].fill_(float("nan"))
+        bufs[0][:x0.numel()] = x0
+        p.run()
+        sync()
+        assert p.error_word() == 0
+        for j in range(2):
+            assert torch.equal(bufs[j].nan_to_num(7.0), ref[j].nan_to_num(7.0)), (rep, j)
+    # the last linear against the oracle, on its input (the previous
+    # linear's output, which nothing overwrote afterwards)
+    (wq, sw, b), (N, K) = parts[-1], CHAIN_SHAPES[-1]
+    xin = npy(ys[-2])
+    assert xin.shape == (K,)
+    qxr, sxr, accr, yr = O.linear_w4a8(u32(wq), npy(sw), None if b is None else npy(b), xin)
+    assert O.rel_err_rowwise(npy(ys[-1]), yr, npy(sw), sxr, accr, None if b is None else npy(b)).max() <= TOL
 
 
 def test_decode_pass_wait_limit_sets_error_and_ends():
@@ -547,6 +603,25 @@ def test_qwen_stream_full_size_persistent_sampled():
         qxr, sxr, accr, y_r = O.linear_w4a8(wr, sr, br, npy(d["x"]))
         err = O.rel_err_rowwise(npy(d["y"][idx]), y_r, sr, sxr, accr, br)
         assert err.max() <= TOL, (k, err.max())
+    # The same 113 linears chained as a decoder chains them: each reads the
+    # previous one's output (a prefix where the previous linear is wider,
+    # e.g. QKV -> O); every output equals the chain launched one linear at a
+    # time.
+    lins = [bqd.make_linear(d["wq"], d["sw"], d["b"]) for d in s.linears]
+    ys = [torch.full((d["N"],), float("nan"), device=DEV) for d in s.linears]
+    xs = [s.linears[0]["x"]] + [ys[i - 1][:d["K"]] for i, d in enumerate(s.linears) if i > 0]
+    p = bqd.DecodePass(lins, xs, ys)
+    assert _x_in_pass(p) == [0] + [1] * (len(lins) - 1)
+    p.run()
+    p.run()
+    sync()
+    assert p.error_word() == 0
+    xr = s.linears[0]["x"]
+    for i, d in enumerate(s.linears):
+        yr = bqd.linear_w4a8(d["wq"], d["sw"], d["b"], xr)
+        assert torch.equal(ys[i], yr), (i, d["name"])
+        xr = yr[:s.linears[i + 1]["K"]] if i + 1 < len(s.linears) else None
+    sync()
 
 
 def test_decode_pass_rejects_descriptors_for_another_grid():
