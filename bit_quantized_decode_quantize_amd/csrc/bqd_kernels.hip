@@ -1821,11 +1821,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 // launch, one 1024-thread workgroup per CU.  Linear t reads its activation
 // only after every workgroup has finished linear t-1: each workgroup writes
 // its output rows with device-coherent stores, waits for them to complete,
-// and then stores the pass's epoch into its own completion flag for t-1;
-// waiters read all flags of t-1 (one wave, 4 flags per lane) and vote.  That
-// is the data dependency of a decoder, where each GEMV's input derives from
+// and then adds one to a completion counter of t-1 (workgroup w to counter
+// w % 64); waiters read the 64 counters of t-1 (one wave, one per lane) and
+// vote.  That is the data dependency of a decoder, where each GEMV's input derives from
 // the previous GEMV's output.  The weights depend on nothing, so right after
-// flagging a linear the worker waves issue the loads of the first step of
+// counting a linear done the worker waves issue the loads of the first step of
 // their share of the next one; they stream from HBM while the control waves
 // wait and quantise the next activation.
 //   Work split: workgroup w owns a contiguous, balanced range of rows of
@@ -1833,9 +1833,12 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 //   take the range in batches; a lane streams its rows in steps of 8
 //   16-byte chunks, double-buffered in registers.  Shapes are chosen and
 //   encoded on the host for the grid the launch uses (checked in the kernel).
-//   Sync words: err[0], flags[16 + (t * 1024 + w) * 16].  Every workgroup writes
-//   each of its flags once per pass, so between passes all flags hold the
-//   same value and a pass derives its epoch from its own flag.  A wait that
+//   Sync words (each on a 64-byte line of its own): err[0]; epoch[w] at
+//   16 + 16 w (w < 1024); counter k of linear t at 16 + 16 (1024 + 64 t + k).
+//   Every workgroup adds one to one counter of every linear and writes its
+//   epoch word once per pass, so between passes all epoch words hold the
+//   same value e, counter k holds e times its number of workgroups, and a
+//   pass waits for e + 1 times that (compared modulo 2^32).  A wait that
 //   exceeds its spin limit sets err bit 0 and proceeds, so every wave always
 //   reaches the end of the kernel; descriptors for another grid or another
 //   n set bit 1 and the kernel returns at once.
@@ -1869,11 +1872,17 @@ constexpr int kPassThreads = 1024;    // 16 waves: one workgroup per CU
 constexpr int kPassWorkers = 768;
 constexpr int kPassControl = kPassThreads - kPassWorkers;
 constexpr int kPassSlots = 8;         // 16-byte chunks per lane per pipeline step
-constexpr int kPassMaxGrid = 1024;    // completion flags per linear
-// Words from one flag to the next: each flag has a 64-byte line of its own.
-// Flags of workgroups on different XCDs sharing a line cost 3 % of the pass
-// (1.194 -> 1.158 ms per token with this stride; 256 bytes: 1.168 ms).
+constexpr int kPassMaxGrid = 1024;
+// Words from one sync word to the next: each has a 64-byte line of its own.
+// Completion flags of workgroups on different XCDs sharing a line cost 3 %
+// of the pass (1.194 -> 1.158 ms per token with this stride).
 constexpr int kFlagStride = 16;
+// Completion counters per linear.  One counter serialises 256 device-scope
+// atomics at one address (1.575 ms per token); one flag per workgroup makes
+// every waiter load 256 words per poll (1.165 ms); 8 / 32 / 64 / 128
+// counters: 1.148 / 1.114-1.148 / 1.112 / 1.144 ms.  64 is one load per lane
+// of the polling wave and 4 atomics per address.
+constexpr int kPassCounters = 64;
 constexpr int kPassSpinLimit = 1 << 21;
 constexpr int kPassWgPerCu = 1;
 constexpr int kPassMaxK = BQD_MAX_PASS_K;  // LDS: codes (K bytes) + fp32 activation (4K bytes)
@@ -2008,7 +2017,7 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
 // this one's, and a buffer the decoder reuses may still have old lines in
 // this CU's L1 or this XCD's L2.  Such an x is read with device-scope loads
 // (sc1), coherent with the writers' device-scope stores, which completed
-// before their flag.  (An acquire fence would invalidate both caches
+// before their count.  (An acquire fence would invalidate both caches
 // instead: 1.1 us per linear, against a few tens of ns for these loads.)
 // Any other x was written before the launch and is read through the caches.
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -2100,17 +2109,18 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     const bool worker = tid < kPassWorkers;  // uniform per wave
     const int ct = tid - kPassWorkers;       // control-thread index (>= 0 on control waves)
     uint32_t* err = sync;
-    uint32_t* flags = sync + 16;             // flags[(ti * kPassMaxGrid + w) * kFlagStride]
+    uint32_t* epochs = sync + 16;                                // epochs[w * kFlagStride]
+    uint32_t* counts = sync + 16 + kPassMaxGrid * kFlagStride;  // counts[(ti * kPassCounters + k) * kFlagStride]
     if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || G > kPassMaxGrid) {
         // uniform: every workgroup leaves
         if (tid == 0 && w == 0)
             __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    // Every workgroup writes each of its flags once per pass, so all flags
+    // Every workgroup writes its epoch word once per pass, so all of them
     // hold the same value between passes: this pass writes that value + 1.
     if (tid == 0)
-        s_epoch = __hip_atomic_load(&flags[(size_t)w * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        s_epoch = __hip_atomic_load(&epochs[(size_t)w * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     __syncthreads();
     const uint32_t epoch = s_epoch;
 
@@ -2131,15 +2141,19 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     }
     for (int ti = 0; ti < n; ++ti) {
         const PassTask tn = tasks[ti + 1 < n ? ti + 1 : ti];
-        // 1. wait until every workgroup has flagged linear ti-1: the first
-        //    control wave reads all G flags (4 per lane per round) and votes.
+        // 1. wait until every workgroup has counted linear ti-1 done: the
+        //    first control wave reads the counters and votes.
         if (ti > 0 && ct >= 0 && ct < kWave) {
-            const uint32_t* f = flags + (size_t)(ti - 1) * kPassMaxGrid * kFlagStride;
+            const uint32_t* c = counts + (size_t)(ti - 1) * kPassCounters * kFlagStride;
             int spins = 0;
             while (true) {
                 bool done = true;
-                for (int i = ct; i < G; i += kWave)
-                    done &= __hip_atomic_load(&f[(size_t)i * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+#pragma unroll
+                for (int k = ct; k < kPassCounters; k += kWave) {
+                    const uint32_t target = epoch * (uint32_t)(G / kPassCounters + (k < G % kPassCounters ? 1 : 0));
+                    done &= (int32_t)(__hip_atomic_load(&c[(size_t)k * kFlagStride], __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT) - target) >= 0;
+                }
                 if (__all(done))
                     break;
                 __builtin_amdgcn_s_sleep(1);
@@ -2192,10 +2206,10 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         if (worker)
             __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // 5. flag linear ti done for this workgroup; workers prefetch ti+1
+        // 5. count linear ti done for this workgroup; workers prefetch ti+1
         if (ct == 0)
-            __hip_atomic_store(&flags[((size_t)ti * kPassMaxGrid + w) * kFlagStride], epoch, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&counts[((size_t)ti * kPassCounters + w % kPassCounters) * kFlagStride], 1u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         have_cur = false;
         if (worker && ti + 1 < n) {
             int rs, rw;
@@ -2210,6 +2224,8 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         }
         t = tn;
     }
+    if (ct == 0)
+        __hip_atomic_store(&epochs[(size_t)w * kFlagStride], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------
@@ -3215,7 +3231,7 @@ size_t decode_pass_desc_bytes(int32_t n)
 
 size_t decode_pass_sync_bytes(int32_t n)
 {
-    return n > 0 ? (16 + (size_t)n * kPassMaxGrid * kFlagStride) * sizeof(uint32_t) : 0;
+    return n > 0 ? (16 + ((size_t)kPassMaxGrid + (size_t)n * kPassCounters) * kFlagStride) * sizeof(uint32_t) : 0;
 }
 
 // Grid of the pass on the current device: co-resident workgroups, at most

@@ -375,8 +375,8 @@ int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const*
 size_t decode_pass_desc_bytes(int32_t n);
 
 /* Bytes of the synchronisation words of a pass over n linears: an error
- * word and one completion flag per linear and workgroup, each flag on a
- * 64-byte line of its own.
+ * word, an epoch word per workgroup and 64 completion counters per linear,
+ * each on a 64-byte line of its own.
  * The caller allocates them on the device, zero-fills them once, and hands
  * the same buffer to every pass over the same descriptors; passes over one
  * buffer must not overlap in time. */

@@ -150,7 +150,7 @@ def test_decode_pass_encode_validates_and_serialises():
     L = _lib()
     n = 2
     nbytes = L.decode_pass_desc_bytes(n)
-    assert nbytes == 16 + 2 * 80 and L.decode_pass_sync_bytes(n) == (16 + 2 * 1024 * 16) * 4  # a 64-byte line per flag
+    assert nbytes == 16 + 2 * 80 and L.decode_pass_sync_bytes(n) == (16 + (1024 + 2 * 64) * 16) * 4  # a 64-byte line per word
     host = (C.c_uint8 * nbytes)()
     mk = C.c_int32(0)
     # clear of the weights (a: P .. P + 0x2BC00), x[1]: 18944 fp32 = 0x12800 bytes

@@ -558,6 +558,38 @@ def test_decode_pass_chained_through_reused_buffers():
     assert O.rel_err_rowwise(npy(ys[-1]), yr, npy(sw), sxr, accr, None if b is None else npy(b)).max() <= TOL
 
 
+def test_decode_pass_counters_wrap_around():
+    """The completion counters hold epoch x (workgroups per counter) and are
+    compared modulo 2^32: preset from the host to just below the wrap, two
+    passes cross it with every output still equal to the per-linear launches
+    and the words where the two passes leave them."""
+    lins, xs, ys, parts = _pass_fixture(tag="passwrap")
+    p = bqd.DecodePass(lins, xs, ys)
+    G = int(p.desc[4:8].cpu().view(torch.int32).item())
+    E = (1 << 30) - 1                          # 4 * E = 2^32 - 4: the next pass wraps at G = 256
+    per = np.array([G // 64 + (1 if k < G % 64 else 0) for k in range(64)], dtype=np.uint64)
+    words = np.zeros(p.sync.numel(), dtype=np.uint32)
+    words[16:16 + 16 * G:16] = E
+    for t in range(p.n):
+        base = 16 + 16 * (1024 + 64 * t)
+        words[base:base + 16 * 64:16] = (E * per) % (1 << 32)
+    p.sync.copy_(torch.from_numpy(words.view(np.int32)).to(DEV))
+    ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
+    for rep in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        p.run()
+        sync()
+        assert p.error_word() == 0, rep
+        for i, (y, yr) in enumerate(zip(ys, ref)):
+            assert torch.equal(y, yr), (rep, i)
+    out = p.sync.cpu().numpy().view(np.uint32)
+    assert (out[16:16 + 16 * G:16] == E + 2).all()
+    for t in range(p.n):
+        base = 16 + 16 * (1024 + 64 * t)
+        assert (out[base:base + 16 * 64:16] == ((E + 2) * per) % (1 << 32)).all(), t
+
+
 def test_decode_pass_wait_limit_sets_error_and_ends():
     """A one-spin limit, set from the host, makes waits give up at once: the
     kernel still ends, flags the error word, and a normal pass clears."""
