@@ -262,6 +262,16 @@ def run_stream(a, dev):
         avg_us, avg_bytes = sum(dur_us) / len(dur_us), step_bytes
         kernel = f"k_decode_pass (persistent: whole token pass, {len(s.linears)} linears, one launch)"
         traffic = measured_traffic() if layers == 28 else None
+        # The same linears chained (each reads the previous output, as a
+        # decoder that reuses buffers would): coherent activation reads.
+        cp = s.chained_pass()
+        cms, _ = time_steps(lambda: cp.run(), a.steps, a.warmup, 0)
+        if cp.error_word():
+            raise RuntimeError(f"chained pass reported a wait time-out (error word {cp.error_word()})")
+        chained = {"ms_per_step": round(cms, 5), "GB/s": round(step_bytes / (cms * 1e-3) / 1e9, 1),
+                   "tok_per_s": round(1e3 / cms, 2),
+                   "note": "linear i reads the first K_i outputs of linear i-1 (device-scope activation loads)"}
+        del cp
     else:
         # Dominant kernel: the gate/up linears + lm_head (most of the bytes),
         # each launch bracketed by events in a second eager pass.
@@ -296,6 +306,8 @@ def run_stream(a, dev):
     out["us_per_gemv"] = round(ms * 1e3 / len(s.linears), 3)
     out["ms_per_step_spread"] = repeat_spread(s.step, max(1, a.steps // 5))
     out["roofline"] = roofline(achieved, kernel, avg_us, avg_bytes, traffic)
+    if s.persistent:
+        out["chained"] = chained
     ceil = read_ceiling(dev)
     out["read_ceiling"] = ceil
     out["pct_of_read_ceiling"] = round(100.0 * gbs / ceil["GB/s"], 2)

@@ -126,6 +126,17 @@ class QwenW4A8Stream:
             for p in self.plans:
                 p.run(stream)
 
+    def chained_pass(self) -> "bqd.DecodePass":
+        """The same linears chained as a decoder chains them, in one pass:
+        linear i reads the first K_i values of linear i-1's output (through
+        output buffers of its own; ``.outputs``), linear 0 the stream's
+        activation.  Same algorithmic bytes as a step of the stream."""
+        ys = [torch.empty(d["N"], dtype=torch.float32, device=self.device) for d in self.linears]
+        xs = [self.linears[0]["x"]] + [ys[i - 1][:d["K"]] for i, d in enumerate(self.linears) if i > 0]
+        p = bqd.DecodePass([bqd.make_linear(d["wq"], d["sw"], d["b"]) for d in self.linears], xs, ys, self.device)
+        p.outputs = ys
+        return p
+
     def bytes_per_step(self) -> int:
         return sum(algorithmic_bytes_linear(d["N"], d["K"], d["b"] is not None) for d in self.linears)
 

@@ -639,11 +639,11 @@ def test_qwen_stream_full_size_persistent_sampled():
     # previous one's output (a prefix where the previous linear is wider,
     # e.g. QKV -> O); every output equals the chain launched one linear at a
     # time.
-    lins = [bqd.make_linear(d["wq"], d["sw"], d["b"]) for d in s.linears]
-    ys = [torch.full((d["N"],), float("nan"), device=DEV) for d in s.linears]
-    xs = [s.linears[0]["x"]] + [ys[i - 1][:d["K"]] for i, d in enumerate(s.linears) if i > 0]
-    p = bqd.DecodePass(lins, xs, ys)
-    assert _x_in_pass(p) == [0] + [1] * (len(lins) - 1)
+    p = s.chained_pass()
+    ys = p.outputs
+    for y in ys:
+        y.fill_(float("nan"))
+    assert _x_in_pass(p) == [0] + [1] * (len(s.linears) - 1)
     p.run()
     p.run()
     sync()
