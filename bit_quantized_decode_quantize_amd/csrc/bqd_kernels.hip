@@ -1727,7 +1727,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
     __shared__ i32x4 part[WAVES][kWave];
     constexpr int U = 8;
     constexpr int NT = WAVES * kWave;
-    constexpr int kStageBatch = WAVES > 8 ? 4 : 8;  // staging loads in flight per thread
+    // Staging loads in flight per thread.  With up to 8 waves, 16 per thread
+    // take the M = 16 activation in one round trip ([18944, 3584]: 17.3 ->
+    // 16.1 us); 16-wave workgroups have 128 registers per lane, and more than
+    // 4 spill (the [3584, 18944] verify then runs 2-3x slower).
+    constexpr int kStageBatch = WAVES > 8 ? 4 : 16;
     constexpr int TPW = WAVES / SPLIT;  // row tiles per workgroup
     const int TS = 2 * SEGC + 1;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -3139,6 +3143,13 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
                 split = sp;
                 break;
             }
+        // From 4 to 8 tokens, 8-wave workgroups stage 16 loads per thread
+        // where 16-wave ones stage 4 (three staging round trips per K instead
+        // of nine at K = 18944): [3584, 18944] M = 4 / 8 14.6 / 17.5 ->
+        // 13.9 / 16.4 us.  At 16 tokens the longer chains per wave cost more
+        // (22.0 -> 23.3 us).
+        if (M >= 4 && M <= 8 && split > 8)
+            split = 8;
         const int waves = split < 4 ? 4 : split;
         const long long groups = (tiles + waves / split - 1) / (waves / split);
         // One workgroup per CU at most: stage longer segments (fewer barriers).

@@ -119,7 +119,7 @@ def test_gemma_stream_layer_and_lm_head():
 
 
 @pytest.mark.parametrize("N,K", [(18944, 3584), (3584, 18944)])
-@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
 def test_verify_pool(N, K, M):
     """The verify GEMM at its benchmark shapes, automatic kernel choice,
     graph replay over the pool: codes bit-exact, y of every token within
