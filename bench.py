@@ -272,6 +272,15 @@ def run_stream(a, dev):
                    "tok_per_s": round(1e3 / cms, 2),
                    "note": "linear i reads the first K_i outputs of linear i-1 (device-scope activation loads)"}
         del cp
+        # The synchronisation floor: the same linears cut to 64 rows each.
+        fp = s.sync_floor_pass(64)
+        fms, _ = time_steps(lambda: fp.run(), a.steps, a.warmup, 0)
+        if fp.error_word():
+            raise RuntimeError(f"sync-floor pass reported a wait time-out (error word {fp.error_word()})")
+        sync_floor = {"ms_per_step": round(fms, 5), "us_per_linear": round(fms * 1e3 / len(s.linears), 3),
+                      "note": "the same linears cut to 64 rows each: waits, activation staging and output "
+                              "stores with almost no weight traffic"}
+        del fp
     else:
         # Dominant kernel: the gate/up linears + lm_head (most of the bytes),
         # each launch bracketed by events in a second eager pass.
@@ -308,6 +317,7 @@ def run_stream(a, dev):
     out["roofline"] = roofline(achieved, kernel, avg_us, avg_bytes, traffic)
     if s.persistent:
         out["chained"] = chained
+        out["sync_floor"] = sync_floor
     ceil = read_ceiling(dev)
     out["read_ceiling"] = ceil
     out["pct_of_read_ceiling"] = round(100.0 * gbs / ceil["GB/s"], 2)

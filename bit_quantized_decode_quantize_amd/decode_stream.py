@@ -137,6 +137,17 @@ class QwenW4A8Stream:
         p.outputs = ys
         return p
 
+    def sync_floor_pass(self, rows: int = 64) -> "bqd.DecodePass":
+        """The same linears cut to their first ``rows`` rows (views of the
+        stream's weights), in one pass: the waits, activation staging and
+        output stores of every linear with almost no weight traffic."""
+        ys = [torch.empty(rows, dtype=torch.float32, device=self.device) for _ in self.linears]
+        lins = [bqd.make_linear(d["wq"][:rows], d["sw"][:rows], None if d["b"] is None else d["b"][:rows])
+                for d in self.linears]
+        p = bqd.DecodePass(lins, [d["x"] for d in self.linears], ys, self.device)
+        p.outputs = ys
+        return p
+
     def bytes_per_step(self) -> int:
         return sum(algorithmic_bytes_linear(d["N"], d["K"], d["b"] is not None) for d in self.linears)
 

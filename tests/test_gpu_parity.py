@@ -635,6 +635,14 @@ def test_qwen_stream_full_size_persistent_sampled():
         qxr, sxr, accr, y_r = O.linear_w4a8(wr, sr, br, npy(d["x"]))
         err = O.rel_err_rowwise(npy(d["y"][idx]), y_r, sr, sxr, accr, br)
         assert err.max() <= TOL, (k, err.max())
+    # The same linears cut to 64 rows (the bench's synchronisation floor):
+    # the full pass's first 64 rows, bit for bit.
+    fp = s.sync_floor_pass(64)
+    fp.run()
+    sync()
+    assert fp.error_word() == 0
+    for i, d in enumerate(s.linears):
+        assert torch.equal(fp.outputs[i], d["y"][:64]), (i, d["name"])
     # The same 113 linears chained as a decoder chains them: each reads the
     # previous one's output (a prefix where the previous linear is wider,
     # e.g. QKV -> O); every output equals the chain launched one linear at a
