@@ -25,6 +25,7 @@ import hashlib
 import json
 import os
 import re
+import struct
 import sys
 import time
 
@@ -67,20 +68,67 @@ def parse():
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_pass_qwen2-7b-28L_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "bit_quantized_decode_quantize_amd", "csrc", "bqd_kernels.hip")
+
+
+def _elf_sections(b):
+    """Section headers of a little-endian ELF64 image: name, type, address,
+    file offset, size, link."""
+    shoff = struct.unpack_from("<Q", b, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+    secs = []
+    for i in range(shnum):
+        name, typ, _, addr, off, size, link = struct.unpack_from("<IIQQQQI", b, shoff + i * shentsize)
+        secs.append({"name": name, "type": typ, "addr": addr, "off": off, "size": size, "link": link})
+    names = secs[shstrndx]["off"]
+    for sec in secs:
+        sec["name"] = b[names + sec["name"]:b.index(b"\0", names + sec["name"])].decode()
+    return secs
+
+
+def kernel_code_sha256(lib_path, needle="k_decode_pass", arch="gfx950"):
+    """sha256 of a kernel's machine code in the library's ``arch`` code
+    object (the clang offload bundle in .hip_fatbin, then the symbol whose
+    name contains ``needle``), or None if it cannot be found."""
+    try:
+        b = open(lib_path, "rb").read()
+        fb = [sec for sec in _elf_sections(b) if sec["name"] == ".hip_fatbin"][0]
+        d = b[fb["off"]:fb["off"] + fb["size"]]
+        if d[:24] != b"__CLANG_OFFLOAD_BUNDLE__":
+            return None
+        n, p, co = struct.unpack_from("<Q", d, 24)[0], 32, None
+        for _ in range(n):
+            off, size, tl = struct.unpack_from("<QQQ", d, p)
+            triple = d[p + 24:p + 24 + tl].decode()
+            p += 24 + tl
+            if arch in triple:
+                co = d[off:off + size]
+        secs = _elf_sections(co)
+        for sym in (sec for sec in secs if sec["type"] in (2, 11)):   # SHT_SYMTAB, SHT_DYNSYM
+            strs = secs[sym["link"]]["off"]
+            for i in range(sym["size"] // 24):
+                nm, info, _, _, val, size = struct.unpack_from("<IBBHQQ", co, sym["off"] + 24 * i)
+                name = co[strs + nm:co.index(b"\0", strs + nm)].decode()
+                if needle in name and (info & 0xF) == 2 and size:       # STT_FUNC
+                    text = [sec for sec in secs if sec["type"] == 1 and sec["addr"] <= val < sec["addr"] + sec["size"]][0]
+                    start = text["off"] + val - text["addr"]
+                    return hashlib.sha256(co[start:start + size]).hexdigest()
+    except (OSError, IndexError, struct.error, TypeError, ValueError):
+        return None
+    return None
 
 
 def measured_traffic(summary=TRAFFIC_SUMMARY):
     """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary (copy-calibrated), or None once the kernel source differs from
-    the one the counters were taken on."""
+    summary (copy-calibrated), or None unless the library in use holds the
+    same k_decode_pass machine code as the one the counters were taken on."""
+    from bit_quantized_decode_quantize_amd import bqd
     try:
         text = open(summary, encoding="utf-8").read()
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
-    vals = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_source_sha256): (\S+)$", text, re.M))
-    if vals.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in vals:
+    vals = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_code_sha256): (\S+)$", text, re.M))
+    sha = kernel_code_sha256(bqd.LIB_PATH)
+    if sha is None or vals.get("kernel_code_sha256") != sha or "traffic_bytes_per_launch" not in vals:
         return None
     return int(vals["traffic_bytes_per_launch"])
 

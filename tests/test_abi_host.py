@@ -368,3 +368,18 @@ def test_linear_rmsnorm_validates_before_launch():
     assert f(P, P, None, P + 8, None, P, 1e-6, None, P, None, None, None, 4, 64, 0, 0, None) == ALIGN
     assert f(P, P, None, P, None, P, 1e-6, None, P, None, None, None, 4, 64, 3, 0, None) == CONFIG
     assert f(P, P, None, P, None, P, 1e-6, None, P, None, None, None, 0, 64, 0, 0, None) == OK
+
+
+def test_bench_reads_the_pass_kernel_code_hash():
+    """bench.py keys the committed HBM-traffic figure to the sha256 of
+    k_decode_pass's machine code in the library's gfx950 code object: the
+    reader finds it in the in-tree build, and the committed summary holds
+    both of its fields."""
+    import bench
+    sha = bench.kernel_code_sha256(bqd.bqd.LIB_PATH)
+    assert sha is not None and re.fullmatch(r"[0-9a-f]{64}", sha)
+    assert bench.kernel_code_sha256(bqd.bqd.LIB_PATH, needle="no_such_kernel") is None
+    assert bench.kernel_code_sha256(os.path.join(ROOT, "no_such_library.so")) is None
+    text = open(os.path.join(ROOT, "profiles", "k_decode_pass_qwen2-7b-28L_traffic.md")).read()
+    assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M)
+    assert re.search(r"^kernel_code_sha256: [0-9a-f]{64}$", text, re.M)
