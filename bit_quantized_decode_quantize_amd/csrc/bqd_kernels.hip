@@ -1827,11 +1827,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 // its output rows with device-coherent stores, waits for them to complete,
 // and then adds one to a completion counter of t-1 (workgroup w to counter
 // w % 64); waiters read the 64 counters of t-1 (one wave, one per lane) and
-// vote.  That is the data dependency of a decoder, where each GEMV's input derives from
-// the previous GEMV's output.  The weights depend on nothing, so right after
-// counting a linear done the worker waves issue the loads of the first step of
-// their share of the next one; they stream from HBM while the control waves
-// wait and quantise the next activation.
+// vote.  That is the data dependency of a decoder, where each GEMV's input
+// derives from the previous GEMV's output.  The weights depend on nothing,
+// so right after counting a linear done the worker waves issue the loads of
+// the first step of their share of the next one; they stream from HBM while
+// the control waves wait and quantise the next activation.
 //   Work split: workgroup w owns a contiguous, balanced range of rows of
 //   every linear; its lane groups (2^lshift lanes per row, r rows per group)
 //   take the range in batches; a lane streams its rows in steps of 8
@@ -1878,9 +1878,10 @@ constexpr int kPassControl = kPassThreads - kPassWorkers;
 constexpr int kPassSlots = 8;         // 16-byte chunks per lane per pipeline step
 constexpr int kPassMaxGrid = 1024;
 // Words from one sync word to the next: each has a 64-byte line of its own.
-// Completion flags of workgroups on different XCDs sharing a line cost 3 %
-// of the pass (1.194 -> 1.158 ms per token with this stride).
-constexpr int kFlagStride = 16;
+// Sync words of workgroups on different XCDs sharing a line cost 3 % of the
+// pass (measured with one completion flag per workgroup: 1.194 -> 1.158 ms
+// per token with this stride).
+constexpr int kSyncStride = 16;
 // Completion counters per linear.  One counter serialises 256 device-scope
 // atomics at one address (1.575 ms per token); one flag per workgroup makes
 // every waiter load 256 words per poll (1.165 ms); 8 / 32 / 64 / 128
@@ -2113,8 +2114,8 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     const bool worker = tid < kPassWorkers;  // uniform per wave
     const int ct = tid - kPassWorkers;       // control-thread index (>= 0 on control waves)
     uint32_t* err = sync;
-    uint32_t* epochs = sync + 16;                                // epochs[w * kFlagStride]
-    uint32_t* counts = sync + 16 + kPassMaxGrid * kFlagStride;  // counts[(ti * kPassCounters + k) * kFlagStride]
+    uint32_t* epochs = sync + 16;                                // epochs[w * kSyncStride]
+    uint32_t* counts = sync + 16 + kPassMaxGrid * kSyncStride;  // counts[(ti * kPassCounters + k) * kSyncStride]
     if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || G > kPassMaxGrid) {
         // uniform: every workgroup leaves
         if (tid == 0 && w == 0)
@@ -2124,7 +2125,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     // Every workgroup writes its epoch word once per pass, so all of them
     // hold the same value between passes: this pass writes that value + 1.
     if (tid == 0)
-        s_epoch = __hip_atomic_load(&epochs[(size_t)w * kFlagStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        s_epoch = __hip_atomic_load(&epochs[(size_t)w * kSyncStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     __syncthreads();
     const uint32_t epoch = s_epoch;
 
@@ -2148,14 +2149,14 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         // 1. wait until every workgroup has counted linear ti-1 done: the
         //    first control wave reads the counters and votes.
         if (ti > 0 && ct >= 0 && ct < kWave) {
-            const uint32_t* c = counts + (size_t)(ti - 1) * kPassCounters * kFlagStride;
+            const uint32_t* c = counts + (size_t)(ti - 1) * kPassCounters * kSyncStride;
             int spins = 0;
             while (true) {
                 bool done = true;
 #pragma unroll
                 for (int k = ct; k < kPassCounters; k += kWave) {
                     const uint32_t target = epoch * (uint32_t)(G / kPassCounters + (k < G % kPassCounters ? 1 : 0));
-                    done &= (int32_t)(__hip_atomic_load(&c[(size_t)k * kFlagStride], __ATOMIC_RELAXED,
+                    done &= (int32_t)(__hip_atomic_load(&c[(size_t)k * kSyncStride], __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT) - target) >= 0;
                 }
                 if (__all(done))
@@ -2212,7 +2213,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         __syncthreads();
         // 5. count linear ti done for this workgroup; workers prefetch ti+1
         if (ct == 0)
-            __hip_atomic_fetch_add(&counts[((size_t)ti * kPassCounters + w % kPassCounters) * kFlagStride], 1u,
+            __hip_atomic_fetch_add(&counts[((size_t)ti * kPassCounters + w % kPassCounters) * kSyncStride], 1u,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         have_cur = false;
         if (worker && ti + 1 < n) {
@@ -2229,7 +2230,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         t = tn;
     }
     if (ct == 0)
-        __hip_atomic_store(&epochs[(size_t)w * kFlagStride], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&epochs[(size_t)w * kSyncStride], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------
@@ -3242,7 +3243,7 @@ size_t decode_pass_desc_bytes(int32_t n)
 
 size_t decode_pass_sync_bytes(int32_t n)
 {
-    return n > 0 ? (16 + ((size_t)kPassMaxGrid + (size_t)n * kPassCounters) * kFlagStride) * sizeof(uint32_t) : 0;
+    return n > 0 ? (16 + ((size_t)kPassMaxGrid + (size_t)n * kPassCounters) * kSyncStride) * sizeof(uint32_t) : 0;
 }
 
 // Grid of the pass on the current device: co-resident workgroups, at most
