@@ -1032,16 +1032,20 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8_g32(
 // ------------------------------------------------------------------------
 // W8A16 GEMV (int8 codes, fp16 group-32 scales, fp16 activation).
 //   A lane handles whole 32-code groups (two 16-byte chunks).  Each byte
-//   code q in [-32, 31] becomes an exact fp16 by the magic-number route:
-//   u = (q ^ 32) & 63 = q + 32, fp16 bits 0x6400 | u = 1024 + u, minus 1056.
-//   Pairs then go through v_dot2_f32_f16 against the staged fp16 x.
+//   code q becomes an exact fp16 by the magic-number route: u = q ^ 0x80 =
+//   q + 128 in [0, 255], fp16 bits 0x6400 | u = 1024 + u (spacing 1 there),
+//   minus 1152.  One v_perm_b32 against the constant 0x64 bytes builds the
+//   fp16 pair of two codes; pairs then go through v_dot2_f32_f16 against the
+//   staged fp16 x.  (Masking the 6-bit code and assembling the pairs with
+//   shifts took 3.65 VALU instructions per code; this takes 1.75.)
 // ------------------------------------------------------------------------
 __device__ __forceinline__ float dot4_w8_f16(uint32_t w, uint32_t x01, uint32_t x23, float acc)
 {
-    const uint32_t u = (w ^ 0x20202020u) & 0x3F3F3F3Fu;
-    const uint32_t h01 = (u & 0xFFu) | ((u & 0xFF00u) << 8) | 0x64006400u;
-    const uint32_t h23 = ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u;
-    const h16x2 bias = {(_Float16)1056.0f, (_Float16)1056.0f};
+    const uint32_t u = w ^ 0x80808080u;
+    // selector bytes 0-3 take u's bytes, 4 a byte of 0x64646464
+    const uint32_t h01 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // [u0, 64, u1, 64]
+    const uint32_t h23 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // [u2, 64, u3, 64]
+    const h16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
     const h16x2 q01 = __builtin_bit_cast(h16x2, h01) - bias;
     const h16x2 q23 = __builtin_bit_cast(h16x2, h23) - bias;
     acc = __builtin_amdgcn_fdot2(q01, __builtin_bit_cast(h16x2, x01), acc, false);
@@ -1203,15 +1207,26 @@ __global__ __launch_bounds__(kThreads) void k_quantize_weights_q6k(const float* 
 // Eight codes of one low-nibble word w (weights 8k..8k+7) with their high
 // bits hq (already shifted so that pair e sits at bits 2e and 16 + 2e),
 // against the staged activation pairs (x_e, x_{e+4}), e = 0..3.
+// (a & m) | (b & ~m) in one instruction (the compiler splits it into and/or3
+// when b is a constant).
+__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b)
+{
+    uint32_t d;
+    __asm__("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(m), "v"(a), "v"(b));
+    return d;
+}
+
 __device__ __forceinline__ float dot8_q6(uint32_t w, uint32_t hq, uint32_t x04, uint32_t x15, uint32_t x26,
                                          uint32_t x37, float acc)
 {
     const h16x2 bias = {(_Float16)1056.0f, (_Float16)1056.0f};
     const uint32_t xp[4] = {x04, x15, x26, x37};
+    const uint32_t expo = 0x64006400u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = ((w >> (4 * e)) & 0x000F000Fu) | 0x64006400u;
-        const uint32_t u2 = (((hq >> (2 * e)) << 4) & 0x00300030u) | lo;
+        // low nibbles into the fp16 exponent word, then the high bits over them
+        const uint32_t hs = 2 * e <= 4 ? hq << (4 - 2 * e) : hq >> (2 * e - 4);
+        const uint32_t u2 = bfi32(0x00300030u, hs, bfi32(0x000F000Fu, w >> (4 * e), expo));
         acc = __builtin_amdgcn_fdot2(as_h16x2(u2) - bias, as_h16x2(xp[e]), acc, false);
     }
     return acc;
@@ -2959,7 +2974,7 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
         return BQD_ERR_CONFIG;
     const int L = lanes_per_row ? lanes_per_row : 16;
     if (r == 0)
-        r = 2;  // [262144, 1536]: 78 us with r = 2, 84 us with 4 (16 lanes per row)
+        r = 1;  // [262144, 1536], 16 lanes per row: 70.4 / 73.7 / 77.5 us for r = 1 / 2 / 4
     if ((rc = bqd_init()))
         return rc;
     const int G = K / 32;
