@@ -25,6 +25,7 @@ BQD_SCALE_ROW_F32, BQD_SCALE_GROUP32_F16 = 0, 1
 BQD_MAX_K = 65536
 BQD_MAX_TOKENS = 16
 BQD_MAX_PROD_K = 32768
+BQD_MAX_PASS_K = 24576
 BQD_INT8X_BLOCK = 512
 
 ENTRY_POINTS = (

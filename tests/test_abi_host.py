@@ -172,6 +172,7 @@ def test_decode_pass_encode_validates_and_serialises():
     assert enc([a, bqd.LinearW4A8(P, P, 0, 0, 64, 0, 0, 0)]) == SHAPE       # N = 0
     assert enc([a, bqd.LinearW4A8(P4, P, 0, 7, 64, 0, 0, 0)]) == ALIGN
     assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 40, 0, 0, 0)]) == SHAPE       # K % 32
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, bqd.BQD_MAX_PASS_K + 32, 0, 0, 0)]) == BOUND  # LDS
     assert enc([a, b], n=0) == SHAPE
     # a linear whose output overlaps its own activation: its workgroups would
     # write y while others still read x (fp32 x[1] spans 4 * 18944 bytes, fp16 half that)
@@ -383,3 +384,21 @@ def test_bench_reads_the_pass_kernel_code_hash():
     text = open(os.path.join(ROOT, "profiles", "k_decode_pass_qwen2-7b-28L_traffic.md")).read()
     assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M)
     assert re.search(r"^kernel_code_sha256: [0-9a-f]{64}$", text, re.M)
+
+
+def test_binding_constants_match_the_header():
+    """Every BQD_ constant the binding defines has the value include/bqd.h
+    gives it, and the status codes these tests use are the header's."""
+    text = open(os.path.join(ROOT, "include", "bqd.h")).read()
+    defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"^#define (BQD_\w+) \(?(-?\d+)\)?", text, re.M)}
+    mod = bqd.bqd
+    shared = [n for n in defs if hasattr(mod, n)]
+    assert {"BQD_MAX_K", "BQD_MAX_TOKENS", "BQD_MAX_PROD_K", "BQD_MAX_PASS_K", "BQD_INT8X_BLOCK", "BQD_F32",
+            "BQD_F16", "BQD_SCALE_ROW_F32", "BQD_SCALE_GROUP32_F16"} <= set(shared)
+    for n in shared:
+        assert getattr(mod, n) == defs[n], n
+    codes = {"BQD_OK": OK, "BQD_ERR_NULL": NULL, "BQD_ERR_SHAPE": SHAPE, "BQD_ERR_ALIGN": ALIGN,
+             "BQD_ERR_BOUND": BOUND, "BQD_ERR_DTYPE": DTYPE, "BQD_ERR_CONFIG": CONFIG, "BQD_ERR_LAUNCH": LAUNCH,
+             "BQD_ERR_DEVICE": DEVICE}
+    for n, v in codes.items():
+        assert defs[n] == v, n

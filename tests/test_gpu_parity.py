@@ -590,6 +590,36 @@ def test_decode_pass_counters_wrap_around():
         assert (out[base:base + 16 * 64:16] == ((E + 2) * per) % (1 << 32)).all(), t
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_decode_pass_at_the_largest_k(dtype):
+    """Linears at the pass's largest K (its LDS holds K codes and 4K bytes of
+    fp32 activation) between small ones, ragged row counts: every output
+    equals the per-linear launch, one against the oracle."""
+    K = bqd.BQD_MAX_PASS_K
+    shapes = [(300, K), (1000, 32), (17, K), (4100, 64)]
+    lins, xs, ys, parts = [], [], [], []
+    for i, (N, Ki) in enumerate(shapes):
+        W = I.normal(f"gpu/passmax/{i}/W", (N, Ki), 0.02, device=DEV)
+        wq, sw = bqd.quantize_weights_int4_rowwise(W)
+        b = I.normal(f"gpu/passmax/{i}/b", N, 0.01, device=DEV) if i % 2 == 0 else None
+        x = I.normal(f"gpu/passmax/{i}/x", Ki, 1.0, device=DEV, dtype=dtype)
+        lins.append(bqd.make_linear(wq, sw, b))
+        xs.append(x)
+        ys.append(torch.full((N,), float("nan"), device=DEV))
+        parts.append((wq, sw, b, x))
+    p = bqd.DecodePass(lins, xs, ys)
+    assert p.max_k == K
+    p.run()
+    p.run()
+    sync()
+    assert p.error_word() == 0
+    for i, ((wq, sw, b, x), y) in enumerate(zip(parts, ys)):
+        assert torch.equal(y, bqd.linear_w4a8(wq, sw, b, x)), i
+    wq, sw, b, x = parts[0]
+    qxr, sxr, accr, yr = O.linear_w4a8(u32(wq), npy(sw), npy(b), npy(x))
+    assert O.rel_err_rowwise(npy(ys[0]), yr, npy(sw), sxr, accr, npy(b)).max() <= TOL
+
+
 def test_decode_pass_wait_limit_sets_error_and_ends():
     """A one-spin limit, set from the host, makes waits give up at once: the
     kernel still ends, flags the error word, and a normal pass clears."""
