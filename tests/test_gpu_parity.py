@@ -620,6 +620,22 @@ def test_decode_pass_at_the_largest_k(dtype):
     assert O.rel_err_rowwise(npy(ys[0]), yr, npy(sw), sxr, accr, npy(b)).max() <= TOL
 
 
+def test_decode_pass_zero_activation_gives_the_bias():
+    """A linear of the pass whose activation is all zero has s^x = 0, zero
+    codes and y = b exactly (the degenerate case of the per-token scale);
+    the linears around it are unaffected."""
+    lins, xs, ys, parts = _pass_fixture(tag="passzero")
+    xs[2].zero_()
+    p = bqd.DecodePass(lins, xs, ys)
+    p.run()
+    sync()
+    assert p.error_word() == 0
+    wq, sw, b, x = parts[2]
+    assert b is not None and torch.equal(ys[2], b)
+    for i, ((wq, sw, b, x), y) in enumerate(zip(parts, ys)):
+        assert torch.equal(y, bqd.linear_w4a8(wq, sw, b, x)), i
+
+
 def test_decode_pass_wait_limit_sets_error_and_ends():
     """A one-spin limit, set from the host, makes waits give up at once: the
     kernel still ends, flags the error word, and a normal pass clears."""
