@@ -532,8 +532,11 @@ def gemm_w4a8_verify(wq, sw, bias, qx, sx, y=None, acc=None, impl=0, stream=None
 
 
 def make_linear(wq, scales, bias=None, r=0, lanes_per_row=0) -> LinearW4A8:
-    """Descriptor of one linear for layer_w4a8_forward (keeps no references:
-    the caller keeps the tensors alive)."""
+    """Descriptor of one linear for layer_w4a8_forward / DecodePass.  The
+    descriptor holds references to its tensors (``_tensors``), and LayerPlan
+    and DecodePass hold their descriptors, so the device memory they point
+    to stays allocated while they exist (the C structure itself carries only
+    raw pointers)."""
     N, K = _wshape(wq, None)
     _dev(wq, "wq", _WORD, N * K // 8)
     if scales.dtype == torch.float32:
@@ -543,7 +546,9 @@ def make_linear(wq, scales, bias=None, r=0, lanes_per_row=0) -> LinearW4A8:
         _dev(scales, "scales", (torch.float16,), N * (K // 32))
         kind = BQD_SCALE_GROUP32_F16
     _opt(bias, "bias", _F32, N)
-    return LinearW4A8(wq.data_ptr(), scales.data_ptr(), _ptr(bias), N, K, kind, r, lanes_per_row)
+    d = LinearW4A8(wq.data_ptr(), scales.data_ptr(), _ptr(bias), N, K, kind, r, lanes_per_row)
+    d._tensors = (wq, scales, bias)
+    return d
 
 
 class LayerPlan:
@@ -563,7 +568,7 @@ class LayerPlan:
         self.lin = (LinearW4A8 * max(n, 1))(*linears)
         self.xp = (C.c_void_p * max(n, 1))(*[x.data_ptr() for x in xs])
         self.yp = (C.c_void_p * max(n, 1))(*[y.data_ptr() for y in ys])
-        self._keep = (list(xs), list(ys))
+        self._keep = (list(xs), list(ys), list(linears))
 
     def run(self, stream=None):
         _call("layer_w4a8_forward", self.lin, self.n, C.cast(self.xp, C.c_void_p), self.x_dtype,
@@ -603,7 +608,7 @@ class DecodePass:
         self.max_k = mk.value
         self.desc = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device)
         self.sync = torch.zeros(lib().decode_pass_sync_bytes(n) // 4, dtype=torch.int32, device=device)
-        self._keep = (list(xs), list(ys))
+        self._keep = (list(xs), list(ys), list(linears))
 
     def run(self, stream=None, spin_limit: int = 0) -> None:
         _call("decode_pass_w4a8", self.desc.data_ptr(), self.n, self.max_k, self.sync.data_ptr(),

@@ -636,6 +636,31 @@ def test_decode_pass_zero_activation_gives_the_bias():
         assert torch.equal(y, bqd.linear_w4a8(wq, sw, b, x)), i
 
 
+def test_pass_descriptors_keep_their_tensors():
+    """Descriptors built from tensors nothing else refers to (a helper's
+    locals) stay valid: the descriptor holds its tensors and the pass its
+    descriptors, so new allocations cannot take their memory."""
+    def build(i, N, K):
+        W = I.normal(f"gpu/keep/{i}/W", (N, K), 0.02, device=DEV)
+        wq, sw = bqd.quantize_weights_int4_rowwise(W)
+        ref = bqd.linear_w4a8(wq, sw, None, x0[:K])
+        return bqd.make_linear(wq, sw, None), ref
+    x0 = I.normal("gpu/keep/x", 3584, 1.0, device=DEV)
+    built = [build(i, N, K) for i, (N, K) in enumerate([(700, 3584), (300, 1536), (900, 3584)])]
+    sync()
+    lins, refs = [b[0] for b in built], [b[1] for b in built]
+    ys = [torch.full((l.N,), float("nan"), device=DEV) for l in lins]
+    p = bqd.DecodePass(lins, [x0[:l.K] for l in lins], ys)
+    del lins, built
+    junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device=DEV) for _ in range(16)]  # reuse freed memory
+    p.run()
+    sync()
+    assert p.error_word() == 0
+    for y, r in zip(ys, refs):
+        assert torch.equal(y, r)
+    del junk
+
+
 def test_decode_pass_wait_limit_sets_error_and_ends():
     """A one-spin limit, set from the host, makes waits give up at once: the
     kernel still ends, flags the error word, and a normal pass clears."""
