@@ -1852,6 +1852,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 //   take the range in batches; a lane streams its rows in steps of 8
 //   16-byte chunks, double-buffered in registers.  Shapes are chosen and
 //   encoded on the host for the grid the launch uses (checked in the kernel).
+//   An activation that an earlier linear of the pass wrote (flagged on the
+//   host: x_in_pass) is read with device-scope loads; see stage_max.
 //   Sync words (each on a 64-byte line of its own): err[0]; epoch[w] at
 //   16 + 16 w (w < 1024); counter k of linear t at 16 + 16 (1024 + 64 t + k).
 //   Every workgroup adds one to one counter of every linear and writes its
