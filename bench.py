@@ -751,8 +751,9 @@ def run_int8x(a, dev):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {a.gpus} requested); the path's sharding "
-              "is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): the path would shard by output "
+              "rows (K for the O and down projections, with an int32 all-reduce), and one GPU runs its "
+              "share at the real shape", file=sys.stderr)
         sys.exit(2)
     import torch
     dev = torch.device("cuda:0")

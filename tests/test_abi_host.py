@@ -402,3 +402,13 @@ def test_binding_constants_match_the_header():
              "BQD_ERR_DEVICE": DEVICE}
     for n, v in codes.items():
         assert defs[n] == v, n
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py --gpus N > 1 exits with status 2 and a message, before any
+    GPU work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
