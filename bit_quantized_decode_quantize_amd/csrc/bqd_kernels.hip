@@ -1482,23 +1482,25 @@ __global__ __launch_bounds__(kThreads) void k_gemv_int8x(Int8xStreams st, const 
 // dequantises to fp16 and uses fp16 MACs).
 //   Per word: u = w ^ 0x88888888 turns each signed nibble q into q + 8;
 //   bytes (u & 0x0F0F0F0F) hold codes {0,2,4,6}, ((u >> 4) & 0x0F0F0F0F)
-//   codes {1,3,5,7}; each byte pair is spread into fp16 bits 0x6400 | (q+8)
-//   = 1024 + q + 8, and a packed subtract of 1032 gives q exactly; then
-//   v_dot2_f32_f16 against x staged per 8-group as [x0 x2 | x4 x6 | x1 x3 |
-//   x5 x7].  The compiled loop issues about 3.4 VALU instructions per code,
-//   against about 1.1 for the integer dot.  y = fmaf(sw, acc, b) with acc
-//   the fp32 sum.
+//   codes {1,3,5,7}; one v_perm_b32 spreads a byte pair into fp16 bits
+//   0x6400 | (q+8) = 1024 + q + 8, and a packed subtract of 1032 gives q
+//   exactly; then v_dot2_f32_f16 against x staged per 8-group as [x0 x2 |
+//   x4 x6 | x1 x3 | x5 x7].  The compiled loop issues about 2.0 VALU
+//   instructions per code (3.4 when the pairs were assembled with shifts
+//   and masks), against about 1.1 for the integer dot.  y = fmaf(sw, acc, b)
+//   with acc the fp32 sum.
 // ------------------------------------------------------------------------
 __device__ __forceinline__ float dot8_w4_f16(uint32_t w, u32x4 xg, float acc)
 {
     const uint32_t u = w ^ 0x88888888u;
     const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
-    // fp16 pairs [1024 + c_a, 1024 + c_b] from bytes a, b of a code word.
+    // fp16 pairs [1024 + c_a, 1024 + c_b] from bytes a, b of a code word:
+    // one v_perm_b32 each against the constant 0x64 bytes.
     const h16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-    const h16x2 q02 = __builtin_bit_cast(h16x2, (lo & 0xFFu) | ((lo & 0xFF00u) << 8) | 0x64006400u) - bias;
-    const h16x2 q46 = __builtin_bit_cast(h16x2, ((lo >> 16) & 0xFFu) | ((lo >> 8) & 0xFF0000u) | 0x64006400u) - bias;
-    const h16x2 q13 = __builtin_bit_cast(h16x2, (hi & 0xFFu) | ((hi & 0xFF00u) << 8) | 0x64006400u) - bias;
-    const h16x2 q57 = __builtin_bit_cast(h16x2, ((hi >> 16) & 0xFFu) | ((hi >> 8) & 0xFF0000u) | 0x64006400u) - bias;
+    const h16x2 q02 = __builtin_bit_cast(h16x2, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - bias;
+    const h16x2 q46 = __builtin_bit_cast(h16x2, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - bias;
+    const h16x2 q13 = __builtin_bit_cast(h16x2, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - bias;
+    const h16x2 q57 = __builtin_bit_cast(h16x2, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - bias;
     acc = __builtin_amdgcn_fdot2(q02, as_h16x2(xg.x), acc, false);
     acc = __builtin_amdgcn_fdot2(q46, as_h16x2(xg.y), acc, false);
     acc = __builtin_amdgcn_fdot2(q13, as_h16x2(xg.z), acc, false);
