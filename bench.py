@@ -566,12 +566,28 @@ def run_verify(a, dev):
             log(f"verify {N}x{K} M={M}: {sweep[-1]}")
             del w
             torch.cuda.empty_cache()
+    # A1 on its own: the per-token activation quantisation that feeds the
+    # verify GEMM (M tokens, fp32 X), graph-replayed, x read once per call.
+    from bit_quantized_decode_quantize_amd import bqd, inputs as I
+    qa = []
+    for K in (3584, 18944):
+        for M in ms_list:
+            X = I.normal(f"verify/quant/{M}x{K}", (M, K), 1.0, 0, dev)
+            qx = torch.empty(M, K, dtype=torch.int8, device=dev)
+            sx = torch.empty(M, dtype=torch.float32, device=dev)
+            ms, n = time_steps(lambda: bqd.quantize_act(X, qx=qx, sx=sx), max(a.steps, 64), a.warmup,
+                               0 if a.eager else 16)
+            qa.append({"K": K, "M": M, "us": round(ms * 1e3, 3),
+                       "GB/s": round(M * (5 * K + 4) / (ms * 1e-3) / 1e9, 1)})
+            del X, qx, sx
+    log(f"quantize_act: {qa}")
     last = max((r for r in sweep if r["N"] == 18944), key=lambda r: r["M"])
     ms = last["us"] * 1e-3
     out = base_line(a, last["GB/s"], ms, last["steps"], {
         "workload": "M-token verify GEMM, per-row int4 weights [18944,3584] and [3584,18944], int8 X [M,K] "
                     "(per-token scales), bias", "impl": a.impl, "M": ms_list})
     out["sweep"] = sweep
+    out["quantize_act"] = qa
     wl_bytes = WL.bytes_verify(last["M"], 18944, 3584)
     kname = ("k_gemv_w4a8" if last["M"] == 1 and a.impl == 0 else
              "k_verify_w4a8" if a.impl == 1 else "k_verify_mfma")

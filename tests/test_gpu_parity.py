@@ -44,8 +44,11 @@ def rel_err(y, y_ref, mag):
 
 # ------------------------------------------------------ activation quant --
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
-@pytest.mark.parametrize("K", [32, 64, 1536, 3584, 18944])
+@pytest.mark.parametrize("K", [32, 64, 1536, 3584, 4096, 4128, 18944, 32768, 32800, 65536])
 def test_quantize_act_bit_exact(K, dtype):
+    """fp32 tokens up to 32768 values take the register-held producers'
+    quantiser (1, 2, 4 or 8 items per thread), longer ones and fp16 the
+    two-pass kernel: the same codes and scales either way."""
     M = 4
     x = I.normal(f"gpu/act/{K}", (M, K), 1.0, device=DEV, dtype=dtype)
     x[0] = I.with_outliers(x[0].float(), f"gpu/act/{K}/o").to(dtype)
