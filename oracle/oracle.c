@@ -332,6 +332,24 @@ int orc_gemv_w4a8(const uint32_t* w, const float* sw, const float* bias,
     return ORC_OK;
 }
 
+/* The binary32 value of y_j that the GPU path writes and that a decoder
+ * chain hands on as the next linear's activation ([Orin] derivation section:
+ * each linear's input comes from the previous output).  The next codes are
+ * decided from it, so it is taken in the GPU path's precision: with
+ * s = fl32(s^W_j * s^x) and a = fl32(acc_j) (exact while |acc| < 2^24),
+ *   y_j = fl32(s * a + b_j)      (one rounding: C99 fmaf)
+ * and b_j = +0 when there is no bias. */
+int orc_epilogue_f32(const float* sw, const float* bias, float sx, const int32_t* acc, int64_t N, float* y)
+{
+    if (N < 0)
+        return ORC_E_ARG;
+    for (int64_t j = 0; j < N; ++j) {
+        const float s = sw[j] * sx;
+        y[j] = fmaf(s, (float)acc[j], bias ? bias[j] : 0.0f);
+    }
+    return ORC_OK;
+}
+
 /* Group-32 W4A8: acc_jg over each block of 32 weights, then
  *   y_j = s^x * sum_g s_jg * acc_jg + b_j   (binary64, ascending g). */
 int orc_gemv_w4a8_group32(const uint32_t* w, const uint16_t* s16, const float* bias,

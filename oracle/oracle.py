@@ -49,6 +49,7 @@ def _load():
         "orc_quantize_act_f32": (I32, [P, I64, I64, P, P]),
         "orc_quantize_act_f16": (I32, [P, I64, I64, P, P]),
         "orc_gemv_w4a8": (I32, [P, P, P, P, F32, I64, I64, P, P]),
+        "orc_epilogue_f32": (I32, [P, P, F32, P, I64, P]),
         "orc_gemv_w4a8_group32": (I32, [P, P, P, P, F32, I64, I64, P, P]),
         "orc_gemv_w8a16_group32": (I32, [P, P, P, I64, I64, P]),
         "orc_gemm_w4a8_verify": (I32, [P, P, P, P, P, I64, I64, I64, P, P]),
@@ -360,6 +361,19 @@ def gemv_w4a8(w, sw, bias, qx, sx) -> Tuple[np.ndarray, np.ndarray]:
     return acc, y
 
 
+def epilogue_f32(sw, bias, sx, acc) -> np.ndarray:
+    """y_j in binary32 as the GPU path writes it and a chain hands it on:
+    fl32(fl32(sW_j sx) * fl32(acc_j) + b_j) with one rounding (fused)."""
+    sw = _c(sw, np.float32)
+    acc = _c(acc, np.int32)
+    b = None if bias is None else _c(bias, np.float32)
+    N = sw.size
+    assert acc.size == N and (b is None or b.size == N)
+    y = np.empty(N, np.float32)
+    _check(_lib.orc_epilogue_f32(_p(sw), _p(b), C.c_float(float(sx)), _p(acc), N, _p(y)))
+    return y
+
+
 def gemv_w4a8_group32(w, s16, bias, qx, sx) -> Tuple[np.ndarray, np.ndarray]:
     """Per-group int32 partials acc_jg and y_j = sx sum_g s_jg acc_jg + b_j."""
     w = _c(w, np.uint32)
@@ -439,6 +453,24 @@ def linear_w4a8(w, sw, bias, x) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.
     qx, sx = quantize_act(x)
     acc, y = gemv_w4a8(w, sw, bias, qx, sx)
     return qx, sx, acc, y
+
+
+def chain_w4a8(linears, x0):
+    """A decoder's chain of per-row W4A8 linears ([Orin] derivation section,
+    one linear after another): linear t quantises its activation, takes the
+    GEMV, and linear t+1's activation is the first K_{t+1} values of linear
+    t's binary32 output (epilogue_f32).  linears: (w, sw, bias) with w the
+    packed [N, K/8] words.  Returns per linear (qx, sx, acc, y64, y32)."""
+    out, x = [], np.asarray(x0, np.float32)
+    for t, (w, sw, b) in enumerate(linears):
+        K = np.asarray(w).shape[1] * 8
+        assert x.size == K, (t, x.size, K)
+        qx, sx, acc, y64 = linear_w4a8(w, sw, b, x)
+        y32 = epilogue_f32(sw, b, sx, acc)
+        out.append((qx, sx, acc, y64, y32))
+        if t + 1 < len(linears):
+            x = y32[:np.asarray(linears[t + 1][0]).shape[1] * 8]
+    return out
 
 
 def linear_w4a8_group32(w, s16, bias, x):

@@ -727,3 +727,88 @@ def test_gemv_int8x_vs_numpy_integer_matmul():
     ref = q.astype(np.int64) @ qx.astype(np.int64)
     assert np.array_equal(acc, ref)
     np.testing.assert_allclose(y, float(np.float32(0.0031)) * float(np.float32(0.0123)) * ref, rtol=1e-15)
+
+
+# ------------------------------------------------ binary32 epilogue, chain --
+def _round_f32(q):
+    """The binary32 value nearest to the rational q, ties to even (normal
+    and subnormal range; no overflow here)."""
+    from fractions import Fraction
+    if q == 0:
+        return np.float32(0.0)
+    neg, q = q < 0, abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()   # 2^e <= q < 2^(e+2)
+    if Fraction(2) ** e > q:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= q:
+        e += 1
+    e = max(e, -126)
+    scale = Fraction(2) ** (e - 23)
+    m = q / scale
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = float(n * scale)                     # representable: exact in binary64 too
+    return np.float32(-v if neg else v)
+
+
+def test_epilogue_f32_is_one_rounding_of_the_exact_value():
+    """y = fl32(s * a + b) with s = fl32(sW sx) and a = fl32(acc): checked bit
+    for bit against the exact rational rounded once; the samples include
+    cases where an unfused multiply-add, an unrounded s, or a dropped bias
+    would give other bits, so each of those mistakes fails here."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    N = 4000
+    sw = (np.abs(rng.standard_normal(N)) * 3e-3 + 1e-5).astype(np.float32)
+    sx = np.float32(0.0213)
+    acc = rng.integers(-(1 << 26), 1 << 26, N).astype(np.int32)
+    acc[:200] = rng.integers(-3000, 3000, 200)
+    b = (rng.standard_normal(N) * 0.01).astype(np.float32)
+    y = O.epilogue_f32(sw, b, sx, acc)
+    y0 = O.epilogue_f32(sw, None, sx, acc)
+    unfused = unrounded = 0
+    for j in range(N):
+        s = np.float32(sw[j]) * sx
+        a = np.float32(acc[j])
+        exact = Fraction(float(s)) * Fraction(float(a)) + Fraction(float(b[j]))
+        ref = _round_f32(exact)
+        assert y[j].view(np.uint32) == ref.view(np.uint32), j
+        assert y0[j].view(np.uint32) == _round_f32(Fraction(float(s)) * Fraction(float(a))).view(np.uint32), j
+        unfused += np.float32(np.float32(s * a) + b[j]) != ref
+        unrounded += _round_f32(Fraction(float(sw[j])) * Fraction(float(sx)) * Fraction(float(a))
+                                + Fraction(float(b[j]))) != ref
+    assert unfused > 0 and unrounded > 0
+    assert (y != y0).any()
+
+
+def test_chain_brute_force_tiny():
+    """The chain's wiring against a brute force in Python: codes from the
+    pinned activation quantiser, acc from numpy's integer matmul of the
+    unpacked codes, y32 the exact rational rounded once, and each linear's
+    activation the first K values of the previous y32."""
+    from fractions import Fraction
+    shapes = [(64, 32), (48, 64), (16, 32)]
+    rng = np.random.default_rng(5)
+    lins = []
+    for N, K in shapes:
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+        w, sw = O.prepare_int4_rowwise(W)
+        b = (rng.standard_normal(N) * 0.01).astype(np.float32) if N != 48 else None
+        lins.append((w, sw, b))
+    x = rng.standard_normal(32).astype(np.float32)
+    out = O.chain_w4a8(lins, x)
+    for t, ((w, sw, b), (N, K)) in enumerate(zip(lins, shapes)):
+        qx, sx = O.quantize_act(x)
+        acc = O.unpack_int4(w).astype(np.int64) @ qx.astype(np.int64)
+        y32 = np.array([_round_f32(Fraction(float(np.float32(sw[j]) * np.float32(sx)))
+                                   * Fraction(float(np.float32(acc[j])))
+                                   + (Fraction(float(b[j])) if b is not None else 0)) for j in range(N)],
+                       dtype=np.float32)
+        oq, osx, oacc, oy64, oy32 = out[t]
+        assert np.array_equal(oq, qx) and np.float32(osx) == np.float32(sx), t
+        assert np.array_equal(oacc.astype(np.int64), acc), t
+        assert np.array_equal(oy32.view(np.uint32), y32.view(np.uint32)), t
+        if t + 1 < len(shapes):
+            x = y32[:shapes[t + 1][1]]
