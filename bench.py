@@ -253,14 +253,42 @@ def cold_call_us(step, dev, reps=5):
     return round(statistics.median(t), 2)
 
 
+def host_facts():
+    """The host the CPU baseline ran on: logical CPUs, the CPUs this process
+    may use, and the CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpus_allowed": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+HOST = {}
+
+
 def cpu_loop(fn, sample_bytes, seconds):
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        fn()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            return sample_bytes * reps / el / 1e9, reps, el
+    """Runs fn repeatedly for about ``seconds`` on one core: the calling
+    thread (which runs the single-threaded C oracle) is pinned to the first
+    CPU it may use, and its previous affinity restored afterwards."""
+    allowed = os.sched_getaffinity(0)
+    core = min(allowed)
+    HOST.update(host_facts(), pinned_core=core)
+    os.sched_setaffinity(0, {core})
+    try:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return sample_bytes * reps / el / 1e9, reps, el
+    finally:
+        os.sched_setaffinity(0, allowed)
 
 
 # ------------------------------------------------------------ workloads ---
@@ -288,48 +316,51 @@ def run_stream(a, dev):
         del src, dst
 
     graph_steps = 1 if ((not a.eager) and a.per_linear) else 0
-    ms, n = time_steps(s.step, a.steps, a.warmup, graph_steps)
     step_bytes = s.bytes_per_step()
-    gbs = step_bytes / (ms * 1e-3) / 1e9
-
     if s.persistent:
-        # One launch per step: the pass kernel carries every byte.  Second
-        # pass of the same K steps with events around each launch.
+        # The decoder's data flow: each linear reads the previous linear's
+        # output (a prefix where the previous linear is wider), so every
+        # linear waits for the one before it.  One launch per step carries
+        # every byte; a second pass of the same K steps with events around
+        # each launch gives the kernel's own duration.
+        cp = s.chained_pass()
+        step = cp.run
+        ms, n = time_steps(step, a.steps, a.warmup, 0)
         evs = []
         for _ in range(a.steps):
             b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             b0.record(st)
-            s.step()
+            step()
             b1.record(st)
             evs.append((b0, b1))
         torch.cuda.synchronize()
-        err = s.pass_.error_word()
-        if err:
-            raise RuntimeError(f"decode pass reported a wait time-out (error word {err})")
-        dur_us = [b0.elapsed_time(b1) * 1e3 for b0, b1 in evs]
-        avg_us, avg_bytes = sum(dur_us) / len(dur_us), step_bytes
-        kernel = f"k_decode_pass (persistent: whole token pass, {len(s.linears)} linears, one launch)"
-        traffic = measured_traffic() if layers == 28 else None
-        # The same linears chained (each reads the previous output, as a
-        # decoder that reuses buffers would): coherent activation reads.
-        cp = s.chained_pass()
-        cms, _ = time_steps(lambda: cp.run(), a.steps, a.warmup, 0)
         if cp.error_word():
             raise RuntimeError(f"chained pass reported a wait time-out (error word {cp.error_word()})")
-        chained = {"ms_per_step": round(cms, 5), "GB/s": round(step_bytes / (cms * 1e-3) / 1e9, 1),
-                   "tok_per_s": round(1e3 / cms, 2),
-                   "note": "linear i reads the first K_i outputs of linear i-1 (device-scope activation loads)"}
-        del cp
-        # The synchronisation floor: the same linears cut to 64 rows each.
-        fp = s.sync_floor_pass(64)
-        fms, _ = time_steps(lambda: fp.run(), a.steps, a.warmup, 0)
+        dur_us = [b0.elapsed_time(b1) * 1e3 for b0, b1 in evs]
+        avg_us, avg_bytes = sum(dur_us) / len(dur_us), step_bytes
+        kernel = f"k_decode_pass (persistent: whole token pass, {len(s.linears)} chained linears, one launch)"
+        traffic = measured_traffic() if layers == 28 else None
+        # The same linears with independent activations written before the
+        # launch: nothing to wait for, the pass streams (an upper bound).
+        ims, _ = time_steps(s.step, a.steps, a.warmup, 0)
+        if s.pass_.error_word():
+            raise RuntimeError(f"independent pass reported an error (error word {s.pass_.error_word()})")
+        independent = {"ms_per_step": round(ims, 5), "GB/s": round(step_bytes / (ims * 1e-3) / 1e9, 1),
+                       "tok_per_s": round(1e3 / ims, 2),
+                       "note": "the same linears, each with its own activation written before the launch: "
+                               "no dependency between linears"}
+        # The dependency alone: as many chained linears, [64, 64] each.
+        fp = s.link_floor_pass(64)
+        fms, _ = time_steps(fp.run, a.steps, a.warmup, 0)
         if fp.error_word():
-            raise RuntimeError(f"sync-floor pass reported a wait time-out (error word {fp.error_word()})")
-        sync_floor = {"ms_per_step": round(fms, 5), "us_per_linear": round(fms * 1e3 / len(s.linears), 3),
-                      "note": "the same linears cut to 64 rows each: waits, activation staging and output "
-                              "stores with almost no weight traffic"}
+            raise RuntimeError(f"link-floor pass reported a wait time-out (error word {fp.error_word()})")
+        link_floor = {"ms_per_step": round(fms, 5), "us_per_linear": round(fms * 1e3 / len(s.linears), 3),
+                      "note": f"{len(s.linears)} chained [64, 64] linears: output store, poll, activation "
+                              "staging and a few rows per dependency, next to no weight traffic"}
         del fp
     else:
+        step = s.step
+        ms, n = time_steps(step, a.steps, a.warmup, graph_steps)
         # Dominant kernel: the gate/up linears + lm_head (most of the bytes),
         # each launch bracketed by events in a second eager pass.
         dom = [i for i, d in enumerate(s.linears) if d["name"] in ("gate_up", "lm_head")]
@@ -351,21 +382,25 @@ def run_stream(a, dev):
         avg_us, avg_bytes = sum(dur_us) / len(dur_us), sum(dom_bytes) / len(dom_bytes)
         kernel = "k_gemv_w4a8 (fused gate/up linears and lm_head, one launch per linear)"
         traffic = None
+    gbs = step_bytes / (ms * 1e-3) / 1e9
     achieved = avg_bytes / (avg_us * 1e-6) / 1e9
     launch = "persistent pass" if s.persistent else ("per-linear, HIP graph" if graph_steps else "per-linear")
+    flow = ("chained: linear i reads linear i-1's output" if s.persistent
+            else "each linear's activation written before the step")
     out = base_line(a, gbs, ms, n, {
         "workload": f"qwen2-7b-shaped {layers}-layer W4A8 decode weight stream + int4 lm_head "
                     "(per-row scales, fused QKV and gate/up, fused act-quant)",
+        "activations": flow,
         "launch": launch, "layers": layers, "hidden": 3584, "kv_dim": 512, "intermediate": 18944,
         "vocab": 152064, "global_batch": 1, "parallelism": "none",
         "bytes_per_step": step_bytes, "packed_weight_bytes": s.weight_bytes()})
     out["tok_per_s"] = round(1e3 / ms, 2)
     out["us_per_gemv"] = round(ms * 1e3 / len(s.linears), 3)
-    out["ms_per_step_spread"] = repeat_spread(s.step, max(1, a.steps // 5))
+    out["ms_per_step_spread"] = repeat_spread(step, max(1, a.steps // 5))
     out["roofline"] = roofline(achieved, kernel, avg_us, avg_bytes, traffic)
     if s.persistent:
-        out["chained"] = chained
-        out["sync_floor"] = sync_floor
+        out["independent"] = independent
+        out["link_floor"] = link_floor
     ceil = read_ceiling(dev)
     out["read_ceiling"] = ceil
     out["pct_of_read_ceiling"] = round(100.0 * gbs / ceil["GB/s"], 2)
@@ -419,7 +454,7 @@ def cpu_baseline_stream(stream, seconds):
         for w, s, b, x, _ in work:
             O.linear_w4a8(w, s, b, x)
     gbs, reps, el = cpu_loop(once, sample_bytes, seconds)
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": dict(HOST),
             "sample": f"layer 0 of the stream (fused QKV, O, gate/up, down: {sample_bytes} algorithmic bytes), "
                       f"{reps} passes in {el:.1f} s, single-threaded C; implied tok/s over the full "
                       f"stream {gbs * 1e9 / stream.bytes_per_step():.4f}"}
@@ -459,7 +494,7 @@ def run_single(a, dev):
         wq, sw = O.prepare_int4_rowwise(d["W"].numpy())
         x, b = d["x"].numpy(), d["b"].numpy()
         g, reps, el = cpu_loop(lambda: O.linear_w4a8(wq, sw, b, x), w.bytes_per_step(), a.cpu_seconds)
-        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": dict(HOST),
                                "sample": f"the same linear, {reps} calls in {el:.1f} s, single-threaded C"}
     return out
 
@@ -497,7 +532,7 @@ def run_layer(a, dev):
             del W
             work.append((wq, sw, e["b"].cpu().numpy(), e["x"].cpu().numpy()))
         g, reps, el = cpu_loop(lambda: [O.linear_w4a8(*t) for t in work], w.bytes_per_step(), a.cpu_seconds)
-        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": dict(HOST),
                                "sample": f"the same layer, {reps} passes in {el:.1f} s, single-threaded C"}
     return out
 
@@ -543,7 +578,7 @@ def run_gemma(a, dev):
             work.append((wq, s16, None, d["x"].cpu().numpy()))
         sample = sum(WL.bytes_group32_linear(d["N"], d["K"], False) for d in w.linears[:4])
         g, reps, el = cpu_loop(lambda: [O.linear_w4a8_group32(*t) for t in work], sample, a.cpu_seconds)
-        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": dict(HOST),
                                "sample": f"layer 0 of the stream (4 group-32 linears, {sample} B), {reps} "
                                          f"passes in {el:.1f} s, single-threaded C"}
     return out
@@ -604,7 +639,7 @@ def run_verify(a, dev):
         X = I.normal(f"verify/{N}x{K}/X", (M, K), 1.0, 0, dev).cpu().numpy()
         qx, sx = O.quantize_act(X)
         g, reps, el = cpu_loop(lambda: O.gemm_w4a8_verify(wq, sw, b, qx, sx), wl_bytes, a.cpu_seconds)
-        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        out["cpu_baseline"] = {"value": round(g, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": dict(HOST),
                                "sample": f"verify [18944,3584] at M={M}, {reps} calls in {el:.1f} s, "
                                          "single-threaded C"}
     return out
@@ -719,7 +754,7 @@ def cpu_baseline_chain(c, seconds):
         qd, sd, _ = O.swiglu_quant(ygu.astype("float32"))
         O.gemv_w4a8(*prep["down"][:2], prep["down"][2], qd, float(sd))
     gbs, reps, el = cpu_loop(once, sample, seconds)
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": dict(HOST),
             "sample": f"layer 0 of the chain (~{sample} algorithmic bytes, a layer's share of the step), "
                       f"{reps} passes in {el:.1f} s, single-threaded C"}
 

@@ -34,7 +34,7 @@ ENTRY_POINTS = (
     "quantize_weights_int8_group32", "pack_int4_rows_host", "unpack_int4_rows_host",
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
-    "decode_pass_desc_bytes", "decode_pass_sync_bytes", "decode_pass_encode", "decode_pass_w4a8",
+    "decode_pass_desc_bytes", "decode_pass_encode", "decode_pass_w4a8",
     "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant", "linear_rmsnorm_w4a8",
     "quantize_weights_q6k", "gemv_q6k_f16", "int8x_counts_host", "int8x_stream_bytes_host",
     "int8x_encode_host", "gemv_int8x",
@@ -85,9 +85,9 @@ def lib() -> C.CDLL:
         "gemm_w4a8_verify": (I, [P, P, P, P, P, P, P, I, I, I, I, P]),
         "layer_w4a8_forward": (I, [C.POINTER(LinearW4A8), I, P, I, P, P]),
         "decode_pass_desc_bytes": (C.c_size_t, [I]),
-        "decode_pass_sync_bytes": (C.c_size_t, [I]),
-        "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32)]),
-        "decode_pass_w4a8": (I, [P, I, I, P, I, P]),
+        "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32),
+                                   C.POINTER(C.c_size_t)]),
+        "decode_pass_w4a8": (I, [P, I, I, P, C.c_size_t, I, P]),
         "read_probe": (I, [P, C.c_size_t, P, I, I, P]),
         "gemv_w4a16": (I, [P, P, P, P, P, I, I, I, I, P]),
         "add_rmsnorm_quant": (I, [P, P, P, C.c_float, P, P, P, P, I, I, P]),
@@ -584,7 +584,8 @@ def layer_w4a8_forward(linears: Sequence[LinearW4A8], xs: Sequence[torch.Tensor]
 class DecodePass:
     """One persistent launch per decode step over ``linears`` in order
     (decode_pass_w4a8).  Encodes the descriptors once on the host, keeps a
-    device copy and the zero-initialised synchronisation words."""
+    device copy and the zero-initialised workspace (error word, epoch words
+    and the exchange through which linears read earlier outputs)."""
 
     def __init__(self, linears: Sequence[LinearW4A8], xs: Sequence[torch.Tensor],
                  ys: Sequence[torch.Tensor], device=None):
@@ -603,16 +604,18 @@ class DecodePass:
         nbytes = lib().decode_pass_desc_bytes(n)
         host = (C.c_uint8 * nbytes)()
         mk = C.c_int32(0)
+        sb = C.c_size_t(0)
         _call("decode_pass_encode", lin, n, C.cast(xp, C.c_void_p), BQD_F32 if dt == torch.float32 else BQD_F16,
-              C.cast(yp, C.c_void_p), C.cast(host, C.c_void_p), nbytes, C.byref(mk))
+              C.cast(yp, C.c_void_p), C.cast(host, C.c_void_p), nbytes, C.byref(mk), C.byref(sb))
         self.max_k = mk.value
+        self.sync_bytes = sb.value
         self.desc = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device)
-        self.sync = torch.zeros(lib().decode_pass_sync_bytes(n) // 4, dtype=torch.int32, device=device)
+        self.sync = torch.zeros(self.sync_bytes // 4, dtype=torch.int32, device=device)
         self._keep = (list(xs), list(ys), list(linears))
 
     def run(self, stream=None, spin_limit: int = 0) -> None:
         _call("decode_pass_w4a8", self.desc.data_ptr(), self.n, self.max_k, self.sync.data_ptr(),
-              spin_limit, _stream(stream))
+              self.sync_bytes, spin_limit, _stream(stream))
 
     def error_word(self) -> int:
         """Bit 0: a wait ran out of spins; bit 1: descriptors for another
@@ -621,6 +624,17 @@ class DecodePass:
 
     def clear_error(self) -> None:
         self.sync[0].zero_()
+
+    def sources(self) -> List[int]:
+        """Per linear, the exchange word its activation starts at (>= 0: the
+        activation is an earlier output of the pass), or -1 (written before
+        the launch); read back from the encoded descriptors."""
+        raw = self.desc.cpu().numpy().tobytes()
+        return [int.from_bytes(raw[DESC_HEADER + DESC_TASK * i + 76:DESC_HEADER + DESC_TASK * i + 80], "little",
+                               signed=True) for i in range(self.n)]
+
+
+DESC_HEADER, DESC_TASK = 16, 88   # bytes of the descriptor header and of one linear's descriptor
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int, unroll: int = 1, stream=None) -> None:

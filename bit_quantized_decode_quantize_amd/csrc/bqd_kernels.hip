@@ -31,6 +31,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "bqd.h"
 
@@ -1839,35 +1840,47 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 
 // ------------------------------------------------------------------------
 // Persistent token pass: every linear of a decode step in one cooperative
-// launch, one 1024-thread workgroup per CU.  Linear t reads its activation
-// only after every workgroup has finished linear t-1: each workgroup writes
-// its output rows with device-coherent stores, waits for them to complete,
-// and then adds one to a completion counter of t-1 (workgroup w to counter
-// w % 64); waiters read the 64 counters of t-1 (one wave, one per lane) and
-// vote.  That is the data dependency of a decoder, where each GEMV's input
-// derives from the previous GEMV's output.  The weights depend on nothing,
-// so right after counting a linear done the worker waves issue the loads of
-// the first step of their share of the next one; they stream from HBM while
-// the control waves wait and quantise the next activation.
+// launch, one 1024-thread workgroup per CU.
+//
+// Dependencies travel with the data.  When linear t reads an output of an
+// earlier linear k of the same pass (a decoder's chain: each GEMV's input is
+// derived from the previous GEMV's output), it does not read k's output
+// buffer: every row k's workgroups compute is also stored into an exchange
+// array in the synchronisation workspace, as the bitwise NOT of its fp32
+// bits, with a relaxed device-scope atomic store, and an exchange word holds
+// 0 until its row has been written in this pass.  Linear t's workgroups load
+// the words of their activation with device-scope loads and load again the
+// ones still 0.  Each word is an atomic object that carries its own value,
+// so nothing relies on the order in which stores to different locations
+// become visible: no fences, no store-completion waits, no counters.  The
+// chain from a writer's store to a reader's use is one store and one load.
+// Two exchange sets alternate between passes (epoch parity): the writer of a
+// row also stores 0 to that row in the other set, which the previous pass
+// used and this pass never reads, so a set is all zero when its pass starts
+// (consecutive passes are ordered by the kernel boundary).  An activation
+// written before the launch is read through the caches, with no wait.
+//
+// The weights depend on nothing, so when a workgroup finishes its share of
+// a linear its worker waves issue the loads of the first step of their
+// share of the next one; they stream from HBM while the activation is
+// awaited and quantised.
 //   Work split: workgroup w owns a contiguous, balanced range of rows of
 //   every linear; its lane groups (2^lshift lanes per row, r rows per group)
 //   take the range in batches; a lane streams its rows in steps of 8
 //   16-byte chunks, double-buffered in registers.  Shapes are chosen and
 //   encoded on the host for the grid the launch uses (checked in the kernel).
-//   An activation that an earlier linear of the pass wrote (flagged on the
-//   host: x_in_pass) is read with device-scope loads; see stage_max.
-//   Sync words (each on a 64-byte line of its own): err[0]; epoch[w] at
-//   16 + 16 w (w < 1024); counter k of linear t at 16 + 16 (1024 + 64 t + k).
-//   Every workgroup adds one to one counter of every linear and writes its
-//   epoch word once per pass, so between passes all epoch words hold the
-//   same value e, counter k holds e times its number of workgroups, and a
-//   pass waits for e + 1 times that (compared modulo 2^32).  A wait that
-//   exceeds its spin limit sets err bit 0 and proceeds, so every wave always
-//   reaches the end of the kernel; descriptors for another grid or another
-//   n set bit 1 and the kernel returns at once.
+//   Workspace (32-bit words): err at 0; epoch[w] at 64 + 16 w (w < 1024,
+//   one 64-byte line each); exchange set s at kXchBase + s * xch_words.
+//   Each workgroup writes its epoch word once per pass, so all of them hold
+//   the same value e between passes; a pass runs as epoch e + 1 and uses
+//   exchange set (e + 1) & 1.  A wait that exceeds its spin limit sets err
+//   bit 0 and proceeds, so every wave always reaches the end of the kernel;
+//   descriptors for another grid or another n set bit 1 and the kernel
+//   returns at once, as do descriptors whose exchange does not fit the
+//   workspace the launch was given.
 // ------------------------------------------------------------------------
 struct PassHeader {
-    int32_t n, grid, max_k, reserved;
+    int32_t n, grid, max_k, xch_words;  // xch_words: 32-bit words per exchange set
 };
 static_assert(sizeof(PassHeader) == 16, "descriptor header layout");
 
@@ -1875,42 +1888,39 @@ struct PassTask {
     const u32x4* wq;
     const float* sw;
     const float* bias;
-    const void* x;
+    const void* x;                  // activation written before the launch (xin < 0)
     float* y;
     int32_t N, C;                   // rows; 16-byte chunks per row (K / 32)
     int32_t rows_base, rows_extra;  // workgroup w owns rows_base + (w < rows_extra) rows
     int32_t lshift, r;              // 2^lshift lanes per row; r rows per lane group
     int32_t iters, batches;         // chunk iterations per row per lane; row batches
     int32_t steps;                  // pipeline steps per batch
-    int16_t x_dtype;                // X_F32 or X_F16
-    int16_t x_in_pass;              // 1: an earlier linear of the pass writes x
+    int32_t xin;                    // exchange word of x[0] (x is an output of the pass), or -1
+    int32_t xout;                   // exchange word of y[0] (a later linear reads y), or -1
+    int16_t x_dtype;                // X_F32 or X_F16 (xin < 0)
+    int16_t reserved;
 };
-static_assert(sizeof(PassTask) == 80, "descriptor layout");
+static_assert(sizeof(PassTask) == 88, "descriptor layout");
 
 constexpr int kPassThreads = 1024;    // 16 waves: one workgroup per CU
-// Waves 0..11 stream weights; waves 12..15 poll, stage the activation and
-// signal.  The control waves never hold weight loads: vmcnt completes in
-// order, so a poll or activation load issued behind a wave's own prefetch
-// could not be used until that prefetch had landed.
+// Waves 0..11 stream weights; waves 12..15 stage the activation.  The
+// staging waves never hold weight loads: vmcnt completes in order, so an
+// activation load issued behind a wave's own prefetch could not be used
+// until that prefetch had landed.
 constexpr int kPassWorkers = 768;
 constexpr int kPassControl = kPassThreads - kPassWorkers;
 constexpr int kPassSlots = 8;         // 16-byte chunks per lane per pipeline step
 constexpr int kPassMaxGrid = 1024;
-// Words from one sync word to the next: each has a 64-byte line of its own.
-// Sync words of workgroups on different XCDs sharing a line cost 3 % of the
-// pass (measured with one completion flag per workgroup: 1.194 -> 1.158 ms
-// per token with this stride).
-constexpr int kSyncStride = 16;
-// Completion counters per linear.  One counter serialises 256 device-scope
-// atomics at one address (1.575 ms per token); one flag per workgroup makes
-// every waiter load 256 words per poll (1.165 ms); 8 / 32 / 64 / 128
-// counters: 1.148 / 1.114-1.148 / 1.112 / 1.144 ms.  64 is one load per lane
-// of the polling wave and 4 atomics per address.
-constexpr int kPassCounters = 64;
 constexpr int kPassSpinLimit = 1 << 21;
 constexpr int kPassWgPerCu = 1;
 constexpr int kPassMaxK = BQD_MAX_PASS_K;  // LDS: codes (K bytes) + fp32 activation (4K bytes)
 static_assert(5 * kPassMaxK <= 160 * 1024, "pass activation must fit LDS");
+// Workspace layout (32-bit words).
+constexpr int kEpochBase = 64;        // after err's 256-byte line
+constexpr int kSyncStride = 16;       // one 64-byte line per epoch word
+constexpr int kXchBase = kEpochBase + kPassMaxGrid * kSyncStride;  // 16448 words = 65792 bytes
+// 8-value groups a staging thread loads at once (all issued before the first use).
+constexpr int kStageGroups = 4;
 
 inline size_t pass_lds_bytes(int max_k) { return (size_t)((max_k + 15) & ~15) + 4 * (size_t)max_k; }
 
@@ -1963,10 +1973,14 @@ __device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], float& esw, 
 }
 
 // One linear's share of this workgroup: batches of rows, each streamed in
-// steps with the next step's loads in flight during the current step.
+// steps with the next step's loads in flight during the current step.  Each
+// row's y goes to the output buffer and, when a later linear of the pass
+// reads it, to the exchange (xcur) as ~bits, with the same row of the other
+// set (xold) cleared for the next pass.
 template <int R>
 __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, float& eb, bool have_cur,
-                                         const PassTask& t, int row_start, int rows, const u32x4* xs, float sx)
+                                         const PassTask& t, int row_start, int rows, const u32x4* xs, float sx,
+                                         uint32_t* xcur, uint32_t* xold)
 {
     constexpr int U = kPassSlots / R;
     const int L = 1 << t.lshift;
@@ -2021,9 +2035,15 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
                 v += __shfl_xor(v, 32);
             const int rl = (b * groups + grp) * R + rr;
             if (lane == rr && rl < rows) {
-                // device-coherent store: visible to every XCD once complete
-                __hip_atomic_store(gptr_mut(t.y) + row_start + rl, fmaf(esw * sx, (float)v, eb),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const float yv = fmaf(esw * sx, (float)v, eb);
+                const int row = row_start + rl;
+                gptr_mut(t.y)[row] = yv;
+                if (t.xout >= 0) {
+                    __hip_atomic_store(gptr_mut(xcur) + t.xout + row, ~__builtin_bit_cast(uint32_t, yv),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(gptr_mut(xold) + t.xout + row, 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
         esw = nsw;
@@ -2031,66 +2051,122 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
     }
 }
 
-// Activation staging in two phases around a workgroup barrier, by `nst`
-// threads (index st): phase 1 reads x once from memory, keeps it as fp32 in
-// LDS (xf, fp16 widened exactly) and reduces max |x| per wave; phase 2 reads
-// xf back from LDS and writes the permuted codes.
+// Activation staging, phase 1, by `nst` threads (index st): x is read once
+// from memory into LDS as fp32 (xf; fp16 widens exactly) and max |x| is
+// reduced per thread.  Each thread loads up to kStageGroups of its 8-value
+// groups at once.
 //
-// An activation that an earlier linear of the same pass wrote (x_in_pass)
-// comes from workgroups on other XCDs, whose caches are not coherent with
-// this one's, and a buffer the decoder reuses may still have old lines in
-// this CU's L1 or this XCD's L2.  Such an x is read with device-scope loads
-// (sc1), coherent with the writers' device-scope stores, which completed
-// before their count.  (An acquire fence would invalidate both caches
-// instead: 1.1 us per linear, against a few tens of ns for these loads.)
-// Any other x was written before the launch and is read through the caches.
+// From the exchange (XCH): words of rows not yet written in this pass are 0;
+// they are loaded again (device scope, sc1: coherent with the writers'
+// device-scope stores on every XCD, where a plain load could be served a
+// stale line by this CU's L1 or this XCD's L2) until none is left.  A word
+// is a relaxed atomic load: every 32-bit word of an aligned 16-byte load is
+// read single-copy atomically.  After spin_limit rounds the wait gives up,
+// sets err bit 0 and takes the words as they are; so does every wait of a
+// workgroup that finds bit 0 already set.
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kDeviceScope = 16;          // buffer-load cache-policy bit sc1
 
-template <int XIN>
-__device__ __forceinline__ void load8_device(__amdgpu_buffer_rsrc_t r, int g, float v[8])
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes)
 {
-    constexpr int kDeviceScope = 16;  // cache-policy bit sc1
-    if constexpr (XIN == X_F32) {
-        const f32x4 a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g, 0, kDeviceScope));
-        const f32x4 b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g + 16, 0, kDeviceScope));
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-        const u32x4 h = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * g, 0, kDeviceScope));
-        const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+    // the address is wave-uniform: keep the resource in scalar registers
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ bool written8(u32x4 a, u32x4 b)
+{
+    return a.x && a.y && a.z && a.w && b.x && b.y && b.z && b.w;
+}
+
+template <int XIN, bool XCH>
+__device__ __forceinline__ float stage_load(const void* x, f32x4* xf, int G8, int st, int nst, uint32_t* err,
+                                            int spin_limit)
+{
+    constexpr int kGroupBytes = XIN == X_F16 ? 16 : 32;
+    const __amdgpu_buffer_rsrc_t r = uniform_rsrc(x, G8 * kGroupBytes);
+    float amax = 0.0f;
+    for (int g0 = st; g0 < G8; g0 += kStageGroups * nst) {
+        u32x4 v[kStageGroups][2];
+        uint32_t todo = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[k] & 0xFFFFu));
-            v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[k] >> 16));
+        for (int k = 0; k < kStageGroups; ++k) {
+            const int g = g0 + k * nst;
+            v[k][0] = v[k][1] = u32x4{0u, 0u, 0u, 0u};
+            if (g < G8) {
+                todo |= 1u << k;
+                if constexpr (XCH) {
+                    v[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g, 0, kDeviceScope));
+                    v[k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g + 16, 0, kDeviceScope));
+                } else if constexpr (XIN == X_F32) {
+                    v[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g, 0, 0));
+                    v[k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g + 16, 0, 0));
+                } else {
+                    v[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * g, 0, 0));
+                }
+            }
+        }
+        if constexpr (XCH) {
+            int spins = 0;
+            while (true) {
+                uint32_t left = 0;
+#pragma unroll
+                for (int k = 0; k < kStageGroups; ++k)
+                    if (((todo >> k) & 1u) && !written8(v[k][0], v[k][1]))
+                        left |= 1u << k;
+                if (!left)
+                    break;
+                ++spins;
+                if (spins >= spin_limit ||
+                    ((spins & 255) == 0 && (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u))) {
+                    __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                for (int k = 0; k < kStageGroups; ++k) {
+                    if ((left >> k) & 1u) {
+                        const int g = g0 + k * nst;
+                        v[k][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g, 0, kDeviceScope));
+                        v[k][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * g + 16, 0, kDeviceScope));
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kStageGroups; ++k) {
+            if ((todo >> k) & 1u) {
+                const int g = g0 + k * nst;
+                float u[8];
+                if constexpr (XIN == X_F32) {
+                    // whole-vector casts: a bit cast of one ext-vector
+                    // element (a.y) was compiled as a read of element 0
+                    const f32x4 a = __builtin_bit_cast(f32x4, XCH ? ~v[k][0] : v[k][0]);
+                    const f32x4 b = __builtin_bit_cast(f32x4, XCH ? ~v[k][1] : v[k][1]);
+                    u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
+                    u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
+                } else {
+                    const uint32_t hw[4] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        u[2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[e] & 0xFFFFu));
+                        u[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(hw[e] >> 16));
+                    }
+                }
+                xf[2 * g] = f32x4{u[0], u[1], u[2], u[3]};
+                xf[2 * g + 1] = f32x4{u[4], u[5], u[6], u[7]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    amax = fmaxf(amax, fabsf(u[e]));
+            }
         }
     }
+    return amax;
 }
 
-template <int XIN, bool IN_PASS>
-__device__ __forceinline__ float stage_max(const void* x, f32x4* xf, int G8, int st, int nst)
-{
-    // the descriptor is wave-uniform: keep the resource in scalar registers
-    const uint64_t xa = reinterpret_cast<uint64_t>(x);
-    const uint64_t xu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(xa >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)xa);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(xu), (short)0, G8 * (XIN == X_F32 ? 32 : 16), kBufferWord3);
-    float amax = 0.0f;
-    for (int g = st; g < G8; g += nst) {
-        float u[8];
-        if constexpr (IN_PASS)
-            load8_device<XIN>(r, g, u);
-        else
-            load8<XIN>(x, g, u);
-        xf[2 * g] = f32x4{u[0], u[1], u[2], u[3]};
-        xf[2 * g + 1] = f32x4{u[4], u[5], u[6], u[7]};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            amax = fmaxf(amax, fabsf(u[e]));
-    }
-    return wave_max(amax);
-}
-
+// Phase 2: the permuted codes from the fp32 values in LDS.
 __device__ __forceinline__ void stage_codes(u32x2* xs, const f32x4* xf, int G8, int st, int nst,
                                             const ActScale& a)
 {
@@ -2104,7 +2180,7 @@ __device__ __forceinline__ void stage_codes(u32x2* xs, const f32x4* xf, int G8, 
 }
 
 // Above this many 8-value groups (K > 8192) every wave stages; below, only
-// the control waves, which hold no weight loads.
+// the staging waves, which hold no weight loads.
 constexpr int kPassStageAllAbove = 1024;
 
 template <int R>
@@ -2120,7 +2196,7 @@ __device__ __forceinline__ void pass_prefetch(u32x4 (&cur)[kPassSlots], float& e
 __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* __restrict__ hdr,
                                                               const PassTask* __restrict__ tasks, int n_launch,
                                                               int max_k_launch, uint32_t* __restrict__ sync,
-                                                              int spin_limit)
+                                                              size_t sync_words, int spin_limit)
 {
     extern __shared__ u32x4 xs[];  // codes: max_k bytes, then fp32 x at xf_offset
     const int xf_offset = (hdr->max_k + 15) & ~15;
@@ -2131,11 +2207,11 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     const int w = blockIdx.x;
     const int tid = threadIdx.x;
     const bool worker = tid < kPassWorkers;  // uniform per wave
-    const int ct = tid - kPassWorkers;       // control-thread index (>= 0 on control waves)
+    const int ct = tid - kPassWorkers;       // staging-thread index (>= 0 on the staging waves)
     uint32_t* err = sync;
-    uint32_t* epochs = sync + 16;                                // epochs[w * kSyncStride]
-    uint32_t* counts = sync + 16 + kPassMaxGrid * kSyncStride;  // counts[(ti * kPassCounters + k) * kSyncStride]
-    if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || G > kPassMaxGrid) {
+    uint32_t* epochs = sync + kEpochBase;    // epochs[w * kSyncStride]
+    if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || G > kPassMaxGrid ||
+        (size_t)kXchBase + 2 * (size_t)(uint32_t)hdr->xch_words > sync_words) {
         // uniform: every workgroup leaves
         if (tid == 0 && w == 0)
             __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2147,6 +2223,9 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         s_epoch = __hip_atomic_load(&epochs[(size_t)w * kSyncStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     __syncthreads();
     const uint32_t epoch = s_epoch;
+    const size_t xw = (size_t)(uint32_t)hdr->xch_words;
+    uint32_t* xcur = sync + kXchBase + (epoch & 1u) * xw;
+    uint32_t* xold = sync + kXchBase + ((epoch & 1u) ^ 1u) * xw;
 
     u32x4 cur[kPassSlots];
     float esw = 0.0f, eb = 0.0f;  // first batch's epilogue operands, loaded with cur
@@ -2163,50 +2242,27 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
             have_cur = true;
         }
     }
+    f32x4* xf = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(xs) + xf_offset);
     for (int ti = 0; ti < n; ++ti) {
         const PassTask tn = tasks[ti + 1 < n ? ti + 1 : ti];
-        // 1. wait until every workgroup has counted linear ti-1 done: the
-        //    first control wave reads the counters and votes.
-        if (ti > 0 && ct >= 0 && ct < kWave) {
-            const uint32_t* c = counts + (size_t)(ti - 1) * kPassCounters * kSyncStride;
-            int spins = 0;
-            while (true) {
-                bool done = true;
-#pragma unroll
-                for (int k = ct; k < kPassCounters; k += kWave) {
-                    const uint32_t target = epoch * (uint32_t)(G / kPassCounters + (k < G % kPassCounters ? 1 : 0));
-                    done &= (int32_t)(__hip_atomic_load(&c[(size_t)k * kSyncStride], __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT) - target) >= 0;
-                }
-                if (__all(done))
-                    break;
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins >= spin_limit ||
-                    ((spins & 255) == 0 && (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u))) {
-                    if (ct == 0)
-                        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-            }
-        }
-        __syncthreads();
         int row_start, rows;
         pass_range(t, w, row_start, rows);
         const int G8 = 4 * t.C;
         float* rd = red[ti & 1];
-        // 2. max |x| (control waves; every wave for long activations)
+        // 1. the activation into LDS (fp32) and max |x|: staging waves, or
+        //    every wave for long activations
         const bool all_stage = G8 > kPassStageAllAbove;
         const int st = all_stage ? tid : ct;
         const int nst = all_stage ? kPassThreads : kPassControl;
-        f32x4* xf = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(xs) + xf_offset);
         if (rows > 0 && st >= 0) {
             float m;
-            if (t.x_in_pass)
-                m = t.x_dtype == X_F16 ? stage_max<X_F16, true>(t.x, xf, G8, st, nst)
-                                       : stage_max<X_F32, true>(t.x, xf, G8, st, nst);
+            if (t.xin >= 0)
+                m = stage_load<X_F32, true>(xcur + t.xin, xf, G8, st, nst, err, spin_limit);
+            else if (t.x_dtype == X_F16)
+                m = stage_load<X_F16, false>(t.x, xf, G8, st, nst, err, spin_limit);
             else
-                m = t.x_dtype == X_F16 ? stage_max<X_F16, false>(t.x, xf, G8, st, nst)
-                                       : stage_max<X_F32, false>(t.x, xf, G8, st, nst);
+                m = stage_load<X_F32, false>(t.x, xf, G8, st, nst, err, spin_limit);
+            m = wave_max(m);
             if ((st & (kWave - 1)) == 0)
                 rd[st / kWave] = m;
         }
@@ -2216,24 +2272,18 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         for (int i = 1; i < nw; ++i)
             amax = fmaxf(amax, rd[i]);
         const ActScale a = act_scale(amax);
-        // 3. codes into LDS
+        // 2. codes into LDS
         if (rows > 0 && st >= 0)
             stage_codes(reinterpret_cast<u32x2*>(xs), xf, G8, st, nst, a);
         __syncthreads();
-        // 4. workers: stream the weights, write the rows, wait for the stores
+        // 3. workers: stream the weights, write the rows
         if (rows > 0 && worker) {
             if (t.r == 2)
-                pass_run<2>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s);
+                pass_run<2>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
             else
-                pass_run<1>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s);
+                pass_run<1>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
         }
-        if (worker)
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        // 5. count linear ti done for this workgroup; workers prefetch ti+1
-        if (ct == 0)
-            __hip_atomic_fetch_add(&counts[((size_t)ti * kPassCounters + w % kPassCounters) * kSyncStride], 1u,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // 4. workers prefetch ti+1
         have_cur = false;
         if (worker && ti + 1 < n) {
             int rs, rw;
@@ -2246,9 +2296,13 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
                 have_cur = true;
             }
         }
+        // The next activation is staged after this workgroup's share of ti:
+        // its LDS is free, and the staging waves poll only once the
+        // workgroup has nothing else to do.
+        __syncthreads();
         t = tn;
     }
-    if (ct == 0)
+    if (tid == 0)
         __hip_atomic_store(&epochs[(size_t)w * kSyncStride], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -3277,11 +3331,6 @@ size_t decode_pass_desc_bytes(int32_t n)
     return n > 0 ? sizeof(PassHeader) + (size_t)n * sizeof(PassTask) : 0;
 }
 
-size_t decode_pass_sync_bytes(int32_t n)
-{
-    return n > 0 ? (16 + ((size_t)kPassMaxGrid + (size_t)n * kPassCounters) * kSyncStride) * sizeof(uint32_t) : 0;
-}
-
 // Grid of the pass on the current device: co-resident workgroups, at most
 // kPassWgPerCu per CU, for a given activation staging size.
 static int pass_grid(int max_k, int* grid)
@@ -3323,18 +3372,25 @@ static void pass_shape_host(int N, int C, int G, PassTask& t)
     t.rows_extra = N % G;
 }
 
+static bool contains(const void* outer, size_t no, const void* inner, size_t ni)
+{
+    const uintptr_t a = (uintptr_t)outer, b = (uintptr_t)inner;
+    return b >= a && b + ni <= a + no;
+}
+
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
-                       float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k)
+                       float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k, size_t* sync_bytes)
 {
     if (n <= 0 || n > BQD_MAX_PASS_LINEARS)
         return BQD_ERR_SHAPE;
-    if (!lin || !x || !y || !desc_host || !max_k)
+    if (!lin || !x || !y || !desc_host || !max_k || !sync_bytes)
         return BQD_ERR_NULL;
     int rc = check_x_dtype(x_dtype);
     if (rc)
         return rc;
     if (desc_bytes < decode_pass_desc_bytes(n))
         return BQD_ERR_SHAPE;
+    const size_t xe = x_dtype == BQD_F32 ? 4 : 2;
     int kmax = 0;
     for (int i = 0; i < n; ++i) {
         const bqd_linear_w4a8& l = lin[i];
@@ -3353,23 +3409,64 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
             return BQD_ERR_CONFIG;  // the pass chooses its own work split
         if (l.K > kPassMaxK)
             return BQD_ERR_BOUND;
-        // a linear's workgroups write y while others still read x
-        if (bytes_overlap(x[i], (size_t)l.K * (x_dtype == BQD_F32 ? 4 : 2), y[i], (size_t)l.N * 4))
-            return BQD_ERR_SHAPE;
         kmax = l.K > kmax ? l.K : kmax;
     }
-    // Weights, scales and biases are read (and prefetched before the wait)
-    // through the caches: no output of the pass may overwrite them.
+    // Outputs are disjoint, and none overlaps weights, scales or biases
+    // (read, and prefetched before the activation is ready, through the
+    // caches): each output is written once per pass.
     for (int i = 0; i < n; ++i) {
         const size_t ny = (size_t)lin[i].N * 4;
         for (int j = 0; j < n; ++j) {
             const bqd_linear_w4a8& l = lin[j];
-            if (bytes_overlap(y[i], ny, l.wq, (size_t)l.N * l.K / 2) ||
+            if ((j > i && bytes_overlap(y[i], ny, y[j], (size_t)l.N * 4)) ||
+                bytes_overlap(y[i], ny, l.wq, (size_t)l.N * l.K / 2) ||
                 bytes_overlap(y[i], ny, l.scales, (size_t)l.N * 4) ||
                 (l.bias && bytes_overlap(y[i], ny, l.bias, (size_t)l.N * 4)))
                 return BQD_ERR_SHAPE;
         }
     }
+    // Where each activation comes from: written before the launch (it
+    // overlaps no output), or a contiguous part of one earlier linear's
+    // output (read from the exchange; fp32 only).  Overlapping its own or a
+    // later output, or more than one output, is refused: workgroups run
+    // ahead of each other between dependent linears, so a later output may
+    // be written while the activation is still being read.
+    std::vector<int> src(n, -1);
+    std::vector<int64_t> off(n, 0);
+    for (int i = 0; i < n; ++i) {
+        const size_t nx = (size_t)lin[i].K * xe;
+        for (int k = 0; k < n; ++k) {
+            const size_t ny = (size_t)lin[k].N * 4;
+            if (!bytes_overlap(x[i], nx, y[k], ny))
+                continue;
+            if (k >= i || src[i] >= 0 || !contains(y[k], ny, x[i], nx))
+                return BQD_ERR_SHAPE;
+            if (x_dtype != BQD_F32)
+                return BQD_ERR_DTYPE;
+            const uintptr_t d = (uintptr_t)x[i] - (uintptr_t)y[k];
+            if (d % 4)
+                return BQD_ERR_ALIGN;
+            src[i] = k;
+            off[i] = (int64_t)(d / 4);
+        }
+    }
+    // Exchange offsets: each output a later linear reads gets N words, placed
+    // so that an exchange word and its output element share their position
+    // modulo 16 bytes (a 16-byte-aligned activation is a 16-byte-aligned run
+    // of exchange words); every output starts a 256-byte line.
+    std::vector<int64_t> xout(n, -1);
+    int64_t words = 0;
+    for (int i = 0; i < n; ++i)
+        if (src[i] >= 0 && xout[src[i]] < 0) {
+            const int k = src[i];
+            xout[k] = words + (int64_t)(((uintptr_t)y[k] >> 2) & 3);
+            words += ((int64_t)lin[k].N + 3 + 63) / 64 * 64;
+        }
+    for (int k = 0; k < n; ++k)
+        if (src[k] >= 0 && xout[src[k]] < 0)
+            return BQD_ERR_SHAPE;  // unreachable: every source has an offset
+    if (words > (int64_t)(INT32_MAX / 2) - kXchBase)
+        return BQD_ERR_BOUND;
     if ((rc = bqd_init()))
         return rc;
     int G = 0;
@@ -3377,7 +3474,7 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         return rc;
     if (G > kPassMaxGrid)
         return BQD_ERR_LAUNCH;
-    PassHeader h{n, G, kmax, 0};  // reserved = 0
+    PassHeader h{n, G, kmax, (int32_t)words};
     std::memcpy(desc_host, &h, sizeof h);
     PassTask* d = reinterpret_cast<PassTask*>(reinterpret_cast<char*>(desc_host) + sizeof(PassHeader));
     for (int i = 0; i < n; ++i) {
@@ -3392,48 +3489,69 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         t.N = l.N;
         t.C = l.K / 32;
         t.x_dtype = x_dtype == BQD_F16 ? X_F16 : X_F32;
-        const size_t nx = (size_t)l.K * (x_dtype == BQD_F32 ? 4 : 2);
-        for (int k = 0; k < i && !t.x_in_pass; ++k)
-            t.x_in_pass = bytes_overlap(x[i], nx, y[k], (size_t)lin[k].N * 4) ? 1 : 0;
+        t.xin = src[i] >= 0 ? (int32_t)(xout[src[i]] + off[i]) : -1;
+        t.xout = (int32_t)xout[i];
         pass_shape_host(t.N, t.C, G, t);
         std::memcpy(d + i, &t, sizeof t);
     }
     *max_k = kmax;
+    *sync_bytes = ((size_t)kXchBase + 2 * (size_t)words) * sizeof(uint32_t);
     return BQD_OK;
 }
 
-int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev,
-                     int32_t spin_limit, void* stream)
+static int pass_check_launch(const void* desc_dev, int32_t n, int32_t max_k, size_t sync_bytes, int32_t spin_limit)
 {
     if (n <= 0 || n > BQD_MAX_PASS_LINEARS)
         return BQD_ERR_SHAPE;
-    if (!desc_dev || !sync_dev)
+    if (!desc_dev)
         return BQD_ERR_NULL;
     int rc = check_k(max_k);
     if (rc)
         return rc;
     if (max_k > kPassMaxK)
         return BQD_ERR_BOUND;
+    if (sync_bytes < (size_t)kXchBase * 4 || sync_bytes % 256)
+        return BQD_ERR_SHAPE;
     if (spin_limit < 0)
         return BQD_ERR_CONFIG;
-    if (!aligned(desc_dev, 16) || !aligned(sync_dev, 4))
+    if (!aligned(desc_dev, 16))
         return BQD_ERR_ALIGN;
-    if ((rc = bqd_init()))
-        return rc;
+    return BQD_OK;
+}
+
+static int pass_launch(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync, size_t sync_bytes,
+                       int32_t spin_limit, hipStream_t stream)
+{
     int G = 0;
-    if ((rc = pass_grid(max_k, &G)))
+    int rc = pass_grid(max_k, &G);
+    if (rc)
         return rc;
     const PassHeader* hdr = reinterpret_cast<const PassHeader*>(desc_dev);
     const PassTask* tasks =
         reinterpret_cast<const PassTask*>(reinterpret_cast<const char*>(desc_dev) + sizeof(PassHeader));
     int spin = spin_limit ? spin_limit : kPassSpinLimit;
     int nn = n, mk = max_k;
-    void* args[] = {(void*)&hdr, (void*)&tasks, (void*)&nn, (void*)&mk, (void*)&sync_dev, (void*)&spin};
+    size_t words = sync_bytes / 4;
+    void* args[] = {(void*)&hdr, (void*)&tasks, (void*)&nn, (void*)&mk, (void*)&sync, (void*)&words, (void*)&spin};
     if (hipLaunchCooperativeKernel((const void*)k_decode_pass, dim3(G), dim3(kPassThreads), args,
-                                   (unsigned)pass_lds_bytes(max_k),
-                                   (hipStream_t)stream) != hipSuccess)
+                                   (unsigned)pass_lds_bytes(max_k), stream) != hipSuccess)
         return BQD_ERR_LAUNCH;
     return launched();
+}
+
+int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev, size_t sync_bytes,
+                     int32_t spin_limit, void* stream)
+{
+    int rc = pass_check_launch(desc_dev, n, max_k, sync_bytes, spin_limit);
+    if (rc)
+        return rc;
+    if (!sync_dev)
+        return BQD_ERR_NULL;
+    if (!aligned(sync_dev, 256))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    return pass_launch(desc_dev, n, max_k, sync_dev, sync_bytes, spin_limit, (hipStream_t)stream);
 }
 
 int read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll, void* stream)

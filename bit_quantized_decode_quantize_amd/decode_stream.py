@@ -130,17 +130,33 @@ class QwenW4A8Stream:
         """The same linears chained as a decoder chains them, in one pass:
         linear i reads the first K_i values of linear i-1's output (through
         output buffers of its own; ``.outputs``), linear 0 the stream's
-        activation.  Same algorithmic bytes as a step of the stream."""
+        activation.  Same algorithmic bytes as a step of the stream; each
+        linear waits for the previous one's rows (the decoder's dependency)."""
         ys = [torch.empty(d["N"], dtype=torch.float32, device=self.device) for d in self.linears]
         xs = [self.linears[0]["x"]] + [ys[i - 1][:d["K"]] for i, d in enumerate(self.linears) if i > 0]
         p = bqd.DecodePass([bqd.make_linear(d["wq"], d["sw"], d["b"]) for d in self.linears], xs, ys, self.device)
         p.outputs = ys
         return p
 
-    def sync_floor_pass(self, rows: int = 64) -> "bqd.DecodePass":
+    def link_floor_pass(self, size: int = 64) -> "bqd.DecodePass":
+        """As many linears as the stream, each [size, size] and chained like
+        ``chained_pass``: the dependency between consecutive linears (store,
+        poll, staging, a few rows) with next to no weight traffic."""
+        n = len(self.linears)
+        W = I.normal("qwen/linkfloor/W", (n * size, size), 0.02, self.seed, self.device)
+        wq, sw = bqd.quantize_weights_int4_rowwise(W)
+        del W
+        x0 = I.normal("qwen/linkfloor/x", size, 1.0, self.seed, self.device)
+        ys = [torch.empty(size, dtype=torch.float32, device=self.device) for _ in range(n)]
+        lins = [bqd.make_linear(wq[i * size:(i + 1) * size], sw[i * size:(i + 1) * size], None) for i in range(n)]
+        p = bqd.DecodePass(lins, [x0] + ys[:-1], ys, self.device)
+        p.outputs = ys
+        return p
+
+    def cut_pass(self, rows: int = 64) -> "bqd.DecodePass":
         """The same linears cut to their first ``rows`` rows (views of the
-        stream's weights), in one pass: the waits, activation staging and
-        output stores of every linear with almost no weight traffic."""
+        stream's weights) with the stream's own activations, in one pass;
+        outputs in ``.outputs``."""
         ys = [torch.empty(rows, dtype=torch.float32, device=self.device) for _ in self.linears]
         lins = [bqd.make_linear(d["wq"][:rows], d["sw"][:rows], None if d["b"] is None else d["b"][:rows])
                 for d in self.linears]

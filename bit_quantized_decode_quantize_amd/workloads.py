@@ -102,7 +102,8 @@ class LayerPool:
     """One Qwen2-7B-shaped decoder layer (the four fused linears of layer 0
     of the 28-layer stream), replicated into >= 9 copies.  One step = one
     layer: four fused launches (``layer_w4a8_forward``), or, persistent,
-    one launch of the pass runs every copy in turn (``copies`` layer steps)."""
+    one launch of the pass runs every copy in turn (``copies`` layer steps),
+    each linear reading the previous linear's output."""
 
     def __init__(self, seed: int = 0, device="cuda", persistent: bool = False):
         self.device = torch.device(device)
@@ -133,9 +134,12 @@ class LayerPool:
         self.persistent = persistent
         self.pass_ = None
         if persistent:
+            # chained as a decoder chains them: each linear reads the first K
+            # values of the previous linear's output (the first one its own x)
             flat = [e for lin in self.layers for e in lin]
+            xs = [flat[0]["x"]] + [flat[i - 1]["y"][:e["K"]] for i, e in enumerate(flat) if i > 0]
             self.pass_ = bqd.DecodePass([bqd.make_linear(e["wq"], e["sw"], e["b"]) for e in flat],
-                                        [e["x"] for e in flat], [e["y"] for e in flat], self.device)
+                                        xs, [e["y"] for e in flat], self.device)
         self.i = 0
         self.launches_per_step = 1.0 / self.copies if persistent else 4
         self.steps_per_call = self.copies if persistent else 1

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BQD_ABI_VERSION 1
+#define BQD_ABI_VERSION 2
 
 #define BQD_OK 0
 #define BQD_ERR_NULL (-1)      /* a required pointer is NULL                 */
@@ -374,47 +374,59 @@ int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const*
 /* Bytes of the descriptors decode_pass_encode writes for n linears. */
 size_t decode_pass_desc_bytes(int32_t n);
 
-/* Bytes of the synchronisation words of a pass over n linears: an error
- * word, an epoch word per workgroup and 64 completion counters per linear,
- * each on a 64-byte line of its own.
- * The caller allocates them on the device, zero-fills them once, and hands
- * the same buffer to every pass over the same descriptors; passes over one
- * buffer must not overlap in time. */
-size_t decode_pass_sync_bytes(int32_t n);
-
 /* Validates n per-row linears (bqd_linear_w4a8 with BQD_SCALE_ROW_F32 and
  * r = lanes_per_row = 0: the pass chooses its own work split) with their
  * activation x[i] (device, [K_i] of x_dtype) and output y[i] (device float
  * [N_i], N_i > 0), and serialises them into desc_host (host,
  * decode_pass_desc_bytes(n) bytes) for the current device: the work split
  * is encoded for the grid the launch will use there, so a device must be
- * current (BQD_ERR_DEVICE otherwise).  *max_k receives the largest K.
+ * current (BQD_ERR_DEVICE otherwise).  *max_k receives the largest K and
+ * *sync_bytes the size of the workspace decode_pass_w4a8 needs.
  * K_i % 32 == 0 and K_i <= BQD_MAX_PASS_K (BQD_ERR_BOUND otherwise).
- * x[i] must not overlap y[i] (BQD_ERR_SHAPE): a linear's workgroups write
- * y while others still read x.  y[i] may be x[j] for any j > i (a
- * decoder's chain, also through buffers reused within the pass).  The
+ * Where each activation comes from:
+ *   - x[i] overlaps no output: it was written before the launch and is read
+ *     with no wait;
+ *   - x[i] lies inside the output y[k] of an earlier linear (k < i; a
+ *     decoder's chain, "从 FP 线性层到 INT4 DP4A 的数学推导" of the Jetson
+ *     Orin page: each linear's input derives from the previous output): it
+ *     is read from the pass's own exchange once y[k]'s rows are written.
+ *     x_dtype must then be BQD_F32 (BQD_ERR_DTYPE) and x[i] 4-byte aligned
+ *     within y[k] (BQD_ERR_ALIGN).
+ * Refused with BQD_ERR_SHAPE: x[i] overlapping y[k] for k >= i or two
+ * outputs, or not contained in the one it overlaps; outputs overlapping
+ * each other or any linear's weights, scales or bias.  (Workgroups run
+ * ahead of each other wherever no data dependency holds them, so an output
+ * is written exactly once and never over anything the pass reads.)  The
  * caller copies desc_host unchanged to 16-byte-aligned device memory
  * before decode_pass_w4a8 reads it. */
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
-                       float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k);
+                       float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k,
+                       size_t* sync_bytes);
 
 /* One decode step over the n encoded linears in order, in one cooperative
  * launch: for each linear, the activation quantisation of quantize_act and
- * the GEMV of gemv_w4a8 (same codes, same y bits as linear_w4a8).  Linear
- * i+1 reads its activation only after every workgroup has finished linear
- * i and its output stores have completed (the decoder's data dependency);
- * an activation that an earlier linear of the pass wrote is read with
- * device-scope loads, so stale lines of a reused buffer in a workgroup's
- * caches are not served; weights of linear i+1 are prefetched while
- * waiting.  desc_dev (device)
- * holds the encoded descriptors; max_k is the value decode_pass_encode
- * reported; sync_dev (device) the zero-initialised words of
- * decode_pass_sync_bytes(n).  spin_limit bounds each wait (0 = default,
- * about 0.1 s); a wait that runs out sets bit 0 of sync_dev[0] and
- * proceeds, so the kernel always ends; bit 1 is set (and nothing computed)
- * when the descriptors were encoded for another grid or another n.  The
- * caller reads sync_dev[0] to check, and clears it to reuse. */
-int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev,
+ * the GEMV of gemv_w4a8 (same codes, same y bits as linear_w4a8).  A linear
+ * whose activation is an earlier linear's output waits for exactly those
+ * values: each output row read later in the pass is also stored into an
+ * exchange in sync_dev, and the readers poll the words they need (one
+ * device-scope store and one device-scope load per dependency, no counters
+ * or fences).  Weights of the next linear are prefetched while waiting.
+ * desc_dev (device) holds the encoded descriptors; max_k is the value
+ * decode_pass_encode reported; sync_dev (device, 256-byte aligned) is the
+ * workspace of *sync_bytes bytes it reported, zero-filled once by the
+ * caller (sync_bytes: that size, which bounds what the kernel may
+ * touch; descriptors needing more are refused in the kernel with bit 1)
+ * and then handed unchanged to every pass over the same descriptors (each pass leaves it ready for the next; zero it again
+ * before using it with other descriptors).  Passes over one workspace must
+ * not overlap in time.  An output row equal to the NaN bit pattern
+ * 0xFFFFFFFF cannot be passed on (its exchange word would read as "not
+ * written"); finite inputs never produce it.  spin_limit bounds each wait
+ * (0 = default: 2^21 polling rounds, about 2 s); a wait that runs out sets bit 0 of
+ * sync_dev[0] and proceeds with what it read, so the kernel always ends;
+ * bit 1 is set (and nothing computed) when the descriptors were encoded
+ * for another grid or another n.  The caller reads sync_dev[0] to check,
+ * and clears it to reuse. */
+int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev, size_t sync_bytes,
                      int32_t spin_limit, void* stream);
 
 /* ---------------------------------------------------------------------- */

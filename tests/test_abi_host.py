@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bqd.abi_version() == 1
+    assert bqd.abi_version() == 2
     for s in (OK, NULL, SHAPE, ALIGN, BOUND, DTYPE, CONFIG, LAUNCH, DEVICE):
         assert bqd.status_string(s)
     assert bqd.status_string(12345) == "unknown status"
@@ -150,9 +150,10 @@ def test_decode_pass_encode_validates_and_serialises():
     L = _lib()
     n = 2
     nbytes = L.decode_pass_desc_bytes(n)
-    assert nbytes == 16 + 2 * 80 and L.decode_pass_sync_bytes(n) == (16 + (1024 + 2 * 64) * 16) * 4  # a 64-byte line per word
+    assert nbytes == 16 + 2 * 88
     host = (C.c_uint8 * nbytes)()
     mk = C.c_int32(0)
+    sb = C.c_size_t(0)
     # clear of the weights (a: P .. P + 0x2BC00), x[1]: 18944 fp32 = 0x12800 bytes
     X0, X1, Y0, Y1 = P + 0x400000, P + 0x410000, P + 0x440000, P + 0x450000
 
@@ -161,7 +162,7 @@ def test_decode_pass_encode_validates_and_serialises():
         xs = (C.c_void_p * 2)(*x)
         ys = (C.c_void_p * 2)(*y)
         return L.decode_pass_encode(arr, n, C.cast(xs, C.c_void_p), dt, C.cast(ys, C.c_void_p),
-                                    C.cast(host, C.c_void_p), nbytes, C.byref(mk))
+                                    C.cast(host, C.c_void_p), nbytes, C.byref(mk), C.byref(sb))
 
     a = bqd.LinearW4A8(P, P + 0x400, 0, 100, 3584, 0, 0, 0)
     b = bqd.LinearW4A8(P + 0x1000, P + 0x500, P + 0x600, 7, 18944, 0, 0, 0)
@@ -180,40 +181,69 @@ def test_decode_pass_encode_validates_and_serialises():
     assert enc([a, b], y=(Y0, X1 - 4 * 7 + 4)) == SHAPE
     assert enc([a, b], y=(X0 + 4 * 3584 - 4, Y1)) == SHAPE
     assert enc([a, b], y=(Y0, X1 + 2 * 18944 - 4), dt=1) == SHAPE
-    assert enc([a, b], y=(Y0, X1 + 2 * 18944), dt=1) != SHAPE           # fp16 x ends before y
-    assert enc([a, b], y=(Y0, X1 - 4 * 7)) != SHAPE                     # y ends where x starts
+    # an activation read before the launch that a later linear overwrites:
+    # workgroups run ahead, so it could be overwritten before every reader
+    # has it (x[0] over y[1])
+    assert enc([a, b], y=(Y0, X0 + 64)) == SHAPE
+    # outputs overlapping each other (each is written once per pass)
+    assert enc([a, b], y=(Y0, Y0 + 4 * 100 - 4)) == SHAPE
+    valid = DEVICE if not torch.cuda.is_available() else OK   # encoding needs the device's grid
+    assert enc([a, b], y=(Y0, Y0 + 4 * 100)) == valid
+    # x[1] inside y[0] is the chain (read from the exchange): fp32 only, and
+    # wholly inside.  y[0] of 20000 rows holds x[1] (18944 values) 16 values in.
+    Y1b = P + 0x480000
+    wide = bqd.LinearW4A8(P + 0x10000000, P + 0x400, 0, 20000, 3584, 0, 0, 0)
+    chained = dict(x=(X0, Y0 + 64), y=(Y0, Y1b))
+    assert enc([wide, b], **chained) == valid
+    assert enc([wide, b], x=(X0, Y0 + 4 * 20000 - 64), y=(Y0, Y1b)) == SHAPE     # runs past y[0]'s end
+    assert enc([wide, b], dt=1, x=(X0, Y0 + 64), y=(Y0, Y1b)) == DTYPE          # fp16 over an fp32 output
     # an output over a linear's weights, scales or bias (read, and prefetched
-    # before the wait, through the caches)
+    # before the activation is ready, through the caches)
     W, S, B = P + 0x100000, P + 0x200000, P + 0x300000
     c = bqd.LinearW4A8(W, S, B, 64, 64, 0, 0, 0)                      # 2048 weight bytes, 256 scale bytes
     assert enc([a, c], y=(W + 2048 - 4, Y1)) == SHAPE
     assert enc([a, c], y=(Y0, S + 252)) == SHAPE
     assert enc([a, c], y=(B - 4 * 64 + 4, Y1)) == SHAPE
     assert enc([a, c], y=(W + 2048, Y1)) != SHAPE
-    rc = enc([a, b])                         # valid: encoding needs the device's grid
+    rc = enc([a, b])
     if not torch.cuda.is_available():
         assert rc == DEVICE
         return
     assert rc == OK and mk.value == 18944
     import struct
     raw = bytes(host)
-    hn, grid, hk, reserved = struct.unpack("<4i", raw[:16])
-    assert (hn, hk, reserved) == (2, 18944, 0) and 0 < grid <= 1024
-    f = struct.unpack("<5Q9i2h", raw[16 + 80:16 + 160])
+    hn, grid, hk, words = struct.unpack("<4i", raw[:16])
+    assert (hn, hk, words) == (2, 18944, 0) and 0 < grid <= 1024   # nothing read from the exchange
+    assert sb.value == (64 + 1024 * 16) * 4                        # err line + epoch lines
+    f = struct.unpack("<5Q11i2h", raw[16 + 88:16 + 176])
     assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, X1, Y1)
-    N, C_, base, extra, lshift, r, iters, batches, steps, xdt, x_in_pass = f[5:]
-    assert (N, C_, base, extra, xdt, x_in_pass) == (7, 592, 7 // grid, 7 % grid, 1, 0)
+    N, C_, base, extra, lshift, r, iters, batches, steps, xin, xout, xdt, _ = f[5:]
+    assert (N, C_, base, extra, xin, xout, xdt) == (7, 592, 7 // grid, 7 % grid, -1, -1, 1)
     assert lshift in (4, 5, 6) and r in (1, 2)
     assert iters == -(-592 // (1 << lshift)) and steps == -(-iters * r // 8)
+    # the chain: y[0] gets 20000 exchange words (+ its offset mod 16 bytes),
+    # x[1] starts 16 words into them
+    assert enc([wide, b], **chained) == OK
+    raw = bytes(host)
+    words = struct.unpack("<4i", raw[:16])[3]
+    xin0, xout0 = struct.unpack("<2i", raw[16 + 76:16 + 84])
+    xin1, xout1 = struct.unpack("<2i", raw[16 + 88 + 76:16 + 88 + 84])
+    assert (xin0, xout0, xout1) == (-1, (Y0 >> 2) & 3, -1) and xin1 == xout0 + 16
+    assert words == -(-(20000 + 3) // 64) * 64 and sb.value == (64 + 1024 * 16 + 2 * words) * 4
 
 
 def test_decode_pass_launch_validates_before_launch():
     L = _lib()
-    assert L.decode_pass_w4a8(P, 0, 64, P, 0, None) == SHAPE
-    assert L.decode_pass_w4a8(None, 2, 64, P, 0, None) == NULL
-    assert L.decode_pass_w4a8(P, 2, 40, P, 0, None) == SHAPE
-    assert L.decode_pass_w4a8(P, 2, 64, P, -1, None) == CONFIG
-    assert L.decode_pass_w4a8(P + 8, 2, 64, P, 0, None) == ALIGN
+    WS = (64 + 1024 * 16) * 4                # the smallest workspace: no exchange
+    assert L.decode_pass_w4a8(P, 0, 64, P, WS, 0, None) == SHAPE
+    assert L.decode_pass_w4a8(None, 2, 64, P, WS, 0, None) == NULL
+    assert L.decode_pass_w4a8(P, 2, 64, None, WS, 0, None) == NULL
+    assert L.decode_pass_w4a8(P, 2, 40, P, WS, 0, None) == SHAPE
+    assert L.decode_pass_w4a8(P, 2, 64, P, WS, -1, None) == CONFIG
+    assert L.decode_pass_w4a8(P + 8, 2, 64, P, WS, 0, None) == ALIGN
+    assert L.decode_pass_w4a8(P, 2, 64, P + 64, WS, 0, None) == ALIGN   # the workspace is 256-byte aligned
+    assert L.decode_pass_w4a8(P, 2, 64, P, WS - 256, 0, None) == SHAPE  # smaller than any workspace
+    assert L.decode_pass_w4a8(P, 2, 64, P, WS + 4, 0, None) == SHAPE    # not a workspace size
 
 
 def test_read_probe_validates_before_launch():

@@ -490,9 +490,9 @@ def _pass_fixture(dtype=torch.float32, tag="pass"):
 def test_decode_pass_equals_per_linear_launches(dtype):
     lins, xs, ys, parts = _pass_fixture(dtype, f"pass{dtype}")
     p = bqd.DecodePass(lins, xs, ys)
-    assert _x_in_pass(p) == [0] * len(lins)  # no activation is an output of the pass
+    assert p.sources() == [-1] * len(lins)  # no activation is an output of the pass
     ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
-    for rep in range(3):                     # the counters carry over between passes
+    for rep in range(3):                     # the workspace carries over between passes
         for y in ys:
             y.fill_(float("nan"))
         p.run()
@@ -506,78 +506,117 @@ def test_decode_pass_equals_per_linear_launches(dtype):
     assert O.rel_err_rowwise(npy(ys[2]), yr, npy(sw), sxr, accr, npy(b)).max() <= TOL
 
 
-def _x_in_pass(p):
-    """The descriptors' flags for activations written earlier in the pass."""
-    raw = p.desc.cpu().numpy().tobytes()
-    return [int(np.frombuffer(raw[16 + 80 * i + 78:16 + 80 * i + 80], dtype=np.int16)[0]) for i in range(p.n)]
-
-
 CHAIN_SHAPES = [(2048, 1024), (1024, 2048), (4096, 1024), (1024, 4096), (1024, 1024), (2944, 1024),
-                (1024, 2944), (8192, 1024), (1024, 8192)]
+                (1024, 2944), (8192, 1024), (1024, 8192), (24576, 1024), (1000, 24576)]
+
+XCH_BASE = 64 + 1024 * 16   # exchange words start after the error line and the epoch lines
 
 
-def test_decode_pass_chained_through_reused_buffers():
-    """A decoder's chain inside one pass: linear i+1 reads what linear i
-    wrote, through two buffers used in turn, so every buffer is read again
-    after workgroups on every XCD have rewritten it (a line read earlier in
-    the pass must not be served stale).  Both buffers after each of three
-    passes equal the same chain run as one launch per linear."""
-    cap = max(max(N, K) for N, K in CHAIN_SHAPES)
-    lins, parts = [], []
-    for i, (N, K) in enumerate(CHAIN_SHAPES):
-        W = I.normal(f"gpu/chain/{i}/W", (N, K), 0.02, device=DEV)
-        wq, sw = bqd.quantize_weights_int4_rowwise(W)
-        b = I.normal(f"gpu/chain/{i}/b", N, 0.01, device=DEV) if i % 2 == 0 else None
-        lins.append(bqd.make_linear(wq, sw, b))
-        parts.append((wq, sw, b))
-    x0 = I.normal("gpu/chain/x", CHAIN_SHAPES[0][1], 1.0, device=DEV)
-    bufs = [torch.full((cap,), float("nan"), device=DEV), torch.full((cap,), float("nan"), device=DEV)]
-    xs = [bufs[i % 2][:K] for i, (N, K) in enumerate(CHAIN_SHAPES)]
-    ys = [bufs[(i + 1) % 2][:N] for i, (N, K) in enumerate(CHAIN_SHAPES)]
-    # the same chain, one launch per linear (kernel boundaries order it)
-    ref = [torch.full((cap,), float("nan"), device=DEV), torch.full((cap,), float("nan"), device=DEV)]
-    ref[0][:x0.numel()] = x0
-    for i, ((N, K), (wq, sw, b)) in enumerate(zip(CHAIN_SHAPES, parts)):
-        ref[(i + 1) % 2][:N] = bqd.linear_w4a8(wq, sw, b, ref[i % 2][:K].clone())
+def _chain(tag, shapes, oracle_chain=False):
+    """Linears chained as a decoder chains them: linear i+1 reads the first
+    K values of linear i's output (distinct buffers).  Returns the pass
+    pieces, the same chain run one launch per linear, and (oracle_chain)
+    the oracle's own run of the chain from the same fp32 weights, biases and
+    first activation (drawn on the host, copied to the device)."""
+    lins, parts, host = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        W = I.normal(f"gpu/{tag}/{i}/W", (N, K), 0.02)
+        b = I.normal(f"gpu/{tag}/{i}/b", N, 0.01) if i % 2 == 0 else None
+        wq, sw = bqd.quantize_weights_int4_rowwise(W.to(DEV))
+        bd = None if b is None else b.to(DEV)
+        lins.append(bqd.make_linear(wq, sw, bd))
+        parts.append((wq, sw, bd))
+        host.append((W, b))
+    x0h = I.normal(f"gpu/{tag}/x", shapes[0][1], 1.0)
+    x0 = x0h.to(DEV)
+    ys = [torch.full((N,), float("nan"), device=DEV) for N, _ in shapes]
+    xs = [x0] + [ys[i - 1][:K] for i, (_, K) in enumerate(shapes) if i > 0]
+    ref, xr = [], x0
+    for i, ((N, K), (wq, sw, b)) in enumerate(zip(shapes, parts)):
+        ref.append(bqd.linear_w4a8(wq, sw, b, xr))
+        xr = ref[-1][:shapes[i + 1][1]] if i + 1 < len(shapes) else None
     sync()
+    orc = None
+    if oracle_chain:
+        prepared = []
+        for (W, b), (wq, sw, _) in zip(host, parts):
+            w_r, s_r = O.prepare_int4_rowwise(W.numpy())
+            assert np.array_equal(u32(wq), w_r) and np.array_equal(npy(sw), s_r)
+            prepared.append((w_r, s_r, None if b is None else b.numpy()))
+        orc = (prepared, O.chain_w4a8(prepared, x0h.numpy()))
+    return lins, parts, xs, ys, ref, orc
+
+
+def test_decode_pass_chained():
+    """A decoder's chain inside one pass, K up to the pass's largest: each
+    linear reads what the previous one wrote, through the exchange.  Every
+    output equals the oracle's own run of the chain bit for bit (the value
+    handed on is decided in binary32 on both sides, so codes, accumulators
+    and the binary32 y agree exactly) and lies within the tolerance of the
+    binary64 y; it also equals the chain launched one linear at a time.
+    After each of three passes the exchange set the pass used holds every
+    read output as ~bits(y), and the other set is all zero (ready for the
+    next pass)."""
+    lins, parts, xs, ys, ref, (prepared, orc) = _chain("chain", CHAIN_SHAPES, oracle_chain=True)
+    for i, (yr, (qx, sx, acc, y64, y32)) in enumerate(zip(ref, orc)):
+        w_r, s_r, b_r = prepared[i]
+        assert np.array_equal(npy(yr).view(np.uint32), y32.view(np.uint32)), i
+        assert O.rel_err_rowwise(npy(yr), y64, s_r, sx, acc, b_r).max() <= TOL, i
     p = bqd.DecodePass(lins, xs, ys)
-    # every linear but the first reads an output of the pass: device-scope loads
-    assert _x_in_pass(p) == [0] + [1] * (len(CHAIN_SHAPES) - 1)
+    src = p.sources()
+    assert src[0] == -1 and all(v >= 0 for v in src[1:])
+    words = (p.sync.numel() - XCH_BASE) // 2
     for rep in range(3):
-        bufs[0].fill_(float("nan"))
-        bufs[1].fill_(float("nan"))
-        bufs[0][:x0.numel()] = x0
+        for y in ys:
+            y.fill_(float("nan"))
         p.run()
         sync()
         assert p.error_word() == 0
-        for j in range(2):
-            assert torch.equal(bufs[j].nan_to_num(7.0), ref[j].nan_to_num(7.0)), (rep, j)
-    # the last linear against the oracle, on its input (the previous
-    # linear's output, which nothing overwrote afterwards)
-    (wq, sw, b), (N, K) = parts[-1], CHAIN_SHAPES[-1]
-    xin = npy(ys[-2])
-    assert xin.shape == (K,)
-    qxr, sxr, accr, yr = O.linear_w4a8(u32(wq), npy(sw), None if b is None else npy(b), xin)
-    assert O.rel_err_rowwise(npy(ys[-1]), yr, npy(sw), sxr, accr, None if b is None else npy(b)).max() <= TOL
+        for i, (y, yr) in enumerate(zip(ys, ref)):
+            assert torch.equal(y, yr), (rep, i)
+        w = p.sync.cpu().numpy().view(np.uint32)
+        epoch = int(w[64])
+        assert epoch == rep + 1 and (w[64:64 + 16 * 1024:16][:_grid(p)] == epoch).all()
+        cur = w[XCH_BASE + (epoch & 1) * words:][:words]
+        old = w[XCH_BASE + ((epoch & 1) ^ 1) * words:][:words]
+        assert not old.any()
+        for i in range(len(lins) - 1):           # y[i] is read by linear i + 1
+            o = src[i + 1]                        # x[i+1] = y[i][:K]: its words start y[i]'s
+            yb = npy(ys[i]).view(np.uint32)
+            assert np.array_equal(~cur[o:o + yb.size], yb), (rep, i)
 
 
-def test_decode_pass_counters_wrap_around():
-    """The completion counters hold epoch x (workgroups per counter) and are
-    compared modulo 2^32: preset from the host to just below the wrap, two
-    passes cross it with every output still equal to the per-linear launches
-    and the words where the two passes leave them."""
-    lins, xs, ys, parts = _pass_fixture(tag="passwrap")
+def _grid(p):
+    return int(p.desc[4:8].cpu().view(torch.int32).item())
+
+
+def test_decode_pass_rejects_reused_buffers():
+    """Workgroups run ahead of each other where no data dependency holds
+    them, so a pass writes each output exactly once and never over an
+    activation it reads: a chain through two reused buffers is refused."""
+    shapes = CHAIN_SHAPES[:4]
+    cap = max(max(N, K) for N, K in shapes)
+    lins = []
+    for i, (N, K) in enumerate(shapes):
+        wq, sw = bqd.quantize_weights_int4_rowwise(I.normal(f"gpu/reuse/{i}/W", (N, K), 0.02, device=DEV))
+        lins.append(bqd.make_linear(wq, sw, None))
+    bufs = [torch.zeros(cap, device=DEV), torch.zeros(cap, device=DEV)]
+    xs = [bufs[i % 2][:K] for i, (N, K) in enumerate(shapes)]
+    ys = [bufs[(i + 1) % 2][:N] for i, (N, K) in enumerate(shapes)]
+    with pytest.raises(bqd.BQDError) as e:
+        bqd.DecodePass(lins, xs, ys)
+    assert e.value.status == -2
+
+
+def test_decode_pass_epochs_wrap_around():
+    """Epoch words preset from the host to 2^32 - 1: the next two passes run
+    as epochs 0 and 1 (the exchange sets alternate by parity across the
+    wrap) with every output equal to the per-linear launches."""
+    lins, parts, xs, ys, ref, _ = _chain("chainwrap", CHAIN_SHAPES[:5])
     p = bqd.DecodePass(lins, xs, ys)
-    G = int(p.desc[4:8].cpu().view(torch.int32).item())
-    E = (1 << 30) - 1                          # 4 * E = 2^32 - 4: the next pass wraps at G = 256
-    per = np.array([G // 64 + (1 if k < G % 64 else 0) for k in range(64)], dtype=np.uint64)
     words = np.zeros(p.sync.numel(), dtype=np.uint32)
-    words[16:16 + 16 * G:16] = E
-    for t in range(p.n):
-        base = 16 + 16 * (1024 + 64 * t)
-        words[base:base + 16 * 64:16] = (E * per) % (1 << 32)
+    words[64:64 + 16 * 1024:16] = 0xFFFFFFFF
     p.sync.copy_(torch.from_numpy(words.view(np.int32)).to(DEV))
-    ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
     for rep in range(2):
         for y in ys:
             y.fill_(float("nan"))
@@ -587,10 +626,7 @@ def test_decode_pass_counters_wrap_around():
         for i, (y, yr) in enumerate(zip(ys, ref)):
             assert torch.equal(y, yr), (rep, i)
     out = p.sync.cpu().numpy().view(np.uint32)
-    assert (out[16:16 + 16 * G:16] == E + 2).all()
-    for t in range(p.n):
-        base = 16 + 16 * (1024 + 64 * t)
-        assert (out[base:base + 16 * 64:16] == ((E + 2) * per) % (1 << 32)).all(), t
+    assert (out[64:64 + 16 * _grid(p):16] == 1).all()
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
@@ -665,21 +701,34 @@ def test_pass_descriptors_keep_their_tensors():
 
 
 def test_decode_pass_wait_limit_sets_error_and_ends():
-    """A one-spin limit, set from the host, makes waits give up at once: the
-    kernel still ends, flags the error word, and a normal pass clears."""
-    lins, xs, ys, parts = _pass_fixture(tag="passlim")
+    """A one-round spin limit, set from the host, makes a wait give up at its
+    first unanswered poll.  Linears 0..9 ([32, K_max] each) occupy
+    workgroups 0..31 only, each staging a 96 KB activation per linear; the
+    other workgroups have no rows there and go straight to linear 10, which
+    reads linear 9's output, long before it can exist: their waits run out,
+    bit 0 is set (bit 1 is not), and the kernel still ends.  A normal pass
+    afterwards gives the outputs of one launch per linear."""
+    K = bqd.BQD_MAX_PASS_K
+    lins, xs, ys, parts = [], [], [], []
+    for i in range(11):
+        N, Ki = (32, K) if i < 10 else (4096, 32)
+        wq, sw = bqd.quantize_weights_int4_rowwise(I.normal(f"gpu/passlim/{i}/W", (N, Ki), 0.02, device=DEV))
+        lins.append(bqd.make_linear(wq, sw, None))
+        ys.append(torch.full((N,), float("nan"), device=DEV))
+        xs.append(I.normal(f"gpu/passlim/{i}/x", Ki, 1.0, device=DEV) if i < 10 else ys[9])
+        parts.append((wq, sw))
     p = bqd.DecodePass(lins, xs, ys)
+    assert p.sources()[:10] == [-1] * 10 and p.sources()[10] >= 0
     p.run(spin_limit=1)
     sync()
-    assert p.error_word() in (0, 1)
+    assert p.error_word() == 1
     p.clear_error()
     p.run()
     sync()
     assert p.error_word() == 0
-    ref = [bqd.linear_w4a8(wq, sw, b, x) for wq, sw, b, x in parts]
-    sync()
-    for y, yr in zip(ys, ref):
-        assert torch.equal(y, yr)
+    for i in range(11):
+        wq, sw = parts[i]
+        assert torch.equal(ys[i], bqd.linear_w4a8(wq, sw, None, xs[i] if i < 10 else ys[9])), i
 
 
 def test_qwen_stream_full_size_persistent_sampled():
@@ -709,9 +758,9 @@ def test_qwen_stream_full_size_persistent_sampled():
         qxr, sxr, accr, y_r = O.linear_w4a8(wr, sr, br, npy(d["x"]))
         err = O.rel_err_rowwise(npy(d["y"][idx]), y_r, sr, sxr, accr, br)
         assert err.max() <= TOL, (k, err.max())
-    # The same linears cut to 64 rows (the bench's synchronisation floor):
-    # the full pass's first 64 rows, bit for bit.
-    fp = s.sync_floor_pass(64)
+    # The same linears cut to 64 rows: the full pass's first 64 rows, bit
+    # for bit.
+    fp = s.cut_pass(64)
     fp.run()
     sync()
     assert fp.error_word() == 0
@@ -725,7 +774,8 @@ def test_qwen_stream_full_size_persistent_sampled():
     ys = p.outputs
     for y in ys:
         y.fill_(float("nan"))
-    assert _x_in_pass(p) == [0] + [1] * (len(s.linears) - 1)
+    src = p.sources()
+    assert src[0] == -1 and all(v >= 0 for v in src[1:])
     p.run()
     p.run()
     sync()

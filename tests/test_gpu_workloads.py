@@ -69,20 +69,34 @@ def test_single_gemv_pool_graph_replay():
 
 @pytest.mark.parametrize("persistent", [True, False])
 def test_layer_pool(persistent):
-    """One layer's four fused linears over the rotation pool: the persistent
-    pass (all copies in one launch) and per-linear graph replay give the
-    same bits in every copy, matching the oracle on sampled rows."""
+    """One layer's four fused linears over the rotation pool.  Per-linear
+    graph replay: every copy gives the same bits, matching the oracle on
+    sampled rows.  Persistent: one launch chains every copy's linears as a
+    decoder does (each reads the previous output), equal bit for bit to the
+    same chain launched one linear at a time; its first linear reads the
+    layer's own activation and matches the oracle on sampled rows."""
     w = WL.LayerPool(device=DEV, persistent=persistent)
+    lins = I.qwen_layer_linears()
     if persistent:
         w.step()
         torch.cuda.synchronize()
         assert w.pass_.error_word() == 0
+        flat = [e for lin in w.layers for e in lin]
+        xr = flat[0]["x"]
+        for i, e in enumerate(flat):
+            yr = bqd.linear_w4a8(e["wq"], e["sw"], e["b"], xr)
+            assert torch.equal(e["y"], yr), i
+            xr = yr[:flat[i + 1]["K"]] if i + 1 < len(flat) else None
+        checked = lins[:1]
     else:
         _graph_replay(w.step, w.copies)
-    for k, (name, N, K) in enumerate(I.qwen_layer_linears()):
+        for k in range(len(lins)):
+            y0 = w.layers[0][k]["y"]
+            for c in range(1, w.copies):
+                assert torch.equal(w.layers[c][k]["y"], y0)
+        checked = lins
+    for k, (name, N, K) in enumerate(checked):
         y0 = w.layers[0][k]["y"]
-        for c in range(1, w.copies):
-            assert torch.equal(w.layers[c][k]["y"], y0)
         rows = _rows(N, f"layer/{name}")
         W = DS.linear_weight_fp32("qwen/L0", name, 0, DEV)[torch.as_tensor(rows, device=DEV)]
         b = DS.layer_biases("qwen/L0", 0, DEV)[name]
