@@ -26,6 +26,7 @@ BQD_MAX_K = 65536
 BQD_MAX_TOKENS = 16
 BQD_MAX_PROD_K = 32768
 BQD_MAX_PASS_K = 24576
+BQD_STATIC_PASS_BYTES = 16 << 20
 BQD_INT8X_BLOCK = 512
 
 ENTRY_POINTS = (
@@ -34,7 +35,7 @@ ENTRY_POINTS = (
     "quantize_weights_int8_group32", "pack_int4_rows_host", "unpack_int4_rows_host",
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
     "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
-    "decode_pass_desc_bytes", "decode_pass_encode", "decode_pass_w4a8",
+    "decode_pass_desc_bytes", "decode_pass_encode", "decode_pass_w4a8", "decode_pass_w4a8_static",
     "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant", "linear_rmsnorm_w4a8",
     "quantize_weights_q6k", "gemv_q6k_f16", "int8x_counts_host", "int8x_stream_bytes_host",
     "int8x_encode_host", "gemv_int8x",
@@ -88,6 +89,7 @@ def lib() -> C.CDLL:
         "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32),
                                    C.POINTER(C.c_size_t)]),
         "decode_pass_w4a8": (I, [P, I, I, P, C.c_size_t, I, P]),
+        "decode_pass_w4a8_static": (I, [P, I, I, C.c_size_t, I, P, P]),
         "read_probe": (I, [P, C.c_size_t, P, I, I, P]),
         "gemv_w4a16": (I, [P, P, P, P, P, I, I, I, I, P]),
         "add_rmsnorm_quant": (I, [P, P, P, C.c_float, P, P, P, P, I, I, P]),
@@ -616,6 +618,14 @@ class DecodePass:
     def run(self, stream=None, spin_limit: int = 0) -> None:
         _call("decode_pass_w4a8", self.desc.data_ptr(), self.n, self.max_k, self.sync.data_ptr(),
               self.sync_bytes, spin_limit, _stream(stream))
+
+    def run_static(self, err: torch.Tensor, stream=None, spin_limit: int = 0) -> None:
+        """The same pass over the library's static per-GPU workspace
+        (decode_pass_w4a8_static): allocates nothing; the error word lands in
+        ``err`` (one int32 on the device)."""
+        _dev(err, "err", (torch.int32,), 1)
+        _call("decode_pass_w4a8_static", self.desc.data_ptr(), self.n, self.max_k, self.sync_bytes, spin_limit,
+              err.data_ptr(), _stream(stream))
 
     def error_word(self) -> int:
         """Bit 0: a wait ran out of spins; bit 1: descriptors for another

@@ -2468,6 +2468,32 @@ int check_x_dtype(int d) { return (d == BQD_F32 || d == BQD_F16) ? BQD_OK : BQD_
 
 }  // namespace
 
+// Workspace of decode_pass_w4a8_static, for callers that cannot allocate
+// device memory: one copy per GPU, held until the process ends.  Host code
+// never uses this name as an address (on the host it is a stand-in); it
+// uses the device address bqd_init looked up for the current GPU.
+static __device__ __align__(256) uint32_t scratch[BQD_STATIC_PASS_BYTES / 4];
+
+namespace {
+
+uint32_t* g_scratch[kMaxDevices];  // device address of `scratch` on each GPU, or NULL
+
+// Zero-fills n 16-byte words (graph-capture safe, unlike hipMemsetAsync).
+__global__ __launch_bounds__(kThreads) void k_zero16(u32x4* p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// The pass's error word, copied out to the caller's buffer.
+__global__ void k_copy_word(const uint32_t* src, uint32_t* dst)
+{
+    if (threadIdx.x == 0)
+        *dst = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
 // ==========================================================================
 // C ABI
 // ==========================================================================
@@ -2510,6 +2536,14 @@ int bqd_init(void)
         } else {
             s = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
             g_dev_cus[dev] = p.multiProcessorCount;
+            // This device's copy of the static workspace (its address
+            // differs per GPU); NULL if the lookup fails, which only
+            // decode_pass_w4a8_static reports.
+            void* ptr = nullptr;
+            if (s == 1 && hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess)
+                g_scratch[dev] = static_cast<uint32_t*>(ptr);
+            else
+                (void)hipGetLastError();
         }
         g_dev_state[dev].store(s, std::memory_order_release);
     }
@@ -3552,6 +3586,41 @@ int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* s
     if ((rc = bqd_init()))
         return rc;
     return pass_launch(desc_dev, n, max_k, sync_dev, sync_bytes, spin_limit, (hipStream_t)stream);
+}
+
+int decode_pass_w4a8_static(const void* desc_dev, int32_t n, int32_t max_k, size_t sync_bytes,
+                            int32_t spin_limit, uint32_t* err_dev, void* stream)
+{
+    int rc = pass_check_launch(desc_dev, n, max_k, sync_bytes, spin_limit);
+    if (rc)
+        return rc;
+    if (sync_bytes > (size_t)BQD_STATIC_PASS_BYTES)
+        return BQD_ERR_BOUND;
+    if (!err_dev)
+        return BQD_ERR_NULL;
+    if (!aligned(err_dev, 4))
+        return BQD_ERR_ALIGN;
+    if ((rc = bqd_init()))
+        return rc;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return BQD_ERR_DEVICE;
+    uint32_t* ws = g_scratch[dev];
+    if (!ws)
+        return BQD_ERR_LAUNCH;
+    hipStream_t st = (hipStream_t)stream;
+    // The array keeps the previous call's contents (any descriptors):
+    // every call starts from a zeroed workspace of its own size.
+    const size_t n16 = sync_bytes / 16;
+    const long long want = (long long)((n16 + kThreads - 1) / kThreads);
+    const unsigned grid = (unsigned)(want < 1024 ? want : 1024);
+    hipLaunchKernelGGL(k_zero16, dim3(grid), dim3(kThreads), 0, st, reinterpret_cast<u32x4*>(ws), n16);
+    if ((rc = launched()))
+        return rc;
+    if ((rc = pass_launch(desc_dev, n, max_k, ws, sync_bytes, spin_limit, st)))
+        return rc;
+    hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(kWave), 0, st, ws, err_dev);
+    return launched();
 }
 
 int read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll, void* stream)

@@ -429,6 +429,29 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
 int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev, size_t sync_bytes,
                      int32_t spin_limit, void* stream);
 
+/* Largest workspace decode_pass_w4a8_static holds: 16 MiB of device memory
+ * per GPU the library runs on (a 28-layer Qwen2-7B-shaped chained pass with
+ * its lm_head needs about 11 MiB). */
+#define BQD_STATIC_PASS_BYTES 16777216 /* 16 MiB */
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the pass
+ * of decode_pass_w4a8 with its workspace in a static device array the
+ * library holds per GPU, instead of a caller's sync_dev.  sync_bytes is
+ * the size decode_pass_encode reported (BQD_ERR_BOUND above
+ * BQD_STATIC_PASS_BYTES; BQD_ERR_SHAPE if it is not a workspace size).
+ * Each call first zero-fills that much of the array with a kernel on
+ * `stream` (the array keeps the last call's contents, whatever descriptors
+ * it ran), then runs the pass, then copies the pass's error word (bits as
+ * in decode_pass_w4a8) to err_dev (device, one uint32).  Nothing is
+ * allocated.  All calls on one GPU share its array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and give wrong
+ * results, so callers serialise them.  Launch errors and argument checks as
+ * in decode_pass_w4a8; BQD_ERR_LAUNCH also if the array's address could
+ * not be found on this GPU. */
+int decode_pass_w4a8_static(const void* desc_dev, int32_t n, int32_t max_k, size_t sync_bytes,
+                            int32_t spin_limit, uint32_t* err_dev, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* Measurement                                                             */
 /* ---------------------------------------------------------------------- */
