@@ -153,6 +153,22 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
+// The same maximum without LDS traffic (lane shuffles are LDS permutes):
+// DPP row rotations 8, 4, 2, 1 inside each row of 16 lanes, then the four
+// row maxima read as scalars.  Needs every lane of the wave active.
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, dpp_f<0x128>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x122>(v));
+    v = fmaxf(v, dpp_f<0x121>(v));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Max over the workgroup (every thread gets it).  red: 4 floats of LDS.
 __device__ __forceinline__ float block_max(float v, float* red)
 {
@@ -1897,8 +1913,7 @@ struct PassTask {
     int32_t steps;                  // pipeline steps per batch
     int32_t xin;                    // exchange word of x[0] (x is an output of the pass), or -1
     int32_t xout;                   // exchange word of y[0] (a later linear reads y), or -1
-    int16_t x_dtype;                // X_F32 or X_F16 (xin < 0)
-    int16_t reserved;
+    int32_t x_dtype;                // X_F32 or X_F16 (xin < 0)
 };
 static_assert(sizeof(PassTask) == 88, "descriptor layout");
 
@@ -1923,6 +1938,39 @@ constexpr int kXchBase = kEpochBase + kPassMaxGrid * kSyncStride;  // 16448 word
 constexpr int kStageGroups = 4;
 
 inline size_t pass_lds_bytes(int max_k) { return (size_t)((max_k + 15) & ~15) + 4 * (size_t)max_k; }
+
+// Descriptors are read from a ring in LDS, not with scalar loads: a scalar
+// load misses the scalar cache once per linear and per CU in every pass,
+// and LDS waits (lgkmcnt) also wait for scalar loads, so its latency would
+// land on each linear's staging.  The ring holds kDescRing descriptors;
+// the staging waves refill half of it every kDescRing / 2 linears.
+constexpr int kDescRing = 64;
+constexpr int kDescWords = (int)(sizeof(PassTask) / 4);
+static_assert(sizeof(PassTask) % 4 == 0, "descriptor words");
+static_assert(5 * kPassMaxK + 32 + kDescRing * (int)sizeof(PassTask) + 1024 <= 160 * 1024, "pass LDS");
+
+// Copies descriptors [lo, hi) into their ring slots, threads t, t + nt, ...
+__device__ __forceinline__ void ring_fill(uint32_t* dring, const PassTask* tasks, int lo, int hi, int t, int nt)
+{
+    const BQD_GLOBAL uint32_t* src = gptr(reinterpret_cast<const uint32_t*>(tasks));
+    for (int i = t; i < (hi - lo) * kDescWords; i += nt) {
+        const int d = lo + i / kDescWords, k = i % kDescWords;
+        dring[(d % kDescRing) * kDescWords + k] = src[(size_t)d * kDescWords + k];
+    }
+}
+
+// Descriptor i from the ring, every field wave-uniform (scalar registers).
+__device__ __forceinline__ PassTask ring_get(const uint32_t* dring, int i)
+{
+    uint32_t w[kDescWords];
+    const uint32_t* d = dring + (i % kDescRing) * kDescWords;
+#pragma unroll
+    for (int k = 0; k < kDescWords; ++k)
+        w[k] = __builtin_amdgcn_readfirstlane(d[k]);
+    PassTask t;
+    __builtin_memcpy(&t, w, sizeof t);
+    return t;
+}
 
 __device__ __forceinline__ void pass_range(const PassTask& t, int w, int& row_start, int& rows)
 {
@@ -2202,6 +2250,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     const int xf_offset = (hdr->max_k + 15) & ~15;
     __shared__ float red[2][kPassThreads / kWave];
     __shared__ uint32_t s_epoch;
+    __shared__ uint32_t dring[kDescRing * kDescWords];
     const int n = hdr->n;
     const int G = gridDim.x;
     const int w = blockIdx.x;
@@ -2221,6 +2270,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     // hold the same value between passes: this pass writes that value + 1.
     if (tid == 0)
         s_epoch = __hip_atomic_load(&epochs[(size_t)w * kSyncStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    ring_fill(dring, tasks, 0, n < kDescRing ? n : kDescRing, tid, kPassThreads);
     __syncthreads();
     const uint32_t epoch = s_epoch;
     const size_t xw = (size_t)(uint32_t)hdr->xch_words;
@@ -2229,7 +2279,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
 
     u32x4 cur[kPassSlots];
     float esw = 0.0f, eb = 0.0f;  // first batch's epilogue operands, loaded with cur
-    PassTask t = tasks[0];
+    PassTask t = ring_get(dring, 0);
     bool have_cur = false;
     if (worker) {
         int rs, rw;
@@ -2244,7 +2294,9 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     }
     f32x4* xf = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(xs) + xf_offset);
     for (int ti = 0; ti < n; ++ti) {
-        const PassTask tn = tasks[ti + 1 < n ? ti + 1 : ti];
+        if (ti > 0 && ti % (kDescRing / 2) == 0 && ct >= 0)
+            ring_fill(dring, tasks, ti + kDescRing / 2, min(n, ti + kDescRing), ct, kPassControl);
+        const PassTask tn = ring_get(dring, ti + 1 < n ? ti + 1 : ti);
         int row_start, rows;
         pass_range(t, w, row_start, rows);
         const int G8 = 4 * t.C;
@@ -2262,7 +2314,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
                 m = stage_load<X_F16, false>(t.x, xf, G8, st, nst, err, spin_limit);
             else
                 m = stage_load<X_F32, false>(t.x, xf, G8, st, nst, err, spin_limit);
-            m = wave_max(m);
+            m = wave_max_dpp(m);
             if ((st & (kWave - 1)) == 0)
                 rd[st / kWave] = m;
         }
@@ -2273,8 +2325,8 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
             amax = fmaxf(amax, rd[i]);
         const ActScale a = act_scale(amax);
         // 2. codes into LDS
-        if (rows > 0 && st >= 0)
-            stage_codes(reinterpret_cast<u32x2*>(xs), xf, G8, st, nst, a);
+        if (rows > 0)
+            stage_codes(reinterpret_cast<u32x2*>(xs), xf, G8, tid, kPassThreads, a);
         __syncthreads();
         // 3. workers: stream the weights, write the rows
         if (rows > 0 && worker) {

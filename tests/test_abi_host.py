@@ -215,9 +215,9 @@ def test_decode_pass_encode_validates_and_serialises():
     hn, grid, hk, words = struct.unpack("<4i", raw[:16])
     assert (hn, hk, words) == (2, 18944, 0) and 0 < grid <= 1024   # nothing read from the exchange
     assert sb.value == (64 + 1024 * 16) * 4                        # err line + epoch lines
-    f = struct.unpack("<5Q11i2h", raw[16 + 88:16 + 176])
+    f = struct.unpack("<5Q12i", raw[16 + 88:16 + 176])
     assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, X1, Y1)
-    N, C_, base, extra, lshift, r, iters, batches, steps, xin, xout, xdt, _ = f[5:]
+    N, C_, base, extra, lshift, r, iters, batches, steps, xin, xout, xdt = f[5:]
     assert (N, C_, base, extra, xin, xout, xdt) == (7, 592, 7 // grid, 7 % grid, -1, -1, 1)
     assert lshift in (4, 5, 6) and r in (1, 2)
     assert iters == -(-592 // (1 << lshift)) and steps == -(-iters * r // 8)
