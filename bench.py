@@ -546,8 +546,30 @@ def run_gemma(a, dev):
     w = WL.GemmaG32Stream(layers=layers, device=dev, r=a.r, lanes_per_row=a.lanes, head=a.lm_head)
     log(f"gemma stream built: {w.launches_per_step} launches, {w.weight_bytes() / 1e9:.3f} GB, "
         f"{time.time() - t0:.1f} s")
-    ms, n = time_steps(w.step, a.steps, a.warmup, 1 if (not a.eager) else 0)
-    gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
+    # The token step: the 140 group-32 linears chained in one persistent
+    # pass (each reads the previous output), then the lm_head (--per-linear:
+    # one graph-replayed launch per linear, each with its own activation).
+    if a.per_linear:
+        step, step_bytes = w.step, w.bytes_per_step()
+        ms, n = time_steps(step, a.steps, a.warmup, 1 if (not a.eager) else 0)
+    else:
+        gp = w.make_pass(chained=True)
+
+        def step():
+            gp.run()
+            w.run_head()
+        step_bytes = w.pass_bytes(chained=True)
+        ms, n = time_steps(step, a.steps, a.warmup, 0)
+        if gp.error_word():
+            raise RuntimeError(f"gemma pass reported an error (error word {gp.error_word()})")
+        ip = w.make_pass(chained=False)
+
+        def istep():
+            ip.run()
+            w.run_head()
+        ims, _ = time_steps(istep, a.steps, a.warmup, 0)
+        pms, _ = time_steps(w.step, a.steps, a.warmup, 1)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
     # Both lm_head forms alone (the largest single matrix), back to back.
     heads = {}
     for kind, fn in (("w8a16", w.lm_head), ("q6k", w.lm_head_q6k)):
@@ -556,13 +578,23 @@ def run_gemma(a, dev):
                        "GB/s": round(w.head_bytes(kind) / (ms_h * 1e-3) / 1e9, 1)}
     head_form = {"w8a16": "W8A16 lm_head [262144,1536] (int8 in [-32,31], fp16 group-32 scales)",
                  "q6k": "packed 6-bit lm_head [262144,1536] (210 B per 256 weights, decoded in registers)"}
+    launch = ("per-linear, HIP graph" if (not a.eager) else "per-linear") if a.per_linear else \
+        "persistent pass (140 chained linears) + lm_head launch"
     out = base_line(a, gbs, ms, n, {
-        "workload": f"gemma-shaped {layers}-layer Q4_0-style group-32 W4A8 stream (fp16 x) + "
-                    + head_form[a.lm_head],
-        "launch": "per-linear, HIP graph" if (not a.eager) else "per-linear", "layers": layers,
-        "bytes_per_step": w.bytes_per_step(), "weight_bytes": w.weight_bytes()}, dtype="int8+fp16")
+        "workload": f"gemma-shaped {layers}-layer Q4_0-style group-32 W4A8 stream + " + head_form[a.lm_head],
+        "activations": ("each linear's own fp16 activation" if a.per_linear else
+                        "chained: linear i reads linear i-1's fp32 output"),
+        "launch": launch, "layers": layers,
+        "bytes_per_step": step_bytes, "weight_bytes": w.weight_bytes()}, dtype="int8+fp16")
     out["tok_per_s"] = round(1e3 / ms, 2)
     out["us_per_gemv"] = round(ms * 1e3 / w.launches_per_step, 3)
+    if not a.per_linear:
+        ib = w.pass_bytes(chained=False)
+        out["independent"] = {"ms_per_step": round(ims, 5), "GB/s": round(ib / (ims * 1e-3) / 1e9, 1),
+                              "note": "the same pass with each linear's own fp16 activation (no dependency)"}
+        out["per_linear_graph"] = {"ms_per_step": round(pms, 5),
+                                   "GB/s": round(w.bytes_per_step() / (pms * 1e-3) / 1e9, 1),
+                                   "note": "one graph-replayed launch per linear, own fp16 activations"}
     out["lm_head"] = heads[a.lm_head]
     out["lm_head_forms"] = heads
     h = heads[a.lm_head]

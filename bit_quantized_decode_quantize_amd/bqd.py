@@ -644,7 +644,7 @@ class DecodePass:
                                signed=True) for i in range(self.n)]
 
 
-DESC_HEADER, DESC_TASK = 16, 88   # bytes of the descriptor header and of one linear's descriptor
+DESC_HEADER, DESC_TASK = 16, 96   # bytes of the descriptor header and of one linear's descriptor
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int, unroll: int = 1, stream=None) -> None:

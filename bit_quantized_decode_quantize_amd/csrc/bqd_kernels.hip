@@ -1902,7 +1902,7 @@ static_assert(sizeof(PassHeader) == 16, "descriptor header layout");
 
 struct PassTask {
     const u32x4* wq;
-    const float* sw;
+    const void* scales;             // float s^W [N] (kind 0) or fp16 group scales [N, C] (kind 1)
     const float* bias;
     const void* x;                  // activation written before the launch (xin < 0)
     float* y;
@@ -1914,8 +1914,10 @@ struct PassTask {
     int32_t xin;                    // exchange word of x[0] (x is an output of the pass), or -1
     int32_t xout;                   // exchange word of y[0] (a later linear reads y), or -1
     int32_t x_dtype;                // X_F32 or X_F16 (xin < 0)
+    int32_t kind;                   // 0: per-row fp32 scales; 1: one fp16 scale per 32 weights
+    int32_t reserved;
 };
-static_assert(sizeof(PassTask) == 88, "descriptor layout");
+static_assert(sizeof(PassTask) == 96, "descriptor layout");
 
 constexpr int kPassThreads = 1024;    // 16 waves: one workgroup per CU
 // Waves 0..11 stream weights; waves 12..15 stage the activation.  The
@@ -1945,9 +1947,11 @@ inline size_t pass_lds_bytes(int max_k) { return (size_t)((max_k + 15) & ~15) + 
 // land on each linear's staging.  The ring holds kDescRing descriptors;
 // the staging waves refill half of it every kDescRing / 2 linears.
 constexpr int kDescRing = 64;
+// A group-32 linear's scales for this workgroup's rows, staged in LDS.
+constexpr int kPassScaleLds = 16384;
 constexpr int kDescWords = (int)(sizeof(PassTask) / 4);
 static_assert(sizeof(PassTask) % 4 == 0, "descriptor words");
-static_assert(5 * kPassMaxK + 32 + kDescRing * (int)sizeof(PassTask) + 1024 <= 160 * 1024, "pass LDS");
+static_assert(5 * kPassMaxK + kDescRing * (int)sizeof(PassTask) + kPassScaleLds + 1024 <= 160 * 1024, "pass LDS");
 
 // Copies descriptors [lo, hi) into their ring slots, threads t, t + nt, ...
 __device__ __forceinline__ void ring_fill(uint32_t* dring, const PassTask* tasks, int lo, int hi, int t, int nt)
@@ -2015,7 +2019,7 @@ __device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], float& esw, 
     if (j == 0) {
         const int rl = (b * groups + grp) * R + lane;
         const bool own = lane < R && rl < rows;
-        esw = own ? gptr(t.sw)[row_start + rl] : 0.0f;
+        esw = (own && t.kind == 0) ? gptr(reinterpret_cast<const float*>(t.scales))[row_start + rl] : 0.0f;
         eb = (own && t.bias) ? gptr(t.bias)[row_start + rl] : 0.0f;
     }
 }
@@ -2092,6 +2096,70 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
                     __hip_atomic_store(gptr_mut(xold) + t.xout + row, 0u, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
                 }
+            }
+        }
+        esw = nsw;
+        eb = nbv;
+    }
+}
+
+// A group-32 linear ("在香橙派上跑 Gemma4 ..." section 3.1: INT4 with one fp16
+// scale per 32 weights): per 16-byte chunk the exact int32 partial acc_g
+// times its scale s_g, accumulated in fp32 in the lane's chunk order, the
+// lanes' sums added by the same DPP and shuffle tree, and y = s^x sum + b:
+// the arithmetic and order, hence the bits, of k_gemv_w4a8_g32 at 32
+// lanes per row (the encoder fixes 32 lanes and one row per lane group).
+// sl holds the workgroup's rows' scales, staged in LDS.
+__device__ __forceinline__ void pass_run_g32(u32x4 (&cur)[kPassSlots], float& esw, float& eb, bool have_cur,
+                                             const PassTask& t, int row_start, int rows, const u32x4* xs, float sx,
+                                             const uint16_t* sl, uint32_t* xcur, uint32_t* xold)
+{
+    constexpr int L = 32;
+    const int lane = threadIdx.x & (L - 1);
+    const int groups = kPassWorkers / L;
+    const int grp = threadIdx.x / L;
+    if (!have_cur)
+        pass_load<1>(cur, esw, eb, t, row_start, rows, 0, 0);
+    float nsw = 0.0f, nbv = 0.0f;
+    for (int b = 0; b < t.batches; ++b) {
+        const int rl = b * groups + grp;
+        const uint16_t* srow = sl + (size_t)min(rl, rows - 1) * t.C;
+        float facc = 0.0f;
+        for (int j = 0; j < t.steps; ++j) {
+            u32x4 nxt[kPassSlots];
+            int nb = b, nj = j + 1;
+            if (nj == t.steps) {
+                nb = b + 1;
+                nj = 0;
+            }
+            const bool more = nb < t.batches;
+            if (more)
+                pass_load<1>(nxt, nsw, nbv, t, row_start, rows, nb, nj);
+#pragma unroll
+            for (int u = 0; u < kPassSlots; ++u) {
+                const int i = j * kPassSlots + u;
+                if (i < t.iters) {  // uniform across the wave
+                    const int c = min(i * L + lane, t.C - 1);
+                    const int ag = dot_chunk16(cur[u], xs[2 * c], xs[2 * c + 1], 0) >> 4;
+                    const float sg = (float)__builtin_bit_cast(_Float16, srow[c]);
+                    facc = fmaf((float)ag, sg, facc);
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int k = 0; k < kPassSlots; ++k)
+                    cur[k] = nxt[k];
+            }
+        }
+        facc = sum_lanes_f<L>(facc);
+        if (lane == 0 && rl < rows) {
+            const float yv = fmaf(sx, facc, eb);
+            const int row = row_start + rl;
+            gptr_mut(t.y)[row] = yv;
+            if (t.xout >= 0) {
+                __hip_atomic_store(gptr_mut(xcur) + t.xout + row, ~__builtin_bit_cast(uint32_t, yv),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(gptr_mut(xold) + t.xout + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         esw = nsw;
@@ -2251,6 +2319,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     __shared__ float red[2][kPassThreads / kWave];
     __shared__ uint32_t s_epoch;
     __shared__ uint32_t dring[kDescRing * kDescWords];
+    __shared__ u32x4 sl16[kPassScaleLds / 16];  // group-32 scales of this workgroup's rows
     const int n = hdr->n;
     const int G = gridDim.x;
     const int w = blockIdx.x;
@@ -2306,6 +2375,14 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         const bool all_stage = G8 > kPassStageAllAbove;
         const int st = all_stage ? tid : ct;
         const int nst = all_stage ? kPassThreads : kPassControl;
+        if (t.kind == 1 && rows > 0 && ct >= 0) {
+            // this workgroup's rows' group scales: rows * C fp16 values,
+            // contiguous and 16-byte aligned (C % 8 == 0, checked on the host)
+            const BQD_GLOBAL u32x4* src =
+                gptr(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(t.scales) + (size_t)row_start * t.C));
+            for (int i = ct; i < rows * t.C / 8; i += kPassControl)
+                sl16[i] = src[i];
+        }
         if (rows > 0 && st >= 0) {
             float m;
             if (t.xin >= 0)
@@ -2330,7 +2407,10 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         __syncthreads();
         // 3. workers: stream the weights, write the rows
         if (rows > 0 && worker) {
-            if (t.r == 2)
+            if (t.kind == 1)
+                pass_run_g32(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s,
+                             reinterpret_cast<const uint16_t*>(sl16), xcur, xold);
+            else if (t.r == 2)
                 pass_run<2>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
             else
                 pass_run<1>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
@@ -3480,15 +3560,18 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
     int kmax = 0;
     for (int i = 0; i < n; ++i) {
         const bqd_linear_w4a8& l = lin[i];
-        if (l.scale_kind != BQD_SCALE_ROW_F32)
+        if (l.scale_kind != BQD_SCALE_ROW_F32 && l.scale_kind != BQD_SCALE_GROUP32_F16)
             return BQD_ERR_DTYPE;
+        const bool g32 = l.scale_kind == BQD_SCALE_GROUP32_F16;
         if (l.N <= 0)
             return BQD_ERR_SHAPE;
         if ((rc = check_k(l.K)))
             return rc;
+        if (g32 && l.K % 256)
+            return BQD_ERR_SHAPE;  // a row's group scales fill whole 16-byte words
         if (!l.wq || !l.scales || !x[i] || !y[i])
             return BQD_ERR_NULL;
-        if (!aligned(l.wq, 16) || !aligned(x[i], 16) || !aligned(l.scales, 4) || !aligned(l.bias, 4) ||
+        if (!aligned(l.wq, 16) || !aligned(x[i], 16) || !aligned(l.scales, g32 ? 16 : 4) || !aligned(l.bias, 4) ||
             !aligned(y[i], 4))
             return BQD_ERR_ALIGN;
         if (l.r != 0 || l.lanes_per_row != 0)
@@ -3504,9 +3587,11 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         const size_t ny = (size_t)lin[i].N * 4;
         for (int j = 0; j < n; ++j) {
             const bqd_linear_w4a8& l = lin[j];
+            const size_t scale_bytes =
+                l.scale_kind == BQD_SCALE_GROUP32_F16 ? (size_t)l.N * (l.K / 32) * 2 : (size_t)l.N * 4;
             if ((j > i && bytes_overlap(y[i], ny, y[j], (size_t)l.N * 4)) ||
                 bytes_overlap(y[i], ny, l.wq, (size_t)l.N * l.K / 2) ||
-                bytes_overlap(y[i], ny, l.scales, (size_t)l.N * 4) ||
+                bytes_overlap(y[i], ny, l.scales, scale_bytes) ||
                 (l.bias && bytes_overlap(y[i], ny, l.bias, (size_t)l.N * 4)))
                 return BQD_ERR_SHAPE;
         }
@@ -3568,7 +3653,8 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         PassTask t;
         std::memset(&t, 0, sizeof t);
         t.wq = reinterpret_cast<const u32x4*>(l.wq);
-        t.sw = reinterpret_cast<const float*>(l.scales);
+        t.scales = l.scales;
+        t.kind = l.scale_kind == BQD_SCALE_GROUP32_F16 ? 1 : 0;
         t.bias = l.bias;
         t.x = x[i];
         t.y = y[i];
@@ -3578,6 +3664,18 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         t.xin = src[i] >= 0 ? (int32_t)(xout[src[i]] + off[i]) : -1;
         t.xout = (int32_t)xout[i];
         pass_shape_host(t.N, t.C, G, t);
+        if (t.kind == 1) {
+            // the per-linear group-32 kernel's lanes per row (its sums run
+            // in that order), one row per lane group
+            const int rows_max = (t.N + G - 1) / G;
+            if ((size_t)rows_max * t.C * 2 > (size_t)kPassScaleLds)
+                return BQD_ERR_BOUND;
+            t.lshift = 5;
+            t.r = 1;
+            t.iters = (t.C + 31) / 32;
+            t.batches = (rows_max + (kPassWorkers >> 5) - 1) / (kPassWorkers >> 5);
+            t.steps = (t.iters + kPassSlots - 1) / kPassSlots;
+        }
         std::memcpy(d + i, &t, sizeof t);
     }
     *max_k = kmax;

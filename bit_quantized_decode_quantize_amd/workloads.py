@@ -200,10 +200,38 @@ class GemmaG32Stream:
         for d in self.linears:
             bqd.linear_w4a8_group32(d["wq"], d["s16"], None, d["x"], y=d["y"], r=self.r,
                                     lanes_per_row=self.lanes_per_row, stream=stream)
+        self.run_head(stream)
+
+    def run_head(self, stream=None) -> None:
         if self.head == "q6k":
             self.lm_head_q6k(stream)
         else:
             self.lm_head(stream)
+
+    def make_pass(self, chained: bool = True) -> "bqd.DecodePass":
+        """The 140 group-32 linears as one persistent pass.  chained: linear
+        i reads the first K_i values of linear i-1's output (fp32, through
+        the pass's exchange; linear 0 reads its activation widened to fp32),
+        outputs in ``.outputs``; otherwise each linear reads its own fp16
+        activation and writes the stream's outputs."""
+        lins = [bqd.make_linear(d["wq"], d["s16"], None) for d in self.linears]
+        if chained:
+            ys = [torch.empty(d["N"], dtype=torch.float32, device=self.device) for d in self.linears]
+            x0 = self.linears[0]["x"].float()
+            xs = [x0] + [ys[i - 1][:d["K"]] for i, d in enumerate(self.linears) if i > 0]
+        else:
+            ys = [d["y"] for d in self.linears]
+            xs = [d["x"] for d in self.linears]
+        p = bqd.DecodePass(lins, xs, ys, self.device)
+        p.outputs = ys
+        p.inputs = xs
+        return p
+
+    def pass_bytes(self, chained: bool = True) -> int:
+        """Algorithmic bytes of the pass's linears (fp32 activations when
+        chained, fp16 otherwise) plus the lm_head."""
+        xb = 4 if chained else 2
+        return sum(bytes_group32_linear(d["N"], d["K"], False, xb) for d in self.linears) + self.head_bytes()
 
     def lm_head(self, stream=None) -> None:
         """The int8-expanded lm_head (W8A16, fp16 group-32 scales)."""

@@ -150,7 +150,7 @@ def test_decode_pass_encode_validates_and_serialises():
     L = _lib()
     n = 2
     nbytes = L.decode_pass_desc_bytes(n)
-    assert nbytes == 16 + 2 * 88
+    assert nbytes == 16 + 2 * 96
     host = (C.c_uint8 * nbytes)()
     mk = C.c_int32(0)
     sb = C.c_size_t(0)
@@ -168,7 +168,9 @@ def test_decode_pass_encode_validates_and_serialises():
     b = bqd.LinearW4A8(P + 0x1000, P + 0x500, P + 0x600, 7, 18944, 0, 0, 0)
     assert enc([a, b], nbytes=100) == SHAPE
     assert enc([a, b], dt=4) == DTYPE
-    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 1, 0, 0)]) == DTYPE       # group-32 scales
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 2, 0, 0)]) == DTYPE       # unknown scale kind
+    assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 96, 1, 0, 0)]) == SHAPE       # group-32: K % 256
+    assert enc([a, bqd.LinearW4A8(P, P + 8, 0, 7, 256, 1, 0, 0)]) == ALIGN  # group-32 scales: 16-byte aligned
     assert enc([a, bqd.LinearW4A8(P, P, 0, 7, 64, 0, 2, 16)]) == CONFIG     # the pass picks the split
     assert enc([a, bqd.LinearW4A8(P, P, 0, 0, 64, 0, 0, 0)]) == SHAPE       # N = 0
     assert enc([a, bqd.LinearW4A8(P4, P, 0, 7, 64, 0, 0, 0)]) == ALIGN
@@ -215,10 +217,10 @@ def test_decode_pass_encode_validates_and_serialises():
     hn, grid, hk, words = struct.unpack("<4i", raw[:16])
     assert (hn, hk, words) == (2, 18944, 0) and 0 < grid <= 1024   # nothing read from the exchange
     assert sb.value == (64 + 1024 * 16) * 4                        # err line + epoch lines
-    f = struct.unpack("<5Q12i", raw[16 + 88:16 + 176])
+    f = struct.unpack("<5Q14i", raw[16 + 96:16 + 192])
     assert f[:5] == (P + 0x1000, P + 0x500, P + 0x600, X1, Y1)
-    N, C_, base, extra, lshift, r, iters, batches, steps, xin, xout, xdt = f[5:]
-    assert (N, C_, base, extra, xin, xout, xdt) == (7, 592, 7 // grid, 7 % grid, -1, -1, 1)
+    N, C_, base, extra, lshift, r, iters, batches, steps, xin, xout, xdt, kind, _ = f[5:]
+    assert (N, C_, base, extra, xin, xout, xdt, kind) == (7, 592, 7 // grid, 7 % grid, -1, -1, 1, 0)
     assert lshift in (4, 5, 6) and r in (1, 2)
     assert iters == -(-592 // (1 << lshift)) and steps == -(-iters * r // 8)
     # the chain: y[0] gets 20000 exchange words (+ its offset mod 16 bytes),
@@ -227,7 +229,7 @@ def test_decode_pass_encode_validates_and_serialises():
     raw = bytes(host)
     words = struct.unpack("<4i", raw[:16])[3]
     xin0, xout0 = struct.unpack("<2i", raw[16 + 76:16 + 84])
-    xin1, xout1 = struct.unpack("<2i", raw[16 + 88 + 76:16 + 88 + 84])
+    xin1, xout1 = struct.unpack("<2i", raw[16 + 96 + 76:16 + 96 + 84])
     assert (xin0, xout0, xout1) == (-1, (Y0 >> 2) & 3, -1) and xin1 == xout0 + 16
     assert words == -(-(20000 + 3) // 64) * 64 and sb.value == (64 + 1024 * 16 + 2 * words) * 4
 

@@ -788,6 +788,88 @@ def test_qwen_stream_full_size_persistent_sampled():
     sync()
 
 
+def _g32_pass(tag, chained):
+    """Two Gemma-shaped group-32 layers (QKV, O, gate/up, down) as one pass:
+    fp16 activations written before the launch, or chained through fp32
+    outputs (linear i+1 reads the first K values of linear i's output)."""
+    lins, parts, xs, ys, xhost = [], [], [], [], []
+    for l in range(2):
+        for name, N, K in I.gemma_layer_linears():
+            W = I.normal(f"gpu/{tag}/{l}/{name}/W", (N, K), 0.02)
+            wq, s16 = bqd.quantize_weights_int4_group32(W.to(DEV))
+            lins.append(bqd.make_linear(wq, s16, None))
+            parts.append((W, wq, s16))
+            ys.append(torch.full((N,), float("nan"), device=DEV))
+            if not chained:
+                xh = I.linear_input(f"gpu/{tag}/{l}", name, K, 0, "cpu", torch.float16)
+                xhost.append(xh)
+                xs.append(xh.to(DEV))
+    if chained:
+        xh = I.normal(f"gpu/{tag}/x0", parts[0][0].shape[1], 1.0)
+        xhost.append(xh)
+        xs = [xh.to(DEV)] + [ys[i - 1][:W.shape[1]] for i, (W, _, _) in enumerate(parts) if i > 0]
+    return lins, parts, xs, ys, xhost
+
+
+def _g32_oracle_first(parts, xhost, y):
+    """The pass's first linear against the oracle run from the host's fp32
+    weights and activation: packed words and scales equal, y within the
+    tolerance of the magnitude before cancellation."""
+    W, wq, s16 = parts[0]
+    wr, sr = O.prepare_int4_group32(W.numpy())
+    assert np.array_equal(u32(wq), wr) and np.array_equal(f16bits(s16), sr)
+    xr = xhost[0].numpy()
+    _, sxr, accr, yr = O.linear_w4a8_group32(wr, sr, None, xr)
+    mag = float(sxr) * np.abs(sr.view(np.float16).astype(np.float64) * accr).sum(1)
+    assert rel_err(npy(y), yr, mag).max() <= TOL
+
+
+def test_decode_pass_group32_equals_per_linear_launches():
+    """Group-32 linears ("在香橙派上跑 Gemma4 ..." section 3.1) in the pass, fp16
+    activations: every output equals linear_w4a8_group32 bit for bit over
+    three passes (same lanes per row, chunk order and sum tree), and the
+    first linear matches the oracle."""
+    lins, parts, xs, ys, xhost = _g32_pass("g32pass", chained=False)
+    ref = [bqd.linear_w4a8_group32(wq, s16, None, x) for (_, wq, s16), x in zip(parts, xs)]
+    p = bqd.DecodePass(lins, xs, ys)
+    assert p.sources() == [-1] * len(lins)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        p.run()
+        sync()
+        assert p.error_word() == 0
+        for i, (y, yr) in enumerate(zip(ys, ref)):
+            assert torch.equal(y, yr), (rep, i)
+    _g32_oracle_first(parts, xhost, ys[0])
+
+
+def test_decode_pass_group32_chained():
+    """The same two group-32 layers chained through the exchange (fp32
+    activations): every output equals the chain launched one linear at a
+    time, over three passes; the first linear matches the oracle.  (Each
+    group-32 output is a sum in fp32 whose rounding depends on the lanes'
+    order, so further links are compared with the per-linear chain, which
+    sums in the same order, not with an oracle chain.)"""
+    lins, parts, xs, ys, xhost = _g32_pass("g32chain", chained=True)
+    ref, xr = [], xs[0]
+    for i, (W, wq, s16) in enumerate(parts):
+        ref.append(bqd.linear_w4a8_group32(wq, s16, None, xr))
+        xr = ref[-1][:parts[i + 1][0].shape[1]] if i + 1 < len(parts) else None
+    p = bqd.DecodePass(lins, xs, ys)
+    src = p.sources()
+    assert src[0] == -1 and all(v >= 0 for v in src[1:])
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        p.run()
+        sync()
+        assert p.error_word() == 0
+        for i, (y, yr) in enumerate(zip(ys, ref)):
+            assert torch.equal(y, yr), (rep, i)
+    _g32_oracle_first(parts, xhost, ys[0])
+
+
 def test_decode_pass_rejects_descriptors_for_another_grid():
     """Descriptors encoded for another grid size are refused in the kernel
     (error bit 1, nothing computed) instead of being misread."""
