@@ -30,6 +30,7 @@
 #include <cfloat>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -2929,6 +2930,37 @@ int unpack_int4_rows_host(const uint32_t* w, int32_t N, int32_t K, int8_t* out)
 
 inline int prod_items(int K);
 
+static bool bytes_overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// One buffer of a launch: address and bytes (NULL or empty: absent).
+struct Span {
+    const void* p;
+    size_t n;
+};
+
+// True when an output overlaps anything the launch reads or another output.
+// Every workgroup of these kernels reads the activation (and its own rows'
+// weights) while other workgroups already write outputs, so an overlap
+// would make the results depend on timing.
+static bool io_overlap(std::initializer_list<Span> ins, std::initializer_list<Span> outs)
+{
+    for (const Span* o = outs.begin(); o != outs.end(); ++o) {
+        if (!o->p || !o->n)
+            continue;
+        for (const Span& i : ins)
+            if (i.p && i.n && bytes_overlap(o->p, o->n, i.p, i.n))
+                return true;
+        for (const Span* o2 = o + 1; o2 != outs.end(); ++o2)
+            if (o2->p && o2->n && bytes_overlap(o->p, o->n, o2->p, o2->n))
+                return true;
+    }
+    return false;
+}
+
 int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K, int8_t* qx, float* sx,
                  void* stream)
 {
@@ -2945,6 +2977,8 @@ int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K, int8_t* q
         return BQD_ERR_NULL;
     if (!aligned(x, 16) || !aligned(qx, 16) || !aligned(sx, 4))
         return BQD_ERR_ALIGN;
+    if (io_overlap({{x, (size_t)M * K * (x_dtype == BQD_F32 ? 4 : 2)}}, {{qx, (size_t)M * K}, {sx, 4 * (size_t)M}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     if (x_dtype == BQD_F32 && K <= BQD_MAX_PROD_K && M <= 65535) {
@@ -2995,6 +3029,21 @@ int add_rmsnorm_quant(const float* h, const float* delta, const float* gamma, fl
     if (!aligned(h, 16) || !aligned(delta, 16) || !aligned(gamma, 16) || !aligned(h_out, 16) ||
         !aligned(y_out, 16) || !aligned(qx, 16) || !aligned(sx, 4))
         return BQD_ERR_ALIGN;
+    {
+        // h_out and y_out may each be h or delta itself (every element is read
+        // by the thread that later writes it), never a shifted view of them.
+        const size_t tb = 4 * (size_t)M * K;
+        const auto same_or_apart = [tb](const void* o, const void* i) {
+            return !o || !i || o == i || !bytes_overlap(o, tb, i, tb);
+        };
+        if (!same_or_apart(h_out, h) || !same_or_apart(h_out, delta) || !same_or_apart(y_out, h) ||
+            !same_or_apart(y_out, delta))
+            return BQD_ERR_SHAPE;
+        if (io_overlap({{gamma, 4 * (size_t)K}}, {{h_out, tb}, {y_out, tb}}) ||
+            io_overlap({{h, tb}, {delta, tb}, {gamma, 4 * (size_t)K}, {h_out, tb}, {y_out, tb}},
+                       {{qx, (size_t)M * K}, {sx, 4 * (size_t)M}}))
+            return BQD_ERR_SHAPE;
+    }
     if ((rc = bqd_init()))
         return rc;
     hipStream_t st = (hipStream_t)stream;
@@ -3024,6 +3073,8 @@ int swiglu_quant(const float* gu, float* h_out, int8_t* qx, float* sx, int32_t M
         return BQD_ERR_NULL;
     if (!aligned(gu, 16) || !aligned(h_out, 16) || !aligned(qx, 16) || !aligned(sx, 4))
         return BQD_ERR_ALIGN;
+    if (io_overlap({{gu, 8 * (size_t)M * I}}, {{h_out, 4 * (size_t)M * I}, {qx, (size_t)M * I}, {sx, 4 * (size_t)M}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     hipStream_t st = (hipStream_t)stream;
@@ -3060,6 +3111,9 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8
     if (!aligned(wq, 16) || !aligned(qx, 16) || !aligned(sw, 4) || !aligned(sx, 4) ||
         !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4))
         return BQD_ERR_ALIGN;
+    if (io_overlap({{wq, (size_t)N * K / 2}, {sw, 4 * (size_t)N}, {bias, 4 * (size_t)N}, {qx, (size_t)K}, {sx, 4}},
+                   {{y, 4 * (size_t)N}, {acc, 4 * (size_t)N}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     return launch_gemv_rowwise<X_Q8>(wq, sw, bias, qx, sx, y, acc, nullptr, nullptr, N, K,
@@ -3086,6 +3140,10 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
         return BQD_ERR_ALIGN;
     if (!valid_config(r, lanes_per_row))
         return BQD_ERR_CONFIG;
+    if (io_overlap({{wq, (size_t)N * K / 2}, {sw, 4 * (size_t)N}, {bias, 4 * (size_t)N},
+                    {x, (size_t)K * (x_dtype == BQD_F32 ? 4 : 2)}},
+                   {{y, 4 * (size_t)N}, {qx_out, (size_t)K}, {sx_out, 4}, {acc, 4 * (size_t)N}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 1);
@@ -3096,16 +3154,6 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
                                       (hipStream_t)stream);
 }
 
-static bool overlaps(const float* a, const float* b, int K)
-{
-    return a && b && a < b + K && b < a + K;
-}
-
-static bool bytes_overlap(const void* a, size_t na, const void* b, size_t nb)
-{
-    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-    return pa < pb + nb && pb < pa + na;
-}
 
 int linear_rmsnorm_w4a8(const uint32_t* wq, const float* sw, const float* bias, const float* h,
                         const float* delta, const float* gamma, float eps, float* h_out, float* y,
@@ -3121,8 +3169,6 @@ int linear_rmsnorm_w4a8(const uint32_t* wq, const float* sw, const float* bias, 
         return BQD_ERR_BOUND;
     if (!(eps >= 0.0f) || !(eps <= FLT_MAX))
         return BQD_ERR_SHAPE;
-    if (overlaps(h_out, h, K) || overlaps(h_out, delta, K))
-        return BQD_ERR_SHAPE;  // other workgroups still read h and delta while workgroup 0 writes
     if (N == 0)
         return BQD_OK;
     if (!wq || !sw || !h || !gamma || !y)
@@ -3133,6 +3179,11 @@ int linear_rmsnorm_w4a8(const uint32_t* wq, const float* sw, const float* bias, 
         return BQD_ERR_ALIGN;
     if (!valid_config(r, lanes_per_row))
         return BQD_ERR_CONFIG;
+    if (io_overlap({{wq, (size_t)N * K / 2}, {sw, 4 * (size_t)N}, {bias, 4 * (size_t)N}, {h, 4 * (size_t)K},
+                    {delta, 4 * (size_t)K}, {gamma, 4 * (size_t)K}},
+                   {{y, 4 * (size_t)N}, {h_out, 4 * (size_t)K}, {qx_out, (size_t)K}, {sx_out, 4},
+                    {acc, 4 * (size_t)N}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 1);
@@ -3159,6 +3210,10 @@ int gemv_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bias
         return BQD_ERR_ALIGN;
     if (!valid_config(r, lanes_per_row))
         return BQD_ERR_CONFIG;
+    if (io_overlap({{wq, (size_t)N * K / 2}, {s16, (size_t)N * (K / 32) * 2}, {bias, 4 * (size_t)N},
+                    {qx, (size_t)K}, {sx, 4}},
+                   {{y, 4 * (size_t)N}, {acc_g, (size_t)N * (K / 32) * 4}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     return launch_gemv_group32<X_Q8>(wq, s16, bias, qx, sx, y, acc_g, nullptr, nullptr, N, K,
@@ -3185,6 +3240,10 @@ int linear_w4a8_group32(const uint32_t* wq, const uint16_t* s16, const float* bi
         return BQD_ERR_ALIGN;
     if (!valid_config(r, lanes_per_row))
         return BQD_ERR_CONFIG;
+    if (io_overlap({{wq, (size_t)N * K / 2}, {s16, (size_t)N * (K / 32) * 2}, {bias, 4 * (size_t)N},
+                    {x, (size_t)K * (x_dtype == BQD_F32 ? 4 : 2)}},
+                   {{y, 4 * (size_t)N}, {qx_out, (size_t)K}, {sx_out, 4}, {acc_g, (size_t)N * (K / 32) * 4}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 2);
@@ -3211,6 +3270,8 @@ int gemv_w8a16_group32(const int8_t* w8, const uint16_t* s16, const uint16_t* x1
         return BQD_ERR_NULL;
     if (!aligned(w8, 16) || !aligned(x16, 16) || !aligned(s16, 2) || !aligned(y, 4))
         return BQD_ERR_ALIGN;
+    if (io_overlap({{w8, (size_t)N * K}, {s16, (size_t)N * (K / 32) * 2}, {x16, 2 * (size_t)K}}, {{y, 4 * (size_t)N}}))
+        return BQD_ERR_SHAPE;
     if (!valid_config(r, lanes_per_row))
         return BQD_ERR_CONFIG;
     const int L = lanes_per_row ? lanes_per_row : 16;
@@ -3372,6 +3433,10 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
     if (!aligned(wq, 16) || !aligned(qx, 16) || !aligned(sw, 4) || !aligned(sx, 4) ||
         !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4))
         return BQD_ERR_ALIGN;
+    if (io_overlap({{wq, (size_t)N * K / 2}, {sw, 4 * (size_t)N}, {bias, 4 * (size_t)N}, {qx, (size_t)M * K},
+                    {sx, 4 * (size_t)M}},
+                   {{y, 4 * (size_t)M * N}, {acc, 4 * (size_t)M * N}}))
+        return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     const int C = K / 32;
@@ -3476,6 +3541,13 @@ int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const*
             return BQD_ERR_ALIGN;
         if (!valid_config(l.r, l.lanes_per_row))
             return BQD_ERR_CONFIG;
+        // each linear is its own launch, so only a linear's own output may
+        // not overlap what that launch reads
+        const size_t sb = l.scale_kind == BQD_SCALE_ROW_F32 ? 4 * (size_t)l.N : (size_t)l.N * (l.K / 32) * 2;
+        if (io_overlap({{l.wq, (size_t)l.N * l.K / 2}, {l.scales, sb}, {l.bias, 4 * (size_t)l.N},
+                        {x[i], (size_t)l.K * (x_dtype == BQD_F32 ? 4 : 2)}},
+                       {{y[i], 4 * (size_t)l.N}}))
+            return BQD_ERR_SHAPE;
     }
     for (int i = 0; i < n; ++i) {
         const bqd_linear_w4a8& l = lin[i];

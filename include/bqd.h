@@ -59,6 +59,15 @@ extern "C" {
 #define BQD_ERR_LAUNCH (-7)    /* the HIP runtime rejected a launch          */
 #define BQD_ERR_DEVICE (-8)    /* no HIP device, or not a gfx950 device      */
 
+/* Buffers of one launch: an output of a per-token entry point (y, acc,
+ * qx_out, sx_out, h_out, ...) may overlap neither another output of the same
+ * call nor anything that call reads (weights, scales, bias, x, qx, sx, h,
+ * delta, gamma): every workgroup reads the inputs while other workgroups
+ * already write, so such a call is refused with BQD_ERR_SHAPE and nothing
+ * launched.  add_rmsnorm_quant's h_out / y_out, which may equal h or delta
+ * (each element is read before it is written by the same thread), and the
+ * persistent pass's chaining rules below are the stated exceptions. */
+
 #define BQD_F32 0              /* activation dtype: IEEE binary32            */
 #define BQD_F16 1              /* activation dtype: IEEE binary16            */
 
@@ -165,8 +174,8 @@ int add_rmsnorm_quant(const float* h, const float* delta, const float* gamma, fl
  * runs the GEMV of gemv_w4a8 on them; workgroup 0 writes h1 to h_out.
  *   y[j] = sw[j] * s^x * acc[j] + bias[j]
  * h, delta (NULL allowed), gamma, h_out (NULL allowed): device float [K],
- * 16-byte aligned; h_out must not overlap h or delta (BQD_ERR_SHAPE: other
- * workgroups read them while workgroup 0 writes).  qx_out int8 [K], sx_out
+ * 16-byte aligned; no output may overlap h, delta, gamma or another output
+ * (BQD_ERR_SHAPE: other workgroups read them while workgroup 0 writes).  qx_out int8 [K], sx_out
  * float [1], acc int32 [N]: optional outputs.  K % 32 == 0 and K <= 8192
  * (BQD_ERR_BOUND); eps >= 0 finite.  r, lanes_per_row as in gemv_w4a8. */
 int linear_rmsnorm_w4a8(const uint32_t* wq, const float* sw, const float* bias, const float* h,
@@ -357,7 +366,9 @@ typedef struct bqd_linear_w4a8 {
  * With q/k/v and gate/up rows concatenated at load time ("在香橙派上跑 Gemma4
  * ...", section 3.1) a layer is 4 linears and 4 launches.  lin (host) [n];
  * x (host) array of n device pointers to [K_i] activations of x_dtype;
- * y (host) array of n device pointers to float [N_i].  0 <= n <= 64. */
+ * y (host) array of n device pointers to float [N_i].  0 <= n <= 64.
+ * y[i] may not overlap x[i] or linear i's weights, scales or bias; it may
+ * be a later linear's x (the launches run in order on the stream). */
 int layer_w4a8_forward(const bqd_linear_w4a8* lin, int32_t n, const void* const* x,
                        int32_t x_dtype, float* const* y, void* stream);
 

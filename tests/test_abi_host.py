@@ -112,17 +112,90 @@ def test_other_entry_points_validate_before_launch():
 
 def test_layer_forward_validates_every_linear_first():
     L = _lib()
-    good = bqd.LinearW4A8(P, P, 0, 8, 64, 0, 0, 0)
-    bad_k = bqd.LinearW4A8(P, P, 0, 8, 40, 0, 0, 0)
-    bad_kind = bqd.LinearW4A8(P, P, 0, 8, 64, 3, 0, 0)
-    xs = (C.c_void_p * 2)(P, P)
-    ys = (C.c_void_p * 2)(P, P)
+    good = bqd.LinearW4A8(P, P + 0x1000, 0, 8, 64, 0, 0, 0)
+    bad_k = bqd.LinearW4A8(P, P + 0x1000, 0, 8, 40, 0, 0, 0)
+    bad_kind = bqd.LinearW4A8(P, P + 0x1000, 0, 8, 64, 3, 0, 0)
+    xs = (C.c_void_p * 2)(P + 0x2000, P + 0x3000)
+    ys = (C.c_void_p * 2)(P + 0x3000, P + 0x4000)
     arr = (bqd.LinearW4A8 * 2)(good, bad_k)
     assert L.layer_w4a8_forward(arr, 2, C.cast(xs, C.c_void_p), 0, C.cast(ys, C.c_void_p), None) == SHAPE
     arr = (bqd.LinearW4A8 * 2)(good, bad_kind)
     assert L.layer_w4a8_forward(arr, 2, C.cast(xs, C.c_void_p), 0, C.cast(ys, C.c_void_p), None) == DTYPE
     assert L.layer_w4a8_forward(arr, 65, C.cast(xs, C.c_void_p), 0, C.cast(ys, C.c_void_p), None) == SHAPE
     assert L.layer_w4a8_forward(None, 0, None, 0, None, None) == OK
+
+
+def _no_device():
+    return bqd.lib().bqd_init() == DEVICE
+
+
+def test_outputs_may_not_overlap_what_the_launch_reads():
+    """Every entry point refuses an output that overlaps one of its inputs
+    or another output: workgroups read the inputs while others write."""
+    L = _lib()
+    N, K = 8, 64
+    A = [P + 0x1000 * i for i in range(16)]   # disjoint 4 KiB windows
+    wq, sw, bias, qx, sx, y, acc, x = A[:8]
+    # gemv_w4a8(wq, sw, bias, qx, sx, y, acc, N, K, r, lanes, stream)
+    g = L.gemv_w4a8
+    assert g(wq, sw, bias, qx, sx, qx, None, N, K, 0, 0, None) == SHAPE       # y over qx
+    assert g(wq, sw, bias, qx, sx, y, y + 16, N, K, 0, 0, None) == SHAPE      # acc over y
+    assert g(wq, sw, bias, qx, sx, wq + 16, None, N, K, 0, 0, None) == SHAPE  # y inside the weights
+    assert g(wq, sw, bias, qx, sx, sx, None, N, K, 0, 0, None) == SHAPE
+    # linear_w4a8(wq, sw, bias, x, dtype, y, qx_out, sx_out, acc, N, K, r, lanes, stream)
+    f = L.linear_w4a8
+    assert f(wq, sw, bias, x, 0, x, None, None, None, N, K, 0, 0, None) == SHAPE           # y is x
+    assert f(wq, sw, bias, x, 0, y, x + 128, None, None, N, K, 0, 0, None) == SHAPE       # qx_out in x
+    assert f(wq, sw, bias, x, 1, y, None, x + 124, None, N, K, 0, 0, None) == SHAPE       # sx_out in fp16 x
+    assert f(wq, sw, bias, x, 0, y, qx, y + 28, None, N, K, 0, 0, None) == SHAPE          # sx_out in y
+    assert f(wq, sw, bias, x, 0, y, None, None, bias, N, K, 0, 0, None) == SHAPE          # acc over bias
+    # group-32: s16 is [N, K/32] fp16, acc_g [N, K/32] int32
+    h = L.gemv_w4a8_group32
+    assert h(wq, sw, bias, qx, sx, y, sw + 16, N, K, 0, 0, None) == SHAPE                 # acc_g over s16
+    assert h(wq, sw, bias, qx, sx, qx + 32, None, N, K, 0, 0, None) == SHAPE
+    h = L.linear_w4a8_group32
+    assert h(wq, sw, bias, x, 0, x + 252, None, None, None, N, K, 0, 0, None) == SHAPE
+    assert h(wq, sw, bias, x, 0, y, y, None, None, N, K, 0, 0, None) == SHAPE            # qx_out over y
+    # linear_rmsnorm_w4a8: every output apart from h, delta, gamma and each other
+    r = L.linear_rmsnorm_w4a8
+    hh, dd, gg, ho = A[8:12]
+    assert r(wq, sw, bias, hh, dd, gg, 1e-6, ho, gg, None, None, None, N, K, 0, 0, None) == SHAPE   # y over gamma
+    assert r(wq, sw, bias, hh, dd, gg, 1e-6, ho, y, ho + 64, None, None, N, K, 0, 0, None) == SHAPE  # qx_out in h_out
+    assert r(wq, sw, bias, hh, dd, gg, 1e-6, ho, y, qx, dd, None, N, K, 0, 0, None) == SHAPE      # sx_out in delta
+    assert r(wq, sw, bias, hh, dd, gg, 1e-6, ho, y, None, None, ho, N, K, 0, 0, None) == SHAPE    # acc over h_out
+    # quantize_act, the producers, verify and the W8A16 head
+    assert L.quantize_act(x, 0, 2, K, x + 256, sx, None) == SHAPE      # codes over token 1
+    assert L.quantize_act(x, 0, 2, K, qx, x + 508, None) == SHAPE
+    assert L.quantize_act(x, 0, 2, K, qx, qx + 64, None) == SHAPE     # sx over the codes of token 1
+    rq = L.add_rmsnorm_quant
+    assert rq(hh, dd, gg, 1e-6, hh + 16, None, qx, sx, 2, K, None) == SHAPE   # shifted h_out
+    assert rq(hh, dd, gg, 1e-6, None, gg, qx, sx, 2, K, None) == SHAPE        # y_out over gamma
+    assert rq(hh, dd, gg, 1e-6, ho, ho, qx, sx, 2, K, None) == SHAPE          # h_out and y_out one buffer
+    assert rq(hh, dd, gg, 1e-6, None, None, hh, sx, 2, K, None) == SHAPE      # codes over h
+    assert L.swiglu_quant(x, x + 256, qx, sx, 2, K, None) == SHAPE
+    assert L.swiglu_quant(x, ho, ho + 16, sx, 2, K, None) == SHAPE
+    assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, qx + 64, None, 2, N, K, 0, None) == SHAPE  # y over token 1
+    assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, y, y + 32, 2, N, K, 0, None) == SHAPE
+    assert L.gemv_w8a16_group32(wq, sw, x, x + 64, N, K, 0, 0, None) == SHAPE
+    # a layer: y[i] may be x[i+1], never x[i] itself
+    lin = bqd.LinearW4A8(wq, sw, 0, N, K, 0, 0, 0)
+    arr = (bqd.LinearW4A8 * 2)(lin, lin)
+    xs = (C.c_void_p * 2)(x, y)
+    bad = (C.c_void_p * 2)(y, y)
+    assert L.layer_w4a8_forward(arr, 2, C.cast(xs, C.c_void_p), 0, C.cast(bad, C.c_void_p), None) == SHAPE
+    if _no_device():
+        # the same calls with disjoint buffers pass every host check and reach
+        # the device lookup (no device here)
+        assert g(wq, sw, bias, qx, sx, y, acc, N, K, 0, 0, None) == DEVICE
+        assert f(wq, sw, bias, x, 0, y, qx, sx, acc, N, K, 0, 0, None) == DEVICE
+        assert r(wq, sw, bias, hh, dd, gg, 1e-6, ho, y, qx, sx, acc, N, K, 0, 0, None) == DEVICE
+        assert rq(hh, dd, gg, 1e-6, hh, dd, qx, sx, 2, K, None) == DEVICE   # in place is allowed
+        assert L.quantize_act(x, 0, 2, K, qx, sx, None) == DEVICE
+        assert L.swiglu_quant(x, ho, qx, sx, 2, K, None) == DEVICE
+        assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, y, acc, 2, N, K, 0, None) == DEVICE
+        assert L.gemv_w8a16_group32(wq, sw, x, y, N, K, 0, 0, None) == DEVICE
+        good = (C.c_void_p * 2)(y, acc)
+        assert L.layer_w4a8_forward(arr, 2, C.cast(xs, C.c_void_p), 0, C.cast(good, C.c_void_p), None) == DEVICE
 
 
 def test_host_pack_helpers_match_oracle():
