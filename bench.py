@@ -63,6 +63,10 @@ def parse():
                    help="before the timed region, run one plain device copy of this many MiB "
                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--weights-cache", default="", metavar="PATH",
+                   help="stream workload: copy the weights and activations from PATH (safetensors) when it "
+                        "holds this stream, else generate them and write PATH; a run that loads it launches "
+                        "none of the generator's kernels")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
 
@@ -300,11 +304,15 @@ def run_stream(a, dev):
     layers = a.layers or 28
     t0 = time.time()
     s = DS.QwenW4A8Stream(layers=layers, device=dev, r=a.r, lanes_per_row=a.lanes,
-                          persistent=not (a.per_linear or a.w4a16))
+                          persistent=not (a.per_linear or a.w4a16), cache=a.weights_cache or None)
     if a.w4a16:
         return run_stream_w4a16(a, dev, s, layers)
     log(f"stream built: {len(s.linears)} linears, {s.weight_bytes() / 1e9:.3f} GB packed, "
-        f"{time.time() - t0:.1f} s")
+        f"{time.time() - t0:.1f} s ({'copied from ' + a.weights_cache if s.cached else 'generated'})")
+    if a.weights_cache and not s.cached:
+        t0 = time.time()
+        s.save(a.weights_cache)
+        log(f"stream written to {a.weights_cache}, {time.time() - t0:.1f} s")
     st = torch.cuda.current_stream()
     if a.copy_calibration:
         src = torch.empty(a.copy_calibration << 18, dtype=torch.float32, device=dev).fill_(1.0)
@@ -844,6 +852,14 @@ def main():
     out = {"stream": run_stream, "single": run_single, "layer": run_layer, "gemma": run_gemma,
            "verify": run_verify, "chain": run_chain, "int8x": run_int8x}[a.workload](a, dev)
     print(json.dumps(out), flush=True)
+    # Tear the device state down before the interpreter exits: every launch
+    # done, the workload's buffers and passes dropped, torch's cache empty.
+    import gc
+    torch.cuda.synchronize()
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    log("done")
 
 
 if __name__ == "__main__":

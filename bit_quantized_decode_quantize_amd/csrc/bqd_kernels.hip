@@ -1856,8 +1856,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 }
 
 // ------------------------------------------------------------------------
-// Persistent token pass: every linear of a decode step in one cooperative
-// launch, one 1024-thread workgroup per CU.
+// Persistent token pass: every linear of a decode step in one launch, one
+// 1024-thread workgroup per CU, all resident at once.
 //
 // Dependencies travel with the data.  When linear t reads an output of an
 // earlier linear k of the same pass (a decoder's chain: each GEMV's input is
@@ -3789,8 +3789,14 @@ static int pass_launch(const void* desc_dev, int32_t n, int32_t max_k, uint32_t*
     int nn = n, mk = max_k;
     size_t words = sync_bytes / 4;
     void* args[] = {(void*)&hdr, (void*)&tasks, (void*)&nn, (void*)&mk, (void*)&sync, (void*)&words, (void*)&spin};
-    if (hipLaunchCooperativeKernel((const void*)k_decode_pass, dim3(G), dim3(kPassThreads), args,
-                                   (unsigned)pass_lds_bytes(max_k), stream) != hipSuccess)
+    // An ordinary launch: the grid is what the occupancy query says fits at
+    // once (one workgroup per CU), so on a device with no other work every
+    // workgroup is resident from the start; were some held back by other
+    // work, the bounded waits end them with bit 0 of the error word instead
+    // of a hang.  (A cooperative launch gives the same residency, costs
+    // about 1.5 % per pass and has made the profiler's exit handlers crash.)
+    if (hipLaunchKernel((const void*)k_decode_pass, dim3(G), dim3(kPassThreads), args,
+                        (size_t)pass_lds_bytes(max_k), stream) != hipSuccess)
         return BQD_ERR_LAUNCH;
     return launched();
 }

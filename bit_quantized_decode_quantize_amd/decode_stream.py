@@ -17,7 +17,8 @@ this path (norms, attention, residuals).
 """
 from __future__ import annotations
 
-from typing import Dict, List, Tuple
+import os
+from typing import Dict, List, Optional, Tuple
 
 import torch
 
@@ -65,32 +66,61 @@ def layer_inputs(prefix: str, seed: int, device) -> Dict[str, torch.Tensor]:
     return out
 
 
+def load_cache(path: str, meta: Dict[str, str], device) -> Optional[Dict[str, torch.Tensor]]:
+    """Tensors of a stream cache written by ``QwenW4A8Stream.save``, copied
+    to ``device``, or None when ``path`` is missing or holds another stream.
+    safetensors stores raw tensors only: nothing in the file is executed."""
+    from safetensors import safe_open
+    if not os.path.exists(path):
+        return None
+    with safe_open(path, framework="pt", device="cpu") as f:
+        if f.metadata() != meta:
+            return None
+        return {k: f.get_tensor(k).to(device) for k in f.keys()}
+
+
 def algorithmic_bytes_linear(N: int, K: int, bias: bool, x_bytes: int = 4) -> int:
     """Bytes one fused decode linear must move: packed weights N*K/2, fp32
     scales 4N, bias 4N, the activation x (read once), the output y 4N."""
     return N * K // 2 + 4 * N + (4 * N if bias else 0) + K * x_bytes + 4 * N
 
 
+CACHE_FORMAT = "qwen-w4a8-stream/1"
+
+
 class QwenW4A8Stream:
+    """``cache``: path of a safetensors file holding a stream built earlier
+    with the same layers, seed and head (``save``); when it matches, every
+    tensor is copied from it instead of being generated and quantised, so
+    the process launches none of the generator's or quantiser's kernels."""
+
     def __init__(self, layers: int = 28, seed: int = 0, device="cuda", lm_head: bool = True,
-                 r: int = 0, lanes_per_row: int = 0, persistent: bool = True):
+                 r: int = 0, lanes_per_row: int = 0, persistent: bool = True, cache: Optional[str] = None):
         self.device = torch.device(device)
         self.layers = layers
         self.seed = seed
+        self.lm_head = lm_head
         self.linears: List[Dict] = []       # every linear in step order
         self.plans: List[bqd.LayerPlan] = []
+        self.cached = load_cache(cache, self.cache_meta(), self.device) if cache else None
+        c = self.cached
         for l in range(layers):
             prefix = f"qwen/L{l}"
             descs, xs, ys = [], [], []
-            biases = layer_biases(prefix, seed, self.device)
-            inputs = layer_inputs(prefix, seed, self.device)
+            if c is None:
+                biases = layer_biases(prefix, seed, self.device)
+                inputs = layer_inputs(prefix, seed, self.device)
             for name, N, K in I.qwen_layer_linears():
-                W = linear_weight_fp32(prefix, name, seed, self.device)
-                assert W.shape == (N, K)
-                wq, sw = bqd.quantize_weights_int4_rowwise(W)
-                del W
-                b = biases[name]
-                x = inputs[name]
+                i = len(self.linears)
+                if c is not None:
+                    wq, sw, b, x = c[f"{i}.wq"], c[f"{i}.sw"], c.get(f"{i}.b"), c[f"{i}.x"]
+                else:
+                    W = linear_weight_fp32(prefix, name, seed, self.device)
+                    assert W.shape == (N, K)
+                    wq, sw = bqd.quantize_weights_int4_rowwise(W)
+                    del W
+                    b = biases[name]
+                    x = inputs[name]
                 y = torch.empty(N, dtype=torch.float32, device=self.device)
                 d = dict(layer=l, name=name, N=N, K=K, wq=wq, sw=sw, b=b, x=x, y=y, prefix=prefix)
                 self.linears.append(d)
@@ -100,10 +130,14 @@ class QwenW4A8Stream:
             self.plans.append(bqd.LayerPlan(descs, xs, ys))
         if lm_head:
             N, K = I.QWEN["vocab"], I.QWEN["hidden"]
-            W = I.normal("qwen/lm_head/W", (N, K), 0.02, seed, self.device)
-            wq, sw = bqd.quantize_weights_int4_rowwise(W)
-            del W
-            x = I.normal("qwen/lm_head/x", K, 1.0, seed, self.device)
+            i = len(self.linears)
+            if c is not None:
+                wq, sw, x = c[f"{i}.wq"], c[f"{i}.sw"], c[f"{i}.x"]
+            else:
+                W = I.normal("qwen/lm_head/W", (N, K), 0.02, seed, self.device)
+                wq, sw = bqd.quantize_weights_int4_rowwise(W)
+                del W
+                x = I.normal("qwen/lm_head/x", K, 1.0, seed, self.device)
             y = torch.empty(N, dtype=torch.float32, device=self.device)
             self.linears.append(dict(layer=layers, name="lm_head", N=N, K=K, wq=wq, sw=sw, b=None,
                                      x=x, y=y, prefix="qwen/lm_head"))
@@ -143,10 +177,7 @@ class QwenW4A8Stream:
         ``chained_pass``: the dependency between consecutive linears (store,
         poll, staging, a few rows) with next to no weight traffic."""
         n = len(self.linears)
-        W = I.normal("qwen/linkfloor/W", (n * size, size), 0.02, self.seed, self.device)
-        wq, sw = bqd.quantize_weights_int4_rowwise(W)
-        del W
-        x0 = I.normal("qwen/linkfloor/x", size, 1.0, self.seed, self.device)
+        wq, sw, x0 = self._link_floor_tensors(size)
         ys = [torch.empty(size, dtype=torch.float32, device=self.device) for _ in range(n)]
         lins = [bqd.make_linear(wq[i * size:(i + 1) * size], sw[i * size:(i + 1) * size], None) for i in range(n)]
         p = bqd.DecodePass(lins, [x0] + ys[:-1], ys, self.device)
@@ -163,6 +194,37 @@ class QwenW4A8Stream:
         p = bqd.DecodePass(lins, [d["x"] for d in self.linears], ys, self.device)
         p.outputs = ys
         return p
+
+    def _link_floor_tensors(self, size: int):
+        key = f"linkfloor{size}"
+        if self.cached is not None and f"{key}.wq" in self.cached:
+            return self.cached[f"{key}.wq"], self.cached[f"{key}.sw"], self.cached[f"{key}.x"]
+        W = I.normal("qwen/linkfloor/W", (len(self.linears) * size, size), 0.02, self.seed, self.device)
+        wq, sw = bqd.quantize_weights_int4_rowwise(W)
+        del W
+        return wq, sw, I.normal("qwen/linkfloor/x", size, 1.0, self.seed, self.device)
+
+    def cache_meta(self) -> Dict[str, str]:
+        return {"format": CACHE_FORMAT, "layers": str(self.layers), "seed": str(self.seed),
+                "lm_head": str(int(self.lm_head))}
+
+    def save(self, path: str, link_floor_sizes=(64,)) -> None:
+        """Write every tensor the stream generated (weights, scales, biases,
+        activations, and the link-floor linears of ``link_floor_sizes``)
+        to ``path`` (safetensors, written to a temporary name and renamed)."""
+        from safetensors.torch import save_file
+        t = {}
+        for i, d in enumerate(self.linears):
+            t[f"{i}.wq"], t[f"{i}.sw"], t[f"{i}.x"] = d["wq"], d["sw"], d["x"]
+            if d["b"] is not None:
+                t[f"{i}.b"] = d["b"]
+        for size in link_floor_sizes:
+            t[f"linkfloor{size}.wq"], t[f"linkfloor{size}.sw"], t[f"linkfloor{size}.x"] = \
+                self._link_floor_tensors(size)
+        t = {k: v.detach().contiguous().cpu() for k, v in t.items()}
+        tmp = f"{path}.tmp{os.getpid()}"
+        save_file(t, tmp, metadata=self.cache_meta())
+        os.replace(tmp, path)
 
     def bytes_per_step(self) -> int:
         return sum(algorithmic_bytes_linear(d["N"], d["K"], d["b"] is not None) for d in self.linears)

@@ -414,8 +414,8 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
                        float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k,
                        size_t* sync_bytes);
 
-/* One decode step over the n encoded linears in order, in one cooperative
- * launch: for each linear, the activation quantisation of quantize_act and
+/* One decode step over the n encoded linears in order, in one launch of one
+ * workgroup per compute unit, all resident at once: for each linear, the activation quantisation of quantize_act and
  * the GEMV of gemv_w4a8 (same codes, same y bits as linear_w4a8).  A linear
  * whose activation is an earlier linear's output waits for exactly those
  * values: each output row read later in the pass is also stored into an
