@@ -71,7 +71,15 @@ def parse():
     return p.parse_args()
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_pass_qwen2-7b-28L_traffic.md")
+# Counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) of
+# each workload's dominant kernel, at the configuration the file names.
+TRAFFIC = {w: os.path.join(ROOT, "profiles", f) for w, f in (
+    ("stream", "k_decode_pass_qwen2-7b-28L_traffic.md"),
+    ("layer", "k_decode_pass_qwen2-7b-layer-pool_traffic.md"),
+    ("single", "k_gemv_w4a8_single-q-proj-3584x3584_traffic.md"),
+    ("verify", "k_verify_mfma_verify-18944x3584-M16_traffic.md"),
+    ("gemma", "k_gemv_w8a16_g32_gemma-lm-head_traffic.md"))}
+TRAFFIC_SUMMARY = TRAFFIC["stream"]
 
 
 def _elf_sections(b):
@@ -89,10 +97,11 @@ def _elf_sections(b):
     return secs
 
 
-def kernel_code_sha256(lib_path, needle="k_decode_pass", arch="gfx950"):
+def kernel_code_sha256(lib_path, needle="k_decode_pass", arch="gfx950", exact=False):
     """sha256 of a kernel's machine code in the library's ``arch`` code
     object (the clang offload bundle in .hip_fatbin, then the symbol whose
-    name contains ``needle``), or None if it cannot be found."""
+    name contains ``needle``, or is ``needle`` when ``exact``), or None if it
+    cannot be found."""
     try:
         b = open(lib_path, "rb").read()
         fb = [sec for sec in _elf_sections(b) if sec["name"] == ".hip_fatbin"][0]
@@ -112,7 +121,7 @@ def kernel_code_sha256(lib_path, needle="k_decode_pass", arch="gfx950"):
             for i in range(sym["size"] // 24):
                 nm, info, _, _, val, size = struct.unpack_from("<IBBHQQ", co, sym["off"] + 24 * i)
                 name = co[strs + nm:co.index(b"\0", strs + nm)].decode()
-                if needle in name and (info & 0xF) == 2 and size:       # STT_FUNC
+                if (name == needle if exact else needle in name) and (info & 0xF) == 2 and size:  # STT_FUNC
                     text = [sec for sec in secs if sec["type"] == 1 and sec["addr"] <= val < sec["addr"] + sec["size"]][0]
                     start = text["off"] + val - text["addr"]
                     return hashlib.sha256(co[start:start + size]).hexdigest()
@@ -124,14 +133,18 @@ def kernel_code_sha256(lib_path, needle="k_decode_pass", arch="gfx950"):
 def measured_traffic(summary=TRAFFIC_SUMMARY):
     """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary (copy-calibrated), or None unless the library in use holds the
-    same k_decode_pass machine code as the one the counters were taken on."""
+    same machine code for the summary's kernel (``kernel_symbol``, else
+    k_decode_pass) as the one the counters were taken on."""
     from bit_quantized_decode_quantize_amd import bqd
     try:
         text = open(summary, encoding="utf-8").read()
     except OSError:
         return None
-    vals = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_code_sha256): (\S+)$", text, re.M))
-    sha = kernel_code_sha256(bqd.LIB_PATH)
+    vals = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_code_sha256|kernel_symbol): (\S+)$", text, re.M))
+    if "kernel_symbol" in vals:
+        sha = kernel_code_sha256(bqd.LIB_PATH, vals["kernel_symbol"], exact=True)
+    else:
+        sha = kernel_code_sha256(bqd.LIB_PATH)
     if sha is None or vals.get("kernel_code_sha256") != sha or "traffic_bytes_per_launch" not in vals:
         return None
     return int(vals["traffic_bytes_per_launch"])
@@ -314,14 +327,6 @@ def run_stream(a, dev):
         s.save(a.weights_cache)
         log(f"stream written to {a.weights_cache}, {time.time() - t0:.1f} s")
     st = torch.cuda.current_stream()
-    if a.copy_calibration:
-        src = torch.empty(a.copy_calibration << 18, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
-        del src, dst
 
     graph_steps = 1 if ((not a.eager) and a.per_linear) else 0
     step_bytes = s.bytes_per_step()
@@ -495,7 +500,8 @@ def run_single(a, dev):
     ms16, _ = time_steps(step16, a.steps, a.warmup, w.copies if (not a.eager) else 0)
     out["w4a16_us_per_gemv"] = round(ms16 * 1e3, 3)
     out["roofline"] = roofline(gbs, "k_gemv_w4a8 (fused linear, one launch per step)", ms * 1e3,
-                               w.bytes_per_step())
+                               w.bytes_per_step(),
+                               measured_traffic(TRAFFIC["single"]) if not (a.r or a.lanes) else None)
     if not a.no_cpu_baseline:
         import oracle as O
         d = I.single_gemv_inputs(0, "cpu")
@@ -529,7 +535,8 @@ def run_layer(a, dev):
         "launch": launch, "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
     out["us_per_layer"] = round(ms * 1e3, 3)
     out["implied_28_layer_gemv_us"] = round(28 * ms * 1e3, 1)
-    out["roofline"] = roofline(avg_bytes / (avg_us * 1e-6) / 1e9, kernel, avg_us, avg_bytes)
+    out["roofline"] = roofline(avg_bytes / (avg_us * 1e-6) / 1e9, kernel, avg_us, avg_bytes,
+                               measured_traffic(TRAFFIC["layer"]) if w.persistent else None)
     if not a.no_cpu_baseline:
         import oracle as O
         from bit_quantized_decode_quantize_amd import decode_stream as DS
@@ -607,7 +614,8 @@ def run_gemma(a, dev):
     out["lm_head_forms"] = heads
     h = heads[a.lm_head]
     kern = {"w8a16": "k_gemv_w8a16_g32", "q6k": "k_gemv_q6k"}[a.lm_head]
-    out["roofline"] = roofline(h["GB/s"], f"{kern} (lm_head, largest single launch)", h["us"], h["bytes"])
+    out["roofline"] = roofline(h["GB/s"], f"{kern} (lm_head, largest single launch)", h["us"], h["bytes"],
+                               measured_traffic(TRAFFIC["gemma"]) if a.lm_head == "w8a16" else None)
     if not a.no_cpu_baseline:
         import oracle as O
         work = []
@@ -667,7 +675,8 @@ def run_verify(a, dev):
     kname = ("k_gemv_w4a8" if last["M"] == 1 and a.impl == 0 else
              "k_verify_w4a8" if a.impl == 1 else "k_verify_mfma")
     out["roofline"] = roofline(last["GB/s"], f"{kname} (M={last['M']}, [18944,3584], one launch per step)",
-                               last["us"], wl_bytes)
+                               last["us"], wl_bytes,
+                               measured_traffic(TRAFFIC["verify"]) if (last["M"] == 16 and a.impl == 0) else None)
     if not a.no_cpu_baseline:
         import oracle as O
         from bit_quantized_decode_quantize_amd import inputs as I
@@ -849,6 +858,17 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.copy_calibration:
+        # One plain device-to-device copy of known size, for scaling the
+        # memory counters of a profiled run.
+        src = torch.empty(a.copy_calibration << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {src.numel() * 4} bytes read, {dst.numel() * 4} bytes written")
+        del src, dst
+        torch.cuda.empty_cache()
     out = {"stream": run_stream, "single": run_single, "layer": run_layer, "gemma": run_gemma,
            "verify": run_verify, "chain": run_chain, "int8x": run_int8x}[a.workload](a, dev)
     print(json.dumps(out), flush=True)

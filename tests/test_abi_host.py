@@ -486,9 +486,16 @@ def test_bench_reads_the_pass_kernel_code_hash():
     assert sha is not None and re.fullmatch(r"[0-9a-f]{64}", sha)
     assert bench.kernel_code_sha256(bqd.bqd.LIB_PATH, needle="no_such_kernel") is None
     assert bench.kernel_code_sha256(os.path.join(ROOT, "no_such_library.so")) is None
-    text = open(os.path.join(ROOT, "profiles", "k_decode_pass_qwen2-7b-28L_traffic.md")).read()
-    assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M)
-    assert re.search(r"^kernel_code_sha256: [0-9a-f]{64}$", text, re.M)
+    for path in bench.TRAFFIC.values():
+        if not os.path.exists(path):
+            continue
+        text = open(path).read()
+        assert re.search(r"^traffic_bytes_per_launch: \d+$", text, re.M), path
+        assert re.search(r"^kernel_code_sha256: [0-9a-f]{64}$", text, re.M), path
+        sym = re.search(r"^kernel_symbol: (\S+)$", text, re.M)
+        assert sym, path
+        # the symbol exists in the in-tree build (its code may have changed since)
+        assert bench.kernel_code_sha256(bqd.bqd.LIB_PATH, sym.group(1), exact=True) is not None, path
 
 
 def test_binding_constants_match_the_header():
