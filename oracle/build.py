@@ -16,12 +16,12 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
           "-fno-fast-math", "-Wall", "-Wextra", "-Werror"]
 
 
-def build(extra=()):
-    tmp = OUT + ".tmp"
+def build(extra=(), out=OUT):
+    tmp = out + ".tmp"
     cmd = ["gcc", *CFLAGS, *extra, SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -18,7 +18,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_LIB_PATH = os.environ.get("BQD_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _ERR = {-1: "bad argument", -2: "value outside the format's range",
         -3: "non-finite input", -4: "accumulator outside the int32 bound"}
