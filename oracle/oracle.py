@@ -479,6 +479,21 @@ def linear_w4a8_group32(w, s16, bias, x):
     return qx, sx, accg, y
 
 
+def rel_err_plain(y_test, y_ref, floor: float = 1e-3) -> float:
+    """max |y_test - y_ref| / |y_ref| over the rows with |y_ref| >= floor *
+    max |y_ref| (0 when there is none): the plain relative error reported
+    beside the gated one of ``rel_err_rowwise``."""
+    yt = np.asarray(y_test, np.float64).ravel()
+    yr = np.asarray(y_ref, np.float64).ravel()
+    if yr.size == 0:
+        return 0.0
+    big = np.abs(yr) >= floor * np.abs(yr).max()
+    big &= np.abs(yr) > 0
+    if not big.any():
+        return 0.0
+    return float((np.abs(yt[big] - yr[big]) / np.abs(yr[big])).max())
+
+
 def rel_err_rowwise(y_test, y_ref, sw, sx, acc, bias) -> np.ndarray:
     """|y_test - y_ref| / m_j with m_j = |sW_j sx acc_j| + |b_j|: the error
     relative to the row's magnitude before cancellation (0/0 counts as 0)."""

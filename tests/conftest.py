@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -32,3 +33,22 @@ def read_golden(name):
 @pytest.fixture
 def golden():
     return read_golden
+
+
+def pytest_terminal_summary(terminalreporter):
+    try:
+        import parity_log
+    except ImportError:
+        return
+    recs = parity_log.RECORDS
+    if not recs:
+        return
+    tr = terminalreporter
+    tr.section("parity: gated error (over the magnitude before cancellation) and plain relative error over |y_ref| >= 1e-3 max")
+    for r in recs:
+        tr.write_line(f"{r['test']} [{r['case']}]: rows {r['rows']}, gated {r['gated_max']:.3e}, "
+                      f"plain {r['plain_max']:.3e}")
+    out = os.environ.get("BQD_PARITY_REPORT")
+    if out:
+        with open(out, "w", encoding="utf-8") as f:
+            json.dump(recs, f, indent=1)

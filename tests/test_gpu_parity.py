@@ -12,6 +12,7 @@ import torch
 
 import bit_quantized_decode_quantize_amd as bqd
 import oracle as O
+import parity_log as P
 from bit_quantized_decode_quantize_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -161,8 +162,7 @@ def _check_rowwise(y, acc, w, sw, b, qx, sx):
     bb = None if b is None else npy(b)
     acc_r, y_r = O.gemv_w4a8(u32(w), npy(sw), bb, npy(qx), float(npy(sx)[0]))
     assert np.array_equal(npy(acc), acc_r)
-    err = O.rel_err_rowwise(npy(y), y_r, npy(sw), npy(sx)[0], acc_r, bb)
-    assert err.max() <= TOL, err.max()
+    P.check_rowwise(f"N={y.numel()} K={npy(qx).size}", npy(y), y_r, npy(sw), npy(sx)[0], acc_r, bb, TOL)
 
 
 GEMV_SHAPES = [(1, 32), (17, 64), (64, 96), (333, 3584), (3584, 3584), (130, 18944),
@@ -394,8 +394,7 @@ def test_gemm_w4a8_verify(M, N, K, impl):
     acc_r, y_r = O.gemm_w4a8_verify(u32(w), npy(sw), npy(b), npy(qx), npy(sx))
     assert np.array_equal(npy(acc), acc_r)
     for m in range(M):
-        err = O.rel_err_rowwise(npy(y)[m], y_r[m], npy(sw), npy(sx)[m], acc_r[m], npy(b))
-        assert err.max() <= TOL
+        P.check_rowwise(f"token {m}", npy(y)[m], y_r[m], npy(sw), npy(sx)[m], acc_r[m], npy(b), TOL)
     # token m's column equals the single-token GEMV bit for bit
     for m in (0, M - 1):
         y1 = bqd.gemv_w4a8(w, sw, b, qx[m].contiguous(), sx[m:m + 1].contiguous())
@@ -420,8 +419,7 @@ def test_gemm_w4a8_verify_mfma_row_tilings(M, N, K):
     acc_r, y_r = O.gemm_w4a8_verify(u32(w), npy(sw), npy(b), npy(qx), npy(sx))
     assert np.array_equal(npy(acc), acc_r)
     for m in range(M):
-        err = O.rel_err_rowwise(npy(y)[m], y_r[m], npy(sw), npy(sx)[m], acc_r[m], npy(b))
-        assert err.max() <= TOL
+        P.check_rowwise(f"token {m}", npy(y)[m], y_r[m], npy(sw), npy(sx)[m], acc_r[m], npy(b), TOL)
     assert torch.equal(y, y1)
 
 
@@ -463,8 +461,7 @@ def test_qwen_layer_full_size_sampled(persistent):
         assert np.array_equal(npy(d["sw"][idx]), sr)
         br = npy(d["b"][idx])
         qxr, sxr, accr, yr = O.linear_w4a8(wr, sr, br, npy(d["x"]))
-        err = O.rel_err_rowwise(npy(d["y"][idx]), yr, sr, sxr, accr, br)
-        assert err.max() <= TOL, (d["name"], err.max())
+        P.check_rowwise(d["name"], npy(d["y"][idx]), yr, sr, sxr, accr, br, TOL)
 
 
 # ------------------------------------------------------- persistent pass --
@@ -561,7 +558,7 @@ def test_decode_pass_chained():
     for i, (yr, (qx, sx, acc, y64, y32)) in enumerate(zip(ref, orc)):
         w_r, s_r, b_r = prepared[i]
         assert np.array_equal(npy(yr).view(np.uint32), y32.view(np.uint32)), i
-        assert O.rel_err_rowwise(npy(yr), y64, s_r, sx, acc, b_r).max() <= TOL, i
+        P.check_rowwise(f"linear {i}", npy(yr), y64, s_r, sx, acc, b_r, TOL)
     p = bqd.DecodePass(lins, xs, ys)
     src = p.sources()
     assert src[0] == -1 and all(v >= 0 for v in src[1:])
@@ -756,8 +753,7 @@ def test_qwen_stream_full_size_persistent_sampled():
         assert np.array_equal(u32(d["wq"][idx]), wr)
         br = None if d["b"] is None else npy(d["b"][idx])
         qxr, sxr, accr, y_r = O.linear_w4a8(wr, sr, br, npy(d["x"]))
-        err = O.rel_err_rowwise(npy(d["y"][idx]), y_r, sr, sxr, accr, br)
-        assert err.max() <= TOL, (k, err.max())
+        P.check_rowwise(f"linear {k} {d['name']}", npy(d["y"][idx]), y_r, sr, sxr, accr, br, TOL)
     # The same linears cut to 64 rows: the full pass's first 64 rows, bit
     # for bit.
     fp = s.cut_pass(64)

@@ -812,3 +812,15 @@ def test_chain_brute_force_tiny():
         assert np.array_equal(oy32.view(np.uint32), y32.view(np.uint32)), t
         if t + 1 < len(shapes):
             x = y32[:shapes[t + 1][1]]
+
+
+def test_plain_relative_error_by_hand():
+    """rel_err_plain: rows below 1e-3 of the largest |y_ref| (and zeros) are
+    left out; the rest give |y - y_ref| / |y_ref|, worked by hand."""
+    y_ref = np.array([1000.0, -2.0, 0.5, 0.0])
+    y = np.array([1000.5, -2.002, 0.6, 1.0])
+    assert O.rel_err_plain(y, y_ref) == pytest.approx(1e-3, rel=1e-9)      # the -2 row; 0.5 is below 1
+    assert O.rel_err_plain(y, y_ref, floor=1e-4) == pytest.approx(0.2, rel=1e-9)   # 0.5 now counts
+    assert O.rel_err_plain(y[:1], y_ref[:1]) == pytest.approx(5e-4, rel=1e-9)
+    assert O.rel_err_plain(np.zeros(3), np.zeros(3)) == 0.0
+    assert O.rel_err_plain(np.zeros(0), np.zeros(0)) == 0.0
