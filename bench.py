@@ -58,7 +58,8 @@ def parse():
     p.add_argument("--lm-head", choices=("w8a16", "q6k"), default="w8a16",
                    help="gemma: the lm_head form in the token step (int8-expanded or packed 6-bit)")
     p.add_argument("--verify-m", default="1,2,4,8,16")
-    p.add_argument("--impl", type=int, default=0, help="verify kernel: 0 automatic, 1 dot4, 2 MFMA")
+    p.add_argument("--impl", type=int, default=0,
+                   help="verify kernel: 0 automatic, 1 dot4, 2 MFMA per tile, 3 MFMA balanced blocks")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="before the timed region, run one plain device copy of this many MiB "
                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -77,7 +78,7 @@ TRAFFIC = {w: os.path.join(ROOT, "profiles", f) for w, f in (
     ("stream", "k_decode_pass_qwen2-7b-28L_traffic.md"),
     ("layer", "k_decode_pass_qwen2-7b-layer-pool_traffic.md"),
     ("single", "k_gemv_w4a8_single-q-proj-3584x3584_traffic.md"),
-    ("verify", "k_verify_mfma_verify-18944x3584-M16_traffic.md"),
+    ("verify", "k_verify_blocks_verify-18944x3584-M16_traffic.md"),
     ("gemma", "k_gemv_w8a16_g32_gemma-lm-head_traffic.md"))}
 TRAFFIC_SUMMARY = TRAFFIC["stream"]
 
@@ -660,8 +661,7 @@ def run_verify(a, dev):
             sx = torch.empty(M, dtype=torch.float32, device=dev)
             ms, n = time_steps(lambda: bqd.quantize_act(X, qx=qx, sx=sx), max(a.steps, 64), a.warmup,
                                0 if a.eager else 16)
-            qa.append({"K": K, "M": M, "us": round(ms * 1e3, 3),
-                       "GB/s": round(M * (5 * K + 4) / (ms * 1e-3) / 1e9, 1)})
+            qa.append({"K": K, "M": M, "us": round(ms * 1e3, 3)})
             del X, qx, sx
     log(f"quantize_act: {qa}")
     last = max((r for r in sweep if r["N"] == 18944), key=lambda r: r["M"])
@@ -671,9 +671,12 @@ def run_verify(a, dev):
                     "(per-token scales), bias", "impl": a.impl, "M": ms_list})
     out["sweep"] = sweep
     out["quantize_act"] = qa
+    out["quantize_act_note"] = ("graph-replayed calls on one resident X (L2-resident after the first): "
+                                "per-call latency, not a bandwidth")
     wl_bytes = WL.bytes_verify(last["M"], 18944, 3584)
     kname = ("k_gemv_w4a8" if last["M"] == 1 and a.impl == 0 else
-             "k_verify_w4a8" if a.impl == 1 else "k_verify_mfma")
+             "k_verify_w4a8" if a.impl == 1 else "k_verify_mfma" if a.impl == 2 or (a.impl == 0 and last["M"] < 8)
+             else "k_verify_blocks")
     out["roofline"] = roofline(last["GB/s"], f"{kname} (M={last['M']}, [18944,3584], one launch per step)",
                                last["us"], wl_bytes,
                                measured_traffic(TRAFFIC["verify"]) if (last["M"] == 16 and a.impl == 0) else None)

@@ -34,7 +34,8 @@ ENTRY_POINTS = (
     "quantize_weights_int4_rowwise", "quantize_weights_int4_group32",
     "quantize_weights_int8_group32", "pack_int4_rows_host", "unpack_int4_rows_host",
     "quantize_act", "gemv_w4a8", "linear_w4a8", "gemv_w4a8_group32",
-    "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "layer_w4a8_forward",
+    "linear_w4a8_group32", "gemv_w8a16_group32", "gemm_w4a8_verify", "gemm_w4a8_verify_workspace_bytes",
+    "layer_w4a8_forward",
     "decode_pass_desc_bytes", "decode_pass_encode", "decode_pass_w4a8", "decode_pass_w4a8_static",
     "read_probe", "gemv_w4a16", "add_rmsnorm_quant", "swiglu_quant", "linear_rmsnorm_w4a8",
     "quantize_weights_q6k", "gemv_q6k_f16", "int8x_counts_host", "int8x_stream_bytes_host",
@@ -83,7 +84,8 @@ def lib() -> C.CDLL:
         "gemv_w4a8_group32": (I, [P, P, P, P, P, P, P, I, I, I, I, P]),
         "linear_w4a8_group32": (I, [P, P, P, P, I, P, P, P, P, I, I, I, I, P]),
         "gemv_w8a16_group32": (I, [P, P, P, P, I, I, I, I, P]),
-        "gemm_w4a8_verify": (I, [P, P, P, P, P, P, P, I, I, I, I, P]),
+        "gemm_w4a8_verify": (I, [P, P, P, P, P, P, P, I, I, I, I, P, C.c_size_t, P]),
+        "gemm_w4a8_verify_workspace_bytes": (C.c_size_t, [I, I, I]),
         "layer_w4a8_forward": (I, [C.POINTER(LinearW4A8), I, P, I, P, P]),
         "decode_pass_desc_bytes": (C.c_size_t, [I]),
         "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32),
@@ -517,8 +519,30 @@ def gemv_w4a16(wq, sw, bias, x16, y=None, r=0, lanes_per_row=0, stream=None):
     return y
 
 
-def gemm_w4a8_verify(wq, sw, bias, qx, sx, y=None, acc=None, impl=0, stream=None):
-    """M tokens: qx int8 [M, K], sx fp32 [M] -> y fp32 [M, N] (and acc [M, N])."""
+_VERIFY_WS = {}
+
+
+def verify_workspace(M: int, N: int, K: int, device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace of at least the bytes gemm_w4a8_verify needs
+    for this shape, kept per device and grown when a shape needs more (the
+    kernel leaves it zeroed).  None when the shape needs none.  Calls that
+    share it must not overlap in time (one stream)."""
+    nb = lib().gemm_w4a8_verify_workspace_bytes(M, N, K)
+    if nb == 0:
+        return None
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _VERIFY_WS.get(key)
+    if ws is None or ws.numel() * 4 < nb:
+        ws = torch.zeros((nb + 255) // 4, dtype=torch.int32, device=dev)
+        _VERIFY_WS[key] = ws
+    return ws
+
+
+def gemm_w4a8_verify(wq, sw, bias, qx, sx, y=None, acc=None, impl=0, workspace=None, stream=None):
+    """M tokens: qx int8 [M, K], sx fp32 [M] -> y fp32 [M, N] (and acc [M, N]).
+    ``workspace``: int32 device tensor for the balanced matrix-core kernel
+    (default: ``verify_workspace``'s shared one)."""
     N, K = _wshape(wq, None)
     M = qx.shape[0]
     _dev(wq, "wq", _WORD, N * K // 8)
@@ -528,8 +552,13 @@ def gemm_w4a8_verify(wq, sw, bias, qx, sx, y=None, acc=None, impl=0, stream=None
     _dev(sx, "sx", _F32, M)
     y = _empty((M, N), torch.float32, wq) if y is None else _dev(y, "y", _F32, M * N)
     acc_t = _empty((M, N), torch.int32, wq) if acc is True else None
+    if workspace is None and M >= 1 and N >= 1:
+        workspace = verify_workspace(M, N, K, wq.device)
+    if workspace is not None:
+        _dev(workspace, "workspace", (torch.int32,))
     _call("gemm_w4a8_verify", wq.data_ptr(), sw.data_ptr(), _ptr(bias), qx.data_ptr(),
-          sx.data_ptr(), y.data_ptr(), _ptr(acc_t), M, N, K, impl, _stream(stream))
+          sx.data_ptr(), y.data_ptr(), _ptr(acc_t), M, N, K, impl, _ptr(workspace),
+          0 if workspace is None else workspace.numel() * 4, _stream(stream))
     return (y, acc_t) if acc_t is not None else y
 
 

@@ -1856,6 +1856,203 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 }
 
 // ------------------------------------------------------------------------
+// Verify on the matrix cores in balanced blocks.  The tiles x K work (16-row
+// tiles; a "quad" is 4 chunks = 128 codes of a tile, one pair of MFMAs) is
+// cut into one block per workgroup: a range of tiles times a K slice, all
+// blocks holding about the same number of quads.  A workgroup stages only
+// its slice's codes of the M tokens (issued before its weight loads, so they
+// do not queue behind them), its 16 waves split the block's quads into
+// contiguous runs with every weight load of a run in flight at once, and
+// each wave adds its exact int32 partials into per-tile LDS accumulators.
+// With one K slice the workgroup owns its tiles and writes y directly.
+// With several, each block stores its tiles' partials into the workspace
+// and counts in on the tile; the block that counts in last adds the slices'
+// partials (integers: the order does not matter), writes y and clears the
+// tile's count and partials, so the whole workspace is zero again for the
+// next call, of any shape.  No block waits for another to reach anything:
+// the last one only waits for stores already issued to arrive.
+// ------------------------------------------------------------------------
+constexpr int kVbWaves = 16;
+constexpr int kVbThreads = kVbWaves * kWave;
+constexpr int kVbMaxTiles = 16;             // tiles per block (LDS accumulators)
+constexpr int kVbQ = 10;                    // quads a wave has in flight
+constexpr int kVbStage = 8;                 // staging loads per thread per batch
+constexpr int kVbXsBytes = 112 * 1024;      // LDS for the staged codes
+constexpr int kVbCountWords = 64;           // tile counts are padded to 256 bytes
+constexpr int kVbSpinLimit = 1 << 20;       // polls of one partial word (its store is already issued)
+constexpr int kVbSplitCost = 600;           // fixed charge of a K split in vb_plan, sixths of a quad
+
+__device__ __forceinline__ void vb_load(u32x4 (&buf)[kVbQ], const u32x4* __restrict__ wq, int u0, int ue,
+                                        int qs, int t0, int N, int C, int c0, int nc, int g, int col)
+{
+#pragma unroll
+    for (int j = 0; j < kVbQ; ++j) {
+        const int u = u0 + j;
+        if (u < ue) {  // uniform across the wave
+            const int lt = u / qs, q = u - lt * qs;
+            const int row = min((t0 + lt) * 16 + col, N - 1);
+            const int c = min(4 * q + g, nc - 1);  // past the slice: any chunk, its codes meet zeros
+            buf[j] = wq[(size_t)row * C + c0 + c];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
+    const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
+    const int8_t* __restrict__ qx, const float* __restrict__ sx, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int M, int N, int C, int ksplit, int kslice, int ntg,
+    uint32_t* __restrict__ ws)
+{
+    extern __shared__ u32x4 xs[];  // token m's slice chunk c: xs[m * TS + 2c], [.. + 1]
+    __shared__ int32_t tacc[kVbMaxTiles * 256];  // [tile][row 16][token 16]
+    __shared__ uint32_t s_last[kVbMaxTiles];
+    const int T = (N + 15) >> 4;
+    const int ks = blockIdx.x % ksplit, tg = blockIdx.x / ksplit;
+    const int t0 = (int)((long long)tg * T / ntg), nt = (int)((long long)(tg + 1) * T / ntg) - t0;
+    const int c0 = ks * kslice, nc = min(kslice, C - c0);
+    if (nt <= 0 || nc <= 0)
+        return;  // uniform: a block with no tiles contributes to none
+    const int qs = (nc + 3) >> 2;  // quads per tile in this slice
+    const int total = nt * qs;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int g = lane >> 4, col = lane & 15;
+    const bool tok = col < M;
+    const int TS = 2 * kslice + 1;
+    const int nh = 2 * nc, items = M * nh;
+    const u32x4* qv = reinterpret_cast<const u32x4*>(qx);
+    const int K2 = 2 * C;  // 16-byte halves per token row
+    // 1. the first staging batch, ahead of the weights
+    u32x4 sv[kVbStage];
+#pragma unroll
+    for (int j = 0; j < kVbStage; ++j) {
+        const int i = min(tid + j * kVbThreads, items - 1);
+        sv[j] = qv[(size_t)(i / nh) * K2 + 2 * c0 + i % nh];
+    }
+    for (int i = tid; i < nt * 256; i += kVbThreads)
+        tacc[i] = 0;
+    // 2. this wave's run of quads [qa, qb): the first kVbQ of them in flight
+    const int qa = (int)((long long)wave * total / kVbWaves), qb = (int)((long long)(wave + 1) * total / kVbWaves);
+    u32x4 wb[kVbQ];
+    vb_load(wb, wq, qa, min(qb, qa + kVbQ), qs, t0, N, C, c0, nc, g, col);
+    // 3. staged codes into LDS, permuted for the unpacked weight halves
+    for (int i0 = tid;; i0 += kVbStage * kVbThreads) {
+#pragma unroll
+        for (int j = 0; j < kVbStage; ++j) {
+            const int i = i0 + j * kVbThreads;
+            if (i < items)
+                xs[(i / nh) * TS + i % nh] = u32x4{perm_even(sv[j].x, sv[j].y), perm_odd(sv[j].x, sv[j].y),
+                                                   perm_even(sv[j].z, sv[j].w), perm_odd(sv[j].z, sv[j].w)};
+        }
+        if (i0 + kVbStage * kVbThreads >= items)
+            break;
+#pragma unroll
+        for (int j = 0; j < kVbStage; ++j) {
+            const int i = min(i0 + (kVbStage + j) * kVbThreads, items - 1);
+            sv[j] = qv[(size_t)(i / nh) * K2 + 2 * c0 + i % nh];
+        }
+    }
+    __syncthreads();
+    // 4. the MFMAs; a change of tile flushes the wave's partial into LDS
+    i32x4 acc = {0, 0, 0, 0};
+    int cur = -1;
+    const int xrow = col * TS;
+    for (int u0 = qa; u0 < qb; u0 += kVbQ) {
+        const int ue = min(qb, u0 + kVbQ);
+        if (u0 != qa)
+            vb_load(wb, wq, u0, ue, qs, t0, N, C, c0, nc, g, col);
+#pragma unroll
+        for (int j = 0; j < kVbQ; ++j) {
+            const int u = u0 + j;
+            if (u < ue) {
+                const int lt = u / qs, q = u - lt * qs;
+                if (lt != cur) {
+                    if (cur >= 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            __hip_atomic_fetch_add(&tacc[cur * 256 + (4 * g + e) * 16 + col], acc[e],
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                    acc = i32x4{0, 0, 0, 0};
+                    cur = lt;
+                }
+                const int c = 4 * q + g;
+                u32x4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
+                if (tok && c < nc) {
+                    xa = xs[xrow + 2 * c];
+                    xb = xs[xrow + 2 * c + 1];
+                }
+                acc = mfma_chunk(wb[j], xa, xb, acc);
+            }
+        }
+    }
+    if (cur >= 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            __hip_atomic_fetch_add(&tacc[cur * 256 + (4 * g + e) * 16 + col], acc[e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    // 5. outputs
+    if (ksplit == 1) {
+        for (int i = tid; i < nt * 256; i += kVbThreads) {
+            const int row = (t0 + (i >> 8)) * 16 + ((i >> 4) & 15), m = i & 15;
+            if (row < N && m < M) {
+                const int a = tacc[i] >> 4;
+                if (acc_out)
+                    acc_out[(size_t)m * N + row] = a;
+                y[(size_t)m * N + row] = fmaf(sw[row] * sx[m], (float)a, bias ? bias[row] : 0.0f);
+            }
+        }
+        return;
+    }
+    // Each partial word goes out as one 64-bit atomic store {1, value}: its
+    // high half says it is there, so no store needs to be ordered before
+    // another and no fence is needed.  The count only decides which slice
+    // adds the tile up; that slice loads each word until its high half is
+    // set (the other slices issued their stores before counting in, so
+    // every such wait ends), then clears it.
+    uint32_t* cnt = ws;
+    uint64_t* part = reinterpret_cast<uint64_t*>(ws + (((size_t)T + kVbCountWords - 1) / kVbCountWords) * kVbCountWords);
+    for (int i = tid; i < nt * 256; i += kVbThreads)
+        __hip_atomic_store(&part[((size_t)ks * T + t0 + (i >> 8)) * 256 + (i & 255)],
+                           (1ull << 32) | (uint32_t)tacc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (wave == 0 && lane < nt) {
+        const uint32_t old = __hip_atomic_fetch_add(&cnt[t0 + lane], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (uint32_t)(ksplit - 1);
+        if (last)  // every other slice has counted in: ready for the next call
+            __hip_atomic_store(&cnt[t0 + lane], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last[lane] = last;
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * 256; i += kVbThreads) {
+        const int lt = i >> 8;
+        if (!s_last[lt])
+            continue;
+        // every slice's partial, then cleared: the whole workspace is zero
+        // again when the call ends, whatever shape uses it next
+        int s = 0;
+        for (int k = 0; k < ksplit; ++k) {
+            uint64_t* pp = &part[((size_t)k * T + t0 + lt) * 256 + (i & 255)];
+            uint64_t v = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int spin = 0; (v >> 32) == 0 && spin < kVbSpinLimit; ++spin) {
+                __builtin_amdgcn_s_sleep(1);
+                v = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            s += (int32_t)(uint32_t)v;
+            __hip_atomic_store(pp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const int row = (t0 + lt) * 16 + ((i >> 4) & 15), m = i & 15;
+        if (row < N && m < M) {
+            const int a = s >> 4;
+            if (acc_out)
+                acc_out[(size_t)m * N + row] = a;
+            y[(size_t)m * N + row] = fmaf(sw[row] * sx[m], (float)a, bias ? bias[row] : 0.0f);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // Persistent token pass: every linear of a decode step in one launch, one
 // 1024-thread workgroup per CU, all resident at once.
 //
@@ -3413,9 +3610,67 @@ int gemv_w4a16(const uint32_t* wq, const float* sw, const float* bias, const uin
     return BQD_ERR_CONFIG;
 }
 
+// Blocks of k_verify_blocks for M tokens over N x C chunks: the K split,
+// the slice length (a multiple of 4 chunks) and the number of tile groups
+// with the least work on the busiest CU, counted in sixths of a quad (1 KB
+// of weights from HBM): the block's quads, its staged codes (from L2, about
+// a sixth of the cost per byte) and, with a split, its partials plus a
+// fixed charge for the count and the gathering (measured: [3584, 18944]
+// with two tokens, 224 blocks of whole tiles 13.4 us, 256 half-K blocks
+// 16.1 us).  Tile groups are at
+// least ceil(T / kVbMaxTiles) and, when there are more than one round of
+// them, fill whole rounds.  Splits are tried while the tiles alone do not
+// fill the CUs, or until one lets the codes fit.  False when no slice's
+// codes fit the LDS.
+struct VbPlan {
+    int ksplit, kslice, ntg;
+};
+static bool vb_plan(int M, int N, int C, VbPlan& p)
+{
+    const long long T = (N + 15) / 16, G = current_cus();
+    const int maxc = (kVbXsBytes / (16 * M) - 1) / 2;
+    const long long need = (T + kVbMaxTiles - 1) / kVbMaxTiles;
+    long long best = -1;
+    for (int s = 1; s <= 64 && s <= C; ++s) {
+        const int ksl = (((C + s - 1) / s) + 3) & ~3;
+        if (ksl > maxc || (C + ksl - 1) / ksl != s)
+            continue;
+        if (s > 1 && T * s > 2 * G && best >= 0)
+            break;  // enough tiles: no further split unless the codes need one
+        const long long per_round = G / s > 0 ? G / s : 1;
+        long long ng = need > per_round ? (need + per_round - 1) / per_round * per_round : per_round;
+        ng = ng > T ? T : ng;
+        const long long rounds = (ng * s + G - 1) / G;
+        const long long tmax = (T + ng - 1) / ng;
+        const long long cost = rounds * (6 * tmax * ((ksl + 3) / 4) + (long long)ksl * M / 32 +
+                                         (s > 1 ? kVbSplitCost + tmax * (6 + 3 * s / 2) : 0));
+        if (best < 0 || cost < best) {
+            best = cost;
+            p = VbPlan{s, ksl, (int)ng};
+        }
+    }
+    return best >= 0;
+}
+
+static size_t vb_workspace_bytes(int N, const VbPlan& p)
+{
+    if (p.ksplit <= 1)
+        return 0;
+    const size_t T = (size_t)(N + 15) / 16;
+    return 4 * (((T + kVbCountWords - 1) / kVbCountWords) * kVbCountWords) + 8 * (size_t)p.ksplit * T * 256;
+}
+
+size_t gemm_w4a8_verify_workspace_bytes(int32_t M, int32_t N, int32_t K)
+{
+    if (M < 1 || M > BQD_MAX_TOKENS || N < 1 || check_k(K) || bqd_init())
+        return 0;
+    VbPlan p;
+    return vb_plan(M, N, K / 32, p) ? vb_workspace_bytes(N, p) : 0;
+}
+
 int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, const int8_t* qx,
                      const float* sx, float* y, int32_t* acc, int32_t M, int32_t N, int32_t K,
-                     int32_t impl, void* stream)
+                     int32_t impl, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (M < 0 || N < 0)
         return BQD_ERR_SHAPE;
@@ -3424,30 +3679,50 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
         return rc;
     if (M > BQD_MAX_TOKENS)
         return BQD_ERR_BOUND;
-    if (impl < 0 || impl > 2)
+    if (impl < 0 || impl > 3)
         return BQD_ERR_CONFIG;
     if (M == 0 || N == 0)
         return BQD_OK;
     if (!wq || !sw || !qx || !sx || !y)
         return BQD_ERR_NULL;
     if (!aligned(wq, 16) || !aligned(qx, 16) || !aligned(sw, 4) || !aligned(sx, 4) ||
-        !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4))
+        !aligned(y, 4) || !aligned(bias, 4) || !aligned(acc, 4) || !aligned(workspace, 256))
         return BQD_ERR_ALIGN;
     if (io_overlap({{wq, (size_t)N * K / 2}, {sw, 4 * (size_t)N}, {bias, 4 * (size_t)N}, {qx, (size_t)M * K},
                     {sx, 4 * (size_t)M}},
-                   {{y, 4 * (size_t)M * N}, {acc, 4 * (size_t)M * N}}))
+                   {{y, 4 * (size_t)M * N}, {acc, 4 * (size_t)M * N}, {workspace, workspace_bytes}}))
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
     const int C = K / 32;
     hipStream_t st = (hipStream_t)stream;
     const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+    VbPlan vp{1, C, 1};
+    const bool vb_ok = vb_plan(M, N, C, vp);
+    const bool vb_fits = vb_ok && (vb_workspace_bytes(N, vp) == 0 ||
+                                   (workspace && workspace_bytes >= vb_workspace_bytes(N, vp)));
     if (impl == 0) {
         // One token is the decode GEMV; from two tokens on the matrix cores
-        // beat the dot-product kernel on both verify shapes (measured).
+        // beat the dot-product kernel on both verify shapes (measured).  The
+        // balanced blocks win from 8 tokens on, and at any token count when
+        // there are fewer tiles than CUs (the blocks then split K); below 8
+        // tokens over many tiles the per-tile kernel is a little faster
+        // (us, impl 2 / 3: [18944, 3584] M = 2 12.2 / 13.0, M = 8 14.0 /
+        // 13.3, M = 16 16.2 / 14.2; [3584, 18944] M = 2 13.5 / 12.9, M = 16
+        // 21.6 / 16.9).
         if (M == 1)
             return gemv_w4a8(wq, sw, bias, qx, sx, y, acc, N, K, 0, 0, stream);
-        impl = 2;
+        impl = vb_fits && (M >= 8 || (N + 15) / 16 < current_cus()) ? 3 : 2;
+    }
+    if (impl == 3) {
+        if (!vb_ok)
+            return BQD_ERR_CONFIG;
+        if (!vb_fits)
+            return workspace ? BQD_ERR_BOUND : BQD_ERR_NULL;
+        const size_t lds = (size_t)M * (2 * vp.kslice + 1) * 16;
+        hipLaunchKernelGGL(k_verify_blocks, dim3(vp.ntg * vp.ksplit), dim3(kVbThreads), lds, st, w, sw, bias, qx,
+                           sx, y, acc, M, N, C, vp.ksplit, vp.kslice, vp.ntg, static_cast<uint32_t*>(workspace));
+        return launched();
     }
     if (impl == 2) {
         // Matrix cores, 16-row tiles x 16 token columns.  The smallest K split

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define BQD_ABI_VERSION 2
+#define BQD_ABI_VERSION 3
 
 #define BQD_OK 0
 #define BQD_ERR_NULL (-1)      /* a required pointer is NULL                 */
@@ -341,12 +341,32 @@ int gemv_w4a16(const uint32_t* wq, const float* sw, const float* bias, const uin
  * qx (device) int8 [M, K]; sx (device) float [M]; y (device) float [M, N];
  * acc (device) int32 [M, N] or NULL.  1 <= M <= BQD_MAX_TOKENS.
  * impl: 1 integer dot-product kernel (v_dot4_i32_i8); 2 matrix-core
- * kernel (v_mfma_i32_16x16x64_i8, 16 token columns); 0 automatic: M = 1
- * runs gemv_w4a8's kernel, M >= 2 the matrix-core kernel.  Every impl gives
- * the same acc and y bits. */
+ * kernel (v_mfma_i32_16x16x64_i8, 16 token columns), every workgroup
+ * staging all K of the tokens' codes; 3 the same matrix-core arithmetic in
+ * balanced blocks: one block per workgroup, a range of 16-row tiles times a
+ * K slice with about the same number of weights in each, only the slice's
+ * codes staged.  When the K range is split, each slice's exact int32
+ * partials go through the workspace and the slice that finishes a tile last
+ * adds them and writes y (no workgroup waits for another to reach
+ * anything).  0 automatic: M = 1 runs gemv_w4a8's kernel; M >= 2 impl 3
+ * from 8 tokens on or when N has fewer 16-row tiles than the device has
+ * CUs (and the workspace suffices), else impl 2.  Every impl gives the same
+ * acc and y bits.
+ * workspace (device, 256-byte aligned) of workspace_bytes bytes, or NULL /
+ * 0: needed by impl 3 when gemm_w4a8_verify_workspace_bytes reports more
+ * than 0 for the shape (impl 3 refuses a NULL one with BQD_ERR_NULL and a
+ * smaller one with BQD_ERR_BOUND).  Zero-filled once by the caller; every
+ * call leaves it zeroed again.  Calls that share a workspace must not
+ * overlap in time. */
 int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias,
                      const int8_t* qx, const float* sx, float* y, int32_t* acc,
-                     int32_t M, int32_t N, int32_t K, int32_t impl, void* stream);
+                     int32_t M, int32_t N, int32_t K, int32_t impl, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemm_w4a8_verify's impl 3 needs for M tokens over
+ * [N, K] on the current device: 0 when it splits no tile's K range (or for
+ * invalid shapes, or without a gfx950 device). */
+size_t gemm_w4a8_verify_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* One linear of a decoder layer, as handed to layer_w4a8_forward.  The
  * struct lives in host memory; its pointers are device pointers. */

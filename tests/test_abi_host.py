@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bqd.abi_version() == 2
+    assert bqd.abi_version() == 3
     for s in (OK, NULL, SHAPE, ALIGN, BOUND, DTYPE, CONFIG, LAUNCH, DEVICE):
         assert bqd.status_string(s)
     assert bqd.status_string(12345) == "unknown status"
@@ -101,9 +101,16 @@ def test_other_entry_points_validate_before_launch():
     assert L.gemv_w8a16_group32(P, P, P, P, 8, 65536, 0, 0, None) == BOUND
     assert L.gemv_w8a16_group32(P, P, P4, P, 8, 64, 0, 0, None) == ALIGN
     # verify: token count bound, impl
-    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 17, 8, 64, 0, None) == BOUND
-    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 2, 8, 64, 9, None) == CONFIG
-    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, -1, 8, 64, 0, None) == SHAPE
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 17, 8, 64, 0, None, 0, None) == BOUND
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 2, 8, 64, 9, None, 0, None) == CONFIG
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 2, 8, 64, 4, None, 0, None) == CONFIG
+    assert L.gemm_w4a8_verify(P, P + 0x1000, None, P + 0x2000, P + 0x3000, P + 0x4000, None, 2, 8, 64, 3,
+                              P + 0x5000 + 16, 1024, None) == ALIGN         # workspace not 256-byte aligned
+    assert L.gemm_w4a8_verify(P, P + 0x1000, None, P + 0x2000, P + 0x3000, P + 0x4000, None, 2, 8, 64, 3,
+                              P + 0x4000, 1024, None) == SHAPE             # workspace over y
+    assert L.gemm_w4a8_verify_workspace_bytes(0, 8, 64) == 0
+    assert L.gemm_w4a8_verify_workspace_bytes(2, 8, 40) == 0
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, -1, 8, 64, 0, None, 0, None) == SHAPE
     # weight quantisers
     assert L.quantize_weights_int4_rowwise(P, 8, 36, P, P, None) == SHAPE
     assert L.quantize_weights_int4_group32(P4, 8, 64, P, P, None) == ALIGN
@@ -174,8 +181,8 @@ def test_outputs_may_not_overlap_what_the_launch_reads():
     assert rq(hh, dd, gg, 1e-6, None, None, hh, sx, 2, K, None) == SHAPE      # codes over h
     assert L.swiglu_quant(x, x + 256, qx, sx, 2, K, None) == SHAPE
     assert L.swiglu_quant(x, ho, ho + 16, sx, 2, K, None) == SHAPE
-    assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, qx + 64, None, 2, N, K, 0, None) == SHAPE  # y over token 1
-    assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, y, y + 32, 2, N, K, 0, None) == SHAPE
+    assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, qx + 64, None, 2, N, K, 0, None, 0, None) == SHAPE  # y over token 1
+    assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, y, y + 32, 2, N, K, 0, None, 0, None) == SHAPE
     assert L.gemv_w8a16_group32(wq, sw, x, x + 64, N, K, 0, 0, None) == SHAPE
     # a layer: y[i] may be x[i+1], never x[i] itself
     lin = bqd.LinearW4A8(wq, sw, 0, N, K, 0, 0, 0)
@@ -192,7 +199,7 @@ def test_outputs_may_not_overlap_what_the_launch_reads():
         assert rq(hh, dd, gg, 1e-6, hh, dd, qx, sx, 2, K, None) == DEVICE   # in place is allowed
         assert L.quantize_act(x, 0, 2, K, qx, sx, None) == DEVICE
         assert L.swiglu_quant(x, ho, qx, sx, 2, K, None) == DEVICE
-        assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, y, acc, 2, N, K, 0, None) == DEVICE
+        assert L.gemm_w4a8_verify(wq, sw, bias, qx, sx, y, acc, 2, N, K, 0, None, 0, None) == DEVICE
         assert L.gemv_w8a16_group32(wq, sw, x, y, N, K, 0, 0, None) == DEVICE
         good = (C.c_void_p * 2)(y, acc)
         assert L.layer_w4a8_forward(arr, 2, C.cast(xs, C.c_void_p), 0, C.cast(good, C.c_void_p), None) == DEVICE

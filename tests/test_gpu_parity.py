@@ -379,13 +379,15 @@ def test_gemv_w4a16_integer_x_equals_w4a8():
 
 
 # -------------------------------------------------------------- verify --
-@pytest.mark.parametrize("impl", [0, 1, 2])
+@pytest.mark.parametrize("impl", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16])
 @pytest.mark.parametrize("N,K", [(200, 3584), (150, 18944), (33, 64), (70, 96)])
 def test_gemm_w4a8_verify(M, N, K, impl):
     """impl 1: dot-product kernel; impl 2: matrix cores (K split over 16
     waves here: few rows; K = 64 / 96 leave lane groups without a chunk);
-    impl 0: automatic (the GEMV kernel for one token)."""
+    impl 3: matrix cores in balanced blocks (few tiles: K split over
+    workgroups, partials through the workspace); impl 0: automatic (the
+    GEMV kernel for one token)."""
     w, _, sw, b, _ = _rand_gemv(N, K, f"ver/{N}/{K}")
     X = I.normal(f"gpu/ver/{M}/{K}/X", (M, K), 1.0, device=DEV)
     qx, sx = bqd.quantize_act(X)
@@ -415,12 +417,49 @@ def test_gemm_w4a8_verify_mfma_row_tilings(M, N, K):
     qx, sx = bqd.quantize_act(X)
     y, acc = bqd.gemm_w4a8_verify(w, sw, b, qx, sx, acc=True, impl=2)
     y1 = bqd.gemm_w4a8_verify(w, sw, b, qx, sx, impl=1)
+    y3, acc3 = bqd.gemm_w4a8_verify(w, sw, b, qx, sx, acc=True, impl=3)
     sync()
     acc_r, y_r = O.gemm_w4a8_verify(u32(w), npy(sw), npy(b), npy(qx), npy(sx))
     assert np.array_equal(npy(acc), acc_r)
+    assert np.array_equal(npy(acc3), acc_r)
     for m in range(M):
         P.check_rowwise(f"token {m}", npy(y)[m], y_r[m], npy(sw), npy(sx)[m], acc_r[m], npy(b), TOL)
     assert torch.equal(y, y1)
+    assert torch.equal(y3, y1)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 3584, 18944), (2, 100, 65536), (16, 4100, 2048), (5, 17, 32)])
+def test_verify_blocks_workspace(M, N, K):
+    """The balanced matrix-core verify at shapes whose K is split over
+    workgroups (the down-shaped verify, a long K with few rows) or not: the
+    workspace the binding hands over is zero again after each call, calls in
+    a row give the same bits, a caller's own zeroed workspace works too, and
+    acc equals the oracle's."""
+    w, _, sw, b, _ = _rand_gemv(N, K, f"vbws/{N}/{K}")
+    X = I.normal(f"gpu/vbws/{M}/{K}/X", (M, K), 1.0, device=DEV)
+    qx, sx = bqd.quantize_act(X)
+    need = bqd.lib().gemm_w4a8_verify_workspace_bytes(M, N, K)
+    ws = bqd.verify_workspace(M, N, K, DEV)
+    assert (ws is None) == (need == 0)
+    outs = []
+    for _ in range(3):
+        outs.append(bqd.gemm_w4a8_verify(w, sw, b, qx, sx, acc=True, impl=3))
+        sync()
+        if ws is not None:
+            assert int(ws.abs().max()) == 0   # the whole workspace is zero again
+    if need:
+        own = torch.zeros(need // 4 + 64, dtype=torch.int32, device=DEV)
+        outs.append(bqd.gemm_w4a8_verify(w, sw, b, qx, sx, acc=True, impl=3, workspace=own))
+        sync()
+        assert int(own.abs().max()) == 0    # counts and partials are zero again
+        with pytest.raises(bqd.BQDError):
+            bqd.gemm_w4a8_verify(w, sw, b, qx, sx, impl=3, workspace=own[:16])
+    for y, acc in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(acc, outs[0][1])
+    acc_r, y_r = O.gemm_w4a8_verify(u32(w), npy(sw), npy(b), npy(qx), npy(sx))
+    assert np.array_equal(npy(outs[0][1]), acc_r)
+    for m in (0, M - 1):
+        P.check_rowwise(f"token {m}", npy(outs[0][0])[m], y_r[m], npy(sw), npy(sx)[m], acc_r[m], npy(b), TOL)
 
 
 # -------------------------------------------------------- layer launcher --
