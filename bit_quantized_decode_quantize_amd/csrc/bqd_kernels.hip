@@ -60,6 +60,7 @@ __device__ __forceinline__ h16x2 as_h16x2(uint32_t v)
 // count only in vmcnt) instead of flat loads, which also count in lgkmcnt and
 // so would be drained by every LDS wait.
 #define BQD_GLOBAL __attribute__((address_space(1)))
+#define BQD_LDS __attribute__((address_space(3)))
 template <typename T>
 __device__ __forceinline__ const BQD_GLOBAL T* gptr(const T* p)
 {
@@ -335,38 +336,56 @@ __device__ __forceinline__ void stage_q8(u32x2* xs, const int8_t* qx, int G8)
 // registers: every load is issued before the first use (one memory round
 // trip), and the codes come from the registers.  Longer activations take
 // two passes over x (the second from cache), 4 groups per thread at a time.
+// A short activation (G8 <= 4 * kThreads groups of 8) in registers: the
+// loads alone, so that a kernel can issue them ahead of its weight loads
+// (a CU serves its loads in order, and the activation is on the critical
+// path: its maximum and codes come before the first dot product).
+template <int XIN>
+__device__ __forceinline__ void preload_x(const void* x, int G8, float (&v)[4][8])
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        load8<XIN>(x, min((int)threadIdx.x + k * kThreads, G8 - 1), v[k]);
+}
+
+// Codes and scale of a short activation already in registers (preload_x).
+__device__ float quant_from_regs(u32x2* xs, const float (&v)[4][8], int G8, float* red, int8_t* qx_out,
+                                 float* sx_out)
+{
+    const bool out = (qx_out != nullptr) && blockIdx.x == 0;
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            m = fmaxf(m, fabsf(v[k][e]));  // clamped groups repeat a real one
+    const ActScale a = act_scale(block_max(m, red));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int g = threadIdx.x + k * kThreads;
+        if (g < G8) {
+            uint32_t lo, hi;
+            quant8_fast(v[k], a, lo, hi);
+            xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+            if (out)
+                reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+        }
+    }
+    if (sx_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+        *sx_out = a.s;
+    return a.s;
+}
+
 template <int XIN>
 __device__ float stage_quant(u32x2* xs, const void* x, int G8, float* red, int8_t* qx_out,
                              float* sx_out)
 {
-    const bool out = (qx_out != nullptr) && blockIdx.x == 0;
     if (G8 <= 4 * kThreads) {
         float v[4][8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            load8<XIN>(x, min((int)threadIdx.x + k * kThreads, G8 - 1), v[k]);
-        float m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                m = fmaxf(m, fabsf(v[k][e]));  // clamped groups repeat a real one
-        const ActScale a = act_scale(block_max(m, red));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int g = threadIdx.x + k * kThreads;
-            if (g < G8) {
-                uint32_t lo, hi;
-                quant8_fast(v[k], a, lo, hi);
-                xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
-                if (out)
-                    reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
-            }
-        }
-        if (sx_out != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
-            *sx_out = a.s;
-        return a.s;
+        preload_x<XIN>(x, G8, v);
+        return quant_from_regs(xs, v, G8, red, qx_out, sx_out);
     }
+    const bool out = (qx_out != nullptr) && blockIdx.x == 0;
     // batches of 4 groups per thread, the batch's loads issued together
     float amax = 0.0f;
     for (int g0 = threadIdx.x; g0 < G8; g0 += 4 * kThreads) {
@@ -906,8 +925,22 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
 
     int tile = blockIdx.x;
     u32x4 cur[U][R];
-    load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
-    const float sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out, rms);
+    float sx;
+    bool staged = false;
+    if constexpr (XIN == X_F32 || XIN == X_F16) {
+        if (C <= kThreads) {
+            // the activation's loads first, then the first weight step's
+            float v[4][8];
+            preload_x<XIN>(xin, 4 * C, v);
+            load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+            sx = quant_from_regs(reinterpret_cast<u32x2*>(xs), v, 4 * C, red, qx_out, sx_out);
+            staged = true;
+        }
+    }
+    if (!staged) {
+        load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+        sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out, rms);
+    }
     __syncthreads();
 
     for (; tile < tiles; tile += gridDim.x) {
@@ -985,9 +1018,24 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8_g32(
     int tile = blockIdx.x;
     u32x4 cur[U][R];
     uint16_t scur[U][R];
-    load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
-    load_scales<R, L, U>(scur, s16, N, C, tile * ROWS + grp * R, 0, lane);
-    const float sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out);
+    float sx;
+    bool staged = false;
+    if constexpr (XIN == X_F32 || XIN == X_F16) {
+        if (C <= kThreads) {
+            // the activation's loads first, then the first weight step's
+            float v[4][8];
+            preload_x<XIN>(xin, 4 * C, v);
+            load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+            load_scales<R, L, U>(scur, s16, N, C, tile * ROWS + grp * R, 0, lane);
+            sx = quant_from_regs(reinterpret_cast<u32x2*>(xs), v, 4 * C, red, qx_out, sx_out);
+            staged = true;
+        }
+    }
+    if (!staged) {
+        load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+        load_scales<R, L, U>(scur, s16, N, C, tile * ROWS + grp * R, 0, lane);
+        sx = stage_activation<XIN>(xs, xin, sx_in, C, red, qx_out, sx_out);
+    }
     __syncthreads();
 
     for (; tile < tiles; tile += gridDim.x) {
@@ -2147,6 +2195,7 @@ inline size_t pass_lds_bytes(int max_k) { return (size_t)((max_k + 15) & ~15) + 
 constexpr int kDescRing = 64;
 // A group-32 linear's scales for this workgroup's rows, staged in LDS.
 constexpr int kPassScaleLds = 16384;
+static_assert(kPassScaleLds % (16 * 256) == 0, "scale block: whole registers per staging thread");
 constexpr int kDescWords = (int)(sizeof(PassTask) / 4);
 static_assert(sizeof(PassTask) % 4 == 0, "descriptor words");
 static_assert(5 * kPassMaxK + kDescRing * (int)sizeof(PassTask) + kPassScaleLds + 1024 <= 160 * 1024, "pass LDS");
@@ -2573,13 +2622,21 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         const bool all_stage = G8 > kPassStageAllAbove;
         const int st = all_stage ? tid : ct;
         const int nst = all_stage ? kPassThreads : kPassControl;
+        // this workgroup's rows' group scales: rows * C fp16 values,
+        // contiguous and 16-byte aligned (C % 8 == 0, checked on the host),
+        // copied straight into LDS (no registers) ahead of the activation's
+        // loads, so the two overlap; the staging waves wait for every load
+        // before the barrier that hands the scales to the workers
         if (t.kind == 1 && rows > 0 && ct >= 0) {
-            // this workgroup's rows' group scales: rows * C fp16 values,
-            // contiguous and 16-byte aligned (C % 8 == 0, checked on the host)
+            const int nsc = rows * t.C / 8;
             const BQD_GLOBAL u32x4* src =
                 gptr(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(t.scales) + (size_t)row_start * t.C));
-            for (int i = ct; i < rows * t.C / 8; i += kPassControl)
-                sl16[i] = src[i];
+            const int lane = ct & (kWave - 1);
+            for (int base = ct - lane; base < nsc; base += kPassControl) {  // wave-uniform
+                if (base + lane < nsc)
+                    __builtin_amdgcn_global_load_lds(const_cast<BQD_GLOBAL u32x4*>(src + base + lane),
+                                                     (BQD_LDS void*)(sl16 + base), 16, 0, 0);
+            }
         }
         if (rows > 0 && st >= 0) {
             float m;
@@ -2593,6 +2650,8 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
             if ((st & (kWave - 1)) == 0)
                 rd[st / kWave] = m;
         }
+        if (t.kind == 1 && rows > 0 && ct >= 0)
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the scale copies are in LDS
         __syncthreads();
         float amax = rd[0];
         const int nw = all_stage ? kPassThreads / kWave : kPassControl / kWave;
