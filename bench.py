@@ -77,7 +77,7 @@ def parse():
 TRAFFIC = {w: os.path.join(ROOT, "profiles", f) for w, f in (
     ("stream", "k_decode_pass_qwen2-7b-28L_traffic.md"),
     ("layer", "k_decode_pass_qwen2-7b-layer-pool_traffic.md"),
-    ("single", "k_gemv_w4a8_single-q-proj-3584x3584_traffic.md"),
+    ("single", "k_linear_wide_single-q-proj-3584x3584_traffic.md"),
     ("verify", "k_verify_blocks_verify-18944x3584-M16_traffic.md"),
     ("gemma", "k_gemv_w8a16_g32_gemma-lm-head_traffic.md"))}
 TRAFFIC_SUMMARY = TRAFFIC["stream"]
@@ -500,9 +500,11 @@ def run_single(a, dev):
         bqd.gemv_w4a16(w.wq[c], w.sw[c], w.b[c], x16, y=w.y, r=a.r, lanes_per_row=a.lanes)
     ms16, _ = time_steps(step16, a.steps, a.warmup, w.copies if (not a.eager) else 0)
     out["w4a16_us_per_gemv"] = round(ms16 * 1e3, 3)
-    out["roofline"] = roofline(gbs, "k_gemv_w4a8 (fused linear, one launch per step)", ms * 1e3,
-                               w.bytes_per_step(),
-                               measured_traffic(TRAFFIC["single"]) if not (a.r or a.lanes) else None)
+    auto = not (a.r or a.lanes)
+    kname = ("k_linear_wide<2, X_F32> (fused linear, one 1024-thread workgroup per 16 rows, one launch per step)"
+             if auto else "k_gemv_w4a8 (fused linear, one launch per step)")
+    out["roofline"] = roofline(gbs, kname, ms * 1e3, w.bytes_per_step(),
+                               measured_traffic(TRAFFIC["single"]) if auto else None)
     if not a.no_cpu_baseline:
         import oracle as O
         d = I.single_gemv_inputs(0, "cpu")

@@ -994,6 +994,76 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
 }
 
 // ------------------------------------------------------------------------
+// One fused linear in wide workgroups: 1024 threads, one wave per output
+// row (16 rows per workgroup), for short activations (K <= 64 * 32 * U).
+// Every thread loads at most one 8-value group of x, then its wave's row
+// chunks (64 lanes, U chunks each), so the activation's loads go out first
+// and the whole workgroup finds max|x| and writes the codes in one round.
+// Same codes and, the accumulator being exact, the same y bits as
+// k_gemv_w4a8.
+// ------------------------------------------------------------------------
+constexpr int kWideThreads = 1024;
+constexpr int kWideRows = kWideThreads / kWave;
+constexpr int kWideMaxN = 8192;  // linear_w4a8 takes the wide kernel up to this many rows
+
+template <int U, int XIN>
+__global__ __launch_bounds__(kWideThreads) void k_linear_wide(
+    const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
+    const void* __restrict__ x, float* __restrict__ y, int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out,
+    float* __restrict__ sx_out, int N, int C)
+{
+    __shared__ u32x2 xs[kWideThreads];  // codes of 8 values per group, permuted
+    __shared__ float red[kWideThreads / kWave];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int G8 = 4 * C;
+    const int row = min(blockIdx.x * kWideRows + wave, N - 1);
+    float v[8];
+    load8<XIN>(x, min(tid, G8 - 1), v);
+    u32x4 w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+        w[j] = wq[(size_t)row * C + min(lane + kWave * j, C - 1)];
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        m = fmaxf(m, fabsf(v[e]));  // a clamped group repeats a real one
+    m = wave_max_dpp(m);
+    if (lane == 0)
+        red[wave] = m;
+    __syncthreads();
+    float amax = red[0];
+#pragma unroll
+    for (int i = 1; i < kWideThreads / kWave; ++i)
+        amax = fmaxf(amax, red[i]);
+    const ActScale a = act_scale(amax);
+    if (tid < G8) {
+        uint32_t lo, hi;
+        quant8_fast(v, a, lo, hi);
+        xs[tid] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+        if (qx_out && blockIdx.x == 0)
+            reinterpret_cast<u32x2*>(qx_out)[tid] = u32x2{lo, hi};
+    }
+    if (sx_out && blockIdx.x == 0 && tid == 0)
+        *sx_out = a.s;
+    __syncthreads();
+    int acc = 0;
+    const u32x4* xq = reinterpret_cast<const u32x4*>(xs);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int c = lane + kWave * j;
+        if (c < C)
+            acc = dot_chunk16(w[j], xq[2 * c], xq[2 * c + 1], acc);
+    }
+    acc = sum_lanes<kWave>(acc >> 4);
+    const int r = blockIdx.x * kWideRows + wave;
+    if (lane == 0 && r < N) {
+        if (acc_out)
+            acc_out[r] = acc;
+        y[r] = fmaf(sw[r] * a.s, (float)acc, bias ? bias[r] : 0.0f);
+    }
+}
+
+// ------------------------------------------------------------------------
 // W4A8 GEMV, one fp16 scale per 32 codes (= per 16-byte chunk).
 //   y = sx * sum_g s_g * acc_g + b; acc_g exact int32, the scaled sum fp32.
 //   Same pipeline as k_gemv_w4a8, with each chunk's scale loaded beside it.
@@ -3402,6 +3472,29 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
+    if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= 8192) {
+        // wide workgroups for short activations and few rows (measured, the
+        // single Q projection [3584, 3584] graph-replayed: 5.54 -> 4.38 us,
+        // cold 8.6 -> 7.6 us; the per-linear 28-layer stream 1.266 -> 1.215
+        // ms; with gate/up and the lm_head also wide the stream is slower,
+        // 1.279 ms)
+        const int C = K / 32, U = (C + kWave - 1) / kWave;
+        const dim3 grid((N + kWideRows - 1) / kWideRows), block(kWideThreads);
+        hipStream_t st = (hipStream_t)stream;
+        const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+#define BQD_WIDE_CASE(UU)                                                                                 \
+        if (U <= UU) {                                                                                    \
+            if (x_dtype == BQD_F32)                                                                       \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F32>), grid, block, 0, st, w, sw, bias, x, y, acc, \
+                                   qx_out, sx_out, N, C);                                                 \
+            else                                                                                          \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F16>), grid, block, 0, st, w, sw, bias, x, y, acc, \
+                                   qx_out, sx_out, N, C);                                                 \
+            return launched();                                                                            \
+        }
+        BQD_WIDE_CASE(1) BQD_WIDE_CASE(2) BQD_WIDE_CASE(4)
+#undef BQD_WIDE_CASE
+    }
     const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 1);
     if (x_dtype == BQD_F32)
         return launch_gemv_rowwise<X_F32>(wq, sw, bias, x, nullptr, y, acc, qx_out, sx_out, N, K, c,
