@@ -1006,46 +1006,12 @@ constexpr int kWideThreads = 1024;
 constexpr int kWideRows = kWideThreads / kWave;
 constexpr int kWideMaxN = 8192;  // linear_w4a8 takes the wide kernel up to this many rows
 
-template <int U, int XIN>
-__global__ __launch_bounds__(kWideThreads) void k_linear_wide(
-    const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
-    const void* __restrict__ x, float* __restrict__ y, int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out,
-    float* __restrict__ sx_out, int N, int C)
+// One wave's row of the wide kernels: U chunks per lane against the staged
+// codes, the lanes' exact sum, the fp32 epilogue.
+template <int U>
+__device__ __forceinline__ void wide_dot(const u32x4 (&w)[U], const u32x2* xs, int C, int lane, int r, int N,
+                                         const float* sw, const float* bias, float sx, float* y, int32_t* acc_out)
 {
-    __shared__ u32x2 xs[kWideThreads];  // codes of 8 values per group, permuted
-    __shared__ float red[kWideThreads / kWave];
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int G8 = 4 * C;
-    const int row = min(blockIdx.x * kWideRows + wave, N - 1);
-    float v[8];
-    load8<XIN>(x, min(tid, G8 - 1), v);
-    u32x4 w[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j)
-        w[j] = wq[(size_t)row * C + min(lane + kWave * j, C - 1)];
-    float m = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        m = fmaxf(m, fabsf(v[e]));  // a clamped group repeats a real one
-    m = wave_max_dpp(m);
-    if (lane == 0)
-        red[wave] = m;
-    __syncthreads();
-    float amax = red[0];
-#pragma unroll
-    for (int i = 1; i < kWideThreads / kWave; ++i)
-        amax = fmaxf(amax, red[i]);
-    const ActScale a = act_scale(amax);
-    if (tid < G8) {
-        uint32_t lo, hi;
-        quant8_fast(v, a, lo, hi);
-        xs[tid] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
-        if (qx_out && blockIdx.x == 0)
-            reinterpret_cast<u32x2*>(qx_out)[tid] = u32x2{lo, hi};
-    }
-    if (sx_out && blockIdx.x == 0 && tid == 0)
-        *sx_out = a.s;
-    __syncthreads();
     int acc = 0;
     const u32x4* xq = reinterpret_cast<const u32x4*>(xs);
 #pragma unroll
@@ -1055,11 +1021,69 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
             acc = dot_chunk16(w[j], xq[2 * c], xq[2 * c + 1], acc);
     }
     acc = sum_lanes<kWave>(acc >> 4);
-    const int r = blockIdx.x * kWideRows + wave;
     if (lane == 0 && r < N) {
         if (acc_out)
             acc_out[r] = acc;
-        y[r] = fmaf(sw[r] * a.s, (float)acc, bias ? bias[r] : 0.0f);
+        y[r] = fmaf(sw[r] * sx, (float)acc, bias ? bias[r] : 0.0f);
+    }
+}
+
+template <int U, int XIN>
+__global__ __launch_bounds__(kWideThreads) void k_linear_wide(
+    const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
+    const void* __restrict__ x, const float* __restrict__ sx_in, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out, float* __restrict__ sx_out, int N, int C)
+{
+    __shared__ u32x2 xs[kWideThreads];  // codes of 8 values per group, permuted
+    __shared__ float red[kWideThreads / kWave];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int G8 = 4 * C;
+    const int row = min(blockIdx.x * kWideRows + wave, N - 1);
+    float sxv;
+    if constexpr (XIN == X_Q8) {
+        // codes already made (a producer's): one 8-byte group per thread
+        const u32x2 q = reinterpret_cast<const u32x2*>(x)[min(tid, G8 - 1)];
+        u32x4 w[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            w[j] = wq[(size_t)row * C + min(lane + kWave * j, C - 1)];
+        if (tid < G8)
+            xs[tid] = u32x2{perm_even(q.x, q.y), perm_odd(q.x, q.y)};
+        sxv = *sx_in;
+        __syncthreads();
+        wide_dot<U>(w, xs, C, lane, blockIdx.x * kWideRows + wave, N, sw, bias, sxv, y, acc_out);
+        return;
+    } else {
+        float v[8];
+        load8<XIN>(x, min(tid, G8 - 1), v);
+        u32x4 w[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            w[j] = wq[(size_t)row * C + min(lane + kWave * j, C - 1)];
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            m = fmaxf(m, fabsf(v[e]));  // a clamped group repeats a real one
+        m = wave_max_dpp(m);
+        if (lane == 0)
+            red[wave] = m;
+        __syncthreads();
+        float amax = red[0];
+#pragma unroll
+        for (int i = 1; i < kWideThreads / kWave; ++i)
+            amax = fmaxf(amax, red[i]);
+        const ActScale a = act_scale(amax);
+        if (tid < G8) {
+            uint32_t lo, hi;
+            quant8_fast(v, a, lo, hi);
+            xs[tid] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+            if (qx_out && blockIdx.x == 0)
+                reinterpret_cast<u32x2*>(qx_out)[tid] = u32x2{lo, hi};
+        }
+        if (sx_out && blockIdx.x == 0 && tid == 0)
+            *sx_out = a.s;
+        __syncthreads();
+        wide_dot<U>(w, xs, C, lane, blockIdx.x * kWideRows + wave, N, sw, bias, a.s, y, acc_out);
     }
 }
 
@@ -3442,6 +3466,20 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
+    if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= 8192) {
+        // wide workgroups, as for linear_w4a8
+        const int C = K / 32, U = (C + kWave - 1) / kWave;
+        const dim3 grid((N + kWideRows - 1) / kWideRows), block(kWideThreads);
+        const u32x4* w = reinterpret_cast<const u32x4*>(wq);
+#define BQD_WIDE_Q8_CASE(UU)                                                                               \
+        if (U <= UU) {                                                                                     \
+            hipLaunchKernelGGL((k_linear_wide<UU, X_Q8>), grid, block, 0, (hipStream_t)stream, w, sw, bias, \
+                               qx, sx, y, acc, nullptr, nullptr, N, C);                                    \
+            return launched();                                                                             \
+        }
+        BQD_WIDE_Q8_CASE(1) BQD_WIDE_Q8_CASE(2) BQD_WIDE_Q8_CASE(4)
+#undef BQD_WIDE_Q8_CASE
+    }
     return launch_gemv_rowwise<X_Q8>(wq, sw, bias, qx, sx, y, acc, nullptr, nullptr, N, K,
                                      make_cfg(N, K / 32, r, lanes_per_row, 1), (hipStream_t)stream);
 }
@@ -3485,11 +3523,11 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
 #define BQD_WIDE_CASE(UU)                                                                                 \
         if (U <= UU) {                                                                                    \
             if (x_dtype == BQD_F32)                                                                       \
-                hipLaunchKernelGGL((k_linear_wide<UU, X_F32>), grid, block, 0, st, w, sw, bias, x, y, acc, \
-                                   qx_out, sx_out, N, C);                                                 \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F32>), grid, block, 0, st, w, sw, bias, x, nullptr, \
+                                   y, acc, qx_out, sx_out, N, C);                                         \
             else                                                                                          \
-                hipLaunchKernelGGL((k_linear_wide<UU, X_F16>), grid, block, 0, st, w, sw, bias, x, y, acc, \
-                                   qx_out, sx_out, N, C);                                                 \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F16>), grid, block, 0, st, w, sw, bias, x, nullptr, \
+                                   y, acc, qx_out, sx_out, N, C);                                         \
             return launched();                                                                            \
         }
         BQD_WIDE_CASE(1) BQD_WIDE_CASE(2) BQD_WIDE_CASE(4)
