@@ -241,6 +241,20 @@ def roofline(achieved_gbs, kernel, avg_us, avg_bytes, traffic=None):
             "avg_launch_us": round(avg_us, 3), "avg_algorithmic_bytes": int(avg_bytes)}
 
 
+def inputs_digest(*tensors, nbytes=1 << 20):
+    """First 16 hex digits of a sha256 over the first ``nbytes`` bytes of each
+    tensor (copied to the host), in order: names the seeded synthetic inputs
+    a line ran on, so two runs can be seen to have used the same data."""
+    import torch
+    h = hashlib.sha256()
+    for t in tensors:
+        if t is None:
+            continue
+        b = t.detach().contiguous().reshape(-1).view(torch.uint8)[:nbytes]
+        h.update(b.cpu().numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
 def base_line(a, value, ms, steps, config, dtype="int8"):
     return {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
             "steps": steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
@@ -410,6 +424,8 @@ def run_stream(a, dev):
         "bytes_per_step": step_bytes, "packed_weight_bytes": s.weight_bytes()})
     out["tok_per_s"] = round(1e3 / ms, 2)
     out["us_per_gemv"] = round(ms * 1e3 / len(s.linears), 3)
+    d0, dl = s.linears[0], s.linears[-1]
+    out["inputs_sha256"] = inputs_digest(d0["wq"], d0["sw"], d0["b"], d0["x"], dl["wq"], dl["sw"], dl["x"])
     out["ms_per_step_spread"] = repeat_spread(step, max(1, a.steps // 5))
     out["roofline"] = roofline(achieved, kernel, avg_us, avg_bytes, traffic)
     if s.persistent:
@@ -488,6 +504,7 @@ def run_single(a, dev):
                     "outliers, fused act-quant", "launch": "HIP graph" if (not a.eager) else "eager",
         "N": w.N, "K": w.K, "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
     out["us_per_gemv"] = round(ms * 1e3, 3)
+    out["inputs_sha256"] = inputs_digest(w.wq[0], w.sw[0], w.b[0], w.x)
     out["cold_single_call_us"] = cold_call_us(w.step, dev)
     # The float-unpack comparison (W4A16) on the same weights, fp16 x.
     from bit_quantized_decode_quantize_amd import bqd
@@ -538,6 +555,7 @@ def run_layer(a, dev):
         "launch": launch, "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
     out["us_per_layer"] = round(ms * 1e3, 3)
     out["implied_28_layer_gemv_us"] = round(28 * ms * 1e3, 1)
+    out["inputs_sha256"] = inputs_digest(*[t for e in w.layers[0] for t in (e["wq"], e["sw"], e["b"], e["x"])])
     out["roofline"] = roofline(avg_bytes / (avg_us * 1e-6) / 1e9, kernel, avg_us, avg_bytes,
                                measured_traffic(TRAFFIC["layer"]) if w.persistent else None)
     if not a.no_cpu_baseline:
@@ -606,6 +624,8 @@ def run_gemma(a, dev):
         "bytes_per_step": step_bytes, "weight_bytes": w.weight_bytes()}, dtype="int8+fp16")
     out["tok_per_s"] = round(1e3 / ms, 2)
     out["us_per_gemv"] = round(ms * 1e3 / w.launches_per_step, 3)
+    out["inputs_sha256"] = inputs_digest(w.linears[0]["wq"], w.linears[0]["s16"], w.linears[0]["x"],
+                                         w.linears[-1]["wq"], w.linears[-1]["s16"])
     if not a.per_linear:
         ib = w.pass_bytes(chained=False)
         out["independent"] = {"ms_per_step": round(ims, 5), "GB/s": round(ib / (ims * 1e-3) / 1e9, 1),
@@ -650,6 +670,8 @@ def run_verify(a, dev):
                           "Tops": round(w.int_ops_per_step() / (ms * 1e-3) / 1e12, 2),
                           "rotation_copies": w.copies, "steps": n})
             log(f"verify {N}x{K} M={M}: {sweep[-1]}")
+            if N == 18944:
+                digest = inputs_digest(w.wq[0], w.sw[0], w.b[0], w.qx, w.sx)
             del w
             torch.cuda.empty_cache()
     # A1 on its own: the per-token activation quantisation that feeds the
@@ -672,6 +694,7 @@ def run_verify(a, dev):
         "workload": "M-token verify GEMM, per-row int4 weights [18944,3584] and [3584,18944], int8 X [M,K] "
                     "(per-token scales), bias", "impl": a.impl, "M": ms_list})
     out["sweep"] = sweep
+    out["inputs_sha256"] = digest  # the [18944, 3584] pool at the largest M
     out["quantize_act"] = qa
     out["quantize_act_note"] = ("graph-replayed calls on one resident X (L2-resident after the first): "
                                 "per-call latency, not a bandwidth")

@@ -531,3 +531,19 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_bench_inputs_digest_names_the_data():
+    """The digest bench.py puts on each line changes with any input byte and
+    not with the order of equal calls."""
+    import bench
+    a = torch.arange(64, dtype=torch.float32)
+    b = torch.ones(8, dtype=torch.int8)
+    d = bench.inputs_digest(a, b)
+    assert re.fullmatch(r"[0-9a-f]{16}", d)
+    assert bench.inputs_digest(a, b) == d
+    a2 = a.clone()
+    a2[5] += 1
+    assert bench.inputs_digest(a2, b) != d
+    assert bench.inputs_digest(b, a) != d
+    assert bench.inputs_digest(a, None, b) == d
