@@ -1020,3 +1020,24 @@ def test_gemv_int8x_matches_oracle(N, K, dist):
         assert np.array_equal(npy(acc), acc_r), rows
         mag = np.abs(y_r)
         assert np.all(np.abs(npy(y).astype(np.float64) - y_r) <= TOL * np.where(mag > 0, mag, 1.0)), rows
+
+
+@pytest.mark.parametrize("N,K", [(3584, 3584), (4608, 3584), (17, 32), (8192, 8192), (1000, 1536)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_wide_workgroups_give_the_same_bits(N, K, dtype):
+    """The automatic configuration runs short, few-row linears in 1024-thread
+    workgroups (one wave per row): codes, scale, accumulators and y equal the
+    256-thread kernel's bit for bit, for the fused linear and for the GEMV on
+    a producer's codes."""
+    w = I.random_words(f"gpu/wide/{N}/{K}/w", (N, K // 8), device=DEV)
+    sw = I.normal(f"gpu/wide/{N}/{K}/s", N, 0.003, device=DEV).abs() + 1e-4
+    b = I.normal(f"gpu/wide/{N}/{K}/b", N, 0.01, device=DEV)
+    x = I.normal(f"gpu/wide/{K}/x", K, 1.0, device=DEV).to(dtype)
+    y0, q0, s0, a0 = bqd.linear_w4a8(w, sw, b, x, want_q=True, want_acc=True)
+    y1, q1, s1, a1 = bqd.linear_w4a8(w, sw, b, x, want_q=True, want_acc=True, r=1, lanes_per_row=32)
+    g0, ga0 = bqd.gemv_w4a8(w, sw, b, q0, s0, acc=True)
+    g1, ga1 = bqd.gemv_w4a8(w, sw, b, q0, s0, acc=True, r=1, lanes_per_row=16)
+    sync()
+    assert torch.equal(q0, q1) and torch.equal(s0, s1)
+    assert torch.equal(a0, a1) and torch.equal(y0, y1)
+    assert torch.equal(ga0, ga1) and torch.equal(g0, g1) and torch.equal(g0, y0)
