@@ -68,3 +68,35 @@ def test_static_pass_refuses_a_workspace_beyond_its_array():
     too_big = bqd.BQD_STATIC_PASS_BYTES + 256
     assert L.decode_pass_w4a8_static(p.desc.data_ptr(), p.n, p.max_k, too_big, 0, err.data_ptr(), None) == -4
     assert L.decode_pass_w4a8_static(p.desc.data_ptr(), p.n, p.max_k, p.sync_bytes, 0, None, None) == -1
+
+
+def test_static_pass_replays_from_a_hip_graph():
+    """The case the entry point is for: captured once into a HIP graph
+    (nothing allocated inside the capture, the workspace cleared by a kernel)
+    and replayed three times, with eager work between the replays; every
+    replay's outputs equal the ordinary entry point's, bit for bit."""
+    torch.cuda.set_device(DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    p, ys = _chained("static/graph", [(4608, 3584), (3584, 3584), (8192, 3584), (3584, 8192)])
+    p.run()
+    torch.cuda.synchronize()
+    assert p.error_word() == 0
+    ref = [y.clone() for y in ys]
+    p.run_static(err)  # warm: library set-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        p.run_static(err)
+    other, other_ys = _chained("static/graph-other", [(1024, 512), (512, 1024)])
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        err.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0, rep
+        for i, (y, r) in enumerate(zip(ys, ref)):
+            assert torch.equal(y, r), (rep, i)
+        other.run_static(err)  # eager use of the same static array between replays
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
