@@ -72,6 +72,22 @@ __device__ __forceinline__ BQD_GLOBAL T* gptr_mut(T* p)
     return (BQD_GLOBAL T*)p;
 }
 
+// Raw buffer resources.  A buffer load at an offset past the resource's
+// size returns zeros and makes no memory access: loads that must not read
+// can still be issued unconditionally, so the compiler counts them exactly.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kDeviceScope = 16;          // buffer-load cache-policy bit sc1
+constexpr int kBufferPast = 0x7FFFFFF0;   // an offset past every resource this file makes
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes)
+{
+    // the address is wave-uniform: keep the resource in scalar registers
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, bytes, kBufferWord3);
+}
+
 // ------------------------------------------------------------------------
 // Bit helpers
 // ------------------------------------------------------------------------
@@ -2003,40 +2019,119 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 // cut into one block per workgroup: a range of tiles times a K slice, all
 // blocks holding about the same number of quads.  A workgroup stages only
 // its slice's codes of the M tokens (issued before its weight loads, so they
-// do not queue behind them), its 16 waves split the block's quads into
-// contiguous runs with every weight load of a run in flight at once, and
-// each wave adds its exact int32 partials into per-tile LDS accumulators.
+// do not queue behind them), its 16 waves split the block's 4-quad groups
+// into contiguous runs with the weight loads of up to 3 groups in flight at
+// once, and each wave adds its exact int32 partials into per-tile LDS
+// accumulators.
 // With one K slice the workgroup owns its tiles and writes y directly.
-// With several, each block stores its tiles' partials into the workspace
-// and counts in on the tile; the block that counts in last adds the slices'
-// partials (integers: the order does not matter), writes y and clears the
-// tile's count and partials, so the whole workspace is zero again for the
-// next call, of any shape.  No block waits for another to reach anything:
-// the last one only waits for stores already issued to arrive.
+// With several, each block counts in on its tiles as it starts (the count's
+// round trip overlaps its staging and MFMAs); the block that counted in
+// last on a tile gathers it: it loads the other slices' partials, adds its
+// own (integers: the order does not matter), writes y and clears the
+// tile's count and the partials, so the whole workspace is zero again for
+// the next call, of any shape.  The others store their partials and leave.
+// A gatherer only waits for blocks that have already counted in, hence
+// started; the blocks of a tile group walk the tiles' words in the same
+// order, and at each word one block waits for what the others store at that
+// same word, so every wait ends without any assumption about which blocks
+// are resident together.
 // ------------------------------------------------------------------------
 constexpr int kVbWaves = 16;
 constexpr int kVbThreads = kVbWaves * kWave;
 constexpr int kVbMaxTiles = 16;             // tiles per block (LDS accumulators)
-constexpr int kVbQ = 10;                    // quads a wave has in flight
+constexpr int kVbGroups = 3;                // 4-quad groups a wave has in flight
+constexpr int kVbQ = 4 * kVbGroups;         // their registers (one quad each)
 constexpr int kVbStage = 8;                 // staging loads per thread per batch
 constexpr int kVbXsBytes = 112 * 1024;      // LDS for the staged codes
 constexpr int kVbCountWords = 64;           // tile counts are padded to 256 bytes
 constexpr int kVbSpinLimit = 1 << 20;       // polls of one partial word (its store is already issued)
 constexpr int kVbSplitCost = 600;           // fixed charge of a K split in vb_plan, sixths of a quad
+static_assert(kVbStage * kVbThreads * 16 >= kVbXsBytes, "one staging batch holds a whole slice");
 
-__device__ __forceinline__ void vb_load(u32x4 (&buf)[kVbQ], const u32x4* __restrict__ wq, int u0, int ue,
-                                        int qs, int t0, int N, int C, int c0, int nc, int g, int col)
+// Weights stream in groups: a group is one tile's 16 rows times 16 chunks
+// (256 bytes of each row, 4 quads), read by 4 loads of 4 rows x 256
+// contiguous bytes each (load p, lane l: row 4p + l / 16, chunk l % 16):
+// a 16-lane quarter of a load covers two whole 128-byte lines, where the
+// matrix cores' own operand order (16 rows x 64 bytes per load) would touch
+// 16 half lines, and the verify ran 1.5 us slower for it at [3584, 18944].
+// Slots past ue, rows past the matrix and chunks past the slice load at an
+// offset past the resource: zeros, no memory access.  wr covers this
+// block's tiles' rows (16-byte chunks, row pitch C).
+__device__ __forceinline__ void vb_load(u32x4 (&buf)[kVbQ], __amdgpu_buffer_rsrc_t wr, int u0, int ue, int qg,
+                                        int nrows, int C, int c0, int nc, int lane)
 {
 #pragma unroll
-    for (int j = 0; j < kVbQ; ++j) {
-        const int u = u0 + j;
-        if (u < ue) {  // uniform across the wave
-            const int lt = u / qs, q = u - lt * qs;
-            const int row = min((t0 + lt) * 16 + col, N - 1);
-            const int c = min(4 * q + g, nc - 1);  // past the slice: any chunk, its codes meet zeros
-            buf[j] = wq[(size_t)row * C + c0 + c];
+    for (int h = 0; h < kVbGroups; ++h) {
+        const int u = u0 + h;
+        const int lt = u / qg, c = 16 * (u - lt * qg) + (lane & 15);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int row = lt * 16 + 4 * p + (lane >> 4);
+            const int off = u < ue && row < nrows && c < nc ? 16 * (row * C + c0 + c) : kBufferPast;
+            buf[4 * h + p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
         }
     }
+}
+
+// Exchange between registers a and b across lane distance D (4 or 8, inside
+// a 16-lane row): lanes with bit D set take b from D lanes below into a,
+// lanes with it clear take a from D lanes above into b.
+template <int D>
+__device__ __forceinline__ void vb_xchg(uint32_t& a, uint32_t& b, bool hi)
+{
+    constexpr int kHi = D == 4 ? 0xA : 0xC, kLo = D == 4 ? 0x5 : 0x3;  // banks with / without lane bit D
+    const uint32_t na = (uint32_t)__builtin_amdgcn_update_dpp((int)a, (int)b, 0x110 | D, 0xF, kHi, false);
+    const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp((int)b, (int)a, 0x100 | D, 0xF, kLo, false);
+    a = na;
+    b = nb;
+}
+
+// A group from its load order (register p, lane l: row 4p + l / 16, chunk
+// l % 16) into the matrix cores' (register t, lane 16g + i: row i, chunk
+// 4t + g).  With the index bits written out, a load's element sits at
+// register (r2 r3), lane (c0 c1 c2 c3 r0 r1) and must go to register
+// (c2 c3), lane (r0 r1 r2 r3 c0 c1): a lane permutation swapping lane bits
+// 0,1 with 4,5, then register bit 0 exchanged with lane bit 2 and register
+// bit 1 with lane bit 3.  The lane permutation goes through the wave's own
+// LDS scratch (each register written in lane order and read back permuted:
+// two 16-byte LDS accesses per lane, where ds_bpermute takes four 4-byte
+// ones and measured slower); the exchanges are DPP row shifts whose bank
+// masks pick the lanes (lane bits 2 and 3 select 4-lane banks).
+constexpr int kVbScratch = 68;  // 16-byte slots per wave: 4 rows of 16 lanes, each + 1 against bank conflicts
+static_assert(kVbXsBytes + kVbMaxTiles * 256 * 4 + kVbWaves * kVbScratch * 16 + kVbMaxTiles * 4 <= kLdsMaxBytes,
+              "verify LDS: staged codes, tile sums, transpose scratch");
+
+__device__ __forceinline__ int vb_slot(int l)
+{
+    return 17 * (l >> 4) + (l & 15);
+}
+
+__device__ __forceinline__ void vb_transpose(u32x4& w0, u32x4& w1, u32x4& w2, u32x4& w3, u32x4* sc, int rd, int lane)
+{
+    // sc: this wave's scratch; rd: this lane's read slot (its source lane's write slot)
+    const int wr = vb_slot(lane);
+    sc[wr] = w0;
+    w0 = sc[rd];
+    sc[wr] = w1;
+    w1 = sc[rd];
+    sc[wr] = w2;
+    w2 = sc[rd];
+    sc[wr] = w3;
+    w3 = sc[rd];
+    uint32_t v[4][4] = {{w0.x, w0.y, w0.z, w0.w}, {w1.x, w1.y, w1.z, w1.w},
+                        {w2.x, w2.y, w2.z, w2.w}, {w3.x, w3.y, w3.z, w3.w}};
+    const bool b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        vb_xchg<4>(v[0][e], v[1][e], b2);
+        vb_xchg<4>(v[2][e], v[3][e], b2);
+        vb_xchg<8>(v[0][e], v[2][e], b3);
+        vb_xchg<8>(v[1][e], v[3][e], b3);
+    }
+    w0 = u32x4{v[0][0], v[0][1], v[0][2], v[0][3]};
+    w1 = u32x4{v[1][0], v[1][1], v[1][2], v[1][3]};
+    w2 = u32x4{v[2][0], v[2][1], v[2][2], v[2][3]};
+    w3 = u32x4{v[3][0], v[3][1], v[3][2], v[3][3]};
 }
 
 __global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
@@ -2048,14 +2143,15 @@ __global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
     extern __shared__ u32x4 xs[];  // token m's slice chunk c: xs[m * TS + 2c], [.. + 1]
     __shared__ int32_t tacc[kVbMaxTiles * 256];  // [tile][row 16][token 16]
     __shared__ uint32_t s_last[kVbMaxTiles];
+    __shared__ u32x4 vbt[kVbWaves * kVbScratch];  // the waves' transpose scratch
     const int T = (N + 15) >> 4;
     const int ks = blockIdx.x % ksplit, tg = blockIdx.x / ksplit;
     const int t0 = (int)((long long)tg * T / ntg), nt = (int)((long long)(tg + 1) * T / ntg) - t0;
     const int c0 = ks * kslice, nc = min(kslice, C - c0);
     if (nt <= 0 || nc <= 0)
         return;  // uniform: a block with no tiles contributes to none
-    const int qs = (nc + 3) >> 2;  // quads per tile in this slice
-    const int total = nt * qs;
+    const int qg = (nc + 15) >> 4;  // 4-quad groups per tile in this slice
+    const int total = nt * qg;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int g = lane >> 4, col = lane & 15;
     const bool tok = col < M;
@@ -2063,7 +2159,13 @@ __global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
     const int nh = 2 * nc, items = M * nh;
     const u32x4* qv = reinterpret_cast<const u32x4*>(qx);
     const int K2 = 2 * C;  // 16-byte halves per token row
-    // 1. the first staging batch, ahead of the weights
+    // 0. with a split, count in on this block's tiles; the old count is
+    //    first used after the MFMAs, when wave 0's loads have all landed
+    uint32_t* cnt = ws;
+    uint32_t cnt_old = 0;
+    if (ksplit > 1 && wave == 0 && lane < nt)
+        cnt_old = __hip_atomic_fetch_add(&cnt[t0 + lane], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // 1. the staging loads (one batch holds the whole slice), ahead of the weights
     u32x4 sv[kVbStage];
 #pragma unroll
     for (int j = 0; j < kVbStage; ++j) {
@@ -2072,41 +2174,34 @@ __global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
     }
     for (int i = tid; i < nt * 256; i += kVbThreads)
         tacc[i] = 0;
-    // 2. this wave's run of quads [qa, qb): the first kVbQ of them in flight
-    const int qa = (int)((long long)wave * total / kVbWaves), qb = (int)((long long)(wave + 1) * total / kVbWaves);
+    // 2. this wave's run of groups [ga, gb): the first kVbGroups of them in flight
+    const int ga = (int)((long long)wave * total / kVbWaves), gb = (int)((long long)(wave + 1) * total / kVbWaves);
+    const int nrows = min(nt * 16, N - t0 * 16);
+    const __amdgpu_buffer_rsrc_t wr = uniform_rsrc(wq + (size_t)t0 * 16 * C, nrows * C * 16);
     u32x4 wb[kVbQ];
-    vb_load(wb, wq, qa, min(qb, qa + kVbQ), qs, t0, N, C, c0, nc, g, col);
+    vb_load(wb, wr, ga, min(gb, ga + kVbGroups), qg, nrows, C, c0, nc, lane);
     // 3. staged codes into LDS, permuted for the unpacked weight halves
-    for (int i0 = tid;; i0 += kVbStage * kVbThreads) {
 #pragma unroll
-        for (int j = 0; j < kVbStage; ++j) {
-            const int i = i0 + j * kVbThreads;
-            if (i < items)
-                xs[(i / nh) * TS + i % nh] = u32x4{perm_even(sv[j].x, sv[j].y), perm_odd(sv[j].x, sv[j].y),
-                                                   perm_even(sv[j].z, sv[j].w), perm_odd(sv[j].z, sv[j].w)};
-        }
-        if (i0 + kVbStage * kVbThreads >= items)
-            break;
-#pragma unroll
-        for (int j = 0; j < kVbStage; ++j) {
-            const int i = min(i0 + (kVbStage + j) * kVbThreads, items - 1);
-            sv[j] = qv[(size_t)(i / nh) * K2 + 2 * c0 + i % nh];
-        }
+    for (int j = 0; j < kVbStage; ++j) {
+        const int i = tid + j * kVbThreads;
+        if (i < items)
+            xs[(i / nh) * TS + i % nh] = u32x4{perm_even(sv[j].x, sv[j].y), perm_odd(sv[j].x, sv[j].y),
+                                               perm_even(sv[j].z, sv[j].w), perm_odd(sv[j].z, sv[j].w)};
     }
     __syncthreads();
     // 4. the MFMAs; a change of tile flushes the wave's partial into LDS
     i32x4 acc = {0, 0, 0, 0};
     int cur = -1;
     const int xrow = col * TS;
-    for (int u0 = qa; u0 < qb; u0 += kVbQ) {
-        const int ue = min(qb, u0 + kVbQ);
-        if (u0 != qa)
-            vb_load(wb, wq, u0, ue, qs, t0, N, C, c0, nc, g, col);
+    u32x4* const sc = vbt + kVbScratch * wave;
+    const int rd = vb_slot(((lane & 3) << 4) | ((lane >> 4) & 3) | (lane & 12));  // lane bits 0,1 <-> 4,5
+    for (int u0 = ga; u0 < gb; u0 += kVbGroups) {
 #pragma unroll
-        for (int j = 0; j < kVbQ; ++j) {
-            const int u = u0 + j;
-            if (u < ue) {
-                const int lt = u / qs, q = u - lt * qs;
+        for (int h = 0; h < kVbGroups; ++h) {
+            const int u = u0 + h;
+            if (u < gb) {  // uniform across the wave
+                vb_transpose(wb[4 * h], wb[4 * h + 1], wb[4 * h + 2], wb[4 * h + 3], sc, rd, lane);
+                const int lt = u / qg, cg = 16 * (u - lt * qg);
                 if (lt != cur) {
                     if (cur >= 0) {
 #pragma unroll
@@ -2117,21 +2212,32 @@ __global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
                     acc = i32x4{0, 0, 0, 0};
                     cur = lt;
                 }
-                const int c = 4 * q + g;
-                u32x4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
-                if (tok && c < nc) {
-                    xa = xs[xrow + 2 * c];
-                    xb = xs[xrow + 2 * c + 1];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int c = cg + 4 * t + g;
+                    u32x4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
+                    if (tok && c < nc) {
+                        xa = xs[xrow + 2 * c];
+                        xb = xs[xrow + 2 * c + 1];
+                    }
+                    acc = mfma_chunk(wb[4 * h + t], xa, xb, acc);
                 }
-                acc = mfma_chunk(wb[j], xa, xb, acc);
             }
         }
+        if (u0 + kVbGroups < gb)  // the run's next groups
+            vb_load(wb, wr, u0 + kVbGroups, min(gb, u0 + 2 * kVbGroups), qg, nrows, C, c0, nc, lane);
     }
     if (cur >= 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             __hip_atomic_fetch_add(&tacc[cur * 256 + (4 * g + e) * 16 + col], acc[e], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (ksplit > 1 && wave == 0 && lane < nt) {
+        const bool last = cnt_old == (uint32_t)(ksplit - 1);
+        if (last)  // every slice of the tile has counted in: ready for the next call
+            __hip_atomic_store(&cnt[t0 + lane], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last[lane] = last;
     }
     __syncthreads();
     // 5. outputs
@@ -2149,32 +2255,23 @@ __global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
     }
     // Each partial word goes out as one 64-bit atomic store {1, value}: its
     // high half says it is there, so no store needs to be ordered before
-    // another and no fence is needed.  The count only decides which slice
-    // adds the tile up; that slice loads each word until its high half is
-    // set (the other slices issued their stores before counting in, so
-    // every such wait ends), then clears it.
-    uint32_t* cnt = ws;
+    // another and no fence is needed.  The gatherer loads each other slice's
+    // word until its high half is set, then clears it.  (Loading all slices'
+    // words at once, and those not there yet again together, was measured
+    // slower: the gatherer mostly waits for the slowest other slice, and
+    // one word at a time finds the later slices' words already there.)
     uint64_t* part = reinterpret_cast<uint64_t*>(ws + (((size_t)T + kVbCountWords - 1) / kVbCountWords) * kVbCountWords);
-    for (int i = tid; i < nt * 256; i += kVbThreads)
-        __hip_atomic_store(&part[((size_t)ks * T + t0 + (i >> 8)) * 256 + (i & 255)],
-                           (1ull << 32) | (uint32_t)tacc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (wave == 0 && lane < nt) {
-        const uint32_t old = __hip_atomic_fetch_add(&cnt[t0 + lane], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old == (uint32_t)(ksplit - 1);
-        if (last)  // every other slice has counted in: ready for the next call
-            __hip_atomic_store(&cnt[t0 + lane], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last[lane] = last;
-    }
-    __syncthreads();
     for (int i = tid; i < nt * 256; i += kVbThreads) {
-        const int lt = i >> 8;
-        if (!s_last[lt])
+        const int lt = i >> 8;  // uniform across the wave
+        if (!s_last[lt]) {
+            __hip_atomic_store(&part[((size_t)ks * T + t0 + lt) * 256 + (i & 255)], (1ull << 32) | (uint32_t)tacc[i],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             continue;
-        // every slice's partial, then cleared: the whole workspace is zero
-        // again when the call ends, whatever shape uses it next
-        int s = 0;
+        }
+        int s = tacc[i];
         for (int k = 0; k < ksplit; ++k) {
+            if (k == ks)
+                continue;
             uint64_t* pp = &part[((size_t)k * T + t0 + lt) * 256 + (i & 255)];
             uint64_t v = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int spin = 0; (v >> 32) == 0 && spin < kVbSpinLimit; ++spin) {
@@ -2521,18 +2618,6 @@ __device__ __forceinline__ void pass_run_g32(u32x4 (&cur)[kPassSlots], float& es
 // read single-copy atomically.  After spin_limit rounds the wait gives up,
 // sets err bit 0 and takes the words as they are; so does every wait of a
 // workgroup that finds bit 0 already set.
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kDeviceScope = 16;          // buffer-load cache-policy bit sc1
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes)
-{
-    // the address is wave-uniform: keep the resource in scalar registers
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
-                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), (short)0, bytes, kBufferWord3);
-}
-
 __device__ __forceinline__ bool written8(u32x4 a, u32x4 b)
 {
     return a.x && a.y && a.z && a.w && b.x && b.y && b.z && b.w;
@@ -3822,7 +3907,7 @@ static bool vb_plan(int M, int N, int C, VbPlan& p)
     const long long need = (T + kVbMaxTiles - 1) / kVbMaxTiles;
     long long best = -1;
     for (int s = 1; s <= 64 && s <= C; ++s) {
-        const int ksl = (((C + s - 1) / s) + 3) & ~3;
+        const int ksl = (((C + s - 1) / s) + 15) & ~15;  // whole 4-quad groups
         if (ksl > maxc || (C + ksl - 1) / ksl != s)
             continue;
         if (s > 1 && T * s > 2 * G && best >= 0)

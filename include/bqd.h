@@ -348,9 +348,10 @@ int gemv_w4a16(const uint32_t* wq, const float* sw, const float* bias, const uin
  * balanced blocks: one block per workgroup, a range of 16-row tiles times a
  * K slice with about the same number of weights in each, only the slice's
  * codes staged.  When the K range is split, each slice's exact int32
- * partials go through the workspace and the slice that finishes a tile last
- * adds them and writes y (no workgroup waits for another to reach
- * anything).  0 automatic: M = 1 runs gemv_w4a8's kernel; M >= 2 impl 3
+ * partials go through the workspace and the slice that started a tile last
+ * adds them and writes y (it waits only for slices that have already
+ * started, so no wait depends on which workgroups are resident together).
+ * 0 automatic: M = 1 runs gemv_w4a8's kernel; M >= 2 impl 3
  * from 8 tokens on or when N has fewer 16-row tiles than the device has
  * CUs (and the workspace suffices), else impl 2.  Every impl gives the same
  * acc and y bits.
