@@ -1427,6 +1427,74 @@ __device__ __forceinline__ float sum_lanes_q6(float v)
 // bytes, high fields 16 bytes, the four sub-block scales as one 4-byte word
 // and the fp16 super-block scale -- five loads per 64 weights; U units per
 // step, R rows per lane group, L lanes per row.
+template <int R, int U>
+struct Q6Step {
+    u32x4 la[U][R], lb[U][R], hw[U][R];
+    uint32_t s4[U][R], dd[U][R];
+};
+
+// The loads of step `it` of the rows rr (clamped rows; a unit past the row
+// loads at a clamped unit with its scales zeroed, so it adds nothing).
+template <int R, int L, int U>
+__device__ __forceinline__ void q6k_load(Q6Step<R, U>& s, const u32x4* __restrict__ ql, const u32x4* __restrict__ qh,
+                                         const uint32_t* __restrict__ sc4, const uint16_t* __restrict__ d16,
+                                         const size_t (&rr)[R], int it, int iters, int C, int lane)
+{
+    const int C2 = C / 2, D = C / 8;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c2 = (it + u) * L + lane;
+        const bool ok = (it + u < iters) && (c2 < C2);
+        const int cc = min(c2, C2 - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            s.la[u][r] = ql[rr[r] * C + 2 * cc];
+            s.lb[u][r] = ql[rr[r] * C + 2 * cc + 1];
+            s.hw[u][r] = qh[rr[r] * C2 + cc];
+            const uint32_t sv = sc4[rr[r] * C2 + cc];
+            s.s4[u][r] = ok ? sv : 0u;
+            s.dd[u][r] = d16[rr[r] * D + cc / 4];
+        }
+    }
+}
+
+template <int R, int L, int U>
+__device__ __forceinline__ void q6k_dot(const Q6Step<R, U>& s, const u32x4* xs, int it, int C, int lane,
+                                        float (&facc)[R])
+{
+    const int C2 = C / 2;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = 2 * min((it + u) * L + lane, C2 - 1);
+        const u32x4 g0 = xs[4 * c], g1 = xs[4 * c + 1], g2 = xs[4 * c + 2], g3 = xs[4 * c + 3];
+        const u32x4 g4 = xs[4 * c + 4], g5 = xs[4 * c + 5], g6 = xs[4 * c + 6], g7 = xs[4 * c + 7];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x4 wa = s.la[u][r], wb = s.lb[u][r], h = s.hw[u][r];
+            float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+            p0 = dot8_q6(wa.x, h.x, g0.x, g0.y, g0.z, g0.w, p0);
+            p0 = dot8_q6(wa.y, h.x >> 8, g1.x, g1.y, g1.z, g1.w, p0);
+            p1 = dot8_q6(wa.z, h.y, g2.x, g2.y, g2.z, g2.w, p1);
+            p1 = dot8_q6(wa.w, h.y >> 8, g3.x, g3.y, g3.z, g3.w, p1);
+            p2 = dot8_q6(wb.x, h.z, g4.x, g4.y, g4.z, g4.w, p2);
+            p2 = dot8_q6(wb.y, h.z >> 8, g5.x, g5.y, g5.z, g5.w, p2);
+            p3 = dot8_q6(wb.z, h.w, g6.x, g6.y, g6.z, g6.w, p3);
+            p3 = dot8_q6(wb.w, h.w >> 8, g7.x, g7.y, g7.z, g7.w, p3);
+            const float df = (float)__builtin_bit_cast(_Float16, (uint16_t)s.dd[u][r]);
+            const uint32_t sv = s.s4[u][r];
+            float a = facc[r];
+            a = fmaf(df * (float)(int8_t)(sv & 0xFFu), p0, a);
+            a = fmaf(df * (float)(int8_t)((sv >> 8) & 0xFFu), p1, a);
+            a = fmaf(df * (float)(int8_t)((sv >> 16) & 0xFFu), p2, a);
+            a = fmaf(df * (float)(int8_t)(sv >> 24), p3, a);
+            facc[r] = a;
+        }
+    }
+}
+
+// Up to 2 rows per lane group the next step's loads are issued before the
+// current step's decode (two register sets; with more rows one set, as the
+// registers run out).
 template <int R, int L>
 __global__ __launch_bounds__(kThreads) void k_gemv_q6k(const u32x4* __restrict__ ql, const u32x4* __restrict__ qh,
                                                        const uint32_t* __restrict__ sc4,
@@ -1435,6 +1503,28 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q6k(const u32x4* __restrict__
                                                        int C)
 {
     extern __shared__ u32x4 xs[];  // per 8 weights: (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+    constexpr int GROUPS = kThreads / L;
+    constexpr int ROWS = GROUPS * R;
+    constexpr bool kPipe = R <= 2;
+    constexpr int U = kPipe ? 1 : 2;
+    const int lane = threadIdx.x % L;
+    const int grp = threadIdx.x / L;
+    const int tiles = (N + ROWS - 1) / ROWS;
+    const int C2 = C / 2;  // 64-weight units per row
+    const int iters = (C2 + L - 1) / L;
+    const int steps = (iters + U - 1) / U;
+    auto rows_of = [&](int tile, size_t (&rr)[R]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            rr[r] = (size_t)min(tile * ROWS + grp * R + r, N - 1);
+    };
+
+    int tile = blockIdx.x;
+    size_t rr[R];
+    rows_of(tile, rr);
+    Q6Step<R, U> cur;
+    if (kPipe && tile < tiles)
+        q6k_load<R, L, U>(cur, ql, qh, sc4, d16, rr, 0, iters, C, lane);  // ahead of the staging
     for (int g = threadIdx.x; g < 4 * C; g += kThreads) {
         const u32x4 v = x16[g];
         xs[g] = u32x4{(v.x & 0xFFFFu) | (v.z << 16), (v.x >> 16) | (v.z & 0xFFFF0000u),
@@ -1442,72 +1532,32 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q6k(const u32x4* __restrict__
     }
     __syncthreads();
 
-    constexpr int GROUPS = kThreads / L;
-    constexpr int ROWS = GROUPS * R;
-    constexpr int U = 2;
-    const int lane = threadIdx.x % L;
-    const int grp = threadIdx.x / L;
-    const int tiles = (N + ROWS - 1) / ROWS;
-    const int C2 = C / 2;  // 64-weight units per row
-    const int iters = (C2 + L - 1) / L;
-    const int D = C / 8;   // super-blocks per row
-
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const int row0 = tile * ROWS + grp * R;
-        size_t rr[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            rr[r] = (size_t)min(row0 + r, N - 1);
+    for (; tile < tiles; tile += gridDim.x) {
+        rows_of(tile, rr);
         float facc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
             facc[r] = 0.0f;
-        for (int it = 0; it < iters; it += U) {
-            u32x4 la[U][R], lb[U][R], hw[U][R];
-            uint32_t s4[U][R], dd[U][R];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c2 = (it + u) * L + lane;
-                const bool ok = (it + u < iters) && (c2 < C2);
-                const int cc = min(c2, C2 - 1);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    // unconditional loads at a clamped unit; past the row the
-                    // scales are zeroed, so the unit adds nothing
-                    la[u][r] = ql[rr[r] * C + 2 * cc];
-                    lb[u][r] = ql[rr[r] * C + 2 * cc + 1];
-                    hw[u][r] = qh[rr[r] * C2 + cc];
-                    const uint32_t sv = sc4[rr[r] * C2 + cc];
-                    s4[u][r] = ok ? sv : 0u;
-                    dd[u][r] = d16[rr[r] * D + cc / 4];
+        for (int st = 0; st < steps; ++st) {
+            if constexpr (kPipe) {
+                int ntile = tile, nst = st + 1;
+                if (nst == steps) {
+                    ntile += gridDim.x;
+                    nst = 0;
                 }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = 2 * min((it + u) * L + lane, C2 - 1);
-                const u32x4 g0 = xs[4 * c], g1 = xs[4 * c + 1], g2 = xs[4 * c + 2], g3 = xs[4 * c + 3];
-                const u32x4 g4 = xs[4 * c + 4], g5 = xs[4 * c + 5], g6 = xs[4 * c + 6], g7 = xs[4 * c + 7];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const u32x4 wa = la[u][r], wb = lb[u][r], h = hw[u][r];
-                    float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
-                    p0 = dot8_q6(wa.x, h.x, g0.x, g0.y, g0.z, g0.w, p0);
-                    p0 = dot8_q6(wa.y, h.x >> 8, g1.x, g1.y, g1.z, g1.w, p0);
-                    p1 = dot8_q6(wa.z, h.y, g2.x, g2.y, g2.z, g2.w, p1);
-                    p1 = dot8_q6(wa.w, h.y >> 8, g3.x, g3.y, g3.z, g3.w, p1);
-                    p2 = dot8_q6(wb.x, h.z, g4.x, g4.y, g4.z, g4.w, p2);
-                    p2 = dot8_q6(wb.y, h.z >> 8, g5.x, g5.y, g5.z, g5.w, p2);
-                    p3 = dot8_q6(wb.z, h.w, g6.x, g6.y, g6.z, g6.w, p3);
-                    p3 = dot8_q6(wb.w, h.w >> 8, g7.x, g7.y, g7.z, g7.w, p3);
-                    const float df = (float)__builtin_bit_cast(_Float16, (uint16_t)dd[u][r]);
-                    const uint32_t sv = s4[u][r];
-                    float a = facc[r];
-                    a = fmaf(df * (float)(int8_t)(sv & 0xFFu), p0, a);
-                    a = fmaf(df * (float)(int8_t)((sv >> 8) & 0xFFu), p1, a);
-                    a = fmaf(df * (float)(int8_t)((sv >> 16) & 0xFFu), p2, a);
-                    a = fmaf(df * (float)(int8_t)(sv >> 24), p3, a);
-                    facc[r] = a;
+                Q6Step<R, U> nxt;
+                const bool more = ntile < tiles;  // uniform across the workgroup
+                if (more) {
+                    size_t nr[R];
+                    rows_of(ntile, nr);
+                    q6k_load<R, L, U>(nxt, ql, qh, sc4, d16, nr, nst * U, iters, C, lane);
                 }
+                q6k_dot<R, L, U>(cur, xs, st * U, C, lane, facc);
+                if (more)
+                    cur = nxt;
+            } else {
+                q6k_load<R, L, U>(cur, ql, qh, sc4, d16, rr, st * U, iters, C, lane);
+                q6k_dot<R, L, U>(cur, xs, st * U, C, lane, facc);
             }
         }
 #pragma unroll
@@ -1515,7 +1565,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_q6k(const u32x4* __restrict__
             facc[r] = sum_lanes_q6<L>(facc[r]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = row0 + r;
+            const int row = tile * ROWS + grp * R + r;
             if (lane == r && row < N)
                 y[row] = facc[r];
         }
@@ -3815,7 +3865,9 @@ int gemv_q6k_f16(const uint8_t* ql, const uint8_t* qh, const int8_t* sc, const u
         return BQD_ERR_ALIGN;
     if (!valid_config(r, lanes_per_row == 8 ? 16 : lanes_per_row))
         return BQD_ERR_CONFIG;
-    const int L = lanes_per_row ? lanes_per_row : 16;
+    // automatic: 2 rows per lane group, 8 lanes per row (the [262144, 1536]
+    // head, us: 63.3 against 70.1 at 16 lanes and 77.6 at 1 row x 16 lanes)
+    const int L = lanes_per_row ? lanes_per_row : 8;
     if (r == 0)
         r = 2;
     if ((rc = bqd_init()))

@@ -279,7 +279,7 @@ int quantize_weights_q6k(const float* W, int32_t N, int32_t K, uint8_t* ql, uint
  * x16 (device) fp16 bits [K], 16-byte aligned; y (device) float [N]; ql and
  * qh 16-, sc 4-, d 2-byte aligned (true for row-major arrays from aligned
  * bases).  K <= 32768.  r, lanes_per_row as in gemv_w4a8, and lanes_per_row
- * may also be 8 (0 = 2 rows, 16 lanes). */
+ * may also be 8 (0 = 2 rows, 8 lanes). */
 int gemv_q6k_f16(const uint8_t* ql, const uint8_t* qh, const int8_t* sc, const uint16_t* d,
                  const uint16_t* x16, float* y, int32_t N, int32_t K, int32_t r,
                  int32_t lanes_per_row, void* stream);
