@@ -700,8 +700,7 @@ def run_verify(a, dev):
                                 "per-call latency, not a bandwidth")
     wl_bytes = WL.bytes_verify(last["M"], 18944, 3584)
     kname = ("k_gemv_w4a8" if last["M"] == 1 and a.impl == 0 else
-             "k_verify_w4a8" if a.impl == 1 else "k_verify_mfma" if a.impl == 2 or (a.impl == 0 and last["M"] < 8)
-             else "k_verify_blocks")
+             "k_verify_w4a8" if a.impl == 1 else "k_verify_mfma" if a.impl == 2 else "k_verify_blocks")
     out["roofline"] = roofline(last["GB/s"], f"{kname} (M={last['M']}, [18944,3584], one launch per step)",
                                last["us"], wl_bytes,
                                measured_traffic(TRAFFIC["verify"]) if (last["M"] == 16 and a.impl == 0) else None)

@@ -2070,9 +2070,8 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 // blocks holding about the same number of quads.  A workgroup stages only
 // its slice's codes of the M tokens (issued before its weight loads, so they
 // do not queue behind them), its 16 waves split the block's 4-quad groups
-// into contiguous runs with the weight loads of up to 3 groups in flight at
-// once, and each wave adds its exact int32 partials into per-tile LDS
-// accumulators.
+// into contiguous runs, one group's weight loads in flight per wave, and
+// each wave adds its exact int32 partials into per-tile LDS accumulators.
 // With one K slice the workgroup owns its tiles and writes y directly.
 // With several, each block counts in on its tiles as it starts (the count's
 // round trip overlaps its staging and MFMAs); the block that counted in
@@ -2089,7 +2088,9 @@ __global__ __launch_bounds__(WAVES * 64) void k_verify_mfma(
 constexpr int kVbWaves = 16;
 constexpr int kVbThreads = kVbWaves * kWave;
 constexpr int kVbMaxTiles = 16;             // tiles per block (LDS accumulators)
-constexpr int kVbGroups = 3;                // 4-quad groups a wave has in flight
+constexpr int kVbGroups = 1;                // 4-quad groups a wave has in flight: with more, the later waves'
+                                            // staging loads queue behind them (16 tokens, [3584, 18944] /
+                                            // [18944, 3584]: 3 groups 15.3 / 14.1 us, 2 15.0 / 13.9, 1 13.9 / 12.9)
 constexpr int kVbQ = 4 * kVbGroups;         // their registers (one quad each)
 constexpr int kVbStage = 8;                 // staging loads per thread per batch
 constexpr int kVbXsBytes = 112 * 1024;      // LDS for the staged codes
@@ -4031,16 +4032,15 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
                                    (workspace && workspace_bytes >= vb_workspace_bytes(N, vp)));
     if (impl == 0) {
         // One token is the decode GEMV; from two tokens on the matrix cores
-        // beat the dot-product kernel on both verify shapes (measured).  The
-        // balanced blocks win from 8 tokens on, and at any token count when
-        // there are fewer tiles than CUs (the blocks then split K); below 8
-        // tokens over many tiles the per-tile kernel is a little faster
-        // (us, impl 2 / 3: [18944, 3584] M = 2 12.2 / 13.0, M = 8 14.0 /
-        // 13.3, M = 16 16.2 / 14.2; [3584, 18944] M = 2 13.5 / 12.9, M = 16
-        // 21.6 / 16.9).
+        // beat the dot-product kernel on both verify shapes (measured), and
+        // the balanced blocks beat the per-tile kernel at every token count
+        // (us, impl 2 / 3: [18944, 3584] M = 2 12.2 / 11.9, M = 4 12.8 /
+        // 11.9, M = 16 16.1 / 12.9; [3584, 18944] M = 2 13.5 / 11.6, M = 16
+        // 21.7 / 13.9).  The per-tile kernel remains for a split plan whose
+        // workspace the caller did not give.
         if (M == 1)
             return gemv_w4a8(wq, sw, bias, qx, sx, y, acc, N, K, 0, 0, stream);
-        impl = vb_fits && (M >= 8 || (N + 15) / 16 < current_cus()) ? 3 : 2;
+        impl = vb_fits ? 3 : 2;
     }
     if (impl == 3) {
         if (!vb_ok)

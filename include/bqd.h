@@ -351,10 +351,9 @@ int gemv_w4a16(const uint32_t* wq, const float* sw, const float* bias, const uin
  * partials go through the workspace and the slice that started a tile last
  * adds them and writes y (it waits only for slices that have already
  * started, so no wait depends on which workgroups are resident together).
- * 0 automatic: M = 1 runs gemv_w4a8's kernel; M >= 2 impl 3
- * from 8 tokens on or when N has fewer 16-row tiles than the device has
- * CUs (and the workspace suffices), else impl 2.  Every impl gives the same
- * acc and y bits.
+ * 0 automatic: M = 1 runs gemv_w4a8's kernel; M >= 2 impl 3 when the
+ * shape needs no workspace or the given one suffices, else impl 2.  Every
+ * impl gives the same acc and y bits.
  * workspace (device, 256-byte aligned) of workspace_bytes bytes, or NULL /
  * 0: needed by impl 3 when gemm_w4a8_verify_workspace_bytes reports more
  * than 0 for the shape (impl 3 refuses a NULL one with BQD_ERR_NULL and a
