@@ -2104,8 +2104,8 @@ static_assert(kVbStage * kVbThreads * 16 >= kVbXsBytes, "one staging batch holds
 // contiguous bytes each (load p, lane l: row 4p + l / 16, chunk l % 16):
 // a 16-lane quarter of a load covers two whole 128-byte lines, where the
 // matrix cores' own operand order (16 rows x 64 bytes per load) touches 16
-// half lines.  Measured at [3584, 18944], 16 tokens: 16.2 us in operand
-// order, 15.3 us in row order with the transpose below.
+// half lines.  Measured at [3584, 18944], 16 tokens, 3 groups in flight:
+// 16.2 us in operand order, 15.3 us in row order with the transpose below.
 // Slots past ue, rows past the matrix and chunks past the slice load at an
 // offset past the resource: zeros, no memory access.  wr covers this
 // block's tiles' rows (16-byte chunks, row pitch C).
