@@ -791,7 +791,9 @@ __global__ __launch_bounds__(kProdThreads) void k_quantize_rows(const float* __r
 //   (R*U 16-byte loads); step s+1 (possibly of the next tile) is loaded while
 //   step s is computed, and the first step is issued before the activation
 //   prologue so that its latency overlaps the staging.  Rows past N read
-//   row N-1 (in bounds) and are never written.
+//   row N-1 (in bounds) and are never written.  Weights are read once, with
+//   non-temporal loads (the single [3584, 3584] GEMV 4.41 -> 4.09 us, the
+//   per-linear 28-layer stream 1.222 -> 1.177 ms).
 // ------------------------------------------------------------------------
 template <int R, int L, int U>
 __device__ __forceinline__ void load_step(u32x4 (&buf)[U][R], const u32x4* __restrict__ wq, int N,
@@ -807,7 +809,7 @@ __device__ __forceinline__ void load_step(u32x4 (&buf)[U][R], const u32x4* __res
         const bool ok = c < C;
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            buf[u][r] = ok ? wrow[r][c] : u32x4{0u, 0u, 0u, 0u};
+            buf[u][r] = ok ? __builtin_nontemporal_load(wrow[r] + c) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -1063,7 +1065,7 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
         u32x4 w[U];
 #pragma unroll
         for (int j = 0; j < U; ++j)
-            w[j] = wq[(size_t)row * C + min(lane + kWave * j, C - 1)];
+            w[j] = __builtin_nontemporal_load(wq + (size_t)row * C + min(lane + kWave * j, C - 1));
         if (tid < G8)
             xs[tid] = u32x2{perm_even(q.x, q.y), perm_odd(q.x, q.y)};
         sxv = *sx_in;
@@ -1076,7 +1078,7 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
         u32x4 w[U];
 #pragma unroll
         for (int j = 0; j < U; ++j)
-            w[j] = wq[(size_t)row * C + min(lane + kWave * j, C - 1)];
+            w[j] = __builtin_nontemporal_load(wq + (size_t)row * C + min(lane + kWave * j, C - 1));
         float m = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
