@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) for W4A8 decode GEMV; implied 28-layer tok/s"
 HBM_PEAK_GBS = 8000.0
-WORKLOADS = ("stream", "single", "layer", "gemma", "verify", "chain", "int8x")
+WORKLOADS = ("stream", "single", "layer", "gemma", "verify", "chain", "int8x", "shard")
 
 
 def parse():
@@ -586,6 +586,74 @@ def run_layer(a, dev):
     return out
 
 
+def run_shard(a, dev):
+    """One GPU's share of the Qwen2-7B-shaped layer under 8-way tensor
+    parallelism, at its real shapes: QKV and gate/up by output rows, O and
+    down by K slices with int32 partial accumulators (the collectives that
+    would join the shares are not part of a one-GPU run)."""
+    from bit_quantized_decode_quantize_amd import workloads as WL
+
+    w = WL.ShardLayerPool(device=dev, G=8, rank=0)
+    log(f"shard pool: {w.copies} copies of {w.weight_bytes()} B")
+    graph = w.copies if (not a.eager) else 0
+    ms, n = time_steps(w.step, a.steps, a.warmup, graph)
+    gbs = w.bytes_per_step() / (ms * 1e-3) / 1e9
+    shapes = ", ".join(f"{e['name']} {'rows' if e['kind'] == 'rows' else 'K slice'} [{e['N']}, {e['K']}]"
+                       for e in w.layers[0])
+    out = base_line(a, gbs, ms, n, {
+        "workload": f"one GPU's share (rank 0 of 8) of a qwen2-7b-shaped decoder layer under tensor parallelism: "
+                    f"{shapes}; per-row int4, fused act-quant on the row shares, int32 partials on the K slices",
+        "launch": "per-linear, HIP graph" if graph else "per-linear", "tp_degree": w.G, "rank": w.rank,
+        "rotation_copies": w.copies, "bytes_per_step": w.bytes_per_step()})
+    out["us_per_share_layer"] = round(ms * 1e3, 3)
+    per = []
+    for j, e0 in enumerate(w.layers[0]):
+        state = {"i": 0}
+
+        def one(j=j):
+            WL.ShardLayerPool.run_linear(w.layers[state["i"] % w.copies][j])
+            state["i"] += 1
+        ms_j, _ = time_steps(one, a.steps, a.warmup, graph)
+        nb = WL.ShardLayerPool.linear_bytes(e0)
+        per.append({"name": e0["name"], "split": "rows" if e0["kind"] == "rows" else "K", "N": e0["N"],
+                    "K": e0["K"], "us": round(ms_j * 1e3, 3), "GB/s": round(nb / (ms_j * 1e-3) / 1e9, 1),
+                    "bytes": nb})
+    out["linears"] = per
+    out["inputs_sha256"] = inputs_digest(*[t for e in w.layers[0] for t in (e["wq"], e["sw"])])
+    g = next(d for d in per if d["name"] == "gate_up")
+    out["roofline"] = roofline(g["GB/s"], "k_linear_wide<2, X_F32> (the gate/up row share, fused act-quant, "
+                               "one launch)", g["us"], g["bytes"], None)
+    if not a.no_cpu_baseline:
+        import oracle as O
+        from bit_quantized_decode_quantize_amd import decode_stream as DS
+        work = []
+        acts = DS.layer_inputs("qwen/L0", 0, dev)
+        for e in w.layers[0]:
+            W = DS.linear_weight_fp32("qwen/L0", e["name"], 0, dev)
+            if e["kind"] == "rows":
+                rows = WL.shard_row_index(e["name"], w.rank, w.G, dev)
+                wq, sw = O.prepare_int4_rowwise(W[rows].cpu().numpy())
+                work.append(("rows", wq, sw, e["b"].cpu().numpy(), e["x"].cpu().numpy()))
+            else:
+                wq, sw = O.prepare_int4_rowwise(W.cpu().numpy())
+                qx, sx = O.quantize_act(acts[e["name"]].cpu().numpy())
+                k0, ks = e["k0"], e["K"]
+                work.append(("k", wq[:, k0 // 8:(k0 + ks) // 8].copy(), sw, float(sx), qx[k0:k0 + ks].copy()))
+            del W
+
+        def once():
+            for kind, wq, sw, b_or_sx, x in work:
+                if kind == "rows":
+                    O.linear_w4a8(wq, sw, b_or_sx, x)
+                else:
+                    O.gemv_w4a8(wq, sw, None, x, b_or_sx)
+        g_cpu, reps, el = cpu_loop(once, w.bytes_per_step(), a.cpu_seconds)
+        out["cpu_baseline"] = {"value": round(g_cpu, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "host": dict(HOST),
+                               "sample": f"the same share, {reps} passes in {el:.1f} s, single-threaded C"}
+    return out
+
+
 def run_gemma(a, dev):
     from bit_quantized_decode_quantize_amd import workloads as WL
     from bit_quantized_decode_quantize_amd import inputs as I
@@ -892,8 +960,8 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {a.gpus} requested): the path would shard by output "
-              "rows (K for the O and down projections, with an int32 all-reduce), and one GPU runs its "
-              "share at the real shape", file=sys.stderr)
+              "rows (K for the O and down projections, with an int32 all-reduce); --workload shard runs one "
+              "GPU's share of a layer at its real shapes", file=sys.stderr)
         sys.exit(2)
     import torch
     dev = torch.device("cuda:0")
@@ -910,7 +978,7 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     out = {"stream": run_stream, "single": run_single, "layer": run_layer, "gemma": run_gemma,
-           "verify": run_verify, "chain": run_chain, "int8x": run_int8x}[a.workload](a, dev)
+           "verify": run_verify, "chain": run_chain, "int8x": run_int8x, "shard": run_shard}[a.workload](a, dev)
     print(json.dumps(out), flush=True)
     # Tear the device state down before the interpreter exits: every launch
     # done, the workload's buffers and passes dropped, torch's cache empty.

@@ -19,6 +19,9 @@ its weights from HBM, as a decode step over a full model does.
   packed 6-bit (section 3 of "在香橙派上跑 Gemma4：vLLM 适配昇腾 310B 的内核开发实录").
 * ``VerifyPool``: the M-token verify GEMM over [18944, 3584] or
   [3584, 18944] (section 5 of the same page).
+* ``ShardLayerPool``: one GPU's share of the Qwen2-7B-shaped layer under
+  8-way tensor parallelism (output rows of QKV and gate/up, a K slice of O
+  and down with int32 partial accumulators).
 * ``Int8XPool``: INT8-X (3,5,8) encoded int8 weights ("定長無損 INT8 壓縮與
   Triton 融合解碼") at a Qwen2-7B linear's shape, codes drawn with the page's
   level shares, through the decode-fused W8A8 GEMV.
@@ -31,7 +34,7 @@ import torch
 
 from . import bqd
 from . import inputs as I
-from .decode_stream import algorithmic_bytes_linear, layer_biases, layer_inputs, linear_weight_fp32
+from .decode_stream import _qwen_part_shapes, algorithmic_bytes_linear, layer_biases, layer_inputs, linear_weight_fp32
 
 POOL_BYTES = 1 << 30
 
@@ -155,6 +158,112 @@ class LayerPool:
 
     def bytes_per_step(self) -> int:
         return sum(algorithmic_bytes_linear(e["N"], e["K"], True) for e in self.layers[0])
+
+    def weight_bytes(self) -> int:
+        return sum(e["N"] * e["K"] // 2 for e in self.layers[0])
+
+
+def shard_row_index(name: str, rank: int, G: int, device) -> torch.Tensor:
+    """Rows of a fused linear that rank ``rank`` of ``G`` holds when the
+    output rows are split: the same share of each fused part (q, k, v; gate,
+    up), so every GPU holds whole heads and matching gate and up rows."""
+    parts, _ = _qwen_part_shapes()[name]
+    idx, off = [], 0
+    for _, n in parts:
+        if n % G:
+            raise ValueError(f"{name}: {n} rows do not split {G} ways")
+        idx.append(torch.arange(off + rank * (n // G), off + (rank + 1) * (n // G)))
+        off += n
+    return torch.cat(idx).to(device)
+
+
+def bytes_partial_gemv(N: int, K: int) -> int:
+    """A K-slice GEMV on int8 codes with int32 partials: packed weights N*K/2,
+    scales 4N, codes K, s^x 4, y 4N and the int32 partials 4N (the entry
+    point writes y as well; the partials are what the all-reduce sums)."""
+    return N * K // 2 + 4 * N + K + 4 + 4 * N + 4 * N
+
+
+class ShardLayerPool:
+    """One GPU's share of the Qwen2-7B-shaped decoder layer (layer 0 of the
+    stream) under G-way tensor parallelism, at its real shapes:
+
+    * QKV and gate/up split by output rows ([576, 3584] and [4736, 3584] at
+      G = 8): x is replicated and every GPU quantises it bit-identically in
+      the fused linear, so no reduction is needed;
+    * O and down split along K ([3584, 448] and [3584, 2368]): each GPU
+      computes exact int32 partial accumulators over its K slice on the
+      activation's codes (s^x being the all-reduced maximum, the codes are
+      the full activation's), an int32 all-reduce of [N] would sum them
+      exactly, and the per-row epilogue (scale, bias) runs once after it.
+
+    Replicated into >= 1 GB of copies; one step = the share's four launches."""
+
+    def __init__(self, seed: int = 0, device="cuda", G: int = 8, rank: int = 0):
+        self.device = torch.device(device)
+        self.G, self.rank = G, rank
+        prefix = "qwen/L0"
+        biases = layer_biases(prefix, seed, self.device)
+        inputs = layer_inputs(prefix, seed, self.device)
+        base = []
+        for name, N, K in I.qwen_layer_linears():
+            W = linear_weight_fp32(prefix, name, seed, self.device)
+            wq, sw = bqd.quantize_weights_int4_rowwise(W)
+            del W
+            if name in ("qkv", "gate_up"):
+                rows = shard_row_index(name, rank, G, self.device)
+                base.append(dict(name=name, kind="rows", N=rows.numel(), K=K, wq=wq[rows].contiguous(),
+                                 sw=sw[rows].contiguous(), b=biases[name][rows].contiguous(), x=inputs[name]))
+            else:
+                if K % (32 * G):
+                    raise ValueError(f"{name}: K = {K} does not split {G} ways into whole 32-value groups")
+                ks = K // G
+                k0 = rank * ks
+                qx, sx = bqd.quantize_act(inputs[name])
+                base.append(dict(name=name, kind="k", N=N, K=ks, k0=k0,
+                                 wq=wq[:, k0 // 8:(k0 + ks) // 8].contiguous(), sw=sw, b=None,
+                                 qx=qx[k0:k0 + ks].contiguous(), sx=sx))
+            del wq
+        share = sum(d["N"] * d["K"] // 2 for d in base)
+        self.copies = _copies(share, 9)
+        self.layers: List[List[Dict]] = []
+        for c in range(self.copies):
+            lin = []
+            for d in base:
+                e = dict(d)
+                if c:
+                    e.update(wq=d["wq"].clone(), sw=d["sw"].clone())
+                    if d["b"] is not None:
+                        e["b"] = d["b"].clone()
+                e["y"] = torch.empty(d["N"], dtype=torch.float32, device=self.device)
+                if d["kind"] == "k":
+                    e["acc"] = torch.empty(d["N"], dtype=torch.int32, device=self.device)
+                lin.append(e)
+            self.layers.append(lin)
+        self.i = 0
+        self.launches_per_step = 4
+        torch.cuda.synchronize(self.device)
+
+    @staticmethod
+    def run_linear(e, stream=None) -> None:
+        if e["kind"] == "rows":
+            bqd.linear_w4a8(e["wq"], e["sw"], e["b"], e["x"], y=e["y"], stream=stream)
+        else:
+            bqd.gemv_w4a8(e["wq"], e["sw"], None, e["qx"], e["sx"], y=e["y"], acc=e["acc"], stream=stream)
+
+    def step(self, stream=None) -> None:
+        for e in self.layers[self.i % self.copies]:
+            self.run_linear(e, stream)
+        self.i += 1
+
+    @staticmethod
+    def linear_bytes(e) -> int:
+        if e["kind"] == "rows":
+            return algorithmic_bytes_linear(e["N"], e["K"], True)
+        return bytes_partial_gemv(e["N"], e["K"])
+
+    def bytes_per_step(self) -> int:
+        return sum(self.linear_bytes(e) for e in self.layers[0])
 
     def weight_bytes(self) -> int:
         return sum(e["N"] * e["K"] // 2 for e in self.layers[0])
