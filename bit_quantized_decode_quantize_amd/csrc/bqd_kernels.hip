@@ -347,6 +347,37 @@ __device__ __forceinline__ void stage_q8(u32x2* xs, const int8_t* qx, int G8)
     }
 }
 
+// Codes a producer already wrote, for K <= 16 * kThreads * kQ8Pre: every
+// 16-byte load (two 8-value groups) issued at once, before the kernel's
+// first weight step, and waited for once.  A CU serves its loads in order,
+// so codes loaded after that step (stage_q8's loop, one round trip per
+// iteration) wait for its weights first.
+constexpr int kQ8Pre = 5;
+__device__ __forceinline__ void preload_q8(const void* qx, int G16, u32x4 (&v)[kQ8Pre])
+{
+    const __amdgpu_buffer_rsrc_t r = uniform_rsrc(qx, 16 * G16);
+#pragma unroll
+    for (int k = 0; k < kQ8Pre; ++k) {
+        const int g = (int)threadIdx.x + k * kThreads;
+        v[k] = u32x4{0u, 0u, 0u, 0u};
+        if (k * kThreads < G16)  // uniform: only the rounds the activation needs
+            v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g < G16 ? 16 * g : kBufferPast,
+                                                                                   0, 0));
+    }
+}
+
+__device__ __forceinline__ void write_q8(u32x2* xs, const u32x4 (&v)[kQ8Pre], int G16)
+{
+#pragma unroll
+    for (int k = 0; k < kQ8Pre; ++k) {
+        const int g = (int)threadIdx.x + k * kThreads;
+        if (g < G16) {
+            xs[2 * g] = u32x2{perm_even(v[k].x, v[k].y), perm_odd(v[k].x, v[k].y)};
+            xs[2 * g + 1] = u32x2{perm_even(v[k].z, v[k].w), perm_odd(v[k].z, v[k].w)};
+        }
+    }
+}
+
 // Quantise x (fp32/fp16, [K]) in the workgroup and stage the codes into LDS.
 // Returns s^x.  Workgroup 0 optionally writes the codes and scale out.
 // Up to K = 8192 each thread keeps its (at most 4) 8-value groups in
@@ -955,6 +986,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
             sx = quant_from_regs(reinterpret_cast<u32x2*>(xs), v, 4 * C, red, qx_out, sx_out);
             staged = true;
         }
+    } else if constexpr (XIN == X_Q8) {
+        if (2 * C <= kQ8Pre * kThreads) {
+            u32x4 v[kQ8Pre];
+            preload_q8(xin, 2 * C, v);
+            load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+            write_q8(reinterpret_cast<u32x2*>(xs), v, 2 * C);
+            sx = *sx_in;
+            staged = true;
+        }
     }
     if (!staged) {
         load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
@@ -1141,6 +1181,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8_g32(
             load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
             load_scales<R, L, U>(scur, s16, N, C, tile * ROWS + grp * R, 0, lane);
             sx = quant_from_regs(reinterpret_cast<u32x2*>(xs), v, 4 * C, red, qx_out, sx_out);
+            staged = true;
+        }
+    } else if constexpr (XIN == X_Q8) {
+        if (2 * C <= kQ8Pre * kThreads) {
+            u32x4 v[kQ8Pre];
+            preload_q8(xin, 2 * C, v);
+            load_step<R, L, U>(cur, wq, N, C, tile * ROWS + grp * R, 0, lane);
+            load_scales<R, L, U>(scur, s16, N, C, tile * ROWS + grp * R, 0, lane);
+            write_q8(reinterpret_cast<u32x2*>(xs), v, 2 * C);
+            sx = *sx_in;
             staged = true;
         }
     }
