@@ -1054,16 +1054,24 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
 
 // ------------------------------------------------------------------------
 // One fused linear in wide workgroups: 1024 threads, one wave per output
-// row (16 rows per workgroup), for short activations (K <= 64 * 32 * U).
-// Every thread loads at most one 8-value group of x, then its wave's row
-// chunks (64 lanes, U chunks each), so the activation's loads go out first
-// and the whole workgroup finds max|x| and writes the codes in one round.
-// Same codes and, the accumulator being exact, the same y bits as
-// k_gemv_w4a8.
+// row (16 rows per workgroup), U 16-byte chunks per lane (K <= 64 * 32 * U,
+// at most 24576).  Every thread first loads its (at most 3) 8-value groups
+// of x (fp32 / fp16) or its (at most 2) 16-byte pieces of codes, then its
+// wave's row chunks, so the activation's loads go out ahead of the weights
+// in the CU's in-order queue; the whole workgroup finds max|x| and writes
+// the codes in one round, and every weight of the workgroup is in flight
+// while it does.  Same codes and, the accumulator being exact, the same y
+// bits as k_gemv_w4a8.
 // ------------------------------------------------------------------------
 constexpr int kWideThreads = 1024;
 constexpr int kWideRows = kWideThreads / kWave;
-constexpr int kWideMaxN = 8192;  // linear_w4a8 takes the wide kernel up to this many rows
+constexpr int kWideMaxN = 8192;   // linear_w4a8 / gemv_w4a8 take the wide kernel up to this many rows
+constexpr int kWideMaxK = 24576;  // and this K (U <= 12 chunks per lane: 16 spilled)
+// On a producer's codes only up to this K: at K = 18944 the 256-thread
+// kernel, which preloads the codes too, was faster ([3584, 18944] 9.0
+// against 9.6 us), while for the fused linear the wide one was ([3584, 18944]
+// in the per-linear 28-layer stream 1.18 -> 1.10 ms per token).
+constexpr int kWideMaxKQ8 = 8192;
 
 // One wave's row of the wide kernels: U chunks per lane against the staged
 // codes, the lanes' exact sum, the fp32 epilogue.
@@ -1093,36 +1101,57 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
     const void* __restrict__ x, const float* __restrict__ sx_in, float* __restrict__ y,
     int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out, float* __restrict__ sx_out, int N, int C)
 {
-    __shared__ u32x2 xs[kWideThreads];  // codes of 8 values per group, permuted
+    constexpr int NG = (U + 3) / 4;  // 8-value groups of x per thread: 4C <= 1024 NG
+    constexpr int NQ = (U + 7) / 8;  // 16-byte pieces of codes per thread: 2C <= 1024 NQ
+    extern __shared__ u32x4 xsd[];   // codes of 8 values per group, permuted (K bytes)
+    u32x2* xs = reinterpret_cast<u32x2*>(xsd);
     __shared__ float red[kWideThreads / kWave];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int G8 = 4 * C;
     const int row = min(blockIdx.x * kWideRows + wave, N - 1);
     float sxv;
     if constexpr (XIN == X_Q8) {
-        // codes already made (a producer's): one 8-byte group per thread
-        const u32x2 q = reinterpret_cast<const u32x2*>(x)[min(tid, G8 - 1)];
+        // codes already made (a producer's)
+        const int G16 = 2 * C;
+        const __amdgpu_buffer_rsrc_t r = uniform_rsrc(x, 16 * G16);
+        u32x4 q[NQ];
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int g = tid + k * kWideThreads;
+            q[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g < G16 ? 16 * g : kBufferPast,
+                                                                                   0, 0));
+        }
         u32x4 w[U];
 #pragma unroll
         for (int j = 0; j < U; ++j)
             w[j] = __builtin_nontemporal_load(wq + (size_t)row * C + min(lane + kWave * j, C - 1));
-        if (tid < G8)
-            xs[tid] = u32x2{perm_even(q.x, q.y), perm_odd(q.x, q.y)};
+#pragma unroll
+        for (int k = 0; k < NQ; ++k) {
+            const int g = tid + k * kWideThreads;
+            if (g < G16) {
+                xs[2 * g] = u32x2{perm_even(q[k].x, q[k].y), perm_odd(q[k].x, q[k].y)};
+                xs[2 * g + 1] = u32x2{perm_even(q[k].z, q[k].w), perm_odd(q[k].z, q[k].w)};
+            }
+        }
         sxv = *sx_in;
         __syncthreads();
         wide_dot<U>(w, xs, C, lane, blockIdx.x * kWideRows + wave, N, sw, bias, sxv, y, acc_out);
         return;
     } else {
-        float v[8];
-        load8<XIN>(x, min(tid, G8 - 1), v);
+        float v[NG][8];
+#pragma unroll
+        for (int k = 0; k < NG; ++k)
+            load8<XIN>(x, min(tid + k * kWideThreads, G8 - 1), v[k]);  // a clamped group repeats a real one
         u32x4 w[U];
 #pragma unroll
         for (int j = 0; j < U; ++j)
             w[j] = __builtin_nontemporal_load(wq + (size_t)row * C + min(lane + kWave * j, C - 1));
         float m = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            m = fmaxf(m, fabsf(v[e]));  // a clamped group repeats a real one
+        for (int k = 0; k < NG; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                m = fmaxf(m, fabsf(v[k][e]));
         m = wave_max_dpp(m);
         if (lane == 0)
             red[wave] = m;
@@ -1132,12 +1161,16 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
         for (int i = 1; i < kWideThreads / kWave; ++i)
             amax = fmaxf(amax, red[i]);
         const ActScale a = act_scale(amax);
-        if (tid < G8) {
-            uint32_t lo, hi;
-            quant8_fast(v, a, lo, hi);
-            xs[tid] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
-            if (qx_out && blockIdx.x == 0)
-                reinterpret_cast<u32x2*>(qx_out)[tid] = u32x2{lo, hi};
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const int g = tid + k * kWideThreads;
+            if (g < G8) {
+                uint32_t lo, hi;
+                quant8_fast(v[k], a, lo, hi);
+                xs[g] = u32x2{perm_even(lo, hi), perm_odd(lo, hi)};
+                if (qx_out && blockIdx.x == 0)
+                    reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+            }
         }
         if (sx_out && blockIdx.x == 0 && tid == 0)
             *sx_out = a.s;
@@ -3073,6 +3106,9 @@ inline bool valid_config(int r, int L)
 // INT4: 1 -- the Qwen-shaped stream takes 1.42 ms per token with 1 and
 // 1.51 ms with 2; group-32: 2, which the Gemma-shaped stream prefers).  U
 // covers a lane's whole row when it fits the register budget.
+// Chunks per lane of the wide kernel's instances (the smallest that covers C / 64 is launched).
+#define BQD_WIDE_CASES(X) X(1) X(2) X(3) X(4) X(6) X(8) X(10) X(12)
+
 inline GemvCfg make_cfg(int N, int C, int r, int L, int r_large)
 {
     GemvCfg c;
@@ -3658,18 +3694,18 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
-    if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= 8192) {
+    if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= kWideMaxKQ8) {
         // wide workgroups, as for linear_w4a8
         const int C = K / 32, U = (C + kWave - 1) / kWave;
         const dim3 grid((N + kWideRows - 1) / kWideRows), block(kWideThreads);
         const u32x4* w = reinterpret_cast<const u32x4*>(wq);
 #define BQD_WIDE_Q8_CASE(UU)                                                                               \
         if (U <= UU) {                                                                                     \
-            hipLaunchKernelGGL((k_linear_wide<UU, X_Q8>), grid, block, 0, (hipStream_t)stream, w, sw, bias, \
-                               qx, sx, y, acc, nullptr, nullptr, N, C);                                    \
+            hipLaunchKernelGGL((k_linear_wide<UU, X_Q8>), grid, block, (size_t)K, (hipStream_t)stream, w, sw, \
+                               bias, qx, sx, y, acc, nullptr, nullptr, N, C);                              \
             return launched();                                                                             \
         }
-        BQD_WIDE_Q8_CASE(1) BQD_WIDE_Q8_CASE(2) BQD_WIDE_Q8_CASE(4)
+        BQD_WIDE_Q8_CASE(1) BQD_WIDE_Q8_CASE(2) BQD_WIDE_Q8_CASE(3) BQD_WIDE_Q8_CASE(4)
 #undef BQD_WIDE_Q8_CASE
     }
     return launch_gemv_rowwise<X_Q8>(wq, sw, bias, qx, sx, y, acc, nullptr, nullptr, N, K,
@@ -3702,12 +3738,11 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
-    if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= 8192) {
-        // wide workgroups for short activations and few rows (measured, the
-        // single Q projection [3584, 3584] graph-replayed: 5.54 -> 4.38 us,
-        // cold 8.6 -> 7.6 us; the per-linear 28-layer stream 1.266 -> 1.215
-        // ms; with gate/up and the lm_head also wide the stream is slower,
-        // 1.279 ms)
+    if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= kWideMaxK) {
+        // wide workgroups for few rows (measured, the single Q projection
+        // [3584, 3584] graph-replayed: 5.54 -> 4.38 us, cold 8.6 -> 7.6 us;
+        // the per-linear 28-layer stream 1.266 -> 1.215 ms; with gate/up and
+        // the lm_head also wide the stream is slower, 1.279 ms)
         const int C = K / 32, U = (C + kWave - 1) / kWave;
         const dim3 grid((N + kWideRows - 1) / kWideRows), block(kWideThreads);
         hipStream_t st = (hipStream_t)stream;
@@ -3715,14 +3750,14 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
 #define BQD_WIDE_CASE(UU)                                                                                 \
         if (U <= UU) {                                                                                    \
             if (x_dtype == BQD_F32)                                                                       \
-                hipLaunchKernelGGL((k_linear_wide<UU, X_F32>), grid, block, 0, st, w, sw, bias, x, nullptr, \
-                                   y, acc, qx_out, sx_out, N, C);                                         \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F32>), grid, block, (size_t)K, st, w, sw, bias, x, \
+                                   nullptr, y, acc, qx_out, sx_out, N, C);                                \
             else                                                                                          \
-                hipLaunchKernelGGL((k_linear_wide<UU, X_F16>), grid, block, 0, st, w, sw, bias, x, nullptr, \
-                                   y, acc, qx_out, sx_out, N, C);                                         \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F16>), grid, block, (size_t)K, st, w, sw, bias, x, \
+                                   nullptr, y, acc, qx_out, sx_out, N, C);                                \
             return launched();                                                                            \
         }
-        BQD_WIDE_CASE(1) BQD_WIDE_CASE(2) BQD_WIDE_CASE(4)
+        BQD_WIDE_CASES(BQD_WIDE_CASE)
 #undef BQD_WIDE_CASE
     }
     const GemvCfg c = make_cfg(N, K / 32, r, lanes_per_row, 1);

@@ -218,7 +218,7 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias,
  * memory.  x (device) [K] of x_dtype.  qx_out (device int8 [K]) and sx_out
  * (device float [1]) are optional copies of the quantised activation written
  * by one workgroup; acc as in gemv_w4a8.  With r = lanes_per_row = 0, up to
- * 8192 rows and K <= 8192 run in 1024-thread workgroups of one wave per row
+ * 8192 rows and K <= 24576 run in 1024-thread workgroups of one wave per row
  * (same bits). */
 int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias,
                 const void* x, int32_t x_dtype, float* y, int8_t* qx_out,

@@ -1022,10 +1022,12 @@ def test_gemv_int8x_matches_oracle(N, K, dist):
         assert np.all(np.abs(npy(y).astype(np.float64) - y_r) <= TOL * np.where(mag > 0, mag, 1.0)), rows
 
 
-@pytest.mark.parametrize("N,K", [(3584, 3584), (4608, 3584), (17, 32), (8192, 8192), (1000, 1536)])
+@pytest.mark.parametrize("N,K", [(3584, 3584), (4608, 3584), (17, 32), (8192, 8192), (1000, 1536), (33, 8224),
+                                 (3584, 18944), (8192, 12800), (100, 24576)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
 def test_wide_workgroups_give_the_same_bits(N, K, dtype):
-    """The automatic configuration runs short, few-row linears in 1024-thread
+    """The automatic configuration runs few-row linears (K <= 24576: 1 to 12
+    chunks per lane, 1 to 3 activation groups per thread) in 1024-thread
     workgroups (one wave per row): codes, scale, accumulators and y equal the
     256-thread kernel's bit for bit, for the fused linear and for the GEMV on
     a producer's codes."""
