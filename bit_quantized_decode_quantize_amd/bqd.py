@@ -23,6 +23,7 @@ LIB_PATH = os.environ.get("BQD_LIB") or os.path.join(_HERE, "libbqd.so")
 BQD_F32, BQD_F16 = 0, 1
 BQD_SCALE_ROW_F32, BQD_SCALE_GROUP32_F16 = 0, 1
 BQD_MAX_K = 65536
+BQD_MAX_K_ANY = 2113664
 BQD_MAX_TOKENS = 16
 BQD_MAX_PROD_K = 32768
 BQD_MAX_PASS_K = 24576

@@ -1180,6 +1180,84 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
 }
 
 // ------------------------------------------------------------------------
+// W4A8 GEMV for any K % 8 == 0 up to the int32 bound of the page "Jetson
+// Orin AGX INT4 ..." (section "INT32 accumulator 是否安全"), the shapes the
+// kernels above refuse (K % 32 != 0, or more codes than LDS holds): one wave
+// per row, four rows per workgroup, the row read as 4-byte words (a row
+// needs only 4-byte alignment) and the activation from memory, one 8-value
+// group per word.  For an fp32 / fp16 x each workgroup first finds max|x|
+// over the whole activation, then codes every group it meets with
+// quantize_act's arithmetic (the same codes).  A correctness path: it keeps
+// no activation on chip and streams no wider than 4 bytes per lane.
+// ------------------------------------------------------------------------
+constexpr int kAnyRows = kThreads / kWave;
+
+template <int XIN>
+__global__ __launch_bounds__(kThreads) void k_gemv_w4a8_any(
+    const uint32_t* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
+    const void* __restrict__ x, const float* __restrict__ sx_in, float* __restrict__ y,
+    int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out, float* __restrict__ sx_out, int N, int K)
+{
+    __shared__ float red[4];
+    const int G8 = K / 8;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    ActScale a{0.0f, 0.0f, false};
+    float s;
+    if constexpr (XIN == X_Q8) {
+        s = *sx_in;
+    } else {
+        float amax = 0.0f;
+        for (int g = threadIdx.x; g < G8; g += kThreads) {
+            float v[8];
+            load8<XIN>(x, g, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                amax = fmaxf(amax, fabsf(v[e]));
+        }
+        a = act_scale(block_max(amax, red));
+        s = a.s;
+        if (blockIdx.x == 0) {
+            if (qx_out) {
+                for (int g = threadIdx.x; g < G8; g += kThreads) {
+                    float v[8];
+                    load8<XIN>(x, g, v);
+                    uint32_t lo, hi;
+                    quant8_fast(v, a, lo, hi);
+                    reinterpret_cast<u32x2*>(qx_out)[g] = u32x2{lo, hi};
+                }
+            }
+            if (sx_out && threadIdx.x == 0)
+                *sx_out = a.s;
+        }
+    }
+    for (int row = blockIdx.x * kAnyRows + wave; row < N; row += gridDim.x * kAnyRows) {  // wave-uniform
+        const uint32_t* wr = wq + (size_t)row * G8;
+        int acc = 0;
+        for (int g = lane; g < G8; g += kWave) {
+            const uint32_t wv = __builtin_nontemporal_load(wr + g);
+            uint32_t lo, hi;
+            if constexpr (XIN == X_Q8) {
+                const u32x2 q = reinterpret_cast<const u32x2*>(x)[g];
+                lo = q.x;
+                hi = q.y;
+            } else {
+                float v[8];
+                load8<XIN>(x, g, v);
+                quant8_fast(v, a, lo, hi);
+            }
+            acc = __builtin_amdgcn_sdot4(lo16(wv), (int)perm_even(lo, hi), acc, false);
+            acc = __builtin_amdgcn_sdot4(hi16(wv), (int)perm_odd(lo, hi), acc, false);
+        }
+        acc = sum_lanes<kWave>(acc >> 4);
+        if (lane == 0) {
+            if (acc_out)
+                acc_out[row] = acc;
+            y[row] = fmaf(sw[row] * s, (float)acc, bias ? bias[row] : 0.0f);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // W4A8 GEMV, one fp16 scale per 32 codes (= per 16-byte chunk).
 //   y = sx * sum_g s_g * acc_g + b; acc_g exact int32, the scaled sum fp32.
 //   Same pipeline as k_gemv_w4a8, with each chunk's scale loaded beside it.
@@ -3076,6 +3154,31 @@ inline int check_k(int K, int mult = 32)
     return BQD_OK;
 }
 
+// The entry points with a general path (gemv_w4a8, linear_w4a8,
+// quantize_act, gemm_w4a8_verify) take any K % 8 == 0 up to the int32 bound;
+// the fast kernels take K % 32 == 0 up to BQD_MAX_K.
+inline int check_k_any(int K)
+{
+    if (K <= 0 || K % 8)
+        return BQD_ERR_SHAPE;
+    if (K > BQD_MAX_K_ANY)
+        return BQD_ERR_BOUND;
+    return BQD_OK;
+}
+inline bool fast_k(int K) { return K % 32 == 0 && K <= BQD_MAX_K; }
+
+// Launch of the general-K GEMV (rows in a grid-stride loop).
+template <int XIN>
+int launch_gemv_any(const uint32_t* wq, const float* sw, const float* bias, const void* x, const float* sx,
+                    float* y, int32_t* acc, int8_t* qx_out, float* sx_out, int N, int K, hipStream_t st)
+{
+    const long long tiles = ((long long)N + kAnyRows - 1) / kAnyRows;
+    const long long cap = (long long)current_cus() * 8;
+    hipLaunchKernelGGL(k_gemv_w4a8_any<XIN>, dim3((unsigned)(tiles < cap ? tiles : cap)), dim3(kThreads), 0, st, wq,
+                       sw, bias, x, sx, y, acc, qx_out, sx_out, N, K);
+    return launched();
+}
+
 // Launch shape of a GEMV: r rows per lane group, L lanes per row, U chunk
 // iterations per pipeline step, and the number of workgroups.
 struct GemvCfg {
@@ -3547,7 +3650,7 @@ int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K, int8_t* q
         return rc;
     if (M < 0)
         return BQD_ERR_SHAPE;
-    if ((rc = check_k(K)))
+    if ((rc = check_k_any(K)))
         return rc;
     if (M == 0)
         return BQD_OK;
@@ -3559,7 +3662,7 @@ int quantize_act(const void* x, int32_t x_dtype, int32_t M, int32_t K, int8_t* q
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
-    if (x_dtype == BQD_F32 && K <= BQD_MAX_PROD_K && M <= 65535) {
+    if (x_dtype == BQD_F32 && K % 32 == 0 && K <= BQD_MAX_PROD_K && M <= 65535) {
         // fp32 tokens up to 32768 values: the producers' quantiser, ceil(K/4096)
         // workgroups of 1024 threads per token, each holding the whole token in
         // registers (one memory round trip; K = 18944: 8.7 -> ~3 us), the
@@ -3677,7 +3780,7 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8
 {
     if (N < 0)
         return BQD_ERR_SHAPE;
-    int rc = check_k(K);
+    int rc = check_k_any(K);
     if (rc)
         return rc;
     if (!valid_config(r, lanes_per_row))
@@ -3694,6 +3797,8 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
+    if (!fast_k(K))
+        return launch_gemv_any<X_Q8>(wq, sw, bias, qx, sx, y, acc, nullptr, nullptr, N, K, (hipStream_t)stream);
     if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= kWideMaxKQ8) {
         // wide workgroups, as for linear_w4a8
         const int C = K / 32, U = (C + kWave - 1) / kWave;
@@ -3721,7 +3826,7 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
         return rc;
     if (N < 0)
         return BQD_ERR_SHAPE;
-    if ((rc = check_k(K)))
+    if ((rc = check_k_any(K)))
         return rc;
     if (N == 0)
         return BQD_OK;
@@ -3738,6 +3843,11 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
         return BQD_ERR_SHAPE;
     if ((rc = bqd_init()))
         return rc;
+    if (!fast_k(K)) {
+        if (x_dtype == BQD_F32)
+            return launch_gemv_any<X_F32>(wq, sw, bias, x, nullptr, y, acc, qx_out, sx_out, N, K, (hipStream_t)stream);
+        return launch_gemv_any<X_F16>(wq, sw, bias, x, nullptr, y, acc, qx_out, sx_out, N, K, (hipStream_t)stream);
+    }
     if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= kWideMaxK) {
         // wide workgroups for few rows (measured, the single Q projection
         // [3584, 3584] graph-replayed: 5.54 -> 4.38 us, cold 8.6 -> 7.6 us;
@@ -4081,7 +4191,7 @@ static size_t vb_workspace_bytes(int N, const VbPlan& p)
 
 size_t gemm_w4a8_verify_workspace_bytes(int32_t M, int32_t N, int32_t K)
 {
-    if (M < 1 || M > BQD_MAX_TOKENS || N < 1 || check_k(K) || bqd_init())
+    if (M < 1 || M > BQD_MAX_TOKENS || N < 1 || check_k_any(K) || !fast_k(K) || bqd_init())
         return 0;
     VbPlan p;
     return vb_plan(M, N, K / 32, p) ? vb_workspace_bytes(N, p) : 0;
@@ -4093,7 +4203,7 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
 {
     if (M < 0 || N < 0)
         return BQD_ERR_SHAPE;
-    int rc = check_k(K);
+    int rc = check_k_any(K);
     if (rc)
         return rc;
     if (M > BQD_MAX_TOKENS)
@@ -4111,10 +4221,19 @@ int gemm_w4a8_verify(const uint32_t* wq, const float* sw, const float* bias, con
                     {sx, 4 * (size_t)M}},
                    {{y, 4 * (size_t)M * N}, {acc, 4 * (size_t)M * N}, {workspace, workspace_bytes}}))
         return BQD_ERR_SHAPE;
+    if (!fast_k(K) && impl != 0)
+        return BQD_ERR_CONFIG;
     if ((rc = bqd_init()))
         return rc;
-    const int C = K / 32;
     hipStream_t st = (hipStream_t)stream;
+    if (!fast_k(K)) {
+        // the general-K GEMV once per token
+        for (int m = 0; m < M && rc == BQD_OK; ++m)
+            rc = launch_gemv_any<X_Q8>(wq, sw, bias, qx + (size_t)m * K, sx + m, y + (size_t)m * N,
+                                       acc ? acc + (size_t)m * N : nullptr, nullptr, nullptr, N, K, st);
+        return rc;
+    }
+    const int C = K / 32;
     const u32x4* w = reinterpret_cast<const u32x4*>(wq);
     VbPlan vp{1, C, 1};
     const bool vb_ok = vb_plan(M, N, C, vp);

@@ -31,7 +31,11 @@
  *     "Jetson Orin AGX INT4 ..." section "DP4A 做了什么"), each nibble the
  *     two's-complement low four bits of the code.  Row j of an [N, K] matrix
  *     is K/8 consecutive words.
- *   - K must be a positive multiple of 32 and at most BQD_MAX_K; N >= 0
+ *   - K must be a positive multiple of 32 and at most BQD_MAX_K, except for
+ *     gemv_w4a8, linear_w4a8, quantize_act and gemm_w4a8_verify (impl 0),
+ *     which take any K % 8 == 0 up to BQD_MAX_K_ANY: shapes outside the
+ *     first range run a general kernel (4-byte weight words, the activation
+ *     read from memory, r and lanes_per_row not used); N >= 0
  *     (N == 0 or M == 0 enqueue nothing).  Packed weights, int8 activations
  *     and fp32/fp16 activation inputs must be 16-byte aligned; every other
  *     array 4-byte aligned (2-byte for fp16 arrays).
@@ -51,7 +55,7 @@ extern "C" {
 
 #define BQD_OK 0
 #define BQD_ERR_NULL (-1)      /* a required pointer is NULL                 */
-#define BQD_ERR_SHAPE (-2)     /* N/M < 0, K <= 0, K % 32 != 0, bad count     */
+#define BQD_ERR_SHAPE (-2)     /* N/M < 0, K <= 0, K % 32 (or 8) != 0, count */
 #define BQD_ERR_ALIGN (-3)     /* a pointer violates its alignment           */
 #define BQD_ERR_BOUND (-4)     /* K > BQD_MAX_K or M > BQD_MAX_TOKENS        */
 #define BQD_ERR_DTYPE (-5)     /* unknown dtype or scale kind                */
@@ -80,6 +84,9 @@ extern "C" {
  * the kernels stage the whole activation in 64 KiB of LDS, which is the
  * tighter limit. */
 #define BQD_MAX_K 65536
+/* Largest K of the entry points with a general path: the int32 bound above,
+ * rounded down to a multiple of 8. */
+#define BQD_MAX_K_ANY 2113664
 /* Largest token count of gemm_w4a8_verify. */
 #define BQD_MAX_TOKENS 16
 

@@ -66,8 +66,8 @@ def _lib():
     ((P, P, None, P, P, None, None, 8, 64, 0, 0), NULL),
     ((P, P, None, P, P, P, None, -1, 64, 0, 0), SHAPE),
     ((P, P, None, P, P, P, None, 8, 0, 0, 0), SHAPE),
-    ((P, P, None, P, P, P, None, 8, 40, 0, 0), SHAPE),
-    ((P, P, None, P, P, P, None, 8, 65536 + 32, 0, 0), BOUND),
+    ((P, P, None, P, P, P, None, 8, 36, 0, 0), SHAPE),                # K % 8
+    ((P, P, None, P, P, P, None, 8, 2113664 + 8, 0, 0), BOUND),      # past the int32 bound
     ((P4, P, None, P, P, P, None, 8, 64, 0, 0), ALIGN),
     ((P, P, None, P4, P, P, None, 8, 64, 0, 0), ALIGN),
     ((P, P + 2, None, P, P, P, None, 8, 64, 0, 0), ALIGN),
@@ -87,7 +87,17 @@ def test_other_entry_points_validate_before_launch():
     assert L.quantize_act(None, 0, 1, 64, P, P, None) == NULL
     assert L.quantize_act(P, 0, -1, 64, P, P, None) == SHAPE
     assert L.quantize_act(P4, 0, 1, 64, P, P, None) == ALIGN
-    assert L.quantize_act(P, 0, 1, 48, P, P, None) == SHAPE
+    assert L.quantize_act(P, 0, 1, 44, P, P, None) == SHAPE
+    assert L.quantize_act(P, 0, 1, 2113664 + 8, P, P, None) == BOUND
+    # the general path: K % 8 == 0 up to the int32 bound for gemv_w4a8,
+    # linear_w4a8, quantize_act and the automatic verify; other kernels keep K % 32
+    assert L.linear_w4a8(P, P, None, P, 0, P, None, None, None, 8, 44, 0, 0, None) == SHAPE
+    assert L.linear_w4a8(P, P, None, P, 0, P, None, None, None, 8, 2113664 + 8, 0, 0, None) == BOUND
+    assert L.gemm_w4a8_verify(P, P, None, P, P, P, None, 2, 8, 44, 0, None, 0, None) == SHAPE
+    assert L.gemm_w4a8_verify(P, P + 0x1000, None, P + 0x2000, P + 0x3000, P + 0x4000, None, 2, 8, 40, 3,
+                              None, 0, None) == CONFIG                      # impl 1-3 need K % 32
+    assert L.gemv_w4a8_group32(P, P, None, P, P, P, None, 8, 40, 0, 0, None) == SHAPE
+    assert L.gemm_w4a8_verify_workspace_bytes(2, 8, 40) == 0
     # linear_w4a8(wq, sw, bias, x, dtype, y, qx_out, sx_out, acc, N, K, r, lanes, stream)
     assert L.linear_w4a8(P, P, None, P, 7, P, None, None, None, 8, 64, 0, 0, None) == DTYPE
     assert L.linear_w4a8(P, P, None, P4, 0, P, None, None, None, 8, 64, 0, 0, None) == ALIGN
@@ -512,7 +522,7 @@ def test_binding_constants_match_the_header():
     defs = {m.group(1): int(m.group(2)) for m in re.finditer(r"^#define (BQD_\w+) \(?(-?\d+)\)?", text, re.M)}
     mod = bqd.bqd
     shared = [n for n in defs if hasattr(mod, n)]
-    assert {"BQD_MAX_K", "BQD_MAX_TOKENS", "BQD_MAX_PROD_K", "BQD_MAX_PASS_K", "BQD_INT8X_BLOCK", "BQD_F32",
+    assert {"BQD_MAX_K", "BQD_MAX_K_ANY", "BQD_MAX_TOKENS", "BQD_MAX_PROD_K", "BQD_MAX_PASS_K", "BQD_INT8X_BLOCK", "BQD_F32",
             "BQD_F16", "BQD_SCALE_ROW_F32", "BQD_SCALE_GROUP32_F16"} <= set(shared)
     for n in shared:
         assert getattr(mod, n) == defs[n], n

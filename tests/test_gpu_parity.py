@@ -378,6 +378,42 @@ def test_gemv_w4a16_integer_x_equals_w4a8():
     assert torch.equal(y8, y16)
 
 
+# ------------------------------------------------------- general K path --
+@pytest.mark.parametrize("N,K", [(7, 8), (33, 40), (64, 104), (300, 3592), (5, 65544), (3, 2113664)])
+def test_general_k_path(N, K):
+    """K % 8 == 0 outside the fast kernels' range (K % 32 != 0, or more codes
+    than BQD_MAX_K, up to the int32 bound): quantize_act, gemv_w4a8,
+    linear_w4a8 (fp32 and fp16 x) and the automatic verify take the general
+    kernel.  Codes, s^x and acc bit-exact against the oracle, y within
+    tolerance, the verify's token rows equal to the one-token GEMV."""
+    w, qx, sw, b, sx = _rand_gemv(N, K, f"anyk/{N}/{K}")
+    g, acc = bqd.gemv_w4a8(w, sw, b, qx, sx, acc=True, r=2, lanes_per_row=16)  # r, lanes not used here
+    sync()
+    _check_rowwise(g, acc, w, sw, b, qx, sx)
+    X = I.normal(f"gpu/anyk/{K}/X", (2, K), 1.0, device=DEV)
+    for xin in (X[1].contiguous(), X[1].to(torch.float16)):
+        y, q, s1, a = bqd.linear_w4a8(w, sw, b, xin, want_q=True, want_acc=True)
+        sync()
+        qo, so = O.quantize_act(npy(xin))
+        assert np.array_equal(npy(q), qo) and npy(s1)[0] == so
+        acc_r, y_r = O.gemv_w4a8(u32(w), npy(sw), npy(b), qo, float(so))
+        assert np.array_equal(npy(a), acc_r)
+        P.check_rowwise(f"linear {xin.dtype} N={N} K={K}", npy(y), y_r, npy(sw), so, acc_r, npy(b), TOL)
+    QX, SX = bqd.quantize_act(X)
+    sync()
+    qo, so = O.quantize_act(npy(X))
+    assert np.array_equal(npy(QX), qo) and np.array_equal(npy(SX), so)
+    Y, A = bqd.gemm_w4a8_verify(w, sw, b, QX, SX, acc=True)
+    sync()
+    acc_r, y_r = O.gemm_w4a8_verify(u32(w), npy(sw), npy(b), qo, so)
+    assert np.array_equal(npy(A), acc_r)
+    for m in range(2):
+        P.check_rowwise(f"verify token {m}", npy(Y)[m], y_r[m], npy(sw), so[m], acc_r[m], npy(b), TOL)
+        y1 = bqd.gemv_w4a8(w, sw, b, QX[m].clone(), SX[m:m + 1].clone())  # a copy: 16-byte aligned
+        sync()
+        assert torch.equal(y1, Y[m])
+
+
 # -------------------------------------------------------------- verify --
 @pytest.mark.parametrize("impl", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16])
