@@ -1063,8 +1063,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
 // while it does.  Same codes and, the accumulator being exact, the same y
 // bits as k_gemv_w4a8.
 // ------------------------------------------------------------------------
-constexpr int kWideThreads = 1024;
-constexpr int kWideRows = kWideThreads / kWave;
+constexpr int kWideThreads = 1024;  // on a producer's codes
+constexpr int kWideThreadsX = 512;  // quantising x in the prologue (single [3584, 3584]: 4.10 -> 3.96 us; on
+                                    // codes 512 threads were slower, 3.38 -> 3.45 us)
 constexpr int kWideMaxN = 8192;   // linear_w4a8 / gemv_w4a8 take the wide kernel up to this many rows
 constexpr int kWideMaxK = 24576;  // and this K (U <= 12 chunks per lane: 16 spilled)
 // On a producer's codes only up to this K: at K = 18944 the 256-thread
@@ -1095,20 +1096,21 @@ __device__ __forceinline__ void wide_dot(const u32x4 (&w)[U], const u32x2* xs, i
     }
 }
 
-template <int U, int XIN>
-__global__ __launch_bounds__(kWideThreads) void k_linear_wide(
+template <int U, int XIN, int TH>
+__global__ __launch_bounds__(TH) void k_linear_wide(
     const u32x4* __restrict__ wq, const float* __restrict__ sw, const float* __restrict__ bias,
     const void* __restrict__ x, const float* __restrict__ sx_in, float* __restrict__ y,
     int32_t* __restrict__ acc_out, int8_t* __restrict__ qx_out, float* __restrict__ sx_out, int N, int C)
 {
-    constexpr int NG = (U + 3) / 4;  // 8-value groups of x per thread: 4C <= 1024 NG
-    constexpr int NQ = (U + 7) / 8;  // 16-byte pieces of codes per thread: 2C <= 1024 NQ
+    constexpr int ROWS = TH / kWave;                     // one wave per row
+    constexpr int NG = (4 * kWave * U + TH - 1) / TH;  // 8-value groups of x per thread: 4C <= TH NG
+    constexpr int NQ = (2 * kWave * U + TH - 1) / TH;  // 16-byte pieces of codes per thread: 2C <= TH NQ
     extern __shared__ u32x4 xsd[];   // codes of 8 values per group, permuted (K bytes)
     u32x2* xs = reinterpret_cast<u32x2*>(xsd);
-    __shared__ float red[kWideThreads / kWave];
+    __shared__ float red[ROWS];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int G8 = 4 * C;
-    const int row = min(blockIdx.x * kWideRows + wave, N - 1);
+    const int row = min(blockIdx.x * ROWS + wave, N - 1);
     float sxv;
     if constexpr (XIN == X_Q8) {
         // codes already made (a producer's)
@@ -1117,7 +1119,7 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
         u32x4 q[NQ];
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
-            const int g = tid + k * kWideThreads;
+            const int g = tid + k * TH;
             q[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g < G16 ? 16 * g : kBufferPast,
                                                                                    0, 0));
         }
@@ -1127,7 +1129,7 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
             w[j] = __builtin_nontemporal_load(wq + (size_t)row * C + min(lane + kWave * j, C - 1));
 #pragma unroll
         for (int k = 0; k < NQ; ++k) {
-            const int g = tid + k * kWideThreads;
+            const int g = tid + k * TH;
             if (g < G16) {
                 xs[2 * g] = u32x2{perm_even(q[k].x, q[k].y), perm_odd(q[k].x, q[k].y)};
                 xs[2 * g + 1] = u32x2{perm_even(q[k].z, q[k].w), perm_odd(q[k].z, q[k].w)};
@@ -1135,13 +1137,13 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
         }
         sxv = *sx_in;
         __syncthreads();
-        wide_dot<U>(w, xs, C, lane, blockIdx.x * kWideRows + wave, N, sw, bias, sxv, y, acc_out);
+        wide_dot<U>(w, xs, C, lane, blockIdx.x * ROWS + wave, N, sw, bias, sxv, y, acc_out);
         return;
     } else {
         float v[NG][8];
 #pragma unroll
         for (int k = 0; k < NG; ++k)
-            load8<XIN>(x, min(tid + k * kWideThreads, G8 - 1), v[k]);  // a clamped group repeats a real one
+            load8<XIN>(x, min(tid + k * TH, G8 - 1), v[k]);  // a clamped group repeats a real one
         u32x4 w[U];
 #pragma unroll
         for (int j = 0; j < U; ++j)
@@ -1158,12 +1160,12 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
         __syncthreads();
         float amax = red[0];
 #pragma unroll
-        for (int i = 1; i < kWideThreads / kWave; ++i)
+        for (int i = 1; i < ROWS; ++i)
             amax = fmaxf(amax, red[i]);
         const ActScale a = act_scale(amax);
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
-            const int g = tid + k * kWideThreads;
+            const int g = tid + k * TH;
             if (g < G8) {
                 uint32_t lo, hi;
                 quant8_fast(v[k], a, lo, hi);
@@ -1175,7 +1177,7 @@ __global__ __launch_bounds__(kWideThreads) void k_linear_wide(
         if (sx_out && blockIdx.x == 0 && tid == 0)
             *sx_out = a.s;
         __syncthreads();
-        wide_dot<U>(w, xs, C, lane, blockIdx.x * kWideRows + wave, N, sw, bias, a.s, y, acc_out);
+        wide_dot<U>(w, xs, C, lane, blockIdx.x * ROWS + wave, N, sw, bias, a.s, y, acc_out);
     }
 }
 
@@ -3802,11 +3804,12 @@ int gemv_w4a8(const uint32_t* wq, const float* sw, const float* bias, const int8
     if (r == 0 && lanes_per_row == 0 && N <= kWideMaxN && K <= kWideMaxKQ8) {
         // wide workgroups, as for linear_w4a8
         const int C = K / 32, U = (C + kWave - 1) / kWave;
-        const dim3 grid((N + kWideRows - 1) / kWideRows), block(kWideThreads);
+        constexpr int rows = kWideThreads / kWave;
+        const dim3 grid((N + rows - 1) / rows), block(kWideThreads);
         const u32x4* w = reinterpret_cast<const u32x4*>(wq);
 #define BQD_WIDE_Q8_CASE(UU)                                                                               \
         if (U <= UU) {                                                                                     \
-            hipLaunchKernelGGL((k_linear_wide<UU, X_Q8>), grid, block, (size_t)K, (hipStream_t)stream, w, sw, \
+            hipLaunchKernelGGL((k_linear_wide<UU, X_Q8, kWideThreads>), grid, block, (size_t)K, (hipStream_t)stream, w, sw, \
                                bias, qx, sx, y, acc, nullptr, nullptr, N, C);                              \
             return launched();                                                                             \
         }
@@ -3854,17 +3857,18 @@ int linear_w4a8(const uint32_t* wq, const float* sw, const float* bias, const vo
         // the per-linear 28-layer stream 1.266 -> 1.215 ms; with gate/up and
         // the lm_head also wide the stream is slower, 1.279 ms)
         const int C = K / 32, U = (C + kWave - 1) / kWave;
-        const dim3 grid((N + kWideRows - 1) / kWideRows), block(kWideThreads);
+        constexpr int rows = kWideThreadsX / kWave;
+        const dim3 grid((N + rows - 1) / rows), block(kWideThreadsX);
         hipStream_t st = (hipStream_t)stream;
         const u32x4* w = reinterpret_cast<const u32x4*>(wq);
 #define BQD_WIDE_CASE(UU)                                                                                 \
         if (U <= UU) {                                                                                    \
             if (x_dtype == BQD_F32)                                                                       \
-                hipLaunchKernelGGL((k_linear_wide<UU, X_F32>), grid, block, (size_t)K, st, w, sw, bias, x, \
-                                   nullptr, y, acc, qx_out, sx_out, N, C);                                \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F32, kWideThreadsX>), grid, block, (size_t)K, st, w, sw, \
+                                   bias, x, nullptr, y, acc, qx_out, sx_out, N, C);                       \
             else                                                                                          \
-                hipLaunchKernelGGL((k_linear_wide<UU, X_F16>), grid, block, (size_t)K, st, w, sw, bias, x, \
-                                   nullptr, y, acc, qx_out, sx_out, N, C);                                \
+                hipLaunchKernelGGL((k_linear_wide<UU, X_F16, kWideThreadsX>), grid, block, (size_t)K, st, w, sw, \
+                                   bias, x, nullptr, y, acc, qx_out, sx_out, N, C);                       \
             return launched();                                                                            \
         }
         BQD_WIDE_CASES(BQD_WIDE_CASE)
