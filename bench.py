@@ -531,7 +531,7 @@ def run_single(a, dev):
     out["int8_x_note"] = ("x quantised by its producer (not timed here): the GEMV alone on int8 codes and s^x, "
                           "k_linear_wide<2, X_Q8>")
     auto = not (a.r or a.lanes)
-    kname = ("k_linear_wide<2, X_F32> (fused linear, one 1024-thread workgroup per 16 rows, one launch per step)"
+    kname = ("k_linear_wide<2, X_F32, 512> (fused linear, one 512-thread workgroup per 8 rows, one launch per step)"
              if auto else "k_gemv_w4a8 (fused linear, one launch per step)")
     out["roofline"] = roofline(gbs, kname, ms * 1e3, w.bytes_per_step(),
                                measured_traffic(TRAFFIC["single"]) if auto else None)
