@@ -1053,10 +1053,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_w4a8(
 }
 
 // ------------------------------------------------------------------------
-// One fused linear in wide workgroups: 1024 threads, one wave per output
-// row (16 rows per workgroup), U 16-byte chunks per lane (K <= 64 * 32 * U,
-// at most 24576).  Every thread first loads its (at most 3) 8-value groups
-// of x (fp32 / fp16) or its (at most 2) 16-byte pieces of codes, then its
+// One fused linear in wide workgroups: TH threads, one wave per output
+// row (TH / 64 rows per workgroup), U 16-byte chunks per lane (K <= 64 * 32
+// * U, at most 24576).  Every thread first loads its 8-value groups of x
+// (fp32 / fp16; NG of them) or its 16-byte pieces of codes (NQ), then its
 // wave's row chunks, so the activation's loads go out ahead of the weights
 // in the CU's in-order queue; the whole workgroup finds max|x| and writes
 // the codes in one round, and every weight of the workgroup is in flight
