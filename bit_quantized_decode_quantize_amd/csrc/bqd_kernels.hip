@@ -2941,9 +2941,11 @@ __device__ __forceinline__ void stage_codes(u32x2* xs, const f32x4* xf, int G8, 
     }
 }
 
-// Above this many 8-value groups (K > 8192) every wave stages; below, only
-// the staging waves, which hold no weight loads.
-constexpr int kPassStageAllAbove = 1024;
+// Above this many 8-value groups (K > 4096) every wave stages; below, only
+// the staging waves, which hold no weight loads.  (From K > 8192 before:
+// the Gemma-shaped pass, whose down projection has K = 6144, 0.747 -> 0.731
+// ms per token; the Qwen2-7B-shaped one, K = 3584 or 18944, unchanged.)
+constexpr int kPassStageAllAbove = 512;
 
 template <int R>
 __device__ __forceinline__ void pass_prefetch(u32x4 (&cur)[kPassSlots], float& esw, float& eb, const PassTask& t,
