@@ -2593,8 +2593,11 @@ static_assert(5 * kPassMaxK <= 160 * 1024, "pass activation must fit LDS");
 constexpr int kEpochBase = 64;        // after err's 256-byte line
 constexpr int kSyncStride = 16;       // one 64-byte line per epoch word
 constexpr int kXchBase = kEpochBase + kPassMaxGrid * kSyncStride;  // 16448 words = 65792 bytes
-// 8-value groups a staging thread loads at once (all issued before the first use).
-constexpr int kStageGroups = 4;
+// 8-value groups a staging thread loads at once (all issued before the first
+// use): 3 covers K = 3584 on the 4 staging waves and K = 18944 on all 16 in
+// one round and holds fewer registers than 4 (Gemma-shaped pass 0.733 ->
+// 0.725 ms, Qwen2-7B-shaped unchanged; 2 needs a second round at K = 18944).
+constexpr int kStageGroups = 3;
 
 inline size_t pass_lds_bytes(int max_k) { return (size_t)((max_k + 15) & ~15) + 4 * (size_t)max_k; }
 
