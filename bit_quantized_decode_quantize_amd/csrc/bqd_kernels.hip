@@ -3035,10 +3035,17 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
             const int nsc = rows * t.C / 8;
             const BQD_GLOBAL u32x4* src =
                 gptr(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(t.scales) + (size_t)row_start * t.C));
-            const int lane = ct & (kWave - 1);
-            for (int base = ct - lane; base < nsc; base += kPassControl) {  // wave-uniform
-                if (base + lane < nsc)
-                    __builtin_amdgcn_global_load_lds(const_cast<BQD_GLOBAL u32x4*>(src + base + lane),
+            // The lane number is made inside the loop (v_mbcnt, nothing
+            // loaded): hoisted out of it, the per-lane values were among the
+            // kernel's spills, and their scratch reloads joined the CU's
+            // memory queue behind the weight prefetch at the start of every
+            // group-32 linear (Gemma-shaped pass 0.723 -> 0.707 ms; the
+            // kernel now keeps no value in scratch).
+            for (int base = __builtin_amdgcn_readfirstlane(ct) & ~(kWave - 1); base < nsc; base += kPassControl) {
+                int ln;
+                asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+                if (base + ln < nsc)
+                    __builtin_amdgcn_global_load_lds(const_cast<BQD_GLOBAL u32x4*>(src + base + ln),
                                                      (BQD_LDS void*)(sl16 + base), 16, 0, 0);
             }
         }
