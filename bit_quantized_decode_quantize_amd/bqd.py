@@ -90,9 +90,9 @@ def lib() -> C.CDLL:
         "layer_w4a8_forward": (I, [C.POINTER(LinearW4A8), I, P, I, P, P]),
         "decode_pass_desc_bytes": (C.c_size_t, [I]),
         "decode_pass_encode": (I, [C.POINTER(LinearW4A8), I, P, I, P, P, C.c_size_t, C.POINTER(C.c_int32),
-                                   C.POINTER(C.c_size_t)]),
-        "decode_pass_w4a8": (I, [P, I, I, P, C.c_size_t, I, P]),
-        "decode_pass_w4a8_static": (I, [P, I, I, C.c_size_t, I, P, P]),
+                                   C.POINTER(C.c_size_t), C.POINTER(C.c_int32)]),
+        "decode_pass_w4a8": (I, [P, I, I, I, P, C.c_size_t, I, P]),
+        "decode_pass_w4a8_static": (I, [P, I, I, I, C.c_size_t, I, P, P]),
         "read_probe": (I, [P, C.c_size_t, P, I, I, P]),
         "gemv_w4a16": (I, [P, P, P, P, P, I, I, I, I, P]),
         "add_rmsnorm_quant": (I, [P, P, P, C.c_float, P, P, P, P, I, I, P]),
@@ -637,16 +637,18 @@ class DecodePass:
         host = (C.c_uint8 * nbytes)()
         mk = C.c_int32(0)
         sb = C.c_size_t(0)
+        sl = C.c_int32(0)
         _call("decode_pass_encode", lin, n, C.cast(xp, C.c_void_p), BQD_F32 if dt == torch.float32 else BQD_F16,
-              C.cast(yp, C.c_void_p), C.cast(host, C.c_void_p), nbytes, C.byref(mk), C.byref(sb))
+              C.cast(yp, C.c_void_p), C.cast(host, C.c_void_p), nbytes, C.byref(mk), C.byref(sb), C.byref(sl))
         self.max_k = mk.value
         self.sync_bytes = sb.value
+        self.slots = sl.value  # chunks per lane per step: the kernel instance
         self.desc = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device)
         self.sync = torch.zeros(self.sync_bytes // 4, dtype=torch.int32, device=device)
         self._keep = (list(xs), list(ys), list(linears))
 
     def run(self, stream=None, spin_limit: int = 0) -> None:
-        _call("decode_pass_w4a8", self.desc.data_ptr(), self.n, self.max_k, self.sync.data_ptr(),
+        _call("decode_pass_w4a8", self.desc.data_ptr(), self.n, self.max_k, self.slots, self.sync.data_ptr(),
               self.sync_bytes, spin_limit, _stream(stream))
 
     def run_static(self, err: torch.Tensor, stream=None, spin_limit: int = 0) -> None:
@@ -654,8 +656,8 @@ class DecodePass:
         (decode_pass_w4a8_static): allocates nothing; the error word lands in
         ``err`` (one int32 on the device)."""
         _dev(err, "err", (torch.int32,), 1)
-        _call("decode_pass_w4a8_static", self.desc.data_ptr(), self.n, self.max_k, self.sync_bytes, spin_limit,
-              err.data_ptr(), _stream(stream))
+        _call("decode_pass_w4a8_static", self.desc.data_ptr(), self.n, self.max_k, self.slots, self.sync_bytes,
+              spin_limit, err.data_ptr(), _stream(stream))
 
     def error_word(self) -> int:
         """Bit 0: a wait ran out of spins; bit 1: descriptors for another
@@ -674,7 +676,7 @@ class DecodePass:
                                signed=True) for i in range(self.n)]
 
 
-DESC_HEADER, DESC_TASK = 16, 96   # bytes of the descriptor header and of one linear's descriptor
+DESC_HEADER, DESC_TASK = 32, 96   # bytes of the descriptor header and of one linear's descriptor
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int, unroll: int = 1, stream=None) -> None:

@@ -2554,8 +2554,10 @@ __global__ __launch_bounds__(kVbThreads) void k_verify_blocks(
 // ------------------------------------------------------------------------
 struct PassHeader {
     int32_t n, grid, max_k, xch_words;  // xch_words: 32-bit words per exchange set
+    int32_t slots;                      // chunks per lane per step: the kernel instance (k_decode_pass<slots>)
+    int32_t pad[3];
 };
-static_assert(sizeof(PassHeader) == 16, "descriptor header layout");
+static_assert(sizeof(PassHeader) == 32, "descriptor header layout");
 
 struct PassTask {
     const u32x4* wq;
@@ -2584,6 +2586,12 @@ constexpr int kPassThreads = 1024;    // 16 waves: one workgroup per CU
 constexpr int kPassWorkers = 768;
 constexpr int kPassControl = kPassThreads - kPassWorkers;
 constexpr int kPassSlots = 8;         // 16-byte chunks per lane per pipeline step
+// Passes whose linears are all group-32 (small per-CU shares: 6-37 KB in the
+// Gemma-shaped stream) run an instance with 4: a step's fixed work (the
+// predicated loads, the register copy) sits on every small linear's
+// critical path (Gemma-shaped pass 0.65 against 0.71 ms); per-row passes
+// keep 8 (4 there: 1.06 against 1.00 ms, the large linears stream slower).
+constexpr int kPassSlotsSmall = 4;
 constexpr int kPassMaxGrid = 1024;
 constexpr int kPassSpinLimit = 1 << 21;
 constexpr int kPassWgPerCu = 1;
@@ -2652,11 +2660,11 @@ __device__ __forceinline__ u32x4 ld_stream(const BQD_GLOBAL u32x4* p)
 // Loads step j of row batch b into buf; with the first step of a batch, lane
 // rr of each lane group also loads the scale and bias of the group's row rr
 // (the epilogue's operands arrive with the weights, not after them).
-template <int R>
-__device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], float& esw, float& eb, const PassTask& t,
+template <int R, int S>
+__device__ __forceinline__ void pass_load(u32x4 (&buf)[S], float& esw, float& eb, const PassTask& t,
                                           int row_start, int rows, int b, int j)
 {
-    constexpr int U = kPassSlots / R;
+    constexpr int U = S / R;
     const int L = 1 << t.lshift;
     const int lane = threadIdx.x & (L - 1);
     const int groups = kPassWorkers >> t.lshift;
@@ -2690,18 +2698,18 @@ __device__ __forceinline__ void pass_load(u32x4 (&buf)[kPassSlots], float& esw, 
 // row's y goes to the output buffer and, when a later linear of the pass
 // reads it, to the exchange (xcur) as ~bits, with the same row of the other
 // set (xold) cleared for the next pass.
-template <int R>
-__device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, float& eb, bool have_cur,
+template <int R, int S>
+__device__ __forceinline__ void pass_run(u32x4 (&cur)[S], float& esw, float& eb, bool have_cur,
                                          const PassTask& t, int row_start, int rows, const u32x4* xs, float sx,
                                          uint32_t* xcur, uint32_t* xold)
 {
-    constexpr int U = kPassSlots / R;
+    constexpr int U = S / R;
     const int L = 1 << t.lshift;
     const int lane = threadIdx.x & (L - 1);
     const int groups = kPassWorkers >> t.lshift;
     const int grp = threadIdx.x >> t.lshift;
     if (!have_cur)
-        pass_load<R>(cur, esw, eb, t, row_start, rows, 0, 0);
+        pass_load<R, S>(cur, esw, eb, t, row_start, rows, 0, 0);
     float nsw = 0.0f, nbv = 0.0f;  // next batch's epilogue operands
     for (int b = 0; b < t.batches; ++b) {
         int acc[R];
@@ -2709,7 +2717,7 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
         for (int rr = 0; rr < R; ++rr)
             acc[rr] = 0;
         for (int j = 0; j < t.steps; ++j) {
-            u32x4 nxt[kPassSlots];
+            u32x4 nxt[S];
             int nb = b, nj = j + 1;
             if (nj == t.steps) {
                 nb = b + 1;
@@ -2717,7 +2725,7 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
             }
             const bool more = nb < t.batches;
             if (more)
-                pass_load<R>(nxt, nsw, nbv, t, row_start, rows, nb, nj);
+                pass_load<R, S>(nxt, nsw, nbv, t, row_start, rows, nb, nj);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = j * U + u;
@@ -2731,7 +2739,7 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
             }
             if (more) {
 #pragma unroll
-                for (int k = 0; k < kPassSlots; ++k)
+                for (int k = 0; k < S; ++k)
                     cur[k] = nxt[k];
             }
         }
@@ -2771,7 +2779,8 @@ __device__ __forceinline__ void pass_run(u32x4 (&cur)[kPassSlots], float& esw, f
 // the arithmetic and order, hence the bits, of k_gemv_w4a8_g32 at 32
 // lanes per row (the encoder fixes 32 lanes and one row per lane group).
 // sl holds the workgroup's rows' scales, staged in LDS.
-__device__ __forceinline__ void pass_run_g32(u32x4 (&cur)[kPassSlots], float& esw, float& eb, bool have_cur,
+template <int S>
+__device__ __forceinline__ void pass_run_g32(u32x4 (&cur)[S], float& esw, float& eb, bool have_cur,
                                              const PassTask& t, int row_start, int rows, const u32x4* xs, float sx,
                                              const uint16_t* sl, uint32_t* xcur, uint32_t* xold)
 {
@@ -2780,14 +2789,14 @@ __device__ __forceinline__ void pass_run_g32(u32x4 (&cur)[kPassSlots], float& es
     const int groups = kPassWorkers / L;
     const int grp = threadIdx.x / L;
     if (!have_cur)
-        pass_load<1>(cur, esw, eb, t, row_start, rows, 0, 0);
+        pass_load<1, S>(cur, esw, eb, t, row_start, rows, 0, 0);
     float nsw = 0.0f, nbv = 0.0f;
     for (int b = 0; b < t.batches; ++b) {
         const int rl = b * groups + grp;
         const uint16_t* srow = sl + (size_t)min(rl, rows - 1) * t.C;
         float facc = 0.0f;
         for (int j = 0; j < t.steps; ++j) {
-            u32x4 nxt[kPassSlots];
+            u32x4 nxt[S];
             int nb = b, nj = j + 1;
             if (nj == t.steps) {
                 nb = b + 1;
@@ -2795,10 +2804,10 @@ __device__ __forceinline__ void pass_run_g32(u32x4 (&cur)[kPassSlots], float& es
             }
             const bool more = nb < t.batches;
             if (more)
-                pass_load<1>(nxt, nsw, nbv, t, row_start, rows, nb, nj);
+                pass_load<1, S>(nxt, nsw, nbv, t, row_start, rows, nb, nj);
 #pragma unroll
-            for (int u = 0; u < kPassSlots; ++u) {
-                const int i = j * kPassSlots + u;
+            for (int u = 0; u < S; ++u) {
+                const int i = j * S + u;
                 if (i < t.iters) {  // uniform across the wave
                     const int c = min(i * L + lane, t.C - 1);
                     const int ag = dot_chunk16(cur[u], xs[2 * c], xs[2 * c + 1], 0) >> 4;
@@ -2808,7 +2817,7 @@ __device__ __forceinline__ void pass_run_g32(u32x4 (&cur)[kPassSlots], float& es
             }
             if (more) {
 #pragma unroll
-                for (int k = 0; k < kPassSlots; ++k)
+                for (int k = 0; k < S; ++k)
                     cur[k] = nxt[k];
             }
         }
@@ -2950,16 +2959,17 @@ __device__ __forceinline__ void stage_codes(u32x2* xs, const f32x4* xf, int G8, 
 // ms per token; the Qwen2-7B-shaped one, K = 3584 or 18944, unchanged.)
 constexpr int kPassStageAllAbove = 512;
 
-template <int R>
-__device__ __forceinline__ void pass_prefetch(u32x4 (&cur)[kPassSlots], float& esw, float& eb, const PassTask& t,
+template <int R, int S>
+__device__ __forceinline__ void pass_prefetch(u32x4 (&cur)[S], float& esw, float& eb, const PassTask& t,
                                               int w)
 {
     int row_start, rows;
     pass_range(t, w, row_start, rows);
     if (rows > 0)
-        pass_load<R>(cur, esw, eb, t, row_start, rows, 0, 0);
+        pass_load<R, S>(cur, esw, eb, t, row_start, rows, 0, 0);
 }
 
+template <int S>
 __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* __restrict__ hdr,
                                                               const PassTask* __restrict__ tasks, int n_launch,
                                                               int max_k_launch, uint32_t* __restrict__ sync,
@@ -2979,7 +2989,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     const int ct = tid - kPassWorkers;       // staging-thread index (>= 0 on the staging waves)
     uint32_t* err = sync;
     uint32_t* epochs = sync + kEpochBase;    // epochs[w * kSyncStride]
-    if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || G > kPassMaxGrid ||
+    if (hdr->grid != G || n != n_launch || hdr->max_k != max_k_launch || hdr->slots != S || G > kPassMaxGrid ||
         (size_t)kXchBase + 2 * (size_t)(uint32_t)hdr->xch_words > sync_words) {
         // uniform: every workgroup leaves
         if (tid == 0 && w == 0)
@@ -2997,7 +3007,7 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
     uint32_t* xcur = sync + kXchBase + (epoch & 1u) * xw;
     uint32_t* xold = sync + kXchBase + ((epoch & 1u) ^ 1u) * xw;
 
-    u32x4 cur[kPassSlots];
+    u32x4 cur[S];
     float esw = 0.0f, eb = 0.0f;  // first batch's epilogue operands, loaded with cur
     PassTask t = ring_get(dring, 0);
     bool have_cur = false;
@@ -3006,9 +3016,9 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         pass_range(t, w, rs, rw);
         if (rw > 0) {
             if (t.r == 2)
-                pass_prefetch<2>(cur, esw, eb, t, w);
+                pass_prefetch<2, S>(cur, esw, eb, t, w);
             else
-                pass_prefetch<1>(cur, esw, eb, t, w);
+                pass_prefetch<1, S>(cur, esw, eb, t, w);
             have_cur = true;
         }
     }
@@ -3076,12 +3086,12 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
         // 3. workers: stream the weights, write the rows
         if (rows > 0 && worker) {
             if (t.kind == 1)
-                pass_run_g32(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s,
+                pass_run_g32<S>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s,
                              reinterpret_cast<const uint16_t*>(sl16), xcur, xold);
             else if (t.r == 2)
-                pass_run<2>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
+                pass_run<2, S>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
             else
-                pass_run<1>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
+                pass_run<1, S>(cur, esw, eb, have_cur, t, row_start, rows, xs, a.s, xcur, xold);
         }
         // 4. workers prefetch ti+1
         have_cur = false;
@@ -3090,9 +3100,9 @@ __global__ __launch_bounds__(kPassThreads) void k_decode_pass(const PassHeader* 
             pass_range(tn, w, rs, rw);
             if (rw > 0) {
                 if (tn.r == 2)
-                    pass_prefetch<2>(cur, esw, eb, tn, w);
+                    pass_prefetch<2, S>(cur, esw, eb, tn, w);
                 else
-                    pass_prefetch<1>(cur, esw, eb, tn, w);
+                    pass_prefetch<1, S>(cur, esw, eb, tn, w);
                 have_cur = true;
             }
         }
@@ -4402,7 +4412,7 @@ size_t decode_pass_desc_bytes(int32_t n)
 static int pass_grid(int max_k, int* grid)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pass, kPassThreads, pass_lds_bytes(max_k)) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pass<kPassSlots>, kPassThreads, pass_lds_bytes(max_k)) !=
             hipSuccess ||
         per_cu < 1)
         return BQD_ERR_LAUNCH;
@@ -4413,7 +4423,7 @@ static int pass_grid(int max_k, int* grid)
 // Lanes per row and rows per lane group for one linear on a grid of G
 // workgroups: fewest loads per lane, plus a charge per pipeline step (small
 // linears then take one step, whose loads are all issued before the wait).
-static void pass_shape_host(int N, int C, int G, PassTask& t)
+static void pass_shape_host(int N, int C, int G, int slots, PassTask& t)
 {
     const int rows_max = (N + G - 1) / G;
     long best = -1;
@@ -4422,7 +4432,7 @@ static void pass_shape_host(int N, int C, int G, PassTask& t)
             const int L = 1 << ls, groups = kPassWorkers >> ls;
             const int iters = (C + L - 1) / L;
             const int batches = (rows_max + groups * r - 1) / (groups * r);
-            const int steps = (iters * r + kPassSlots - 1) / kPassSlots;
+            const int steps = (iters * r + slots - 1) / slots;
             const long cost = (long)batches * r * iters + 4L * batches * steps;
             if (best < 0 || cost < best) {
                 best = cost;
@@ -4445,11 +4455,12 @@ static bool contains(const void* outer, size_t no, const void* inner, size_t ni)
 }
 
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
-                       float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k, size_t* sync_bytes)
+                       float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k, size_t* sync_bytes,
+                       int32_t* slots_out)
 {
     if (n <= 0 || n > BQD_MAX_PASS_LINEARS)
         return BQD_ERR_SHAPE;
-    if (!lin || !x || !y || !desc_host || !max_k || !sync_bytes)
+    if (!lin || !x || !y || !desc_host || !max_k || !sync_bytes || !slots_out)
         return BQD_ERR_NULL;
     int rc = check_x_dtype(x_dtype);
     if (rc)
@@ -4540,12 +4551,17 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         return BQD_ERR_BOUND;
     if ((rc = bqd_init()))
         return rc;
+    // the kernel instance: 4 chunks per step when every linear is group-32
+    bool all_g32 = true;
+    for (int i = 0; i < n; ++i)
+        all_g32 = all_g32 && lin[i].scale_kind == BQD_SCALE_GROUP32_F16;
+    const int slots = all_g32 ? kPassSlotsSmall : kPassSlots;
     int G = 0;
     if ((rc = pass_grid(kmax, &G)))
         return rc;
     if (G > kPassMaxGrid)
         return BQD_ERR_LAUNCH;
-    PassHeader h{n, G, kmax, (int32_t)words};
+    PassHeader h{n, G, kmax, (int32_t)words, slots, {0, 0, 0}};
     std::memcpy(desc_host, &h, sizeof h);
     PassTask* d = reinterpret_cast<PassTask*>(reinterpret_cast<char*>(desc_host) + sizeof(PassHeader));
     for (int i = 0; i < n; ++i) {
@@ -4563,7 +4579,7 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
         t.x_dtype = x_dtype == BQD_F16 ? X_F16 : X_F32;
         t.xin = src[i] >= 0 ? (int32_t)(xout[src[i]] + off[i]) : -1;
         t.xout = (int32_t)xout[i];
-        pass_shape_host(t.N, t.C, G, t);
+        pass_shape_host(t.N, t.C, G, slots, t);
         if (t.kind == 1) {
             // the per-linear group-32 kernel's lanes per row (its sums run
             // in that order), one row per lane group
@@ -4574,19 +4590,23 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
             t.r = 1;
             t.iters = (t.C + 31) / 32;
             t.batches = (rows_max + (kPassWorkers >> 5) - 1) / (kPassWorkers >> 5);
-            t.steps = (t.iters + kPassSlots - 1) / kPassSlots;
+            t.steps = (t.iters + slots - 1) / slots;
         }
         std::memcpy(d + i, &t, sizeof t);
     }
     *max_k = kmax;
     *sync_bytes = ((size_t)kXchBase + 2 * (size_t)words) * sizeof(uint32_t);
+    *slots_out = slots;
     return BQD_OK;
 }
 
-static int pass_check_launch(const void* desc_dev, int32_t n, int32_t max_k, size_t sync_bytes, int32_t spin_limit)
+static int pass_check_launch(const void* desc_dev, int32_t n, int32_t max_k, int32_t slots, size_t sync_bytes,
+                             int32_t spin_limit)
 {
     if (n <= 0 || n > BQD_MAX_PASS_LINEARS)
         return BQD_ERR_SHAPE;
+    if (slots != kPassSlots && slots != kPassSlotsSmall)
+        return BQD_ERR_CONFIG;
     if (!desc_dev)
         return BQD_ERR_NULL;
     int rc = check_k(max_k);
@@ -4603,8 +4623,8 @@ static int pass_check_launch(const void* desc_dev, int32_t n, int32_t max_k, siz
     return BQD_OK;
 }
 
-static int pass_launch(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync, size_t sync_bytes,
-                       int32_t spin_limit, hipStream_t stream)
+static int pass_launch(const void* desc_dev, int32_t n, int32_t max_k, int32_t slots, uint32_t* sync,
+                       size_t sync_bytes, int32_t spin_limit, hipStream_t stream)
 {
     int G = 0;
     int rc = pass_grid(max_k, &G);
@@ -4623,16 +4643,18 @@ static int pass_launch(const void* desc_dev, int32_t n, int32_t max_k, uint32_t*
     // work, the bounded waits end them with bit 0 of the error word instead
     // of a hang.  (A cooperative launch gives the same residency, costs
     // about 1.5 % per pass and has made the profiler's exit handlers crash.)
-    if (hipLaunchKernel((const void*)k_decode_pass, dim3(G), dim3(kPassThreads), args,
+    const void* fn = slots == kPassSlotsSmall ? (const void*)k_decode_pass<kPassSlotsSmall>
+                                              : (const void*)k_decode_pass<kPassSlots>;
+    if (hipLaunchKernel(fn, dim3(G), dim3(kPassThreads), args,
                         (size_t)pass_lds_bytes(max_k), stream) != hipSuccess)
         return BQD_ERR_LAUNCH;
     return launched();
 }
 
-int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev, size_t sync_bytes,
-                     int32_t spin_limit, void* stream)
+int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, int32_t slots, uint32_t* sync_dev,
+                     size_t sync_bytes, int32_t spin_limit, void* stream)
 {
-    int rc = pass_check_launch(desc_dev, n, max_k, sync_bytes, spin_limit);
+    int rc = pass_check_launch(desc_dev, n, max_k, slots, sync_bytes, spin_limit);
     if (rc)
         return rc;
     if (!sync_dev)
@@ -4641,13 +4663,13 @@ int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* s
         return BQD_ERR_ALIGN;
     if ((rc = bqd_init()))
         return rc;
-    return pass_launch(desc_dev, n, max_k, sync_dev, sync_bytes, spin_limit, (hipStream_t)stream);
+    return pass_launch(desc_dev, n, max_k, slots, sync_dev, sync_bytes, spin_limit, (hipStream_t)stream);
 }
 
-int decode_pass_w4a8_static(const void* desc_dev, int32_t n, int32_t max_k, size_t sync_bytes,
+int decode_pass_w4a8_static(const void* desc_dev, int32_t n, int32_t max_k, int32_t slots, size_t sync_bytes,
                             int32_t spin_limit, uint32_t* err_dev, void* stream)
 {
-    int rc = pass_check_launch(desc_dev, n, max_k, sync_bytes, spin_limit);
+    int rc = pass_check_launch(desc_dev, n, max_k, slots, sync_bytes, spin_limit);
     if (rc)
         return rc;
     if (sync_bytes > (size_t)BQD_STATIC_PASS_BYTES)
@@ -4673,7 +4695,7 @@ int decode_pass_w4a8_static(const void* desc_dev, int32_t n, int32_t max_k, size
     hipLaunchKernelGGL(k_zero16, dim3(grid), dim3(kThreads), 0, st, reinterpret_cast<u32x4*>(ws), n16);
     if ((rc = launched()))
         return rc;
-    if ((rc = pass_launch(desc_dev, n, max_k, ws, sync_bytes, spin_limit, st)))
+    if ((rc = pass_launch(desc_dev, n, max_k, slots, ws, sync_bytes, spin_limit, st)))
         return rc;
     hipLaunchKernelGGL(k_copy_word, dim3(1), dim3(kWave), 0, st, ws, err_dev);
     return launched();

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BQD_ABI_VERSION 3
+#define BQD_ABI_VERSION 4
 
 #define BQD_OK 0
 #define BQD_ERR_NULL (-1)      /* a required pointer is NULL                 */
@@ -420,8 +420,12 @@ size_t decode_pass_desc_bytes(int32_t n);
  * [N_i], N_i > 0), and serialises them into desc_host (host,
  * decode_pass_desc_bytes(n) bytes) for the current device: the work split
  * is encoded for the grid the launch will use there, so a device must be
- * current (BQD_ERR_DEVICE otherwise).  *max_k receives the largest K and
- * *sync_bytes the size of the workspace decode_pass_w4a8 needs.
+ * current (BQD_ERR_DEVICE otherwise).  *max_k receives the largest K,
+ * *sync_bytes the size of the workspace decode_pass_w4a8 needs and *slots
+ * the 16-byte chunks per lane of each pipeline step, which selects the
+ * kernel instance: 4 when every linear is group-32 (small shares per
+ * compute unit: a step's fixed work is on each link's critical path), else
+ * 8.  The launch takes all three back unchanged.
  * K_i % 32 == 0 and K_i <= BQD_MAX_PASS_K (BQD_ERR_BOUND otherwise).
  * Where each activation comes from:
  *   - x[i] overlaps no output: it was written before the launch and is read
@@ -441,7 +445,7 @@ size_t decode_pass_desc_bytes(int32_t n);
  * before decode_pass_w4a8 reads it. */
 int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const* x, int32_t x_dtype,
                        float* const* y, void* desc_host, size_t desc_bytes, int32_t* max_k,
-                       size_t* sync_bytes);
+                       size_t* sync_bytes, int32_t* slots);
 
 /* One decode step over the n encoded linears in order, in one launch of one
  * workgroup per compute unit, all resident at once: for each linear, the activation quantisation of quantize_act and
@@ -451,8 +455,10 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
  * exchange in sync_dev, and the readers poll the words they need (one
  * device-scope store and one device-scope load per dependency, no counters
  * or fences).  Weights of the next linear are prefetched while waiting.
- * desc_dev (device) holds the encoded descriptors; max_k is the value
- * decode_pass_encode reported; sync_dev (device, 256-byte aligned) is the
+ * desc_dev (device) holds the encoded descriptors; max_k and slots are the
+ * values decode_pass_encode reported (slots 4 or 8, else BQD_ERR_CONFIG;
+ * descriptors encoded for the other instance set bit 1 in the kernel);
+ * sync_dev (device, 256-byte aligned) is the
  * workspace of *sync_bytes bytes it reported, zero-filled once by the
  * caller (sync_bytes: that size, which bounds what the kernel may
  * touch; descriptors needing more are refused in the kernel with bit 1)
@@ -464,10 +470,10 @@ int decode_pass_encode(const bqd_linear_w4a8* lin, int32_t n, const void* const*
  * (0 = default: 2^21 polling rounds, about 2 s); a wait that runs out sets bit 0 of
  * sync_dev[0] and proceeds with what it read, so the kernel always ends;
  * bit 1 is set (and nothing computed) when the descriptors were encoded
- * for another grid or another n.  The caller reads sync_dev[0] to check,
+ * for another grid, another n or another slots.  The caller reads sync_dev[0] to check,
  * and clears it to reuse. */
-int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* sync_dev, size_t sync_bytes,
-                     int32_t spin_limit, void* stream);
+int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, int32_t slots, uint32_t* sync_dev,
+                     size_t sync_bytes, int32_t spin_limit, void* stream);
 
 /* Largest workspace decode_pass_w4a8_static holds: 16 MiB of device memory
  * per GPU the library runs on (a 28-layer Qwen2-7B-shaped chained pass with
@@ -489,7 +495,7 @@ int decode_pass_w4a8(const void* desc_dev, int32_t n, int32_t max_k, uint32_t* s
  * results, so callers serialise them.  Launch errors and argument checks as
  * in decode_pass_w4a8; BQD_ERR_LAUNCH also if the array's address could
  * not be found on this GPU. */
-int decode_pass_w4a8_static(const void* desc_dev, int32_t n, int32_t max_k, size_t sync_bytes,
+int decode_pass_w4a8_static(const void* desc_dev, int32_t n, int32_t max_k, int32_t slots, size_t sync_bytes,
                             int32_t spin_limit, uint32_t* err_dev, void* stream);
 
 /* ---------------------------------------------------------------------- */

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bqd.abi_version() == 3
+    assert bqd.abi_version() == 4
     for s in (OK, NULL, SHAPE, ALIGN, BOUND, DTYPE, CONFIG, LAUNCH, DEVICE):
         assert bqd.status_string(s)
     assert bqd.status_string(12345) == "unknown status"
@@ -240,10 +240,11 @@ def test_decode_pass_encode_validates_and_serialises():
     L = _lib()
     n = 2
     nbytes = L.decode_pass_desc_bytes(n)
-    assert nbytes == 16 + 2 * 96
+    assert nbytes == 32 + 2 * 96
     host = (C.c_uint8 * nbytes)()
     mk = C.c_int32(0)
     sb = C.c_size_t(0)
+    sl = C.c_int32(0)
     # clear of the weights (a: P .. P + 0x2BC00), x[1]: 18944 fp32 = 0x12800 bytes
     X0, X1, Y0, Y1 = P + 0x400000, P + 0x410000, P + 0x440000, P + 0x450000
 
@@ -252,7 +253,7 @@ def test_decode_pass_encode_validates_and_serialises():
         xs = (C.c_void_p * 2)(*x)
         ys = (C.c_void_p * 2)(*y)
         return L.decode_pass_encode(arr, n, C.cast(xs, C.c_void_p), dt, C.cast(ys, C.c_void_p),
-                                    C.cast(host, C.c_void_p), nbytes, C.byref(mk), C.byref(sb))
+                                    C.cast(host, C.c_void_p), nbytes, C.byref(mk), C.byref(sb), C.byref(sl))
 
     a = bqd.LinearW4A8(P, P + 0x400, 0, 100, 3584, 0, 0, 0)
     b = bqd.LinearW4A8(P + 0x1000, P + 0x500, P + 0x600, 7, 18944, 0, 0, 0)
@@ -327,15 +328,16 @@ def test_decode_pass_encode_validates_and_serialises():
 def test_decode_pass_launch_validates_before_launch():
     L = _lib()
     WS = (64 + 1024 * 16) * 4                # the smallest workspace: no exchange
-    assert L.decode_pass_w4a8(P, 0, 64, P, WS, 0, None) == SHAPE
-    assert L.decode_pass_w4a8(None, 2, 64, P, WS, 0, None) == NULL
-    assert L.decode_pass_w4a8(P, 2, 64, None, WS, 0, None) == NULL
-    assert L.decode_pass_w4a8(P, 2, 40, P, WS, 0, None) == SHAPE
-    assert L.decode_pass_w4a8(P, 2, 64, P, WS, -1, None) == CONFIG
-    assert L.decode_pass_w4a8(P + 8, 2, 64, P, WS, 0, None) == ALIGN
-    assert L.decode_pass_w4a8(P, 2, 64, P + 64, WS, 0, None) == ALIGN   # the workspace is 256-byte aligned
-    assert L.decode_pass_w4a8(P, 2, 64, P, WS - 256, 0, None) == SHAPE  # smaller than any workspace
-    assert L.decode_pass_w4a8(P, 2, 64, P, WS + 4, 0, None) == SHAPE    # not a workspace size
+    assert L.decode_pass_w4a8(P, 0, 64, 8, P, WS, 0, None) == SHAPE
+    assert L.decode_pass_w4a8(None, 2, 64, 8, P, WS, 0, None) == NULL
+    assert L.decode_pass_w4a8(P, 2, 64, 8, None, WS, 0, None) == NULL
+    assert L.decode_pass_w4a8(P, 2, 40, 8, P, WS, 0, None) == SHAPE
+    assert L.decode_pass_w4a8(P, 2, 64, 8, P, WS, -1, None) == CONFIG
+    assert L.decode_pass_w4a8(P + 8, 2, 64, 8, P, WS, 0, None) == ALIGN
+    assert L.decode_pass_w4a8(P, 2, 64, 8, P + 64, WS, 0, None) == ALIGN   # the workspace is 256-byte aligned
+    assert L.decode_pass_w4a8(P, 2, 64, 8, P, WS - 256, 0, None) == SHAPE  # smaller than any workspace
+    assert L.decode_pass_w4a8(P, 2, 64, 8, P, WS + 4, 0, None) == SHAPE    # not a workspace size
+    assert L.decode_pass_w4a8(P, 2, 64, 6, P, WS, 0, None) == CONFIG            # slots: 4 or 8
 
 
 def test_read_probe_validates_before_launch():

@@ -66,8 +66,8 @@ def test_static_pass_refuses_a_workspace_beyond_its_array():
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     L = bqd.lib()
     too_big = bqd.BQD_STATIC_PASS_BYTES + 256
-    assert L.decode_pass_w4a8_static(p.desc.data_ptr(), p.n, p.max_k, too_big, 0, err.data_ptr(), None) == -4
-    assert L.decode_pass_w4a8_static(p.desc.data_ptr(), p.n, p.max_k, p.sync_bytes, 0, None, None) == -1
+    assert L.decode_pass_w4a8_static(p.desc.data_ptr(), p.n, p.max_k, p.slots, too_big, 0, err.data_ptr(), None) == -4
+    assert L.decode_pass_w4a8_static(p.desc.data_ptr(), p.n, p.max_k, p.slots, p.sync_bytes, 0, None, None) == -1
 
 
 def test_static_pass_replays_from_a_hip_graph():
