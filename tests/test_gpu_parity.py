@@ -963,6 +963,34 @@ def test_decode_pass_rejects_descriptors_for_another_grid():
     assert p.error_word() == 0 and not any(torch.isnan(y).any() for y in ys)
 
 
+@pytest.mark.parametrize("kind", ["rowwise", "group32"])
+def test_decode_pass_instance_matches_the_encoded_step(kind):
+    """The encoder picks 4 chunks per lane per step when every linear is
+    group-32 and 8 otherwise; a launch of the other instance on those
+    descriptors is refused in the kernel (error bit 1, nothing computed), and
+    the encoded one then runs clean."""
+    if kind == "rowwise":
+        lins, xs, ys, _ = _pass_fixture(tag="passslots")
+    else:
+        lins, _, xs, ys, _ = _g32_pass("g32slots", chained=True)
+    p = bqd.DecodePass(lins, xs, ys)
+    want = 8 if kind == "rowwise" else 4
+    assert p.slots == want
+    assert int(p.desc[16:20].cpu().view(torch.int32).item()) == want  # the header's slots word
+    for y in ys:
+        y.fill_(float("nan"))
+    p.slots = 12 - want
+    p.run()
+    sync()
+    assert p.error_word() & 2
+    assert all(torch.isnan(y).all() for y in ys)
+    p.slots = want
+    p.clear_error()
+    p.run()
+    sync()
+    assert p.error_word() == 0 and not any(torch.isnan(y).any() for y in ys)
+
+
 # ------------------------------------------------ packed 6-bit lm_head --
 @pytest.mark.parametrize("N,K", [(3, 256), (37, 1536), (5, 4096)])
 def test_quantize_weights_q6k_bit_exact(N, K):
